@@ -1,0 +1,200 @@
+"""Seeded synthetic inputs for the SLA2 forward: the only module both the HIP path's tests/bench
+and the CPU oracle use.
+
+It draws tensors and nothing else: no pooling, projection, scoring, softmax or selection lives
+here.  Callers that need the router's k-th/(k+1)-th score gap (the tests) check it with the oracle
+and ask this module to redraw the noise of single query blocks (``redraw_query_blocks``).
+
+Workloads (the pages measure on Wan2.1 video DiT attention, which is not available; these
+tensors stand in for it with the same shapes and an attention-concentrating structure):
+
+* ``tiny``       B=1 H=2  N=1024  d=64  k=4   fp32, Q/K/V iid N(0,1).
+* ``video_s``    B=1 H=12 N=32768 d=128 k=51  bf16, latent 8x64x64 (t, h, w) flattened.
+* ``video_l``    B=1 H=40 N=75600 d=128 k=60  bf16, latent 21x45x80, last block 16 tokens.
+* ``sweep``      B=2 H=12 N=32768 d=128, keep in {20,10,5,3}% (k = round(keep*512)),
+                 cluster scale in {0.5,1,2}, alpha fixed 0.5 or random.
+* ``video_l_fp8`` the ``video_l`` tensors, for the fp8 sparse-branch path.
+
+Clustered Q/K: the latent grid is cut into boxes of (2, 8, 8) tokens (smaller at the edges);
+per (batch, head, box) a centre mu ~ N(0, s^2 I_d) is shared by the box's queries and keys,
+Q_n = mu + e_q, K_n = mu + e_k with e ~ N(0, 0.3) (0.3 read as the variance).  V ~ N(0, 1),
+alpha = sigmoid(N(0, 1)) per (batch, head, token), proj_q and proj_k ~ N(0, 1/d) (variance).
+Every stream is a numpy PCG64 seeded by SeedSequence([seed, workload id, tensor id, b, h, ...]).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "workload",
+    "sweep_workloads",
+    "draw",
+    "redraw_query_blocks",
+]
+
+NOISE_VAR = 0.3
+BOX = (2, 8, 8)
+
+# tensor ids of the seed streams
+_T_Q, _T_K, _T_V, _T_ALPHA, _T_WQ, _T_WK, _T_CENTRE, _T_QNOISE, _T_KNOISE, _T_REDRAW = range(10)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    topk: int
+    dtype: str  # "fp32" or "bf16"
+    kind: str  # "iid" or "clustered"
+    grid: tuple = ()
+    cluster_scale: float = 1.0
+    alpha: str = "random"  # "random" (sigmoid(N(0,1))) or "half" (0.5)
+    fp8: bool = False
+    block: int = 64
+    wid: int = 0  # seed-stream id of the workload
+
+    @property
+    def n_blocks(self) -> int:
+        return -(-self.N // self.block)
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 1024, 64, 4, "fp32", "iid", wid=1),
+    "video_s": Workload("video_s", 1, 12, 32768, 128, 51, "bf16", "clustered", (8, 64, 64), wid=2),
+    "video_l": Workload("video_l", 1, 40, 75600, 128, 60, "bf16", "clustered", (21, 45, 80), wid=3),
+    "video_l_fp8": Workload(
+        "video_l_fp8", 1, 40, 75600, 128, 60, "bf16", "clustered", (21, 45, 80), fp8=True, wid=3
+    ),
+}
+
+
+def workload(name: str, **kw) -> Workload:
+    return WORKLOADS[name].with_(**kw) if kw else WORKLOADS[name]
+
+
+def sweep_workloads():
+    """The sparsity sweep: keep {20,10,5,3}% x cluster scale {0.5,1,2} x alpha {0.5, random}."""
+    out = []
+    for keep in (0.20, 0.10, 0.05, 0.03):
+        for s in (0.5, 1.0, 2.0):
+            for a in ("half", "random"):
+                k = int(round(keep * 512))
+                out.append(
+                    Workload(
+                        f"sweep_k{k}_s{s:g}_{a}", 2, 12, 32768, 128, k, "bf16", "clustered",
+                        (8, 64, 64), cluster_scale=s, alpha=a, wid=4,
+                    )
+                )
+    return out
+
+
+def _rng(seed: int, *key) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *key])))
+
+
+def _cluster_ids(grid) -> tuple[np.ndarray, int]:
+    """Box id of every token of a (T, Hh, W) latent grid flattened as n = (t*Hh + h)*W + w."""
+    T, Hh, W = grid
+    t, h, w = np.meshgrid(np.arange(T), np.arange(Hh), np.arange(W), indexing="ij")
+    nt, nh, nw = (math.ceil(T / BOX[0]), math.ceil(Hh / BOX[1]), math.ceil(W / BOX[2]))
+    cid = ((t // BOX[0]) * nh + (h // BOX[1])) * nw + (w // BOX[2])
+    return cid.reshape(-1), nt * nh * nw
+
+
+def _round(x: np.ndarray, dtype: str):
+    """float32 numpy -> torch CPU tensor of the workload dtype (bf16 by torch's RNE cast)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def _head_qk(wl: Workload, seed: int, b: int, h: int):
+    """Float32 Q and K of one head before rounding."""
+    N, d = wl.N, wl.d
+    if wl.kind == "iid":
+        q = _rng(seed, wl.wid, _T_Q, b, h).standard_normal((N, d), dtype=np.float32)
+        k = _rng(seed, wl.wid, _T_K, b, h).standard_normal((N, d), dtype=np.float32)
+        return q, k
+    cid, ncl = _cluster_ids(wl.grid)
+    assert len(cid) == N, (wl.grid, N)
+    mu = _rng(seed, wl.wid, _T_CENTRE, b, h).standard_normal((ncl, d), dtype=np.float32)
+    mu *= np.float32(wl.cluster_scale)
+    sd = np.float32(math.sqrt(NOISE_VAR))
+    eq = _rng(seed, wl.wid, _T_QNOISE, b, h).standard_normal((N, d), dtype=np.float32)
+    ek = _rng(seed, wl.wid, _T_KNOISE, b, h).standard_normal((N, d), dtype=np.float32)
+    c = mu[cid]
+    return c + sd * eq, c + sd * ek
+
+
+def draw(wl: Workload, seed: int = 0) -> dict:
+    """All inputs of one workload as CPU torch tensors.
+
+    Returns {'Q','K','V': [B,H,N,d] (fp32 or bf16), 'Wq','Wk': [d,d] fp32, 'alpha': [B,H,N]
+    fp32, 'workload': wl, 'seed': seed}.
+    """
+    import torch
+
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    Q = torch.empty((B, H, N, d), dtype=tdt)
+    K = torch.empty((B, H, N, d), dtype=tdt)
+    V = torch.empty((B, H, N, d), dtype=tdt)
+    alpha = torch.empty((B, H, N), dtype=torch.float32)
+    for b in range(B):
+        for h in range(H):
+            q, k = _head_qk(wl, seed, b, h)
+            Q[b, h] = _round(q, wl.dtype)
+            K[b, h] = _round(k, wl.dtype)
+            v = _rng(seed, wl.wid, _T_V, b, h).standard_normal((N, d), dtype=np.float32)
+            V[b, h] = _round(v, wl.dtype)
+            if wl.alpha == "half":
+                alpha[b, h] = 0.5
+            else:
+                x = _rng(seed, wl.wid, _T_ALPHA, b, h).standard_normal(N)
+                alpha[b, h] = torch.from_numpy((1.0 / (1.0 + np.exp(-x))).astype(np.float32))
+    sw = 1.0 / math.sqrt(d)
+    Wq = torch.from_numpy(_rng(seed, wl.wid, _T_WQ).normal(0.0, sw, (d, d)).astype(np.float32))
+    Wk = torch.from_numpy(_rng(seed, wl.wid, _T_WK).normal(0.0, sw, (d, d)).astype(np.float32))
+    return {"Q": Q, "K": K, "V": V, "Wq": Wq, "Wk": Wk, "alpha": alpha, "workload": wl, "seed": seed}
+
+
+def redraw_query_blocks(inputs: dict, b: int, h: int, blocks, attempt: int) -> None:
+    """Redraw, in place, the query-token noise of the listed query blocks of head (b, h).
+
+    Cluster centres (and K, V, alpha) are kept; only Q rows of those blocks change, from a
+    stream keyed by (seed, workload, b, h, block, attempt).  Used to enforce the router's score
+    gap by rejection; since a row of the block-score map depends only on its own query block,
+    no other row moves.
+    """
+    wl: Workload = inputs["workload"]
+    seed = inputs["seed"]
+    N, d, blk = wl.N, wl.d, wl.block
+    Q = inputs["Q"]
+    if wl.kind == "clustered":
+        cid, ncl = _cluster_ids(wl.grid)
+        mu = _rng(seed, wl.wid, _T_CENTRE, b, h).standard_normal((ncl, d), dtype=np.float32)
+        mu *= np.float32(wl.cluster_scale)
+    sd = np.float32(math.sqrt(NOISE_VAR))
+    for i in blocks:
+        a, e = i * blk, min(i * blk + blk, N)
+        noise = _rng(seed, wl.wid, _T_REDRAW, b, h, int(i), int(attempt)).standard_normal(
+            (e - a, d), dtype=np.float32
+        )
+        if wl.kind == "clustered":
+            rows = mu[cid[a:e]] + sd * noise
+        else:
+            rows = noise
+        Q[b, h, a:e] = _round(rows, wl.dtype)

@@ -1,0 +1,388 @@
+"""Pins of the CPU oracle: checks against something other than the oracle itself.
+
+Each ``pin_*`` takes the oracle module (the real one, or a planted mutant in
+test_oracle_mutations.py) and raises AssertionError when the oracle disagrees with a library
+routine, a closed form, a hand-derived worked example under tests/golden/, dense brute force on
+a tiny input, or an invariant of the method.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _rand_idx(n_b, k, seed, rows=None):
+    rng = np.random.default_rng(seed)
+    rows = n_b if rows is None else rows
+    return np.stack([np.sort(rng.choice(n_b, size=k, replace=False)) for _ in range(rows)]).astype(np.int32)
+
+
+def _sdpa(Q, K, V, mask=None):
+    """torch's scaled_dot_product_attention on CPU in float64 (its math path)."""
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x)) for x in (Q, K, V))
+    m = None if mask is None else torch.from_numpy(mask)
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m).numpy()
+
+
+# ----------------------------------------------------------------------------------------------
+# whole-output reductions
+
+
+def pin_full_attention(orc):
+    """All blocks kept and alpha = 1: the output is full softmax attention (torch SDPA)."""
+    N, d, blk = 200, 16, 64  # 4 blocks, the last one 8 tokens
+    Q, K, V = (_rand((N, d), s) for s in (1, 2, 3))
+    n_b = -(-N // blk)
+    idx = np.tile(np.arange(n_b, dtype=np.int32), (n_b, 1))
+    O, O_s, O_l = orc.forward(Q[None, None], K[None, None], V[None, None], idx[None, None], np.ones((1, 1, N)), blk)
+    ref = _sdpa(Q, K, V)
+    np.testing.assert_allclose(O[0, 0], ref, rtol=0, atol=1e-12)
+    assert np.all(O_l == 0.0), "an empty unselected set must give a zero linear branch"
+
+
+def pin_linear_attention(orc):
+    """Nothing kept and alpha = 0: plain ReLU linear attention phi(Q)phi(K)^T V / row sums,
+    evaluated densely over all N tokens with torch."""
+    N, d, blk = 150, 8, 32
+    Q, K, V = (_rand((N, d), s) for s in (4, 5, 6))
+    n_b = -(-N // blk)
+    idx = np.zeros((n_b, 0), dtype=np.int32)
+    O, O_s, _ = orc.forward(Q[None, None], K[None, None], V[None, None], idx[None, None], np.zeros((1, 1, N)), blk)
+    q, k, v = (torch.from_numpy(x) for x in (Q, K, V))
+    w = torch.relu(q) @ torch.relu(k).T
+    den = w.sum(dim=1, keepdim=True)
+    ref = torch.where(den > 0, (w @ v) / den, torch.zeros_like(v)).numpy()
+    assert (den == 0).any() and (den > 0).sum() > N // 2  # both cases occur
+    np.testing.assert_allclose(O[0, 0], ref, rtol=1e-12, atol=1e-12)
+    assert np.all(O_s == 0.0), "no kept block must give a zero sparse branch"
+
+
+def pin_sparse_is_masked_sdpa(orc):
+    """alpha = 1 with any mask: SDPA with the token-level boolean mask expanded from M."""
+    N, d, blk, k = 176, 16, 32, 2  # 6 blocks, last one 16 tokens
+    Q, K, V = (_rand((N, d), s, 1.5) for s in (7, 8, 9))
+    n_b = -(-N // blk)
+    idx = _rand_idx(n_b, k, 10)
+    O, _, _ = orc.forward(Q[None, None], K[None, None], V[None, None], idx[None, None], np.ones((1, 1, N)), blk)
+    blk_of = np.arange(N) // blk
+    mask = np.zeros((N, N), dtype=bool)
+    for q in range(N):
+        mask[q] = np.isin(blk_of, idx[blk_of[q]])
+    np.testing.assert_allclose(O[0, 0], _sdpa(Q, K, V, mask), rtol=0, atol=1e-12)
+
+
+def pin_dense_brute_force(orc):
+    """Tiny inputs: the dense token-level P = alpha P_s + (1 - alpha) P_l, built entry by entry
+    with Python loops, is row-stochastic and O = P V."""
+    N, d, blk, k = 22, 3, 4, 2  # 6 blocks, the last one 2 tokens
+    Q, K, V = (_rand((N, d), s) for s in (11, 12, 13))
+    alpha = np.random.default_rng(14).uniform(0.05, 0.95, N)
+    n_b = -(-N // blk)
+    idx = _rand_idx(n_b, k, 15)
+    O, _, _ = orc.forward(Q[None, None], K[None, None], V[None, None], idx[None, None], alpha[None, None], blk)
+    P = np.zeros((N, N))
+    rowsum = np.zeros(N)  # alpha + (1 - alpha) when the linear denominator is positive, else alpha
+    for q in range(N):
+        kept = [n for n in range(N) if (n // blk) in set(idx[q // blk].tolist())]
+        rest = [n for n in range(N) if n not in kept]
+        logit = {n: sum(Q[q, c] * K[n, c] for c in range(d)) / math.sqrt(d) for n in kept}
+        mx = max(logit.values())
+        zs = sum(math.exp(logit[n] - mx) for n in kept)
+        lin = {n: sum(max(Q[q, c], 0.0) * max(K[n, c], 0.0) for c in range(d)) for n in rest}
+        zl = sum(lin.values())
+        for n in kept:
+            P[q, n] += alpha[q] * math.exp(logit[n] - mx) / zs
+        for n in rest:
+            P[q, n] += (1.0 - alpha[q]) * (lin[n] / zl if zl > 0 else 0.0)
+        rowsum[q] = alpha[q] + ((1.0 - alpha[q]) if zl > 0 else 0.0)
+    assert np.all(P >= 0)
+    assert np.sum(rowsum == 1.0) >= N // 2  # most rows have a positive linear denominator
+    np.testing.assert_allclose(P.sum(axis=1), rowsum, atol=1e-12)
+    np.testing.assert_allclose(O[0, 0], P @ V, rtol=0, atol=1e-12)
+    Pd, _, _ = orc.dense_P(Q, K, idx, alpha, blk)
+    np.testing.assert_allclose(Pd, P, rtol=0, atol=1e-12)
+
+
+def pin_forward_worked_example(orc):
+    """The hand-derived worked example in tests/golden/forward_worked_example.json."""
+    with open(os.path.join(GOLDEN, "forward_worked_example.json")) as f:
+        g = json.load(f)
+    a = math.sqrt(2.0) * math.log(2.0)
+
+    def val(x):
+        if x == "a":
+            return a
+        if isinstance(x, str):
+            return float(Fraction(x))
+        return float(x)
+
+    arr = lambda rows: np.array([[val(x) for x in r] for r in rows])  # noqa: E731
+    Q, K, V = arr(g["Q"]), arr(g["K"]), arr(g["V"])
+    alpha = np.array(g["alpha"], dtype=np.float64)
+    idx = np.array(g["idx"], dtype=np.int32)
+    O, O_s, O_l = orc.forward(Q[None, None], K[None, None], V[None, None], idx[None, None], alpha[None, None], g["block"])
+    np.testing.assert_allclose(O_s[0, 0], arr(g["expected_O_s"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O_l[0, 0], arr(g["expected_O_l"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O[0, 0], arr(g["expected_O"]), rtol=0, atol=1e-12)
+
+
+def pin_block_constant_closed_form(orc):
+    """Keys constant inside each block: both branches reduce to block sums of V.
+    O_s = sum_sel r_j-weighted e^{q.k_j/sqrt d} vbar_j / ..., O_l likewise with phi(q).phi(k_j)."""
+    N, d, blk, k = 45, 5, 8, 3  # 6 blocks, the last one 5 tokens
+    n_b = -(-N // blk)
+    kb = _rand((n_b, d), 21)
+    K = np.repeat(kb, blk, axis=0)[:N]
+    Q, V = _rand((N, d), 22), _rand((N, d), 23)
+    alpha = np.random.default_rng(24).uniform(0, 1, N)
+    idx = _rand_idx(n_b, k, 25)
+    O, _, _ = orc.forward(Q[None, None], K[None, None], V[None, None], idx[None, None], alpha[None, None], blk)
+    vsum = np.array([V[j * blk : (j + 1) * blk].sum(axis=0) for j in range(n_b)])
+    cnt = np.array([min(blk, N - j * blk) for j in range(n_b)], dtype=np.float64)
+    for q in range(N):
+        i = q // blk
+        sel = list(idx[i])
+        uns = [j for j in range(n_b) if j not in sel]
+        e = {j: math.exp(float(Q[q] @ kb[j]) / math.sqrt(d)) for j in sel}
+        o_s = sum(e[j] * vsum[j] for j in sel) / sum(e[j] * cnt[j] for j in sel)
+        w = {j: float(np.maximum(Q[q], 0) @ np.maximum(kb[j], 0)) for j in uns}
+        den = sum(w[j] * cnt[j] for j in uns)
+        o_l = sum(w[j] * vsum[j] for j in uns) / den if den > 0 else 0.0 * o_s
+        np.testing.assert_allclose(O[0, 0, q], alpha[q] * o_s + (1 - alpha[q]) * o_l, rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# invariants of the method
+
+
+def _small_case(seed, N=150, d=8, blk=16, k=3, B=1, H=2):
+    """Random inputs whose channel 0 of Q and K is positive, so no linear denominator is 0."""
+    rng = np.random.default_rng(seed)
+    Q, K, V = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    Q[..., 0] = np.abs(Q[..., 0]) + 0.1
+    K[..., 0] = np.abs(K[..., 0]) + 0.1
+    alpha = rng.uniform(0, 1, (B, H, N))
+    n_b = -(-N // blk)
+    idx = np.stack([np.stack([_rand_idx(n_b, k, seed + 100 * b + h) for h in range(H)]) for b in range(B)])
+    return Q, K, V, alpha, idx, blk
+
+
+def pin_convexity(orc):
+    """Every output row is a convex combination of V rows (the output stays row-normalised)."""
+    Q, K, V, alpha, idx, blk = _small_case(31)
+    O, _, _ = orc.forward(Q, K, V, idx, alpha, blk)
+    lo = V.min(axis=2, keepdims=True)
+    hi = V.max(axis=2, keepdims=True)
+    assert np.all(O >= lo - 1e-12) and np.all(O <= hi + 1e-12)
+
+
+def pin_v_affine(orc):
+    """O(a V + 1 c^T) = a O(V) + 1 c^T: both branches are row-stochastic and linear in V."""
+    Q, K, V, alpha, idx, blk = _small_case(32)
+    c = np.random.default_rng(33).standard_normal(V.shape[-1])
+    O1, _, _ = orc.forward(Q, K, V, idx, alpha, blk)
+    O2, _, _ = orc.forward(Q, K, -2.5 * V + c, idx, alpha, blk)
+    np.testing.assert_allclose(O2, -2.5 * O1 + c, rtol=0, atol=1e-11)
+
+
+def pin_within_block_permutation(orc):
+    """Permuting tokens inside blocks (Q, K, V, alpha together) leaves the mask unchanged and
+    permutes the output rows the same way."""
+    Q, K, V, alpha, idx, blk = _small_case(34)
+    rng = np.random.default_rng(35)
+    W = [rng.standard_normal((Q.shape[-1],) * 2) for _ in range(2)]
+    N = Q.shape[2]
+    perm = np.concatenate([s + rng.permutation(min(blk, N - s)) for s in range(0, N, blk)])
+    r1 = orc.route(Q, K, W[0], W[1], 3, blk)
+    r2 = orc.route(Q[:, :, perm], K[:, :, perm], W[0], W[1], 3, blk)
+    assert np.array_equal(r1["idx"], r2["idx"])
+    O1, _, _ = orc.forward(Q, K, V, r1["idx"], alpha, blk)
+    O2, _, _ = orc.forward(Q[:, :, perm], K[:, :, perm], V[:, :, perm], r1["idx"], alpha[:, :, perm], blk)
+    np.testing.assert_allclose(O2, O1[:, :, perm], rtol=0, atol=1e-12)
+
+
+def pin_alpha_isolates_branches(orc):
+    """alpha = 1 returns O_s, alpha = 0 returns O_l, and any alpha mixes them linearly."""
+    Q, K, V, alpha, idx, blk = _small_case(36)
+    O1, Os, Ol = orc.forward(Q, K, V, idx, np.ones_like(alpha), blk)
+    O0, _, _ = orc.forward(Q, K, V, idx, np.zeros_like(alpha), blk)
+    Oa, _, _ = orc.forward(Q, K, V, idx, alpha, blk)
+    np.testing.assert_array_equal(O1, Os)
+    np.testing.assert_array_equal(O0, Ol)
+    np.testing.assert_allclose(Oa, alpha[..., None] * O1 + (1 - alpha[..., None]) * O0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------------------------
+# router
+
+
+def pin_pool_is_avg_pool(orc):
+    """Block means equal torch's avg_pool1d with ceil_mode (a short last window is averaged over
+    its valid entries)."""
+    X = _rand((2, 3, 203, 5), 41)
+    ref = torch.nn.functional.avg_pool1d(
+        torch.from_numpy(X).reshape(6, 203, 5).transpose(1, 2), 64, 64, ceil_mode=True
+    ).transpose(1, 2).reshape(2, 3, 4, 5).numpy()
+    np.testing.assert_allclose(orc.pool_blocks(X, 64), ref, rtol=0, atol=1e-14)
+
+
+def pin_router_worked_example(orc):
+    """The hand-derived router example in tests/golden/router_worked_example.json."""
+    with open(os.path.join(GOLDEN, "router_worked_example.json")) as f:
+        g = json.load(f)
+    blk, d, N = g["block"], g["d"], g["N"]
+
+    def tokens(means, offs):
+        rows = []
+        for n in range(N):
+            rows.append(np.array(means[n // blk], float) + (-1) ** (n % blk) * np.array(offs, float))
+        return np.stack(rows)
+
+    Q = tokens(g["q_block_means"], g["q_token_offsets"])
+    K = tokens(g["k_block_means"], g["k_token_offsets"])
+    r = orc.route(Q, K, np.array(g["Wq"], float), np.array(g["Wk"], float), g["topk"], blk)
+    np.testing.assert_allclose(r["scores"], np.array(g["expected_scores"], float), rtol=0, atol=1e-14)
+    assert r["idx"].tolist() == g["expected_idx"]
+    np.testing.assert_allclose(r["probs"].sum(axis=-1), 1.0, atol=1e-14)
+
+
+def pin_router_matches_torch_topk(orc):
+    """On distinct scores the kept set equals torch.topk's, sorted ascending."""
+    Q, K = _rand((1, 2, 700, 16), 42), _rand((1, 2, 700, 16), 43)
+    Wq, Wk = _rand((16, 16), 44, 0.25), _rand((16, 16), 45, 0.25)
+    k = 5
+    r = orc.route(Q, K, Wq, Wk, k, 64)
+    qt = torch.nn.functional.avg_pool1d(torch.from_numpy(Q[0]).transpose(1, 2), 64, 64, ceil_mode=True).transpose(1, 2)
+    kt = torch.nn.functional.avg_pool1d(torch.from_numpy(K[0]).transpose(1, 2), 64, 64, ceil_mode=True).transpose(1, 2)
+    s = torch.matmul(qt @ torch.from_numpy(Wq), (kt @ torch.from_numpy(Wk)).transpose(1, 2)) / 4.0
+    ref = torch.sort(torch.topk(s, k, dim=-1).indices, dim=-1).values.numpy()
+    assert np.array_equal(r["idx"][0], ref)
+    np.testing.assert_allclose(r["probs"][0], torch.softmax(s, dim=-1).numpy(), atol=1e-14)
+    assert r["mask"].sum(axis=-1).max() == k and r["mask"].sum(axis=-1).min() == k
+
+
+def pin_router_invariances(orc):
+    """Positive rescaling of proj_q or proj_k, and the presence of V, do not change the mask;
+    permuting whole KV blocks permutes the kept indices."""
+    Q, K = _rand((1, 1, 512, 8), 46), _rand((1, 1, 512, 8), 47)
+    Wq, Wk = _rand((8, 8), 48), _rand((8, 8), 49)
+    k = 3
+    base = orc.route(Q, K, Wq, Wk, k, 64)["idx"]
+    assert np.array_equal(orc.route(Q, K, 3.0 * Wq, Wk, k, 64)["idx"], base)
+    assert np.array_equal(orc.route(Q, K, Wq, 0.1 * Wk, k, 64)["idx"], base)
+    perm = np.random.default_rng(50).permutation(8)  # block permutation
+    Kp = K.reshape(1, 1, 8, 64, 8)[:, :, perm].reshape(1, 1, 512, 8)
+    got = orc.route(Q, Kp, Wq, Wk, k, 64)["idx"]
+    inv = np.argsort(perm)  # block j of K sits at position inv[j] of Kp
+    assert np.array_equal(got[0, 0], np.sort(inv[base[0, 0]], axis=-1))
+
+
+def pin_router_ties_and_edges(orc):
+    """Exact ties keep the lowest block indices; k = 0 keeps nothing; k = n_b keeps all."""
+    Q = np.ones((1, 1, 300, 4))
+    K = np.ones((1, 1, 300, 4))
+    W = np.eye(4)
+    r = orc.route(Q, K, W, W, 3, 64)  # every score equal
+    assert r["idx"].tolist() == [[[[0, 1, 2]] * 5]]
+    assert orc.route(Q, K, W, W, 0, 64)["idx"].shape == (1, 1, 5, 0)
+    assert orc.route(Q, K, W, W, 5, 64)["idx"].tolist() == [[[[0, 1, 2, 3, 4]] * 5]]
+
+
+# ----------------------------------------------------------------------------------------------
+# fp8
+
+
+def _torch_e4m3_bits(x32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_decode_all_codes(orc):
+    """All 254 finite codes decode to torch's float8_e4m3fn values; 0x7F/0xFF are NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.e4m3_decode(codes)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), ~fin)
+    assert np.array_equal(got[fin], ref[fin])
+    assert orc.e4m3_decode(np.uint8(0x7E)) == 448.0 and orc.e4m3_decode(np.uint8(0x01)) == 2.0 ** -9
+
+
+def pin_e4m3_encode_exhaustive_bf16(orc):
+    """Every bf16 value with |x| < 464 (torch turns larger ones into NaN, the codec saturates)
+    encodes to torch's round-to-nearest-even float8_e4m3fn bits."""
+    bits = np.arange(65536, dtype=np.uint32) << 16
+    x = bits.view(np.float32)
+    ok = np.isfinite(x) & (np.abs(x) < 464.0)
+    x = x[ok]
+    assert np.array_equal(orc.e4m3_encode(x), _torch_e4m3_bits(x))
+
+
+def pin_e4m3_encode_fp32_ties_and_saturation(orc):
+    """Random fp32 values, exact ties between neighbouring codes, and saturation above 448."""
+    rng = np.random.default_rng(51)
+    x = (rng.standard_normal(200_000) * np.exp2(rng.integers(-12, 9, 200_000))).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    assert np.array_equal(orc.e4m3_encode(x), _torch_e4m3_bits(x))
+    codes = np.arange(0x7E, dtype=np.uint8)
+    v = orc.e4m3_decode(codes)
+    mid = ((v[:-1] + v[1:]) / 2).astype(np.float32)  # exact midpoints: ties go to the even code
+    assert np.array_equal(orc.e4m3_encode(mid), _torch_e4m3_bits(mid))
+    assert np.all(orc.e4m3_encode(np.array([448.0, 470.0, 1e6, -1e30])) == np.array([0x7E, 0x7E, 0x7E, 0xFE]))
+    assert orc.e4m3_encode(np.array([-0.0]))[0] == 0x80
+
+
+def pin_quantize_blocks(orc):
+    """Per-block absmax codes equal torch's e4m3 cast of fp32(x * fp32(448 / absmax)); a zero
+    block keeps scale 1 and codes 0; the largest magnitude maps to 448."""
+    X = (_rand((150, 16), 52) * 3).astype(np.float32).astype(np.float64)
+    X[64:128] = 0.0
+    codes, scales, deq = orc.quantize_blocks(X, 64)
+    for t, (a, b) in enumerate([(0, 64), (64, 128), (128, 150)]):
+        xb = X[a:b].astype(np.float32)
+        amax = np.abs(xb).max()
+        if amax == 0:
+            assert scales[t] == 1.0 and np.all(codes[a:b] == 0)
+            continue
+        inv = np.float32(448.0) / np.float32(amax)
+        assert scales[t] == np.float32(np.float32(amax) / np.float32(448.0))
+        assert np.array_equal(codes[a:b], _torch_e4m3_bits(xb * inv))
+        assert np.abs(deq[a:b]).max() == np.float64(scales[t]) * 448.0
+    np.testing.assert_allclose(deq, X, rtol=0.0625, atol=np.abs(X).max() * 2.0 ** -9)
+
+
+def pin_fp8_identity_codec(orc):
+    """With the e4m3 codec replaced by the identity, the fp8 forward equals the unquantised one
+    up to the fp32 rounding of the scales."""
+    Q, K, V, alpha, idx, blk = _small_case(53, N=200, d=16, blk=64, k=2)
+    O, Os, Ol = orc.forward(Q, K, V, idx, alpha, blk)
+    O8, Os8, Ol8 = orc.forward_fp8(Q, K, V, idx, alpha, blk, codec=lambda y: np.asarray(y, np.float64))
+    np.testing.assert_array_equal(Ol8, Ol)
+    np.testing.assert_allclose(Os8, Os, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(O8, O, rtol=1e-5, atol=1e-6)
+
+
+def pin_fp8_error_scale(orc):
+    """With the real codec the fp8 sparse branch differs from the exact one by the size e4m3
+    rounding predicts (three mantissa bits: a few per cent on unconcentrated iid data), and the
+    linear branch is untouched."""
+    Q, K, V, alpha, idx, blk = _small_case(54, N=256, d=32, blk=64, k=2)
+    _, Os, Ol = orc.forward(Q, K, V, idx, alpha, blk)
+    _, Os8, Ol8 = orc.forward_fp8(Q, K, V, idx, alpha, blk)
+    np.testing.assert_array_equal(Ol8, Ol)
+    rel = np.linalg.norm(Os8 - Os) / np.linalg.norm(Os)
+    assert 5e-3 < rel < 0.1, rel
+
+
+ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

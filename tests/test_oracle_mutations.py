@@ -1,0 +1,63 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin (CPU only).
+
+Each mutation edits one line of the oracle's source in a temporary copy of the package (the
+real oracle is never touched), imports the copy, and runs every pin against it.
+"""
+
+import importlib.util
+import os
+import shutil
+import sys
+import uuid
+
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+MUTATIONS = {
+    "no_sparse_scale": ("sla.py", "scale = 1.0 / np.sqrt(d)\n    outs", "scale = 1.0\n    outs"),
+    "no_router_scale": ("sla.py", "return (qt @ np.swapaxes(kt, -1, -2)) / np.sqrt(d)", "return qt @ np.swapaxes(kt, -1, -2)"),
+    "transposed_proj_q": ("sla.py", "qt = pool_blocks(Q, block) @ Wq", "qt = pool_blocks(Q, block) @ Wq.T"),
+    "pool_divides_by_block": ("sla.py", "/ float(b - a)", "/ float(block)"),
+    "no_relu_on_q": ("sla.py", "pq = np.maximum(q, 0.0)", "pq = q"),
+    "no_relu_on_k": ("sla.py", "pk = np.maximum(K[a:b], 0.0)", "pk = np.abs(K[a:b])"),
+    "alpha_swapped": ("sla.py", "outs.append(al * o_s + (1.0 - al) * o_l)", "outs.append(al * o_l + (1.0 - al) * o_s)"),
+    "linear_over_kept": ("sla.py", "unsel = (~keep).astype(np.float64)", "unsel = np.ones(n_b)"),
+    "ties_to_higher_index": ("sla.py", 'order = np.argsort(-s, axis=-1, kind="stable")[..., :k]', 'order = np.argsort(s, axis=-1, kind="stable")[..., ::-1][..., :k]'),
+    "unsorted_indices": ("sla.py", "idx = np.sort(order, axis=-1).astype(np.int32)", "idx = order.astype(np.int32)"),
+    "sparse_norm_wrong_axis": ("sla.py", "o_s = (p @ V[tok]) / p.sum(axis=1, keepdims=True)", "o_s = (p @ V[tok]) / p.sum()"),
+    "no_zero_denominator_guard": ("sla.py", "o_l[nz] = num[nz] / den[nz, None]", "o_l = num / den[:, None]"),
+    "fp8_scale_dropped": ("fp8.py", "deq[a:b] = e4m3_decode(codes[a:b]) * np.float64(scales[t])", "deq[a:b] = e4m3_decode(codes[a:b])"),
+    "fp8_truncating_round": ("fp8.py", "m8 = np.rint((mant * 2.0 - 1.0) * 8.0)", "m8 = np.floor((mant * 2.0 - 1.0) * 8.0)"),
+    "fp8_bias_off_by_one": ("fp8.py", "_E4M3_BIAS = 7", "_E4M3_BIAS = 8"),
+    "fp8_tile_scale_dropped": ("fp8.py", "num += (enc(p / sP) * sP) @ Vd[starts[j]:ends[j]]", "num += enc(p / sP) @ Vd[starts[j]:ends[j]]"),
+}
+
+
+def _load_mutant(tmp_path, fname, old, new):
+    name = f"oracle_mutant_{uuid.uuid4().hex[:8]}"
+    dst = tmp_path / name
+    shutil.copytree(ORACLE_DIR, dst, ignore=shutil.ignore_patterns("__pycache__"))
+    path = dst / fname
+    src = path.read_text()
+    assert src.count(old) == 1, f"mutation anchor not unique in {fname}: {old!r}"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(name, dst / "__init__.py", submodule_search_locations=[str(dst)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[name] = mod
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_mutation_is_caught(tmp_path, mutation):
+    mod = _load_mutant(tmp_path, *MUTATIONS[mutation])
+    caught = []
+    for name, pin in ALL_PINS.items():
+        try:
+            pin(mod)
+        except Exception:  # an AssertionError, or the mutant crashing on a pin's input
+            caught.append(name)
+    assert caught, f"no pin catches the planted mistake '{mutation}'"
