@@ -1,0 +1,242 @@
+"""Benchmark of the SLA2 sparse-linear attention inference forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video_s]
+
+One step = sla.route + sla.forward (router, linear-branch states, block-sparse flash kernel with
+the fused linear removal and alpha combine) over one batch of synthetic inputs already resident
+in HBM.  Prints ONE JSON line: value = effective TFLOP/s (sparse FLOPs 4 d sum_i r_i sum_{j in
+sel(i)} c_j of the step's actual index lists, divided by the step time), ms_per_step, the
+dominant kernel's roofline (its algorithmic FLOPs per launch over its event-timed duration) and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video_s", help="video_s | video_l | video_l_fp8")
+    ap.add_argument("--linear-mode", default="fused", choices=["fused", "literal"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def sparse_flops(idx, N, d, block=64):
+    """4 d sum over (b, h, query block i, kept j) of r_i * c_j (QK^T and PV, exp not counted)."""
+    import torch
+
+    nb = idx.shape[2]
+    r = torch.full((nb,), block, dtype=torch.float64, device=idx.device)
+    r[-1] = N - block * (nb - 1)
+    cj = r[idx.long()].sum(dim=-1)            # [B, H, nb]: kept keys per query block
+    return float(4.0 * d * (cj * r).sum().item())
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+SPARSE_SOURCES = [
+    "block_sparse_linear_02_amd/csrc/sparse.hip",
+    "block_sparse_linear_02_amd/csrc/sla_tiles.hpp",
+    "block_sparse_linear_02_amd/csrc/sla_device.hpp",
+]
+
+
+def traffic_for(kernel_key, digest):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this exact
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(kernel_key)
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(inputs, wl, idx_gpu, budget_s=20.0):
+    """The oracle as it stands on a bounded sample: one head's router, then query blocks of that
+    head's forward until about `budget_s` of CPU time; scaled to the whole workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+
+    Q, K, V = inputs["Q"][0, 0], inputs["K"][0, 0], inputs["V"][0, 0]
+    t0 = time.perf_counter()
+    r = oracle.route(Q[None, None], K[None, None], inputs["Wq"].double(), inputs["Wk"].double(), wl.topk, 64)
+    t_route = time.perf_counter() - t0
+    idx = r["idx"][0, 0]
+    t0 = time.perf_counter()
+    states = oracle.block_states(K, V, 64)
+    t_states = time.perf_counter() - t0
+    nb = wl.n_blocks
+    done, t_fwd = 0, 0.0
+    rng = np.random.default_rng(0)
+    order = rng.permutation(nb)
+    while t_fwd < budget_s and done < nb:
+        blocks = order[done : done + 8]
+        t0 = time.perf_counter()
+        if wl.fp8:
+            oracle.forward_fp8_head(Q, K, V, idx, inputs["alpha"][0, 0], 64, q_blocks=blocks, states=states)
+        else:
+            oracle.forward_head(Q, K, V, idx, inputs["alpha"][0, 0], 64, q_blocks=blocks, states=states)
+        t_fwd += time.perf_counter() - t0
+        done += len(blocks)
+    heads = wl.B * wl.H
+    per_call = heads * (t_route + t_states + t_fwd * nb / done)
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    return {
+        "seconds_per_call": per_call,
+        "sample": f"1 of {heads} heads: router + block states + {done} of {nb} query blocks "
+                  f"({t_route + t_states + t_fwd:.1f} s), scaled by heads and query blocks",
+        "cores": int(threads),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards over (batch, head) with no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(1)
+
+    import torch
+
+    import block_sparse_linear_02_amd as sla
+    import gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    sla.lib()
+
+    if a.copy_calib:
+        n = a.copy_calib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n}))
+        return
+
+    wl = gen.workload(a.workload)
+    inputs = gen.draw(wl, 0)
+    Q, K, V, alpha = (inputs[k].to(dev) for k in ("Q", "K", "V", "alpha"))
+    Wq, Wk = inputs["Wq"].to(dev), inputs["Wk"].to(dev)
+    B, H, N, d = Q.shape
+    nb = wl.n_blocks
+    fp8 = wl.fp8
+    idx = torch.empty((B, H, nb, wl.topk), dtype=torch.int32, device=dev)
+    ws_r = torch.empty(sla.route_workspace_bytes(Q, wl.topk), dtype=torch.uint8, device=dev)
+    variant = 1 if fp8 else (2 if a.linear_mode == "literal" else 0)
+    ws_f = torch.empty(sla.forward_workspace_bytes(Q, wl.topk, variant), dtype=torch.uint8, device=dev)
+    O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    ev_r = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e in ev + ev_r:
+        e[0].record()
+        e[1].record()
+    torch.cuda.synchronize()
+
+    def step(i=None):
+        if i is not None:
+            ev_r[i][0].record()
+        sla.route(Q, K, Wq, Wk, wl.topk, workspace=ws_r, idx_out=idx)
+        if i is not None:
+            ev_r[i][1].record()
+        sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O,
+                    events=ev[i] if i is not None else None)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = 1e3 * elapsed / a.steps
+    flops = sparse_flops(idx, N, d)
+    sparse_ms = sum(b.elapsed_time(e) for b, e in ev) / a.steps
+    route_ms = sum(b.elapsed_time(e) for b, e in ev_r) / a.steps
+    # algorithmic work of the sparse kernel per launch: the sparse branch (QK^T + PV) and, with
+    # the fused linear removal, the same again (relu(Q) relu(K_j)^T and its product with V_j)
+    k_flops = flops * (2.0 if a.linear_mode == "fused" else 1.0)
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    achieved = k_flops / (sparse_ms * 1e-3) / 1e12
+    digest = source_digest(SPARSE_SOURCES if not fp8 else ["block_sparse_linear_02_amd/csrc/fp8.hip"])
+    kernel_key = ("sparse_fp8_kernel" if fp8 else "sparse_kernel") + f"@{a.workload}"
+    rec = {
+        "metric": "sparse-linear attn fwd ms/call + effective TFLOPS, N=32768 H=12 d=128 90% sparse",
+        "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective: sparse FLOPs / call time)",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 sparse branch, bf16 linear" if fp8 else "bf16",
+        "data": "synthetic (seeded clustered video-DiT-shaped tensors, random projections)",
+        "config": {
+            "workload": f"{a.workload}: B={B} H={H} N={N} d={d} block=64 topk={wl.topk} of {nb} "
+                        f"({100 * (1 - wl.topk / nb):.1f}% block sparsity), linear={a.linear_mode}",
+            "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": wl.topk,
+        },
+        "sparse_tflop_per_call": flops / 1e12,
+        "kernels_ms": {"route": route_ms, "sparse": sparse_ms, "states_and_other": ms - route_ms - sparse_ms},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": kernel_key.split("@")[0],
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": traffic_for(kernel_key, digest),
+            "flops_per_launch": k_flops,
+        },
+    }
+    if not a.no_cpu_baseline:
+        cb = cpu_baseline(inputs, wl, idx)
+        rec["cpu_baseline"] = {
+            "value": flops / cb["seconds_per_call"] / 1e12,
+            "unit": "TFLOP/s (effective, same FLOP count)",
+            "ms_per_call": 1e3 * cb["seconds_per_call"],
+            "cores": cb["cores"],
+            "kind": "oracle",
+            "sample": cb["sample"],
+        }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

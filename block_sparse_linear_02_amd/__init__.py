@@ -1,0 +1,206 @@
+"""Python binding of libsla, the MI355X (gfx950) SLA2 sparse-linear attention forward.
+
+Argument marshalling only: every step of the forward runs in the HIP kernels of libsla.so
+(C ABI in include/sla.h).  torch supplies device memory (tensors, workspaces) and the HIP
+stream (torch.cuda.current_stream()).  There is no CPU fallback: without the built library or
+a GPU every call raises.
+
+    idx, mask, scores = route(Q, K, proj_q, proj_k, topk, want_mask=False, want_scores=False)
+    O = forward(Q, K, V, idx, alpha)                     # bf16 (or fp32-input) sparse branch
+    O = forward(Q, K, V, idx, alpha, fp8=True)           # e4m3 sparse branch
+    O = forward(Q, K, V, idx, alpha, linear_mode="literal")
+
+Shapes: Q, K, V [B, H, N, d] (bf16 or fp32, d in {64, 128}), proj_q / proj_k [d, d] fp32,
+alpha [B, H, N] fp32, idx [B, H, ceil(N/64), topk] int32 ascending, O [B, H, N, d] fp32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SLAError",
+    "lib",
+    "lib_path",
+    "route",
+    "forward",
+    "quantize_e4m3",
+    "route_workspace_bytes",
+    "forward_workspace_bytes",
+    "BLOCK",
+]
+
+BLOCK = 64
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsla.so")
+_LIB = None
+
+SLA_OK, SLA_ERR_INVALID, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_HIP = 0, -1, -2, -3, -4
+SLA_F32, SLA_BF16 = 0, 1
+LINEAR_MODES = {"fused": 0, "literal": 1}
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "H", "N", "d", "block", "topk", "dtype")]
+
+
+class ForwardOpts(ctypes.Structure):
+    _fields_ = [
+        ("linear_mode", ctypes.c_int32),
+        ("sparse_begin", ctypes.c_void_p),
+        ("sparse_end", ctypes.c_void_p),
+    ]
+
+
+class SLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib().sla_status_string(status).decode()
+        if status == SLA_ERR_HIP:
+            msg += f" (hipError {lib().sla_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsla.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m block_sparse_linear_02_amd.build`"
+            )
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.sla_route_workspace_bytes.argtypes = [P]
+        L.sla_route_workspace_bytes.restype = sz
+        L.sla_forward_workspace_bytes.argtypes = [P, i32]
+        L.sla_forward_workspace_bytes.restype = sz
+        L.sla_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sla_route.restype = i32
+        fwd = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in ("sla_forward", "sla_forward_fp8"):
+            getattr(L, name).argtypes = fwd
+            getattr(L, name).restype = i32
+        for name in ("sla_forward_ex", "sla_forward_fp8_ex"):
+            getattr(L, name).argtypes = fwd + [ctypes.POINTER(ForwardOpts)]
+            getattr(L, name).restype = i32
+        L.sla_quantize_e4m3.argtypes = [P, vp, vp, vp, vp]
+        L.sla_quantize_e4m3.restype = i32
+        L.sla_status_string.argtypes = [i32]
+        L.sla_status_string.restype = ctypes.c_char_p
+        L.sla_last_hip_error.argtypes = []
+        L.sla_last_hip_error.restype = i32
+        _LIB = L
+    return _LIB
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_qkv(*ts):
+    B, H, N, d = ts[0].shape
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError("inputs must be GPU tensors")
+        if t.shape != (B, H, N, d) or t.dtype != ts[0].dtype:
+            raise ValueError("Q, K, V must share shape [B, H, N, d] and dtype")
+    if ts[0].dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("Q, K, V must be bf16 or fp32")
+
+
+def make_problem(B, H, N, d, topk, dtype) -> Problem:
+    dt = SLA_BF16 if dtype == torch.bfloat16 else SLA_F32
+    return Problem(B, H, N, d, BLOCK, topk, dt)
+
+
+def _problem(Q, topk) -> Problem:
+    B, H, N, d = Q.shape
+    return make_problem(B, H, N, d, topk, Q.dtype)
+
+
+def route_workspace_bytes(Q, topk: int) -> int:
+    return lib().sla_route_workspace_bytes(ctypes.byref(_problem(Q, topk)))
+
+
+def forward_workspace_bytes(Q, topk: int, variant: int = 0) -> int:
+    return lib().sla_forward_workspace_bytes(ctypes.byref(_problem(Q, topk)), variant)
+
+
+def route(Q, K, proj_q, proj_k, topk: int, want_mask: bool = False, want_scores: bool = False,
+          workspace=None, idx_out=None):
+    """Router: block mean-pool, projection, block scores, HardTop-k.  Returns (idx, mask,
+    scores); mask / scores are None unless requested."""
+    _check_qkv(Q, K)
+    Q, K = Q.contiguous(), K.contiguous()
+    proj_q = proj_q.contiguous().to(torch.float32)
+    proj_k = proj_k.contiguous().to(torch.float32)
+    B, H, N, d = Q.shape
+    nb = -(-N // BLOCK)
+    p = _problem(Q, topk)
+    dev = Q.device
+    idx = idx_out if idx_out is not None else torch.empty((B, H, nb, topk), dtype=torch.int32, device=dev)
+    mask = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev) if want_mask else None
+    scores = torch.empty((B, H, nb, nb), dtype=torch.float32, device=dev) if want_scores else None
+    need = lib().sla_route_workspace_bytes(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().sla_route(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(proj_q), _ptr(proj_k), _ptr(idx),
+                         _ptr(mask), _ptr(scores), _ptr(ws), ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_route")
+    return idx, mask, scores
+
+
+def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", workspace=None,
+            out=None, events=None):
+    """O = alpha * O_s + (1 - alpha) * O_l.  `events` = (begin, end) torch.cuda.Event pair
+    recorded around the sparse kernel (both must already exist, e.g. recorded once)."""
+    _check_qkv(Q, K, V)
+    Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
+    B, H, N, d = Q.shape
+    topk = idx.shape[-1]
+    idx = idx.contiguous().to(torch.int32)
+    alpha = alpha.contiguous().to(torch.float32)
+    p = _problem(Q, topk)
+    mode = LINEAR_MODES[linear_mode]
+    variant = 1 if fp8 else (2 if mode == 1 else 0)
+    need = lib().sla_forward_workspace_bytes(ctypes.byref(p), variant)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    O = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device)
+    opts = ForwardOpts(mode, None, None)
+    if events is not None:
+        opts.sparse_begin = ctypes.c_void_p(events[0].cuda_event)
+        opts.sparse_end = ctypes.c_void_p(events[1].cuda_event)
+    fn = lib().sla_forward_fp8_ex if fp8 else lib().sla_forward_ex
+    st = fn(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(alpha), _ptr(O), _ptr(ws),
+            ws.numel(), _stream(), ctypes.byref(opts))
+    if st != SLA_OK:
+        raise SLAError(st, "sla_forward_fp8" if fp8 else "sla_forward")
+    return O
+
+
+def quantize_e4m3(X):
+    """Per-(b, h, 64-token block) absmax e4m3 codes of X (bf16, d = 128) and their scales."""
+    _check_qkv(X)
+    X = X.contiguous()
+    B, H, N, d = X.shape
+    nb = -(-N // BLOCK)
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=X.device)
+    scales = torch.empty((B, H, nb), dtype=torch.float32, device=X.device)
+    p = _problem(X, 0)
+    st = lib().sla_quantize_e4m3(ctypes.byref(p), _ptr(X), _ptr(codes), _ptr(scales), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_quantize_e4m3")
+    return codes, scales

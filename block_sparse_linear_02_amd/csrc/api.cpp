@@ -1,0 +1,241 @@
+// api.cpp - the C ABI of libsla (declared in include/sla.h): argument checks, workspace
+// carving and the launch sequence on the caller's stream.
+#include "sla.h"
+
+#include <climits>
+#include <cstdint>
+
+#include "sla_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over the caller's workspace (sizes only when base == nullptr).
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+// Host-side checks shared by every entry point; fills dims on success.
+int check_problem(const sla_problem* p, sla::Dims* dims) {
+  if (!p) return SLA_ERR_INVALID;
+  if (p->B < 1 || p->H < 1 || p->N < 1 || p->d < 1 || p->block < 1) return SLA_ERR_INVALID;
+  const int64_t nb = ((int64_t)p->N + p->block - 1) / p->block;
+  if (p->topk < 0 || p->topk > nb) return SLA_ERR_INVALID;
+  const int64_t elems = (int64_t)p->B * p->H;
+  if (elems > (int64_t)INT_MAX / nb) return SLA_ERR_INVALID;  // (b, h, block) ids fit an int
+  if ((__int128)elems * p->N * p->d > ((__int128)1 << 62)) return SLA_ERR_INVALID;
+  if (p->dtype != SLA_F32 && p->dtype != SLA_BF16) return SLA_ERR_UNSUPPORTED;
+  if (p->block != 64) return SLA_ERR_UNSUPPORTED;
+  if (p->d != 64 && p->d != 128) return SLA_ERR_UNSUPPORTED;
+  if (nb > sla::route_max_blocks()) return SLA_ERR_UNSUPPORTED;
+  dims->B = p->B;
+  dims->H = p->H;
+  dims->N = p->N;
+  dims->d = p->d;
+  dims->nb = (int)nb;
+  dims->topk = p->topk;
+  dims->dtype = p->dtype == SLA_BF16 ? sla::kBF16 : sla::kF32;
+  return SLA_OK;
+}
+
+struct RouteWs {
+  __bf16 *q_hi, *q_lo, *k_hi, *k_lo;
+};
+size_t carve_route(const sla::Dims& d, void* ws, RouteWs* out) {
+  Carve c(ws);
+  const size_t n = (size_t)d.B * d.H * d.nb * d.d;
+  RouteWs r;
+  r.q_hi = c.take<__bf16>(n);
+  r.q_lo = c.take<__bf16>(n);
+  r.k_hi = c.take<__bf16>(n);
+  r.k_lo = c.take<__bf16>(n);
+  if (out) *out = r;
+  return c.off;
+}
+
+struct FwdWs {
+  float *zb, *h_part, *z_part, *Z, *hj, *h_full;
+  __bf16 *ht_hi, *ht_lo;
+  uint8_t *q8, *k8, *v8;
+  float *sq, *sk, *sv;
+};
+// variant: 0 fused, 1 fp8 (fused), 2 literal
+size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
+  Carve c(ws);
+  const size_t BH = (size_t)d.B * d.H;
+  const size_t dd = (size_t)d.d * d.d;
+  const int cb = sla::state_chunk_blocks(d);
+  const size_t nchunk = (d.nb + cb - 1) / cb;
+  FwdWs f = {};
+  f.zb = c.take<float>(BH * d.nb * d.d);
+  f.h_part = c.take<float>(BH * nchunk * dd);
+  f.z_part = c.take<float>(BH * nchunk * d.d);
+  f.Z = c.take<float>(BH * d.d);
+  f.ht_hi = c.take<__bf16>(BH * dd);
+  f.ht_lo = c.take<__bf16>(BH * dd);
+  if (variant == 2) {
+    f.hj = c.take<float>(BH * d.nb * dd);
+    f.h_full = c.take<float>(BH * dd);
+  }
+  if (variant == 1) {
+    const size_t n = BH * d.N * d.d;
+    f.q8 = c.take<uint8_t>(n);
+    f.k8 = c.take<uint8_t>(n);
+    f.v8 = c.take<uint8_t>(BH * d.nb * 64 * d.d);  // per-block transposed, padded to 64 keys
+    f.sq = c.take<float>(BH * d.nb);
+    f.sk = c.take<float>(BH * d.nb);
+    f.sv = c.take<float>(BH * d.nb);
+  }
+  if (out) *out = f;
+  return c.off;
+}
+
+inline int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return SLA_ERR_HIP;
+}
+
+int forward_impl(const sla_problem* p, const void* Q, const void* K, const void* V,
+                 const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                 hipStream_t stream, const sla_forward_opts* opts, bool fp8) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  const int mode = opts ? opts->linear_mode : SLA_LINEAR_FUSED;
+  if (mode != SLA_LINEAR_FUSED && mode != SLA_LINEAR_LITERAL) return SLA_ERR_INVALID;
+  if (fp8 && mode != SLA_LINEAR_FUSED) return SLA_ERR_INVALID;
+  if (fp8 && (d.dtype != sla::kBF16 || d.d != 128)) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !alpha || !O || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
+  const int variant = fp8 ? 1 : (mode == SLA_LINEAR_LITERAL ? 2 : 0);
+  const size_t need = carve_forward(d, variant, nullptr, nullptr);
+  if (!ws) return SLA_ERR_INVALID;
+  if (ws_bytes < need) return SLA_ERR_WORKSPACE;
+  FwdWs w;
+  carve_forward(d, variant, ws, &w);
+
+  hipError_t e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  e = sla::launch_state_reduce(d, w.h_part, w.z_part, w.ht_hi, w.ht_lo, w.Z, w.h_full, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (fp8) {
+    e = sla::launch_quantize(d, Q, w.q8, w.sq, stream);
+    if (e == hipSuccess) e = sla::launch_quantize(d, K, w.k8, w.sk, stream);
+    if (e == hipSuccess) e = sla::launch_quantize_v8t(d, V, w.v8, w.sv, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (opts && opts->sparse_begin) {
+    e = hipEventRecord(opts->sparse_begin, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (fp8)
+    e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
+                               w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
+  else
+    e = sla::launch_sparse(d, Q, K, V, idx, alpha, w.ht_hi, w.ht_lo, w.Z, w.zb, O,
+                           mode == SLA_LINEAR_FUSED ? 1 : 0, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (opts && opts->sparse_end) {
+    e = hipEventRecord(opts->sparse_end, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (mode == SLA_LINEAR_LITERAL) {
+    e = sla::launch_linear_literal(d, Q, idx, alpha, w.h_full, w.Z, w.hj, w.zb, O, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return SLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sla_route_workspace_bytes(const sla_problem* p) {
+  sla::Dims d;
+  if (check_problem(p, &d) != SLA_OK) return 0;
+  return carve_route(d, nullptr, nullptr);
+}
+
+size_t sla_forward_workspace_bytes(const sla_problem* p, int variant) {
+  sla::Dims d;
+  if (check_problem(p, &d) != SLA_OK || variant < 0 || variant > 2) return 0;
+  return carve_forward(d, variant, nullptr, nullptr);
+}
+
+int sla_route(const sla_problem* p, const void* Q, const void* K, const float* proj_q,
+              const float* proj_k, int32_t* idx, uint8_t* mask, float* scores, void* ws,
+              size_t ws_bytes, hipStream_t stream) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !K || !proj_q || !proj_k || (d.topk > 0 && !idx) || !ws) return SLA_ERR_INVALID;
+  if (ws_bytes < carve_route(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  RouteWs w;
+  carve_route(d, ws, &w);
+  hipError_t e = sla::launch_route(d, Q, K, proj_q, proj_k, w.q_hi, w.q_lo, w.k_hi, w.k_lo, idx,
+                                   mask, scores, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+int sla_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, nullptr, false);
+}
+
+int sla_forward_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
+                   const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                   hipStream_t stream, const sla_forward_opts* opts) {
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, opts, false);
+}
+
+int sla_forward_fp8(const sla_problem* p, const void* Q, const void* K, const void* V,
+                    const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, nullptr, true);
+}
+
+int sla_forward_fp8_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
+                       const int32_t* idx, const float* alpha, float* O, void* ws,
+                       size_t ws_bytes, hipStream_t stream, const sla_forward_opts* opts) {
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, opts, true);
+}
+
+int sla_quantize_e4m3(const sla_problem* p, const void* X, uint8_t* codes, float* scales,
+                      hipStream_t stream) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (d.dtype != sla::kBF16 || d.d != 128) return SLA_ERR_UNSUPPORTED;
+  if (!X || !codes || !scales) return SLA_ERR_INVALID;
+  hipError_t e = sla::launch_quantize(d, X, codes, scales, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+const char* sla_status_string(int status) {
+  switch (status) {
+    case SLA_OK: return "ok";
+    case SLA_ERR_INVALID: return "invalid argument";
+    case SLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SLA_ERR_WORKSPACE: return "workspace too small";
+    case SLA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int sla_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+// linear_state.hip - per-key-block states of the ReLU linear branch on gfx950.
+//
+// The linear branch ("SALAD: Achieve High-Sparsity Attention via Efficient Linear Attention
+// Tuning for Video Diffusion Transformer", section 2: ReLU kernel function; SLA2 Italian summary
+// section 1: it covers what the sparse branch leaves out) needs, per key block j,
+//   h_j = relu(K_j)^T V_j  [d x d]   and   z_j = relu(K_j)^T 1  [d],
+// and their totals H = sum_j h_j, Z = sum_j z_j per (batch, head).
+//
+//   state_kernel   one workgroup per (chunk of key blocks, head).  Each 64-token tile of K and
+//                  V is streamed from HBM with 16-byte coalesced loads (the next tile's loads
+//                  are in flight while the current one is used) into row-major LDS tiles; the
+//                  4 wavefronts read them back transposed (ds_read_b64_tr_b16) as MFMA operands
+//                  and accumulate H^T = V^T relu(K) (bf16 MFMA, fp32 accumulation) for the
+//                  chunk, z_j by fp32 sums.  Literal mode also stores every h_j.
+//   reduce_kernel  sums the chunk partials in a fixed order (deterministic), splits H^T into
+//                  bf16 hi + lo parts (the sparse kernel's MFMA operand) and writes Z.
+#include "sla_device.hpp"
+#include "sla_launch.hpp"
+#include "sla_tiles.hpp"
+
+namespace sla {
+
+namespace {
+
+constexpr int kStateThreads = 256;
+
+template <class T, int D, bool LITERAL>
+__global__ __launch_bounds__(kStateThreads) void state_kernel(
+    const T* __restrict__ K, const T* __restrict__ V, int N, int nb, int cb,
+    float* __restrict__ zb, float* __restrict__ h_part, float* __restrict__ z_part,
+    float* __restrict__ hj) {
+  constexpr int NT = D / 64;  // 32x32 output tiles per wave per dimension (D=128: 2, D=64: 1)
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBlock * (D + kPad)];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[kBlock * (D + kPad)];
+  __shared__ float zred[kStateThreads / D][D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int nchunk = gridDim.x;
+  const int j0 = chunk * cb;
+  const int j1 = min(nb, j0 + cb);
+  const T* Kb = K + (size_t)bh * N * D;
+  const T* Vb = V + (size_t)bh * N * D;
+
+  // wave -> (rows c of H^T = V channels, cols c' = K channels)
+  const int r0 = (wave / 2) * 32 * NT;
+  const int c0 = (wave % 2) * 32 * NT;
+
+  f32x16 acc[NT][NT];
+  f32x16 tot[LITERAL ? NT : 1][LITERAL ? NT : 1];
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = f32x16{};
+  if constexpr (LITERAL) {
+#pragma unroll
+    for (int a = 0; a < NT; ++a)
+#pragma unroll
+      for (int b = 0; b < NT; ++b) tot[a][b] = f32x16{};
+  }
+  float zsum = 0.f;  // thread tid < D: running chunk z for channel tid
+
+  TileLoader<T, D, kStateThreads> lk, lv;
+  lk.load(Kb + (size_t)j0 * kBlock * D, min(kBlock, N - j0 * kBlock), tid);
+  lv.load(Vb + (size_t)j0 * kBlock * D, min(kBlock, N - j0 * kBlock), tid);
+
+  for (int j = j0; j < j1; ++j) {
+    __syncthreads();  // previous tile fully consumed
+    lk.store(Ks, tid);
+    lv.store(Vs, tid);
+    __syncthreads();
+    if (j + 1 < j1) {
+      const int nv = min(kBlock, N - (j + 1) * kBlock);
+      lk.load(Kb + (size_t)(j + 1) * kBlock * D, nv, tid);
+      lv.load(Vb + (size_t)(j + 1) * kBlock * D, nv, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kBlock / 16; ++ks) {
+      bf16x8 av[NT], bk[NT];
+#pragma unroll
+      for (int a = 0; a < NT; ++a) av[a] = tr_operand<D, 8, 4>(Vs, 16 * ks, r0 + 32 * a, lane);
+#pragma unroll
+      for (int b = 0; b < NT; ++b) bk[b] = relu8(tr_operand<D, 8, 4>(Ks, 16 * ks, c0 + 32 * b, lane));
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int b = 0; b < NT; ++b) acc[a][b] = mfma32(av[a], bk[b], acc[a][b]);
+    }
+    // z_j = sum over the tile's rows of relu(K)
+    {
+      constexpr int PARTS = kStateThreads / D;
+      const int c = tid % D, part = tid / D;
+      float s = 0.f;
+#pragma unroll 8
+      for (int n = part * (kBlock / PARTS); n < (part + 1) * (kBlock / PARTS); ++n)
+        s += fmaxf(bf2f(Ks[n * (D + kPad) + c]), 0.f);
+      zred[part][c] = s;
+    }
+    if constexpr (LITERAL) {
+      // store h_j in natural layout h_j[c'][c]; lane holds c' = col, c = rows 8(i/4)+4g+i%4
+      float* dst = hj + ((size_t)bh * nb + j) * D * D;
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int b = 0; b < NT; ++b) {
+          const int cp = c0 + 32 * b + lane % 32;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = r0 + 32 * a + 8 * q + 4 * (lane / 32);
+            f32x4 v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                       acc[a][b][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(dst + (size_t)cp * D + c) = v;
+          }
+          tot[a][b] += acc[a][b];
+          acc[a][b] = f32x16{};
+        }
+    }
+    __syncthreads();
+    if (tid < D) {
+      float z = 0.f;
+#pragma unroll
+      for (int p = 0; p < kStateThreads / D; ++p) z += zred[p][tid];
+      zb[((size_t)bh * nb + j) * D + tid] = z;
+      zsum += z;
+    }
+  }
+
+  // chunk partial of H^T [c][c'] and Z
+  float* hp = h_part + ((size_t)bh * nchunk + chunk) * D * D;
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const f32x16 v = LITERAL ? tot[LITERAL ? a : 0][LITERAL ? b : 0] : acc[a][b];
+      const int cp = c0 + 32 * b + lane % 32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = r0 + 32 * a + 8 * (i / 4) + 4 * (lane / 32) + i % 4;
+        hp[(size_t)c * D + cp] = v[i];
+      }
+    }
+  if (tid < D) z_part[((size_t)bh * nchunk + chunk) * D + tid] = zsum;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h_part,
+                                                     const float* __restrict__ z_part,
+                                                     int nchunk, __bf16* __restrict__ ht_hi,
+                                                     __bf16* __restrict__ ht_lo,
+                                                     float* __restrict__ Z,
+                                                     float* __restrict__ h_full) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;  // element of H^T: c = e / D, c' = e % D
+  const float* hp = h_part + (size_t)bh * nchunk * D * D;
+  float s = 0.f;
+  for (int k = 0; k < nchunk; ++k) s += hp[(size_t)k * D * D + e];
+  const __bf16 hi = f2bf(s);
+  ht_hi[(size_t)bh * D * D + e] = hi;
+  ht_lo[(size_t)bh * D * D + e] = f2bf(s - bf2f(hi));
+  if (h_full) h_full[(size_t)bh * D * D + (size_t)(e % D) * D + e / D] = s;
+  if (blockIdx.x == 0 && threadIdx.x < D) {
+    const float* zp = z_part + (size_t)bh * nchunk * D;
+    float z = 0.f;
+    for (int k = 0; k < nchunk; ++k) z += zp[(size_t)k * D + threadIdx.x];
+    Z[(size_t)bh * D + threadIdx.x] = z;
+  }
+}
+
+template <class T, int D>
+hipError_t launch_states_t(const Dims& p, const void* K, const void* V, float* zb,
+                           float* h_part, float* z_part, float* hj, hipStream_t stream) {
+  const int cb = state_chunk_blocks(p);
+  dim3 grid((p.nb + cb - 1) / cb, p.B * p.H);
+  if (hj)
+    state_kernel<T, D, true><<<grid, kStateThreads, 0, stream>>>(
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj);
+  else
+    state_kernel<T, D, false><<<grid, kStateThreads, 0, stream>>>(
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int state_chunk_blocks(const Dims& p) {
+  // about >= 512 workgroups while keeping the partials small next to the K/V stream
+  const long work = (long)p.nb * p.B * p.H;
+  long cb = work / 512;
+  if (cb < 1) cb = 1;
+  if (cb > 16) cb = 16;
+  return (int)cb;
+}
+
+hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
+                         float* z_part, float* hj, hipStream_t stream) {
+  if (p.dtype == kBF16 && p.d == 128) return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, stream);
+  if (p.dtype == kBF16 && p.d == 64) return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, stream);
+  if (p.dtype == kF32 && p.d == 128) return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, stream);
+  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, stream);
+}
+
+hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,
+                               __bf16* ht_hi, __bf16* ht_lo, float* Z, float* h_full,
+                               hipStream_t stream) {
+  const int cb = state_chunk_blocks(p);
+  const int nchunk = (p.nb + cb - 1) / cb;
+  dim3 grid(p.d * p.d / 256, p.B * p.H);
+  if (p.d == 128)
+    reduce_kernel<128><<<grid, 256, 0, stream>>>(h_part, z_part, nchunk, ht_hi, ht_lo, Z, h_full);
+  else
+    reduce_kernel<64><<<grid, 256, 0, stream>>>(h_part, z_part, nchunk, ht_hi, ht_lo, Z, h_full);
+  return hipGetLastError();
+}
+
+}  // namespace sla

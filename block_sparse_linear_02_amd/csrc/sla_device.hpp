@@ -1,0 +1,93 @@
+// sla_device.hpp - device-side types and helpers shared by the gfx950 kernels of libsla.
+//
+// MFMA operand layouts used throughout (64-lane wavefronts, verified on gfx950):
+//   v_mfma_f32_32x32x16_bf16: A[32][16]  lane l holds A[l%32][8*(l/32) + 0..7]
+//                             B[16][32]  lane l holds B[8*(l/32) + 0..7][l%32]
+//                             C[32][32]  lane l, reg i holds C[8*(i/4) + 4*(l/32) + i%4][l%32]
+//   v_mfma_f32_16x16x32_bf16: A[16][32]  lane l holds A[l%16][8*(l/16) + 0..7]
+//                             B[32][16]  lane l holds B[8*(l/16) + 0..7][l%16]
+//                             C[16][16]  lane l, reg i holds C[4*(l/16) + i][l%16]
+// The order of the k-slots inside a lane is free as long as A and B use the same order.
+//   ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives element (i%4) of the
+//   64-bit words read by lanes 4e + i/4, e = 0..3.  With lane L of the group addressing row
+//   r0 + L/4, columns c0 + 4*(L%4) .. +3 of a row-major bf16 tile, lane i receives
+//   T[r0 + e][c0 + i], e = 0..3: four consecutive rows of one column.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32;
+
+constexpr int kBlock = 64;   // tokens per block (the compiled block size)
+constexpr int kWave = 64;    // gfx950 wavefront size
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16 <-> float (round to nearest even; the gfx950 conversion instruction)
+__device__ __forceinline__ __bf16 f2bf(float x) { return (__bf16)x; }
+__device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+
+// relu of 8 packed bf16 values with integer max: a bf16 with the sign bit set is a negative
+// int16, so max(x, 0) as int16 is relu(x) (and maps -0 to +0).
+__device__ __forceinline__ bf16x8 relu8(bf16x8 x) {
+  i32x4 v = __builtin_bit_cast(i32x4, x);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int lo = (int)(short)(v[i] & 0xffff);
+    int hi = v[i] >> 16;
+    lo = lo < 0 ? 0 : lo;
+    hi = hi < 0 ? 0 : hi;
+    v[i] = (hi << 16) | (lo & 0xffff);
+  }
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Transposing LDS read (see the header comment); `p` must point into LDS.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// Wave-wide reductions over all 64 lanes.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key); -0 and +0 map to
+// the same key.
+__device__ __forceinline__ u32 float_key(float f) {
+  u32 u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 16-byte global load/store helpers (addresses must be 16-byte aligned).
+template <class T>
+__device__ __forceinline__ i32x4 ld16(const T* p) { return *reinterpret_cast<const i32x4*>(p); }
+template <class T>
+__device__ __forceinline__ void st16(T* p, i32x4 v) { *reinterpret_cast<i32x4*>(p) = v; }
+
+}  // namespace sla

@@ -1,0 +1,60 @@
+// sla_launch.hpp - host-side launchers of the gfx950 kernels (internal to libsla).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sla {
+
+enum { kF32 = 0, kBF16 = 1 };
+
+struct Dims {
+  int B, H, N, d, nb, topk, dtype;
+};
+
+// Router: pool + project (split bf16 outputs [BH][nb][d]) then scores + HardTop-k.
+hipError_t launch_route(const Dims& p, const void* Q, const void* K, const float* Wq,
+                        const float* Wk, __bf16* q_hi, __bf16* q_lo, __bf16* k_hi,
+                        __bf16* k_lo, int32_t* idx, uint8_t* mask, float* probs,
+                        hipStream_t stream);
+size_t route_lds_bytes(int nb);
+int route_max_blocks();
+
+// Linear-branch states. Per chunk of `chunk_blocks` key blocks: partial H^T [d][d] and partial
+// Z [d]; per block z_j [d]; optionally (literal mode) every h_j [d][d] (K-channel major).
+int state_chunk_blocks(const Dims& p);
+hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
+                         float* z_part, float* hj, hipStream_t stream);
+// Reduce the chunk partials (fixed order): H^T as bf16 hi/lo [d][d], Z [d]; optionally H [d][d]
+// in fp32 (K-channel major, literal mode).
+hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,
+                               __bf16* ht_hi, __bf16* ht_lo, float* Z, float* h_full,
+                               hipStream_t stream);
+
+// Sparse branch (+ fused linear removal + combine): writes O.  fused_linear == 0 writes
+// alpha * O_s only (literal mode adds the linear branch afterwards).
+hipError_t launch_sparse(const Dims& p, const void* Q, const void* K, const void* V,
+                         const int32_t* idx, const float* alpha, const __bf16* ht_hi,
+                         const __bf16* ht_lo, const float* Z, const float* zb, float* O,
+                         int fused_linear, hipStream_t stream);
+
+// Literal linear apply: O += (1 - alpha) * relu(Q)(H - sum_sel h_j) / relu(Q).(Z - sum_sel z_j).
+hipError_t launch_linear_literal(const Dims& p, const void* Q, const int32_t* idx,
+                                 const float* alpha, const float* h_full, const float* Z,
+                                 const float* hj, const float* zb, float* O, hipStream_t stream);
+
+// fp8 path.
+hipError_t launch_quantize(const Dims& p, const void* X, uint8_t* codes, float* scales,
+                           hipStream_t stream);
+// V codes in the per-block transposed layout [BH][nb][d][64] read by the fp8 PV MFMA.
+hipError_t launch_quantize_v8t(const Dims& p, const void* X, uint8_t* codes, float* scales,
+                               hipStream_t stream);
+hipError_t launch_sparse_fp8(const Dims& p, const void* Q, const void* K, const void* V,
+                             const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                             const float* sq, const float* sk, const float* sv,
+                             const int32_t* idx, const float* alpha, const __bf16* ht_hi,
+                             const __bf16* ht_lo, const float* Z, const float* zb, float* O,
+                             hipStream_t stream);
+
+}  // namespace sla

@@ -1,0 +1,89 @@
+// sla_tiles.hpp - 64-token tile staging shared by the gfx950 kernels of libsla.
+//
+// A tile is 64 consecutive tokens x D channels of one (batch, head).  It travels HBM ->
+// registers (16-byte coalesced loads, issued one tile ahead) -> LDS (row-major bf16, each row
+// padded by kPad elements so that row-wise 16-byte reads of 16 consecutive rows hit distinct
+// banks).  fp32 inputs are rounded to bf16 (nearest even) on the way into LDS.
+#pragma once
+
+#include "sla_device.hpp"
+
+namespace sla {
+
+constexpr int kPad = 8;  // bf16 elements of padding per LDS row
+
+template <class T>
+struct Vec16;  // elements of one 16-byte global load
+template <>
+struct Vec16<__bf16> {
+  static constexpr int n = 8;
+};
+template <>
+struct Vec16<float> {
+  static constexpr int n = 4;
+};
+
+// Registers holding one tile of a [rows][D] tensor for THREADS cooperating threads; rows at or
+// beyond `valid` read as zero.
+template <class T, int D, int THREADS>
+struct TileLoader {
+  static constexpr int VEC = Vec16<T>::n;
+  static constexpr int CPR = D / VEC;                 // 16-byte chunks per row
+  static constexpr int PER = kBlock * CPR / THREADS;  // chunks per thread
+  static_assert(PER * THREADS == kBlock * CPR, "tile must split evenly over the threads");
+  i32x4 r[PER];
+  __device__ __forceinline__ void load(const T* base, int valid, int tid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * THREADS;
+      const int row = q / CPR, ch = q % CPR;
+      r[u] = row < valid ? ld16(base + (size_t)row * D + ch * VEC) : i32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * THREADS;
+      const int row = q / CPR, ch = q % CPR;
+      __bf16* dst = lds + row * (D + kPad) + ch * VEC;
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<i32x4*>(dst) = r[u];
+      } else {
+        const f32x4 f = __builtin_bit_cast(f32x4, r[u]);
+        bf16x4 b = {f2bf(f[0]), f2bf(f[1]), f2bf(f[2]), f2bf(f[3])};
+        *reinterpret_cast<bf16x4*>(dst) = b;
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 a, i16x4 b) {
+  i32x4 v = {(int)((u32)(uint16_t)a[0] | ((u32)(uint16_t)a[1] << 16)),
+             (int)((u32)(uint16_t)a[2] | ((u32)(uint16_t)a[3] << 16)),
+             (int)((u32)(uint16_t)b[0] | ((u32)(uint16_t)b[1] << 16)),
+             (int)((u32)(uint16_t)b[2] | ((u32)(uint16_t)b[3] << 16))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Transposed MFMA operand from a row-major [64][D + kPad] LDS tile: lane l (g = l/32) receives
+// column col0 + l%32 at the rows row0 + r_off + e and row0 + r_off + gap + e (e = 0..3) where
+// r_off = step * g.  step = 8, gap = 4 gives rows row0 + 8g + 0..7; step = 4, gap = 8 gives
+// rows row0 + 4g + {0..3, 8..11} (the key order of a 32x32 MFMA accumulator).
+template <int D, int STEP, int GAP>
+__device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int row0, int col0, int lane) {
+  const int h = lane / 16, L = lane % 16;
+  const int g = h / 2, cs = h % 2;
+  const __bf16* p = tile + (row0 + STEP * g + L / 4) * (D + kPad) + col0 + 16 * cs + 4 * (L % 4);
+  return join_tr(lds_read_tr16(p), lds_read_tr16(p + GAP * (D + kPad)));
+}
+
+// Map a workgroup id to a logical work item so that each of the 8 XCDs (which receive
+// workgroups round-robin) processes one contiguous range of items: neighbouring query blocks
+// of a head share their XCD's L2.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  const int q = total / 8, r = total % 8;
+  const int xcd = wg % 8, k = wg / 8;
+  return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+}  // namespace sla

@@ -24,8 +24,10 @@ Every stream is a numpy PCG64 seeded by SeedSequence([seed, workload id, tensor 
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -100,6 +102,15 @@ def sweep_workloads():
     return out
 
 
+def workers() -> int:
+    """Host threads for per-head work (bounded: the GPU machines grant a 16-core share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _rng(seed: int, *key) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *key])))
 
@@ -153,18 +164,23 @@ def draw(wl: Workload, seed: int = 0) -> dict:
     K = torch.empty((B, H, N, d), dtype=tdt)
     V = torch.empty((B, H, N, d), dtype=tdt)
     alpha = torch.empty((B, H, N), dtype=torch.float32)
-    for b in range(B):
-        for h in range(H):
-            q, k = _head_qk(wl, seed, b, h)
-            Q[b, h] = _round(q, wl.dtype)
-            K[b, h] = _round(k, wl.dtype)
-            v = _rng(seed, wl.wid, _T_V, b, h).standard_normal((N, d), dtype=np.float32)
-            V[b, h] = _round(v, wl.dtype)
-            if wl.alpha == "half":
-                alpha[b, h] = 0.5
-            else:
-                x = _rng(seed, wl.wid, _T_ALPHA, b, h).standard_normal(N)
-                alpha[b, h] = torch.from_numpy((1.0 / (1.0 + np.exp(-x))).astype(np.float32))
+
+    def one_head(bh):
+        b, h = divmod(bh, H)
+        q, k = _head_qk(wl, seed, b, h)
+        Q[b, h] = _round(q, wl.dtype)
+        K[b, h] = _round(k, wl.dtype)
+        v = _rng(seed, wl.wid, _T_V, b, h).standard_normal((N, d), dtype=np.float32)
+        V[b, h] = _round(v, wl.dtype)
+        if wl.alpha == "half":
+            alpha[b, h] = 0.5
+        else:
+            x = _rng(seed, wl.wid, _T_ALPHA, b, h).standard_normal(N)
+            alpha[b, h] = torch.from_numpy((1.0 / (1.0 + np.exp(-x))).astype(np.float32))
+
+    # every head has its own seed streams, so the result does not depend on the thread count
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers()) as ex:
+        list(ex.map(one_head, range(B * H)))
     sw = 1.0 / math.sqrt(d)
     Wq = torch.from_numpy(_rng(seed, wl.wid, _T_WQ).normal(0.0, sw, (d, d)).astype(np.float32))
     Wk = torch.from_numpy(_rng(seed, wl.wid, _T_WK).normal(0.0, sw, (d, d)).astype(np.float32))
@@ -174,27 +190,27 @@ def draw(wl: Workload, seed: int = 0) -> dict:
 def redraw_query_blocks(inputs: dict, b: int, h: int, blocks, attempt: int) -> None:
     """Redraw, in place, the query-token noise of the listed query blocks of head (b, h).
 
-    Cluster centres (and K, V, alpha) are kept; only Q rows of those blocks change, from a
-    stream keyed by (seed, workload, b, h, block, attempt).  Used to enforce the router's score
-    gap by rejection; since a row of the block-score map depends only on its own query block,
-    no other row moves.
+    Cluster centres (and K, V, alpha) are kept; only Q rows of those blocks change.  The new
+    noise of all listed blocks (ascending) comes from one stream keyed by
+    (seed, workload, b, h, attempt), 64 rows per block (a short last block uses its first
+    rows).  Used to enforce the router's score gap by rejection: a row of the block-score map
+    depends only on its own query block, so no other row moves.
     """
     wl: Workload = inputs["workload"]
     seed = inputs["seed"]
     N, d, blk = wl.N, wl.d, wl.block
-    Q = inputs["Q"]
+    blocks = np.sort(np.asarray(blocks, dtype=np.int64))
+    noise = _rng(seed, wl.wid, _T_REDRAW, b, h, int(attempt)).standard_normal(
+        (len(blocks), blk, d), dtype=np.float32
+    )
+    rows = np.concatenate([np.arange(i * blk, min(i * blk + blk, N)) for i in blocks])
+    pos = np.concatenate([np.arange(min(blk, N - i * blk)) + n * blk for n, i in enumerate(blocks)])
+    new = noise.reshape(-1, d)[pos]
     if wl.kind == "clustered":
         cid, ncl = _cluster_ids(wl.grid)
         mu = _rng(seed, wl.wid, _T_CENTRE, b, h).standard_normal((ncl, d), dtype=np.float32)
         mu *= np.float32(wl.cluster_scale)
-    sd = np.float32(math.sqrt(NOISE_VAR))
-    for i in blocks:
-        a, e = i * blk, min(i * blk + blk, N)
-        noise = _rng(seed, wl.wid, _T_REDRAW, b, h, int(i), int(attempt)).standard_normal(
-            (e - a, d), dtype=np.float32
-        )
-        if wl.kind == "clustered":
-            rows = mu[cid[a:e]] + sd * noise
-        else:
-            rows = noise
-        Q[b, h, a:e] = _round(rows, wl.dtype)
+        new = mu[cid[rows]] + np.float32(math.sqrt(NOISE_VAR)) * new
+    import torch
+
+    inputs["Q"][b, h, torch.from_numpy(rows)] = _round(new, wl.dtype)

@@ -1,0 +1,143 @@
+/*
+ * sla.h - C ABI of the MI355X (gfx950) SLA2 hybrid sparse-linear attention inference forward.
+ *
+ * The operator (SLA2: Sparse-Linear Attention with Learnable Routing and QAT; Italian summary
+ * sections 1 and 2, Arabic summary sections 1 and 2) for one (batch, head):
+ *
+ *   router   Q and K are mean-pooled over blocks of `block` adjacent tokens, projected by the
+ *            learnable proj_q / proj_k (y = x @ W), scored s_ij = q~_i . k~_j / sqrt(d), and a
+ *            HardTop-k per query block keeps `topk` key blocks (mask M, index list idx).
+ *   sparse   O_s: exact softmax attention of each query over the tokens of its kept blocks.
+ *   linear   O_l: ReLU-feature linear attention (the kernel function of "SALAD: Achieve
+ *            High-Sparsity Attention via Efficient Linear Attention Tuning for Video Diffusion
+ *            Transformer", section 2) over the tokens of the unselected blocks,
+ *            O_l(q) = relu(q) A_i / (relu(q) . zeta_i), A_i = sum_{j unselected} relu(K_j)^T V_j,
+ *            zeta_i = sum_{j unselected} relu(K_j)^T 1; 0 when nothing is unselected or the
+ *            denominator is 0.
+ *   combine  O = alpha * O_s + (1 - alpha) * O_l  (SLA2 Italian summary section 2.A).
+ *   fp8      The sparse branch may run on e4m3-quantised Q, K, P, V (SLA2 Italian summary
+ *            section 2.C, Arabic summary section 2.jim); router and linear branch stay
+ *            unquantised.
+ *
+ * Layouts (all row-major, innermost index last, densely packed):
+ *   Q, K, V  [B][H][N][d], dtype `dtype` (SLA_BF16 or SLA_F32)
+ *   proj_q, proj_k  [d][d] float32, y[c] = sum_r x[r] * W[r][c]; one matrix for every (b, h)
+ *   alpha    [B][H][N] float32, mixing weight of the sparse branch per query token
+ *   idx      [B][H][n_b][topk] int32, kept key blocks per query block, strictly ascending
+ *   mask     [B][H][n_b][n_b] uint8 (1 = kept)
+ *   scores   [B][H][n_b][n_b] float32, row softmax of the block-score map
+ *   O        [B][H][N][d] float32
+ * with n_b = ceil(N / block); the last block may be short (its mean runs over its valid
+ * tokens, its missing keys are masked, nothing is stored past N).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller, including the workspace;
+ * the library allocates no device memory, keeps no pointer after a call returns and does not
+ * synchronise the host.  Work is enqueued on `stream` in call order; calls are re-entrant.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued.  A null required
+ * pointer, a non-positive size, topk outside [0, n_b] or an element count over 2^62 gives
+ * SLA_ERR_INVALID; a shape outside the compiled set (block != 64, d not in {64, 128}, dtype
+ * not in sla_dtype) gives SLA_ERR_UNSUPPORTED; a workspace smaller than the matching
+ * *_workspace_bytes() gives SLA_ERR_WORKSPACE; a failed launch gives SLA_ERR_HIP (the hipError_t
+ * is available from sla_last_hip_error()).  idx contents are trusted (ascending, in range);
+ * non-finite inputs give undefined output.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLA_OK = 0,
+  SLA_ERR_INVALID = -1,
+  SLA_ERR_UNSUPPORTED = -2,
+  SLA_ERR_WORKSPACE = -3,
+  SLA_ERR_HIP = -4
+} sla_status;
+
+typedef enum { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype; /* dtype of Q, K, V */
+
+typedef struct {
+  int32_t B, H, N, d; /* batch, heads, tokens, head dim */
+  int32_t block;      /* tokens per block (compiled: 64) */
+  int32_t topk;       /* kept key blocks per query block, 0 <= topk <= n_b */
+  int32_t dtype;      /* sla_dtype */
+} sla_problem;
+
+/* How the forward removes the kept blocks' states from the linear branch.
+ * SLA_LINEAR_FUSED (default): relu(Q_i) (H - sum_sel h_j) is evaluated as
+ *   relu(Q_i) H - sum_sel (relu(Q_i) relu(K_j)^T) V_j inside the sparse kernel, on the K/V
+ *   tiles it already holds (no per-block d x d state is read).
+ * SLA_LINEAR_LITERAL: every h_j = relu(K_j)^T V_j is materialised in the workspace and a
+ *   separate kernel sums the kept ones per query block before applying relu(Q). */
+enum { SLA_LINEAR_FUSED = 0, SLA_LINEAR_LITERAL = 1 };
+
+typedef struct {
+  int32_t linear_mode;     /* SLA_LINEAR_FUSED or SLA_LINEAR_LITERAL */
+  hipEvent_t sparse_begin; /* if non-null: recorded on `stream` right before the sparse kernel */
+  hipEvent_t sparse_end;   /* if non-null: recorded on `stream` right after it */
+} sla_forward_opts;
+
+/* Workspace sizes in bytes for a problem (0 when the problem is invalid or unsupported). */
+size_t sla_route_workspace_bytes(const sla_problem* p);
+/* variant: 0 = sla_forward (fused linear), 1 = sla_forward_fp8, 2 = literal linear mode. */
+size_t sla_forward_workspace_bytes(const sla_problem* p, int variant);
+
+/* Router (SLA2 Italian summary section 2.B, Arabic summary section 2.ba and 2.dal): block
+ * mean-pool of Q and K, projection, block-score map, HardTop-k.  Among equal scores the lower
+ * block index is kept; the kept indices are written in ascending order.  mask and scores are
+ * optional outputs (NULL to skip).  Needs sla_route_workspace_bytes(p) bytes of workspace. */
+int sla_route(const sla_problem* p, const void* Q, const void* K, const float* proj_q,
+              const float* proj_k, int32_t* idx, uint8_t* mask, float* scores, void* ws,
+              size_t ws_bytes, hipStream_t stream);
+
+/* Forward with the bf16 (or fp32-input) sparse branch: O = alpha O_s + (1 - alpha) O_l
+ * (SLA2 Italian summary section 2.A).  topk == 0 gives O_s = 0; topk == n_b gives O_l = 0.
+ * Needs sla_forward_workspace_bytes(p, 0) bytes of workspace. */
+int sla_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* sla_forward with options (linear mode, events around the sparse kernel); opts may be NULL.
+ * Needs sla_forward_workspace_bytes(p, 2) bytes in literal mode, (p, 0) otherwise. */
+int sla_forward_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
+                   const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                   hipStream_t stream, const sla_forward_opts* opts);
+
+/* Forward with the quantised sparse branch (SLA2 Italian summary section 2.C, Arabic summary
+ * section 2.jim): Q, K, V are quantised per (b, h, 64-token block) to OCP e4m3 with an absmax
+ * scale (x * fp32(448 / absmax), round to nearest even, saturating), P is quantised per
+ * (query block x key block) tile with scale max(tile) / 448 over exp(S - rowmax) using the
+ * exact row maximum, and O_s = sum (P8 sP)(V8 sV) / sum exp(S - rowmax).  Only dtype
+ * SLA_BF16 with d = 128 is compiled.  Needs sla_forward_workspace_bytes(p, 1) bytes. */
+int sla_forward_fp8(const sla_problem* p, const void* Q, const void* K, const void* V,
+                    const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* sla_forward_fp8 with events around its sparse kernel (opts->linear_mode must be fused). */
+int sla_forward_fp8_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
+                       const int32_t* idx, const float* alpha, float* O, void* ws,
+                       size_t ws_bytes, hipStream_t stream, const sla_forward_opts* opts);
+
+/* Quantisation step of sla_forward_fp8 on its own (for byte-exact checks): writes e4m3 codes
+ * of X [B][H][N][d] (bf16) to codes [B][H][N][d] (uint8) and the per-block scales to
+ * scales [B][H][n_b] (float32). */
+int sla_quantize_e4m3(const sla_problem* p, const void* X, uint8_t* codes, float* scales,
+                      hipStream_t stream);
+
+const char* sla_status_string(int status);
+/* hipError_t of the most recent SLA_ERR_HIP on the calling thread (0 if none). */
+int sla_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

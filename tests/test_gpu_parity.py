@@ -1,0 +1,309 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU float64 oracle.
+
+Bars: router indices and mask bit-exact; O within max-abs 1e-2 and relative L2 5e-3 (bf16 or
+fp32 inputs, fp32 accumulation), relative L2 3e-2 for the fp8 sparse branch; e4m3 codes and
+scales byte-exact.  Small cases are compared element by element over every output; the
+full-size workloads (the ones the benchmark times) over every router row and over sampled query
+blocks of sampled heads (always including the first and the last, possibly short, block).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_linear_02_amd as sla
+import gen
+import oracle
+from tests import cases
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX = 1e-2
+TOL_REL = 5e-3
+TOL_REL_FP8 = 3e-2
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sla.lib()  # fail loudly if the library is missing
+
+
+def dev(c):
+    d = torch.device("cuda:0")
+    return {k: c[k].to(d) for k in ("Q", "K", "V", "alpha", "Wq", "Wk")}
+
+
+def oracle_route(c, k):
+    return oracle.route(c["Q"], c["K"], c["Wq"].double(), c["Wk"].double(), k, 64)
+
+
+def rel_l2(got, ref):
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def check_close(got, ref, rel_tol=TOL_REL, max_tol=TOL_MAX, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    rel = rel_l2(got, ref) if got.size else 0.0
+    say(f"{what}: max|d| {err:.3e}  rel-L2 {rel:.3e}")
+    if max_tol is not None:
+        assert err <= max_tol, f"{what}: max abs error {err}"
+    assert rel <= rel_tol, f"{what}: relative L2 error {rel}"
+
+
+_CACHE = {}
+
+
+def case(key, wl, ks=None):
+    if key not in _CACHE:
+        say(f"generating {key} {wl}")
+        _CACHE[key] = cases.make_case(wl, ks=ks)
+    return _CACHE[key]
+
+
+def small_ragged(H=2, k=6, **kw):
+    return gen.workload("video_l", H=H, N=3600, grid=(1, 45, 80), topk=k, **kw)  # 57 blocks
+
+
+# ---------------------------------------------------------------------------------- router
+
+
+@pytest.mark.parametrize(
+    "name,wl",
+    [
+        ("tiny", gen.workload("tiny")),
+        ("ragged_bf16", small_ragged()),
+        ("ragged_d64", small_ragged(k=9).with_(d=64, name="ragged_d64")),
+        ("ragged_fp32", small_ragged(k=3).with_(dtype="fp32", name="ragged_fp32")),
+    ],
+)
+def test_route_bitexact_small(name, wl):
+    c = case(name, wl)
+    g = dev(c)
+    say(f"route {name}")
+    idx, mask, probs = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], wl.topk, want_mask=True, want_scores=True)
+    r = oracle_route(c, wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"])
+    assert np.array_equal(mask.cpu().numpy(), r["mask"])
+    np.testing.assert_allclose(probs.cpu().numpy(), r["probs"], rtol=0, atol=2e-5)
+
+
+@pytest.mark.parametrize("k", [0, 1, 57])
+def test_route_degenerate_k(k):
+    wl = small_ragged(k=k)
+    c = case(f"ragged_k{k}", wl)
+    g = dev(c)
+    say(f"route k={k}")
+    idx, mask, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], k, want_mask=True)
+    r = oracle_route(c, k)
+    assert idx.shape == (1, 2, 57, k)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"])
+    assert np.array_equal(mask.cpu().numpy(), r["mask"])
+
+
+def test_route_exact_ties_keep_lowest_index():
+    d = torch.device("cuda:0")
+    Q = torch.ones((1, 1, 1000, 128), dtype=torch.bfloat16, device=d)
+    W = torch.eye(128, dtype=torch.float32, device=d)
+    say("route ties")
+    idx, _, _ = sla.route(Q, Q, W, W, 5)
+    assert idx.cpu().numpy().tolist() == [[[[0, 1, 2, 3, 4]] * 16]]
+
+
+# ---------------------------------------------------------------------------------- forward
+
+
+def run_forward(c, idx_np, **kw):
+    g = dev(c)
+    idx = torch.from_numpy(np.ascontiguousarray(idx_np)).to(g["Q"].device)
+    alpha = kw.pop("alpha", g["alpha"])
+    O = sla.forward(g["Q"], g["K"], g["V"], idx, alpha, **kw)
+    torch.cuda.synchronize()
+    return O.cpu().double().numpy()
+
+
+@pytest.mark.parametrize(
+    "name,wl",
+    [
+        ("tiny", gen.workload("tiny")),
+        ("ragged_bf16", small_ragged()),
+        ("ragged_d64", small_ragged(k=9).with_(d=64, name="ragged_d64")),
+        ("ragged_fp32", small_ragged(k=3).with_(dtype="fp32", name="ragged_fp32")),
+    ],
+)
+def test_forward_small_every_element(name, wl):
+    c = case(name, wl)
+    r = oracle_route(c, wl.topk)
+    say(f"forward {name}")
+    got = run_forward(c, r["idx"])
+    ref, _, _ = oracle.forward(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, what=f"forward {name}")
+
+
+def test_forward_branches_isolated():
+    """alpha = 1 gives the sparse branch alone, alpha = 0 the linear branch alone."""
+    wl = small_ragged()
+    c = case("ragged_bf16", wl)
+    r = oracle_route(c, wl.topk)
+    _, Os, Ol = oracle.forward(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    d = torch.device("cuda:0")
+    one = torch.ones_like(c["alpha"]).to(d)
+    say("forward alpha=1")
+    check_close(run_forward(c, r["idx"], alpha=one), Os, what="sparse branch (alpha=1)")
+    say("forward alpha=0")
+    check_close(run_forward(c, r["idx"], alpha=torch.zeros_like(one)), Ol, what="linear branch (alpha=0)")
+
+
+@pytest.mark.parametrize("k", [0, 1, 57])
+def test_forward_degenerate_k(k):
+    """k = 0: no sparse branch; k = n_b: full softmax attention and no linear branch."""
+    wl = small_ragged(k=k)
+    c = case(f"ragged_k{k}", wl)
+    r = oracle_route(c, k)
+    say(f"forward k={k}")
+    got = run_forward(c, r["idx"])
+    ref, _, Ol = oracle.forward(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, what=f"forward k={k}")
+    if k == 57:
+        assert np.all(Ol == 0)
+
+
+def test_forward_literal_linear_mode():
+    wl = small_ragged()
+    c = case("ragged_bf16", wl)
+    r = oracle_route(c, wl.topk)
+    say("forward literal")
+    got = run_forward(c, r["idx"], linear_mode="literal")
+    ref, _, _ = oracle.forward(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, what="forward literal")
+    fused = run_forward(c, r["idx"])
+    check_close(got, fused, rel_tol=1e-3, max_tol=1e-3, what="literal vs fused")
+
+
+def test_forward_deterministic():
+    wl = small_ragged()
+    c = case("ragged_bf16", wl)
+    g = dev(c)
+    say("determinism")
+    outs = []
+    for _ in range(2):
+        idx, _, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], wl.topk)
+        outs.append((idx.cpu(), sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"]).cpu(),
+                     sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], fp8=True).cpu()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------------- fp8
+
+
+def test_quantize_e4m3_bytes_exact():
+    wl = small_ragged()
+    c = case("ragged_bf16", wl)
+    g = dev(c)
+    for name in ("Q", "K", "V"):
+        say(f"quantize {name}")
+        codes, scales = sla.quantize_e4m3(g[name])
+        codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+        for b in range(wl.B):
+            for h in range(wl.H):
+                rc, rs, _ = oracle.quantize_blocks(c[name][b, h], 64)
+                assert np.array_equal(scales[b, h], rs)
+                assert np.array_equal(codes[b, h], rc)
+
+
+def test_fp8_forward_small():
+    wl = small_ragged()
+    c = case("ragged_bf16", wl)
+    r = oracle_route(c, wl.topk)
+    say("forward fp8 small")
+    got = run_forward(c, r["idx"], fp8=True)
+    ref, _, _ = oracle.forward_fp8(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what="forward fp8 small")
+
+
+# ---------------------------------------------------------------------------------- full size
+
+
+def sampled_compare(c, idx_np, got_O, heads, blocks, fp8=False, what=""):
+    wl = c["workload"]
+    gots, refs = [], []
+    for bh in heads:
+        b, h = divmod(bh, wl.H)
+        args = (c["Q"][b, h], c["K"][b, h], c["V"][b, h], idx_np[b, h], c["alpha"][b, h], 64)
+        if fp8:
+            o, _, _ = oracle.forward_fp8_head(*args, q_blocks=blocks)
+        else:
+            o, _, _ = oracle.forward_head(*args, q_blocks=blocks)
+        for i, oi in zip(blocks, o):
+            refs.append(oi)
+            gots.append(got_O[b, h, i * 64 : i * 64 + len(oi)])
+    got = np.concatenate(gots)
+    ref = np.concatenate(refs)
+    if fp8:
+        check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what=what)
+    else:
+        check_close(got, ref, what=what)
+
+
+def full_size(c, heads, blocks, fp8=False, what=""):
+    wl = c["workload"]
+    g = dev(c)
+    say(f"route {what}")
+    idx, mask, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], wl.topk, want_mask=True)
+    r = oracle_route(c, wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"]), f"{what}: router indices differ"
+    assert np.array_equal(mask.cpu().numpy(), r["mask"]), f"{what}: router mask differs"
+    say(f"forward {what}")
+    O = sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], fp8=fp8)
+    torch.cuda.synchronize()
+    got = O.cpu().double().numpy()
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    sampled_compare(c, r["idx"], got, heads, blocks, fp8=fp8, what=what)
+
+
+def test_video_s_full_size():
+    c = case("video_s", gen.workload("video_s"))
+    full_size(c, heads=[0, 5, 11], blocks=[0, 1, 200, 511], what="video_s N=32768 H=12 k=51")
+
+
+def test_video_l_full_size():
+    c = case("video_l", gen.workload("video_l"))
+    full_size(c, heads=[0, 39], blocks=[0, 600, 1181], what="video_l N=75600 H=40 k=60")
+
+
+def test_video_l_fp8_full_size():
+    c = case("video_l", gen.workload("video_l"))
+    full_size(c, heads=[0, 21], blocks=[0, 1181], fp8=True, what="video_l fp8")
+
+
+@pytest.mark.parametrize("scale", [0.5, 1.0, 2.0])
+def test_sparsity_sweep(scale):
+    """keep {20,10,5,3}% x alpha {0.5, random} at cluster scale `scale` (B=2, H=12, N=32768)."""
+    ks = (102, 51, 26, 15)
+    base = gen.workload("video_s", B=2, topk=ks[0], cluster_scale=scale, name=f"sweep_s{scale:g}", wid=4)
+    c = case(f"sweep_s{scale:g}", base, ks=ks)
+    g = dev(c)
+    for k in ks:
+        r = oracle_route(c, k)
+        say(f"sweep s={scale} k={k} route")
+        idx, _, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], k)
+        assert np.array_equal(idx.cpu().numpy(), r["idx"]), f"sweep s={scale} k={k}: indices differ"
+        for a in ("half", "random"):
+            alpha = torch.full_like(g["alpha"], 0.5) if a == "half" else g["alpha"]
+            cc = dict(c, alpha=alpha.cpu())
+            say(f"sweep s={scale} k={k} alpha={a} forward")
+            O = sla.forward(g["Q"], g["K"], g["V"], idx, alpha)
+            torch.cuda.synchronize()
+            sampled_compare(cc, r["idx"], O.cpu().double().numpy(), heads=[0, 23], blocks=[0, 511],
+                            what=f"sweep s={scale} k={k} alpha={a}")
