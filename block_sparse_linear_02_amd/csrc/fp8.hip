@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kF8Threads) void sparse_fp8_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const bool ok = row_ok && 32 * kt + 8 * (i / 4) + 4 * g + i % 4 < nv;
-        p[kt][i] = ok ? exp2f(fmaf(s[kt][i], sc, -mrow)) : 0.f;
+        p[kt][i] = ok ? fast_exp2(fmaf(s[kt][i], sc, -mrow)) : 0.f;
         lsum += p[kt][i];
         pmax = fmaxf(pmax, p[kt][i]);
       }

@@ -43,20 +43,17 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ __bf16 f2bf(float x) { return (__bf16)x; }
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
 
-// relu of 8 packed bf16 values with integer max: a bf16 with the sign bit set is a negative
-// int16, so max(x, 0) as int16 is relu(x) (and maps -0 to +0).
+// relu of 8 packed bf16 values with a packed 16-bit integer max: a bf16 with the sign bit set
+// is a negative int16, so max(x, 0) as int16 is relu(x) (and maps -0 to +0).
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ bf16x8 relu8(bf16x8 x) {
-  i32x4 v = __builtin_bit_cast(i32x4, x);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int lo = (int)(short)(v[i] & 0xffff);
-    int hi = v[i] >> 16;
-    lo = lo < 0 ? 0 : lo;
-    hi = hi < 0 ? 0 : hi;
-    v[i] = (hi << 16) | (lo & 0xffff);
-  }
-  return __builtin_bit_cast(bf16x8, v);
+  const i16x8 v = __builtin_bit_cast(i16x8, x);
+  return __builtin_bit_cast(bf16x8, __builtin_elementwise_max(v, i16x8{}));
 }
+
+// 2^x on the hardware transcendental unit (v_exp_f32): about 1 ulp; results below 2^-126 may
+// flush to zero, which only drops probabilities under 2^-126 of the row maximum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Transposing LDS read (see the header comment); `p` must point into LDS.
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {

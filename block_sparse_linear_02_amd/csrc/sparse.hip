@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_kernel(
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(mrun, mx * c_log2);
-    const float corr = exp2f(mrun - mnew);
+    const float corr = fast_exp2(mrun - mnew);
     mrun = mnew;
     float psum = 0.f;
     bf16x8 pb[4], lb[4];
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kSparseThreads) void sparse_kernel(
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const float p = exp2f(fmaf(s[u / 2][8 * (u % 2) + jj], c_log2, -mnew));
+        const float p = fast_exp2(fmaf(s[u / 2][8 * (u % 2) + jj], c_log2, -mnew));
         psum += p;
         pb[u][jj] = f2bf(p);
         if constexpr (FUSED) lb[u][jj] = f2bf(-l[u / 2][8 * (u % 2) + jj]);

@@ -3,7 +3,8 @@ and the CPU oracle use.
 
 It draws tensors and nothing else: no pooling, projection, scoring, softmax or selection lives
 here.  Callers that need the router's k-th/(k+1)-th score gap (the tests) check it with the oracle
-and ask this module to redraw the noise of single query blocks (``redraw_query_blocks``).
+and ask this module to redraw single query blocks (``query_noise_means`` then
+``realize_query_blocks``).
 
 Workloads (the pages measure on Wan2.1 video DiT attention, which is not available; these
 tensors stand in for it with the same shapes and an attention-concentrating structure):
@@ -26,6 +27,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import dataclasses
+import functools
 import math
 import os
 
@@ -37,14 +39,18 @@ __all__ = [
     "workload",
     "sweep_workloads",
     "draw",
-    "redraw_query_blocks",
+    "noise_std",
+    "query_block_centres",
+    "query_noise_means",
+    "realize_query_blocks",
 ]
 
 NOISE_VAR = 0.3
 BOX = (2, 8, 8)
 
 # tensor ids of the seed streams
-_T_Q, _T_K, _T_V, _T_ALPHA, _T_WQ, _T_WK, _T_CENTRE, _T_QNOISE, _T_KNOISE, _T_REDRAW = range(10)
+(_T_Q, _T_K, _T_V, _T_ALPHA, _T_WQ, _T_WK, _T_CENTRE, _T_QNOISE, _T_KNOISE, _T_REDRAW,
+ _T_REALIZE) = range(11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -115,6 +121,7 @@ def _rng(seed: int, *key) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *key])))
 
 
+@functools.lru_cache(maxsize=8)
 def _cluster_ids(grid) -> tuple[np.ndarray, int]:
     """Box id of every token of a (T, Hh, W) latent grid flattened as n = (t*Hh + h)*W + w."""
     T, Hh, W = grid
@@ -141,8 +148,7 @@ def _head_qk(wl: Workload, seed: int, b: int, h: int):
         return q, k
     cid, ncl = _cluster_ids(wl.grid)
     assert len(cid) == N, (wl.grid, N)
-    mu = _rng(seed, wl.wid, _T_CENTRE, b, h).standard_normal((ncl, d), dtype=np.float32)
-    mu *= np.float32(wl.cluster_scale)
+    mu = _centres(seed, wl, b, h)
     sd = np.float32(math.sqrt(NOISE_VAR))
     eq = _rng(seed, wl.wid, _T_QNOISE, b, h).standard_normal((N, d), dtype=np.float32)
     ek = _rng(seed, wl.wid, _T_KNOISE, b, h).standard_normal((N, d), dtype=np.float32)
@@ -187,30 +193,72 @@ def draw(wl: Workload, seed: int = 0) -> dict:
     return {"Q": Q, "K": K, "V": V, "Wq": Wq, "Wk": Wk, "alpha": alpha, "workload": wl, "seed": seed}
 
 
-def redraw_query_blocks(inputs: dict, b: int, h: int, blocks, attempt: int) -> None:
-    """Redraw, in place, the query-token noise of the listed query blocks of head (b, h).
+def noise_std(wl: Workload) -> float:
+    """Standard deviation of the per-token query/key noise."""
+    return math.sqrt(NOISE_VAR) if wl.kind == "clustered" else 1.0
 
-    Cluster centres (and K, V, alpha) are kept; only Q rows of those blocks change.  The new
-    noise of all listed blocks (ascending) comes from one stream keyed by
-    (seed, workload, b, h, attempt), 64 rows per block (a short last block uses its first
-    rows).  Used to enforce the router's score gap by rejection: a row of the block-score map
-    depends only on its own query block, so no other row moves.
-    """
+
+def query_block_centres(inputs: dict, b: int, h: int, block: int) -> np.ndarray:
+    """The cluster-centre part of the query tokens of one block (zeros for iid workloads),
+    float32 [r, d] with r the block's number of tokens."""
     wl: Workload = inputs["workload"]
-    seed = inputs["seed"]
-    N, d, blk = wl.N, wl.d, wl.block
-    blocks = np.sort(np.asarray(blocks, dtype=np.int64))
-    noise = _rng(seed, wl.wid, _T_REDRAW, b, h, int(attempt)).standard_normal(
-        (len(blocks), blk, d), dtype=np.float32
+    a = block * wl.block
+    e = min(a + wl.block, wl.N)
+    if wl.kind != "clustered":
+        return np.zeros((e - a, wl.d), dtype=np.float32)
+    cid, ncl = _cluster_ids(wl.grid)
+    mu = _centres(inputs["seed"], wl, b, h)
+    return mu[cid[a:e]]
+
+
+def _centres(seed, wl, b, h):
+    mu = _rng(seed, wl.wid, _T_CENTRE, b, h).standard_normal((_cluster_ids(wl.grid)[1], wl.d), dtype=np.float32)
+    return mu * np.float32(wl.cluster_scale)
+
+
+def query_noise_means(inputs: dict, b: int, h: int, blocks, attempt: int, count: int,
+                      chunk: int = 0) -> np.ndarray:
+    """`count` candidate values, per listed block of head (b, h), of the mean over the block's
+    r tokens of their i.i.d. N(0, 1) query noise: N(0, 1/r) per channel, float32
+    [len(blocks), count, d], from the stream (seed, workload, b, h, attempt, chunk)."""
+    wl: Workload = inputs["workload"]
+    blocks = np.asarray(blocks, dtype=np.int64)
+    r = np.minimum(wl.block, wl.N - blocks * wl.block).astype(np.float32)
+    z = _rng(inputs["seed"], wl.wid, _T_REDRAW, b, h, int(attempt), int(chunk)).standard_normal(
+        (len(blocks), count, wl.d), dtype=np.float32
     )
-    rows = np.concatenate([np.arange(i * blk, min(i * blk + blk, N)) for i in blocks])
-    pos = np.concatenate([np.arange(min(blk, N - i * blk)) + n * blk for n, i in enumerate(blocks)])
-    new = noise.reshape(-1, d)[pos]
-    if wl.kind == "clustered":
-        cid, ncl = _cluster_ids(wl.grid)
-        mu = _rng(seed, wl.wid, _T_CENTRE, b, h).standard_normal((ncl, d), dtype=np.float32)
-        mu *= np.float32(wl.cluster_scale)
-        new = mu[cid[rows]] + np.float32(math.sqrt(NOISE_VAR)) * new
+    return z / np.sqrt(r)[:, None, None]
+
+
+def realize_query_blocks(inputs: dict, b: int, h: int, blocks, noise_means, attempt: int,
+                         chunk: int = 0) -> None:
+    """Redraw, in place, the query tokens of the listed blocks (ascending) so that each block's
+    noise has the given mean (noise_means [len(blocks), d]).
+
+    The noise of a block with r tokens is Z - mean(Z) + noise_mean with Z i.i.d. N(0, 1) [r, d]
+    (one stream keyed by (seed, workload, b, h, attempt, chunk) for all listed blocks): for
+    i.i.d. Gaussian noise the mean is independent of the deviations from it, so drawing the mean
+    first (query_noise_means) and the deviations here gives tokens with the same distribution as
+    a direct draw.  Cluster centres (and K, V, alpha) are kept, so only these blocks' rows of the
+    block-score map move.
+    """
     import torch
 
-    inputs["Q"][b, h, torch.from_numpy(rows)] = _round(new, wl.dtype)
+    wl: Workload = inputs["workload"]
+    blk, N, d = wl.block, wl.N, wl.d
+    blocks = np.asarray(blocks, dtype=np.int64)
+    if len(blocks) == 0:
+        return
+    z = _rng(inputs["seed"], wl.wid, _T_REALIZE, b, h, int(attempt), int(chunk)).standard_normal(
+        (len(blocks), blk, d), dtype=np.float32
+    )
+    r = np.minimum(blk, N - blocks * blk)
+    valid = np.arange(blk)[None, :] < r[:, None]  # [n, blk]
+    zsum = (z * valid[..., None]).sum(axis=1)
+    noise = z - (zsum / r[:, None])[:, None, :] + np.asarray(noise_means, np.float32)[:, None, :]
+    rows = (blocks[:, None] * blk + np.arange(blk)[None, :])[valid]
+    noise = noise[valid]  # [sum r, d]
+    if wl.kind == "clustered":
+        cid, _ = _cluster_ids(wl.grid)
+        noise = _centres(inputs["seed"], wl, b, h)[cid[rows]] + np.float32(noise_std(wl)) * noise
+    inputs["Q"][b, h, torch.from_numpy(rows)] = _round(noise, wl.dtype)

@@ -1,0 +1,132 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every function that
+include/sla.h declares, sizes workspaces, and rejects bad arguments with the documented status
+before enqueuing anything."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import block_sparse_linear_02_amd as sla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sla.lib_path()):
+        from block_sparse_linear_02_amd import build
+
+        build.build()
+    return sla.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sla_\w+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    out = subprocess.run(["nm", "-D", "--defined-only", sla.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sla_\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in names:
+        assert hasattr(L, n)
+
+
+def P(B=1, H=2, N=4096, d=128, block=64, topk=8, dtype=sla.SLA_BF16):
+    return sla.Problem(B, H, N, d, block, topk, dtype)
+
+
+def test_workspace_sizes(L):
+    r = lambda p: L.sla_route_workspace_bytes(ctypes.byref(p))  # noqa: E731
+    f = lambda p, v: L.sla_forward_workspace_bytes(ctypes.byref(p), v)  # noqa: E731
+    assert r(P()) > 0 and f(P(), 0) > 0
+    assert r(P(N=8192)) > r(P()) and r(P(H=4)) > r(P())
+    for v in (0, 1, 2):
+        assert f(P(N=8192), v) > f(P(), v) and f(P(H=4), v) > f(P(), v)
+    assert f(P(), 2) > f(P(), 0) and f(P(), 1) > f(P(), 0)
+    # invalid or unsupported problems size to 0
+    assert r(P(B=0)) == 0 and r(P(block=32)) == 0 and r(P(d=96)) == 0 and r(P(topk=65)) == 0
+    assert f(P(), 3) == 0 and f(P(), -1) == 0
+    assert L.sla_route_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize(
+    "prob,status",
+    [
+        (P(B=0), sla.SLA_ERR_INVALID),
+        (P(H=-1), sla.SLA_ERR_INVALID),
+        (P(N=0), sla.SLA_ERR_INVALID),
+        (P(topk=-1), sla.SLA_ERR_INVALID),
+        (P(topk=65), sla.SLA_ERR_INVALID),  # n_b = 64
+        (P(block=32), sla.SLA_ERR_UNSUPPORTED),
+        (P(d=96), sla.SLA_ERR_UNSUPPORTED),
+        (P(dtype=7), sla.SLA_ERR_UNSUPPORTED),
+        (P(N=64 * 2049, topk=1), sla.SLA_ERR_UNSUPPORTED),  # more key blocks than the router holds
+        (P(B=1 << 20, H=1 << 12, N=1 << 17, topk=1), sla.SLA_ERR_INVALID),  # too many (b, h, block)
+    ],
+)
+def test_problem_checks(L, prob, status):
+    ws = 1 << 40
+    assert L.sla_route(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws, None) == status
+    assert L.sla_forward(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == status
+
+
+def test_pointer_and_workspace_checks(L):
+    p = P()
+    ws_r = L.sla_route_workspace_bytes(ctypes.byref(p))
+    ws_f = L.sla_forward_workspace_bytes(ctypes.byref(p), 0)
+    assert L.sla_route(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws_r, None) == sla.SLA_ERR_INVALID
+    assert L.sla_route(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws_r, None) == sla.SLA_ERR_INVALID
+    assert L.sla_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, ws_r, None) == sla.SLA_ERR_INVALID
+    assert L.sla_route(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, ws_r, None) == sla.SLA_ERR_INVALID
+    assert L.sla_route(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws_r - 1, None) == sla.SLA_ERR_WORKSPACE
+    assert L.sla_forward(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, ws_f, None) == sla.SLA_ERR_INVALID
+    assert L.sla_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws_f, None) == sla.SLA_ERR_INVALID
+    assert L.sla_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_f, None) == sla.SLA_ERR_INVALID
+    assert L.sla_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws_f, None) == sla.SLA_ERR_INVALID
+    assert L.sla_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_f - 1, None) == sla.SLA_ERR_WORKSPACE
+    # idx may be NULL only when nothing is kept
+    p0 = P(topk=0)
+    assert L.sla_forward(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws_f, None) == sla.SLA_ERR_INVALID
+    ws0 = L.sla_forward_workspace_bytes(ctypes.byref(p0), 0)
+    assert L.sla_forward(ctypes.byref(p0), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws0 - 1, None) == sla.SLA_ERR_WORKSPACE
+
+
+def test_fp8_and_mode_checks(L):
+    p = P()
+    ws = 1 << 40
+    opts_lit = sla.ForwardOpts(sla.LINEAR_MODES["literal"], None, None)
+    opts_bad = sla.ForwardOpts(7, None, None)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert L.sla_forward_fp8(ctypes.byref(P(d=64)), *args) == sla.SLA_ERR_UNSUPPORTED
+    assert L.sla_forward_fp8(ctypes.byref(P(dtype=sla.SLA_F32)), *args) == sla.SLA_ERR_UNSUPPORTED
+    assert L.sla_forward_fp8_ex(ctypes.byref(p), *args, ctypes.byref(opts_lit)) == sla.SLA_ERR_INVALID
+    assert L.sla_forward_ex(ctypes.byref(p), *args, ctypes.byref(opts_bad)) == sla.SLA_ERR_INVALID
+    assert L.sla_quantize_e4m3(ctypes.byref(P(d=64)), FAKE, FAKE, FAKE, None) == sla.SLA_ERR_UNSUPPORTED
+    assert L.sla_quantize_e4m3(ctypes.byref(p), None, FAKE, FAKE, None) == sla.SLA_ERR_INVALID
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4):
+        assert L.sla_status_string(st).decode()
+    assert L.sla_status_string(42) == b"unknown status"
+    assert L.sla_last_hip_error() == 0
+
+
+def test_binding_refuses_cpu_tensors(L):
+    x = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sla.route(x, x, torch.eye(128), torch.eye(128), 1)
+    with pytest.raises(ValueError):
+        sla.forward(x, x, x, torch.zeros((1, 1, 1, 1), dtype=torch.int32), torch.zeros((1, 1, 64)))
