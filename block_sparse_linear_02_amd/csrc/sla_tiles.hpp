@@ -40,6 +40,24 @@ struct TileLoader {
       r[u] = row < valid ? ld16(base + (size_t)row * D + ch * VEC) : i32x4{0, 0, 0, 0};
     }
   }
+  // fp32 inputs only: store the bf16 rounding (hi) and the bf16 rounding of the remainder (lo)
+  __device__ __forceinline__ void store_split(__bf16* hi, __bf16* lo, int tid) const {
+    static_assert(sizeof(T) == 4, "split staging is for fp32 inputs");
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * THREADS;
+      const int row = q / CPR, ch = q % CPR;
+      const f32x4 f = __builtin_bit_cast(f32x4, r[u]);
+      bf16x4 h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f2bf(f[e]);
+        l[e] = f2bf(f[e] - bf2f(h[e]));
+      }
+      *reinterpret_cast<bf16x4*>(hi + row * (D + kPad) + ch * VEC) = h;
+      *reinterpret_cast<bf16x4*>(lo + row * (D + kPad) + ch * VEC) = l;
+    }
+  }
   __device__ __forceinline__ void store(__bf16* lds, int tid) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {

@@ -1,25 +1,30 @@
-// sparse.hip - block-sparse softmax branch with the fused linear-branch removal and the alpha
+// sparse.hip - block-sparse softmax branch, the kept blocks' linear states, and the alpha
 // combine, on gfx950.
 //
 // Sources: SLA2 Italian summary sections 1 and 2.A and Arabic summary sections 1 and 2.alef
 // (sparse branch renormalised over the kept blocks; O = alpha O_s + (1 - alpha) O_l); SALAD
-// section 2 (ReLU feature map of the linear branch).
+// section 2 (ReLU feature map of the linear branch, over the blocks the sparse branch leaves).
 //
-// One workgroup = one query block (64 rows) of one (batch, head); two wavefronts of 32 query
-// rows each.  For every kept key block j (the router's ascending list):
-//   * K_j and V_j arrive in LDS as row-major bf16 tiles (the next tile's global loads are in
-//     flight while the current one is used);
-//   * S^T = K_j Q^T by v_mfma_f32_32x32x16_bf16 with Q held in registers (B operand), so each
-//     lane owns one query row: row max / rescale / sum stay inside a lane (plus one exchange
-//     with lane^32);
-//   * online softmax in the log2 domain, P rounded to bf16;
-//   * O_s^T += V_j^T P^T, the V operand read transposed from LDS (ds_read_b64_tr_b16);
-//   * fused linear removal: L^T = relu(K_j) relu(Q)^T on the same K registers and
-//     O_l^T -= V_j^T L^T on the same V registers, i.e. sum over kept blocks of
-//     relu(Q) h_j = (relu(Q) relu(K_j)^T) V_j without reading the d x d state h_j.
-// Epilogue: O_l numerator += relu(Q) H (H^T split bf16 hi + lo, MFMA), denominator
-// relu(q) . (Z - sum_kept z_j), O = alpha O_s / l + (1 - alpha) num / den (0 if nothing is
-// unselected or den == 0), fp32 stores; rows past N are not stored.
+// One workgroup = one query block (64 rows) of one (batch, head), four wavefronts in two roles
+// (the roles swap with the workgroup's parity so that co-resident workgroups pair a sparse and a
+// state wavefront on a SIMD):
+//   * two "sparse" wavefronts, 32 query rows each: S^T = K_j Q^T (v_mfma_f32_32x32x16_bf16, Q
+//     in registers as the B operand, so each lane owns one query row and the row statistics stay
+//     in-lane), online softmax in the log2 domain (the running maximum only moves when a row's
+//     maximum grows by more than 2^8, so rescaling is rare), P rounded to bf16, row sums taken
+//     from the bf16 P with v_dot2, and O_s^T += V_j^T P^T with the V operand read transposed
+//     from LDS (ds_read_b64_tr_b16);
+//   * two "state" wavefronts, each owning half of the d x d matrix
+//     S_sel = sum over kept blocks of h_j = relu(K_j)^T V_j, accumulated from the same LDS
+//     tiles (relu(K_j)^T and V_j both read transposed), i.e. the kept blocks' states recomputed
+//     on chip instead of read from memory.
+// K_j and V_j tiles are double-buffered in LDS (registers carry tile t+2 while tile t is used;
+// one barrier per tile); the workgroup walks the router's ascending list.
+// Epilogue: the state wavefronts form T = H - S_sel (H from the state kernel, fp32) split into
+// bf16 hi + lo in LDS, and zeta = Z - sum_kept z_j; the sparse wavefronts compute
+// num = relu(Q) T by MFMA, den = relu(q) . zeta, and O = alpha O_s / l + (1 - alpha) num / den
+// (the linear part is 0 when nothing is unselected or den == 0), fp32 stores; rows past N are
+// not stored.
 #include "sla_device.hpp"
 #include "sla_launch.hpp"
 #include "sla_tiles.hpp"
@@ -28,7 +33,7 @@ namespace sla {
 
 namespace {
 
-constexpr int kSparseThreads = 128;
+constexpr int kSparseThreads = 256;
 
 template <class T>
 __device__ __forceinline__ bf16x8 load_row8(const T* p);
@@ -44,171 +49,279 @@ __device__ __forceinline__ bf16x8 load_row8<float>(const float* p) {
                 f2bf(b[0]), f2bf(b[1]), f2bf(b[2]), f2bf(b[3])};
 }
 
+// fp32 inputs: the bf16 remainder x - bf16(x) of 8 consecutive values (0 for bf16 inputs)
+template <class T>
+__device__ __forceinline__ bf16x8 load_row8_lo(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return bf16x8{};
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = f2bf(a[e] - bf2f(f2bf(a[e])));
+      r[e + 4] = f2bf(b[e] - bf2f(f2bf(b[e])));
+    }
+    return r;
+  }
+}
+
+// sum of the 8 bf16 values of v (fp32 accumulation)
+__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {f2bf(1.f), f2bf(1.f)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2 * i], v[2 * i + 1]}, one, acc, false);
+  return acc;
+}
+
+constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before the maximum moves
+
 template <class T, int D, bool FUSED>
-__global__ __launch_bounds__(kSparseThreads) void sparse_kernel(
+__global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const __bf16* __restrict__ ht_hi, const __bf16* __restrict__ ht_lo,
     const float* __restrict__ Z, const float* __restrict__ zb, float* __restrict__ O, int N,
     int nb, int topk, float c_log2) {
-  constexpr int NS = D / 16;  // MFMA k-steps over the head dim
-  constexpr int NC = D / 32;  // 32-channel output tiles
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBlock * (D + kPad)];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[kBlock * (D + kPad)];
+  constexpr int NS = D / 16;       // MFMA k-steps over the head dim
+  constexpr int NC = D / 32;       // 32-channel output tiles
+  constexpr int RT = D / 64;       // 32-row tiles of S_sel per state wavefront
+  constexpr int PITCH = D + kPad;  // LDS row pitch (bf16 elements)
+  constexpr int TILE = kBlock * PITCH;
+  // fp32 inputs keep K as bf16 hi + lo tiles so that S = K Q^T is about fp32-accurate
+  // (Kh Qh + Kh Ql + Kl Qh); bf16 inputs are exact in one bf16 tile
+  constexpr bool SPLIT = sizeof(T) == 4;
+  constexpr int TILES = SPLIT ? 3 : 2;  // per buffer: K (hi), V, [K lo]
+  constexpr int LDS_ELEMS = (2 * TILES * TILE > 2 * D * PITCH) ? 2 * TILES * TILE : 2 * D * PITCH;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[LDS_ELEMS];
   __shared__ float zeta[D];
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, w = tid / kWave, g = lane / 32;
+  const int lane = tid % kWave, g = lane / 32;
+  const int role = (tid / kWave) ^ ((blockIdx.x & 1) ? 2 : 0);  // 0,1 sparse; 2,3 state
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / nb, qb = item % nb;
-  const int m = 32 * w + lane % 32;  // this lane's query row inside the block
-  const int row = qb * kBlock + m;
-  const bool row_ok = row < N;
   const size_t hoff = (size_t)bh * N * D;
   const int32_t* sel = idx + ((size_t)bh * nb + qb) * topk;
+  __bf16* t_hi = lds;              // epilogue: T^T [c][c'] = H^T - S_sel^T, bf16 hi part
+  __bf16* t_lo = lds + D * PITCH;  // and lo part
 
-  // Q rows as the B operand of S^T = K Q^T: k-slot 8g + jj of step s <-> channel 16s + 8g + jj
-  bf16x8 q[NS], pq[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    q[s] = row_ok ? load_row8<T>(Q + hoff + (size_t)row * D + 16 * s + 8 * g) : bf16x8{};
-    pq[s] = relu8(q[s]);
-  }
-
-  f32x16 os[NC], ol[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    os[c] = f32x16{};
-    ol[c] = f32x16{};
-  }
-  float mrun = -INFINITY, lsum = 0.f;
-  float zacc = 0.f;  // thread tid < D: sum of z_j over the kept blocks, channel tid
-
+  // Tile staging shared by both roles: every thread loads and stores its share of each tile.
+  // Both roles execute the same barriers: one after the first tile, one per tile, one before
+  // the epilogue exchange.
   TileLoader<T, D, kSparseThreads> lk, lv;
-  if (topk > 0) {
-    const int j = sel[0];
+  auto fetch = [&](int t) {
+    const int j = sel[t];
     const int nv = min(kBlock, N - j * kBlock);
     lk.load(K + hoff + (size_t)j * kBlock * D, nv, tid);
     lv.load(V + hoff + (size_t)j * kBlock * D, nv, tid);
-  }
-
-  for (int t = 0; t < topk; ++t) {
-    const int j = sel[t];
-    const int nv = min(kBlock, N - j * kBlock);
-    __syncthreads();  // the previous tile is consumed
-    lk.store(Ks, tid);
-    lv.store(Vs, tid);
-    __syncthreads();
+  };
+  auto put = [&](int t) {
+    __bf16* dst = lds + (t & 1) * TILES * TILE;
+    if constexpr (SPLIT)
+      lk.store_split(dst, dst + 2 * TILE, tid);
+    else
+      lk.store(dst, tid);
+    lv.store(dst + TILE, tid);
+  };
+  auto first = [&]() {
+    if (topk > 0) {
+      fetch(0);
+      put(0);
+      if (topk > 1) fetch(1);
+      __syncthreads();
+    }
+  };
+  // after using tile t: stage tile t + 1 into the other buffer (last read in iteration t - 1)
+  // and fetch tile t + 2, then wait for everyone
+  auto next = [&](int t) {
     if (t + 1 < topk) {
-      const int jn = sel[t + 1];
-      const int nvn = min(kBlock, N - jn * kBlock);
-      lk.load(K + hoff + (size_t)jn * kBlock * D, nvn, tid);
-      lv.load(V + hoff + (size_t)jn * kBlock * D, nvn, tid);
+      put(t + 1);
+      if (t + 2 < topk) fetch(t + 2);
     }
-    if (FUSED && tid < D) zacc += zb[((size_t)bh * nb + j) * D + tid];
+    __syncthreads();
+  };
 
-    // S^T (and L^T) for the two 32-key halves of the tile
-    f32x16 s[2], l[2];
+  if (role < 2) {
+    // ---------------- sparse role: 32 query rows ----------------
+    // Q as the B operand of S^T = K Q^T: k-slot 8g + jj of step s <-> channel 16s + 8g + jj
+    const int m = 32 * role + lane % 32;
+    const int row = qb * kBlock + m;
+    const bool row_ok = row < N;
+    bf16x8 q[NS], ql[SPLIT ? NS : 1];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
-      l[kt] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Ks + (32 * kt + lane % 32) * (D + kPad) + 16 * st + 8 * g);
-        s[kt] = mfma32(a, q[st], s[kt]);
-        if constexpr (FUSED) l[kt] = mfma32(relu8(a), pq[st], l[kt]);
-      }
+    for (int s = 0; s < NS; ++s) {
+      q[s] = row_ok ? load_row8<T>(Q + hoff + (size_t)row * D + 16 * s + 8 * g) : bf16x8{};
+      if constexpr (SPLIT) ql[s] = row_ok ? load_row8_lo<T>(Q + hoff + (size_t)row * D + 16 * s + 8 * g) : bf16x8{};
     }
-    // key of accumulator register i in half kt: 32kt + 8(i/4) + 4g + i%4
-    if (nv < kBlock) {
+    f32x16 os[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) os[c] = f32x16{};
+    float mrun = -INFINITY, lsum = 0.f;
+
+    first();
+    for (int t = 0; t < topk; ++t) {
+      const int j = sel[t];
+      const int nv = min(kBlock, N - j * kBlock);
+      const __bf16* Ks = lds + (t & 1) * TILES * TILE;
+      const __bf16* Vs = Ks + TILE;
+      f32x16 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt] = f32x16{};
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+          const int off = (32 * kt + lane % 32) * PITCH + 16 * k + 8 * g;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + off);
+          if constexpr (SPLIT) {
+            s[kt] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + 2 * TILE + off), q[k], s[kt]);
+            s[kt] = mfma32(a, ql[k], s[kt]);
+          }
+          s[kt] = mfma32(a, q[k], s[kt]);
+        }
+      }
+      // key of accumulator register i in half kt: 32kt + 8(i/4) + 4g + i%4
+      if (nv < kBlock) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + 8 * (i / 4) + 4 * g + i % 4 >= nv) s[kt][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kt + 8 * (i / 4) + 4 * g + i % 4 >= nv) s[kt][i] = -INFINITY;
-    }
-    // online softmax (log2 domain)
-    float mx = -INFINITY;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_log2;
+      if (__ballot(mx > mrun + kRescaleSlack)) {
+        const float mnew = fmaxf(mrun, mx);
+        const float corr = fast_exp2(mrun - mnew);
+        mrun = mnew;
+        lsum *= corr;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx * c_log2);
-    const float corr = fast_exp2(mrun - mnew);
-    mrun = mnew;
-    float psum = 0.f;
-    bf16x8 pb[4], lb[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float p = fast_exp2(fmaf(s[u / 2][8 * (u % 2) + jj], c_log2, -mnew));
-        psum += p;
-        pb[u][jj] = f2bf(p);
-        if constexpr (FUSED) lb[u][jj] = f2bf(-l[u / 2][8 * (u % 2) + jj]);
+        for (int c = 0; c < NC; ++c) os[c] *= corr;
       }
-    }
-    lsum = lsum * corr + psum;
-    if (__ballot(corr != 1.f)) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) os[c] *= corr;
-    }
-    // O^T += V^T P^T (and the linear removal) ; MFMA u covers keys 16u .. 16u + 15
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
+      bf16x8 pb[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8 av = tr_operand<D, 4, 8>(Vs, 16 * u, 32 * c, lane);
-        os[c] = mfma32(av, pb[u], os[c]);
-        if constexpr (FUSED) ol[c] = mfma32(av, lb[u], ol[c]);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pb[u][jj] = f2bf(fast_exp2(fmaf(s[u / 2][8 * (u % 2) + jj], c_log2, -mrun)));
+        lsum = sum8(pb[u], lsum);
       }
-  }
+      // O^T += V^T P^T ; MFMA u covers keys 16u .. 16u + 15
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) os[c] = mfma32(tr_operand<D, 4, 8>(Vs, 16 * u, 32 * c, lane), pb[u], os[c]);
+      next(t);
+    }
+    __syncthreads();  // the state role has written T and zeta
 
-  // ---- epilogue ----
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  const float inv_l = topk > 0 ? 1.f / ltot : 0.f;
-  float inv_den = 0.f;
-  if constexpr (FUSED) {
-    if (tid < D) zeta[tid] = Z[(size_t)bh * D + tid] - zacc;
-    __syncthreads();
-    // numerator += relu(Q) H : A = H^T rows (V channel c), k-slots = K channel c'
-    const __bf16* hh = ht_hi + (size_t)bh * D * D;
-    const __bf16* hl = ht_lo + (size_t)bh * D * D;
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float inv_l = topk > 0 ? 1.f / ltot : 0.f;
+    f32x16 num[NC];
+    float inv_den = 0.f;
+    if constexpr (FUSED) {
+      // num^T[c][m] = sum_c' T^T[c][c'] relu(Q)[m][c'] (lo then hi part)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) num[c] = f32x16{};
+      float den = 0.f;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const bf16x8 pq = relu8(q[k]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int off = (32 * c + lane % 32) * PITCH + 16 * k + 8 * g;
+          num[c] = mfma32(*reinterpret_cast<const bf16x8*>(t_lo + off), pq, num[c]);
+          num[c] = mfma32(*reinterpret_cast<const bf16x8*>(t_hi + off), pq, num[c]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[16 * k + 8 * g + jj];
+      }
+      den += __shfl_xor(den, 32);
+      inv_den = (topk < nb && den != 0.f) ? 1.f / den : 0.f;
+    }
+    if (!row_ok) return;
+    const float a = alpha[(size_t)bh * N + row];
+    const float ws = a * inv_l, wl = (1.f - a) * inv_den;
+    float* orow = O + hoff + (size_t)row * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const size_t off = (size_t)(32 * c + lane % 32) * D + 16 * st + 8 * g;
-        ol[c] = mfma32(*reinterpret_cast<const bf16x8*>(hl + off), pq[st], ol[c]);
-        ol[c] = mfma32(*reinterpret_cast<const bf16x8*>(hh + off), pq[st], ol[c]);
+      for (int qd = 0; qd < 4; ++qd) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = os[c][4 * qd + e] * ws;
+          v[e] = FUSED ? fmaf(num[c][4 * qd + e], wl, x) : x;
+        }
+        *reinterpret_cast<f32x4*>(orow + 32 * c + 8 * qd + 4 * g) = v;
       }
-    float den = 0.f;
+  } else {
+    // ---------------- state role: rows c' = cp0 .. cp0 + D/2 of S_sel ----------------
+    const int cp0 = (role & 1) * (D / 2);
+    const int st = tid % 128;  // index among the role's 128 threads (channel of z)
+    f32x16 acc[RT][NC];
 #pragma unroll
-    for (int st = 0; st < NS; ++st)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[st][jj]) * zeta[16 * st + 8 * g + jj];
-    den += __shfl_xor(den, 32);
-    inv_den = (topk < nb && den != 0.f) ? 1.f / den : 0.f;
-  }
-  if (!row_ok) return;
-  const float a = alpha[(size_t)bh * N + row];
-  const float ws = a * inv_l, wl = (1.f - a) * inv_den;
-  float* orow = O + hoff + (size_t)row * D;
+      for (int c = 0; c < NC; ++c) acc[r][c] = f32x16{};
+    float zacc = 0.f;
+
+    first();
+    for (int t = 0; t < topk; ++t) {
+      if constexpr (FUSED) {
+        const int j = sel[t];
+        const __bf16* Ks = lds + (t & 1) * TILES * TILE;
+        const __bf16* Vs = Ks + TILE;
+        if (st < D) zacc += zb[((size_t)bh * nb + j) * D + st];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+        for (int ks = 0; ks < kBlock / 16; ++ks) {
+          bf16x8 a[RT], b[NC];
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      f32x4 v;
+          for (int r = 0; r < RT; ++r) a[r] = relu8(tr_operand<D, 8, 4>(Ks, 16 * ks, cp0 + 32 * r, lane));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = os[c][4 * qd + e] * ws;
-        v[e] = FUSED ? fmaf(ol[c][4 * qd + e], wl, x) : x;
+          for (int c = 0; c < NC; ++c) b[c] = tr_operand<D, 8, 4>(Vs, 16 * ks, 32 * c, lane);
+#pragma unroll
+          for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[r][c] = mfma32(a[r], b[c], acc[r][c]);
+        }
       }
-      *reinterpret_cast<f32x4*>(orow + 32 * c + 8 * qd + 4 * g) = v;
+      next(t);
     }
+    if constexpr (FUSED) {
+      const __bf16* hh = ht_hi + (size_t)bh * D * D;
+      const __bf16* hl = ht_lo + (size_t)bh * D * D;
+      // acc[r][c]: lane holds column c (V channel) = 32c + lane%32 and rows
+      // c' = cp0 + 32r + 8(i/4) + 4g + i%4
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int cc = 32 * c + lane % 32;
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int cp = cp0 + 32 * r + 8 * qd + 4 * g;
+            const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(hh + (size_t)cc * D + cp);
+            const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(hl + (size_t)cc * D + cp);
+            bf16x4 vh, vl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float tv = (bf2f(h1[e]) + bf2f(h0[e])) - acc[r][c][4 * qd + e];
+              vh[e] = f2bf(tv);
+              vl[e] = f2bf(tv - bf2f(vh[e]));
+            }
+            *reinterpret_cast<bf16x4*>(t_hi + cc * PITCH + cp) = vh;
+            *reinterpret_cast<bf16x4*>(t_lo + cc * PITCH + cp) = vl;
+          }
+        }
+      if (st < D) zeta[st] = Z[(size_t)bh * D + st] - zacc;
+    }
+    __syncthreads();
+  }
 }
 
 template <class T, int D>
