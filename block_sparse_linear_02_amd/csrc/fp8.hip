@@ -113,8 +113,8 @@ __global__ __launch_bounds__(kF8Threads) void sparse_fp8_kernel(
   static_assert(D == 128, "the fp8 kernel is compiled for d = 128");
   constexpr int NS = D / 16, NC = D / 32, N8 = D / 64;
   constexpr int P8 = D + 16;  // LDS row pitch of the fp8 K tile in bytes
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBlock * (D + kPad)];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[kBlock * (D + kPad)];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[TileLayout<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[TileLayout<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) uint8_t K8s[kBlock * P8];
   __shared__ __attribute__((aligned(16))) uint8_t V8s[D * (kBlock + 16)];
   __shared__ float zeta[D];
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kF8Threads) void sparse_fp8_kernel(
       l[kt] = f32x16{};
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kt + lane % 32) * (D + kPad) + 16 * st + 8 * g);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + TileLayout<D>::off(32 * kt + lane % 32, 16 * st + 8 * g));
         l[kt] = mfma32(relu8(a), pq[st], l[kt]);
       }
     }

@@ -30,8 +30,8 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
     float* __restrict__ zb, float* __restrict__ h_part, float* __restrict__ z_part,
     float* __restrict__ hj) {
   constexpr int NT = D / 64;  // 32x32 output tiles per wave per dimension (D=128: 2, D=64: 1)
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBlock * (D + kPad)];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[kBlock * (D + kPad)];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[TileLayout<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[TileLayout<D>::ELEMS];
   __shared__ float zred[kStateThreads / D][D];
 
   const int tid = threadIdx.x;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
       float s = 0.f;
 #pragma unroll 8
       for (int n = part * (kBlock / PARTS); n < (part + 1) * (kBlock / PARTS); ++n)
-        s += fmaxf(bf2f(Ks[n * (D + kPad) + c]), 0.f);
+        s += fmaxf(bf2f(Ks[TileLayout<D>::off(n, c)]), 0.f);
       zred[part][c] = s;
     }
     if constexpr (LITERAL) {

@@ -61,6 +61,25 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// max / sum of a value and its copy in lane l ^ 32, in every lane (v_permlane32_swap: with
+// both operands equal, the two results hold the lower and the upper half-wave values)
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Asynchronous 16-byte global -> LDS copy (gfx950 global_load_lds_dwordx4): lane i's 16 bytes
+// land at lds_wave_base + 16 i, the 64 lanes of a wavefront fill 1 KB contiguously.  Completion
+// is tracked by vmcnt (wait_vmem() before the barrier that publishes the data).
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
+
 // Wave-wide reductions over all 64 lanes.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -1,16 +1,35 @@
 // sla_tiles.hpp - 64-token tile staging shared by the gfx950 kernels of libsla.
 //
 // A tile is 64 consecutive tokens x D channels of one (batch, head).  It travels HBM ->
-// registers (16-byte coalesced loads, issued one tile ahead) -> LDS (row-major bf16, each row
-// padded by kPad elements so that row-wise 16-byte reads of 16 consecutive rows hit distinct
-// banks).  fp32 inputs are rounded to bf16 (nearest even) on the way into LDS.
+// registers (16-byte coalesced loads, issued ahead of use) -> LDS as row-major bf16 (see
+// TileLayout).  fp32 inputs are rounded to bf16 (nearest even) on the way into LDS.
 #pragma once
 
 #include "sla_device.hpp"
 
 namespace sla {
 
-constexpr int kPad = 8;  // bf16 elements of padding per LDS row
+constexpr int kPad = 8;  // bf16 elements of padding per LDS row (d = 64 tiles)
+
+// Where element (row, col) of a 64-row tile lives in LDS (bf16 elements from the tile base).
+// d = 128: 256-byte rows without padding, the 16-byte chunk c of row r stored at chunk
+// c ^ f(r) with f(r) = 4 (r & 3) + ((r >> 2) & 3).  Then 16 consecutive rows reading one chunk
+// (row-wise 16-byte MFMA operand reads) and 4 consecutive rows x 4 consecutive chunks (the
+// transposed ds_read_b64_tr_b16 reads of two 16-lane groups) each touch 16 distinct 16-byte
+// bank groups.  d = 64: rows padded by kPad elements.
+template <int D>
+struct TileLayout {
+  static constexpr int PITCH = D == 128 ? D : D + kPad;
+  static constexpr int ELEMS = kBlock * PITCH;
+  static __device__ __forceinline__ int off(int row, int col) {
+    if constexpr (D == 128) {
+      const int f = 4 * (row & 3) + ((row >> 2) & 3);
+      return row * PITCH + (((col >> 3) ^ f) << 3) + (col & 7);
+    } else {
+      return row * PITCH + col;
+    }
+  }
+};
 
 template <class T>
 struct Vec16;  // elements of one 16-byte global load
@@ -54,8 +73,8 @@ struct TileLoader {
         h[e] = f2bf(f[e]);
         l[e] = f2bf(f[e] - bf2f(h[e]));
       }
-      *reinterpret_cast<bf16x4*>(hi + row * (D + kPad) + ch * VEC) = h;
-      *reinterpret_cast<bf16x4*>(lo + row * (D + kPad) + ch * VEC) = l;
+      *reinterpret_cast<bf16x4*>(hi + TileLayout<D>::off(row, ch * VEC)) = h;
+      *reinterpret_cast<bf16x4*>(lo + TileLayout<D>::off(row, ch * VEC)) = l;
     }
   }
   __device__ __forceinline__ void store(__bf16* lds, int tid) const {
@@ -63,7 +82,7 @@ struct TileLoader {
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * THREADS;
       const int row = q / CPR, ch = q % CPR;
-      __bf16* dst = lds + row * (D + kPad) + ch * VEC;
+      __bf16* dst = lds + TileLayout<D>::off(row, ch * VEC);
       if constexpr (sizeof(T) == 2) {
         *reinterpret_cast<i32x4*>(dst) = r[u];
       } else {
@@ -75,6 +94,24 @@ struct TileLoader {
   }
 };
 
+// Direct (register-free) copy of a full 64-row bf16 tile with D = 128 into the swizzled
+// TileLayout by THREADS/64 wavefronts: wavefront w fills rows 4(NW u + w) .. +3 for u < 16/NW,
+// 1 KB per load, lane i taking physical chunk i % 16 of row i / 16, i.e. logical chunk
+// (i % 16) ^ f(row) of the source row.  Only for tiles with all 64 rows valid.
+template <int THREADS>
+__device__ __forceinline__ void load_tile_direct(const __bf16* src, __bf16* tile, int tid) {
+  constexpr int NW = THREADS / 64;
+  const int w = tid / 64, lane = tid % 64;
+#pragma unroll
+  for (int u = 0; u < 16 / NW; ++u) {
+    const int r0 = 4 * (NW * u + w);
+    const int row = r0 + lane / 16;
+    const int f = 4 * (row & 3) + ((row >> 2) & 3);
+    const int chunk = (lane % 16) ^ f;
+    load_lds16(src + row * 128 + chunk * 8, tile + r0 * 128);
+  }
+}
+
 __device__ __forceinline__ bf16x8 join_tr(i16x4 a, i16x4 b) {
   i32x4 v = {(int)((u32)(uint16_t)a[0] | ((u32)(uint16_t)a[1] << 16)),
              (int)((u32)(uint16_t)a[2] | ((u32)(uint16_t)a[3] << 16)),
@@ -83,7 +120,7 @@ __device__ __forceinline__ bf16x8 join_tr(i16x4 a, i16x4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Transposed MFMA operand from a row-major [64][D + kPad] LDS tile: lane l (g = l/32) receives
+// Transposed MFMA operand from a 64-row LDS tile (TileLayout): lane l (g = l/32) receives
 // column col0 + l%32 at the rows row0 + r_off + e and row0 + r_off + gap + e (e = 0..3) where
 // r_off = step * g.  step = 8, gap = 4 gives rows row0 + 8g + 0..7; step = 4, gap = 8 gives
 // rows row0 + 4g + {0..3, 8..11} (the key order of a 32x32 MFMA accumulator).
@@ -91,8 +128,10 @@ template <int D, int STEP, int GAP>
 __device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int row0, int col0, int lane) {
   const int h = lane / 16, L = lane % 16;
   const int g = h / 2, cs = h % 2;
-  const __bf16* p = tile + (row0 + STEP * g + L / 4) * (D + kPad) + col0 + 16 * cs + 4 * (L % 4);
-  return join_tr(lds_read_tr16(p), lds_read_tr16(p + GAP * (D + kPad)));
+  const int r = row0 + STEP * g + L / 4;
+  const int c = col0 + 16 * cs + 4 * (L % 4);
+  return join_tr(lds_read_tr16(tile + TileLayout<D>::off(r, c)),
+                 lds_read_tr16(tile + TileLayout<D>::off(r + GAP, c)));
 }
 
 // Map a workgroup id to a logical work item so that each of the 8 XCDs (which receive

@@ -87,8 +87,8 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
   constexpr int NS = D / 16;       // MFMA k-steps over the head dim
   constexpr int NC = D / 32;       // 32-channel output tiles
   constexpr int RT = D / 64;       // 32-row tiles of S_sel per state wavefront
-  constexpr int PITCH = D + kPad;  // LDS row pitch (bf16 elements)
-  constexpr int TILE = kBlock * PITCH;
+  constexpr int PITCH = D + kPad;  // row pitch of the epilogue's T^T array (bf16 elements)
+  constexpr int TILE = TileLayout<D>::ELEMS;
   // fp32 inputs keep K as bf16 hi + lo tiles so that S = K Q^T is about fp32-accurate
   // (Kh Qh + Kh Ql + Kl Qh); bf16 inputs are exact in one bf16 tile
   constexpr bool SPLIT = sizeof(T) == 4;
@@ -107,39 +107,60 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
   __bf16* t_hi = lds;              // epilogue: T^T [c][c'] = H^T - S_sel^T, bf16 hi part
   __bf16* t_lo = lds + D * PITCH;  // and lo part
 
-  // Tile staging shared by both roles: every thread loads and stores its share of each tile.
-  // Both roles execute the same barriers: one after the first tile, one per tile, one before
-  // the epilogue exchange.
-  TileLoader<T, D, kSparseThreads> lk, lv;
-  auto fetch = [&](int t) {
+  // Tile staging shared by both roles: every thread moves its share of each tile.  bf16 tiles
+  // with d = 128 and all 64 rows valid go HBM -> LDS directly (no registers), issued at the
+  // start of the iteration that uses the other buffer; other tiles (fp32 inputs, d = 64, the
+  // short last block) go through registers with zero fill, stored right away.  The state
+  // role's z_j travels with the tile.  Both roles execute the same barriers: one after the
+  // first tile, one per tile, one before the epilogue exchange.
+  constexpr bool DIRECT = sizeof(T) == 2 && D == 128;
+  const bool z_lane = FUSED && role >= 2 && (tid % 128) < D;
+  float z_in = 0.f;        // z_j of the tile being staged (state role)
+  int nv_next = kBlock;    // valid rows of the tile being staged
+  float zacc = 0.f;        // state role: sum of z_j over the staged kept blocks
+  auto stage = [&](int t) {
     const int j = sel[t];
     const int nv = min(kBlock, N - j * kBlock);
-    lk.load(K + hoff + (size_t)j * kBlock * D, nv, tid);
-    lv.load(V + hoff + (size_t)j * kBlock * D, nv, tid);
-  };
-  auto put = [&](int t) {
     __bf16* dst = lds + (t & 1) * TILES * TILE;
-    if constexpr (SPLIT)
-      lk.store_split(dst, dst + 2 * TILE, tid);
-    else
-      lk.store(dst, tid);
-    lv.store(dst + TILE, tid);
+    const T* ksrc = K + hoff + (size_t)j * kBlock * D;
+    const T* vsrc = V + hoff + (size_t)j * kBlock * D;
+    if (z_lane) z_in = zb[((size_t)bh * nb + j) * D + tid % 128];
+    nv_next = nv;
+    if (DIRECT && nv == kBlock) {
+      if constexpr (DIRECT) {
+        load_tile_direct<kSparseThreads>(ksrc, dst, tid);
+        load_tile_direct<kSparseThreads>(vsrc, dst + TILE, tid);
+      }
+    } else {
+      TileLoader<T, D, kSparseThreads> lk, lv;
+      lk.load(ksrc, nv, tid);
+      lv.load(vsrc, nv, tid);
+      if constexpr (SPLIT)
+        lk.store_split(dst, dst + 2 * TILE, tid);
+      else
+        lk.store(dst, tid);
+      lv.store(dst + TILE, tid);
+    }
   };
+  int nv_cur = kBlock;
   auto first = [&]() {
     if (topk > 0) {
-      fetch(0);
-      put(0);
-      if (topk > 1) fetch(1);
+      stage(0);
+      zacc += z_in;
+      nv_cur = nv_next;
+      wait_vmem();
       __syncthreads();
     }
   };
-  // after using tile t: stage tile t + 1 into the other buffer (last read in iteration t - 1)
-  // and fetch tile t + 2, then wait for everyone
-  auto next = [&](int t) {
-    if (t + 1 < topk) {
-      put(t + 1);
-      if (t + 2 < topk) fetch(t + 2);
-    }
+  // start staging tile t + 1 into the other buffer (last read in iteration t - 1)
+  auto begin = [&](int t) {
+    if (t + 1 < topk) stage(t + 1);
+  };
+  // after using tile t: publish tile t + 1
+  auto end = [&](int t) {
+    if (t + 1 < topk) zacc += z_in;
+    nv_cur = nv_next;
+    wait_vmem();
     __syncthreads();
   };
 
@@ -162,25 +183,37 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
 
     first();
     for (int t = 0; t < topk; ++t) {
-      const int j = sel[t];
-      const int nv = min(kBlock, N - j * kBlock);
+      const int nv = nv_cur;
+      begin(t);
       const __bf16* Ks = lds + (t & 1) * TILES * TILE;
       const __bf16* Vs = Ks + TILE;
+      // K operands of both 32-key halves, issued together ahead of their MFMAs
+      bf16x8 ka[2][NS];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+          ka[kt][k] = *reinterpret_cast<const bf16x8*>(Ks + TileLayout<D>::off(32 * kt + lane % 32, 16 * k + 8 * g));
       f32x16 s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         s[kt] = f32x16{};
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-          const int off = (32 * kt + lane % 32) * PITCH + 16 * k + 8 * g;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + off);
           if constexpr (SPLIT) {
+            const int off = TileLayout<D>::off(32 * kt + lane % 32, 16 * k + 8 * g);
             s[kt] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + 2 * TILE + off), q[k], s[kt]);
-            s[kt] = mfma32(a, ql[k], s[kt]);
+            s[kt] = mfma32(ka[kt][k], ql[k], s[kt]);
           }
-          s[kt] = mfma32(a, q[k], s[kt]);
+          s[kt] = mfma32(ka[kt][k], q[k], s[kt]);
         }
       }
+      // V operands for PV: independent of P, so their LDS latency hides under the softmax
+      bf16x8 va[NC][4];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) va[c][u] = tr_operand<D, 4, 8>(Vs, 16 * u, 32 * c, lane);
       // key of accumulator register i in half kt: 32kt + 8(i/4) + 4g + i%4
       if (nv < kBlock) {
 #pragma unroll
@@ -194,7 +227,7 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_log2;
+      mx = xor32_max(mx) * c_log2;
       if (__ballot(mx > mrun + kRescaleSlack)) {
         const float mnew = fmaxf(mrun, mx);
         const float corr = fast_exp2(mrun - mnew);
@@ -214,12 +247,12 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) os[c] = mfma32(tr_operand<D, 4, 8>(Vs, 16 * u, 32 * c, lane), pb[u], os[c]);
-      next(t);
+        for (int u = 0; u < 4; ++u) os[c] = mfma32(va[c][u], pb[u], os[c]);
+      end(t);
     }
     __syncthreads();  // the state role has written T and zeta
 
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float ltot = xor32_sum(lsum);
     const float inv_l = topk > 0 ? 1.f / ltot : 0.f;
     f32x16 num[NC];
     float inv_den = 0.f;
@@ -240,7 +273,7 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[16 * k + 8 * g + jj];
       }
-      den += __shfl_xor(den, 32);
+      den = xor32_sum(den);
       inv_den = (topk < nb && den != 0.f) ? 1.f / den : 0.f;
     }
     if (!row_ok) return;
@@ -268,29 +301,34 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
     for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[r][c] = f32x16{};
-    float zacc = 0.f;
 
     first();
     for (int t = 0; t < topk; ++t) {
+      begin(t);
       if constexpr (FUSED) {
-        const int j = sel[t];
         const __bf16* Ks = lds + (t & 1) * TILES * TILE;
         const __bf16* Vs = Ks + TILE;
-        if (st < D) zacc += zb[((size_t)bh * nb + j) * D + st];
+        // operands of key step ks + 1 are read while the MFMAs of step ks run
+        bf16x8 a[2][RT], b[2][NC];
+        auto rd = [&](int ks, int buf) {
+#pragma unroll
+          for (int r = 0; r < RT; ++r) a[buf][r] = tr_operand<D, 8, 4>(Ks, 16 * ks, cp0 + 32 * r, lane);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) b[buf][c] = tr_operand<D, 8, 4>(Vs, 16 * ks, 32 * c, lane);
+        };
+        rd(0, 0);
 #pragma unroll
         for (int ks = 0; ks < kBlock / 16; ++ks) {
-          bf16x8 a[RT], b[NC];
+          if (ks + 1 < kBlock / 16) rd(ks + 1, (ks + 1) & 1);
 #pragma unroll
-          for (int r = 0; r < RT; ++r) a[r] = relu8(tr_operand<D, 8, 4>(Ks, 16 * ks, cp0 + 32 * r, lane));
+          for (int r = 0; r < RT; ++r) {
+            const bf16x8 ar = relu8(a[ks & 1][r]);
 #pragma unroll
-          for (int c = 0; c < NC; ++c) b[c] = tr_operand<D, 8, 4>(Vs, 16 * ks, 32 * c, lane);
-#pragma unroll
-          for (int r = 0; r < RT; ++r)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) acc[r][c] = mfma32(a[r], b[c], acc[r][c]);
+            for (int c = 0; c < NC; ++c) acc[r][c] = mfma32(ar, b[ks & 1][c], acc[r][c]);
+          }
         }
       }
-      next(t);
+      end(t);
     }
     if constexpr (FUSED) {
       const __bf16* hh = ht_hi + (size_t)bh * D * D;
