@@ -11,12 +11,16 @@
 //                     division), code = e4m3_rne(min(max(x * inv, -448), 448)).  Row-major
 //                     codes, or (for V) a per-block transposed layout [d][64] whose key order
 //                     matches the P operand of the PV MFMA.
-//   sparse_fp8_kernel one workgroup per query block, two wavefronts of 32 query rows.
-//                     Pass 1 walks the kept blocks with S = Q8 K8^T (v_mfma ... f8f6f4,
-//                     32x32x64) to get each row's exact maximum; pass 2 recomputes S, forms
-//                     P = exp(S - max), the tile maximum across both wavefronts, P8, and
-//                     O_s += (P8 V8) sP sV on fp8 MFMA, while the bf16 linear removal
-//                     (relu(Q) relu(K_j)^T V_j) and the combine run as in the bf16 kernel.
+//   sparse_fp8_kernel one workgroup per query block, four wavefronts in the two roles of the
+//                     bf16 kernel.  Pass 1 over the kept blocks: the sparse wavefronts
+//                     compute S = Q8 K8^T (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales; K8
+//                     fetched into registers one tile ahead) for each row's exact maximum,
+//                     while the state wavefronts accumulate the kept blocks' relu(K_j)^T V_j
+//                     from bf16 tiles (direct-to-LDS, as in the bf16 kernel).  Pass 2: K8 and
+//                     V8^T tiles go straight into swizzled LDS; the sparse wavefronts recompute
+//                     S, form P = exp(S - max), exchange the 64x64 tile maximum, quantise P and
+//                     accumulate (P8 V8) sP sV by fp8 MFMA.  Epilogue and combine as in the
+//                     bf16 kernel.
 #include "sla_device.hpp"
 #include "sla_launch.hpp"
 #include "sla_tiles.hpp"
@@ -98,10 +102,21 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16* __restrict_
   }
 }
 
-constexpr int kF8Threads = 128;
+constexpr int kF8Threads = 256;
+
+// LDS layouts of the pass-2 tiles:
+//   K8  [64 keys][128 B]: 16-byte unit u of row r at unit u ^ ((r >> 1) & 7)
+//   V8t [128 channels][64 B]: 16-byte unit u of row c at unit u ^ ((c >> 2) & 3)
+// so that 16 consecutive rows reading one unit hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int k8_off(int r, int b) { return r * 128 + ((((b >> 4) ^ ((r >> 1) & 7))) << 4) + (b & 15); }
+__device__ __forceinline__ int v8_off(int c, int b) { return c * 64 + ((((b >> 4) ^ ((c >> 2) & 3))) << 4) + (b & 15); }
+
+__device__ __forceinline__ i32x8 join8(i32x4 a, i32x4 b) {
+  return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
 template <int D>
-__global__ __launch_bounds__(kF8Threads) void sparse_fp8_kernel(
+__global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ v8t, const float* __restrict__ sq,
@@ -111,209 +126,312 @@ __global__ __launch_bounds__(kF8Threads) void sparse_fp8_kernel(
     const float* __restrict__ Z, const float* __restrict__ zb, float* __restrict__ O, int N,
     int nb, int topk, float c_log2) {
   static_assert(D == 128, "the fp8 kernel is compiled for d = 128");
-  constexpr int NS = D / 16, NC = D / 32, N8 = D / 64;
-  constexpr int P8 = D + 16;  // LDS row pitch of the fp8 K tile in bytes
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[TileLayout<D>::ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[TileLayout<D>::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint8_t K8s[kBlock * P8];
-  __shared__ __attribute__((aligned(16))) uint8_t V8s[D * (kBlock + 16)];
+  constexpr int NS = D / 16, NC = D / 32, RT = D / 64, N8 = D / 64;
+  constexpr int TILE = TileLayout<D>::ELEMS;  // bf16 elements of a K or V tile
+  constexpr int PITCH = D + kPad;             // epilogue T^T pitch
+  constexpr int K8B = kBlock * D;             // bytes of a K8 tile
+  constexpr int LDS_ELEMS = (4 * TILE > 2 * D * PITCH) ? 4 * TILE : 2 * D * PITCH;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[LDS_ELEMS];
   __shared__ float zeta[D];
   __shared__ float tmax_x[2];
+  uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, w = tid / kWave, g = lane / 32;
+  const int lane = tid % kWave, g = lane / 32, w = tid / kWave;
+  const int role = w ^ ((blockIdx.x & 1) ? 2 : 0);  // 0,1 sparse; 2,3 state
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / nb, qb = item % nb;
-  const int m = 32 * w + lane % 32;
-  const int row = qb * kBlock + m;
-  const bool row_ok = row < N;
   const size_t hoff = (size_t)bh * N * D;
   const int32_t* sel = idx + ((size_t)bh * nb + qb) * topk;
   const float sqi = sq[(size_t)bh * nb + qb];
+  __bf16* t_hi = lds;
+  __bf16* t_lo = lds + D * PITCH;
 
-  // bf16 Q (linear branch) and e4m3 Q (sparse branch) as B operands
-  bf16x8 pq[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-    pq[s] = relu8(row_ok ? *reinterpret_cast<const bf16x8*>(Q + hoff + (size_t)row * D + 16 * s + 8 * g)
-                         : bf16x8{});
-  i32x8 qf[N8];
-#pragma unroll
-  for (int s = 0; s < N8; ++s) {
-    if (row_ok) {
-      const i32x4* p = reinterpret_cast<const i32x4*>(q8 + hoff + (size_t)row * D + 64 * s + 32 * g);
-      const i32x4 a = p[0], b = p[1];
-      qf[s] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  // ---- pass 1 staging: bf16 K, V tiles (state role's linear states) ----
+  const bool z_lane = role >= 2 && (tid % 128) < D;
+  float z_in = 0.f, zacc = 0.f;
+  auto stage1 = [&](int t) {
+    const int j = sel[t];
+    const int nv = min(kBlock, N - j * kBlock);
+    __bf16* dst = lds + (t & 1) * 2 * TILE;
+    const __bf16* ksrc = K + hoff + (size_t)j * kBlock * D;
+    const __bf16* vsrc = V + hoff + (size_t)j * kBlock * D;
+    if (z_lane) z_in = zb[((size_t)bh * nb + j) * D + tid % 128];
+    if (nv == kBlock) {
+      load_tile_direct<kF8Threads>(ksrc, dst, tid);
+      load_tile_direct<kF8Threads>(vsrc, dst + TILE, tid);
     } else {
-      qf[s] = i32x8{};
-    }
-  }
-
-  // load an fp8 K tile (row-major, pitch P8) into LDS: 64 rows x D bytes
-  auto load_k8 = [&](int j) {
-    const uint8_t* src = k8 + hoff + (size_t)j * kBlock * D;
-    const int nv = min(kBlock, N - j * kBlock);
-    for (int q = tid; q < kBlock * D / 16; q += kF8Threads) {
-      const int r = q / (D / 16), ch = q % (D / 16);
-      const i32x4 v = r < nv ? *reinterpret_cast<const i32x4*>(src + (size_t)r * D + ch * 16)
-                             : i32x4{0, 0, 0, 0};
-      *reinterpret_cast<i32x4*>(K8s + r * P8 + ch * 16) = v;
+      TileLoader<__bf16, D, kF8Threads> lk, lv;
+      lk.load(ksrc, nv, tid);
+      lv.load(vsrc, nv, tid);
+      lk.store(dst, tid);
+      lv.store(dst + TILE, tid);
     }
   };
-  auto s_tile = [&](f32x16* s) {
+  // ---- pass 2 staging: K8 and V8^T tiles (sparse role), straight into the swizzled layouts ----
+  auto stage2 = [&](int t) {
+    const int j = sel[t];
+    const int nv = min(kBlock, N - j * kBlock);
+    uint8_t* dst = lds8 + (t & 1) * 2 * K8B;
+    const uint8_t* ksrc = k8 + hoff + (size_t)j * kBlock * D;
+    const uint8_t* vsrc = v8t + ((size_t)bh * nb + j) * D * kBlock;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < N8; ++st) {
-        const i32x4* p = reinterpret_cast<const i32x4*>(K8s + (32 * kt + lane % 32) * P8 + 64 * st + 32 * g);
-        const i32x4 a = p[0], b = p[1];
-        s[kt] = mfma_f8(i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}, qf[st], s[kt]);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int r0 = 8 * (2 * w + u);  // 8 K8 rows of 128 B per wave load
+      const int r = r0 + lane / 8;
+      const int unit = (lane % 8) ^ ((r >> 1) & 7);
+      load_lds16(ksrc + (size_t)min(r, nv - 1) * D + unit * 16, dst + r0 * 128);
+      const int c0 = 16 * (2 * w + u);  // 16 V8^T rows of 64 B per wave load
+      const int c = c0 + lane / 4;
+      const int vunit = (lane % 4) ^ ((c >> 2) & 3);
+      load_lds16(vsrc + (size_t)c * kBlock + vunit * 16, dst + K8B + c0 * 64);
     }
   };
 
-  // ---- pass 1: exact row maximum of S (log2 units) over all kept keys ----
-  float mrow = -INFINITY;
-  for (int t = 0; t < topk; ++t) {
-    const int j = sel[t];
-    const int nv = min(kBlock, N - j * kBlock);
-    __syncthreads();
-    load_k8(j);
-    __syncthreads();
-    f32x16 s[2];
-    s_tile(s);
-    const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
+  if (role < 2) {
+    // ================= sparse role: 32 query rows =================
+    const int m = 32 * role + lane % 32;
+    const int row = qb * kBlock + m;
+    const bool row_ok = row < N;
+    i32x8 qf[N8];  // e4m3 Q as the B operand: k-slot 32g + b of step s <-> channel 64s + 32g + b
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (32 * kt + 8 * (i / 4) + 4 * g + i % 4 < nv) mrow = fmaxf(mrow, s[kt][i] * sc);
-  }
-  mrow = fmaxf(mrow, __shfl_xor(mrow, 32));
-
-  // ---- pass 2 ----
-  f32x16 os[NC], ol[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    os[c] = f32x16{};
-    ol[c] = f32x16{};
-  }
-  float lsum = 0.f, zacc = 0.f;
-  TileLoader<__bf16, D, kF8Threads> lk, lv;
-  for (int t = 0; t < topk; ++t) {
-    const int j = sel[t];
-    const int nv = min(kBlock, N - j * kBlock);
-    lk.load(K + hoff + (size_t)j * kBlock * D, nv, tid);
-    lv.load(V + hoff + (size_t)j * kBlock * D, nv, tid);
-    __syncthreads();
-    load_k8(j);
-    {  // transposed V8 block [D][64] -> LDS rows padded to 80 bytes
-      const uint8_t* src = v8t + ((size_t)bh * nb + j) * D * kBlock;
-      for (int q = tid; q < D * kBlock / 16; q += kF8Threads) {
-        const int c = q / (kBlock / 16), ch = q % (kBlock / 16);
-        *reinterpret_cast<i32x4*>(V8s + c * (kBlock + 16) + ch * 16) =
-            *reinterpret_cast<const i32x4*>(src + (size_t)c * kBlock + ch * 16);
+    for (int s = 0; s < N8; ++s) {
+      if (row_ok) {
+        const i32x4* p = reinterpret_cast<const i32x4*>(q8 + hoff + (size_t)row * D + 64 * s + 32 * g);
+        qf[s] = join8(p[0], p[1]);
+      } else {
+        qf[s] = i32x8{};
       }
     }
-    lk.store(Ks, tid);
-    lv.store(Vs, tid);
-    if (tid < D) zacc += zb[((size_t)bh * nb + j) * D + tid];
-    __syncthreads();
-
-    f32x16 s[2];
-    s_tile(s);
-    const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
-    float p[2][16];
-    float pmax = 0.f;
+    // pass 1: exact row maximum of S (log2 units); K8 operands come straight from memory, one
+    // tile ahead (rows past a short block's end re-read its last row: those keys are masked)
+    auto k8_regs = [&](int t, i32x8 (&kr)[2][N8]) {
+      const int j = sel[t];
+      const int nv = min(kBlock, N - j * kBlock);
+      const uint8_t* src = k8 + hoff + (size_t)j * kBlock * D;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool ok = row_ok && 32 * kt + 8 * (i / 4) + 4 * g + i % 4 < nv;
-        p[kt][i] = ok ? fast_exp2(fmaf(s[kt][i], sc, -mrow)) : 0.f;
-        lsum += p[kt][i];
-        pmax = fmaxf(pmax, p[kt][i]);
-      }
-    pmax = wave_max(pmax);
-    if (lane == 0) tmax_x[w] = pmax;
-    // linear removal on the bf16 tiles (independent of the tile maximum)
-    f32x16 l[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      l[kt] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + TileLayout<D>::off(32 * kt + lane % 32, 16 * st + 8 * g));
-        l[kt] = mfma32(relu8(a), pq[st], l[kt]);
-      }
+        for (int st = 0; st < N8; ++st) {
+          const i32x4* p = reinterpret_cast<const i32x4*>(src + (size_t)min(32 * kt + lane % 32, nv - 1) * D + 64 * st + 32 * g);
+          kr[kt][st] = join8(p[0], p[1]);
+        }
+    };
+    float mrow = -INFINITY;
+    i32x8 kr[2][2][N8];
+    if (topk > 0) {
+      stage1(0);
+      zacc += z_in;
+      k8_regs(0, kr[0]);
+      wait_vmem();
+      __syncthreads();
     }
+    for (int t = 0; t < topk; ++t) {
+      if (t + 1 < topk) {
+        stage1(t + 1);
+        k8_regs(t + 1, kr[(t + 1) & 1]);
+      }
+      const int j = sel[t];
+      const int nv = min(kBlock, N - j * kBlock);
+      const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int st = 0; st < N8; ++st) s = mfma_f8(kr[t & 1][kt][st], qf[st], s);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kt + 8 * (i / 4) + 4 * g + i % 4 < nv) mrow = fmaxf(mrow, s[i] * sc);
+      }
+      if (t + 1 < topk) zacc += z_in;
+      wait_vmem();
+      __syncthreads();
+    }
+    mrow = xor32_max(mrow);
+
+    // pass 2: P with the exact maximum, 64x64 tile maximum across both wavefronts, fp8 PV
+    f32x16 os[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) os[c] = f32x16{};
+    float lsum = 0.f;
+    if (topk > 0) {
+      stage2(0);
+      wait_vmem();
+      __syncthreads();
+    }
+    for (int t = 0; t < topk; ++t) {
+      if (t + 1 < topk) stage2(t + 1);
+      const int j = sel[t];
+      const int nv = min(kBlock, N - j * kBlock);
+      const uint8_t* ks = lds8 + (t & 1) * 2 * K8B;
+      const uint8_t* vs = ks + K8B;
+      const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
+      float p[2][16];
+      float pmax = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int st = 0; st < N8; ++st) {
+          const int r = 32 * kt + lane % 32;
+          const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g));
+          const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g + 16));
+          s = mfma_f8(join8(a0, a1), qf[st], s);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool ok = row_ok && 32 * kt + 8 * (i / 4) + 4 * g + i % 4 < nv;
+          p[kt][i] = ok ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
+          lsum += p[kt][i];
+          pmax = fmaxf(pmax, p[kt][i]);
+        }
+      }
+      pmax = wave_max(pmax);
+      if (lane == 0) tmax_x[role] = pmax;
+      // V8^T operands (independent of the tile maximum)
+      i32x8 va[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int cr = 32 * c + lane % 32;
+        va[c] = join8(*reinterpret_cast<const i32x4*>(vs + v8_off(cr, 32 * g)),
+                      *reinterpret_cast<const i32x4*>(vs + v8_off(cr, 32 * g + 16)));
+      }
+      __syncthreads();
+      const float tmax = fmaxf(tmax_x[0], tmax_x[1]);
+      const float qs = tmax > 0.f ? kE4M3Max / tmax : 0.f;  // an all-underflow tile adds 0
+      // P8 as the B operand: slot 16kt + i <-> key 32kt + 8(i/4) + 4g + i%4
+      i32x8 pf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          pf[4 * kt + qd] = (int)cvt4_e4m3(sat(p[kt][4 * qd] * qs), sat(p[kt][4 * qd + 1] * qs),
+                                           sat(p[kt][4 * qd + 2] * qs), sat(p[kt][4 * qd + 3] * qs));
+      const float pv_scale = (tmax / kE4M3Max) * sv[(size_t)bh * nb + j];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const f32x16 tmp = mfma_f8(va[c], pf, f32x16{});
+        os[c] += tmp * pv_scale;
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+    __syncthreads();  // the state role has written T and zeta
+
+    // epilogue (as in the bf16 kernel): linear numerator relu(Q) T, denominator, combine
+    const float ltot = xor32_sum(lsum);
+    const float inv_l = topk > 0 ? 1.f / ltot : 0.f;
+    f32x16 num[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) num[c] = f32x16{};
+    float den = 0.f;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const bf16x8 pq = relu8(row_ok ? *reinterpret_cast<const bf16x8*>(Q + hoff + (size_t)row * D + 16 * k + 8 * g) : bf16x8{});
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int off = (32 * c + lane % 32) * PITCH + 16 * k + 8 * g;
+        num[c] = mfma32(*reinterpret_cast<const bf16x8*>(t_lo + off), pq, num[c]);
+        num[c] = mfma32(*reinterpret_cast<const bf16x8*>(t_hi + off), pq, num[c]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[16 * k + 8 * g + jj];
+    }
+    den = xor32_sum(den);
+    const float inv_den = (topk < nb && den != 0.f) ? 1.f / den : 0.f;
+    if (!row_ok) return;
+    const float a = alpha[(size_t)bh * N + row];
+    const float ws = a * inv_l, wl = (1.f - a) * inv_den;
+    float* orow = O + hoff + (size_t)row * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        bf16x8 lb;
+      for (int qd = 0; qd < 4; ++qd) {
+        f32x4 v;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) lb[jj] = f2bf(-l[u / 2][8 * (u % 2) + jj]);
-        ol[c] = mfma32(tr_operand<D, 4, 8>(Vs, 16 * u, 32 * c, lane), lb, ol[c]);
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(num[c][4 * qd + e], wl, os[c][4 * qd + e] * ws);
+        *reinterpret_cast<f32x4*>(orow + 32 * c + 8 * qd + 4 * g) = v;
       }
+  } else {
+    // ================= state role: rows c' = cp0 .. cp0 + D/2 of S_sel (pass 1) =================
+    const int cp0 = (role & 1) * (D / 2);
+    const int st = tid % 128;
+    f32x16 acc[RT][NC];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[r][c] = f32x16{};
+    if (topk > 0) {
+      stage1(0);
+      zacc += z_in;
+      wait_vmem();
+      __syncthreads();
+    }
+    for (int t = 0; t < topk; ++t) {
+      if (t + 1 < topk) stage1(t + 1);
+      const __bf16* Ks = lds + (t & 1) * 2 * TILE;
+      const __bf16* Vs = Ks + TILE;
+      bf16x8 a[2][RT], b[2][NC];
+      auto rd = [&](int ks, int buf) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) a[buf][r] = tr_operand<D, 8, 4>(Ks, 16 * ks, cp0 + 32 * r, lane);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) b[buf][c] = tr_operand<D, 8, 4>(Vs, 16 * ks, 32 * c, lane);
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < kBlock / 16; ++ks) {
+        if (ks + 1 < kBlock / 16) rd(ks + 1, (ks + 1) & 1);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const bf16x8 ar = relu8(a[ks & 1][r]);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[r][c] = mfma32(ar, b[ks & 1][c], acc[r][c]);
+        }
+      }
+      if (t + 1 < topk) zacc += z_in;
+      wait_vmem();
+      __syncthreads();
+    }
+    // pass 2: only the tile staging and the barriers (two per tile)
+    if (topk > 0) {
+      stage2(0);
+      wait_vmem();
+      __syncthreads();
+    }
+    for (int t = 0; t < topk; ++t) {
+      if (t + 1 < topk) stage2(t + 1);
+      __syncthreads();
+      wait_vmem();
+      __syncthreads();
+    }
+    // T = H - S_sel (bf16 hi + lo) and zeta = Z - sum_kept z_j for the sparse role
+    const __bf16* hh = ht_hi + (size_t)bh * D * D;
+    const __bf16* hl = ht_lo + (size_t)bh * D * D;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int cc = 32 * c + lane % 32;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int cp = cp0 + 32 * r + 8 * qd + 4 * g;
+          const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(hh + (size_t)cc * D + cp);
+          const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(hl + (size_t)cc * D + cp);
+          bf16x4 vh, vl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float tv = (bf2f(h1[e]) + bf2f(h0[e])) - acc[r][c][4 * qd + e];
+            vh[e] = f2bf(tv);
+            vl[e] = f2bf(tv - bf2f(vh[e]));
+          }
+          *reinterpret_cast<bf16x4*>(t_hi + cc * PITCH + cp) = vh;
+          *reinterpret_cast<bf16x4*>(t_lo + cc * PITCH + cp) = vl;
+        }
+      }
+    if (st < D) zeta[st] = Z[(size_t)bh * D + st] - zacc;
     __syncthreads();
-    const float tmax = fmaxf(tmax_x[0], tmax_x[1]);
-    const float qs = tmax > 0.f ? kE4M3Max / tmax : 0.f;  // an all-underflow tile adds 0
-    // P8 as the B operand: slot 16kt + i <-> key 32kt + 8(i/4) + 4g + i%4
-    i32x8 pf;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        pf[4 * kt + qd] = (int)cvt4_e4m3(sat(p[kt][4 * qd] * qs), sat(p[kt][4 * qd + 1] * qs),
-                                         sat(p[kt][4 * qd + 2] * qs), sat(p[kt][4 * qd + 3] * qs));
-    const float pv_scale = (tmax / kE4M3Max) * sv[(size_t)bh * nb + j];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const i32x4* pa = reinterpret_cast<const i32x4*>(V8s + (32 * c + lane % 32) * (kBlock + 16) + 32 * g);
-      const i32x4 a = pa[0], b = pa[1];
-      const f32x16 tmp = mfma_f8(i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}, pf, f32x16{});
-      os[c] += tmp * pv_scale;
-    }
   }
-
-  // ---- epilogue (as in the bf16 kernel) ----
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  const float inv_l = topk > 0 ? 1.f / ltot : 0.f;
-  __syncthreads();
-  if (tid < D) zeta[tid] = Z[(size_t)bh * D + tid] - zacc;
-  __syncthreads();
-  const __bf16* hh = ht_hi + (size_t)bh * D * D;
-  const __bf16* hl = ht_lo + (size_t)bh * D * D;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      const size_t off = (size_t)(32 * c + lane % 32) * D + 16 * st + 8 * g;
-      ol[c] = mfma32(*reinterpret_cast<const bf16x8*>(hl + off), pq[st], ol[c]);
-      ol[c] = mfma32(*reinterpret_cast<const bf16x8*>(hh + off), pq[st], ol[c]);
-    }
-  float den = 0.f;
-#pragma unroll
-  for (int st = 0; st < NS; ++st)
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[st][jj]) * zeta[16 * st + 8 * g + jj];
-  den += __shfl_xor(den, 32);
-  const float inv_den = (topk < nb && den != 0.f) ? 1.f / den : 0.f;
-  if (!row_ok) return;
-  const float a = alpha[(size_t)bh * N + row];
-  const float ws = a * inv_l, wl = (1.f - a) * inv_den;
-  float* orow = O + hoff + (size_t)row * D;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = fmaf(ol[c][4 * qd + e], wl, os[c][4 * qd + e] * ws);
-      *reinterpret_cast<f32x4*>(orow + 32 * c + 8 * qd + 4 * g) = v;
-    }
 }
 
 }  // namespace

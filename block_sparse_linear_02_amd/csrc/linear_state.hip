@@ -153,8 +153,17 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;  // element of H^T: c = e / D, c' = e % D
   const float* hp = h_part + (size_t)bh * nchunk * D * D;
+  // fixed summation order (chunk 0, 1, ...), eight loads in flight
   float s = 0.f;
-  for (int k = 0; k < nchunk; ++k) s += hp[(size_t)k * D * D + e];
+  int k = 0;
+  for (; k + 8 <= nchunk; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = hp[(size_t)(k + u) * D * D + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; k < nchunk; ++k) s += hp[(size_t)k * D * D + e];
   const __bf16 hi = f2bf(s);
   ht_hi[(size_t)bh * D * D + e] = hi;
   ht_lo[(size_t)bh * D * D + e] = f2bf(s - bf2f(hi));

@@ -9,9 +9,11 @@
 //   score_topk_kernel    one workgroup per (16 query blocks, head): the 16 x n_b score tile
 //                        s = (q~ . k~) / sqrt(d) by bf16 MFMA on the split operands
 //                        (hi*hi + hi*lo + lo*hi, fp32 accumulation: about fp32 accuracy) into
-//                        LDS, then per row (one wavefront) the k-th largest score by a
-//                        bitwise search on order-preserving keys, and an ascending compaction
-//                        that keeps the lowest indices among equal scores.
+//                        LDS (8 wavefronts, operand loads of two key tiles issued ahead of
+//                        their MFMAs), then per row (one wavefront) the k-th largest score by
+//                        a 32-step bitwise search on order-preserving keys (counts by ballot),
+//                        and an ascending compaction that keeps the lowest indices among equal
+//                        scores.
 #include "sla_device.hpp"
 #include "sla_launch.hpp"
 
@@ -120,11 +122,15 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
   }
 }
 
-constexpr int kRowsPerWg = 16;   // query blocks per score/top-k workgroup
-constexpr int kTopkThreads = 256;
+constexpr int kRowsPerWg = 16;   // query blocks per score/top-k workgroup (one MFMA row tile)
+constexpr int kTopkThreads = 512;
+constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kMaxChunks = 32;   // n_b <= 2048
 
-template <int D>
+// Scores of 16 query blocks against all key blocks into LDS, then per row the k-th largest
+// score and the ascending compaction.  NCH = key slots per lane (at least ceil(n_b / 64)):
+// invalid slots hold key 0, below every valid key, so no slot needs a guard.
+template <int D, int NCH>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     const __bf16* __restrict__ q_hi, const __bf16* __restrict__ q_lo,
     const __bf16* __restrict__ k_hi, const __bf16* __restrict__ k_lo, int nb, int topk,
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
   const int i0 = blockIdx.x * kRowsPerWg;
   const size_t base = (size_t)bh * nb * D;
 
-  // ---- scores: 16 x n_b tile, 16x16x32 MFMA on split operands ----
+  // ---- scores: 16 x n_b tile, 16x16x32 MFMA on split operands (hi*hi + hi*lo + lo*hi) ----
   {
     constexpr int KS = D / 32;
     bf16x8 ahi[KS], alo[KS];
@@ -145,86 +151,86 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int col = 32 * s + 8 * (lane / 16);
-      if (arow < nb) {
-        ahi[s] = *reinterpret_cast<const bf16x8*>(q_hi + base + (size_t)arow * D + col);
-        alo[s] = *reinterpret_cast<const bf16x8*>(q_lo + base + (size_t)arow * D + col);
-      } else {
-        ahi[s] = bf16x8{};
-        alo[s] = bf16x8{};
-      }
+      ahi[s] = arow < nb ? *reinterpret_cast<const bf16x8*>(q_hi + base + (size_t)arow * D + col) : bf16x8{};
+      alo[s] = arow < nb ? *reinterpret_cast<const bf16x8*>(q_lo + base + (size_t)arow * D + col) : bf16x8{};
     }
     const int ntiles = (nb + 15) / 16;
-    for (int jt = wave; jt < ntiles; jt += kTopkThreads / kWave) {
-      const int j = jt * 16 + lane % 16;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // two key tiles per step: all their operand loads are issued before the MFMAs
+    for (int jt = wave; jt < ntiles; jt += 2 * kTopkWaves) {
+      bf16x8 bhi[2][KS], blo[2][KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int col = 32 * s + 8 * (lane / 16);
-        bf16x8 bhi = bf16x8{}, blo = bf16x8{};
-        if (j < nb) {
-          bhi = *reinterpret_cast<const bf16x8*>(k_hi + base + (size_t)j * D + col);
-          blo = *reinterpret_cast<const bf16x8*>(k_lo + base + (size_t)j * D + col);
+      for (int u = 0; u < 2; ++u) {
+        const int j = (jt + u * kTopkWaves) * 16 + lane % 16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int col = 32 * s + 8 * (lane / 16);
+          bhi[u][s] = j < nb ? *reinterpret_cast<const bf16x8*>(k_hi + base + (size_t)j * D + col) : bf16x8{};
+          blo[u][s] = j < nb ? *reinterpret_cast<const bf16x8*>(k_lo + base + (size_t)j * D + col) : bf16x8{};
         }
-        acc = mfma16(alo[s], bhi, acc);
-        acc = mfma16(ahi[s], blo, acc);
-        acc = mfma16(ahi[s], bhi, acc);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[(4 * (lane / 16) + r) * nbp + j] = acc[r] * scale;
+      for (int u = 0; u < 2; ++u) {
+        const int t = jt + u * kTopkWaves;
+        if (t >= ntiles) break;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          acc = mfma16(alo[s], bhi[u][s], acc);
+          acc = mfma16(ahi[s], blo[u][s], acc);
+          acc = mfma16(ahi[s], bhi[u][s], acc);
+        }
+        const int j = t * 16 + lane % 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[(4 * (lane / 16) + r) * nbp + j] = acc[r] * scale;
+      }
     }
   }
   __syncthreads();
 
   // ---- per row: k-th largest key, then ascending compaction ----
-  const int nch = (nb + kWave - 1) / kWave;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = wave; r < kRowsPerWg; r += kTopkThreads / kWave) {
+  for (int r = wave; r < kRowsPerWg; r += kTopkWaves) {
     const int i = i0 + r;
     if (i >= nb) break;
     const float* srow = S + r * nbp;
-    u32 key[kMaxChunks];
+    u32 key[NCH];
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
+    for (int c = 0; c < NCH; ++c) {
       const int j = c * kWave + lane;
-      key[c] = (c < nch && j < nb) ? float_key(srow[j]) : 0u;
+      key[c] = j < nb ? float_key(srow[j]) : 0u;
     }
-    // largest threshold T with count(key >= T) >= topk; all valid keys are >= 1
-    u32 T = 0;
+    // largest threshold T with count(key >= T) >= topk (all valid keys are >= 1)
+    u32 T = 0xffffffffu;  // topk == 0: nothing is kept
     if (topk > 0) {
+      T = 0;
       for (int bit = 31; bit >= 0; --bit) {
         const u32 cand = T | (1u << bit);
         int cnt = 0;
 #pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c)
-          if (c < nch) cnt += __popcll(__ballot(key[c] >= cand));
+        for (int c = 0; c < NCH; ++c) cnt += __popcll(__ballot(key[c] >= cand));
         if (cnt >= topk) T = cand;
       }
-    } else {
-      T = 0xffffffffu;  // nothing kept
     }
     int gt = 0;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < nch) gt += __popcll(__ballot(key[c] > T));
+    for (int c = 0; c < NCH; ++c) gt += __popcll(__ballot(key[c] > T));
     const int need = topk - gt;  // equal keys to keep, lowest index first
     int pos = 0, ties = 0;
     int32_t* irow = idx + ((size_t)bh * nb + i) * topk;
     uint8_t* mrow = mask ? mask + ((size_t)bh * nb + i) * nb : nullptr;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      if (c < nch) {
-        const int j = c * kWave + lane;
-        const bool valid = j < nb;
-        const bool eq = valid && topk > 0 && key[c] == T;
-        const uint64_t eqm = __ballot(eq);
-        const int rank = ties + __popcll(eqm & lt_mask);
-        const bool sel = valid && topk > 0 && (key[c] > T || (eq && rank < need));
-        const uint64_t selm = __ballot(sel);
-        if (sel) irow[pos + __popcll(selm & lt_mask)] = j;
-        if (mrow && valid) mrow[j] = sel ? 1 : 0;
-        pos += __popcll(selm);
-        ties += __popcll(eqm);
-      }
+    for (int c = 0; c < NCH; ++c) {
+      const int j = c * kWave + lane;
+      const bool valid = j < nb;
+      const bool eq = valid && topk > 0 && key[c] == T;
+      const uint64_t eqm = __ballot(eq);
+      const int rank = ties + __popcll(eqm & lt_mask);
+      const bool sel = valid && topk > 0 && (key[c] > T || (eq && rank < need));
+      const uint64_t selm = __ballot(sel);
+      if (sel) irow[pos + __popcll(selm & lt_mask)] = j;
+      if (mrow && valid) mrow[j] = sel ? 1 : 0;
+      pos += __popcll(selm);
+      ties += __popcll(eqm);
     }
     if (probs) {
       float mx = -INFINITY;
@@ -238,6 +244,29 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
       for (int j = lane; j < nb; j += kWave) prow[j] = __expf(srow[j] - mx) * inv;
     }
   }
+}
+
+template <int D>
+hipError_t launch_topk(const Dims& p, const __bf16* q_hi, const __bf16* q_lo,
+                       const __bf16* k_hi, const __bf16* k_lo, int32_t* idx, uint8_t* mask,
+                       float* probs, size_t lds, hipStream_t stream) {
+  const int nbp = (p.nb + 15) / 16 * 16;
+  dim3 grid((p.nb + kRowsPerWg - 1) / kRowsPerWg, p.B * p.H);
+  const float scale = 1.0f / sqrtf((float)D);
+  const int nch = (p.nb + kWave - 1) / kWave;
+  auto go = [&](auto kern) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    kern<<<grid, kTopkThreads, lds, stream>>>(q_hi, q_lo, k_hi, k_lo, p.nb, p.topk, scale, nbp, idx, mask, probs);
+    return hipGetLastError();
+  };
+  if (nch <= 1) return go(score_topk_kernel<D, 1>);
+  if (nch <= 2) return go(score_topk_kernel<D, 2>);
+  if (nch <= 4) return go(score_topk_kernel<D, 4>);
+  if (nch <= 8) return go(score_topk_kernel<D, 8>);
+  if (nch <= 16) return go(score_topk_kernel<D, 16>);
+  if (nch <= 20) return go(score_topk_kernel<D, 20>);
+  return go(score_topk_kernel<D, kMaxChunks>);
 }
 
 }  // namespace
@@ -270,26 +299,9 @@ hipError_t launch_route(const Dims& p, const void* Q, const void* K, const float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int nbp = (p.nb + 15) / 16 * 16;
   const size_t lds = route_lds_bytes(p.nb);
-  dim3 g2((p.nb + kRowsPerWg - 1) / kRowsPerWg, BH);
-  const float scale = 1.0f / sqrtf((float)p.d);
-  if (p.d == 128) {
-    e = hipFuncSetAttribute((const void*)score_topk_kernel<128>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    score_topk_kernel<128><<<g2, kTopkThreads, lds, stream>>>(q_hi, q_lo, k_hi, k_lo, p.nb,
-                                                              p.topk, scale, nbp, idx, mask,
-                                                              probs);
-  } else {
-    e = hipFuncSetAttribute((const void*)score_topk_kernel<64>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    score_topk_kernel<64><<<g2, kTopkThreads, lds, stream>>>(q_hi, q_lo, k_hi, k_lo, p.nb,
-                                                             p.topk, scale, nbp, idx, mask,
-                                                             probs);
-  }
-  return hipGetLastError();
+  if (p.d == 128) return launch_topk<128>(p, q_hi, q_lo, k_hi, k_lo, idx, mask, probs, lds, stream);
+  return launch_topk<64>(p, q_hi, q_lo, k_hi, k_lo, idx, mask, probs, lds, stream);
 }
 
 }  // namespace sla

@@ -232,6 +232,33 @@ def test_fp8_forward_small():
     check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what="forward fp8 small")
 
 
+@pytest.mark.parametrize("k", [0, 1, 57])
+def test_fp8_forward_degenerate_k(k):
+    """The quantised sparse branch with nothing kept, one block kept, and every block kept."""
+    wl = small_ragged(k=k)
+    c = case(f"ragged_k{k}", wl)
+    r = oracle_route(c, k)
+    say(f"forward fp8 k={k}")
+    got = run_forward(c, r["idx"], fp8=True)
+    ref, _, _ = oracle.forward_fp8(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what=f"forward fp8 k={k}")
+
+
+def test_fp8_forward_branches_isolated():
+    """alpha = 1: the quantised sparse branch alone; alpha = 0: the linear branch, unquantised."""
+    wl = small_ragged()
+    c = case("ragged_bf16", wl)
+    r = oracle_route(c, wl.topk)
+    _, Os, Ol = oracle.forward_fp8(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    one = torch.ones_like(c["alpha"]).to(torch.device("cuda:0"))
+    say("forward fp8 alpha=1")
+    check_close(run_forward(c, r["idx"], alpha=one, fp8=True), Os, rel_tol=TOL_REL_FP8, max_tol=None,
+                what="fp8 sparse branch (alpha=1)")
+    say("forward fp8 alpha=0")
+    check_close(run_forward(c, r["idx"], alpha=torch.zeros_like(one), fp8=True), Ol,
+                what="linear branch beside fp8 (alpha=0)")
+
+
 # ---------------------------------------------------------------------------------- full size
 
 
