@@ -159,9 +159,11 @@ def main():
     variant = 1 if fp8 else (2 if a.linear_mode == "literal" else 0)
     ws_f = torch.empty(sla.forward_workspace_bytes(Q, wl.topk, variant), dtype=torch.uint8, device=dev)
     O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    ev_r = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for e in ev + ev_r:
+    def events(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    ev, ev_r, ev_s = events(a.steps), events(a.steps), events(a.steps)
+    for e in ev + ev_r + ev_s:
         e[0].record()
         e[1].record()
     torch.cuda.synchronize()
@@ -173,7 +175,8 @@ def main():
         if i is not None:
             ev_r[i][1].record()
         sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O,
-                    events=ev[i] if i is not None else None)
+                    events=ev[i] if i is not None else None,
+                    state_events=ev_s[i] if i is not None else None)
 
     for _ in range(a.warmup):
         step()
@@ -184,16 +187,33 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = 1e3 * elapsed / a.steps
+
+    def avg_ms(pairs):
+        return sum(b.elapsed_time(e) for b, e in pairs) / len(pairs)
+
     flops = sparse_flops(idx, N, d)
-    sparse_ms = sum(b.elapsed_time(e) for b, e in ev) / a.steps
-    route_ms = sum(b.elapsed_time(e) for b, e in ev_r) / a.steps
-    # algorithmic work of the sparse kernel per launch: the sparse branch (QK^T + PV) and, with
-    # the fused linear removal, the same again (relu(Q) relu(K_j)^T and its product with V_j)
-    k_flops = flops * (2.0 if a.linear_mode == "fused" else 1.0)
+    sparse_ms, route_ms, states_ms = avg_ms(ev), avg_ms(ev_r), avg_ms(ev_s)
+    # The sparse kernel's algorithmic work per launch: 2.10 MFLOP per kept (query block, key
+    # block) pair (QK^T and PV), i.e. the sparse FLOPs.  With the fused linear mode it also
+    # rebuilds relu(K_j)^T V_j of every kept pair on chip (the same count again) and applies
+    # relu(Q) to the d x d linear state (hi and lo halves): reported as executed MFMA work, not
+    # counted in `achieved`.
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
-    achieved = k_flops / (sparse_ms * 1e-3) / 1e12
+    achieved = flops / (sparse_ms * 1e-3) / 1e12
+    executed = flops * (2.0 if a.linear_mode == "fused" else 1.0) + (4.0 * B * H * N * d * d if a.linear_mode == "fused" else 0.0)
     digest = source_digest(SPARSE_SOURCES if not fp8 else ["block_sparse_linear_02_amd/csrc/fp8.hip"])
     kernel_key = ("sparse_fp8_kernel" if fp8 else "sparse_kernel") + f"@{a.workload}"
+    # HBM streams: the router reads Q and K once and writes the index lists; the state kernels
+    # read K and V once and write per-block z_j plus the per-(b, h) totals
+    es = Q.element_size()
+    route_bytes = 2 * B * H * N * d * es + B * H * nb * wl.topk * 4
+    states_bytes = 2 * B * H * N * d * es + B * H * nb * d * 4 + B * H * (d * d * 4 + d * 4)
+
+    def hbm(nbytes, t_ms):
+        gbs = nbytes / (t_ms * 1e-3) / 1e9
+        return {"bytes": nbytes, "ms": t_ms, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS}
+
     rec = {
         "metric": "sparse-linear attn fwd ms/call + effective TFLOPS, N=32768 H=12 d=128 90% sparse",
         "value": flops / (ms * 1e-3) / 1e12,
@@ -205,7 +225,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 sparse branch, bf16 linear" if fp8 else "bf16",
+        "dtype": "fp8-e4m3 sparse branch, bf16 linear" if fp8 else ("bf16" if es == 2 else "f32"),
         "data": "synthetic (seeded clustered video-DiT-shaped tensors, random projections)",
         "config": {
             "workload": f"{a.workload}: B={B} H={H} N={N} d={d} block=64 topk={wl.topk} of {nb} "
@@ -213,7 +233,8 @@ def main():
             "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": wl.topk,
         },
         "sparse_tflop_per_call": flops / 1e12,
-        "kernels_ms": {"route": route_ms, "sparse": sparse_ms, "states_and_other": ms - route_ms - sparse_ms},
+        "kernels_ms": {"route": route_ms, "states": states_ms, "sparse": sparse_ms,
+                       "other": ms - route_ms - states_ms - sparse_ms},
         "roofline": {
             "bound": "mfma",
             "kernel": kernel_key.split("@")[0],
@@ -222,8 +243,11 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / peak,
             "traffic": traffic_for(kernel_key, digest),
-            "flops_per_launch": k_flops,
+            "flops_per_launch": flops,
+            "mfma_flops_executed_per_launch": executed,
+            "executed_tflops": executed / (sparse_ms * 1e-3) / 1e12,
         },
+        "hbm_kernels": {"route": hbm(route_bytes, route_ms), "states": hbm(states_bytes, states_ms)},
     }
     if not a.no_cpu_baseline:
         cb = cpu_baseline(inputs, wl, idx)

@@ -52,6 +52,8 @@ class ForwardOpts(ctypes.Structure):
         ("linear_mode", ctypes.c_int32),
         ("sparse_begin", ctypes.c_void_p),
         ("sparse_end", ctypes.c_void_p),
+        ("states_begin", ctypes.c_void_p),
+        ("states_end", ctypes.c_void_p),
     ]
 
 
@@ -164,9 +166,10 @@ def route(Q, K, proj_q, proj_k, topk: int, want_mask: bool = False, want_scores:
 
 
 def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", workspace=None,
-            out=None, events=None):
+            out=None, events=None, state_events=None):
     """O = alpha * O_s + (1 - alpha) * O_l.  `events` = (begin, end) torch.cuda.Event pair
-    recorded around the sparse kernel (both must already exist, e.g. recorded once)."""
+    recorded around the sparse kernel, `state_events` likewise around the linear-state kernels
+    (the events must already exist, e.g. recorded once)."""
     _check_qkv(Q, K, V)
     Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
     B, H, N, d = Q.shape
@@ -179,10 +182,13 @@ def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", 
     need = lib().sla_forward_workspace_bytes(ctypes.byref(p), variant)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
     O = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device)
-    opts = ForwardOpts(mode, None, None)
+    opts = ForwardOpts(mode, None, None, None, None)
     if events is not None:
         opts.sparse_begin = ctypes.c_void_p(events[0].cuda_event)
         opts.sparse_end = ctypes.c_void_p(events[1].cuda_event)
+    if state_events is not None:
+        opts.states_begin = ctypes.c_void_p(state_events[0].cuda_event)
+        opts.states_end = ctypes.c_void_p(state_events[1].cuda_event)
     fn = lib().sla_forward_fp8_ex if fp8 else lib().sla_forward_ex
     st = fn(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(alpha), _ptr(O), _ptr(ws),
             ws.numel(), _stream(), ctypes.byref(opts))

@@ -125,10 +125,19 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   FwdWs w;
   carve_forward(d, variant, ws, &w);
 
-  hipError_t e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, stream);
+  hipError_t e = hipSuccess;
+  if (opts && opts->states_begin) {
+    e = hipEventRecord(opts->states_begin, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, stream);
   if (e != hipSuccess) return hip_fail(e);
   e = sla::launch_state_reduce(d, w.h_part, w.z_part, w.ht_hi, w.ht_lo, w.Z, w.h_full, stream);
   if (e != hipSuccess) return hip_fail(e);
+  if (opts && opts->states_end) {
+    e = hipEventRecord(opts->states_end, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if (fp8) {
     e = sla::launch_quantize(d, Q, w.q8, w.sq, stream);
     if (e == hipSuccess) e = sla::launch_quantize(d, K, w.k8, w.sk, stream);

@@ -72,9 +72,10 @@ typedef struct {
 } sla_problem;
 
 /* How the forward removes the kept blocks' states from the linear branch.
- * SLA_LINEAR_FUSED (default): relu(Q_i) (H - sum_sel h_j) is evaluated as
- *   relu(Q_i) H - sum_sel (relu(Q_i) relu(K_j)^T) V_j inside the sparse kernel, on the K/V
- *   tiles it already holds (no per-block d x d state is read).
+ * SLA_LINEAR_FUSED (default): the sparse kernel rebuilds sum_sel relu(K_j)^T V_j and
+ *   sum_sel relu(K_j)^T 1 on chip from the K/V tiles it already stages for the sparse branch,
+ *   subtracts them from the totals H and Z, and applies relu(Q_i) (no per-block d x d state is
+ *   stored or read).
  * SLA_LINEAR_LITERAL: every h_j = relu(K_j)^T V_j is materialised in the workspace and a
  *   separate kernel sums the kept ones per query block before applying relu(Q). */
 enum { SLA_LINEAR_FUSED = 0, SLA_LINEAR_LITERAL = 1 };
@@ -83,6 +84,8 @@ typedef struct {
   int32_t linear_mode;     /* SLA_LINEAR_FUSED or SLA_LINEAR_LITERAL */
   hipEvent_t sparse_begin; /* if non-null: recorded on `stream` right before the sparse kernel */
   hipEvent_t sparse_end;   /* if non-null: recorded on `stream` right after it */
+  hipEvent_t states_begin; /* if non-null: recorded right before the linear-state kernels */
+  hipEvent_t states_end;   /* if non-null: recorded right after them (state build + reduction) */
 } sla_forward_opts;
 
 /* Workspace sizes in bytes for a problem (0 when the problem is invalid or unsupported). */
@@ -105,7 +108,7 @@ int sla_forward(const sla_problem* p, const void* Q, const void* K, const void* 
                 const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                 hipStream_t stream);
 
-/* sla_forward with options (linear mode, events around the sparse kernel); opts may be NULL.
+/* sla_forward with options (linear mode, timing events); opts may be NULL.
  * Needs sla_forward_workspace_bytes(p, 2) bytes in literal mode, (p, 0) otherwise. */
 int sla_forward_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
                    const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
@@ -121,7 +124,7 @@ int sla_forward_fp8(const sla_problem* p, const void* Q, const void* K, const vo
                     const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
-/* sla_forward_fp8 with events around its sparse kernel (opts->linear_mode must be fused). */
+/* sla_forward_fp8 with timing events (opts->linear_mode must be fused). */
 int sla_forward_fp8_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const float* alpha, float* O, void* ws,
                        size_t ws_bytes, hipStream_t stream, const sla_forward_opts* opts);
