@@ -97,9 +97,28 @@ struct TileLoader {
 // Direct (register-free) copy of a full 64-row bf16 tile with D = 128 into the swizzled
 // TileLayout by THREADS/64 wavefronts: wavefront w fills rows 4(NW u + w) .. +3 for u < 16/NW,
 // 1 KB per load, lane i taking physical chunk i % 16 of row i / 16, i.e. logical chunk
-// (i % 16) ^ f(row) of the source row.  Only for tiles with all 64 rows valid.
+// (i % 16) ^ f(row) of the source row.  With NW = 4 the swizzle of those rows is
+// 4 (i / 16) + w for every u, so each lane's source offset is one register and the per-load
+// part is wavefront-uniform.  Only for tiles with all 64 rows valid.
 template <int THREADS>
 __device__ __forceinline__ void load_tile_direct(const __bf16* src, __bf16* tile, int tid) {
+  constexpr int NW = THREADS / 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+#pragma unroll
+  for (int u = 0; u < 16 / NW; ++u) {
+    const int r0 = 4 * (NW * u + w);
+    const int f = 4 * (lane / 16) + ((NW * u + w) & 3);
+    const int lane_off = (lane / 16) * 128 + ((lane % 16) ^ f) * 8;
+    load_lds16(src + r0 * 128 + lane_off, tile + r0 * 128);
+  }
+}
+
+// load_tile_direct for a tile of `valid` < 64 rows: rows at or past `valid` re-read the last
+// valid row (every address stays inside the source tensor); the caller zeroes them with
+// zero_tile_rows once the loads have landed.
+template <int THREADS>
+__device__ __forceinline__ void load_tile_direct_clamped(const __bf16* src, __bf16* tile, int tid,
+                                                         int valid) {
   constexpr int NW = THREADS / 64;
   const int w = tid / 64, lane = tid % 64;
 #pragma unroll
@@ -108,8 +127,16 @@ __device__ __forceinline__ void load_tile_direct(const __bf16* src, __bf16* tile
     const int row = r0 + lane / 16;
     const int f = 4 * (row & 3) + ((row >> 2) & 3);
     const int chunk = (lane % 16) ^ f;
-    load_lds16(src + row * 128 + chunk * 8, tile + r0 * 128);
+    load_lds16(src + min(row, valid - 1) * 128 + chunk * 8, tile + r0 * 128);
   }
+}
+
+// Zero rows valid .. 63 of a D = 128 tile in TileLayout (the swizzle only permutes chunks
+// within a row, so whole rows are contiguous).
+template <int THREADS>
+__device__ __forceinline__ void zero_tile_rows(__bf16* tile, int tid, int valid) {
+  for (int q = valid * 16 + tid; q < kBlock * 16; q += THREADS)
+    *reinterpret_cast<i32x4*>(tile + q * 8) = i32x4{0, 0, 0, 0};
 }
 
 __device__ __forceinline__ bf16x8 join_tr(i16x4 a, i16x4 b) {
@@ -132,6 +159,35 @@ __device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int row0, int c
   const int c = col0 + 16 * cs + 4 * (L % 4);
   return join_tr(lds_read_tr16(tile + TileLayout<D>::off(r, c)),
                  lds_read_tr16(tile + TileLayout<D>::off(r + GAP, c)));
+}
+
+// Byte addressing of a D = 128 TileLayout tile split as (per-lane part) XOR (block part) plus
+// an immediate: with f = swz(r), the 16-byte chunk c of row r sits at chunk c ^ f, and f depends
+// on r & 15 only, so for row offsets that are multiples of 16 and column blocks of 32 channels:
+//   row-wise read of row R0 + lane%32 (R0 % 32 == 0), channels 16k + 8g .. + 7:
+//     R0 * 256 + (row_part(lane) ^ 32k)
+//   transposed read (tr_operand) of rows row0 + STEP g + L/4 [+ GAP], channels
+//   32J + 16cs + 4(L%4) (row0 % 16 == 0):   row0 * 256 + (tr_part<STEP, GAP?>(lane) ^ 64J)
+// The XOR only touches bits 5..7, disjoint from the row part (bits >= 8) and the in-chunk
+// offset (bit 3), which is what makes the split exact.
+__device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ int row_part(int lane) {
+  const int g = lane / 32;
+  return (lane % 32) * 256 + 16 * (swz(lane % 16) ^ g);
+}
+template <int STEP>
+__device__ __forceinline__ int tr_part(int lane, int gap) {
+  const int h = lane / 16, L = lane % 16;
+  const int g = h / 2, cs = h % 2;
+  const int r = STEP * g + L / 4 + gap;  // < 16
+  const int cl = 2 * cs + (L % 4) / 2;
+  return r * 256 + 16 * (cl ^ swz(r)) + 8 * (L % 2);
+}
+__device__ __forceinline__ bf16x8 lds_row16(const __bf16* base, int byte_off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+__device__ __forceinline__ i16x4 lds_tr_at(const __bf16* base, int byte_off) {
+  return lds_read_tr16(reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(base) + byte_off));
 }
 
 // Map a workgroup id to a logical work item so that each of the 8 XCDs (which receive

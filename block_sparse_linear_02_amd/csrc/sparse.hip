@@ -25,6 +25,8 @@
 // num = relu(Q) T by MFMA, den = relu(q) . zeta, and O = alpha O_s / l + (1 - alpha) num / den
 // (the linear part is 0 when nothing is unselected or den == 0), fp32 stores; rows past N are
 // not stored.
+#include <type_traits>
+
 #include "sla_device.hpp"
 #include "sla_launch.hpp"
 #include "sla_tiles.hpp"
@@ -87,15 +89,20 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
   constexpr int NS = D / 16;       // MFMA k-steps over the head dim
   constexpr int NC = D / 32;       // 32-channel output tiles
   constexpr int RT = D / 64;       // 32-row tiles of S_sel per state wavefront
-  constexpr int PITCH = D + kPad;  // row pitch of the epilogue's T^T array (bf16 elements)
   constexpr int TILE = TileLayout<D>::ELEMS;
   // fp32 inputs keep K as bf16 hi + lo tiles so that S = K Q^T is about fp32-accurate
   // (Kh Qh + Kh Ql + Kl Qh); bf16 inputs are exact in one bf16 tile
   constexpr bool SPLIT = sizeof(T) == 4;
   constexpr int TILES = SPLIT ? 3 : 2;  // per buffer: K (hi), V, [K lo]
-  constexpr int LDS_ELEMS = (2 * TILES * TILE > 2 * D * PITCH) ? 2 * TILES * TILE : 2 * D * PITCH;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[LDS_ELEMS];
+  // Two separate LDS arrays, one per tile buffer, so that the compiler can tell the buffer being
+  // filled by direct-to-LDS loads from the one being read (with a single array it waits for the
+  // in-flight loads before every read of the current tile).  After the loop they hold T^T hi
+  // (buffer 0) and lo (buffer 1), each [D][D] in the tile row layout.
+  static_assert(D * TileLayout<D>::PITCH <= TILES * TILE, "T^T must fit in one tile buffer");
+  __shared__ __attribute__((aligned(16))) __bf16 lb0[TILES * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 lb1[TILES * TILE];
   __shared__ float zeta[D];
+  auto buf = [&](auto BUFC) -> __bf16* { return decltype(BUFC)::value ? lb1 : lb0; };
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, g = lane / 32;
@@ -104,8 +111,8 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
   const int bh = item / nb, qb = item % nb;
   const size_t hoff = (size_t)bh * N * D;
   const int32_t* sel = idx + ((size_t)bh * nb + qb) * topk;
-  __bf16* t_hi = lds;              // epilogue: T^T [c][c'] = H^T - S_sel^T, bf16 hi part
-  __bf16* t_lo = lds + D * PITCH;  // and lo part
+  __bf16* t_hi = lb0;  // epilogue: T^T [c][c'] = H^T - S_sel^T (tile row layout), bf16 hi part
+  __bf16* t_lo = lb1;  // and lo part
 
   // Tile staging shared by both roles: every thread moves its share of each tile.  bf16 tiles
   // with d = 128 and all 64 rows valid go HBM -> LDS directly (no registers), issued at the
@@ -118,18 +125,23 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
   float z_in = 0.f;        // z_j of the tile being staged (state role)
   int nv_next = kBlock;    // valid rows of the tile being staged
   float zacc = 0.f;        // state role: sum of z_j over the staged kept blocks
-  auto stage = [&](int t) {
+  auto stage = [&](int t, auto BUFC) {
     const int j = sel[t];
     const int nv = min(kBlock, N - j * kBlock);
-    __bf16* dst = lds + (t & 1) * TILES * TILE;
+    __bf16* dst = buf(BUFC);
     const T* ksrc = K + hoff + (size_t)j * kBlock * D;
     const T* vsrc = V + hoff + (size_t)j * kBlock * D;
     if (z_lane) z_in = zb[((size_t)bh * nb + j) * D + tid % 128];
     nv_next = nv;
-    if (DIRECT && nv == kBlock) {
-      if constexpr (DIRECT) {
+    if constexpr (DIRECT) {
+      // a short tile (the last block of the sequence) is clamped here and its tail rows are
+      // zeroed after the loads land (zero_tail), so no register path sits in the loop
+      if (nv == kBlock) {
         load_tile_direct<kSparseThreads>(ksrc, dst, tid);
         load_tile_direct<kSparseThreads>(vsrc, dst + TILE, tid);
+      } else {
+        load_tile_direct_clamped<kSparseThreads>(ksrc, dst, tid, nv);
+        load_tile_direct_clamped<kSparseThreads>(vsrc, dst + TILE, tid, nv);
       }
     } else {
       TileLoader<T, D, kSparseThreads> lk, lv;
@@ -142,26 +154,91 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
       lv.store(dst + TILE, tid);
     }
   };
+  // DIRECT tiles with fewer than 64 valid rows: zero the tail once every load has landed and
+  // been published by a barrier (workgroup-uniform condition; at most once per head)
+  auto zero_tail = [&](auto BUFC, int nv) {
+    if constexpr (DIRECT) {
+      if (nv < kBlock) {
+        zero_tile_rows<kSparseThreads>(buf(BUFC), tid, nv);
+        zero_tile_rows<kSparseThreads>(buf(BUFC) + TILE, tid, nv);
+        __syncthreads();
+      }
+    }
+  };
+  // LDS operand reads.  d = 128: per-lane address parts computed once and laundered through an
+  // empty asm at the start of every tile (so the compiler re-derives the per-block addresses
+  // with one v_xor each instead of holding dozens of them in registers across the loop); row
+  // and buffer offsets are immediates.  d = 64: the padded layout's plain offsets.
+  constexpr bool XADDR = D == 128;
+  int ap_row = 0, ap_va = 0, ap_vb = 0, ap_sa = 0, ap_sb = 0;
+  if constexpr (XADDR) {
+    ap_row = row_part(lane);
+    ap_va = tr_part<4>(lane, 0);
+    ap_vb = tr_part<4>(lane, 8);
+    ap_sa = tr_part<8>(lane, 0);
+    ap_sb = tr_part<8>(lane, 4);
+  }
+  auto launder = [&]() {
+    if constexpr (XADDR) asm volatile("" : "+v"(ap_row), "+v"(ap_va), "+v"(ap_vb), "+v"(ap_sa), "+v"(ap_sb));
+  };
+  // row-wise operand: row R0 + lane%32 (R0 % 32 == 0), channels 16k + 8g .. + 7
+  auto rd_row = [&](const __bf16* tile, int R0, int k) -> bf16x8 {
+    if constexpr (XADDR)
+      return lds_row16(tile, R0 * 256 + (ap_row ^ (32 * k)));
+    else
+      return *reinterpret_cast<const bf16x8*>(tile + TileLayout<D>::off(R0 + lane % 32, 16 * k + 8 * g));
+  };
+  // transposed operands (tr_operand): PV key order (step 4, gap 8) and state order (8, 4)
+  auto rd_tr_v = [&](const __bf16* tile, int row0, int col0) -> bf16x8 {
+    if constexpr (XADDR)
+      return join_tr(lds_tr_at(tile, row0 * 256 + (ap_va ^ (2 * col0))),
+                     lds_tr_at(tile, row0 * 256 + (ap_vb ^ (2 * col0))));
+    else
+      return tr_operand<D, 4, 8>(tile, row0, col0, lane);
+  };
+  auto rd_tr_s = [&](const __bf16* tile, int row0, int col0) -> bf16x8 {
+    if constexpr (XADDR)
+      return join_tr(lds_tr_at(tile, row0 * 256 + (ap_sa ^ (2 * col0))),
+                     lds_tr_at(tile, row0 * 256 + (ap_sb ^ (2 * col0))));
+    else
+      return tr_operand<D, 8, 4>(tile, row0, col0, lane);
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   int nv_cur = kBlock;
   auto first = [&]() {
     if (topk > 0) {
-      stage(0);
+      stage(0, B0{});
       zacc += z_in;
       nv_cur = nv_next;
       wait_vmem();
       __syncthreads();
+      zero_tail(B0{}, nv_cur);
     }
   };
   // start staging tile t + 1 into the other buffer (last read in iteration t - 1)
-  auto begin = [&](int t) {
-    if (t + 1 < topk) stage(t + 1);
+  auto begin = [&](int t, auto BUFC) {
+    launder();
+    if (t + 1 < topk) stage(t + 1, std::integral_constant<int, 1 - decltype(BUFC)::value>{});
   };
   // after using tile t: publish tile t + 1
-  auto end = [&](int t) {
-    if (t + 1 < topk) zacc += z_in;
+  auto end = [&](int t, auto BUFC) {
     nv_cur = nv_next;
     wait_vmem();
     __syncthreads();
+    // z_j of tile t + 1 is added only now, after the explicit wait above: used earlier, the
+    // compiler would wait for every in-flight tile load at that point
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < topk) zacc += z_in;
+    if (t + 1 < topk) zero_tail(std::integral_constant<int, 1 - decltype(BUFC)::value>{}, nv_cur);
+  };
+  // the kept tiles in pairs, so that each buffer index is a compile-time constant
+  auto loop = [&](auto&& body) {
+    for (int t = 0; t < topk; t += 2) {
+      body(t, B0{});
+      if (t + 1 < topk) body(t + 1, B1{});
+    }
   };
 
   if (role < 2) {
@@ -182,10 +259,10 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
     float mrun = -INFINITY, lsum = 0.f;
 
     first();
-    for (int t = 0; t < topk; ++t) {
+    loop([&](int t, auto BUFC) {
       const int nv = nv_cur;
-      begin(t);
-      const __bf16* Ks = lds + (t & 1) * TILES * TILE;
+      begin(t, BUFC);
+      const __bf16* Ks = buf(BUFC);
       const __bf16* Vs = Ks + TILE;
       // K operands of both 32-key halves, issued together ahead of their MFMAs
       bf16x8 ka[2][NS];
@@ -193,7 +270,7 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int k = 0; k < NS; ++k)
-          ka[kt][k] = *reinterpret_cast<const bf16x8*>(Ks + TileLayout<D>::off(32 * kt + lane % 32, 16 * k + 8 * g));
+          ka[kt][k] = rd_row(Ks, 32 * kt, k);
       f32x16 s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -201,8 +278,7 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
           if constexpr (SPLIT) {
-            const int off = TileLayout<D>::off(32 * kt + lane % 32, 16 * k + 8 * g);
-            s[kt] = mfma32(*reinterpret_cast<const bf16x8*>(Ks + 2 * TILE + off), q[k], s[kt]);
+            s[kt] = mfma32(rd_row(Ks + 2 * TILE, 32 * kt, k), q[k], s[kt]);
             s[kt] = mfma32(ka[kt][k], ql[k], s[kt]);
           }
           s[kt] = mfma32(ka[kt][k], q[k], s[kt]);
@@ -213,14 +289,15 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) va[c][u] = tr_operand<D, 4, 8>(Vs, 16 * u, 32 * c, lane);
+        for (int u = 0; u < 4; ++u) va[c][u] = rd_tr_v(Vs, 16 * u, 32 * c);
       // key of accumulator register i in half kt: 32kt + 8(i/4) + 4g + i%4
       if (nv < kBlock) {
+        const int lim = nv - 4 * g;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (32 * kt + 8 * (i / 4) + 4 * g + i % 4 >= nv) s[kt][i] = -INFINITY;
+            if (32 * kt + 8 * (i / 4) + i % 4 >= lim) s[kt][i] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -248,8 +325,8 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int u = 0; u < 4; ++u) os[c] = mfma32(va[c][u], pb[u], os[c]);
-      end(t);
-    }
+      end(t, BUFC);
+    });
     __syncthreads();  // the state role has written T and zeta
 
     const float ltot = xor32_sum(lsum);
@@ -266,9 +343,8 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
         const bf16x8 pq = relu8(q[k]);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const int off = (32 * c + lane % 32) * PITCH + 16 * k + 8 * g;
-          num[c] = mfma32(*reinterpret_cast<const bf16x8*>(t_lo + off), pq, num[c]);
-          num[c] = mfma32(*reinterpret_cast<const bf16x8*>(t_hi + off), pq, num[c]);
+          num[c] = mfma32(rd_row(t_lo, 32 * c, k), pq, num[c]);
+          num[c] = mfma32(rd_row(t_hi, 32 * c, k), pq, num[c]);
         }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[16 * k + 8 * g + jj];
@@ -303,18 +379,18 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
       for (int c = 0; c < NC; ++c) acc[r][c] = f32x16{};
 
     first();
-    for (int t = 0; t < topk; ++t) {
-      begin(t);
+    loop([&](int t, auto BUFC) {
+      begin(t, BUFC);
       if constexpr (FUSED) {
-        const __bf16* Ks = lds + (t & 1) * TILES * TILE;
+        const __bf16* Ks = buf(BUFC);
         const __bf16* Vs = Ks + TILE;
         // operands of key step ks + 1 are read while the MFMAs of step ks run
         bf16x8 a[2][RT], b[2][NC];
-        auto rd = [&](int ks, int buf) {
+        auto rd = [&](int ks, int bsel) {
 #pragma unroll
-          for (int r = 0; r < RT; ++r) a[buf][r] = tr_operand<D, 8, 4>(Ks, 16 * ks, cp0 + 32 * r, lane);
+          for (int r = 0; r < RT; ++r) a[bsel][r] = rd_tr_s(Ks, 16 * ks, cp0 + 32 * r);
 #pragma unroll
-          for (int c = 0; c < NC; ++c) b[buf][c] = tr_operand<D, 8, 4>(Vs, 16 * ks, 32 * c, lane);
+          for (int c = 0; c < NC; ++c) b[bsel][c] = rd_tr_s(Vs, 16 * ks, 32 * c);
         };
         rd(0, 0);
 #pragma unroll
@@ -328,8 +404,8 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
           }
         }
       }
-      end(t);
-    }
+      end(t, BUFC);
+    });
     if constexpr (FUSED) {
       const __bf16* hh = ht_hi + (size_t)bh * D * D;
       const __bf16* hl = ht_lo + (size_t)bh * D * D;
@@ -352,8 +428,8 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
               vh[e] = f2bf(tv);
               vl[e] = f2bf(tv - bf2f(vh[e]));
             }
-            *reinterpret_cast<bf16x4*>(t_hi + cc * PITCH + cp) = vh;
-            *reinterpret_cast<bf16x4*>(t_lo + cc * PITCH + cp) = vl;
+            *reinterpret_cast<bf16x4*>(t_hi + TileLayout<D>::off(cc, cp)) = vh;
+            *reinterpret_cast<bf16x4*>(t_lo + TileLayout<D>::off(cc, cp)) = vl;
           }
         }
       if (st < D) zeta[st] = Z[(size_t)bh * D + st] - zacc;
