@@ -21,6 +21,8 @@
 //                     S, form P = exp(S - max), exchange the 64x64 tile maximum, quantise P and
 //                     accumulate (P8 V8) sP sV by fp8 MFMA.  Epilogue and combine as in the
 //                     bf16 kernel.
+#include <type_traits>
+
 #include "sla_device.hpp"
 #include "sla_launch.hpp"
 #include "sla_tiles.hpp"
@@ -128,13 +130,18 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
   static_assert(D == 128, "the fp8 kernel is compiled for d = 128");
   constexpr int NS = D / 16, NC = D / 32, RT = D / 64, N8 = D / 64;
   constexpr int TILE = TileLayout<D>::ELEMS;  // bf16 elements of a K or V tile
-  constexpr int PITCH = D + kPad;             // epilogue T^T pitch
   constexpr int K8B = kBlock * D;             // bytes of a K8 tile
-  constexpr int LDS_ELEMS = (4 * TILE > 2 * D * PITCH) ? 4 * TILE : 2 * D * PITCH;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[LDS_ELEMS];
+  // One LDS array per buffer, so that the compiler can tell the buffer being filled by
+  // direct-to-LDS loads from the one being read.  Pass 1: bf16 K, V tiles; pass 2: K8 and V8^T
+  // tiles; afterwards T^T hi (buffer 0) and lo (buffer 1), each [D][D] in the tile row layout.
+  __shared__ __attribute__((aligned(16))) __bf16 lb0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 lb1[2 * TILE];
   __shared__ float zeta[D];
   __shared__ float tmax_x[2];
-  uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
+  auto buf = [&](auto BUFC) -> __bf16* { return decltype(BUFC)::value ? lb1 : lb0; };
+  auto buf8 = [&](auto BUFC) -> uint8_t* { return reinterpret_cast<uint8_t*>(buf(BUFC)); };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, g = lane / 32, w = tid / kWave;
@@ -144,35 +151,55 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
   const size_t hoff = (size_t)bh * N * D;
   const int32_t* sel = idx + ((size_t)bh * nb + qb) * topk;
   const float sqi = sq[(size_t)bh * nb + qb];
-  __bf16* t_hi = lds;
-  __bf16* t_lo = lds + D * PITCH;
+  __bf16* t_hi = lb0;
+  __bf16* t_lo = lb1;
 
-  // ---- pass 1 staging: bf16 K, V tiles (state role's linear states) ----
+  // the kept tiles in pairs, so that each buffer index is a compile-time constant
+  auto loop = [&](auto&& body) {
+    for (int t = 0; t < topk; t += 2) {
+      body(t, B0{});
+      if (t + 1 < topk) body(t + 1, B1{});
+    }
+  };
+  // ---- pass 1 staging: bf16 K, V tiles (state role's linear states); a short tile is clamped
+  // and its tail rows zeroed once the loads have landed ----
   const bool z_lane = role >= 2 && (tid % 128) < D;
   float z_in = 0.f, zacc = 0.f;
-  auto stage1 = [&](int t) {
+  int nv_next = kBlock;
+  auto stage1 = [&](int t, auto BUFC) {
     const int j = sel[t];
     const int nv = min(kBlock, N - j * kBlock);
-    __bf16* dst = lds + (t & 1) * 2 * TILE;
+    __bf16* dst = buf(BUFC);
     const __bf16* ksrc = K + hoff + (size_t)j * kBlock * D;
     const __bf16* vsrc = V + hoff + (size_t)j * kBlock * D;
     if (z_lane) z_in = zb[((size_t)bh * nb + j) * D + tid % 128];
+    nv_next = nv;
     if (nv == kBlock) {
       load_tile_direct<kF8Threads>(ksrc, dst, tid);
       load_tile_direct<kF8Threads>(vsrc, dst + TILE, tid);
     } else {
-      TileLoader<__bf16, D, kF8Threads> lk, lv;
-      lk.load(ksrc, nv, tid);
-      lv.load(vsrc, nv, tid);
-      lk.store(dst, tid);
-      lv.store(dst + TILE, tid);
+      load_tile_direct_clamped<kF8Threads>(ksrc, dst, tid, nv);
+      load_tile_direct_clamped<kF8Threads>(vsrc, dst + TILE, tid, nv);
+    }
+  };
+  auto publish1 = [&](int t, auto NEXT) {  // after the staged loads of tile t (if any) landed
+    wait_vmem();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < topk) {
+      zacc += z_in;
+      if (nv_next < kBlock) {
+        zero_tile_rows<kF8Threads>(buf(NEXT), tid, nv_next);
+        zero_tile_rows<kF8Threads>(buf(NEXT) + TILE, tid, nv_next);
+        __syncthreads();
+      }
     }
   };
   // ---- pass 2 staging: K8 and V8^T tiles (sparse role), straight into the swizzled layouts ----
-  auto stage2 = [&](int t) {
+  auto stage2 = [&](int t, auto BUFC) {
     const int j = sel[t];
     const int nv = min(kBlock, N - j * kBlock);
-    uint8_t* dst = lds8 + (t & 1) * 2 * K8B;
+    uint8_t* dst = buf8(BUFC);
     const uint8_t* ksrc = k8 + hoff + (size_t)j * kBlock * D;
     const uint8_t* vsrc = v8t + ((size_t)bh * nb + j) * D * kBlock;
 #pragma unroll
@@ -220,33 +247,32 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
     float mrow = -INFINITY;
     i32x8 kr[2][2][N8];
     if (topk > 0) {
-      stage1(0);
-      zacc += z_in;
+      stage1(0, B0{});
       k8_regs(0, kr[0]);
-      wait_vmem();
-      __syncthreads();
+      publish1(0, B0{});
     }
-    for (int t = 0; t < topk; ++t) {
+    loop([&](int t, auto BUFC) {
+      constexpr int BUF = decltype(BUFC)::value;
+      using NEXT = std::integral_constant<int, 1 - BUF>;
       if (t + 1 < topk) {
-        stage1(t + 1);
-        k8_regs(t + 1, kr[(t + 1) & 1]);
+        stage1(t + 1, NEXT{});
+        k8_regs(t + 1, kr[1 - BUF]);
       }
       const int j = sel[t];
       const int nv = min(kBlock, N - j * kBlock);
       const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
+      const int lim = nv - 4 * g;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x16 s = f32x16{};
 #pragma unroll
-        for (int st = 0; st < N8; ++st) s = mfma_f8(kr[t & 1][kt][st], qf[st], s);
+        for (int st = 0; st < N8; ++st) s = mfma_f8(kr[BUF][kt][st], qf[st], s);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (32 * kt + 8 * (i / 4) + 4 * g + i % 4 < nv) mrow = fmaxf(mrow, s[i] * sc);
+          if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[i] * sc);
       }
-      if (t + 1 < topk) zacc += z_in;
-      wait_vmem();
-      __syncthreads();
-    }
+      publish1(t + 1, NEXT{});
+    });
     mrow = xor32_max(mrow);
 
     // pass 2: P with the exact maximum, 64x64 tile maximum across both wavefronts, fp8 PV
@@ -255,17 +281,19 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
     for (int c = 0; c < NC; ++c) os[c] = f32x16{};
     float lsum = 0.f;
     if (topk > 0) {
-      stage2(0);
+      stage2(0, B0{});
       wait_vmem();
       __syncthreads();
     }
-    for (int t = 0; t < topk; ++t) {
-      if (t + 1 < topk) stage2(t + 1);
+    loop([&](int t, auto BUFC) {
+      constexpr int BUF = decltype(BUFC)::value;
+      if (t + 1 < topk) stage2(t + 1, std::integral_constant<int, 1 - BUF>{});
       const int j = sel[t];
       const int nv = min(kBlock, N - j * kBlock);
-      const uint8_t* ks = lds8 + (t & 1) * 2 * K8B;
+      const uint8_t* ks = buf8(BUFC);
       const uint8_t* vs = ks + K8B;
       const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
+      const int lim = row_ok ? nv - 4 * g : 0;
       float p[2][16];
       float pmax = 0.f;
 #pragma unroll
@@ -280,8 +308,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const bool ok = row_ok && 32 * kt + 8 * (i / 4) + 4 * g + i % 4 < nv;
-          p[kt][i] = ok ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
+          p[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
           lsum += p[kt][i];
           pmax = fmaxf(pmax, p[kt][i]);
         }
@@ -315,7 +342,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
       }
       wait_vmem();
       __syncthreads();
-    }
+    });
     __syncthreads();  // the state role has written T and zeta
 
     // epilogue (as in the bf16 kernel): linear numerator relu(Q) T, denominator, combine
@@ -330,7 +357,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
       const bf16x8 pq = relu8(row_ok ? *reinterpret_cast<const bf16x8*>(Q + hoff + (size_t)row * D + 16 * k + 8 * g) : bf16x8{});
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int off = (32 * c + lane % 32) * PITCH + 16 * k + 8 * g;
+        const int off = TileLayout<D>::off(32 * c + lane % 32, 16 * k + 8 * g);
         num[c] = mfma32(*reinterpret_cast<const bf16x8*>(t_lo + off), pq, num[c]);
         num[c] = mfma32(*reinterpret_cast<const bf16x8*>(t_hi + off), pq, num[c]);
       }
@@ -362,21 +389,21 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[r][c] = f32x16{};
     if (topk > 0) {
-      stage1(0);
-      zacc += z_in;
-      wait_vmem();
-      __syncthreads();
+      stage1(0, B0{});
+      publish1(0, B0{});
     }
-    for (int t = 0; t < topk; ++t) {
-      if (t + 1 < topk) stage1(t + 1);
-      const __bf16* Ks = lds + (t & 1) * 2 * TILE;
+    loop([&](int t, auto BUFC) {
+      constexpr int BUF = decltype(BUFC)::value;
+      using NEXT = std::integral_constant<int, 1 - BUF>;
+      if (t + 1 < topk) stage1(t + 1, NEXT{});
+      const __bf16* Ks = buf(BUFC);
       const __bf16* Vs = Ks + TILE;
       bf16x8 a[2][RT], b[2][NC];
-      auto rd = [&](int ks, int buf) {
+      auto rd = [&](int ks, int bsel) {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) a[buf][r] = tr_operand<D, 8, 4>(Ks, 16 * ks, cp0 + 32 * r, lane);
+        for (int r = 0; r < RT; ++r) a[bsel][r] = tr_operand<D, 8, 4>(Ks, 16 * ks, cp0 + 32 * r, lane);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) b[buf][c] = tr_operand<D, 8, 4>(Vs, 16 * ks, 32 * c, lane);
+        for (int c = 0; c < NC; ++c) b[bsel][c] = tr_operand<D, 8, 4>(Vs, 16 * ks, 32 * c, lane);
       };
       rd(0, 0);
 #pragma unroll
@@ -389,22 +416,20 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
           for (int c = 0; c < NC; ++c) acc[r][c] = mfma32(ar, b[ks & 1][c], acc[r][c]);
         }
       }
-      if (t + 1 < topk) zacc += z_in;
-      wait_vmem();
-      __syncthreads();
-    }
+      publish1(t + 1, NEXT{});
+    });
     // pass 2: only the tile staging and the barriers (two per tile)
     if (topk > 0) {
-      stage2(0);
+      stage2(0, B0{});
       wait_vmem();
       __syncthreads();
     }
-    for (int t = 0; t < topk; ++t) {
-      if (t + 1 < topk) stage2(t + 1);
+    loop([&](int t, auto BUFC) {
+      if (t + 1 < topk) stage2(t + 1, std::integral_constant<int, 1 - decltype(BUFC)::value>{});
       __syncthreads();
       wait_vmem();
       __syncthreads();
-    }
+    });
     // T = H - S_sel (bf16 hi + lo) and zeta = Z - sum_kept z_j for the sparse role
     const __bf16* hh = ht_hi + (size_t)bh * D * D;
     const __bf16* hl = ht_lo + (size_t)bh * D * D;
@@ -425,8 +450,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
             vh[e] = f2bf(tv);
             vl[e] = f2bf(tv - bf2f(vh[e]));
           }
-          *reinterpret_cast<bf16x4*>(t_hi + cc * PITCH + cp) = vh;
-          *reinterpret_cast<bf16x4*>(t_lo + cc * PITCH + cp) = vl;
+          *reinterpret_cast<bf16x4*>(t_hi + TileLayout<D>::off(cc, cp)) = vh;
+          *reinterpret_cast<bf16x4*>(t_lo + TileLayout<D>::off(cc, cp)) = vl;
         }
       }
     if (st < D) zeta[st] = Z[(size_t)bh * D + st] - zacc;
