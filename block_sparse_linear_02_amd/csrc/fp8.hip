@@ -58,6 +58,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16* __restrict_
                                                        int nb, uint8_t* __restrict__ codes,
                                                        float* __restrict__ scales) {
   __shared__ float wmax[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tl[TRANSPOSED ? D * kBlock : 16];
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   const int t = blockIdx.x, bh = blockIdx.y;
   const int row0 = t * kBlock;
@@ -93,14 +94,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16* __restrict_
       uint8_t* dst = codes + ((size_t)bh * N + row0 + r) * D + ch * 8;
       *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
     } else {
-      // [bh][t][c][pos(r)]; keys past N get code 0 (their P8 is 0 as well)
-      uint8_t* dst = codes + ((size_t)bh * nb + t) * D * kBlock + v8_pos(r);
+      // [c][pos(r)] staged in LDS (keys past N get code 0: their P8 is 0 as well), written out
+      // below with 16-byte stores
+      const u32 lo = cvt4_e4m3(y[0], y[1], y[2], y[3]);
+      const u32 hi = cvt4_e4m3(y[4], y[5], y[6], y[7]);
+      const int pos = v8_pos(r);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const u32 c = cvt4_e4m3(y[e], 0.f, 0.f, 0.f);
-        dst[(size_t)(ch * 8 + e) * kBlock] = (uint8_t)(c & 0xff);
+      for (int e = 0; e < 4; ++e) {
+        tl[(ch * 8 + e) * kBlock + pos] = (uint8_t)(lo >> (8 * e));
+        tl[(ch * 8 + 4 + e) * kBlock + pos] = (uint8_t)(hi >> (8 * e));
       }
     }
+  }
+  if constexpr (TRANSPOSED) {
+    __syncthreads();
+    // [bh][t][c][pos]: D rows of 64 bytes, one 16-byte piece per thread and step
+    uint8_t* dst = codes + ((size_t)bh * nb + t) * D * kBlock;
+    for (int q = tid; q < D * kBlock / 16; q += 256)
+      *reinterpret_cast<i32x4*>(dst + q * 16) = *reinterpret_cast<const i32x4*>(tl + q * 16);
   }
 }
 
