@@ -80,42 +80,49 @@ def traffic_for(kernel_key, digest):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(inputs, wl, idx_gpu, budget_s=20.0):
-    """The oracle as it stands on a bounded sample: one head's router, then query blocks of that
-    head's forward until about `budget_s` of CPU time; scaled to the whole workload."""
+def cpu_baseline(inputs, wl, idx_gpu, budget_s=15.0):
+    """The oracle as it stands on a bounded sample: whole heads (router, block states, every
+    query block's forward) in order until about `budget_s` of CPU time, the last head possibly
+    on a random subset of its query blocks; scaled to the whole workload."""
     import numpy as np
     import threadpoolctl
 
     import oracle
 
-    Q, K, V = inputs["Q"][0, 0], inputs["K"][0, 0], inputs["V"][0, 0]
-    t0 = time.perf_counter()
-    r = oracle.route(Q[None, None], K[None, None], inputs["Wq"].double(), inputs["Wk"].double(), wl.topk, 64)
-    t_route = time.perf_counter() - t0
-    idx = r["idx"][0, 0]
-    t0 = time.perf_counter()
-    states = oracle.block_states(K, V, 64)
-    t_states = time.perf_counter() - t0
     nb = wl.n_blocks
-    done, t_fwd = 0, 0.0
-    rng = np.random.default_rng(0)
-    order = rng.permutation(nb)
-    while t_fwd < budget_s and done < nb:
-        blocks = order[done : done + 8]
-        t0 = time.perf_counter()
-        if wl.fp8:
-            oracle.forward_fp8_head(Q, K, V, idx, inputs["alpha"][0, 0], 64, q_blocks=blocks, states=states)
-        else:
-            oracle.forward_head(Q, K, V, idx, inputs["alpha"][0, 0], 64, q_blocks=blocks, states=states)
-        t_fwd += time.perf_counter() - t0
-        done += len(blocks)
     heads = wl.B * wl.H
-    per_call = heads * (t_route + t_states + t_fwd * nb / done)
+    per_head, used, blocks_done = [], 0.0, 0
+    for bh in range(heads):
+        b, h = divmod(bh, wl.H)
+        Q, K, V = inputs["Q"][b, h], inputs["K"][b, h], inputs["V"][b, h]
+        t0 = time.perf_counter()
+        r = oracle.route(Q[None, None], K[None, None], inputs["Wq"].double(), inputs["Wk"].double(), wl.topk, 64)
+        states = oracle.block_states(K, V, 64)
+        t_fixed = time.perf_counter() - t0
+        idx = r["idx"][0, 0]
+        order = np.random.default_rng(bh).permutation(nb)
+        done, t_fwd = 0, 0.0
+        while done < nb and used + t_fixed + t_fwd < budget_s:
+            blocks = order[done : done + 8]
+            t0 = time.perf_counter()
+            if wl.fp8:
+                oracle.forward_fp8_head(Q, K, V, idx, inputs["alpha"][b, h], 64, q_blocks=blocks, states=states)
+            else:
+                oracle.forward_head(Q, K, V, idx, inputs["alpha"][b, h], 64, q_blocks=blocks, states=states)
+            t_fwd += time.perf_counter() - t0
+            done += len(blocks)
+        used += t_fixed + t_fwd
+        blocks_done += done
+        per_head.append(t_fixed + t_fwd * nb / max(done, 1))
+        if used >= budget_s:
+            break
+    per_call = heads * sum(per_head) / len(per_head)
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
     return {
         "seconds_per_call": per_call,
-        "sample": f"1 of {heads} heads: router + block states + {done} of {nb} query blocks "
-                  f"({t_route + t_states + t_fwd:.1f} s), scaled by heads and query blocks",
+        "sample": f"{len(per_head)} of {heads} heads (router, block states and {blocks_done} query "
+                  f"blocks of {len(per_head) * nb}; {used:.1f} s of CPU time), scaled to all heads "
+                  f"and query blocks",
         "cores": int(threads),
     }
 
