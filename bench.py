@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video_s", help="video_s | video_l | video_l_fp8")
-    ap.add_argument("--linear-mode", default="fused", choices=["fused", "literal"])
+    ap.add_argument("--linear-mode", default="fused", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -61,6 +61,11 @@ def source_digest(files):
 
 SPARSE_SOURCES = [
     "block_sparse_linear_02_amd/csrc/sparse.hip",
+    "block_sparse_linear_02_amd/csrc/sla_tiles.hpp",
+    "block_sparse_linear_02_amd/csrc/sla_device.hpp",
+]
+SPLIT_SOURCES = [
+    "block_sparse_linear_02_amd/csrc/sparse_split.hip",
     "block_sparse_linear_02_amd/csrc/sla_tiles.hpp",
     "block_sparse_linear_02_amd/csrc/sla_device.hpp",
 ]
@@ -163,7 +168,7 @@ def main():
     fp8 = wl.fp8
     idx = torch.empty((B, H, nb, wl.topk), dtype=torch.int32, device=dev)
     ws_r = torch.empty(sla.route_workspace_bytes(Q, wl.topk), dtype=torch.uint8, device=dev)
-    variant = 1 if fp8 else (2 if a.linear_mode == "literal" else 0)
+    variant = 1 if fp8 else {"fused": 0, "literal": 2, "mask_product": 3}[a.linear_mode]
     ws_f = torch.empty(sla.forward_workspace_bytes(Q, wl.topk, variant), dtype=torch.uint8, device=dev)
     O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     def events(n):
@@ -207,9 +212,16 @@ def main():
     # counted in `achieved`.
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     achieved = flops / (sparse_ms * 1e-3) / 1e12
-    executed = flops * (2.0 if a.linear_mode == "fused" else 1.0) + (4.0 * B * H * N * d * d if a.linear_mode == "fused" else 0.0)
-    digest = source_digest(SPARSE_SOURCES if not fp8 else ["block_sparse_linear_02_amd/csrc/fp8.hip"])
-    kernel_key = ("sparse_fp8_kernel" if fp8 else "sparse_kernel") + f"@{a.workload}"
+    apply_flops = 4.0 * B * H * N * d * d  # relu(q) T on hi + lo halves, per query row
+    executed = flops + {"fused": flops + apply_flops, "literal": 0.0, "mask_product": apply_flops}[a.linear_mode]
+    if fp8:
+        sources, kname = ["block_sparse_linear_02_amd/csrc/fp8.hip"], "sparse_fp8_kernel"
+    elif a.linear_mode == "mask_product":
+        sources, kname = SPLIT_SOURCES, "split_kernel"
+    else:
+        sources, kname = SPARSE_SOURCES, "sparse_kernel"
+    digest = source_digest(sources)
+    kernel_key = kname + f"@{a.workload}"
     # HBM streams: the router reads Q and K once and writes the index lists; the state kernels
     # read K and V once and write per-block z_j plus the per-(b, h) totals
     es = Q.element_size()

@@ -68,10 +68,12 @@ size_t carve_route(const sla::Dims& d, void* ws, RouteWs* out) {
 struct FwdWs {
   float *zb, *h_part, *z_part, *Z, *hj, *h_full;
   __bf16 *ht_hi, *ht_lo;
+  __bf16 *hj_hi, *hj_lo, *t_hi, *t_lo;
+  uint32_t* bits;
   uint8_t *q8, *k8, *v8;
   float *sq, *sk, *sv;
 };
-// variant: 0 fused, 1 fp8 (fused), 2 literal
+// variant: 0 fused, 1 fp8 (fused), 2 literal, 3 mask product
 size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
   Carve c(ws);
   const size_t BH = (size_t)d.B * d.H;
@@ -88,6 +90,13 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
   if (variant == 2) {
     f.hj = c.take<float>(BH * d.nb * dd);
     f.h_full = c.take<float>(BH * dd);
+  }
+  if (variant == 3) {
+    f.hj_hi = c.take<__bf16>(BH * d.nb * dd);
+    f.hj_lo = c.take<__bf16>(BH * d.nb * dd);
+    f.t_hi = c.take<__bf16>(BH * d.nb * dd);
+    f.t_lo = c.take<__bf16>(BH * d.nb * dd);
+    f.bits = c.take<uint32_t>(BH * d.nb * sla::mask_words(d.nb));
   }
   if (variant == 1) {
     const size_t n = BH * d.N * d.d;
@@ -114,11 +123,12 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   int st = check_problem(p, &d);
   if (st != SLA_OK) return st;
   const int mode = opts ? opts->linear_mode : SLA_LINEAR_FUSED;
-  if (mode != SLA_LINEAR_FUSED && mode != SLA_LINEAR_LITERAL) return SLA_ERR_INVALID;
+  if (mode != SLA_LINEAR_FUSED && mode != SLA_LINEAR_LITERAL && mode != SLA_LINEAR_MASK_PRODUCT)
+    return SLA_ERR_INVALID;
   if (fp8 && mode != SLA_LINEAR_FUSED) return SLA_ERR_INVALID;
   if (fp8 && (d.dtype != sla::kBF16 || d.d != 128)) return SLA_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !alpha || !O || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
-  const int variant = fp8 ? 1 : (mode == SLA_LINEAR_LITERAL ? 2 : 0);
+  const int variant = fp8 ? 1 : (mode == SLA_LINEAR_LITERAL ? 2 : (mode == SLA_LINEAR_MASK_PRODUCT ? 3 : 0));
   const size_t need = carve_forward(d, variant, nullptr, nullptr);
   if (!ws) return SLA_ERR_INVALID;
   if (ws_bytes < need) return SLA_ERR_WORKSPACE;
@@ -130,10 +140,16 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = hipEventRecord(opts->states_begin, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
-  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, stream);
+  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, w.hj_hi, w.hj_lo, stream);
   if (e != hipSuccess) return hip_fail(e);
   e = sla::launch_state_reduce(d, w.h_part, w.z_part, w.ht_hi, w.ht_lo, w.Z, w.h_full, stream);
   if (e != hipSuccess) return hip_fail(e);
+  if (mode == SLA_LINEAR_MASK_PRODUCT) {
+    e = sla::launch_mask_bits(d, idx, w.bits, stream);  // all-zero rows when topk == 0
+    if (e == hipSuccess)
+      e = sla::launch_tsel(d, w.hj_hi, w.hj_lo, w.bits, w.ht_hi, w.ht_lo, w.t_hi, w.t_lo, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if (opts && opts->states_end) {
     e = hipEventRecord(opts->states_end, stream);
     if (e != hipSuccess) return hip_fail(e);
@@ -151,6 +167,8 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   if (fp8)
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
+  else if (mode == SLA_LINEAR_MASK_PRODUCT)
+    e = sla::launch_sparse_tsel(d, Q, K, V, idx, alpha, w.t_hi, w.t_lo, w.Z, w.zb, O, stream);
   else
     e = sla::launch_sparse(d, Q, K, V, idx, alpha, w.ht_hi, w.ht_lo, w.Z, w.zb, O,
                            mode == SLA_LINEAR_FUSED ? 1 : 0, stream);
@@ -178,7 +196,7 @@ size_t sla_route_workspace_bytes(const sla_problem* p) {
 
 size_t sla_forward_workspace_bytes(const sla_problem* p, int variant) {
   sla::Dims d;
-  if (check_problem(p, &d) != SLA_OK || variant < 0 || variant > 2) return 0;
+  if (check_problem(p, &d) != SLA_OK || variant < 0 || variant > 3) return 0;
   return carve_forward(d, variant, nullptr, nullptr);
 }
 

@@ -11,7 +11,8 @@
 //                  are in flight while the current one is used) into row-major LDS tiles; the
 //                  4 wavefronts read them back transposed (ds_read_b64_tr_b16) as MFMA operands
 //                  and accumulate H^T = V^T relu(K) (bf16 MFMA, fp32 accumulation) for the
-//                  chunk, z_j by fp32 sums.  Literal mode also stores every h_j.
+//                  chunk, z_j by fp32 sums.  Literal mode also stores every h_j (fp32); the
+//                  mask-product mode stores every h_j as bf16 hi + lo.
 //   reduce_kernel  sums the chunk partials in a fixed order (deterministic), splits H^T into
 //                  bf16 hi + lo parts (the sparse kernel's MFMA operand) and writes Z.
 #include "sla_device.hpp"
@@ -24,11 +25,15 @@ namespace {
 
 constexpr int kStateThreads = 256;
 
-template <class T, int D, bool LITERAL>
+// MODE: 0 totals only, 1 also every h_j in fp32 in the natural layout h_j[c'][c] (K channel
+// major), 2 also every h_j^T[c][c'] (V channel major) as bf16 hi + lo (hj, hj_lo), stored in
+// slices of 64 entries, slice-major, so that one slice of all blocks is contiguous
+template <class T, int D, int MODE>
 __global__ __launch_bounds__(kStateThreads) void state_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int N, int nb, int cb,
     float* __restrict__ zb, float* __restrict__ h_part, float* __restrict__ z_part,
-    float* __restrict__ hj) {
+    void* __restrict__ hj, __bf16* __restrict__ hj_lo) {
+  constexpr bool LITERAL = MODE != 0;
   constexpr int NT = D / 64;  // 32x32 output tiles per wave per dimension (D=128: 2, D=64: 1)
   __shared__ __attribute__((aligned(16))) __bf16 Ks[TileLayout<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[TileLayout<D>::ELEMS];
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
     }
     if constexpr (LITERAL) {
       // store h_j in natural layout h_j[c'][c]; lane holds c' = col, c = rows 8(i/4)+4g+i%4
-      float* dst = hj + ((size_t)bh * nb + j) * D * D;
+      const size_t hoff = ((size_t)bh * nb + j) * D * D;
 #pragma unroll
       for (int a = 0; a < NT; ++a)
 #pragma unroll
@@ -108,9 +113,23 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c = r0 + 32 * a + 8 * q + 4 * (lane / 32);
-            f32x4 v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                       acc[a][b][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(dst + (size_t)cp * D + c) = v;
+            const size_t o = hoff + (size_t)cp * D + c;
+            if constexpr (MODE == 1) {
+              f32x4 v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                         acc[a][b][4 * q + 3]};
+              *reinterpret_cast<f32x4*>(static_cast<float*>(hj) + o) = v;
+            } else {
+              // h_j^T[c][c'] in 64-entry slices, slice-major ([bh][n / 64][j][n % 64] with
+              // n = c D + c'): the 32 lanes of a half-wavefront write 32 consecutive c'
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int n = (c + e) * D + cp;
+                const size_t ot = (((size_t)bh * (D * D / 64) + n / 64) * nb + j) * 64 + n % 64;
+                const __bf16 vh = f2bf(acc[a][b][4 * q + e]);
+                static_cast<__bf16*>(hj)[ot] = vh;
+                hj_lo[ot] = f2bf(acc[a][b][4 * q + e] - bf2f(vh));
+              }
+            }
           }
           tot[a][b] += acc[a][b];
           acc[a][b] = f32x16{};
@@ -178,15 +197,19 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
 
 template <class T, int D>
 hipError_t launch_states_t(const Dims& p, const void* K, const void* V, float* zb,
-                           float* h_part, float* z_part, float* hj, hipStream_t stream) {
+                           float* h_part, float* z_part, float* hj, __bf16* hj_hi,
+                           __bf16* hj_lo, hipStream_t stream) {
   const int cb = state_chunk_blocks(p);
   dim3 grid((p.nb + cb - 1) / cb, p.B * p.H);
   if (hj)
-    state_kernel<T, D, true><<<grid, kStateThreads, 0, stream>>>(
-        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj);
+    state_kernel<T, D, 1><<<grid, kStateThreads, 0, stream>>>(
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj, nullptr);
+  else if (hj_hi)
+    state_kernel<T, D, 2><<<grid, kStateThreads, 0, stream>>>(
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj_hi, hj_lo);
   else
-    state_kernel<T, D, false><<<grid, kStateThreads, 0, stream>>>(
-        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, nullptr);
+    state_kernel<T, D, 0><<<grid, kStateThreads, 0, stream>>>(
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -202,11 +225,15 @@ int state_chunk_blocks(const Dims& p) {
 }
 
 hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
-                         float* z_part, float* hj, hipStream_t stream) {
-  if (p.dtype == kBF16 && p.d == 128) return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, stream);
-  if (p.dtype == kBF16 && p.d == 64) return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, stream);
-  if (p.dtype == kF32 && p.d == 128) return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, stream);
-  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, stream);
+                         float* z_part, float* hj, __bf16* hj_hi, __bf16* hj_lo,
+                         hipStream_t stream) {
+  if (p.dtype == kBF16 && p.d == 128)
+    return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, hj_hi, hj_lo, stream);
+  if (p.dtype == kBF16 && p.d == 64)
+    return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, hj_hi, hj_lo, stream);
+  if (p.dtype == kF32 && p.d == 128)
+    return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, hj_hi, hj_lo, stream);
+  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, hj_hi, hj_lo, stream);
 }
 
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,

@@ -77,11 +77,15 @@ typedef struct {
  *   subtracts them from the totals H and Z, and applies relu(Q_i) (no per-block d x d state is
  *   stored or read).
  * SLA_LINEAR_LITERAL: every h_j = relu(K_j)^T V_j is materialised in the workspace and a
- *   separate kernel sums the kept ones per query block before applying relu(Q). */
-enum { SLA_LINEAR_FUSED = 0, SLA_LINEAR_LITERAL = 1 };
+ *   separate kernel sums the kept ones per query block before applying relu(Q).
+ * SLA_LINEAR_MASK_PRODUCT: every h_j is materialised (bf16 hi + lo) and
+ *   T_i = H - sum_{j in sel(i)} h_j is formed for all query blocks at once as the product of the
+ *   0/1 mask with the stacked states (one MFMA GEMM per head); the sparse kernel applies relu(Q)
+ *   to its T_i. */
+enum { SLA_LINEAR_FUSED = 0, SLA_LINEAR_LITERAL = 1, SLA_LINEAR_MASK_PRODUCT = 2 };
 
 typedef struct {
-  int32_t linear_mode;     /* SLA_LINEAR_FUSED or SLA_LINEAR_LITERAL */
+  int32_t linear_mode;     /* SLA_LINEAR_FUSED, SLA_LINEAR_LITERAL or SLA_LINEAR_MASK_PRODUCT */
   hipEvent_t sparse_begin; /* if non-null: recorded on `stream` right before the sparse kernel */
   hipEvent_t sparse_end;   /* if non-null: recorded on `stream` right after it */
   hipEvent_t states_begin; /* if non-null: recorded right before the linear-state kernels */
@@ -90,7 +94,8 @@ typedef struct {
 
 /* Workspace sizes in bytes for a problem (0 when the problem is invalid or unsupported). */
 size_t sla_route_workspace_bytes(const sla_problem* p);
-/* variant: 0 = sla_forward (fused linear), 1 = sla_forward_fp8, 2 = literal linear mode. */
+/* variant: 0 = sla_forward (fused linear), 1 = sla_forward_fp8, 2 = literal linear mode,
+ * 3 = mask-product linear mode. */
 size_t sla_forward_workspace_bytes(const sla_problem* p, int variant);
 
 /* Router (SLA2 Italian summary section 2.B, Arabic summary section 2.ba and 2.dal): block

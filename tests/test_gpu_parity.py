@@ -178,6 +178,43 @@ def test_forward_degenerate_k(k):
         assert np.all(Ol == 0)
 
 
+@pytest.mark.parametrize(
+    "name,wl",
+    [
+        ("tiny", gen.workload("tiny")),
+        ("ragged_bf16", small_ragged()),
+        ("ragged_d64", small_ragged(k=9).with_(d=64, name="ragged_d64")),
+        ("ragged_fp32", small_ragged(k=3).with_(dtype="fp32", name="ragged_fp32")),
+        ("ragged_k0", small_ragged(k=0)),
+        ("ragged_k1", small_ragged(k=1)),
+        ("ragged_k57", small_ragged(k=57)),
+    ],
+)
+def test_forward_mask_product_mode(name, wl):
+    """The mask-product linear mode (all T_i from one mask x states product) against the oracle,
+    on every element, and against the fused mode."""
+    c = case(name, wl)
+    r = oracle_route(c, wl.topk)
+    say(f"forward mask_product {name}")
+    got = run_forward(c, r["idx"], linear_mode="mask_product")
+    ref, _, _ = oracle.forward(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, what=f"forward mask_product {name}")
+    fused = run_forward(c, r["idx"])
+    check_close(got, fused, rel_tol=2e-3, max_tol=5e-3, what=f"mask_product vs fused {name}")
+
+
+def test_mask_product_linear_branch_alone():
+    """alpha = 0: the linear branch alone, built from the mask x states product."""
+    wl = small_ragged()
+    c = case("ragged_bf16", wl)
+    r = oracle_route(c, wl.topk)
+    _, _, Ol = oracle.forward(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    zero = torch.zeros_like(c["alpha"]).to(torch.device("cuda:0"))
+    say("forward mask_product alpha=0")
+    check_close(run_forward(c, r["idx"], alpha=zero, linear_mode="mask_product"), Ol,
+                what="mask_product linear branch (alpha=0)")
+
+
 def test_forward_literal_linear_mode():
     wl = small_ragged()
     c = case("ragged_bf16", wl)
@@ -283,7 +320,7 @@ def sampled_compare(c, idx_np, got_O, heads, blocks, fp8=False, what=""):
         check_close(got, ref, what=what)
 
 
-def full_size(c, heads, blocks, fp8=False, what=""):
+def full_size(c, heads, blocks, fp8=False, what="", linear_mode="fused"):
     wl = c["workload"]
     g = dev(c)
     say(f"route {what}")
@@ -292,7 +329,7 @@ def full_size(c, heads, blocks, fp8=False, what=""):
     assert np.array_equal(idx.cpu().numpy(), r["idx"]), f"{what}: router indices differ"
     assert np.array_equal(mask.cpu().numpy(), r["mask"]), f"{what}: router mask differs"
     say(f"forward {what}")
-    O = sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], fp8=fp8)
+    O = sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], fp8=fp8, linear_mode=linear_mode)
     torch.cuda.synchronize()
     got = O.cpu().double().numpy()
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
@@ -302,6 +339,11 @@ def full_size(c, heads, blocks, fp8=False, what=""):
 def test_video_s_full_size():
     c = case("video_s", gen.workload("video_s"))
     full_size(c, heads=[0, 5, 11], blocks=[0, 1, 200, 511], what="video_s N=32768 H=12 k=51")
+
+
+def test_video_s_full_size_mask_product():
+    c = case("video_s", gen.workload("video_s"))
+    full_size(c, heads=[0, 7], blocks=[0, 300, 511], what="video_s mask_product", linear_mode="mask_product")
 
 
 def test_video_l_full_size():
