@@ -162,6 +162,9 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
   if (tid < D) z_part[((size_t)bh * nchunk + chunk) * D + tid] = zsum;
 }
 
+// One workgroup per 256 consecutive elements of H^T (64 float4 columns): thread t sums every
+// fourth chunk partial starting at chunk t / 64 for the float4 column t % 64, then the four
+// partial sums are added in a fixed order through LDS (deterministic).
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h_part,
                                                      const float* __restrict__ z_part,
@@ -169,28 +172,47 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
                                                      __bf16* __restrict__ ht_lo,
                                                      float* __restrict__ Z,
                                                      float* __restrict__ h_full) {
+  __shared__ f32x4 part[4][64];
   const int bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;  // element of H^T: c = e / D, c' = e % D
-  const float* hp = h_part + (size_t)bh * nchunk * D * D;
-  // fixed summation order (chunk 0, 1, ...), eight loads in flight
-  float s = 0.f;
-  int k = 0;
-  for (; k + 8 <= nchunk; k += 8) {
-    float v[8];
+  const int col = threadIdx.x % 64, grp = threadIdx.x / 64;
+  const int e4 = blockIdx.x * 64 + col;  // float4 index into H^T
+  const f32x4* hp = reinterpret_cast<const f32x4*>(h_part + (size_t)bh * nchunk * D * D);
+  constexpr int ROW4 = D * D / 4;  // float4s per chunk partial
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  int k = grp;
+  for (; k + 12 < nchunk; k += 16) {  // four loads in flight
+    f32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = hp[(size_t)(k + u) * D * D + e];
+    for (int u = 0; u < 4; ++u) v[u] = hp[(size_t)(k + 4 * u) * ROW4 + e4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+    for (int u = 0; u < 4; ++u) s += v[u];
   }
-  for (; k < nchunk; ++k) s += hp[(size_t)k * D * D + e];
-  const __bf16 hi = f2bf(s);
-  ht_hi[(size_t)bh * D * D + e] = hi;
-  ht_lo[(size_t)bh * D * D + e] = f2bf(s - bf2f(hi));
-  if (h_full) h_full[(size_t)bh * D * D + (size_t)(e % D) * D + e / D] = s;
+  for (; k < nchunk; k += 4) s += hp[(size_t)k * ROW4 + e4];
+  part[grp][col] = s;
+  __syncthreads();
+  if (grp == 0) {
+    const f32x4 t = ((part[0][col] + part[1][col]) + part[2][col]) + part[3][col];
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = f2bf(t[e]);
+      lo[e] = f2bf(t[e] - bf2f(hi[e]));
+    }
+    const size_t o = (size_t)bh * D * D + 4 * (size_t)e4;
+    *reinterpret_cast<bf16x4*>(ht_hi + o) = hi;
+    *reinterpret_cast<bf16x4*>(ht_lo + o) = lo;
+    if (h_full) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int el = 4 * e4 + e;  // element of H^T: c = el / D, c' = el % D
+        h_full[(size_t)bh * D * D + (size_t)(el % D) * D + el / D] = t[e];
+      }
+    }
+  }
   if (blockIdx.x == 0 && threadIdx.x < D) {
     const float* zp = z_part + (size_t)bh * nchunk * D;
     float z = 0.f;
-    for (int k = 0; k < nchunk; ++k) z += zp[(size_t)k * D + threadIdx.x];
+    for (int c = 0; c < nchunk; ++c) z += zp[(size_t)c * D + threadIdx.x];
     Z[(size_t)bh * D + threadIdx.x] = z;
   }
 }
@@ -216,11 +238,12 @@ hipError_t launch_states_t(const Dims& p, const void* K, const void* V, float* z
 }  // namespace
 
 int state_chunk_blocks(const Dims& p) {
-  // about >= 512 workgroups while keeping the partials small next to the K/V stream
+  // about >= 512 workgroups (two per CU) while keeping the partials (64 KB per chunk at d = 128)
+  // small next to the K/V stream (32 KB per block)
   const long work = (long)p.nb * p.B * p.H;
   long cb = work / 512;
   if (cb < 1) cb = 1;
-  if (cb > 16) cb = 16;
+  if (cb > 64) cb = 64;
   return (int)cb;
 }
 
@@ -241,7 +264,7 @@ hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* 
                                hipStream_t stream) {
   const int cb = state_chunk_blocks(p);
   const int nchunk = (p.nb + cb - 1) / cb;
-  dim3 grid(p.d * p.d / 256, p.B * p.H);
+  dim3 grid(p.d * p.d / 256, p.B * p.H);  // 256 elements (64 float4 columns) per workgroup
   if (p.d == 128)
     reduce_kernel<128><<<grid, 256, 0, stream>>>(h_part, z_part, nchunk, ht_hi, ht_lo, Z, h_full);
   else
