@@ -377,3 +377,92 @@ def test_sparsity_sweep(scale, k):
         sampled_compare(cc, r["idx"], O.cpu().double().numpy(), heads=[0, 23], blocks=[0, 511],
                         what=f"sweep s={scale} k={k} alpha={a}")
     _CACHE.pop(wl.name, None)  # keep host memory bounded
+
+
+# ---------------------------------------------------------------------------------- edge shapes
+
+
+def edge(name, B, H, N, d, dtype, k):
+    return gen.workload("tiny").with_(name=f"edge_{name}", B=B, H=H, N=N, d=d, dtype=dtype, topk=k, wid=6)
+
+
+EDGE = [
+    edge("n1_d64_f32_k0", 1, 1, 1, 64, "fp32", 0),  # one token, nothing kept
+    edge("n1_d64_f32_k1", 1, 2, 1, 64, "fp32", 1),  # one token, its only block kept
+    edge("n1_d128_bf16_k1", 1, 1, 1, 128, "bf16", 1),
+    edge("n1_d128_bf16_k0", 2, 1, 1, 128, "bf16", 0),
+    edge("n64_d64_bf16_k1", 1, 3, 64, 64, "bf16", 1),  # exactly one full block
+    edge("n65_d128_bf16_k0", 1, 2, 65, 128, "bf16", 0),  # a 1-token tail block
+    edge("n65_d128_bf16_k1", 1, 2, 65, 128, "bf16", 1),
+    edge("n65_d128_f32_k2", 1, 2, 65, 128, "fp32", 2),
+    edge("n127_d64_f32_k1", 2, 1, 127, 64, "fp32", 1),
+    edge("n200_d128_bf16_k2", 2, 3, 200, 128, "bf16", 2),  # batch > 1, 8-token tail
+    edge("n4097_d128_bf16_k33", 1, 1, 4097, 128, "bf16", 33),  # 65 blocks, half kept, 1-token tail
+    edge("n4097_d64_f32_k65", 1, 1, 4097, 64, "fp32", 65),  # every block kept
+]
+
+
+@pytest.mark.parametrize("wl", EDGE, ids=[w.name for w in EDGE])
+def test_edge_shapes(wl):
+    """Tiny and ragged shapes (one token, a one-token tail, one full block, batch > 1, k = 0,
+    1, half and all): router bit-exact, and every linear mode plus the fp8 sparse branch (bf16,
+    d = 128) on every element against the oracle."""
+    c = case(wl.name, wl)
+    g = dev(c)
+    r = oracle_route(c, wl.topk)
+    say(f"edge route {wl.name}")
+    idx, mask, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], wl.topk, want_mask=True)
+    assert idx.shape == (wl.B, wl.H, wl.n_blocks, wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"]), f"{wl.name}: router indices differ"
+    assert np.array_equal(mask.cpu().numpy(), r["mask"]), f"{wl.name}: router mask differs"
+    ref, _, _ = oracle.forward(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    for mode in ("fused", "literal", "mask_product"):
+        say(f"edge forward {wl.name} {mode}")
+        check_close(run_forward(c, r["idx"], linear_mode=mode), ref, what=f"{wl.name} {mode}")
+    if wl.dtype == "bf16" and wl.d == 128:
+        say(f"edge forward {wl.name} fp8")
+        ref8, _, _ = oracle.forward_fp8(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+        check_close(run_forward(c, r["idx"], fp8=True), ref8, rel_tol=TOL_REL_FP8, max_tol=None,
+                    what=f"{wl.name} fp8")
+    _CACHE.pop(wl.name, None)
+
+
+# key-slot counts per lane of the router's top-k: 2, 4, 16, 20, 32 and 32 again at the largest
+# supported n_b (2048); clustered latent grids whose token counts leave a short last block
+ROUTE_GRIDS = [((2, 50, 63), 128), ((4, 50, 63), 64), ((16, 45, 88), 128), ((20, 50, 79), 64),
+               ((24, 50, 79), 128), ((26, 63, 80), 128)]
+
+
+@pytest.mark.parametrize("grid,d", ROUTE_GRIDS, ids=[f"grid{'x'.join(map(str, g))}_d{d}" for g, d in ROUTE_GRIDS])
+def test_route_many_blocks(grid, d):
+    """Every key-slot instantiation of the top-k, up to the largest supported n_b: indices and
+    mask bit-exact; at n_b = 2048 also the forward (fused and mask-product) on sampled blocks."""
+    N = grid[0] * grid[1] * grid[2]
+    nb = -(-N // 64)
+    k = max(1, nb // 10)
+    wl = gen.workload("video_s").with_(name=f"route_nb{nb}", H=1, N=N, d=d, grid=grid, topk=k, wid=7)
+    c = case(wl.name, wl)
+    g = dev(c)
+    say(f"route nb={nb} d={d} k={k}")
+    idx, mask, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], k, want_mask=True)
+    r = oracle_route(c, k)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"]), f"nb={nb}: router indices differ"
+    assert np.array_equal(mask.cpu().numpy(), r["mask"]), f"nb={nb}: router mask differs"
+    if nb == 2048:
+        for mode in ("fused", "mask_product"):
+            say(f"forward nb=2048 {mode}")
+            O = sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], linear_mode=mode)
+            torch.cuda.synchronize()
+            sampled_compare(c, r["idx"], O.cpu().double().numpy(), heads=[0], blocks=[0, 1023, 2047],
+                            what=f"nb=2048 {mode}")
+    _CACHE.pop(wl.name, None)
+
+
+def test_route_rejects_too_many_blocks():
+    """n_b above the largest supported count is an error, not a silent truncation."""
+    nb = 2049
+    d = torch.device("cuda:0")
+    Q = torch.zeros((1, 1, 64 * nb, 64), dtype=torch.bfloat16, device=d)
+    W = torch.eye(64, dtype=torch.float32, device=d)
+    with pytest.raises(Exception):
+        sla.route(Q, Q, W, W, 4)
