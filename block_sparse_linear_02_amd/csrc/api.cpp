@@ -68,7 +68,7 @@ size_t carve_route(const sla::Dims& d, void* ws, RouteWs* out) {
 struct FwdWs {
   float *zb, *h_part, *z_part, *Z, *hj, *h_full;
   __bf16 *ht_hi, *ht_lo;
-  __bf16 *hj_hi, *hj_lo, *t_hi, *t_lo;
+  __bf16 *hj_bf, *t_bf;
   uint32_t* bits;
   uint8_t *q8, *k8, *v8;
   float *sq, *sk, *sv;
@@ -82,7 +82,7 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
   const size_t nchunk = (d.nb + cb - 1) / cb;
   FwdWs f = {};
   f.zb = c.take<float>(BH * d.nb * d.d);
-  f.h_part = c.take<float>(BH * nchunk * dd);
+  if (variant != 3) f.h_part = c.take<float>(BH * nchunk * dd);
   f.z_part = c.take<float>(BH * nchunk * d.d);
   f.Z = c.take<float>(BH * d.d);
   f.ht_hi = c.take<__bf16>(BH * dd);
@@ -92,10 +92,8 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
     f.h_full = c.take<float>(BH * dd);
   }
   if (variant == 3) {
-    f.hj_hi = c.take<__bf16>(BH * d.nb * dd);
-    f.hj_lo = c.take<__bf16>(BH * d.nb * dd);
-    f.t_hi = c.take<__bf16>(BH * d.nb * dd);
-    f.t_lo = c.take<__bf16>(BH * d.nb * dd);
+    f.hj_bf = c.take<__bf16>(BH * d.nb * dd);
+    f.t_bf = c.take<__bf16>(BH * d.nb * dd);
     f.bits = c.take<uint32_t>(BH * d.nb * sla::mask_words(d.nb));
   }
   if (variant == 1) {
@@ -140,14 +138,13 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = hipEventRecord(opts->states_begin, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
-  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, w.hj_hi, w.hj_lo, stream);
+  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, w.hj_bf, stream);
   if (e != hipSuccess) return hip_fail(e);
   e = sla::launch_state_reduce(d, w.h_part, w.z_part, w.ht_hi, w.ht_lo, w.Z, w.h_full, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (mode == SLA_LINEAR_MASK_PRODUCT) {
-    e = sla::launch_mask_bits(d, idx, w.bits, stream);  // all-zero rows when topk == 0
-    if (e == hipSuccess)
-      e = sla::launch_tsel(d, w.hj_hi, w.hj_lo, w.bits, w.ht_hi, w.ht_lo, w.t_hi, w.t_lo, stream);
+    e = sla::launch_mask_bits(d, idx, w.bits, stream);  // every block unselected when topk == 0
+    if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.bits, w.t_bf, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (opts && opts->states_end) {
@@ -168,7 +165,7 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
   else if (mode == SLA_LINEAR_MASK_PRODUCT)
-    e = sla::launch_sparse_tsel(d, Q, K, V, idx, alpha, w.t_hi, w.t_lo, w.Z, w.zb, O, stream);
+    e = sla::launch_sparse_tsel(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream);
   else
     e = sla::launch_sparse(d, Q, K, V, idx, alpha, w.ht_hi, w.ht_lo, w.Z, w.zb, O,
                            mode == SLA_LINEAR_FUSED ? 1 : 0, stream);

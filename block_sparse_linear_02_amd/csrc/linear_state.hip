@@ -12,7 +12,7 @@
 //                  4 wavefronts read them back transposed (ds_read_b64_tr_b16) as MFMA operands
 //                  and accumulate H^T = V^T relu(K) (bf16 MFMA, fp32 accumulation) for the
 //                  chunk, z_j by fp32 sums.  Literal mode also stores every h_j (fp32); the
-//                  mask-product mode stores every h_j as bf16 hi + lo.
+//                  mask-product mode stores every h_j^T rounded to bf16.
 //   reduce_kernel  sums the chunk partials in a fixed order (deterministic), splits H^T into
 //                  bf16 hi + lo parts (the sparse kernel's MFMA operand) and writes Z.
 #include "sla_device.hpp"
@@ -26,14 +26,17 @@ namespace {
 constexpr int kStateThreads = 256;
 
 // MODE: 0 totals only, 1 also every h_j in fp32 in the natural layout h_j[c'][c] (K channel
-// major), 2 also every h_j^T[c][c'] (V channel major) as bf16 hi + lo (hj, hj_lo), stored in
-// slices of 64 entries, slice-major, so that one slice of all blocks is contiguous
+// major), 2 also every h_j^T[c][c'] (V channel major) rounded to bf16, stored in slices of 64
+// entries, slice-major, so that one slice of all blocks is contiguous
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(kStateThreads) void state_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int N, int nb, int cb,
     float* __restrict__ zb, float* __restrict__ h_part, float* __restrict__ z_part,
-    void* __restrict__ hj, __bf16* __restrict__ hj_lo) {
+    void* __restrict__ hj) {
   constexpr bool LITERAL = MODE != 0;
+  // MODE 2 computes h_j = relu(K_j)^T V_j (rows: K channels) so that a lane's four consecutive
+  // accumulator rows are four consecutive entries of a row of h_j^T; the others V^T relu(K)
+  constexpr bool SWAP = MODE == 2;
   constexpr int NT = D / 64;  // 32x32 output tiles per wave per dimension (D=128: 2, D=64: 1)
   __shared__ __attribute__((aligned(16))) __bf16 Ks[TileLayout<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[TileLayout<D>::ELEMS];
@@ -52,13 +55,15 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
   const int r0 = (wave / 2) * 32 * NT;
   const int c0 = (wave % 2) * 32 * NT;
 
+  // MODE 2 needs no totals of h (its linear branch sums the unselected h_j directly)
+  constexpr bool TOT = MODE == 1;
   f32x16 acc[NT][NT];
-  f32x16 tot[LITERAL ? NT : 1][LITERAL ? NT : 1];
+  f32x16 tot[TOT ? NT : 1][TOT ? NT : 1];
 #pragma unroll
   for (int a = 0; a < NT; ++a)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = f32x16{};
-  if constexpr (LITERAL) {
+  if constexpr (TOT) {
 #pragma unroll
     for (int a = 0; a < NT; ++a)
 #pragma unroll
@@ -90,7 +95,8 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
 #pragma unroll
       for (int a = 0; a < NT; ++a)
 #pragma unroll
-        for (int b = 0; b < NT; ++b) acc[a][b] = mfma32(av[a], bk[b], acc[a][b]);
+        for (int b = 0; b < NT; ++b)
+          acc[a][b] = SWAP ? mfma32(bk[b], av[a], acc[a][b]) : mfma32(av[a], bk[b], acc[a][b]);
     }
     // z_j = sum over the tile's rows of relu(K)
     {
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
         s += fmaxf(bf2f(Ks[TileLayout<D>::off(n, c)]), 0.f);
       zred[part][c] = s;
     }
-    if constexpr (LITERAL) {
+    if constexpr (MODE == 1) {
       // store h_j in natural layout h_j[c'][c]; lane holds c' = col, c = rows 8(i/4)+4g+i%4
       const size_t hoff = ((size_t)bh * nb + j) * D * D;
 #pragma unroll
@@ -113,27 +119,53 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c = r0 + 32 * a + 8 * q + 4 * (lane / 32);
-            const size_t o = hoff + (size_t)cp * D + c;
-            if constexpr (MODE == 1) {
-              f32x4 v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                         acc[a][b][4 * q + 3]};
-              *reinterpret_cast<f32x4*>(static_cast<float*>(hj) + o) = v;
-            } else {
-              // h_j^T[c][c'] in 64-entry slices, slice-major ([bh][n / 64][j][n % 64] with
-              // n = c D + c'): the 32 lanes of a half-wavefront write 32 consecutive c'
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int n = (c + e) * D + cp;
-                const size_t ot = (((size_t)bh * (D * D / 64) + n / 64) * nb + j) * 64 + n % 64;
-                const __bf16 vh = f2bf(acc[a][b][4 * q + e]);
-                static_cast<__bf16*>(hj)[ot] = vh;
-                hj_lo[ot] = f2bf(acc[a][b][4 * q + e] - bf2f(vh));
-              }
-            }
+            f32x4 v = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                       acc[a][b][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(static_cast<float*>(hj) + hoff + (size_t)cp * D + c) = v;
           }
           tot[a][b] += acc[a][b];
           acc[a][b] = f32x16{};
         }
+    }
+    if constexpr (MODE == 2) {
+      // h_j^T[c][c'] in bf16, in 64-entry slices, slice-major ([bh][n / 64][j][n % 64] with
+      // n = c D + c').  The wave's quadrant (c = r0 + 0..32NT-1, c' = c0 + 0..32NT-1) is staged
+      // in LDS, where the K and V tiles are no longer needed, as rows of c' (16-byte chunks
+      // XOR-swizzled by row), then stored with 16-byte writes.
+      constexpr int RL = 32 * NT;          // entries per staged row
+      constexpr int CH = RL / 8;           // 16-byte chunks per row
+      constexpr int RPL = 128 / RL;        // rows per 256-byte line of banks
+      auto soff = [&](int row, int chunk) { return row * RL + ((chunk ^ ((row / RPL) & (CH - 1))) << 3); };
+      __syncthreads();  // every wave is done reading Ks and Vs
+      __bf16* stg = (wave < 2 ? Ks : Vs) + (wave % 2) * RL * RL;
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // rows c' = c0 + 32 b + 8 q + 4 g + e, column c = r0 + 32 a + lane % 32
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = f2bf(acc[a][b][4 * q + e]);
+            const int row = 32 * a + lane % 32, col = 32 * b + 8 * q + 4 * (lane / 32);
+            *reinterpret_cast<bf16x4*>(stg + soff(row, col / 8) + (col & 4)) = v;
+          }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __bf16* dst = static_cast<__bf16*>(hj);
+#pragma unroll
+      for (int u = 0; u < RL * CH / kWave; ++u) {
+        const int k = lane + kWave * u;
+        const int row = k / CH, chunk = k % CH;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + soff(row, chunk));
+        const int n = (r0 + row) * D + c0 + 8 * chunk;
+        *reinterpret_cast<bf16x8*>(dst + (((size_t)bh * (D * D / 64) + n / 64) * nb + j) * 64 + n % 64) = v;
+      }
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int b = 0; b < NT; ++b) acc[a][b] = f32x16{};
     }
     __syncthreads();
     if (tid < D) {
@@ -145,26 +177,29 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
     }
   }
 
-  // chunk partial of H^T [c][c'] and Z
-  float* hp = h_part + ((size_t)bh * nchunk + chunk) * D * D;
+  // chunk partial of H^T [c][c'] (not in MODE 2) and Z
+  if constexpr (MODE != 2) {
+    float* hp = h_part + ((size_t)bh * nchunk + chunk) * D * D;
 #pragma unroll
-  for (int a = 0; a < NT; ++a)
+    for (int a = 0; a < NT; ++a)
 #pragma unroll
-    for (int b = 0; b < NT; ++b) {
-      const f32x16 v = LITERAL ? tot[LITERAL ? a : 0][LITERAL ? b : 0] : acc[a][b];
-      const int cp = c0 + 32 * b + lane % 32;
+      for (int b = 0; b < NT; ++b) {
+        const f32x16 v = TOT ? tot[TOT ? a : 0][TOT ? b : 0] : acc[a][b];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = r0 + 32 * a + 8 * (i / 4) + 4 * (lane / 32) + i % 4;
-        hp[(size_t)c * D + cp] = v[i];
+        for (int i = 0; i < 16; ++i) {
+          const int c = r0 + 32 * a + 8 * (i / 4) + 4 * (lane / 32) + i % 4;
+          const int cp = c0 + 32 * b + lane % 32;
+          hp[(size_t)c * D + cp] = v[i];
+        }
       }
-    }
+  }
   if (tid < D) z_part[((size_t)bh * nchunk + chunk) * D + tid] = zsum;
 }
 
 // One workgroup per 256 consecutive elements of H^T (64 float4 columns): thread t sums every
 // fourth chunk partial starting at chunk t / 64 for the float4 column t % 64, then the four
-// partial sums are added in a fixed order through LDS (deterministic).
+// partial sums are added in a fixed order through LDS (deterministic).  Without chunk partials of
+// H (h_part null, mask-product mode) only Z is reduced.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h_part,
                                                      const float* __restrict__ z_part,
@@ -175,37 +210,39 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
   __shared__ f32x4 part[4][64];
   const int bh = blockIdx.y;
   const int col = threadIdx.x % 64, grp = threadIdx.x / 64;
-  const int e4 = blockIdx.x * 64 + col;  // float4 index into H^T
-  const f32x4* hp = reinterpret_cast<const f32x4*>(h_part + (size_t)bh * nchunk * D * D);
-  constexpr int ROW4 = D * D / 4;  // float4s per chunk partial
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  int k = grp;
-  for (; k + 12 < nchunk; k += 16) {  // four loads in flight
-    f32x4 v[4];
+  if (h_part) {
+    const int e4 = blockIdx.x * 64 + col;  // float4 index into H^T
+    const f32x4* hp = reinterpret_cast<const f32x4*>(h_part + (size_t)bh * nchunk * D * D);
+    constexpr int ROW4 = D * D / 4;  // float4s per chunk partial
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    int k = grp;
+    for (; k + 12 < nchunk; k += 16) {  // four loads in flight
+      f32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = hp[(size_t)(k + 4 * u) * ROW4 + e4];
+      for (int u = 0; u < 4; ++u) v[u] = hp[(size_t)(k + 4 * u) * ROW4 + e4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s += v[u];
-  }
-  for (; k < nchunk; k += 4) s += hp[(size_t)k * ROW4 + e4];
-  part[grp][col] = s;
-  __syncthreads();
-  if (grp == 0) {
-    const f32x4 t = ((part[0][col] + part[1][col]) + part[2][col]) + part[3][col];
-    bf16x4 hi, lo;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      hi[e] = f2bf(t[e]);
-      lo[e] = f2bf(t[e] - bf2f(hi[e]));
+      for (int u = 0; u < 4; ++u) s += v[u];
     }
-    const size_t o = (size_t)bh * D * D + 4 * (size_t)e4;
-    *reinterpret_cast<bf16x4*>(ht_hi + o) = hi;
-    *reinterpret_cast<bf16x4*>(ht_lo + o) = lo;
-    if (h_full) {
+    for (; k < nchunk; k += 4) s += hp[(size_t)k * ROW4 + e4];
+    part[grp][col] = s;
+    __syncthreads();
+    if (grp == 0) {
+      const f32x4 t = ((part[0][col] + part[1][col]) + part[2][col]) + part[3][col];
+      bf16x4 hi, lo;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int el = 4 * e4 + e;  // element of H^T: c = el / D, c' = el % D
-        h_full[(size_t)bh * D * D + (size_t)(el % D) * D + el / D] = t[e];
+        hi[e] = f2bf(t[e]);
+        lo[e] = f2bf(t[e] - bf2f(hi[e]));
+      }
+      const size_t o = (size_t)bh * D * D + 4 * (size_t)e4;
+      *reinterpret_cast<bf16x4*>(ht_hi + o) = hi;
+      *reinterpret_cast<bf16x4*>(ht_lo + o) = lo;
+      if (h_full) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int el = 4 * e4 + e;  // element of H^T: c = el / D, c' = el % D
+          h_full[(size_t)bh * D * D + (size_t)(el % D) * D + el / D] = t[e];
+        }
       }
     }
   }
@@ -219,19 +256,19 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
 
 template <class T, int D>
 hipError_t launch_states_t(const Dims& p, const void* K, const void* V, float* zb,
-                           float* h_part, float* z_part, float* hj, __bf16* hj_hi,
-                           __bf16* hj_lo, hipStream_t stream) {
+                           float* h_part, float* z_part, float* hj, __bf16* hj_bf,
+                           hipStream_t stream) {
   const int cb = state_chunk_blocks(p);
   dim3 grid((p.nb + cb - 1) / cb, p.B * p.H);
   if (hj)
     state_kernel<T, D, 1><<<grid, kStateThreads, 0, stream>>>(
-        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj, nullptr);
-  else if (hj_hi)
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj);
+  else if (hj_bf)
     state_kernel<T, D, 2><<<grid, kStateThreads, 0, stream>>>(
-        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj_hi, hj_lo);
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj_bf);
   else
     state_kernel<T, D, 0><<<grid, kStateThreads, 0, stream>>>(
-        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, nullptr, nullptr);
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, nullptr);
   return hipGetLastError();
 }
 
@@ -248,15 +285,15 @@ int state_chunk_blocks(const Dims& p) {
 }
 
 hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
-                         float* z_part, float* hj, __bf16* hj_hi, __bf16* hj_lo,
+                         float* z_part, float* hj, __bf16* hj_bf,
                          hipStream_t stream) {
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, hj_hi, hj_lo, stream);
+    return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream);
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, hj_hi, hj_lo, stream);
+    return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, hj_hi, hj_lo, stream);
-  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, hj_hi, hj_lo, stream);
+    return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream);
+  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream);
 }
 
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,
@@ -264,7 +301,8 @@ hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* 
                                hipStream_t stream) {
   const int cb = state_chunk_blocks(p);
   const int nchunk = (p.nb + cb - 1) / cb;
-  dim3 grid(p.d * p.d / 256, p.B * p.H);  // 256 elements (64 float4 columns) per workgroup
+  // 256 elements (64 float4 columns) of H^T per workgroup; Z alone without chunk partials of H
+  dim3 grid(h_part ? p.d * p.d / 256 : 1, p.B * p.H);
   if (p.d == 128)
     reduce_kernel<128><<<grid, 256, 0, stream>>>(h_part, z_part, nchunk, ht_hi, ht_lo, Z, h_full);
   else

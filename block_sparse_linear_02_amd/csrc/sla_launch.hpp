@@ -22,30 +22,27 @@ size_t route_lds_bytes(int nb);
 int route_max_blocks();
 
 // Linear-branch states. Per chunk of `chunk_blocks` key blocks: partial H^T [d][d] and partial
-// Z [d]; per block z_j [d]; optionally every h_j [d][d] (K-channel major), in fp32 (hj, literal
-// mode) or transposed, h_j^T [d][d] (V-channel major), as bf16 hi + lo (hj_hi, hj_lo,
-// mask-product mode) in slices of 64 entries: [BH][d*d/64][nb][64].
+// Z [d]; per block z_j [d]; optionally every h_j [d][d] (K-channel major) in fp32 (hj, literal
+// mode), or transposed, h_j^T [d][d] (V-channel major), rounded to bf16 (hj_bf, mask-product
+// mode) in slices of 64 entries: [BH][d*d/64][nb][64].
 int state_chunk_blocks(const Dims& p);
 hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
-                         float* z_part, float* hj, __bf16* hj_hi, __bf16* hj_lo,
-                         hipStream_t stream);
+                         float* z_part, float* hj, __bf16* hj_bf, hipStream_t stream);
 
-// Mask-product mode: the router's index lists as bit rows [BH][nb][mask_words(nb)], then
-// T_i^T = H^T - sum_{j in sel(i)} h_j^T for every query block as bf16 hi + lo [BH][nb][d][d]
-// (V-channel major), from the per-block states h_j^T (bf16 hi + lo) and H^T (bf16 hi + lo).
+// Mask-product mode: the complements of the router's index lists as bit rows
+// [BH][nb][mask_words(nb)], then T_i^T = sum_{j not in sel(i)} h_j^T for every query block in
+// bf16 [BH][nb][d][d] (V-channel major), from the per-block states h_j^T (bf16).
 int mask_words(int nb);
 hipError_t launch_mask_bits(const Dims& p, const int32_t* idx, uint32_t* bits,
                             hipStream_t stream);
-hipError_t launch_tsel(const Dims& p, const __bf16* hj_hi, const __bf16* hj_lo,
-                       const uint32_t* bits, const __bf16* ht_hi, const __bf16* ht_lo,
-                       __bf16* t_hi, __bf16* t_lo, hipStream_t stream);
-// Sparse branch with the linear part from the precomputed T_i (hi + lo) and zeta from z_j.
+hipError_t launch_tsel(const Dims& p, const __bf16* hj_bf, const uint32_t* bits, __bf16* t_bf,
+                       hipStream_t stream);
+// Sparse branch with the linear part from the precomputed T_i (bf16) and zeta from z_j.
 hipError_t launch_sparse_tsel(const Dims& p, const void* Q, const void* K, const void* V,
-                              const int32_t* idx, const float* alpha, const __bf16* t_hi,
-                              const __bf16* t_lo, const float* Z, const float* zb, float* O,
-                              hipStream_t stream);
+                              const int32_t* idx, const float* alpha, const __bf16* t_bf,
+                              const float* Z, const float* zb, float* O, hipStream_t stream);
 // Reduce the chunk partials (fixed order): H^T as bf16 hi/lo [d][d], Z [d]; optionally H [d][d]
-// in fp32 (K-channel major, literal mode).
+// in fp32 (K-channel major, literal mode); Z alone when h_part is null (mask-product mode).
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,
                                __bf16* ht_hi, __bf16* ht_lo, float* Z, float* h_full,
                                hipStream_t stream);

@@ -16,7 +16,7 @@
 // halves of a row are merged once at the end (max / rescale / add of two partial softmax
 // states).  K_j, V_j tiles are double-buffered in LDS, one array per buffer so that the compiler
 // can tell the buffer being filled by direct-to-LDS loads from the one being read.
-// Epilogue: T_i^T (bf16 hi + lo, [c][c']) is loaded into the free tile buffers, zeta = Z -
+// Epilogue: T_i^T (bf16, [c][c']) is loaded into a free tile buffer, zeta = Z -
 // sum_kept z_j; wavefront (qh, kh) computes, for its 32 rows and channel half kh,
 // num = relu(Q) T_i by MFMA, den = relu(q) . zeta, and O = alpha O_s / l + (1 - alpha) num / den
 // (the linear part is 0 when nothing is unselected or den == 0), fp32 stores; rows past N are
@@ -106,9 +106,9 @@ template <class T, int D, int QH, int KH>
 __device__ __forceinline__ void split_wave(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
-    const __bf16* __restrict__ t_hi_g, const __bf16* __restrict__ t_lo_g,
-    const float* __restrict__ Z, const float* __restrict__ zb, float* __restrict__ O, int N,
-    int nb, int topk, float c_log2, __bf16* lq, __bf16* lb0, __bf16* lb1, int bh, int qb) {
+    const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
+    float* __restrict__ O, int N, int nb, int topk, float c_log2, __bf16* lq, __bf16* lb0,
+    __bf16* lb1, int bh, int qb) {
   using S_ = SplitShape<T, D>;
   constexpr int NS = S_::NS, NC = S_::NC, HC = S_::HC, PITCH = S_::PITCH, TILE = S_::TILE;
   constexpr bool SPLIT = S_::SPLIT;
@@ -335,6 +335,22 @@ __device__ __forceinline__ void split_wave(
     if (t + 1 < topk) step(t + 1, std::integral_constant<int, 1>{});
   }
 
+  // T_i^T [c][c'] into tile buffer 1, free since the last step's barrier (buffer 0 takes the
+  // split-K exchange below), in the tile row layout; awaited before the epilogue's MFMAs
+  {
+    const __bf16* th = t_g + ((size_t)bh * nb + qb) * D * D;
+#pragma unroll
+    for (int half = 0; half < D / kBlock; ++half) {
+      if constexpr (D == 128) {
+        load_tile_direct<kSplitThreads>(th + half * kBlock * D, lb1 + half * kBlock * D, tid);
+      } else {
+        TileLoader<__bf16, D, kSplitThreads> ld;
+        ld.load(th + half * kBlock * D, kBlock, tid);
+        ld.store(lb1 + half * TILE, tid);
+      }
+    }
+  }
+
   // ---- merge the two key halves of each row: wavefront w hands the channel half it does not
   // own to its partner w ^ 2 and takes the partner's share of its own half ----
   if (topk == 0) {  // the Q tile's direct loads may still be landing in the region reused below
@@ -371,23 +387,6 @@ __device__ __forceinline__ void split_wave(
   f32x16 num[HC];
   float inv_den = 0.f;
   {
-    __syncthreads();  // the exchange area becomes T_i
-    // T_i^T [c][c'], hi into buffer 0 and lo into buffer 1, in the tile row layout
-    const __bf16* th = t_hi_g + ((size_t)bh * nb + qb) * D * D;
-    const __bf16* tl = t_lo_g + ((size_t)bh * nb + qb) * D * D;
-#pragma unroll
-    for (int half = 0; half < D / kBlock; ++half) {
-      if constexpr (D == 128) {
-        load_tile_direct<kSplitThreads>(th + half * kBlock * D, lb0 + half * kBlock * D, tid);
-        load_tile_direct<kSplitThreads>(tl + half * kBlock * D, lb1 + half * kBlock * D, tid);
-      } else {
-        TileLoader<__bf16, D, kSplitThreads> ld;
-        ld.load(th + half * kBlock * D, kBlock, tid);
-        ld.store(lb0 + half * TILE, tid);
-        ld.load(tl + half * kBlock * D, kBlock, tid);
-        ld.store(lb1 + half * TILE, tid);
-      }
-    }
     if (z_lane) zeta[tid] = Z[(size_t)bh * D + tid] - zacc;
     wait_vmem();
     __syncthreads();
@@ -403,7 +402,6 @@ __device__ __forceinline__ void split_wave(
 #pragma unroll
       for (int cc = 0; cc < HC; ++cc) {
         num[cc] = mfma32(rd_row(lb1, c0 + 32 * cc, k), pq, num[cc]);
-        num[cc] = mfma32(rd_row(lb0, c0 + 32 * cc, k), pq, num[cc]);
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[16 * k + 8 * g + jj];
@@ -434,9 +432,8 @@ template <class T, int D>
 __global__ __launch_bounds__(kSplitThreads, 2) void split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
-    const __bf16* __restrict__ t_hi_g, const __bf16* __restrict__ t_lo_g,
-    const float* __restrict__ Z, const float* __restrict__ zb, float* __restrict__ O, int N,
-    int nb, int topk, float c_log2) {
+    const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
+    float* __restrict__ O, int N, int nb, int topk, float c_log2) {
   using S_ = SplitShape<T, D>;
   __shared__ __attribute__((aligned(16))) __bf16 lq[S_::QBUF];
   __shared__ __attribute__((aligned(16))) __bf16 lb0[S_::BUF];
@@ -445,7 +442,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void split_kernel(
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / nb, qb = item % nb;
 #define SLA_WAVE(QH_, KH_) \
-  split_wave<T, D, QH_, KH_>(Q, K, V, idx, alpha, t_hi_g, t_lo_g, Z, zb, O, N, nb, topk, c_log2, lq, lb0, lb1, bh, qb)
+  split_wave<T, D, QH_, KH_>(Q, K, V, idx, alpha, t_g, Z, zb, O, N, nb, topk, c_log2, lq, lb0, lb1, bh, qb)
   // one instantiation per wavefront quarter, so that its row, key and channel offsets are
   // compile-time constants (immediate LDS offsets instead of address registers)
   switch (w) {
@@ -459,13 +456,12 @@ __global__ __launch_bounds__(kSplitThreads, 2) void split_kernel(
 
 template <class T, int D>
 hipError_t launch_split_t(const Dims& p, const void* Q, const void* K, const void* V,
-                          const int32_t* idx, const float* alpha, const __bf16* t_hi,
-                          const __bf16* t_lo, const float* Z, const float* zb, float* O,
-                          hipStream_t stream) {
+                          const int32_t* idx, const float* alpha, const __bf16* t_bf,
+                          const float* Z, const float* zb, float* O, hipStream_t stream) {
   const int total = p.B * p.H * p.nb;
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   split_kernel<T, D><<<total, kSplitThreads, 0, stream>>>(
-      (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_hi, t_lo, Z, zb, O, p.N, p.nb, p.topk,
+      (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
       c_log2);
   return hipGetLastError();
 }
@@ -473,16 +469,15 @@ hipError_t launch_split_t(const Dims& p, const void* Q, const void* K, const voi
 }  // namespace
 
 hipError_t launch_sparse_tsel(const Dims& p, const void* Q, const void* K, const void* V,
-                              const int32_t* idx, const float* alpha, const __bf16* t_hi,
-                              const __bf16* t_lo, const float* Z, const float* zb, float* O,
-                              hipStream_t stream) {
+                              const int32_t* idx, const float* alpha, const __bf16* t_bf,
+                              const float* Z, const float* zb, float* O, hipStream_t stream) {
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_split_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_hi, t_lo, Z, zb, O, stream);
+    return launch_split_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_split_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_hi, t_lo, Z, zb, O, stream);
+    return launch_split_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_split_t<float, 128>(p, Q, K, V, idx, alpha, t_hi, t_lo, Z, zb, O, stream);
-  return launch_split_t<float, 64>(p, Q, K, V, idx, alpha, t_hi, t_lo, Z, zb, O, stream);
+    return launch_split_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
+  return launch_split_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
 }
 
 }  // namespace sla
