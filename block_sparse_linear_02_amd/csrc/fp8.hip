@@ -354,6 +354,15 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
       wait_vmem();
       __syncthreads();
     });
+    // this row of Q for the linear numerator, read before the barrier so that the loads are in
+    // flight while it waits (unconditional, from a clamped row: a load under a branch makes the
+    // compiler wait for it on the spot)
+    bf16x8 qv[NS];
+    {
+      const __bf16* qr = Q + hoff + (size_t)min(row, N - 1) * D + 8 * g;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) qv[k] = *reinterpret_cast<const bf16x8*>(qr + 16 * k);
+    }
     __syncthreads();  // the state role has written T and zeta
 
     // epilogue (as in the bf16 kernel): linear numerator relu(Q) T, denominator, combine
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
     float den = 0.f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const bf16x8 pq = relu8(row_ok ? *reinterpret_cast<const bf16x8*>(Q + hoff + (size_t)row * D + 16 * k + 8 * g) : bf16x8{});
+      const bf16x8 pq = relu8(row_ok ? qv[k] : bf16x8{});
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int off = TileLayout<D>::off(32 * c + lane % 32, 16 * k + 8 * g);

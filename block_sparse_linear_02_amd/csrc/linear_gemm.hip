@@ -14,14 +14,15 @@
 //
 //   mask_bits_kernel  per (b, h, query block): the ascending index list -> a bit row of the
 //                     unselected blocks (n_b bits in 32-bit words), the GEMM's B operand source.
-//   tsel_kernel       T^T = h^T U^T on v_mfma_f32_32x32x16_bf16: rows = 64 columns of h (a slice
-//                     of the d*d state entries), columns = 512 query blocks, k = key blocks in
-//                     stages of kGemmK.  h is stored in bf16, the sum is accumulated in fp32 and
+//   tsel_kernel       T^T = h^T U^T on v_mfma_f32_32x32x16_bf16: rows = 128 columns of h (two
+//                     slices of the d*d state entries), columns = 256 query blocks, k = key
+//                     blocks in stages of kGemmK; each wavefront takes all 128 rows and 64
+//                     columns, so every decoded mask operand feeds four MFMAs.  h is stored in bf16, the sum is accumulated in fp32 and
 //                     T is rounded to bf16 once (a relative error of about 2^-9 on the linear
 //                     branch's state); the h stage goes HBM -> LDS by direct loads into rows of
-//                     128 bytes whose 16-byte chunks are XOR-swizzled (chunk c of row j at
-//                     c ^ 4((j >> 1) & 1)) so that the transposed operand reads
-//                     (ds_read_b64_tr_b16) hit distinct banks; the mask operand is 8 bits per
+//                     256 bytes whose 16-byte chunks are XOR-swizzled (chunk c of row j at
+//                     c ^ 4 (j & 3)) so that the transposed operand reads (ds_read_b64_tr_b16)
+//                     of four consecutive rows hit distinct banks; the mask operand is 8 bits per
 //                     lane turned into eight bf16 0/1 values by integer arithmetic.  Epilogue:
 //                     T_i in bf16, in the transposed state layout [c][c'] (V channel major) per
 //                     query block, staged through LDS so that every lane stores 16 contiguous
@@ -37,11 +38,13 @@ namespace sla {
 namespace {
 
 constexpr int kGemmThreads = 256;
-constexpr int kGemmN = 64;    // state entries (rows of C^T) per workgroup
-constexpr int kGemmM = 512;   // query blocks (columns of C^T) per workgroup
+constexpr int kGemmN = 128;   // state entries (rows of T^T) per workgroup
+constexpr int kGemmRT = kGemmN / 32;      // 32-row tiles per wavefront (all of them)
+constexpr int kGemmM = 256;   // query blocks (columns of T^T) per workgroup
 constexpr int kGemmCT = kGemmM / 4 / 32;  // 32-column tiles per wavefront
 constexpr int kGemmK = 128;   // key blocks per LDS stage
-constexpr int kGemmKW = kGemmK / 32;  // mask words per stage
+constexpr int kGemmKW = kGemmK / 32;      // mask words per stage
+constexpr int kSlice = 64;    // entries per slice of the stored h_j^T
 
 __global__ __launch_bounds__(256) void mask_bits_kernel(const int32_t* __restrict__ idx, int nb,
                                                         int topk, int nw,
@@ -68,9 +71,10 @@ __global__ __launch_bounds__(256) void mask_bits_kernel(const int32_t* __restric
   bits[((size_t)bh * nb + i) * nw + w] = all & ~word;
 }
 
-// byte offset of element (row j, column c) of an h stage tile [kGemmK][kGemmN] bf16
+// byte offset of element (row j, column c) of an h stage [kGemmK][kGemmN] bf16: rows of 256
+// bytes, 16-byte chunk c of row j at c ^ 4 (j & 3)
 __device__ __forceinline__ int hs_off(int j, int c) {
-  return j * 128 + ((((c >> 3) ^ (4 * ((j >> 1) & 1)))) << 4) + (c & 7) * 2;
+  return j * (2 * kGemmN) + (((c >> 3) ^ (4 * (j & 3))) << 4) + (c & 7) * 2;
 }
 
 // eight mask bits (bit e = key block 8 g + e of the k step) as eight bf16 0/1 values: each
@@ -98,8 +102,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
   using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave, g = lane / 32;
-  // workgroup -> (query-block tile, state slice, head) with the query-block tiles fastest, so
-  // that the workgroups reading the same slice of h run next to each other on one XCD
+  // workgroup -> (query-block tile, state rows, head) with the query-block tiles fastest, so
+  // that the workgroups reading the same rows of h run next to each other on one XCD
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int mt = item % tiles_m;
   const int nt = (item / tiles_m) % tiles_n;
@@ -107,53 +111,65 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
   const int n0 = nt * kGemmN;
   const int i0 = mt * kGemmM + 32 * kGemmCT * w;  // this wavefront's query blocks
 
-  // this workgroup's slice of every block's state: [j][64] contiguous (slice-major layout)
-  const __bf16* hh = hj + ((size_t)bh * (DD / kGemmN) + nt) * nb * kGemmN;
+  // this workgroup's two slices of every block's state (slice-major: [j][64] contiguous each)
+  const __bf16* hh = hj + ((size_t)bh * (DD / kSlice) + n0 / kSlice) * nb * kSlice;
   const uint32_t* brow = bits + (size_t)bh * nb * nw;
   const int nstage = (nb + kGemmK - 1) / kGemmK;
 
   // stage s: rows j = kGemmK s + 0 .. kGemmK - 1 (clamped to n_b - 1: their mask bits are 0),
-  // 128 bytes each; each 1 KB direct load covers 8 rows
+  // 256 bytes each (chunks 0..7 from the first slice, 8..15 from the second); each 1 KB direct
+  // load covers 4 rows, wavefront w loads rows 32 w .. 32 w + 31
   auto stage = [&](int s, auto BUFC) {
     __bf16* dst = buf(BUFC);
 #pragma unroll
-    for (int u = 0; u < kGemmK / 32; ++u) {
-      const int r0 = (kGemmK / 4) * w + 8 * u;
-      const int r = r0 + lane / 8;
+    for (int u = 0; u < kGemmK / 16; ++u) {
+      const int r0 = (kGemmK / 4) * w + 4 * u;
+      const int r = r0 + lane / 16;
       const int j = min(kGemmK * s + r, nb - 1);
-      const int chunk = (lane % 8) ^ (4 * ((r >> 1) & 1));
-      load_lds16(hh + (size_t)j * kGemmN + chunk * 8, dst + r0 * kGemmN);
+      const int chunk = (lane % 16) ^ (4 * (r & 3));
+      load_lds16(hh + ((size_t)(chunk / 8) * nb + j) * kSlice + (chunk % 8) * 8, dst + r0 * kGemmN);
     }
   };
-  // mask words of this lane's query-block columns (i0 + 32 ct + lane % 32) for stage s
+  // mask words of this lane's query-block columns (i0 + 32 ct + lane % 32) for stage s; words
+  // past the row are read clamped and zeroed when used (no branch around the loads and no use
+  // right after them: either makes the compiler wait for every outstanding load, the stage
+  // prefetch included, on the spot)
   uint32_t mw[kGemmCT][kGemmKW];
   auto mask_words = [&](int s) {
 #pragma unroll
     for (int ct = 0; ct < kGemmCT; ++ct) {
       const int i = min(i0 + 32 * ct + lane % 32, nb - 1);
 #pragma unroll
-      for (int h = 0; h < kGemmKW; ++h) {
-        const int word = kGemmKW * s + h;
-        mw[ct][h] = word < nw ? brow[(size_t)i * nw + word] : 0u;
-      }
+      for (int h = 0; h < kGemmKW; ++h)
+        mw[ct][h] = brow[(size_t)i * nw + min(kGemmKW * s + h, nw - 1)];
     }
   };
 
-  f32x16 acc[2][kGemmCT];  // [state row tile][query-block column tile]
+  f32x16 acc[kGemmRT][kGemmCT];  // [state row tile][query-block column tile]
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kGemmRT; ++a)
 #pragma unroll
     for (int b = 0; b < kGemmCT; ++b) acc[a][b] = f32x16{};
 
-  auto tr_a = [&](const __bf16* tile, int row0, int col0) -> bf16x8 {
-    // A operand (h^T): lane gets column col0 + lane%32 at rows row0 + 8g + {0..3} and {4..7}
+  // A operand (h^T) of k step ks and row tile a: lane gets column 32 a + lane%32 at rows
+  // 16 ks + 8 gg + {0..3} and {4..7}, byte offsets hs_off(16 ks + 8 gg + L/4, 32 a + 16 cs +
+  // 4 (L%4)) and 1024 past it, i.e. pa[a] + 4096 ks with pa[a] depending on the lane only (the
+  // swizzle depends on j & 3).  The lane parts are laundered through an empty asm so that every
+  // read address stays one offset from the stage array: the compiler then keeps track of which
+  // array each read touches and does not make the reads of one stage wait for the direct loads
+  // into the other.
+  int pa[kGemmRT];
+  {
     const int hq = lane / 16, L = lane % 16;
     const int gg = hq / 2, cs = hq % 2;
-    const int r = row0 + 8 * gg + L / 4;
-    const int c = col0 + 16 * cs + 4 * (L % 4);
-    const char* base = reinterpret_cast<const char*>(tile);
-    return join_tr(lds_read_tr16(reinterpret_cast<const __bf16*>(base + hs_off(r, c))),
-                   lds_read_tr16(reinterpret_cast<const __bf16*>(base + hs_off(r + 4, c))));
+#pragma unroll
+    for (int a = 0; a < kGemmRT; ++a) pa[a] = hs_off(8 * gg + L / 4, 32 * a + 16 * cs + 4 * (L % 4));
+    asm volatile("" : "+v"(pa[0]), "+v"(pa[1]), "+v"(pa[2]), "+v"(pa[3]));
+  }
+  auto tr_a = [&](const __bf16* tile, int ks, int a) -> bf16x8 {
+    const char* p = reinterpret_cast<const char*>(tile) + pa[a] + 16 * ks * (2 * kGemmN);
+    return join_tr(lds_read_tr16(reinterpret_cast<const __bf16*>(p)),
+                   lds_read_tr16(reinterpret_cast<const __bf16*>(p + 4 * (2 * kGemmN))));
   };
 
   stage(0, B0{});
@@ -166,7 +182,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
 #pragma unroll
     for (int ct = 0; ct < kGemmCT; ++ct)
 #pragma unroll
-      for (int h = 0; h < kGemmKW; ++h) cur[ct][h] = mw[ct][h];
+      for (int h = 0; h < kGemmKW; ++h) cur[ct][h] = kGemmKW * s + h < nw ? mw[ct][h] : 0u;
     if (s + 1 < nstage) {
       stage(s + 1, std::integral_constant<int, 1 - BUF>{});
       mask_words(s + 1);
@@ -179,11 +195,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
 #pragma unroll
       for (int ct = 0; ct < kGemmCT; ++ct)
         bm[ct] = bits_to_bf16x8((cur[ct][ks / 2] >> (16 * (ks % 2) + 8 * g)) & 0xffu);
-      bf16x8 ah[2];
+      bf16x8 ah[kGemmRT];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) ah[a] = tr_a(tile, 16 * ks, 32 * a);
+      for (int a = 0; a < kGemmRT; ++a) ah[a] = tr_a(tile, ks, a);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < kGemmRT; ++a)
 #pragma unroll
         for (int ct = 0; ct < kGemmCT; ++ct) acc[a][ct] = mfma32(ah[a], bm[ct], acc[a][ct]);
     }
@@ -197,16 +213,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
 
   // T for this wavefront's query blocks: lane holds query block i0 + 32 ct + lane%32 and state
   // entries n0 + 32 a + 8 q + 4 g + {0..3}.  Each 32-query-block tile goes through this
-  // wavefront's own 4 KB of LDS (32 rows of 128 bytes, 16-byte chunk c of row r at
-  // c ^ ((r >> 1) & 7)) and leaves as 16-byte stores, eight lanes per row.  The stage buffers are
+  // wavefront's own 8 KB of buffer 0 (32 rows of 256 bytes, 16-byte chunk c of row r at
+  // c ^ (r & 15)) and leaves as 16-byte stores, sixteen lanes per row.  The stage buffers are
   // free: the last step ended with a barrier after every wavefront's reads.
-  static_assert(2 * STAGE >= 4 * 32 * kGemmN, "epilogue staging fits the stage buffers");
-  __bf16* stg = (w < 2 ? sb0 : sb1) + (w % 2) * 32 * kGemmN;
-  auto eoff = [](int r, int chunk) { return r * kGemmN + ((chunk ^ ((r >> 1) & 7)) << 3); };
+  static_assert(STAGE >= 4 * 32 * kGemmN, "epilogue staging fits stage buffer 0");
+  __bf16* stg = sb0 + w * 32 * kGemmN;
+  auto eoff = [](int r, int chunk) { return r * kGemmN + ((chunk ^ (r & 15)) << 3); };
 #pragma unroll
   for (int ct = 0; ct < kGemmCT; ++ct) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < kGemmRT; ++a)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         bf16x4 v;
@@ -217,8 +233,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = 8 * u + lane / 8, ch = lane % 8;
+    for (int u = 0; u < 32 * (kGemmN / 8) / kWave; ++u) {
+      const int k = lane + kWave * u;
+      const int r = k / (kGemmN / 8), ch = k % (kGemmN / 8);
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + eoff(r, ch));
       const int i = i0 + 32 * ct + r;
       if (i < nb) *reinterpret_cast<bf16x8*>(t_out + ((size_t)bh * nb + i) * DD + n0 + 8 * ch) = v;

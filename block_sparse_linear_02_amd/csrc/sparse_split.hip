@@ -387,6 +387,14 @@ __device__ __forceinline__ void split_wave(
   f32x16 num[HC];
   float inv_den = 0.f;
   {
+    // this row of Q for the numerator, in flight with the T_i loads (unconditional, from a
+    // clamped row: a load under a branch makes the compiler wait for it on the spot)
+    bf16x8 qv[NS];
+    {
+      const T* qr = Q + hoff + (size_t)min(row, N - 1) * D + 8 * g;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) qv[k] = load_row8<T>(qr + 16 * k);
+    }
     if (z_lane) zeta[tid] = Z[(size_t)bh * D + tid] - zacc;
     wait_vmem();
     __syncthreads();
@@ -398,7 +406,7 @@ __device__ __forceinline__ void split_wave(
     float den = 0.f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const bf16x8 pq = relu8(row_ok ? load_row8<T>(Q + hoff + (size_t)row * D + 16 * k + 8 * g) : bf16x8{});
+      const bf16x8 pq = relu8(row_ok ? qv[k] : bf16x8{});
 #pragma unroll
       for (int cc = 0; cc < HC; ++cc) {
         num[cc] = mfma32(rd_row(lb1, c0 + 32 * cc, k), pq, num[cc]);
