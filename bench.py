@@ -2,9 +2,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video_s]
 
-One step = sla.route + sla.forward (router, linear-branch states, block-sparse flash kernel with
-the fused linear removal and alpha combine) over one batch of synthetic inputs already resident
-in HBM.  Prints ONE JSON line: value = effective TFLOP/s (sparse FLOPs 4 d sum_i r_i sum_{j in
+One step = sla.route + sla.forward over one batch of synthetic inputs already resident in HBM.
+The default linear mode is the mask-product one (router; per-block linear states; every query
+block's unselected-state sum T_i from one MFMA GEMM of the router's complement mask with the
+stacked states; block-sparse flash kernel over two query blocks per workgroup with the relu(Q)
+T_i application and alpha combine in its epilogue); --linear-mode fused rebuilds the kept blocks'
+states on chip instead, literal sums stored states per query block.  Prints ONE JSON line: value = effective TFLOP/s (sparse FLOPs 4 d sum_i r_i sum_{j in
 sel(i)} c_j of the step's actual index lists, divided by the step time), ms_per_step, the
 dominant kernel's roofline (its algorithmic FLOPs per launch over its event-timed duration) and
 the CPU oracle timed on a bounded sample of the same workload.
@@ -33,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video_s", help="video_s | video_l | video_l_fp8")
-    ap.add_argument("--linear-mode", default="fused", choices=["fused", "literal", "mask_product"])
+    ap.add_argument("--linear-mode", default="mask_product", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -64,8 +67,8 @@ SPARSE_SOURCES = [
     "block_sparse_linear_02_amd/csrc/sla_tiles.hpp",
     "block_sparse_linear_02_amd/csrc/sla_device.hpp",
 ]
-SPLIT_SOURCES = [
-    "block_sparse_linear_02_amd/csrc/sparse_split.hip",
+PAIR_SOURCES = [
+    "block_sparse_linear_02_amd/csrc/sparse_pair.hip",
     "block_sparse_linear_02_amd/csrc/sla_tiles.hpp",
     "block_sparse_linear_02_amd/csrc/sla_device.hpp",
 ]
@@ -160,6 +163,8 @@ def main():
         return
 
     wl = gen.workload(a.workload)
+    if wl.fp8:
+        a.linear_mode = "fused"  # the fp8 path pairs the quantised sparse branch with the fused linear one
     inputs = gen.draw(wl, 0)
     Q, K, V, alpha = (inputs[k].to(dev) for k in ("Q", "K", "V", "alpha"))
     Wq, Wk = inputs["Wq"].to(dev), inputs["Wk"].to(dev)
@@ -206,27 +211,35 @@ def main():
     flops = sparse_flops(idx, N, d)
     sparse_ms, route_ms, states_ms = avg_ms(ev), avg_ms(ev_r), avg_ms(ev_s)
     # The sparse kernel's algorithmic work per launch: 2.10 MFLOP per kept (query block, key
-    # block) pair (QK^T and PV), i.e. the sparse FLOPs.  With the fused linear mode it also
-    # rebuilds relu(K_j)^T V_j of every kept pair on chip (the same count again) and applies
-    # relu(Q) to the d x d linear state (hi and lo halves): reported as executed MFMA work, not
-    # counted in `achieved`.
+    # block) pair (QK^T and PV), i.e. the sparse FLOPs.  It also applies relu(Q) to the d x d
+    # linear state (one bf16 T_i in the mask-product mode, hi and lo halves in the fused one),
+    # and the fused mode rebuilds relu(K_j)^T V_j of every kept pair on chip (the sparse count
+    # again): reported as executed MFMA work, not counted in `achieved`.
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     achieved = flops / (sparse_ms * 1e-3) / 1e12
-    apply_flops = 4.0 * B * H * N * d * d  # relu(q) T on hi + lo halves, per query row
-    executed = flops + {"fused": flops + apply_flops, "literal": 0.0, "mask_product": apply_flops}[a.linear_mode]
+    apply_flops = 2.0 * B * H * N * d * d  # relu(q) T per query row, one bf16 operand
+    executed = flops + {"fused": flops + 2 * apply_flops, "literal": 0.0, "mask_product": apply_flops}[a.linear_mode]
     if fp8:
         sources, kname = ["block_sparse_linear_02_amd/csrc/fp8.hip"], "sparse_fp8_kernel"
     elif a.linear_mode == "mask_product":
-        sources, kname = SPLIT_SOURCES, "split_kernel"
+        sources, kname = PAIR_SOURCES, "pair_kernel"
     else:
         sources, kname = SPARSE_SOURCES, "sparse_kernel"
     digest = source_digest(sources)
     kernel_key = kname + f"@{a.workload}"
     # HBM streams: the router reads Q and K once and writes the index lists; the state kernels
-    # read K and V once and write per-block z_j plus the per-(b, h) totals
+    # read K and V once and write per-block z_j plus the per-(b, h) totals; in the mask-product
+    # mode they also write every h_j^T (bf16), which the mask GEMM reads back (once per 256 query
+    # blocks) before writing every T_i (bf16)
     es = Q.element_size()
     route_bytes = 2 * B * H * N * d * es + B * H * nb * wl.topk * 4
     states_bytes = 2 * B * H * N * d * es + B * H * nb * d * 4 + B * H * (d * d * 4 + d * 4)
+    gemm_flops = 0.0
+    if a.linear_mode == "mask_product" and not fp8:
+        hj_bytes = B * H * nb * d * d * 2
+        states_bytes = (2 * B * H * N * d * es + B * H * nb * d * 4 + hj_bytes
+                        + hj_bytes * -(-nb // 256) + hj_bytes)
+        gemm_flops = 2.0 * B * H * nb * nb * d * d
 
     def hbm(nbytes, t_ms):
         gbs = nbytes / (t_ms * 1e-3) / 1e9
@@ -268,6 +281,10 @@ def main():
         },
         "hbm_kernels": {"route": hbm(route_bytes, route_ms), "states": hbm(states_bytes, states_ms)},
     }
+    if gemm_flops:
+        rec["mask_gemm"] = {"flops_per_launch": gemm_flops,
+                            "note": "inside the states time: the complement-mask x stacked-states "
+                                    "GEMM (2 n_b^2 d^2 per head)"}
     if not a.no_cpu_baseline:
         cb = cpu_baseline(inputs, wl, idx)
         rec["cpu_baseline"] = {

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libsla.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["router.hip", "linear_state.hip", "linear_gemm.hip", "sparse.hip", "sparse_split.hip",
+SOURCES = ["router.hip", "linear_state.hip", "linear_gemm.hip", "sparse.hip", "sparse_pair.hip",
            "linear_apply.hip", "fp8.hip", "api.cpp"]
 
 FLAGS = [

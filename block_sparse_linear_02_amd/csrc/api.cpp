@@ -165,7 +165,7 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
   else if (mode == SLA_LINEAR_MASK_PRODUCT)
-    e = sla::launch_sparse_tsel(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream);
+    e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream);
   else
     e = sla::launch_sparse(d, Q, K, V, idx, alpha, w.ht_hi, w.ht_lo, w.Z, w.zb, O,
                            mode == SLA_LINEAR_FUSED ? 1 : 0, stream);

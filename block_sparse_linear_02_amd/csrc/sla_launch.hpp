@@ -37,8 +37,10 @@ hipError_t launch_mask_bits(const Dims& p, const int32_t* idx, uint32_t* bits,
                             hipStream_t stream);
 hipError_t launch_tsel(const Dims& p, const __bf16* hj_bf, const uint32_t* bits, __bf16* t_bf,
                        hipStream_t stream);
-// Sparse branch with the linear part from the precomputed T_i (bf16) and zeta from z_j.
-hipError_t launch_sparse_tsel(const Dims& p, const void* Q, const void* K, const void* V,
+
+// Sparse branch with the linear part from the precomputed T_i (bf16) and zeta from z_j, two
+// query blocks per workgroup over the union of their kept blocks (n_b <= 2048).
+hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream);
 // Reduce the chunk partials (fixed order): H^T as bf16 hi/lo [d][d], Z [d]; optionally H [d][d]

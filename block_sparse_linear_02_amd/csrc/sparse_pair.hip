@@ -1,0 +1,453 @@
+// sparse_pair.hip - block-sparse softmax branch and alpha combine on gfx950 for two query blocks
+// per workgroup, with the linear branch's per-query-block state T_i = sum_{j not in sel(i)} h_j
+// taken from memory (formed for every query block at once by the mask-product kernel,
+// linear_gemm.hip).
+//
+// Sources: SLA2 Italian summary sections 1 and 2.A and Arabic summary sections 1 and 2.alef
+// (sparse branch renormalised over the kept blocks; O = alpha O_s + (1 - alpha) O_l); SALAD
+// section 2 (ReLU feature map of the linear branch, over the blocks the sparse branch leaves).
+//
+// One workgroup = query blocks 2p and 2p + 1 of one (batch, head).  Neighbouring query blocks
+// keep mostly the same key blocks, so the workgroup walks the ascending union of their two
+// index lists and stages each K_j, V_j tile into LDS once for both: every tile byte read from L2
+// serves up to 128 query rows instead of 64.  Wavefront w takes rows 32 (w % 2) .. + 31 of query
+// block 2p + w / 2 against all 64 keys of a tile, and skips the tiles its block did not keep
+// (the result is exactly each block's own sparse branch).  Per tile: S^T = K_j Q^T
+// (v_mfma_f32_32x32x16_bf16, Q in registers as the B operand, so each lane owns one query row
+// and the row statistics stay in-lane), online softmax in the log2 domain (the running maximum
+// only moves when a row's maximum grows by more than 2^8), P rounded to bf16, row sums from the
+// bf16 P with v_dot2, O_s^T += V_j^T P^T with V read transposed from LDS (ds_read_b64_tr_b16).
+// K_j, V_j tiles are double-buffered in LDS, one array per buffer so that the compiler can tell
+// the buffer being filled by direct-to-LDS loads from the one being read.
+// Epilogue: T_i^T (bf16, [c][c']) of each block is loaded into a tile buffer, zeta_i = Z -
+// sum_kept z_j; each wavefront computes num = relu(Q) T_i by MFMA, den = relu(q) . zeta_i, and
+// O = alpha O_s / l + (1 - alpha) num / den (the linear part is 0 when nothing is unselected or
+// den == 0), fp32 stores; rows past N are not stored.
+#include <type_traits>
+
+#include "sla_device.hpp"
+#include "sla_launch.hpp"
+#include "sla_tiles.hpp"
+
+namespace sla {
+
+namespace {
+
+constexpr int kPairThreads = 256;
+constexpr int kPairMaxWords = 64;  // bitmap words of the union: n_b <= 2048
+
+template <class T>
+__device__ __forceinline__ bf16x8 pair_row8(const T* p);
+template <>
+__device__ __forceinline__ bf16x8 pair_row8<__bf16>(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+template <>
+__device__ __forceinline__ bf16x8 pair_row8<float>(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  return bf16x8{f2bf(a[0]), f2bf(a[1]), f2bf(a[2]), f2bf(a[3]),
+                f2bf(b[0]), f2bf(b[1]), f2bf(b[2]), f2bf(b[3])};
+}
+
+// fp32 inputs: the bf16 remainder x - bf16(x) of 8 consecutive values (0 for bf16 inputs)
+template <class T>
+__device__ __forceinline__ bf16x8 pair_row8_lo(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return bf16x8{};
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = f2bf(a[e] - bf2f(f2bf(a[e])));
+      r[e + 4] = f2bf(b[e] - bf2f(f2bf(b[e])));
+    }
+    return r;
+  }
+}
+
+// sum of the 8 bf16 values of v (fp32 accumulation)
+__device__ __forceinline__ float pair_sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {f2bf(1.f), f2bf(1.f)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2 * i], v[2 * i + 1]}, one, acc, false);
+  return acc;
+}
+
+constexpr float kPairRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before the maximum moves
+
+template <class T, int D>
+__global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ idx, const float* __restrict__ alpha,
+    const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
+    float* __restrict__ O, int N, int nb, int topk, float c_log2) {
+  constexpr int NS = D / 16;  // MFMA k-steps over the head dim
+  constexpr int NC = D / 32;  // 32-channel output tiles
+  constexpr int TILE = TileLayout<D>::ELEMS;
+  // fp32 inputs keep K as bf16 hi + lo tiles so that S = K Q^T is about fp32-accurate
+  // (Kh Qh + Kh Ql + Kl Qh); bf16 inputs are exact in one bf16 tile
+  constexpr bool SPLIT = sizeof(T) == 4;
+  constexpr int TILES = SPLIT ? 3 : 2;  // per buffer: K (hi), V, [K lo]
+  static_assert(D * TileLayout<D>::PITCH <= TILES * TILE, "T^T must fit in one tile buffer");
+  __shared__ __attribute__((aligned(16))) __bf16 lb0[TILES * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 lb1[TILES * TILE];
+  __shared__ uint32_t bm[2][kPairMaxWords];  // kept-block bitmaps of the two query blocks
+  __shared__ int32_t ul[kPairMaxWords * 32];  // the union, ascending: (j << 2) | kept-by mask
+  __shared__ int32_t ucount;
+  __shared__ float zeta[2][D];
+  auto buf = [&](auto BUFC) -> __bf16* { return decltype(BUFC)::value ? lb1 : lb0; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave, g = lane / 32;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int npair = (nb + 1) / 2;
+  const int bh = item / npair, pr = item % npair;
+  const int qb0 = 2 * pr;
+  const bool has1 = qb0 + 1 < nb;  // an odd n_b leaves the last workgroup one block
+  const int blk = wave / 2;        // this wavefront's query block: qb0 + blk
+  const size_t hoff = (size_t)bh * N * D;
+  const int nw = (nb + 31) / 32;
+
+  // ---- the union of the two ascending index lists, with the kept-by bits ----
+  if (tid < 2 * kPairMaxWords) bm[tid / kPairMaxWords][tid % kPairMaxWords] = 0u;
+  __syncthreads();
+  for (int t = tid; t < 2 * topk; t += kPairThreads) {
+    const int b = t / topk;
+    if (b == 0 || has1) {
+      const int j = idx[((size_t)bh * nb + qb0 + b) * topk + t % topk];
+      atomicOr(&bm[b][j / 32], 1u << (j % 32));
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t w0 = lane < nw ? bm[0][lane] : 0u, w1 = lane < nw ? bm[1][lane] : 0u;
+    const uint32_t u = w0 | w1;
+    const int cnt = __popc(u);
+    int pos = cnt;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(pos, o);
+      if (lane >= o) pos += v;
+    }
+    if (lane == kWave - 1) ucount = pos;
+    pos -= cnt;
+    for (uint32_t r = u; r; r &= r - 1) {
+      const int b = __ffs(r) - 1;
+      ul[pos++] = ((32 * lane + b) << 2) | (((w0 >> b) & 1u) ? 1 : 0) | (((w1 >> b) & 1u) ? 2 : 0);
+    }
+  }
+  __syncthreads();
+  const int nu = ucount;
+
+  // Tile staging: every thread moves its share of each tile.  bf16 tiles with d = 128 and all
+  // 64 rows valid go HBM -> LDS directly (no registers), issued at the start of the iteration
+  // that uses the other buffer; other tiles (fp32 inputs, d = 64, the short last block) go
+  // through registers with zero fill, stored right away.  z_j travels with the tile: threads
+  // tid < D keep the sum over the first block's kept tiles, threads D .. 2D - 1 the second's.
+  constexpr bool DIRECT = sizeof(T) == 2 && D == 128;
+  const int zb_blk = tid / D;  // 0, 1 for tid < 2D
+  const bool z_lane = tid < 2 * D;
+  float z_in = 0.f;       // z_j of the tile being staged
+  int f_next = 0;         // kept-by bits of the tile being staged
+  int nv_next = kBlock;   // valid rows of the tile being staged
+  float zacc = 0.f;
+  auto stage = [&](int t, auto BUFC) {
+    const int e = ul[t];
+    const int j = e >> 2;
+    const int nv = min(kBlock, N - j * kBlock);
+    __bf16* dst = buf(BUFC);
+    const T* ksrc = K + hoff + (size_t)j * kBlock * D;
+    const T* vsrc = V + hoff + (size_t)j * kBlock * D;
+    if (z_lane) z_in = zb[((size_t)bh * nb + j) * D + tid % D];
+    f_next = e & 3;
+    nv_next = nv;
+    if constexpr (DIRECT) {
+      // a short tile (the last block of the sequence) is clamped here and its tail rows are
+      // zeroed after the loads land (zero_tail), so no register path sits in the loop
+      if (nv == kBlock) {
+        load_tile_direct<kPairThreads>(ksrc, dst, tid);
+        load_tile_direct<kPairThreads>(vsrc, dst + TILE, tid);
+      } else {
+        load_tile_direct_clamped<kPairThreads>(ksrc, dst, tid, nv);
+        load_tile_direct_clamped<kPairThreads>(vsrc, dst + TILE, tid, nv);
+      }
+    } else {
+      TileLoader<T, D, kPairThreads> lk, lv;
+      lk.load(ksrc, nv, tid);
+      lv.load(vsrc, nv, tid);
+      if constexpr (SPLIT)
+        lk.store_split(dst, dst + 2 * TILE, tid);
+      else
+        lk.store(dst, tid);
+      lv.store(dst + TILE, tid);
+    }
+  };
+  // DIRECT tiles with fewer than 64 valid rows: zero the tail once every load has landed and
+  // been published by a barrier (workgroup-uniform condition; at most once per head)
+  auto zero_tail = [&](auto BUFC, int nv) {
+    if constexpr (DIRECT) {
+      if (nv < kBlock) {
+        zero_tile_rows<kPairThreads>(buf(BUFC), tid, nv);
+        zero_tile_rows<kPairThreads>(buf(BUFC) + TILE, tid, nv);
+        __syncthreads();
+      }
+    }
+  };
+  // LDS operand reads.  d = 128: per-lane address parts computed once and laundered through an
+  // empty asm at the start of every tile (so the compiler re-derives the per-block addresses
+  // with one v_xor each instead of holding dozens of them in registers across the loop); row
+  // and buffer offsets are immediates.  d = 64: the padded layout's plain offsets.
+  constexpr bool XADDR = D == 128;
+  int ap_row = 0, ap_va = 0, ap_vb = 0;
+  if constexpr (XADDR) {
+    ap_row = row_part(lane);
+    ap_va = tr_part<4>(lane, 0);
+    ap_vb = tr_part<4>(lane, 8);
+  }
+  auto launder = [&]() {
+    if constexpr (XADDR) asm volatile("" : "+v"(ap_row), "+v"(ap_va), "+v"(ap_vb));
+  };
+  // row-wise operand: row R0 + lane%32 (R0 % 32 == 0), channels 16k + 8g .. + 7
+  auto rd_row = [&](const __bf16* tile, int R0, int k) -> bf16x8 {
+    if constexpr (XADDR)
+      return lds_row16(tile, R0 * 256 + (ap_row ^ (32 * k)));
+    else
+      return *reinterpret_cast<const bf16x8*>(tile + TileLayout<D>::off(R0 + lane % 32, 16 * k + 8 * g));
+  };
+  // transposed operand in PV key order (step 4, gap 8)
+  auto rd_tr_v = [&](const __bf16* tile, int row0, int col0) -> bf16x8 {
+    if constexpr (XADDR)
+      return join_tr(lds_tr_at(tile, row0 * 256 + (ap_va ^ (2 * col0))),
+                     lds_tr_at(tile, row0 * 256 + (ap_vb ^ (2 * col0))));
+    else
+      return tr_operand<D, 4, 8>(tile, row0, col0, lane);
+  };
+
+  // Q of this wavefront's 32 rows as the B operand of S^T = K Q^T: k-slot 8g + jj of step s <->
+  // channel 16s + 8g + jj (rows past N, and the absent second block of an odd n_b, read a
+  // clamped row and are zeroed)
+  const int m = 32 * (wave % 2) + lane % 32;
+  const int row = (qb0 + blk) * kBlock + m;
+  const bool row_ok = row < N;
+  bf16x8 q[NS], ql[SPLIT ? NS : 1];
+  {
+    const T* qr = Q + hoff + (size_t)min(row, N - 1) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      q[s] = row_ok ? pair_row8<T>(qr + 16 * s) : bf16x8{};
+      if constexpr (SPLIT) ql[s] = row_ok ? pair_row8_lo<T>(qr + 16 * s) : bf16x8{};
+    }
+  }
+  f32x16 os[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) os[c] = f32x16{};
+  float mrun = -INFINITY, lsum = 0.f;
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int nv_cur = kBlock, f_cur = 0;
+  if (nu > 0) {
+    stage(0, B0{});
+    if (z_lane && ((f_next >> zb_blk) & 1)) zacc += z_in;
+    nv_cur = nv_next;
+    f_cur = f_next;
+    wait_vmem();
+    __syncthreads();
+    zero_tail(B0{}, nv_cur);
+  }
+  // one tile of the union; BUF (= t & 1, a compile-time constant through the unrolled pair
+  // below) is the buffer holding tile t, and tile t + 1 is staged into the other one (last read
+  // in iteration t - 1).  MASK: the tile may be short (only the last block of the sequence is,
+  // and it comes last in the ascending union), so only the final step carries the key mask
+  // (the compiler turns it into selects on every key otherwise)
+  auto step = [&](int t, auto BUFC, auto MASKC) {
+    constexpr int BUF = decltype(BUFC)::value;
+    constexpr bool MASK = decltype(MASKC)::value;
+    const int nv = nv_cur;
+    launder();
+    if (t + 1 < nu) stage(t + 1, std::integral_constant<int, 1 - BUF>{});
+    if ((f_cur >> blk) & 1) {  // this wavefront's block kept the tile (wavefront-uniform)
+      const __bf16* Ks = buf(BUFC);
+      const __bf16* Vs = Ks + TILE;
+      // K operands of both 32-key halves, issued together ahead of their MFMAs
+      bf16x8 ka[2][NS];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int k = 0; k < NS; ++k) ka[kt][k] = rd_row(Ks, 32 * kt, k);
+      f32x16 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[kt] = f32x16{};
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          if constexpr (SPLIT) {
+            s[kt] = mfma32(rd_row(Ks + 2 * TILE, 32 * kt, k), q[k], s[kt]);
+            s[kt] = mfma32(ka[kt][k], ql[k], s[kt]);
+          }
+          s[kt] = mfma32(ka[kt][k], q[k], s[kt]);
+        }
+      // V operands for PV: independent of P, so their LDS latency hides under the softmax (in
+      // the masked final step they are read after it, which keeps that step within registers)
+      bf16x8 va[NC][4];
+      auto read_v = [&]() {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) va[c][u] = rd_tr_v(Vs, 16 * u, 32 * c);
+      };
+      if constexpr (!MASK) read_v();
+      // key of accumulator register i in half kt: 32kt + 8(i/4) + 4g + i%4
+      if (MASK && nv < kBlock) {
+        const int lim = nv - 4 * g;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + 8 * (i / 4) + i % 4 >= lim) s[kt][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+      mx = xor32_max(mx) * c_log2;
+      if (__ballot(mx > mrun + kPairRescaleSlack)) {
+        const float mnew = fmaxf(mrun, mx);
+        const float corr = fast_exp2(mrun - mnew);
+        mrun = mnew;
+        lsum *= corr;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) os[c] *= corr;
+      }
+      bf16x8 pb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pb[u][jj] = f2bf(fast_exp2(fmaf(s[u / 2][8 * (u % 2) + jj], c_log2, -mrun)));
+        lsum = pair_sum8(pb[u], lsum);
+      }
+      if constexpr (MASK) read_v();
+      // O^T += V^T P^T ; MFMA u covers keys 16u .. 16u + 15
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) os[c] = mfma32(va[c][u], pb[u], os[c]);
+    }
+    nv_cur = nv_next;
+    wait_vmem();
+    __syncthreads();
+    // z_j and the kept-by bits of tile t + 1 are used only now, after the explicit wait above:
+    // used earlier, the compiler would wait for every in-flight tile load at that point
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < nu) {
+      if (z_lane && ((f_next >> zb_blk) & 1)) zacc += z_in;
+      f_cur = f_next;
+      zero_tail(std::integral_constant<int, 1 - BUF>{}, nv_cur);
+    }
+  };
+  {
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+    int t = 0;
+    for (; t + 2 < nu; t += 2) {
+      step(t, B0{}, NoMask{});
+      step(t + 1, B1{}, NoMask{});
+    }
+    if (t + 1 < nu) {
+      step(t, B0{}, NoMask{});
+      step(t + 1, B1{}, Mask{});
+    } else if (t < nu) {
+      step(t, B0{}, Mask{});
+    }
+  }
+
+  // ---- epilogue: T_i^T [c][c'] of block b into tile buffer b (both free since the last
+  // step's barrier), in the tile row layout; zeta of each block ----
+  {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const __bf16* th = t_g + ((size_t)bh * nb + min(qb0 + b, nb - 1)) * D * D;
+      __bf16* dst = b ? lb1 : lb0;
+#pragma unroll
+      for (int half = 0; half < D / kBlock; ++half) {
+        if constexpr (D == 128) {
+          load_tile_direct<kPairThreads>(th + half * kBlock * D, dst + half * kBlock * D, tid);
+        } else {
+          TileLoader<__bf16, D, kPairThreads> ld;
+          ld.load(th + half * kBlock * D, kBlock, tid);
+          ld.store(dst + half * TILE, tid);
+        }
+      }
+    }
+    if (z_lane) zeta[zb_blk][tid % D] = Z[(size_t)bh * D + tid % D] - zacc;
+  }
+  wait_vmem();
+  __syncthreads();
+  launder();
+  const float ltot = xor32_sum(lsum);
+  const float inv_l = ltot > 0.f ? 1.f / ltot : 0.f;
+  // num^T[c][m] = sum_c' T_i^T[c][c'] relu(Q)[m][c']: the A operand (rows c, k = c') is a
+  // row-wise read of T_i^T
+  const __bf16* tt = blk ? lb1 : lb0;
+  f32x16 num[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) num[c] = f32x16{};
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const bf16x8 pq = relu8(q[k]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) num[c] = mfma32(rd_row(tt, 32 * c, k), pq, num[c]);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[blk][16 * k + 8 * g + jj];
+  }
+  den = xor32_sum(den);
+  const float inv_den = (topk < nb && den != 0.f) ? 1.f / den : 0.f;
+  if (!row_ok) return;
+  const float a = alpha[(size_t)bh * N + row];
+  const float ws = a * inv_l, wl = (1.f - a) * inv_den;
+  float* orow = O + hoff + (size_t)row * D;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(num[c][4 * qd + e], wl, os[c][4 * qd + e] * ws);
+      *reinterpret_cast<f32x4*>(orow + 32 * c + 8 * qd + 4 * g) = v;
+    }
+}
+
+template <class T, int D>
+hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void* V,
+                         const int32_t* idx, const float* alpha, const __bf16* t_bf,
+                         const float* Z, const float* zb, float* O, hipStream_t stream) {
+  const int total = p.B * p.H * ((p.nb + 1) / 2);
+  const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
+  pair_kernel<T, D><<<total, kPairThreads, 0, stream>>>(
+      (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
+      c_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
+                              const int32_t* idx, const float* alpha, const __bf16* t_bf,
+                              const float* Z, const float* zb, float* O, hipStream_t stream) {
+  if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
+  if (p.dtype == kBF16 && p.d == 128)
+    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
+  if (p.dtype == kBF16 && p.d == 64)
+    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
+  if (p.dtype == kF32 && p.d == 128)
+    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
+  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
+}
+
+}  // namespace sla
