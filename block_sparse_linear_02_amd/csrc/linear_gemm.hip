@@ -17,13 +17,14 @@
 //   tsel_kernel       T^T = h^T U^T on v_mfma_f32_32x32x16_bf16: rows = 128 columns of h (two
 //                     slices of the d*d state entries), columns = 256 query blocks, k = key
 //                     blocks in stages of kGemmK; each wavefront takes all 128 rows and 64
-//                     columns, so every decoded mask operand feeds four MFMAs.  h is stored in bf16, the sum is accumulated in fp32 and
-//                     T is rounded to bf16 once (a relative error of about 2^-9 on the linear
-//                     branch's state); the h stage goes HBM -> LDS by direct loads into rows of
-//                     256 bytes whose 16-byte chunks are XOR-swizzled (chunk c of row j at
-//                     c ^ 4 (j & 3)) so that the transposed operand reads (ds_read_b64_tr_b16)
-//                     of four consecutive rows hit distinct banks; the mask operand is 8 bits per
-//                     lane turned into eight bf16 0/1 values by integer arithmetic.  Epilogue:
+//                     columns, so every decoded mask operand feeds four MFMAs.  h is stored in
+//                     bf16, the sum is accumulated in fp32 and T is rounded to bf16 once (a
+//                     relative error of about 2^-9 on the linear branch's state); the h stage
+//                     goes HBM -> LDS by direct loads into rows of 256 bytes whose 16-byte chunks
+//                     are XOR-swizzled (chunk c of row j at c ^ 4 (j & 3)) so that the transposed
+//                     operand reads (ds_read_b64_tr_b16) of four consecutive rows hit distinct
+//                     banks; the mask operand is 8 bits per lane turned into eight bf16 0/1
+//                     values by two lookups in a 16-entry LDS table.  Epilogue:
 //                     T_i in bf16, in the transposed state layout [c][c'] (V channel major) per
 //                     query block, staged through LDS so that every lane stores 16 contiguous
 //                     bytes.
@@ -77,18 +78,6 @@ __device__ __forceinline__ int hs_off(int j, int c) {
   return j * (2 * kGemmN) + (((c >> 3) ^ (4 * (j & 3))) << 4) + (c & 7) * 2;
 }
 
-// eight mask bits (bit e = key block 8 g + e of the k step) as eight bf16 0/1 values: each
-// 32-bit pair is (b0 + b1 * 2^16) * 0x3f80, 0x3f80 being bf16 1.0
-__device__ __forceinline__ bf16x8 bits_to_bf16x8(u32 byte) {
-  i32x4 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const u32 x = byte >> (2 * k);
-    r[k] = (int)(((x & 1u) | ((x & 2u) << 15)) * 0x3f80u);
-  }
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 template <int D>
 __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
     const __bf16* __restrict__ hj, const uint32_t* __restrict__ bits, int nb, int nw,
@@ -97,11 +86,21 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
   constexpr int STAGE = kGemmK * kGemmN;  // bf16 elements of one h stage
   __shared__ __attribute__((aligned(16))) __bf16 sb0[STAGE];
   __shared__ __attribute__((aligned(16))) __bf16 sb1[STAGE];
+  // four mask bits -> four bf16 0/1 values: 16 entries of 8 bytes, so the 64 lanes of a lookup
+  // touch at most 16 distinct addresses in distinct bank pairs (no conflict; equal addresses
+  // are broadcast)
+  __shared__ __attribute__((aligned(16))) bf16x4 nib[16];
   auto buf = [&](auto B) -> __bf16* { return decltype(B)::value ? sb1 : sb0; };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave, g = lane / 32;
+  if (tid < 16) {
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = ((tid >> e) & 1) ? f2bf(1.f) : f2bf(0.f);
+    nib[tid] = v;
+  }
   // workgroup -> (query-block tile, state rows, head) with the query-block tiles fastest, so
   // that the workgroups reading the same rows of h run next to each other on one XCD
   const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -194,7 +193,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
       bf16x8 bm[kGemmCT];
 #pragma unroll
       for (int ct = 0; ct < kGemmCT; ++ct)
-        bm[ct] = bits_to_bf16x8((cur[ct][ks / 2] >> (16 * (ks % 2) + 8 * g)) & 0xffu);
+      {
+        const u32 byte = (cur[ct][ks / 2] >> (16 * (ks % 2) + 8 * g)) & 0xffu;
+        const bf16x4 lo = nib[byte & 15u], hi = nib[byte >> 4];
+        bm[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
       bf16x8 ah[kGemmRT];
 #pragma unroll
       for (int a = 0; a < kGemmRT; ++a) ah[a] = tr_a(tile, ks, a);
