@@ -126,13 +126,50 @@ def cpu_baseline(inputs, wl, idx_gpu, budget_s=15.0):
             break
     per_call = heads * sum(per_head) / len(per_head)
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{blas.get('name')} {blas.get('version')}"
+    except Exception:  # numpy without the dict form
+        blas = "unknown"
     return {
         "seconds_per_call": per_call,
+        "blas": blas,
         "sample": f"{len(per_head)} of {heads} heads (router, block states and {blocks_done} query "
                   f"blocks of {len(per_head) * nb}; {used:.1f} s of CPU time), scaled to all heads "
                   f"and query blocks",
         "cores": int(threads),
     }
+
+
+def mass_covered(inputs, wl, idx_np, blocks):
+    """Diagnostic (not pass/fail): the share of each query row's full softmax attention mass
+    that falls on the tokens of its query block's kept blocks, for a few query blocks of head
+    (0, 0), float64 on the host; mean and minimum over their rows.  `best_k_mean` is the same
+    share for the k blocks holding the most mass (the most any k-block selection could cover):
+    it shows how concentrated the data are, independently of the router's projections."""
+    import numpy as np
+
+    Q = inputs["Q"][0, 0].double().numpy()
+    K = inputs["K"][0, 0].double().numpy()
+    N, d = Q.shape
+    k = idx_np.shape[-1]
+    nbk = -(-N // 64)
+    shares, best = [], []
+    for i in blocks:
+        q = Q[64 * i : min(64 * i + 64, N)]
+        s = q @ K.T / np.sqrt(d)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        keep = np.zeros(N, dtype=bool)
+        for j in idx_np[i]:
+            keep[64 * j : min(64 * j + 64, N)] = True
+        shares.append(p[:, keep].sum(axis=1))
+        pb = np.add.reduceat(p, np.arange(0, N, 64), axis=1)[:, :nbk]  # [rows, n_b]
+        top = np.argsort(-pb.mean(axis=0))[:k]
+        best.append(pb[:, top].sum(axis=1))
+    sh, bt = np.concatenate(shares), np.concatenate(best)
+    return {"query_blocks": [int(b) for b in blocks], "head": [0, 0], "mean": float(sh.mean()),
+            "min": float(sh.min()), "best_k_mean": float(bt.mean())}
 
 
 def main():
@@ -179,14 +216,15 @@ def main():
     def events(n):
         return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
-    ev, ev_r, ev_s = events(a.steps), events(a.steps), events(a.steps)
-    for e in ev + ev_r + ev_s:
+    ev, ev_r, ev_s, ev_t = events(a.steps), events(a.steps), events(a.steps), events(a.steps)
+    for e in ev + ev_r + ev_s + ev_t:
         e[0].record()
         e[1].record()
     torch.cuda.synchronize()
 
     def step(i=None):
         if i is not None:
+            ev_t[i][0].record()
             ev_r[i][0].record()
         sla.route(Q, K, Wq, Wk, wl.topk, workspace=ws_r, idx_out=idx)
         if i is not None:
@@ -194,6 +232,8 @@ def main():
         sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O,
                     events=ev[i] if i is not None else None,
                     state_events=ev_s[i] if i is not None else None)
+        if i is not None:
+            ev_t[i][1].record()
 
     for _ in range(a.warmup):
         step()
@@ -207,6 +247,27 @@ def main():
 
     def avg_ms(pairs):
         return sum(b.elapsed_time(e) for b, e in pairs) / len(pairs)
+
+    def quantiles(pairs):
+        t = sorted(b.elapsed_time(e) for b, e in pairs)
+        q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]  # noqa: E731
+        return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "calls": len(t)}
+
+    step_q = quantiles(ev_t)
+    # cold cache: the same call after writing a 512 MB scratch buffer (larger than the 256 MB
+    # MALL), so that Q, K, V and the states come from HBM
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n_cold = min(10, a.steps)
+    ev_c = events(n_cold)
+    for i in range(n_cold):
+        scratch.fill_(i & 0xff)
+        ev_c[i][0].record()
+        sla.route(Q, K, Wq, Wk, wl.topk, workspace=ws_r, idx_out=idx)
+        sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O)
+        ev_c[i][1].record()
+    torch.cuda.synchronize()
+    cold_q = quantiles(ev_c)
+    del scratch
 
     flops = sparse_flops(idx, N, d)
     sparse_ms, route_ms, states_ms = avg_ms(ev), avg_ms(ev_r), avg_ms(ev_s)
@@ -265,6 +326,8 @@ def main():
             "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": wl.topk,
         },
         "sparse_tflop_per_call": flops / 1e12,
+        "step_ms_events": step_q,
+        "cold_cache_step_ms": cold_q,
         "kernels_ms": {"route": route_ms, "states": states_ms, "sparse": sparse_ms,
                        "other": ms - route_ms - states_ms - sparse_ms},
         "roofline": {
@@ -285,6 +348,9 @@ def main():
         rec["mask_gemm"] = {"flops_per_launch": gemm_flops,
                             "note": "inside the states time: the complement-mask x stacked-states "
                                     "GEMM (2 n_b^2 d^2 per head)"}
+    nbk = wl.n_blocks
+    rec["diagnostic_mass_covered"] = mass_covered(
+        inputs, wl, idx[0, 0].cpu().numpy(), sorted({0, nbk // 3, (2 * nbk) // 3, nbk - 1}))
     if not a.no_cpu_baseline:
         cb = cpu_baseline(inputs, wl, idx)
         rec["cpu_baseline"] = {
@@ -292,6 +358,7 @@ def main():
             "unit": "TFLOP/s (effective, same FLOP count)",
             "ms_per_call": 1e3 * cb["seconds_per_call"],
             "cores": cb["cores"],
+            "blas": cb["blas"],
             "kind": "oracle",
             "sample": cb["sample"],
         }
