@@ -200,8 +200,8 @@ def main():
         return
 
     wl = gen.workload(a.workload)
-    if wl.fp8:
-        a.linear_mode = "fused"  # the fp8 path pairs the quantised sparse branch with the fused linear one
+    if wl.fp8 and a.linear_mode == "literal":
+        a.linear_mode = "fused"  # the fp8 path has the fused and mask-product linear modes
     inputs = gen.draw(wl, 0)
     Q, K, V, alpha = (inputs[k].to(dev) for k in ("Q", "K", "V", "alpha"))
     Wq, Wk = inputs["Wq"].to(dev), inputs["Wk"].to(dev)
@@ -210,7 +210,8 @@ def main():
     fp8 = wl.fp8
     idx = torch.empty((B, H, nb, wl.topk), dtype=torch.int32, device=dev)
     ws_r = torch.empty(sla.route_workspace_bytes(Q, wl.topk), dtype=torch.uint8, device=dev)
-    variant = 1 if fp8 else {"fused": 0, "literal": 2, "mask_product": 3}[a.linear_mode]
+    variant = ({"fused": 1, "mask_product": 4}[a.linear_mode] if fp8
+               else {"fused": 0, "literal": 2, "mask_product": 3}[a.linear_mode])
     ws_f = torch.empty(sla.forward_workspace_bytes(Q, wl.topk, variant), dtype=torch.uint8, device=dev)
     O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     def events(n):
@@ -281,7 +282,8 @@ def main():
     apply_flops = 2.0 * B * H * N * d * d  # relu(q) T per query row, one bf16 operand
     executed = flops + {"fused": flops + 2 * apply_flops, "literal": 0.0, "mask_product": apply_flops}[a.linear_mode]
     if fp8:
-        sources, kname = ["block_sparse_linear_02_amd/csrc/fp8.hip"], "sparse_fp8_kernel"
+        sources = ["block_sparse_linear_02_amd/csrc/fp8.hip"]
+        kname = "pair8_kernel" if a.linear_mode == "mask_product" else "sparse_fp8_kernel"
     elif a.linear_mode == "mask_product":
         sources, kname = PAIR_SOURCES, "pair_kernel"
     else:
@@ -296,7 +298,7 @@ def main():
     route_bytes = 2 * B * H * N * d * es + B * H * nb * wl.topk * 4
     states_bytes = 2 * B * H * N * d * es + B * H * nb * d * 4 + B * H * (d * d * 4 + d * 4)
     gemm_flops = 0.0
-    if a.linear_mode == "mask_product" and not fp8:
+    if a.linear_mode == "mask_product":
         hj_bytes = B * H * nb * d * d * 2
         states_bytes = (2 * B * H * N * d * es + B * H * nb * d * 4 + hj_bytes
                         + hj_bytes * -(-nb // 256) + hj_bytes)

@@ -178,7 +178,7 @@ def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", 
     alpha = alpha.contiguous().to(torch.float32)
     p = _problem(Q, topk)
     mode = LINEAR_MODES[linear_mode]
-    variant = 1 if fp8 else {0: 0, 1: 2, 2: 3}[mode]
+    variant = (4 if mode == 2 else 1) if fp8 else {0: 0, 1: 2, 2: 3}[mode]
     need = lib().sla_forward_workspace_bytes(ctypes.byref(p), variant)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
     O = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device)

@@ -73,16 +73,17 @@ struct FwdWs {
   uint8_t *q8, *k8, *v8;
   float *sq, *sk, *sv;
 };
-// variant: 0 fused, 1 fp8 (fused), 2 literal, 3 mask product
+// variant: 0 fused, 1 fp8 (fused), 2 literal, 3 mask product, 4 fp8 (mask product)
 size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
   Carve c(ws);
   const size_t BH = (size_t)d.B * d.H;
   const size_t dd = (size_t)d.d * d.d;
   const int cb = sla::state_chunk_blocks(d);
   const size_t nchunk = (d.nb + cb - 1) / cb;
+  const bool mp = variant == 3 || variant == 4, f8 = variant == 1 || variant == 4;
   FwdWs f = {};
   f.zb = c.take<float>(BH * d.nb * d.d);
-  if (variant != 3) f.h_part = c.take<float>(BH * nchunk * dd);
+  if (!mp) f.h_part = c.take<float>(BH * nchunk * dd);
   f.z_part = c.take<float>(BH * nchunk * d.d);
   f.Z = c.take<float>(BH * d.d);
   f.ht_hi = c.take<__bf16>(BH * dd);
@@ -91,12 +92,12 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
     f.hj = c.take<float>(BH * d.nb * dd);
     f.h_full = c.take<float>(BH * dd);
   }
-  if (variant == 3) {
+  if (mp) {
     f.hj_bf = c.take<__bf16>(BH * d.nb * dd);
     f.t_bf = c.take<__bf16>(BH * d.nb * dd);
     f.bits = c.take<uint32_t>(BH * d.nb * sla::mask_words(d.nb));
   }
-  if (variant == 1) {
+  if (f8) {
     const size_t n = BH * d.N * d.d;
     f.q8 = c.take<uint8_t>(n);
     f.k8 = c.take<uint8_t>(n);
@@ -123,10 +124,11 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   const int mode = opts ? opts->linear_mode : SLA_LINEAR_FUSED;
   if (mode != SLA_LINEAR_FUSED && mode != SLA_LINEAR_LITERAL && mode != SLA_LINEAR_MASK_PRODUCT)
     return SLA_ERR_INVALID;
-  if (fp8 && mode != SLA_LINEAR_FUSED) return SLA_ERR_INVALID;
+  if (fp8 && mode == SLA_LINEAR_LITERAL) return SLA_ERR_INVALID;
   if (fp8 && (d.dtype != sla::kBF16 || d.d != 128)) return SLA_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !alpha || !O || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
-  const int variant = fp8 ? 1 : (mode == SLA_LINEAR_LITERAL ? 2 : (mode == SLA_LINEAR_MASK_PRODUCT ? 3 : 0));
+  const int variant = fp8 ? (mode == SLA_LINEAR_MASK_PRODUCT ? 4 : 1)
+                          : (mode == SLA_LINEAR_LITERAL ? 2 : (mode == SLA_LINEAR_MASK_PRODUCT ? 3 : 0));
   const size_t need = carve_forward(d, variant, nullptr, nullptr);
   if (!ws) return SLA_ERR_INVALID;
   if (ws_bytes < need) return SLA_ERR_WORKSPACE;
@@ -161,7 +163,10 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = hipEventRecord(opts->sparse_begin, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
-  if (fp8)
+  if (fp8 && mode == SLA_LINEAR_MASK_PRODUCT)
+    e = sla::launch_sparse_pair8(d, Q, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha, w.t_bf,
+                                 w.Z, w.zb, O, stream);
+  else if (fp8)
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
   else if (mode == SLA_LINEAR_MASK_PRODUCT)
@@ -193,7 +198,7 @@ size_t sla_route_workspace_bytes(const sla_problem* p) {
 
 size_t sla_forward_workspace_bytes(const sla_problem* p, int variant) {
   sla::Dims d;
-  if (check_problem(p, &d) != SLA_OK || variant < 0 || variant > 3) return 0;
+  if (check_problem(p, &d) != SLA_OK || variant < 0 || variant > 4) return 0;
   return carve_forward(d, variant, nullptr, nullptr);
 }
 

@@ -479,6 +479,313 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
   }
 }
 
+// The quantised sparse branch for two query blocks per workgroup, with the linear branch's
+// T_i = sum of the unselected blocks' states taken from memory (mask-product mode): the
+// workgroup walks the ascending union of the two index lists, stages every K8 (and, in pass 2,
+// V8^T) tile into LDS once for both blocks, and wavefront w takes rows 32 (w % 2) .. + 31 of
+// query block 2p + w / 2, skipping the tiles its block did not keep.  Pass 1: S = Q8 K8^T for
+// each row's exact maximum.  Pass 2: S again, P = exp(S - max); the 64 x 64 tile maximum of the
+// two wavefronts of a block meets in LDS at a barrier; P is quantised with scale max / 448 and
+// (P8 V8) sP sV accumulated by fp8 MFMA; the denominator sums the unquantised P.
+template <int D>
+__global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
+    const __bf16* __restrict__ Q, const uint8_t* __restrict__ q8,
+    const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
+    const int32_t* __restrict__ idx, const float* __restrict__ alpha,
+    const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
+    float* __restrict__ O, int N, int nb, int topk, float c_log2) {
+  static_assert(D == 128, "the fp8 kernel is compiled for d = 128");
+  constexpr int NS = D / 16, NC = D / 32, N8 = D / 64;
+  constexpr int K8B = kBlock * D;  // bytes of a K8 (or V8^T) tile
+  constexpr int kMaxWords = 64;    // union bitmap words: n_b <= 2048
+  // K8 and V8^T tiles double-buffered, one LDS array each so that the compiler can tell the
+  // buffers being filled by direct-to-LDS loads from the ones being read
+  __shared__ __attribute__((aligned(16))) uint8_t kb0[K8B];
+  __shared__ __attribute__((aligned(16))) uint8_t kb1[K8B];
+  __shared__ __attribute__((aligned(16))) uint8_t vb0[K8B];
+  __shared__ __attribute__((aligned(16))) uint8_t vb1[K8B];
+  __shared__ uint32_t bm[2][kMaxWords];
+  __shared__ int32_t ul[kMaxWords * 32];  // the union, ascending: (j << 2) | kept-by mask
+  __shared__ int32_t ucount;
+  __shared__ float zeta[2][D];
+  __shared__ float tmax_x[2][2];  // [block][wavefront half]: partial P tile maxima
+  auto kbuf = [&](auto BUFC) -> uint8_t* { return decltype(BUFC)::value ? kb1 : kb0; };
+  auto vbuf = [&](auto BUFC) -> uint8_t* { return decltype(BUFC)::value ? vb1 : vb0; };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, g = lane / 32, w = tid / kWave;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int npair = (nb + 1) / 2;
+  const int bh = item / npair, pr = item % npair;
+  const int qb0 = 2 * pr;
+  const bool has1 = qb0 + 1 < nb;
+  const int blk = w / 2, half = w % 2;
+  const size_t hoff = (size_t)bh * N * D;
+  const int nw = (nb + 31) / 32;
+
+  // ---- the union of the two ascending index lists, with the kept-by bits ----
+  if (tid < 2 * kMaxWords) bm[tid / kMaxWords][tid % kMaxWords] = 0u;
+  __syncthreads();
+  for (int t = tid; t < 2 * topk; t += kF8Threads) {
+    const int b = t / topk;
+    if (b == 0 || has1) {
+      const int j = idx[((size_t)bh * nb + qb0 + b) * topk + t % topk];
+      atomicOr(&bm[b][j / 32], 1u << (j % 32));
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    const uint32_t w0 = lane < nw ? bm[0][lane] : 0u, w1 = lane < nw ? bm[1][lane] : 0u;
+    const uint32_t u = w0 | w1;
+    const int cnt = __popc(u);
+    int pos = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(pos, o);
+      if (lane >= o) pos += v;
+    }
+    if (lane == kWave - 1) ucount = pos;
+    pos -= cnt;
+    for (uint32_t r = u; r; r &= r - 1) {
+      const int b = __ffs(r) - 1;
+      ul[pos++] = ((32 * lane + b) << 2) | (((w0 >> b) & 1u) ? 1 : 0) | (((w1 >> b) & 1u) ? 2 : 0);
+    }
+  }
+  __syncthreads();
+  const int nu = ucount;
+
+  // tile staging straight into the swizzled layouts; a short tile's rows past its end re-read
+  // its last row (those keys are masked; V8^T codes past N are 0)
+  auto stage_k = [&](int t, uint8_t* dst) {
+    const int j = ul[t] >> 2;
+    const int nv = min(kBlock, N - j * kBlock);
+    const uint8_t* src = k8 + hoff + (size_t)j * kBlock * D;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r0 = 8 * (2 * w + u);  // 8 K8 rows of 128 B per wave load
+      const int r = r0 + lane / 8;
+      const int unit = (lane % 8) ^ ((r >> 1) & 7);
+      load_lds16(src + (size_t)min(r, nv - 1) * D + unit * 16, dst + r0 * 128);
+    }
+  };
+  auto stage_v = [&](int t, uint8_t* dst) {
+    const int j = ul[t] >> 2;
+    const uint8_t* src = v8t + ((size_t)bh * nb + j) * D * kBlock;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c0 = 16 * (2 * w + u);  // 16 V8^T rows of 64 B per wave load
+      const int c = c0 + lane / 4;
+      const int vunit = (lane % 4) ^ ((c >> 2) & 3);
+      load_lds16(src + (size_t)c * kBlock + vunit * 16, dst + c0 * 64);
+    }
+  };
+
+  // this wavefront's 32 rows (absent rows read a clamped one and are zeroed)
+  const int m = 32 * half + lane % 32;
+  const int row = (qb0 + blk) * kBlock + m;
+  const bool row_ok = row < N;
+  i32x8 qf[N8];  // e4m3 Q as the B operand: k-slot 32g + b of step s <-> channel 64s + 32g + b
+  {
+    const uint8_t* qr = q8 + hoff + (size_t)min(row, N - 1) * D + 32 * g;
+#pragma unroll
+    for (int st = 0; st < N8; ++st) {
+      const i32x4* pq = reinterpret_cast<const i32x4*>(qr + 64 * st);
+      qf[st] = row_ok ? join8(pq[0], pq[1]) : i32x8{};
+    }
+  }
+  const float sqi = sq[(size_t)bh * nb + min(qb0 + blk, nb - 1)];
+  // S^T of one tile (keys 32 kt + 8(i/4) + 4g + i%4 in register i of s[kt]), unscaled
+  auto compute_s = [&](const uint8_t* ks, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < N8; ++st) {
+        const int r = 32 * kt + lane % 32;
+        const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g));
+        const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g + 16));
+        s[kt] = mfma_f8(join8(a0, a1), qf[st], s[kt]);
+      }
+    }
+  };
+  auto tile_rows = [&](int t) {
+    const int j = ul[t] >> 2;
+    return min(kBlock, N - j * kBlock);
+  };
+
+  // ---- pass 1: each row's exact maximum of S (log2 units) over its block's kept tiles ----
+  const bool z_lane = tid < 2 * D;  // thread tid < D: block 0's z sum, D .. 2D - 1: block 1's
+  const int zb_blk = tid / D;
+  float z_in = 0.f, zacc = 0.f;
+  float mrow = -INFINITY;
+  int f_cur = 0;
+  if (nu > 0) {
+    stage_k(0, kb0);
+    if (z_lane) z_in = zb[((size_t)bh * nb + (ul[0] >> 2)) * D + tid % D];
+    f_cur = ul[0] & 3;
+    wait_vmem();
+    __syncthreads();
+    if (z_lane && ((f_cur >> zb_blk) & 1)) zacc += z_in;
+  }
+  auto step1 = [&](int t, auto BUFC) {
+    constexpr int BUF = decltype(BUFC)::value;
+    int f_next = 0;
+    if (t + 1 < nu) {
+      stage_k(t + 1, kbuf(std::integral_constant<int, 1 - BUF>{}));
+      if (z_lane) z_in = zb[((size_t)bh * nb + (ul[t + 1] >> 2)) * D + tid % D];
+      f_next = ul[t + 1] & 3;
+    }
+    if ((f_cur >> blk) & 1) {
+      const int j = ul[t] >> 2;
+      const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
+      const int lim = tile_rows(t) - 4 * g;
+      f32x16 s[2];
+      compute_s(kbuf(BUFC), s);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[kt][i] * sc);
+    }
+    wait_vmem();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < nu && z_lane && ((f_next >> zb_blk) & 1)) zacc += z_in;
+    f_cur = f_next;
+  };
+  for (int t = 0; t < nu; t += 2) {
+    step1(t, B0{});
+    if (t + 1 < nu) step1(t + 1, B1{});
+  }
+  mrow = xor32_max(mrow);
+
+  // ---- pass 2: P with the exact maximum, 64 x 64 tile maximum, fp8 PV ----
+  f32x16 os[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) os[c] = f32x16{};
+  float lsum = 0.f;
+  if (nu > 0) {
+    stage_k(0, kb0);
+    stage_v(0, vb0);
+    f_cur = ul[0] & 3;
+    wait_vmem();
+    __syncthreads();
+  }
+  auto step2 = [&](int t, auto BUFC) {
+    constexpr int BUF = decltype(BUFC)::value;
+    using NEXT = std::integral_constant<int, 1 - BUF>;
+    int f_next = 0;
+    if (t + 1 < nu) {
+      stage_k(t + 1, kbuf(NEXT{}));
+      stage_v(t + 1, vbuf(NEXT{}));
+      f_next = ul[t + 1] & 3;
+    }
+    const bool kept = (f_cur >> blk) & 1;  // wavefront-uniform
+    const int j = ul[t] >> 2;
+    float p[2][16];
+    float pmax = 0.f;
+    if (kept) {
+      const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
+      const int lim = row_ok ? tile_rows(t) - 4 * g : 0;
+      f32x16 s[2];
+      compute_s(kbuf(BUFC), s);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[kt][i], sc, -mrow)) : 0.f;
+          lsum += p[kt][i];
+          pmax = fmaxf(pmax, p[kt][i]);
+        }
+      pmax = wave_max(pmax);
+    }
+    if (lane == 0) tmax_x[blk][half] = pmax;
+    __syncthreads();
+    if (kept) {
+      const float tmax = fmaxf(tmax_x[blk][0], tmax_x[blk][1]);
+      const float qs = tmax > 0.f ? kE4M3Max / tmax : 0.f;  // an all-underflow tile adds 0
+      const uint8_t* vs = vbuf(BUFC);
+      i32x8 va[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int cr = 32 * c + lane % 32;
+        va[c] = join8(*reinterpret_cast<const i32x4*>(vs + v8_off(cr, 32 * g)),
+                      *reinterpret_cast<const i32x4*>(vs + v8_off(cr, 32 * g + 16)));
+      }
+      // P8 as the B operand: slot 16kt + i <-> key 32kt + 8(i/4) + 4g + i%4
+      i32x8 pf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          pf[4 * kt + qd] = (int)cvt4_e4m3(sat(p[kt][4 * qd] * qs), sat(p[kt][4 * qd + 1] * qs),
+                                           sat(p[kt][4 * qd + 2] * qs), sat(p[kt][4 * qd + 3] * qs));
+      const float pv_scale = (tmax / kE4M3Max) * sv[(size_t)bh * nb + j];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const f32x16 tmp = mfma_f8(va[c], pf, f32x16{});
+        os[c] += tmp * pv_scale;
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+    f_cur = f_next;
+  };
+  for (int t = 0; t < nu; t += 2) {
+    step2(t, B0{});
+    if (t + 1 < nu) step2(t + 1, B1{});
+  }
+
+  // ---- epilogue: zeta, relu(Q) T_i with T_i^T rows read from memory, combine ----
+  if (z_lane) zeta[zb_blk][tid % D] = Z[(size_t)bh * D + tid % D] - zacc;
+  bf16x8 qv[NS];
+  {
+    const __bf16* qr = Q + hoff + (size_t)min(row, N - 1) * D + 8 * g;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) qv[k] = *reinterpret_cast<const bf16x8*>(qr + 16 * k);
+  }
+  __syncthreads();
+  const float ltot = xor32_sum(lsum);
+  const float inv_l = ltot > 0.f ? 1.f / ltot : 0.f;
+  // num^T[c][m] = sum_c' T_i^T[c][c'] relu(Q)[m][c']: the A operand (rows c, k = c') is row c of
+  // T_i^T, 16 bytes per lane and step, from memory (L2: both wavefronts of a block read it)
+  const __bf16* tt = t_g + ((size_t)bh * nb + min(qb0 + blk, nb - 1)) * D * D;
+  f32x16 num[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) num[c] = f32x16{};
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const bf16x8 pq = relu8(row_ok ? qv[k] : bf16x8{});
+    bf16x8 ta[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      ta[c] = *reinterpret_cast<const bf16x8*>(tt + (size_t)(32 * c + lane % 32) * D + 16 * k + 8 * g);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) num[c] = mfma32(ta[c], pq, num[c]);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[blk][16 * k + 8 * g + jj];
+  }
+  den = xor32_sum(den);
+  const float inv_den = (topk < nb && den != 0.f) ? 1.f / den : 0.f;
+  if (!row_ok) return;
+  const float a = alpha[(size_t)bh * N + row];
+  const float ws = a * inv_l, wl = (1.f - a) * inv_den;
+  float* orow = O + hoff + (size_t)row * D;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(num[c][4 * qd + e], wl, os[c][4 * qd + e] * ws);
+      *reinterpret_cast<f32x4*>(orow + 32 * c + 8 * qd + 4 * g) = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const Dims& p, const void* X, uint8_t* codes, float* scales,
@@ -505,6 +812,19 @@ hipError_t launch_sparse_fp8(const Dims& p, const void* Q, const void* K, const 
   sparse_fp8_kernel<128><<<p.B * p.H * p.nb, kF8Threads, 0, stream>>>(
       (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, q8, k8, v8, sq, sk, sv, idx, alpha,
       ht_hi, ht_lo, Z, zb, O, p.N, p.nb, p.topk, c_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_pair8(const Dims& p, const void* Q, const uint8_t* q8, const uint8_t* k8,
+                               const uint8_t* v8, const float* sq, const float* sk,
+                               const float* sv, const int32_t* idx, const float* alpha,
+                               const __bf16* t_bf, const float* Z, const float* zb, float* O,
+                               hipStream_t stream) {
+  if (p.nb > 2048) return hipErrorInvalidValue;
+  const float c_log2 = 1.4426950408889634f / sqrtf((float)p.d);
+  pair8_kernel<128><<<p.B * p.H * ((p.nb + 1) / 2), kF8Threads, 0, stream>>>(
+      (const __bf16*)Q, q8, k8, v8, sq, sk, sv, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
+      c_log2);
   return hipGetLastError();
 }
 

@@ -95,8 +95,8 @@ typedef struct {
 
 /* Workspace sizes in bytes for a problem (0 when the problem is invalid or unsupported). */
 size_t sla_route_workspace_bytes(const sla_problem* p);
-/* variant: 0 = sla_forward (fused linear), 1 = sla_forward_fp8, 2 = literal linear mode,
- * 3 = mask-product linear mode. */
+/* variant: 0 = sla_forward (fused linear), 1 = sla_forward_fp8 (fused linear), 2 = literal
+ * linear mode, 3 = mask-product linear mode, 4 = sla_forward_fp8 in the mask-product mode. */
 size_t sla_forward_workspace_bytes(const sla_problem* p, int variant);
 
 /* Router (SLA2 Italian summary section 2.B, Arabic summary section 2.ba and 2.dal): block
@@ -114,8 +114,9 @@ int sla_forward(const sla_problem* p, const void* Q, const void* K, const void* 
                 const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                 hipStream_t stream);
 
-/* sla_forward with options (linear mode, timing events); opts may be NULL.
- * Needs sla_forward_workspace_bytes(p, 2) bytes in literal mode, (p, 0) otherwise. */
+/* sla_forward with options (linear mode, timing events); opts may be NULL.  Needs
+ * sla_forward_workspace_bytes(p, 2) bytes in literal mode, (p, 3) in the mask-product mode,
+ * (p, 0) in the fused one. */
 int sla_forward_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
                    const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                    hipStream_t stream, const sla_forward_opts* opts);
@@ -130,7 +131,9 @@ int sla_forward_fp8(const sla_problem* p, const void* Q, const void* K, const vo
                     const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
-/* sla_forward_fp8 with timing events (opts->linear_mode must be fused). */
+/* sla_forward_fp8 with options: opts->linear_mode fused (workspace variant 1) or mask product
+ * (variant 4: two query blocks per workgroup over the union of their kept blocks, T_i from the
+ * mask GEMM); literal is rejected (SLA_ERR_INVALID). */
 int sla_forward_fp8_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const float* alpha, float* O, void* ws,
                        size_t ws_bytes, hipStream_t stream, const sla_forward_opts* opts);

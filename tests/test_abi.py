@@ -52,12 +52,13 @@ def test_workspace_sizes(L):
     f = lambda p, v: L.sla_forward_workspace_bytes(ctypes.byref(p), v)  # noqa: E731
     assert r(P()) > 0 and f(P(), 0) > 0
     assert r(P(N=8192)) > r(P()) and r(P(H=4)) > r(P())
-    for v in (0, 1, 2, 3):
+    for v in (0, 1, 2, 3, 4):
         assert f(P(N=8192), v) > f(P(), v) and f(P(H=4), v) > f(P(), v)
     assert f(P(), 2) > f(P(), 0) and f(P(), 1) > f(P(), 0) and f(P(), 3) > f(P(), 0)
+    assert f(P(), 4) > f(P(), 3) and f(P(), 4) > f(P(), 1)
     # invalid or unsupported problems size to 0
     assert r(P(B=0)) == 0 and r(P(block=32)) == 0 and r(P(d=96)) == 0 and r(P(topk=65)) == 0
-    assert f(P(), 4) == 0 and f(P(), -1) == 0
+    assert f(P(), 5) == 0 and f(P(), -1) == 0
     assert L.sla_route_workspace_bytes(None) == 0
 
 
@@ -113,7 +114,10 @@ def test_fp8_and_mode_checks(L):
     assert L.sla_forward_fp8(ctypes.byref(P(d=64)), *args) == sla.SLA_ERR_UNSUPPORTED
     assert L.sla_forward_fp8(ctypes.byref(P(dtype=sla.SLA_F32)), *args) == sla.SLA_ERR_UNSUPPORTED
     assert L.sla_forward_fp8_ex(ctypes.byref(p), *args, ctypes.byref(opts_lit)) == sla.SLA_ERR_INVALID
-    assert L.sla_forward_fp8_ex(ctypes.byref(p), *args, ctypes.byref(opts_mp)) == sla.SLA_ERR_INVALID
+    # fp8 with the mask-product mode is accepted: with a one-byte workspace it stops at the size
+    # check, before anything is enqueued
+    small = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None)
+    assert L.sla_forward_fp8_ex(ctypes.byref(p), *small, ctypes.byref(opts_mp)) == sla.SLA_ERR_WORKSPACE
     assert L.sla_forward_ex(ctypes.byref(p), *args, ctypes.byref(opts_bad)) == sla.SLA_ERR_INVALID
     assert L.sla_quantize_e4m3(ctypes.byref(P(d=64)), FAKE, FAKE, FAKE, None) == sla.SLA_ERR_UNSUPPORTED
     assert L.sla_quantize_e4m3(ctypes.byref(p), None, FAKE, FAKE, None) == sla.SLA_ERR_INVALID

@@ -281,6 +281,21 @@ def test_fp8_forward_degenerate_k(k):
     check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what=f"forward fp8 k={k}")
 
 
+@pytest.mark.parametrize("k", [6, 0, 1, 57])
+def test_fp8_forward_mask_product(k):
+    """The quantised sparse branch on two query blocks per workgroup (mask-product linear mode)
+    against the oracle, on every element, for k = 6 and the degenerate counts."""
+    wl = small_ragged(k=k)
+    c = case("ragged_bf16" if k == 6 else f"ragged_k{k}", wl)
+    r = oracle_route(c, k)
+    say(f"forward fp8 mask_product k={k}")
+    got = run_forward(c, r["idx"], fp8=True, linear_mode="mask_product")
+    ref, _, _ = oracle.forward_fp8(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what=f"forward fp8 mask_product k={k}")
+    fused = run_forward(c, r["idx"], fp8=True)
+    check_close(got, fused, rel_tol=1e-2, max_tol=None, what=f"fp8 mask_product vs fused k={k}")
+
+
 def test_fp8_forward_branches_isolated():
     """alpha = 1: the quantised sparse branch alone; alpha = 0: the linear branch, unquantised."""
     wl = small_ragged()
@@ -356,6 +371,12 @@ def test_video_l_fp8_full_size():
     full_size(c, heads=[0, 21], blocks=[0, 1181], fp8=True, what="video_l fp8")
 
 
+def test_video_l_fp8_full_size_mask_product():
+    c = case("video_l", gen.workload("video_l"))
+    full_size(c, heads=[3, 30], blocks=[0, 591, 1181], fp8=True, what="video_l fp8 mask_product",
+              linear_mode="mask_product")
+
+
 @pytest.mark.parametrize("k", [102, 51, 26, 15])
 @pytest.mark.parametrize("scale", [0.5, 1.0, 2.0])
 def test_sparsity_sweep(scale, k):
@@ -420,10 +441,11 @@ def test_edge_shapes(wl):
         say(f"edge forward {wl.name} {mode}")
         check_close(run_forward(c, r["idx"], linear_mode=mode), ref, what=f"{wl.name} {mode}")
     if wl.dtype == "bf16" and wl.d == 128:
-        say(f"edge forward {wl.name} fp8")
         ref8, _, _ = oracle.forward_fp8(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
-        check_close(run_forward(c, r["idx"], fp8=True), ref8, rel_tol=TOL_REL_FP8, max_tol=None,
-                    what=f"{wl.name} fp8")
+        for mode in ("fused", "mask_product"):
+            say(f"edge forward {wl.name} fp8 {mode}")
+            check_close(run_forward(c, r["idx"], fp8=True, linear_mode=mode), ref8, rel_tol=TOL_REL_FP8,
+                        max_tol=None, what=f"{wl.name} fp8 {mode}")
     _CACHE.pop(wl.name, None)
 
 
