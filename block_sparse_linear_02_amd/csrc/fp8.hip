@@ -155,7 +155,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
   using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, g = lane / 32, w = tid / kWave;
+  const int lane = tid % kWave, g = lane / 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wavefront-uniform (scalar branches)
   const int role = w ^ ((blockIdx.x & 1) ? 2 : 0);  // 0,1 sparse; 2,3 state
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / nb, qb = item % nb;
@@ -480,13 +481,17 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
 }
 
 // The quantised sparse branch for two query blocks per workgroup, with the linear branch's
-// T_i = sum of the unselected blocks' states taken from memory (mask-product mode): the
-// workgroup walks the ascending union of the two index lists, stages every K8 (and, in pass 2,
-// V8^T) tile into LDS once for both blocks, and wavefront w takes rows 32 (w % 2) .. + 31 of
-// query block 2p + w / 2, skipping the tiles its block did not keep.  Pass 1: S = Q8 K8^T for
-// each row's exact maximum.  Pass 2: S again, P = exp(S - max); the 64 x 64 tile maximum of the
-// two wavefronts of a block meets in LDS at a barrier; P is quantised with scale max / 448 and
-// (P8 V8) sP sV accumulated by fp8 MFMA; the denominator sums the unquantised P.
+// T_i = sum of the unselected blocks' states taken from memory (mask-product mode).  Wavefront w
+// takes rows 32 (w % 2) .. + 31 of query block 2p + w / 2.
+//   Pass 1 (no LDS, no barrier): each wavefront walks its own block's kept list with its K8
+//   operands read straight from memory one tile ahead, S = Q8 K8^T, each row's exact maximum;
+//   z_j of the kept blocks summed on the way.
+//   Pass 2: the workgroup walks the ascending union of the two lists and stages each K8 and V8^T
+//   tile into LDS once for both blocks (K one step ahead of V); per tile t a wavefront whose
+//   block kept it forms P = exp(S - max) and its part of the 64 x 64 tile maximum, which meets
+//   the partner wavefront's in LDS at the step's barrier, so tile t's P is quantised (scale
+//   max / 448) and (P8 V8) sP sV accumulated by fp8 MFMA in step t + 1: one barrier per tile.
+//   The denominator sums the unquantised P.
 template <int D>
 __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     const __bf16* __restrict__ Q, const uint8_t* __restrict__ q8,
@@ -508,21 +513,25 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   __shared__ uint32_t bm[2][kMaxWords];
   __shared__ int32_t ul[kMaxWords * 32];  // the union, ascending: (j << 2) | kept-by mask
   __shared__ int32_t ucount;
+  __shared__ int32_t sl[2][kMaxWords * 32];  // the two kept lists (pass 1 reads them from here)
   __shared__ float zeta[2][D];
-  __shared__ float tmax_x[2][2];  // [block][wavefront half]: partial P tile maxima
+  __shared__ float tmx[2][2][2];  // [step parity][block][wavefront half]: partial P tile maxima
   auto kbuf = [&](auto BUFC) -> uint8_t* { return decltype(BUFC)::value ? kb1 : kb0; };
   auto vbuf = [&](auto BUFC) -> uint8_t* { return decltype(BUFC)::value ? vb1 : vb0; };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, g = lane / 32, w = tid / kWave;
+  const int lane = tid % kWave, g = lane / 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wavefront-uniform (scalar branches)
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int npair = (nb + 1) / 2;
   const int bh = item / npair, pr = item % npair;
   const int qb0 = 2 * pr;
   const bool has1 = qb0 + 1 < nb;
   const int blk = w / 2, half = w % 2;
+  const bool present = blk == 0 || has1;  // the second block of an odd n_b's last pair is absent
+  const int qb = min(qb0 + blk, nb - 1);
   const size_t hoff = (size_t)bh * N * D;
   const int nw = (nb + 31) / 32;
 
@@ -534,6 +543,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     if (b == 0 || has1) {
       const int j = idx[((size_t)bh * nb + qb0 + b) * topk + t % topk];
       atomicOr(&bm[b][j / 32], 1u << (j % 32));
+      sl[b][t % topk] = j;
     }
   }
   __syncthreads();
@@ -557,8 +567,80 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   __syncthreads();
   const int nu = ucount;
 
-  // tile staging straight into the swizzled layouts; a short tile's rows past its end re-read
-  // its last row (those keys are masked; V8^T codes past N are 0)
+  // this wavefront's 32 rows (absent rows read a clamped one and are zeroed)
+  const int m = 32 * half + lane % 32;
+  const int row = (qb0 + blk) * kBlock + m;
+  const bool row_ok = row < N;
+  i32x8 qf[N8];  // e4m3 Q as the B operand: k-slot 32g + b of step s <-> channel 64s + 32g + b
+  {
+    const uint8_t* qr = q8 + hoff + (size_t)min(row, N - 1) * D + 32 * g;
+#pragma unroll
+    for (int st = 0; st < N8; ++st) {
+      const i32x4* pq = reinterpret_cast<const i32x4*>(qr + 64 * st);
+      qf[st] = row_ok ? join8(pq[0], pq[1]) : i32x8{};
+    }
+  }
+  const float sqi = sq[(size_t)bh * nb + qb];
+
+  // ---- pass 1: each row's exact maximum of S (log2 units) over its block's kept tiles (list
+  // from LDS); K8 operands, the K scale and z_j from memory one tile ahead (rows past a short
+  // block's end re-read its last row: those keys are masked); z_j of the kept blocks summed by
+  // thread tid < D for block 0 and D .. 2D - 1 for block 1, i.e. each wavefront's own block ----
+  const int32_t* sel = sl[blk];
+  const int nsel = present ? topk : 0;
+  auto k8_regs = [&](int j, i32x8 (&kr)[2][N8]) {
+    const int nv = min(kBlock, N - j * kBlock);
+    const uint8_t* src = k8 + hoff + (size_t)j * kBlock * D;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int st = 0; st < N8; ++st) {
+        const i32x4* p = reinterpret_cast<const i32x4*>(src + (size_t)min(32 * kt + lane % 32, nv - 1) * D + 64 * st + 32 * g);
+        kr[kt][st] = join8(p[0], p[1]);
+      }
+  };
+  float mrow = -INFINITY, zacc = 0.f;
+  {
+    i32x8 kr[2][2][N8];
+    // z_j and the K scale of the tile in kr[b], loaded with it (used right after a load, they
+    // would make the compiler wait for every load in flight, the prefetch included)
+    float zr[2], skr[2];
+    auto step1 = [&](int t, auto BUFC) {
+      constexpr int BUF = decltype(BUFC)::value;
+      const int j = sel[t];
+      zacc += zr[BUF];
+      const float sc = sqi * skr[BUF] * c_log2;
+      // the next tile's operands, unconditionally (the last step re-reads its own tile): a load
+      // under a branch makes the compiler wait for every load in flight at the join
+      const int jn = sel[min(t + 1, nsel - 1)];
+      k8_regs(jn, kr[1 - BUF]);
+      zr[1 - BUF] = zb[((size_t)bh * nb + jn) * D + tid % D];
+      skr[1 - BUF] = sk[(size_t)bh * nb + jn];
+      const int nv = min(kBlock, N - j * kBlock);
+      const int lim = nv - 4 * g;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int st = 0; st < N8; ++st) s = mfma_f8(kr[BUF][kt][st], qf[st], s);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[i] * sc);
+      }
+    };
+    if (nsel > 0) {
+      k8_regs(sel[0], kr[0]);
+      zr[0] = zb[((size_t)bh * nb + sel[0]) * D + tid % D];
+      skr[0] = sk[(size_t)bh * nb + sel[0]];
+    }
+    for (int t = 0; t < nsel; t += 2) {
+      step1(t, B0{});
+      if (t + 1 < nsel) step1(t + 1, B1{});
+    }
+  }
+  mrow = xor32_max(mrow);
+
+  // ---- pass 2 ----
   auto stage_k = [&](int t, uint8_t* dst) {
     const int j = ul[t] >> 2;
     const int nv = min(kBlock, N - j * kBlock);
@@ -582,165 +664,100 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
       load_lds16(src + (size_t)c * kBlock + vunit * 16, dst + c0 * 64);
     }
   };
-
-  // this wavefront's 32 rows (absent rows read a clamped one and are zeroed)
-  const int m = 32 * half + lane % 32;
-  const int row = (qb0 + blk) * kBlock + m;
-  const bool row_ok = row < N;
-  i32x8 qf[N8];  // e4m3 Q as the B operand: k-slot 32g + b of step s <-> channel 64s + 32g + b
-  {
-    const uint8_t* qr = q8 + hoff + (size_t)min(row, N - 1) * D + 32 * g;
-#pragma unroll
-    for (int st = 0; st < N8; ++st) {
-      const i32x4* pq = reinterpret_cast<const i32x4*>(qr + 64 * st);
-      qf[st] = row_ok ? join8(pq[0], pq[1]) : i32x8{};
-    }
-  }
-  const float sqi = sq[(size_t)bh * nb + min(qb0 + blk, nb - 1)];
-  // S^T of one tile (keys 32 kt + 8(i/4) + 4g + i%4 in register i of s[kt]), unscaled
-  auto compute_s = [&](const uint8_t* ks, f32x16 (&s)[2]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < N8; ++st) {
-        const int r = 32 * kt + lane % 32;
-        const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g));
-        const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g + 16));
-        s[kt] = mfma_f8(join8(a0, a1), qf[st], s[kt]);
-      }
-    }
-  };
-  auto tile_rows = [&](int t) {
-    const int j = ul[t] >> 2;
-    return min(kBlock, N - j * kBlock);
-  };
-
-  // ---- pass 1: each row's exact maximum of S (log2 units) over its block's kept tiles ----
-  const bool z_lane = tid < 2 * D;  // thread tid < D: block 0's z sum, D .. 2D - 1: block 1's
-  const int zb_blk = tid / D;
-  float z_in = 0.f, zacc = 0.f;
-  float mrow = -INFINITY;
-  int f_cur = 0;
-  if (nu > 0) {
-    stage_k(0, kb0);
-    if (z_lane) z_in = zb[((size_t)bh * nb + (ul[0] >> 2)) * D + tid % D];
-    f_cur = ul[0] & 3;
-    wait_vmem();
-    __syncthreads();
-    if (z_lane && ((f_cur >> zb_blk) & 1)) zacc += z_in;
-  }
-  auto step1 = [&](int t, auto BUFC) {
-    constexpr int BUF = decltype(BUFC)::value;
-    int f_next = 0;
-    if (t + 1 < nu) {
-      stage_k(t + 1, kbuf(std::integral_constant<int, 1 - BUF>{}));
-      if (z_lane) z_in = zb[((size_t)bh * nb + (ul[t + 1] >> 2)) * D + tid % D];
-      f_next = ul[t + 1] & 3;
-    }
-    if ((f_cur >> blk) & 1) {
-      const int j = ul[t] >> 2;
-      const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
-      const int lim = tile_rows(t) - 4 * g;
-      f32x16 s[2];
-      compute_s(kbuf(BUFC), s);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[kt][i] * sc);
-    }
-    wait_vmem();
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    if (t + 1 < nu && z_lane && ((f_next >> zb_blk) & 1)) zacc += z_in;
-    f_cur = f_next;
-  };
-  for (int t = 0; t < nu; t += 2) {
-    step1(t, B0{});
-    if (t + 1 < nu) step1(t + 1, B1{});
-  }
-  mrow = xor32_max(mrow);
-
-  // ---- pass 2: P with the exact maximum, 64 x 64 tile maximum, fp8 PV ----
   f32x16 os[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) os[c] = f32x16{};
   float lsum = 0.f;
+  float pp[2][16];        // P of the previous tile (quantised once its tile maximum is known)
+  bool prev_kept = false;
+  int j_prev = 0;
+  // PV of the previous tile from vbuf(VB) with the tile maximum from tmx[PB]
+  auto pv_prev = [&](auto VBC, auto PBC) {
+    constexpr int PB = decltype(PBC)::value;
+    const float tmax = fmaxf(tmx[PB][blk][0], tmx[PB][blk][1]);
+    const float qs = tmax > 0.f ? kE4M3Max / tmax : 0.f;  // an all-underflow tile adds 0
+    const uint8_t* vs = vbuf(VBC);
+    i32x8 va[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int cr = 32 * c + lane % 32;
+      va[c] = join8(*reinterpret_cast<const i32x4*>(vs + v8_off(cr, 32 * g)),
+                    *reinterpret_cast<const i32x4*>(vs + v8_off(cr, 32 * g + 16)));
+    }
+    // P8 as the B operand: slot 16kt + i <-> key 32kt + 8(i/4) + 4g + i%4
+    i32x8 pf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        pf[4 * kt + qd] = (int)cvt4_e4m3(sat(pp[kt][4 * qd] * qs), sat(pp[kt][4 * qd + 1] * qs),
+                                         sat(pp[kt][4 * qd + 2] * qs), sat(pp[kt][4 * qd + 3] * qs));
+    const float pv_scale = (tmax / kE4M3Max) * sv[(size_t)bh * nb + j_prev];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const f32x16 tmp = mfma_f8(va[c], pf, f32x16{});
+      os[c] += tmp * pv_scale;
+    }
+  };
   if (nu > 0) {
     stage_k(0, kb0);
-    stage_v(0, vb0);
-    f_cur = ul[0] & 3;
     wait_vmem();
     __syncthreads();
   }
+  // step t: K(t) in kbuf(B) (B = t & 1), V(t - 1) in vbuf(1 - B); stage K(t + 1) and V(t)
   auto step2 = [&](int t, auto BUFC) {
     constexpr int BUF = decltype(BUFC)::value;
-    using NEXT = std::integral_constant<int, 1 - BUF>;
-    int f_next = 0;
-    if (t + 1 < nu) {
-      stage_k(t + 1, kbuf(NEXT{}));
-      stage_v(t + 1, vbuf(NEXT{}));
-      f_next = ul[t + 1] & 3;
-    }
-    const bool kept = (f_cur >> blk) & 1;  // wavefront-uniform
-    const int j = ul[t] >> 2;
-    float p[2][16];
+    using OTHER = std::integral_constant<int, 1 - BUF>;
+    if (t + 1 < nu) stage_k(t + 1, kbuf(OTHER{}));
+    stage_v(t, vbuf(BUFC));
+    if (prev_kept) pv_prev(OTHER{}, OTHER{});
+    const int e = ul[t];
+    const int j = e >> 2;
+    const bool kept = (e >> blk) & 1;  // wavefront-uniform
     float pmax = 0.f;
     if (kept) {
       const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
-      const int lim = row_ok ? tile_rows(t) - 4 * g : 0;
-      f32x16 s[2];
-      compute_s(kbuf(BUFC), s);
+      const int lim = row_ok ? min(kBlock, N - j * kBlock) - 4 * g : 0;
+      const uint8_t* ks = kbuf(BUFC);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int st = 0; st < N8; ++st) {
+          const int r = 32 * kt + lane % 32;
+          const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g));
+          const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g + 16));
+          s = mfma_f8(join8(a0, a1), qf[st], s);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[kt][i], sc, -mrow)) : 0.f;
-          lsum += p[kt][i];
-          pmax = fmaxf(pmax, p[kt][i]);
+          pp[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
+          lsum += pp[kt][i];
+          pmax = fmaxf(pmax, pp[kt][i]);
         }
+      }
       pmax = wave_max(pmax);
     }
-    if (lane == 0) tmax_x[blk][half] = pmax;
-    __syncthreads();
-    if (kept) {
-      const float tmax = fmaxf(tmax_x[blk][0], tmax_x[blk][1]);
-      const float qs = tmax > 0.f ? kE4M3Max / tmax : 0.f;  // an all-underflow tile adds 0
-      const uint8_t* vs = vbuf(BUFC);
-      i32x8 va[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int cr = 32 * c + lane % 32;
-        va[c] = join8(*reinterpret_cast<const i32x4*>(vs + v8_off(cr, 32 * g)),
-                      *reinterpret_cast<const i32x4*>(vs + v8_off(cr, 32 * g + 16)));
-      }
-      // P8 as the B operand: slot 16kt + i <-> key 32kt + 8(i/4) + 4g + i%4
-      i32x8 pf;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          pf[4 * kt + qd] = (int)cvt4_e4m3(sat(p[kt][4 * qd] * qs), sat(p[kt][4 * qd + 1] * qs),
-                                           sat(p[kt][4 * qd + 2] * qs), sat(p[kt][4 * qd + 3] * qs));
-      const float pv_scale = (tmax / kE4M3Max) * sv[(size_t)bh * nb + j];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const f32x16 tmp = mfma_f8(va[c], pf, f32x16{});
-        os[c] += tmp * pv_scale;
-      }
-    }
+    if (lane == 0) tmx[BUF][blk][half] = pmax;
+    prev_kept = kept;
+    j_prev = j;
     wait_vmem();
     __syncthreads();
-    f_cur = f_next;
   };
   for (int t = 0; t < nu; t += 2) {
     step2(t, B0{});
     if (t + 1 < nu) step2(t + 1, B1{});
   }
+  // the last tile's PV: its V and both partial maxima are in since the last barrier
+  if (prev_kept) {
+    if ((nu - 1) & 1)
+      pv_prev(B1{}, B1{});
+    else
+      pv_prev(B0{}, B0{});
+  }
 
   // ---- epilogue: zeta, relu(Q) T_i with T_i^T rows read from memory, combine ----
-  if (z_lane) zeta[zb_blk][tid % D] = Z[(size_t)bh * D + tid % D] - zacc;
+  if (tid < 2 * D) zeta[blk][tid % D] = Z[(size_t)bh * D + tid % D] - zacc;
   bf16x8 qv[NS];
   {
     const __bf16* qr = Q + hoff + (size_t)min(row, N - 1) * D + 8 * g;
@@ -752,7 +769,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   const float inv_l = ltot > 0.f ? 1.f / ltot : 0.f;
   // num^T[c][m] = sum_c' T_i^T[c][c'] relu(Q)[m][c']: the A operand (rows c, k = c') is row c of
   // T_i^T, 16 bytes per lane and step, from memory (L2: both wavefronts of a block read it)
-  const __bf16* tt = t_g + ((size_t)bh * nb + min(qb0 + blk, nb - 1)) * D * D;
+  const __bf16* tt = t_g + ((size_t)bh * nb + qb) * D * D;
   f32x16 num[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) num[c] = f32x16{};

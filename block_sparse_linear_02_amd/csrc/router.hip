@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     float* __restrict__ probs) {
   extern __shared__ float S[];  // [kRowsPerWg][nbp]
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wavefront-uniform
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * kRowsPerWg;
   const size_t base = (size_t)bh * nb * D;

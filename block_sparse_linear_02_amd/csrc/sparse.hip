@@ -106,7 +106,8 @@ __global__ __launch_bounds__(kSparseThreads, 2) void sparse_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, g = lane / 32;
-  const int role = (tid / kWave) ^ ((blockIdx.x & 1) ? 2 : 0);  // 0,1 sparse; 2,3 state
+  // wavefront-uniform as far as the compiler can tell, so role branches are scalar
+  const int role = __builtin_amdgcn_readfirstlane(tid / kWave) ^ ((blockIdx.x & 1) ? 2 : 0);  // 0,1 sparse; 2,3 state
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = item / nb, qb = item % nb;
   const size_t hoff = (size_t)bh * N * D;

@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   auto buf = [&](auto BUFC) -> __bf16* { return decltype(BUFC)::value ? lb1 : lb0; };
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave, g = lane / 32;
+  const int lane = tid % kWave, g = lane / 32;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wavefront-uniform (scalar branches)
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int npair = (nb + 1) / 2;
   const int bh = item / npair, pr = item % npair;
