@@ -15,6 +15,9 @@ tensors stand in for it with the same shapes and an attention-concentrating stru
 * ``sweep``      B=2 H=12 N=32768 d=128, keep in {20,10,5,3}% (k = round(keep*512)),
                  cluster scale in {0.5,1,2}, alpha fixed 0.5 or random.
 * ``video_l_fp8`` the ``video_l`` tensors, for the fp8 sparse-branch path.
+* ``pisa_video_s``, ``pisa_video_l`` the ``video_s`` / ``video_l`` tensors with 12.5 % of the
+                 KV blocks kept (k = 64 of 512, 148 of 1182), the 87.5 % sparsity at which the
+                 PISA summary reports its Wan2.1-14B result, for the PISA forward.
 
 Clustered Q/K: the latent grid is cut into boxes of (2, 8, 8) tokens (smaller at the edges);
 per (batch, head, box) a centre mu ~ N(0, s^2 I_d) is shared by the box's queries and keys,
@@ -85,6 +88,8 @@ WORKLOADS = {
     "video_l_fp8": Workload(
         "video_l_fp8", 1, 40, 75600, 128, 60, "bf16", "clustered", (21, 45, 80), fp8=True, wid=3
     ),
+    "pisa_video_s": Workload("pisa_video_s", 1, 12, 32768, 128, 64, "bf16", "clustered", (8, 64, 64), wid=2),
+    "pisa_video_l": Workload("pisa_video_l", 1, 40, 75600, 128, 148, "bf16", "clustered", (21, 45, 80), wid=3),
 }
 
 

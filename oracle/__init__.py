@@ -10,6 +10,9 @@ Sources (cited by page title and section; the summaries number their sections th
 * "SLA2: Sparse-Linear Attention with Learnable Routing and QAT" - Italian summary
   (gist.science/it/paper/2602.12675), sections 1, 2.A, 2.B, 2.C; and the Arabic summary of the
   same paper (gist.science/ar/paper/2602.12675), sections 1 and 2 (alef, ba, jim, dal).
+* "PISA - Piecewise Sparse Attention per Efficient Diffusion Transformers" - Italian technical
+  summary (gist.science/it/paper/2602.01077), section 2 (exact-or-approximate forward,
+  covariance-aware routing): ``pisa.py``.
 * "SALAD: Achieve High-Sparsity Attention via Efficient Linear Attention Tuning for Video
   Diffusion Transformer" (gist.science/it/paper/2601.16515), section 2 (ReLU kernel function,
   linear branch sharing Q, K, V with the sparse branch).
@@ -37,4 +40,11 @@ from .fp8 import (  # noqa: F401
     quantize_blocks,
     forward_fp8_head,
     forward_fp8,
+)
+from .pisa import (  # noqa: F401
+    pisa_block_stats,
+    pisa_cov_norms,
+    pisa_route,
+    pisa_forward_head,
+    pisa_forward,
 )

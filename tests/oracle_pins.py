@@ -385,4 +385,149 @@ def pin_fp8_error_scale(orc):
     assert 5e-3 < rel < 0.1, rel
 
 
+# ----------------------------------------------------------------------------------------------
+# PISA (exact-or-approximate) forward and covariance-aware routing
+
+
+def _pisa_golden():
+    with open(os.path.join(GOLDEN, "pisa_worked_example.json")) as f:
+        g = json.load(f)
+    a = math.sqrt(2.0) * math.log(2.0)
+
+    def val(x):
+        if isinstance(x, str) and x.lstrip("-") == "a":
+            return -a if x.startswith("-") else a
+        return float(Fraction(x)) if isinstance(x, str) else float(x)
+
+    return g, (lambda rows: np.array([[val(x) for x in r] for r in rows]))  # noqa: E731
+
+
+def pin_pisa_worked_example(orc):
+    """The hand-derived example in tests/golden/pisa_worked_example.json: block statistics,
+    covariance norms, both routings and the output (exact rationals plus multiples of ln 2)."""
+    g, arr = _pisa_golden()
+    Q, K, V = arr(g["Q"]), arr(g["K"]), arr(g["V"])
+    blk = g["block"]
+    st = orc.pisa_block_stats(K, V, blk)
+    np.testing.assert_allclose(st["centroid"], arr(g["expected_centroid"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(st["vsum"], arr(g["expected_vsum"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(st["H"], np.array(g["expected_H"], dtype=np.float64), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(st["Hbar"], arr(g["expected_Hbar"]), rtol=0, atol=1e-14)
+    M2 = np.array([float(Fraction(x)) for x in g["expected_M_squared"]])
+    np.testing.assert_allclose(orc.pisa_cov_norms(st["H"], st["Hbar"]) ** 2, M2, rtol=1e-13)
+    rc = orc.pisa_route(Q, K, V, g["topk"], blk, covariance=True)
+    rp = orc.pisa_route(Q, K, V, g["topk"], blk, covariance=False)
+    assert np.array_equal(rc["idx"], np.array(g["expected_idx_covariance"])), rc["idx"]
+    assert np.array_equal(rp["idx"], np.array(g["expected_idx_plain"])), rp["idx"]
+    O = orc.pisa_forward(Q[None, None], K[None, None], V[None, None], np.array(g["idx"])[None, None], blk)
+    ln2 = math.log(2.0)
+    exp = np.array([[float(Fraction(c0)) + float(Fraction(c1)) * ln2 for c0, c1 in row] for row in g["expected_O"]])
+    np.testing.assert_allclose(O[0, 0], exp, rtol=0, atol=1e-13)
+
+
+def pin_pisa_all_selected_is_full_attention(orc):
+    """Every block kept: nothing is approximated and PISA is full softmax attention (torch SDPA)."""
+    N, d, blk = 200, 16, 64
+    Q, K, V = (_rand((N, d), s) for s in (71, 72, 73))
+    n_b = -(-N // blk)
+    idx = np.tile(np.arange(n_b, dtype=np.int32), (n_b, 1))
+    O = orc.pisa_forward(Q[None, None], K[None, None], V[None, None], idx[None, None], blk)
+    np.testing.assert_allclose(O[0, 0], _sdpa(Q, K, V), rtol=0, atol=1e-12)
+
+
+def pin_pisa_constant_block_keys_exact(orc):
+    """Keys constant inside each block (short last block included): every H_j is 0 and the
+    zero-order block term is exact, so PISA equals full attention for any kept set, k = 0 too."""
+    N, d, blk = 45, 6, 8
+    n_b = -(-N // blk)
+    kb = _rand((n_b, d), 74, 1.5)
+    K = np.repeat(kb, blk, axis=0)[:N]
+    Q, V = _rand((N, d), 75, 1.5), _rand((N, d), 76)
+    ref = _sdpa(Q, K, V)
+    for k, seed in ((0, 0), (2, 77), (n_b - 1, 78)):
+        idx = _rand_idx(n_b, k, seed) if k else np.zeros((n_b, 0), np.int32)
+        O = orc.pisa_forward(Q[None, None], K[None, None], V[None, None], idx[None, None], blk)
+        np.testing.assert_allclose(O[0, 0], ref, rtol=0, atol=1e-12)
+    st = orc.pisa_block_stats(K, V, blk)
+    assert np.abs(st["H"]).max() < 1e-12 and np.abs(st["Hbar"]).max() < 1e-12
+
+
+def pin_pisa_first_order_convergence(orc):
+    """Keys kbar_j + eps * delta_n with one zero-sum offset pattern for every block and values
+    v0_n + c_j: all H_j equal Hbar, so the first-order correction is exact and the error against
+    full attention falls as eps^2 (ratio ~4 when eps halves).  Without the correction, or with it
+    mis-scaled, the error is first order (ratio ~2)."""
+    blk, n_b, d = 16, 6, 8
+    N = blk * n_b
+    delta = _rand((blk, d), 81)
+    delta -= delta.mean(axis=0)
+    v0 = _rand((blk, d), 82)
+    cen = _rand((n_b, d), 83, 0.7)
+    c = _rand((n_b, d), 84)
+    V = np.concatenate([v0 + c[j] for j in range(n_b)])
+    Q = _rand((N, d), 85, 1.2)
+    idx = _rand_idx(n_b, 2, 86)
+    errs = []
+    for eps in (0.08, 0.04, 0.02):
+        K = np.concatenate([cen[j] + eps * delta for j in range(n_b)])
+        O = orc.pisa_forward(Q[None, None], K[None, None], V[None, None], idx[None, None], blk)
+        errs.append(np.abs(O[0, 0] - _sdpa(Q, K, V)).max())
+        st = orc.pisa_block_stats(K, V, blk)
+        assert np.abs(orc.pisa_cov_norms(st["H"], st["Hbar"])).max() < 1e-12 * (1 + np.abs(st["Hbar"]).max())
+    r1, r2 = errs[0] / errs[1], errs[1] / errs[2]
+    assert 3.4 < r1 < 4.6 and 3.4 < r2 < 4.6, (errs, r1, r2)
+
+
+def pin_pisa_stats_invariances(orc):
+    """H_j and M_j ignore a constant shift of a block's keys (centering) and of its values (the
+    offsets sum to zero); H_j has rank <= r_j - 1; scaling V scales Hbar and M alike."""
+    N, d, blk = 100, 12, 8  # 13 blocks, the last one 4 tokens (rank <= 3 < d)
+    K, V = _rand((N, d), 91), _rand((N, d), 92)
+    st = orc.pisa_block_stats(K, V, blk)
+    M = orc.pisa_cov_norms(st["H"], st["Hbar"])
+    K2, V2 = K.copy(), V.copy()
+    K2[16:24] += _rand((d,), 93, 5.0)
+    V2[96:] += _rand((d,), 94, 5.0)
+    st2 = orc.pisa_block_stats(K2, V2, blk)
+    np.testing.assert_allclose(st2["H"], st["H"], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(orc.pisa_cov_norms(st2["H"], st2["Hbar"]), M, rtol=1e-12)
+    np.testing.assert_allclose(st2["centroid"][2] - st["centroid"][2], K2[16] - K[16], atol=1e-12)
+    np.testing.assert_allclose(st2["vsum"][12] - st["vsum"][12], 4 * (V2[96] - V[96]), atol=1e-11)
+    for j, r in enumerate(st["count"]):
+        sv = np.linalg.svd(st["H"][j], compute_uv=False)
+        assert np.all(sv[int(r) - 1 :] < 1e-10 * sv[0]), (j, sv)
+    st3 = orc.pisa_block_stats(K, -2.5 * V, blk)
+    np.testing.assert_allclose(st3["Hbar"], -2.5 * st["Hbar"], atol=1e-12)
+    np.testing.assert_allclose(orc.pisa_cov_norms(st3["H"], st3["Hbar"]), 2.5 * M, rtol=1e-12)
+
+
+def pin_pisa_route_minimises_error_bound(orc):
+    """Brute force over every kept set of size k on a tiny head: the covariance-aware choice
+    minimises the summed first-order error bound sum_{j not kept} e^{s_ij} ||H_j - Hbar||, with
+    s from torch's average pooling; the plain choice maximises the kept scores."""
+    import itertools
+
+    N, d, blk, k = 6 * 8 - 3, 4, 8, 2
+    Q, K, V = _rand((N, d), 95), _rand((N, d), 96), _rand((N, d), 97)
+    n_b = -(-N // blk)
+    pool = lambda X: torch.nn.functional.avg_pool1d(torch.from_numpy(X).T[None], blk, blk, ceil_mode=True)[0].T.numpy()  # noqa: E731
+    s = pool(Q) @ pool(K).T / math.sqrt(d)
+    Hs = []
+    for j in range(n_b):
+        kk, vv = K[j * blk : (j + 1) * blk], V[j * blk : (j + 1) * blk]
+        Hs.append(sum(np.outer(kk[n] - kk.mean(axis=0), vv[n]) for n in range(len(kk))))
+    Hb = sum(Hs) / n_b
+    M = np.array([np.linalg.norm(h - Hb) for h in Hs])
+    rc = orc.pisa_route(Q, K, V, k, blk, covariance=True)
+    rp = orc.pisa_route(Q, K, V, k, blk, covariance=False)
+    np.testing.assert_allclose(rc["scores"], s, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rc["M"], M, rtol=1e-12)
+    for i in range(n_b):
+        best = min(itertools.combinations(range(n_b), k),
+                   key=lambda S: sum(math.exp(s[i, j]) * M[j] for j in range(n_b) if j not in S))
+        assert tuple(rc["idx"][i]) == best, (i, rc["idx"][i], best)
+        top = max(itertools.combinations(range(n_b), k), key=lambda S: sum(s[i, j] for j in S))
+        assert tuple(rp["idx"][i]) == top, (i, rp["idx"][i], top)
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -32,6 +32,17 @@ MUTATIONS = {
     "fp8_scale_dropped": ("fp8.py", "deq[a:b] = e4m3_decode(codes[a:b]) * np.float64(scales[t])", "deq[a:b] = e4m3_decode(codes[a:b])"),
     "fp8_truncating_round": ("fp8.py", "m8 = np.rint((mant * 2.0 - 1.0) * 8.0)", "m8 = np.floor((mant * 2.0 - 1.0) * 8.0)"),
     "fp8_bias_off_by_one": ("fp8.py", "_E4M3_BIAS = 7", "_E4M3_BIAS = 8"),
+    "pisa_no_first_order": ("pisa.py", "num = e @ V[tok] + al @ vsum[uns] + (q @ Hbar) * al.sum(axis=1, keepdims=True)", "num = e @ V[tok] + al @ vsum[uns]"),
+    "pisa_first_order_unscaled": ("pisa.py", "+ (q @ Hbar) * al.sum(", "+ (Q[a:b] @ Hbar) * al.sum("),
+    "pisa_den_without_counts": ("pisa.py", "den = e.sum(axis=1) + al @ cnt[uns]", "den = e.sum(axis=1) + al.sum(axis=1)"),
+    "pisa_uncentered_H": ("pisa.py", "H[j] = (K[a:b] - centroid[j]).T @ V[a:b]", "H[j] = K[a:b].T @ V[a:b]"),
+    "pisa_hbar_sum": ("pisa.py", '"Hbar": H.mean(axis=0)', '"Hbar": H.sum(axis=0)'),
+    "pisa_cov_sign": ("pisa.py", "sel = s + np.log(M)[None, :]", "sel = s - np.log(M)[None, :]"),
+    "pisa_vsum_mean": ("pisa.py", "vsum[j] = V[a:b].sum(axis=0)", "vsum[j] = V[a:b].mean(axis=0)"),
+    "pisa_centroid_over_block": ("pisa.py", "centroid[j] = K[a:b].mean(axis=0)", "centroid[j] = K[a:b].sum(axis=0) / block"),
+    "pisa_kept_also_approximated": ("pisa.py", "uns = np.flatnonzero(~keep)", "uns = np.arange(n_b)"),
+    "pisa_no_centroid_scale": ("pisa.py", "y = q @ kbar[uns].T", "y = Q[a:b] @ kbar[uns].T"),
+    "pisa_route_unscaled": ("pisa.py", "s = (qbar @ st[\"centroid\"].T) / np.sqrt(Q.shape[1])", "s = qbar @ st[\"centroid\"].T"),
     "fp8_tile_scale_dropped": ("fp8.py", "num += (enc(p / sP) * sP) @ Vd[starts[j]:ends[j]]", "num += enc(p / sP) @ Vd[starts[j]:ends[j]]"),
 }
 
