@@ -10,6 +10,12 @@ a GPU every call raises.
     O = forward(Q, K, V, idx, alpha, fp8=True)           # e4m3 sparse branch
     O = forward(Q, K, V, idx, alpha, linear_mode="literal")
 
+PISA exact-or-approximate attention (C ABI in include/sla_pisa.h):
+
+    st = pisa_stats(K, V)                                # centroids, value sums, Hbar, M_j
+    idx, mask, scores = pisa_route(Q, st, topk, covariance=True)
+    O = pisa_forward(Q, K, V, st, idx)
+
 Shapes: Q, K, V [B, H, N, d] (bf16 or fp32, d in {64, 128}), proj_q / proj_k [d, d] fp32,
 alpha [B, H, N] fp32, idx [B, H, ceil(N/64), topk] int32 ascending, O [B, H, N, d] fp32.
 """
@@ -30,6 +36,10 @@ __all__ = [
     "quantize_e4m3",
     "route_workspace_bytes",
     "forward_workspace_bytes",
+    "PisaStats",
+    "pisa_stats",
+    "pisa_route",
+    "pisa_forward",
     "BLOCK",
 ]
 
@@ -96,6 +106,18 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = i32
         L.sla_quantize_e4m3.argtypes = [P, vp, vp, vp, vp]
         L.sla_quantize_e4m3.restype = i32
+        L.sla_pisa_stats_bytes.argtypes = [P]
+        L.sla_pisa_stats_bytes.restype = sz
+        L.sla_pisa_workspace_bytes.argtypes = [P]
+        L.sla_pisa_workspace_bytes.restype = sz
+        L.sla_pisa_stats_offsets.argtypes = [P, ctypes.POINTER(sz)]
+        L.sla_pisa_stats_offsets.restype = i32
+        L.sla_pisa_stats.argtypes = [P, vp, vp, vp, sz, vp, sz, vp]
+        L.sla_pisa_stats.restype = i32
+        L.sla_pisa_route.argtypes = [P, vp, vp, sz, i32, vp, vp, vp, vp, sz, vp]
+        L.sla_pisa_route.restype = i32
+        L.sla_pisa_forward.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.sla_pisa_forward.restype = i32
         L.sla_status_string.argtypes = [i32]
         L.sla_status_string.restype = ctypes.c_char_p
         L.sla_last_hip_error.argtypes = []
@@ -210,3 +232,90 @@ def quantize_e4m3(X):
     if st != SLA_OK:
         raise SLAError(st, "sla_quantize_e4m3")
     return codes, scales
+
+
+class PisaStats:
+    """The PISA statistics buffer of one K, V (written by pisa_stats) with typed views:
+    kbar_hi, kbar_lo, vsum [B, H, n_b, d] bf16; hbar_t [B, H, d, d] bf16 (Hbar transposed);
+    hbar [B, H, d, d] fp32; M, lnM [B, H, n_b] fp32."""
+
+    _NAMES = ("kbar_hi", "kbar_lo", "vsum", "hbar_t", "hbar", "M", "lnM")
+
+    def __init__(self, buf, shape, offsets):
+        self.buf = buf
+        self.shape = shape  # (B, H, N, d)
+        B, H, N, d = shape
+        nb = -(-N // BLOCK)
+        shapes = [(B, H, nb, d)] * 3 + [(B, H, d, d)] * 2 + [(B, H, nb)] * 2
+        dtypes = [torch.bfloat16] * 4 + [torch.float32] * 3
+        for name, off, shp, dt in zip(self._NAMES, offsets, shapes, dtypes):
+            n = 1
+            for x in shp:
+                n *= x
+            nbytes = n * torch.empty((), dtype=dt).element_size()
+            setattr(self, name, buf[off : off + nbytes].view(dt).view(shp))
+
+
+def pisa_stats(K, V, workspace=None, out=None) -> PisaStats:
+    """PISA statistics pass over K, V [B, H, N, d]: centroids, value sums, Hbar, M_j, ln M_j."""
+    _check_qkv(K, V)
+    K, V = K.contiguous(), V.contiguous()
+    p = _problem(K, 0)
+    L = lib()
+    nbytes = L.sla_pisa_stats_bytes(ctypes.byref(p))
+    offs = (ctypes.c_size_t * 7)()
+    st = L.sla_pisa_stats_offsets(ctypes.byref(p), offs)
+    if st != SLA_OK:
+        raise SLAError(st, "sla_pisa_stats_offsets")
+    buf = out if out is not None else torch.empty(max(nbytes, 1), dtype=torch.uint8, device=K.device)
+    need = L.sla_pisa_workspace_bytes(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=K.device)
+    st = L.sla_pisa_stats(ctypes.byref(p), _ptr(K), _ptr(V), _ptr(buf), buf.numel(), _ptr(ws),
+                          ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_pisa_stats")
+    return PisaStats(buf, tuple(K.shape), list(offs))
+
+
+def pisa_route(Q, stats: PisaStats, topk: int, covariance: bool = True, want_mask: bool = False,
+               want_scores: bool = False, workspace=None, idx_out=None):
+    """Covariance-aware HardTop-k of PISA.  Returns (idx, mask, scores); scores are the ranked
+    selection scores (qbar . kbar / sqrt(d) [+ ln M_j]); mask / scores None unless requested."""
+    _check_qkv(Q)
+    Q = Q.contiguous()
+    if tuple(Q.shape) != stats.shape:
+        raise ValueError("Q must have the shape of the K, V the statistics were taken from")
+    B, H, N, d = Q.shape
+    nb = -(-N // BLOCK)
+    p = _problem(Q, topk)
+    dev = Q.device
+    idx = idx_out if idx_out is not None else torch.empty((B, H, nb, topk), dtype=torch.int32, device=dev)
+    mask = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev) if want_mask else None
+    scores = torch.empty((B, H, nb, nb), dtype=torch.float32, device=dev) if want_scores else None
+    need = lib().sla_pisa_workspace_bytes(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().sla_pisa_route(ctypes.byref(p), _ptr(Q), _ptr(stats.buf), stats.buf.numel(),
+                              1 if covariance else 0, _ptr(idx), _ptr(mask), _ptr(scores), _ptr(ws),
+                              ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_pisa_route")
+    return idx, mask, scores
+
+
+def pisa_forward(Q, K, V, stats: PisaStats, idx, out=None):
+    """PISA forward: exact attention over the kept blocks, zero-order block terms plus the
+    global first-order Hbar correction over the rest.  Returns O [B, H, N, d] fp32."""
+    _check_qkv(Q, K, V)
+    Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
+    if tuple(Q.shape) != stats.shape:
+        raise ValueError("Q, K, V must have the shape the statistics were taken from")
+    B, H, N, d = Q.shape
+    topk = idx.shape[-1]
+    idx = idx.contiguous().to(torch.int32)
+    p = _problem(Q, topk)
+    O = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device)
+    st = lib().sla_pisa_forward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(stats.buf),
+                                stats.buf.numel(), _ptr(idx), _ptr(O), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_pisa_forward")
+    return O

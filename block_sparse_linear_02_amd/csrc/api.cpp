@@ -1,6 +1,7 @@
 // api.cpp - the C ABI of libsla (declared in include/sla.h): argument checks, workspace
 // carving and the launch sequence on the caller's stream.
 #include "sla.h"
+#include "sla_pisa.h"
 
 #include <climits>
 #include <cstdint>
@@ -107,6 +108,47 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
     f.sv = c.take<float>(BH * d.nb);
   }
   if (out) *out = f;
+  return c.off;
+}
+
+// PISA statistics buffer (caller-owned, written by sla_pisa_stats, read by route and forward)
+struct PisaStats {
+  __bf16 *kbar_hi, *kbar_lo, *vsum, *hbar_t;
+  float *hbar, *M, *lnM;
+};
+size_t carve_pisa_stats(const sla::Dims& d, void* base, PisaStats* out, size_t* offsets) {
+  Carve c(base);
+  const size_t BH = (size_t)d.B * d.H;
+  const size_t n = BH * d.nb * d.d, dd = BH * d.d * d.d;
+  PisaStats s;
+  size_t o[7];
+  o[0] = c.off; s.kbar_hi = c.take<__bf16>(n);
+  o[1] = c.off; s.kbar_lo = c.take<__bf16>(n);
+  o[2] = c.off; s.vsum = c.take<__bf16>(n);
+  o[3] = c.off; s.hbar_t = c.take<__bf16>(dd);
+  o[4] = c.off; s.hbar = c.take<float>(dd);
+  o[5] = c.off; s.M = c.take<float>(BH * d.nb);
+  o[6] = c.off; s.lnM = c.take<float>(BH * d.nb);
+  if (out) *out = s;
+  if (offsets)
+    for (int i = 0; i < 7; ++i) offsets[i] = o[i];
+  return c.off;
+}
+// PISA scratch: chunk partials of Hbar (sla_pisa_stats), pooled queries (sla_pisa_route)
+struct PisaWs {
+  float* h_part;
+  __bf16 *q_hi, *q_lo;
+};
+size_t carve_pisa_ws(const sla::Dims& d, void* base, PisaWs* out) {
+  Carve c(base);
+  const size_t BH = (size_t)d.B * d.H;
+  const int cb = sla::state_chunk_blocks(d);
+  const size_t nchunk = (d.nb + cb - 1) / cb;
+  PisaWs w;
+  w.h_part = c.take<float>(BH * nchunk * d.d * d.d);
+  w.q_hi = c.take<__bf16>(BH * d.nb * d.d);
+  w.q_lo = c.take<__bf16>(BH * d.nb * d.d);
+  if (out) *out = w;
   return c.off;
 }
 
@@ -250,6 +292,83 @@ int sla_quantize_e4m3(const sla_problem* p, const void* X, uint8_t* codes, float
   if (d.dtype != sla::kBF16 || d.d != 128) return SLA_ERR_UNSUPPORTED;
   if (!X || !codes || !scales) return SLA_ERR_INVALID;
   hipError_t e = sla::launch_quantize(d, X, codes, scales, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+size_t sla_pisa_stats_bytes(const sla_problem* p) {
+  sla::Dims d;
+  if (check_problem(p, &d) != SLA_OK) return 0;
+  return carve_pisa_stats(d, nullptr, nullptr, nullptr);
+}
+
+int sla_pisa_stats_offsets(const sla_problem* p, size_t offsets[7]) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (!offsets) return SLA_ERR_INVALID;
+  carve_pisa_stats(d, nullptr, nullptr, offsets);
+  return SLA_OK;
+}
+
+size_t sla_pisa_workspace_bytes(const sla_problem* p) {
+  sla::Dims d;
+  if (check_problem(p, &d) != SLA_OK) return 0;
+  return carve_pisa_ws(d, nullptr, nullptr);
+}
+
+int sla_pisa_stats(const sla_problem* p, const void* K, const void* V, void* stats,
+                   size_t stats_bytes, void* ws, size_t ws_bytes, hipStream_t stream) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (!K || !V || !stats || !ws) return SLA_ERR_INVALID;
+  if (stats_bytes < carve_pisa_stats(d, nullptr, nullptr, nullptr) ||
+      ws_bytes < carve_pisa_ws(d, nullptr, nullptr))
+    return SLA_ERR_WORKSPACE;
+  PisaStats s;
+  carve_pisa_stats(d, stats, &s, nullptr);
+  PisaWs w;
+  carve_pisa_ws(d, ws, &w);
+  hipError_t e = sla::launch_pisa_stats(d, K, V, s.kbar_hi, s.kbar_lo, s.vsum, w.h_part, s.hbar_t,
+                                        s.hbar, s.M, s.lnM, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+int sla_pisa_route(const sla_problem* p, const void* Q, const void* stats, size_t stats_bytes,
+                   int covariance, int32_t* idx, uint8_t* mask, float* scores, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !stats || (d.topk > 0 && !idx) || !ws) return SLA_ERR_INVALID;
+  if (covariance != 0 && covariance != 1) return SLA_ERR_INVALID;
+  if (stats_bytes < carve_pisa_stats(d, nullptr, nullptr, nullptr) ||
+      ws_bytes < carve_pisa_ws(d, nullptr, nullptr))
+    return SLA_ERR_WORKSPACE;
+  PisaStats s;
+  carve_pisa_stats(d, const_cast<void*>(stats), &s, nullptr);
+  PisaWs w;
+  carve_pisa_ws(d, ws, &w);
+  hipError_t e = sla::launch_pisa_route(d, Q, w.q_hi, w.q_lo, s.kbar_hi, s.kbar_lo,
+                                        covariance ? s.lnM : nullptr, idx, mask, scores, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+int sla_pisa_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                     const void* stats, size_t stats_bytes, const int32_t* idx, float* O,
+                     hipStream_t stream) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !K || !V || !stats || !O || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
+  if (d.nb > sla::pisa_max_blocks()) return SLA_ERR_UNSUPPORTED;
+  if (stats_bytes < carve_pisa_stats(d, nullptr, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  PisaStats s;
+  carve_pisa_stats(d, const_cast<void*>(stats), &s, nullptr);
+  hipError_t e = sla::launch_pisa(d, Q, K, V, idx, s.kbar_hi, s.kbar_lo, s.vsum, s.hbar_t, O, stream);
   if (e != hipSuccess) return hip_fail(e);
   return SLA_OK;
 }

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
 // One workgroup per 256 consecutive elements of H^T (64 float4 columns): thread t sums every
 // fourth chunk partial starting at chunk t / 64 for the float4 column t % 64, then the four
 // partial sums are added in a fixed order through LDS (deterministic).  Without chunk partials of
-// H (h_part null, mask-product mode) only Z is reduced.
+// H (h_part null, mask-product mode) only Z is reduced; without z_part only H.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h_part,
                                                      const float* __restrict__ z_part,
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
       }
       const size_t o = (size_t)bh * D * D + 4 * (size_t)e4;
       *reinterpret_cast<bf16x4*>(ht_hi + o) = hi;
-      *reinterpret_cast<bf16x4*>(ht_lo + o) = lo;
+      if (ht_lo) *reinterpret_cast<bf16x4*>(ht_lo + o) = lo;
       if (h_full) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
       }
     }
   }
-  if (blockIdx.x == 0 && threadIdx.x < D) {
+  if (z_part && blockIdx.x == 0 && threadIdx.x < D) {
     // in chunk order (deterministic), four loads in flight
     const float* zp = z_part + (size_t)bh * nchunk * D + threadIdx.x;
     float z = 0.f;

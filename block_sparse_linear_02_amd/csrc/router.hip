@@ -98,17 +98,22 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
     __syncthreads();
   }
 
-  // projection: y[b][c] = sum_r xbar[b][r] * W[r][c]
+  // projection: y[b][c] = sum_r xbar[b][r] * W[r][c]; no W: the pooled means themselves
   constexpr int G = kPoolThreads / D;  // thread groups, each covering all D output columns
   const int c = tid % D;
   const int grp = tid / D;
   float y[kPoolBlocksPerWg / G];
+  if (W) {
 #pragma unroll
-  for (int u = 0; u < kPoolBlocksPerWg / G; ++u) y[u] = 0.f;
-  for (int r = 0; r < D; ++r) {
-    const float w = W[r * D + c];
+    for (int u = 0; u < kPoolBlocksPerWg / G; ++u) y[u] = 0.f;
+    for (int r = 0; r < D; ++r) {
+      const float w = W[r * D + c];
 #pragma unroll
-    for (int u = 0; u < kPoolBlocksPerWg / G; ++u) y[u] += xbar[grp + u * G][r] * w;
+      for (int u = 0; u < kPoolBlocksPerWg / G; ++u) y[u] += xbar[grp + u * G][r] * w;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPoolBlocksPerWg / G; ++u) y[u] = xbar[grp + u * G][c];
   }
 #pragma unroll
   for (int u = 0; u < kPoolBlocksPerWg / G; ++u) {
@@ -129,13 +134,15 @@ constexpr int kMaxChunks = 32;   // n_b <= 2048
 
 // Scores of 16 query blocks against all key blocks into LDS, then per row the k-th largest
 // score and the ascending compaction.  NCH = key slots per lane (at least ceil(n_b / 64)):
-// invalid slots hold key 0, below every valid key, so no slot needs a guard.
+// invalid slots hold key 0, below every valid key, so no slot needs a guard.  bias (optional,
+// [bh][n_b]) is added to every score of key block j before the selection; probs receives the
+// row softmax of the scores, or (raw) the scores themselves.
 template <int D, int NCH>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     const __bf16* __restrict__ q_hi, const __bf16* __restrict__ q_lo,
     const __bf16* __restrict__ k_hi, const __bf16* __restrict__ k_lo, int nb, int topk,
-    float scale, int nbp, int32_t* __restrict__ idx, uint8_t* __restrict__ mask,
-    float* __restrict__ probs) {
+    float scale, int nbp, const float* __restrict__ bias, int raw, int32_t* __restrict__ idx,
+    uint8_t* __restrict__ mask, float* __restrict__ probs) {
   extern __shared__ float S[];  // [kRowsPerWg][nbp]
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wavefront-uniform
@@ -180,8 +187,9 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
           acc = mfma16(ahi[s], bhi[u][s], acc);
         }
         const int j = t * 16 + lane % 16;
+        const float bj = (bias && j < nb) ? bias[(size_t)bh * nb + j] : 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[(4 * (lane / 16) + r) * nbp + j] = acc[r] * scale;
+        for (int r = 0; r < 4; ++r) S[(4 * (lane / 16) + r) * nbp + j] = fmaf(acc[r], scale, bj);
       }
     }
   }
@@ -232,7 +240,10 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
       pos += __popcll(selm);
       ties += __popcll(eqm);
     }
-    if (probs) {
+    if (probs && raw) {
+      float* prow = probs + ((size_t)bh * nb + i) * nb;
+      for (int j = lane; j < nb; j += kWave) prow[j] = srow[j];
+    } else if (probs) {
       float mx = -INFINITY;
       for (int j = lane; j < nb; j += kWave) mx = fmaxf(mx, srow[j]);
       mx = wave_max(mx);
@@ -248,8 +259,9 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
 
 template <int D>
 hipError_t launch_topk(const Dims& p, const __bf16* q_hi, const __bf16* q_lo,
-                       const __bf16* k_hi, const __bf16* k_lo, int32_t* idx, uint8_t* mask,
-                       float* probs, size_t lds, hipStream_t stream) {
+                       const __bf16* k_hi, const __bf16* k_lo, const float* bias, int raw,
+                       int32_t* idx, uint8_t* mask, float* probs, size_t lds,
+                       hipStream_t stream) {
   const int nbp = (p.nb + 15) / 16 * 16;
   dim3 grid((p.nb + kRowsPerWg - 1) / kRowsPerWg, p.B * p.H);
   const float scale = 1.0f / sqrtf((float)D);
@@ -257,7 +269,8 @@ hipError_t launch_topk(const Dims& p, const __bf16* q_hi, const __bf16* q_lo,
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    kern<<<grid, kTopkThreads, lds, stream>>>(q_hi, q_lo, k_hi, k_lo, p.nb, p.topk, scale, nbp, idx, mask, probs);
+    kern<<<grid, kTopkThreads, lds, stream>>>(q_hi, q_lo, k_hi, k_lo, p.nb, p.topk, scale, nbp,
+                                              bias, raw, idx, mask, probs);
     return hipGetLastError();
   };
   if (nch <= 1) return go(score_topk_kernel<D, 1>);
@@ -300,8 +313,34 @@ hipError_t launch_route(const Dims& p, const void* Q, const void* K, const float
   if (e != hipSuccess) return e;
 
   const size_t lds = route_lds_bytes(p.nb);
-  if (p.d == 128) return launch_topk<128>(p, q_hi, q_lo, k_hi, k_lo, idx, mask, probs, lds, stream);
-  return launch_topk<64>(p, q_hi, q_lo, k_hi, k_lo, idx, mask, probs, lds, stream);
+  if (p.d == 128)
+    return launch_topk<128>(p, q_hi, q_lo, k_hi, k_lo, nullptr, 0, idx, mask, probs, lds, stream);
+  return launch_topk<64>(p, q_hi, q_lo, k_hi, k_lo, nullptr, 0, idx, mask, probs, lds, stream);
+}
+
+hipError_t launch_pisa_route(const Dims& p, const void* Q, __bf16* q_hi, __bf16* q_lo,
+                             const __bf16* kbar_hi, const __bf16* kbar_lo, const float* bias,
+                             int32_t* idx, uint8_t* mask, float* scores, hipStream_t stream) {
+  // pooled queries only (grid z = 1), no projection
+  dim3 g1((p.nb + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg, p.B * p.H, 1);
+  if (p.dtype == kBF16 && p.d == 128)
+    pool_project_kernel<__bf16, 128><<<g1, kPoolThreads, 0, stream>>>(
+        (const __bf16*)Q, nullptr, nullptr, nullptr, p.N, p.nb, q_hi, q_lo, nullptr, nullptr);
+  else if (p.dtype == kBF16 && p.d == 64)
+    pool_project_kernel<__bf16, 64><<<g1, kPoolThreads, 0, stream>>>(
+        (const __bf16*)Q, nullptr, nullptr, nullptr, p.N, p.nb, q_hi, q_lo, nullptr, nullptr);
+  else if (p.dtype == kF32 && p.d == 128)
+    pool_project_kernel<float, 128><<<g1, kPoolThreads, 0, stream>>>(
+        (const float*)Q, nullptr, nullptr, nullptr, p.N, p.nb, q_hi, q_lo, nullptr, nullptr);
+  else
+    pool_project_kernel<float, 64><<<g1, kPoolThreads, 0, stream>>>(
+        (const float*)Q, nullptr, nullptr, nullptr, p.N, p.nb, q_hi, q_lo, nullptr, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = route_lds_bytes(p.nb);
+  if (p.d == 128)
+    return launch_topk<128>(p, q_hi, q_lo, kbar_hi, kbar_lo, bias, 1, idx, mask, scores, lds, stream);
+  return launch_topk<64>(p, q_hi, q_lo, kbar_hi, kbar_lo, bias, 1, idx, mask, scores, lds, stream);
 }
 
 }  // namespace sla

@@ -81,4 +81,22 @@ hipError_t launch_sparse_fp8(const Dims& p, const void* Q, const void* K, const 
                              const __bf16* ht_lo, const float* Z, const float* zb, float* O,
                              hipStream_t stream);
 
+// PISA.  Statistics: kbar_j as bf16 hi + lo and vs_j as bf16 ([BH][nb][d] each), Hbar^T in
+// bf16 [BH][d][d] ([c][c'], V channel major), Hbar in fp32 [BH][d][d] ([c'][c]), M_j and ln M_j
+// in fp32 [BH][nb]; h_part holds the chunk partials ([BH][chunks][d][d], state_chunk_blocks).
+hipError_t launch_pisa_stats(const Dims& p, const void* K, const void* V, __bf16* kbar_hi,
+                             __bf16* kbar_lo, __bf16* vsum, float* h_part, __bf16* hbar_t,
+                             float* hbar, float* M, float* lnM, hipStream_t stream);
+// Routing: pooled Q (no projection; split bf16 [BH][nb][d] in q_hi, q_lo) against the centroids,
+// plus bias[j] (ln M_j, or null for the attention score alone); scores gets the raw selection
+// scores when non-null.
+hipError_t launch_pisa_route(const Dims& p, const void* Q, __bf16* q_hi, __bf16* q_lo,
+                             const __bf16* kbar_hi, const __bf16* kbar_lo, const float* bias,
+                             int32_t* idx, uint8_t* mask, float* scores, hipStream_t stream);
+// Forward (n_b <= pisa_max_blocks()).
+int pisa_max_blocks();
+hipError_t launch_pisa(const Dims& p, const void* Q, const void* K, const void* V,
+                       const int32_t* idx, const __bf16* kbar_hi, const __bf16* kbar_lo,
+                       const __bf16* vsum, const __bf16* hbar_t, float* O, hipStream_t stream);
+
 }  // namespace sla

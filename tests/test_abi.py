@@ -1,5 +1,5 @@
 """The C ABI on the host (no GPU needed): the library loads, exports every function that
-include/sla.h declares, sizes workspaces, and rejects bad arguments with the documented status
+include/*.h declares, sizes workspaces, and rejects bad arguments with the documented status
 before enqueuing anything."""
 
 import ctypes
@@ -13,7 +13,8 @@ import torch
 import block_sparse_linear_02_amd as sla
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sla.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
 
 
@@ -27,14 +28,17 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sla_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(sla_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) >= 10, names
+    assert len(names) >= 16, names
+    assert "sla_pisa_forward" in names and "sla_route" in names
     out = subprocess.run(["nm", "-D", "--defined-only", sla.lib_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (sla_\w+)$", out, flags=re.M))
     missing = [n for n in names if n not in exported]
@@ -136,3 +140,53 @@ def test_binding_refuses_cpu_tensors(L):
         sla.route(x, x, torch.eye(128), torch.eye(128), 1)
     with pytest.raises(ValueError):
         sla.forward(x, x, x, torch.zeros((1, 1, 1, 1), dtype=torch.int32), torch.zeros((1, 1, 64)))
+
+
+def test_pisa_sizes_and_offsets(L):
+    sb = lambda p: L.sla_pisa_stats_bytes(ctypes.byref(p))  # noqa: E731
+    wb = lambda p: L.sla_pisa_workspace_bytes(ctypes.byref(p))  # noqa: E731
+    p = P()
+    assert sb(p) > 0 and wb(p) > 0
+    assert sb(P(N=8192)) > sb(p) and sb(P(H=4)) > sb(p) and wb(P(H=4)) > wb(p)
+    assert sb(P(B=0)) == 0 and wb(P(d=96)) == 0 and sb(P(block=32)) == 0
+    offs = (ctypes.c_size_t * 7)()
+    assert L.sla_pisa_stats_offsets(ctypes.byref(p), offs) == sla.SLA_OK
+    B, H, N, d = 1, 2, 4096, 128
+    nb = N // 64
+    sizes = [B * H * nb * d * 2] * 3 + [B * H * d * d * 2, B * H * d * d * 4, B * H * nb * 4, B * H * nb * 4]
+    for i in range(7):
+        assert offs[i] % 256 == 0
+        if i:
+            assert offs[i] >= offs[i - 1] + sizes[i - 1]
+    assert offs[6] + sizes[6] <= sb(p)
+    assert L.sla_pisa_stats_offsets(ctypes.byref(P(d=96)), offs) == sla.SLA_ERR_UNSUPPORTED
+    assert L.sla_pisa_stats_offsets(ctypes.byref(p), None) == sla.SLA_ERR_INVALID
+
+
+def test_pisa_argument_checks(L):
+    p = P()
+    sb = L.sla_pisa_stats_bytes(ctypes.byref(p))
+    wb = L.sla_pisa_workspace_bytes(ctypes.byref(p))
+    # every call below fails a check before anything is enqueued
+    assert L.sla_pisa_stats(ctypes.byref(p), FAKE, None, FAKE, sb, FAKE, wb, None) == sla.SLA_ERR_INVALID
+    assert L.sla_pisa_stats(ctypes.byref(p), FAKE, FAKE, FAKE, sb - 1, FAKE, wb, None) == sla.SLA_ERR_WORKSPACE
+    assert L.sla_pisa_stats(ctypes.byref(p), FAKE, FAKE, FAKE, sb, FAKE, wb - 1, None) == sla.SLA_ERR_WORKSPACE
+    assert L.sla_pisa_stats(ctypes.byref(P(d=96)), FAKE, FAKE, FAKE, sb, FAKE, wb, None) == sla.SLA_ERR_UNSUPPORTED
+    r = L.sla_pisa_route
+    assert r(ctypes.byref(p), FAKE, FAKE, sb, 2, FAKE, None, None, FAKE, wb, None) == sla.SLA_ERR_INVALID
+    assert r(ctypes.byref(p), FAKE, FAKE, sb, 1, None, None, None, FAKE, wb, None) == sla.SLA_ERR_INVALID
+    assert r(ctypes.byref(p), FAKE, FAKE, sb - 1, 1, FAKE, None, None, FAKE, wb, None) == sla.SLA_ERR_WORKSPACE
+    assert r(ctypes.byref(p), FAKE, FAKE, sb, 0, FAKE, None, None, FAKE, wb - 1, None) == sla.SLA_ERR_WORKSPACE
+    assert r(ctypes.byref(P(topk=65)), FAKE, FAKE, sb, 1, FAKE, None, None, FAKE, wb, None) == sla.SLA_ERR_INVALID
+    f = L.sla_pisa_forward
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, sb, None, FAKE, None) == sla.SLA_ERR_INVALID
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, None, sb, FAKE, FAKE, None) == sla.SLA_ERR_INVALID
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, sb, FAKE, None, None) == sla.SLA_ERR_INVALID
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, sb - 1, FAKE, FAKE, None) == sla.SLA_ERR_WORKSPACE
+    assert f(ctypes.byref(P(block=32)), FAKE, FAKE, FAKE, FAKE, sb, FAKE, FAKE, None) == sla.SLA_ERR_UNSUPPORTED
+
+
+def test_pisa_binding_refuses_cpu_tensors(L):
+    x = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sla.pisa_stats(x, x)
