@@ -11,6 +11,13 @@ states on chip instead, literal sums stored states per query block.  Prints ONE 
 sel(i)} c_j of the step's actual index lists, divided by the step time), ms_per_step, the
 dominant kernel's roofline (its algorithmic FLOPs per launch over its event-timed duration) and
 the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py --workload pisa_video_s      # the PISA exact-or-approximate forward
+
+With a PISA workload one step = sla.pisa_stats + sla.pisa_route + sla.pisa_forward (statistics of
+K and V, covariance-aware top-k, exact phase + centroid scan + Hbar correction); value = PISA's
+algorithmic TFLOP/s (exact pairs as above, 4 d r_i per unselected block for the scan, 2 d^2 per
+query row for the correction) over the step time.
 """
 
 from __future__ import annotations
@@ -35,7 +42,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="video_s", help="video_s | video_l | video_l_fp8")
+    ap.add_argument("--workload", default="video_s",
+                    help="video_s | video_l | video_l_fp8 | pisa_video_s | pisa_video_l")
     ap.add_argument("--linear-mode", default="mask_product", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0,
@@ -141,6 +149,203 @@ def cpu_baseline(inputs, wl, idx_gpu, budget_s=15.0):
     }
 
 
+def events(n):
+    import torch
+
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def avg_ms(pairs):
+    return sum(b.elapsed_time(e) for b, e in pairs) / len(pairs)
+
+
+def quantiles(pairs):
+    t = sorted(b.elapsed_time(e) for b, e in pairs)
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]  # noqa: E731
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "calls": len(t)}
+
+
+def hbm(nbytes, t_ms):
+    gbs = nbytes / (t_ms * 1e-3) / 1e9
+    return {"bytes": nbytes, "ms": t_ms, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS}
+
+
+PISA_SOURCES = [
+    "block_sparse_linear_02_amd/csrc/pisa.hip",
+    "block_sparse_linear_02_amd/csrc/sla_tiles.hpp",
+    "block_sparse_linear_02_amd/csrc/sla_device.hpp",
+]
+
+
+def pisa_cpu_baseline(inputs, wl, budget_s=15.0):
+    """The PISA oracle on a bounded sample: whole heads (statistics, routing, every query block's
+    forward) in order until about `budget_s` of CPU time, the last head possibly on a random
+    subset of its query blocks; scaled to the whole workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+
+    nb = wl.n_blocks
+    heads = wl.B * wl.H
+    per_head, used, blocks_done = [], 0.0, 0
+    for bh in range(heads):
+        b, h = divmod(bh, wl.H)
+        Q, K, V = inputs["Q"][b, h], inputs["K"][b, h], inputs["V"][b, h]
+        t0 = time.perf_counter()
+        r = oracle.pisa_route(Q, K, V, wl.topk, 64)
+        t_fixed = time.perf_counter() - t0
+        order = np.random.default_rng(bh).permutation(nb)
+        done, t_fwd = 0, 0.0
+        while done < nb and used + t_fixed + t_fwd < budget_s:
+            blocks = order[done : done + 8]
+            t0 = time.perf_counter()
+            oracle.pisa_forward_head(Q, K, V, r["idx"], 64, q_blocks=blocks, stats=r["stats"])
+            t_fwd += time.perf_counter() - t0
+            done += len(blocks)
+        used += t_fixed + t_fwd
+        blocks_done += done
+        per_head.append(t_fixed + t_fwd * nb / max(done, 1))
+        if used >= budget_s:
+            break
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    return {
+        "seconds_per_call": heads * sum(per_head) / len(per_head),
+        "sample": f"{len(per_head)} of {heads} heads (statistics, routing and {blocks_done} query "
+                  f"blocks of {len(per_head) * nb}; {used:.1f} s of CPU time), scaled to all heads "
+                  f"and query blocks",
+        "cores": int(threads),
+    }
+
+
+def bench_pisa(a, wl):
+    """One step = pisa_stats + pisa_route (covariance-aware) + pisa_forward."""
+    import torch
+
+    import block_sparse_linear_02_amd as sla
+    import gen
+
+    dev = torch.device("cuda:0")
+    inputs = gen.draw(wl, 0)
+    Q, K, V = (inputs[k].to(dev) for k in ("Q", "K", "V"))
+    B, H, N, d = Q.shape
+    nb = wl.n_blocks
+    k = wl.topk
+    idx = torch.empty((B, H, nb, k), dtype=torch.int32, device=dev)
+    O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    st = sla.pisa_stats(K, V)  # allocates the statistics buffer once
+    ws = torch.empty(sla.pisa_workspace_bytes(Q, k), dtype=torch.uint8, device=dev)
+    ev_t, ev_s, ev_r, ev_f = events(a.steps), events(a.steps), events(a.steps), events(a.steps)
+    for e in ev_t + ev_s + ev_r + ev_f:
+        e[0].record()
+        e[1].record()
+    torch.cuda.synchronize()
+
+    def step(i=None):
+        rec = (lambda evs, j: evs[i][j].record()) if i is not None else (lambda evs, j: None)
+        rec(ev_t, 0)
+        rec(ev_s, 0)
+        sla.pisa_stats(K, V, workspace=ws, out=st.buf)
+        rec(ev_s, 1)
+        rec(ev_r, 0)
+        sla.pisa_route(Q, st, k, covariance=True, workspace=ws, idx_out=idx)
+        rec(ev_r, 1)
+        rec(ev_f, 0)
+        sla.pisa_forward(Q, K, V, st, idx, out=O)
+        rec(ev_f, 1)
+        rec(ev_t, 1)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / a.steps
+    step_q = quantiles(ev_t)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n_cold = min(10, a.steps)
+    ev_c = events(n_cold)
+    for i in range(n_cold):
+        scratch.fill_(i & 0xff)
+        ev_c[i][0].record()
+        step()
+        ev_c[i][1].record()
+    torch.cuda.synchronize()
+    cold_q = quantiles(ev_c)
+    del scratch
+
+    # algorithmic work: exact pairs (QK^T + PV), the scan over each query block's unselected
+    # blocks (q . kbar and alpha vs: 4 d per query row and block), the Hbar correction (2 d^2
+    # per query row); the kernel also scans the kept centroids (masked), executed but not counted
+    exact = sparse_flops(idx, N, d)
+    r = torch.full((nb,), 64.0, dtype=torch.float64)
+    r[-1] = N - 64 * (nb - 1)
+    rows = float(r.sum()) * B * H
+    scan = 4.0 * d * rows * (nb - k)
+    corr = 2.0 * d * d * rows if k < nb else 0.0
+    flops = exact + scan + corr
+    executed = exact + (4.0 * d * rows * nb if k < nb else 0.0) + corr
+    stats_ms, route_ms, fwd_ms = avg_ms(ev_s), avg_ms(ev_r), avg_ms(ev_f)
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    digest = source_digest(PISA_SOURCES)
+    es = Q.element_size()
+    # statistics: K and V read twice (block statistics, then M_j), kbar hi/lo and vs written;
+    # routing: Q read, kbar hi/lo and ln M read, idx written
+    stats_bytes = 4 * B * H * N * d * es + 3 * B * H * nb * d * 2 + 2 * B * H * nb * 4
+    route_bytes = B * H * N * d * es + 2 * B * H * nb * d * 2 + B * H * nb * 4 + B * H * nb * k * 4
+    rec = {
+        "metric": "PISA exact-or-approximate attn fwd ms/call + effective TFLOPS",
+        "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective: PISA algorithmic FLOPs / call time)",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if es == 2 else "f32",
+        "data": "synthetic (seeded clustered video-DiT-shaped tensors)",
+        "config": {
+            "workload": f"{wl.name}: B={B} H={H} N={N} d={d} block=64 topk={k} of {nb} "
+                        f"({100 * (1 - k / nb):.1f}% of the blocks approximated), covariance-aware routing",
+            "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": k,
+        },
+        "tflop_per_call": {"exact": exact / 1e12, "scan": scan / 1e12, "correction": corr / 1e12},
+        "step_ms_events": step_q,
+        "cold_cache_step_ms": cold_q,
+        "kernels_ms": {"stats": stats_ms, "route": route_ms, "forward": fwd_ms,
+                       "other": ms - stats_ms - route_ms - fwd_ms},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "pisa_kernel",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic_for(f"pisa_kernel@{wl.name}", digest),
+            "flops_per_launch": flops,
+            "mfma_flops_executed_per_launch": executed,
+            "executed_tflops": executed / (fwd_ms * 1e-3) / 1e12,
+        },
+        "hbm_kernels": {"stats": hbm(stats_bytes, stats_ms), "route": hbm(route_bytes, route_ms)},
+    }
+    if not a.no_cpu_baseline:
+        cb = pisa_cpu_baseline(inputs, wl)
+        rec["cpu_baseline"] = {
+            "value": flops / cb["seconds_per_call"] / 1e12,
+            "unit": "TFLOP/s (effective, same FLOP count)",
+            "ms_per_call": 1e3 * cb["seconds_per_call"],
+            "cores": cb["cores"],
+            "kind": "oracle",
+            "sample": cb["sample"],
+        }
+    print(json.dumps(rec), flush=True)
+
+
 def mass_covered(inputs, wl, idx_np, blocks):
     """Diagnostic (not pass/fail): the share of each query row's full softmax attention mass
     that falls on the tokens of its query block's kept blocks, for a few query blocks of head
@@ -200,6 +405,9 @@ def main():
         return
 
     wl = gen.workload(a.workload)
+    if wl.name.startswith("pisa"):
+        bench_pisa(a, wl)
+        return
     if wl.fp8 and a.linear_mode == "literal":
         a.linear_mode = "fused"  # the fp8 path has the fused and mask-product linear modes
     inputs = gen.draw(wl, 0)
@@ -214,9 +422,6 @@ def main():
                else {"fused": 0, "literal": 2, "mask_product": 3}[a.linear_mode])
     ws_f = torch.empty(sla.forward_workspace_bytes(Q, wl.topk, variant), dtype=torch.uint8, device=dev)
     O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
-    def events(n):
-        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-
     ev, ev_r, ev_s, ev_t = events(a.steps), events(a.steps), events(a.steps), events(a.steps)
     for e in ev + ev_r + ev_s + ev_t:
         e[0].record()
@@ -245,14 +450,6 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = 1e3 * elapsed / a.steps
-
-    def avg_ms(pairs):
-        return sum(b.elapsed_time(e) for b, e in pairs) / len(pairs)
-
-    def quantiles(pairs):
-        t = sorted(b.elapsed_time(e) for b, e in pairs)
-        q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]  # noqa: E731
-        return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "calls": len(t)}
 
     step_q = quantiles(ev_t)
     # cold cache: the same call after writing a 512 MB scratch buffer (larger than the 256 MB
@@ -303,11 +500,6 @@ def main():
         states_bytes = (2 * B * H * N * d * es + B * H * nb * d * 4 + hj_bytes
                         + hj_bytes * -(-nb // 256) + hj_bytes)
         gemm_flops = 2.0 * B * H * nb * nb * d * d
-
-    def hbm(nbytes, t_ms):
-        gbs = nbytes / (t_ms * 1e-3) / 1e9
-        return {"bytes": nbytes, "ms": t_ms, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS}
 
     rec = {
         "metric": "sparse-linear attn fwd ms/call + effective TFLOPS, N=32768 H=12 d=128 90% sparse",

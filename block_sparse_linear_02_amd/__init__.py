@@ -40,6 +40,7 @@ __all__ = [
     "pisa_stats",
     "pisa_route",
     "pisa_forward",
+    "pisa_workspace_bytes",
     "BLOCK",
 ]
 
@@ -254,6 +255,11 @@ class PisaStats:
                 n *= x
             nbytes = n * torch.empty((), dtype=dt).element_size()
             setattr(self, name, buf[off : off + nbytes].view(dt).view(shp))
+
+
+def pisa_workspace_bytes(Q, topk: int = 0) -> int:
+    """Scratch bytes of pisa_stats and pisa_route for inputs shaped like Q."""
+    return lib().sla_pisa_workspace_bytes(ctypes.byref(_problem(Q, topk)))
 
 
 def pisa_stats(K, V, workspace=None, out=None) -> PisaStats:
