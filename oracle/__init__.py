@@ -31,6 +31,8 @@ from .sla import (  # noqa: F401
     block_states,
     forward_head,
     forward,
+    branch_drops,
+    forward_dropped,
     dense_P,
 )
 from .fp8 import (  # noqa: F401

@@ -33,6 +33,8 @@ __all__ = [
     "block_states",
     "forward_head",
     "forward",
+    "branch_drops",
+    "forward_dropped",
     "dense_P",
 ]
 
@@ -238,6 +240,36 @@ def forward(Q, K, V, idx, alpha, block: int = 64):
             Os[bb, hh] = np.concatenate(os_)
             Ol[bb, hh] = np.concatenate(ol)
     return O, Os, Ol
+
+
+def branch_drops(alpha, tau: float):
+    """Which branches a head drops (SALAD section 2, Post-Tuning Branch Dropping: a linear
+    branch whose scale is very low is removed at inference).
+
+    In SLA2 the linear branch of query token t is weighted by 1 - alpha_t and the sparse branch
+    by alpha_t (SLA2 Italian summary section 2.A).  Reading: per (batch, head), the linear branch
+    is dropped when max_t (1 - alpha_t) <= tau and the sparse branch when max_t alpha_t <= tau,
+    0 <= tau < 0.5 (so at most one branch of a head is dropped); tau = 0 drops only branches
+    whose weight is exactly 0 everywhere.  The threshold is taken as float32, the precision the
+    GPU compares in; 1 - alpha is exact in both precisions wherever it can reach tau.
+    alpha [B, H, N] -> (drop_linear [B, H] bool, drop_sparse [B, H] bool).
+    """
+    a = _f64(alpha)
+    t = float(np.float32(tau))
+    if not 0.0 <= t < 0.5:
+        raise ValueError("tau must lie in [0, 0.5)")
+    return (1.0 - a).max(axis=-1) <= t, a.max(axis=-1) <= t
+
+
+def forward_dropped(Q, K, V, idx, alpha, tau: float, block: int = 64):
+    """SLA2 forward with branch dropping (see branch_drops): a dropped branch contributes
+    nothing, the kept one keeps its weight, O = [alpha O_s] + [(1 - alpha) O_l].
+    Returns (O, drop_linear, drop_sparse)."""
+    _, Os, Ol = forward(Q, K, V, idx, alpha, block)
+    dl, ds = branch_drops(alpha, tau)
+    a = _f64(alpha)[..., None]
+    O = np.where(ds[..., None, None], 0.0, a * Os) + np.where(dl[..., None, None], 0.0, (1.0 - a) * Ol)
+    return O, dl, ds
 
 
 def dense_P(Q, K, idx, alpha, block: int = 64):

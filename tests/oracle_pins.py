@@ -386,6 +386,59 @@ def pin_fp8_error_scale(orc):
 
 
 # ----------------------------------------------------------------------------------------------
+# branch dropping
+
+
+def _drop_case():
+    B, H, N, d, blk, k = 1, 5, 150, 8, 32, 2
+    rng = np.random.default_rng(61)
+    Q, K, V = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    alpha = rng.uniform(0.0, 1.0, (B, H, N))
+    alpha[0, 0] = 1.0                            # linear weight exactly 0
+    alpha[0, 1] = 0.0                            # sparse weight exactly 0
+    alpha[0, 2] = rng.uniform(0.97, 1.0, N)      # linear weight at most 0.03
+    alpha[0, 2, 7] = 1.0 - 0.03125               # exactly at the threshold below (a float32 value)
+    alpha[0, 3] = rng.uniform(0.0, 0.02, N)      # sparse weight at most 0.02
+    n_b = -(-N // blk)
+    idx = np.stack([_rand_idx(n_b, k, 62 + h) for h in range(H)])[None]
+    return Q, K, V, idx, alpha, blk
+
+
+def pin_branch_drop_exact_at_zero(orc):
+    """tau = 0 drops only branches whose weight is exactly 0 everywhere, so the output equals the
+    undropped forward bit for bit."""
+    Q, K, V, idx, alpha, blk = _drop_case()
+    O, _, _ = orc.forward(Q, K, V, idx, alpha, blk)
+    Od, dl, ds = orc.forward_dropped(Q, K, V, idx, alpha, 0.0, blk)
+    assert dl.tolist() == [[True, False, False, False, False]], dl
+    assert ds.tolist() == [[False, True, False, False, False]], ds
+    assert np.array_equal(Od, O)
+
+
+def pin_branch_drop_threshold(orc):
+    """tau = 1/32: the head whose linear weight reaches 1/32 (inclusive) loses exactly
+    (1 - alpha) O_l, the head whose sparse weight stays below it loses exactly alpha O_s, the
+    others are untouched; tau outside [0, 0.5) is refused."""
+    Q, K, V, idx, alpha, blk = _drop_case()
+    O, Os, Ol = orc.forward(Q, K, V, idx, alpha, blk)
+    Od, dl, ds = orc.forward_dropped(Q, K, V, idx, alpha, 0.03125, blk)
+    assert dl.tolist() == [[True, False, True, False, False]], dl
+    assert ds.tolist() == [[False, True, False, True, False]], ds
+    a = alpha[..., None]
+    np.testing.assert_allclose(Od[0, 2], O[0, 2] - (1 - a[0, 2]) * Ol[0, 2], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(Od[0, 3], O[0, 3] - a[0, 3] * Os[0, 3], rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(Od[0, 4], O[0, 4])
+    _, dl2, _ = orc.forward_dropped(Q, K, V, idx, alpha, 0.0312, blk)
+    assert not dl2[0, 2], "1 - alpha = 1/32 exceeds a threshold just below it"
+    for bad in (-1e-3, 0.5):
+        try:
+            orc.branch_drops(alpha, bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"tau {bad} accepted")
+
+
+# ----------------------------------------------------------------------------------------------
 # PISA (exact-or-approximate) forward and covariance-aware routing
 
 

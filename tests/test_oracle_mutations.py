@@ -32,6 +32,10 @@ MUTATIONS = {
     "fp8_scale_dropped": ("fp8.py", "deq[a:b] = e4m3_decode(codes[a:b]) * np.float64(scales[t])", "deq[a:b] = e4m3_decode(codes[a:b])"),
     "fp8_truncating_round": ("fp8.py", "m8 = np.rint((mant * 2.0 - 1.0) * 8.0)", "m8 = np.floor((mant * 2.0 - 1.0) * 8.0)"),
     "fp8_bias_off_by_one": ("fp8.py", "_E4M3_BIAS = 7", "_E4M3_BIAS = 8"),
+    "drop_strict_threshold": ("sla.py", "return (1.0 - a).max(axis=-1) <= t, a.max(axis=-1) <= t", "return (1.0 - a).max(axis=-1) < t, a.max(axis=-1) <= t"),
+    "drop_by_mean_weight": ("sla.py", "return (1.0 - a).max(axis=-1) <= t, a.max(axis=-1) <= t", "return (1.0 - a).mean(axis=-1) <= t, a.max(axis=-1) <= t"),
+    "drop_sparse_by_min": ("sla.py", "return (1.0 - a).max(axis=-1) <= t, a.max(axis=-1) <= t", "return (1.0 - a).max(axis=-1) <= t, a.min(axis=-1) <= t"),
+    "drop_renormalises": ("sla.py", "O = np.where(ds[..., None, None], 0.0, a * Os) + np.where(dl[..., None, None], 0.0, (1.0 - a) * Ol)", "O = np.where(ds[..., None, None], 0.0 * Os, a * Os) + np.where(dl[..., None, None], Os - a * Os, (1.0 - a) * Ol)"),
     "pisa_no_first_order": ("pisa.py", "num = e @ V[tok] + al @ vsum[uns] + (q @ Hbar) * al.sum(axis=1, keepdims=True)", "num = e @ V[tok] + al @ vsum[uns]"),
     "pisa_first_order_unscaled": ("pisa.py", "+ (q @ Hbar) * al.sum(", "+ (Q[a:b] @ Hbar) * al.sum("),
     "pisa_den_without_counts": ("pisa.py", "den = e.sum(axis=1) + al @ cnt[uns]", "den = e.sum(axis=1) + al.sum(axis=1)"),
