@@ -65,6 +65,8 @@ class ForwardOpts(ctypes.Structure):
         ("sparse_end", ctypes.c_void_p),
         ("states_begin", ctypes.c_void_p),
         ("states_end", ctypes.c_void_p),
+        ("branch_drop", ctypes.c_int32),
+        ("drop_tau", ctypes.c_float),
     ]
 
 
@@ -189,10 +191,12 @@ def route(Q, K, proj_q, proj_k, topk: int, want_mask: bool = False, want_scores:
 
 
 def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", workspace=None,
-            out=None, events=None, state_events=None):
+            out=None, events=None, state_events=None, drop_tau=None):
     """O = alpha * O_s + (1 - alpha) * O_l.  `events` = (begin, end) torch.cuda.Event pair
     recorded around the sparse kernel, `state_events` likewise around the linear-state kernels
-    (the events must already exist, e.g. recorded once)."""
+    (the events must already exist, e.g. recorded once).  drop_tau (0 <= tau < 0.5, bf16
+    mask-product mode): per (b, h), drop the linear branch when max(1 - alpha) <= tau and the
+    sparse branch when max(alpha) <= tau, decided on the GPU."""
     _check_qkv(Q, K, V)
     Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
     B, H, N, d = Q.shape
@@ -205,7 +209,8 @@ def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", 
     need = lib().sla_forward_workspace_bytes(ctypes.byref(p), variant)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
     O = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device)
-    opts = ForwardOpts(mode, None, None, None, None)
+    opts = ForwardOpts(mode, None, None, None, None, 0 if drop_tau is None else 1,
+                       0.0 if drop_tau is None else float(drop_tau))
     if events is not None:
         opts.sparse_begin = ctypes.c_void_p(events[0].cuda_event)
         opts.sparse_end = ctypes.c_void_p(events[1].cuda_event)

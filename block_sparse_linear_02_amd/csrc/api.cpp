@@ -70,7 +70,7 @@ struct FwdWs {
   float *zb, *h_part, *z_part, *Z, *hj, *h_full;
   __bf16 *ht_hi, *ht_lo;
   __bf16 *hj_bf, *t_bf;
-  uint32_t* bits;
+  uint32_t *bits, *flags;
   uint8_t *q8, *k8, *v8;
   float *sq, *sk, *sv;
 };
@@ -97,6 +97,7 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
     f.hj_bf = c.take<__bf16>(BH * d.nb * dd);
     f.t_bf = c.take<__bf16>(BH * d.nb * dd);
     f.bits = c.take<uint32_t>(BH * d.nb * sla::mask_words(d.nb));
+    f.flags = c.take<uint32_t>(BH);
   }
   if (f8) {
     const size_t n = BH * d.N * d.d;
@@ -167,6 +168,9 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   if (mode != SLA_LINEAR_FUSED && mode != SLA_LINEAR_LITERAL && mode != SLA_LINEAR_MASK_PRODUCT)
     return SLA_ERR_INVALID;
   if (fp8 && mode == SLA_LINEAR_LITERAL) return SLA_ERR_INVALID;
+  const bool drop = opts && opts->branch_drop;
+  if (drop && !(opts->drop_tau >= 0.f && opts->drop_tau < 0.5f)) return SLA_ERR_INVALID;
+  if (drop && (fp8 || mode != SLA_LINEAR_MASK_PRODUCT)) return SLA_ERR_UNSUPPORTED;
   if (fp8 && (d.dtype != sla::kBF16 || d.d != 128)) return SLA_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !alpha || !O || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
   const int variant = fp8 ? (mode == SLA_LINEAR_MASK_PRODUCT ? 4 : 1)
@@ -178,17 +182,23 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   carve_forward(d, variant, ws, &w);
 
   hipError_t e = hipSuccess;
+  const uint32_t* flags = nullptr;
+  if (drop) {
+    e = sla::launch_branch_flags(d, alpha, opts->drop_tau, w.flags, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    flags = w.flags;
+  }
   if (opts && opts->states_begin) {
     e = hipEventRecord(opts->states_begin, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
-  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, w.hj_bf, stream);
+  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, w.hj_bf, stream, flags);
   if (e != hipSuccess) return hip_fail(e);
   e = sla::launch_state_reduce(d, w.h_part, w.z_part, w.ht_hi, w.ht_lo, w.Z, w.h_full, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (mode == SLA_LINEAR_MASK_PRODUCT) {
     e = sla::launch_mask_bits(d, idx, w.bits, stream);  // every block unselected when topk == 0
-    if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.bits, w.t_bf, stream);
+    if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.bits, w.t_bf, stream, flags);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (opts && opts->states_end) {
@@ -212,7 +222,7 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
   else if (mode == SLA_LINEAR_MASK_PRODUCT)
-    e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream);
+    e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream, flags);
   else
     e = sla::launch_sparse(d, Q, K, V, idx, alpha, w.ht_hi, w.ht_lo, w.Z, w.zb, O,
                            mode == SLA_LINEAR_FUSED ? 1 : 0, stream);

@@ -81,7 +81,7 @@ __device__ __forceinline__ int hs_off(int j, int c) {
 template <int D>
 __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
     const __bf16* __restrict__ hj, const uint32_t* __restrict__ bits, int nb, int nw,
-    int tiles_m, int tiles_n, __bf16* __restrict__ t_out) {
+    int tiles_m, int tiles_n, __bf16* __restrict__ t_out, const uint32_t* __restrict__ flags) {
   constexpr int DD = D * D;
   constexpr int STAGE = kGemmK * kGemmN;  // bf16 elements of one h stage
   __shared__ __attribute__((aligned(16))) __bf16 sb0[STAGE];
@@ -107,6 +107,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
   const int mt = item % tiles_m;
   const int nt = (item / tiles_m) % tiles_n;
   const int bh = item / (tiles_m * tiles_n);
+  if (flags && (flags[bh] & kDropLinear)) return;  // the head's linear branch is dropped
   const int n0 = nt * kGemmN;
   const int i0 = mt * kGemmM + 32 * kGemmCT * w;  // this wavefront's query blocks
 
@@ -261,16 +262,16 @@ hipError_t launch_mask_bits(const Dims& p, const int32_t* idx, uint32_t* bits,
 }
 
 hipError_t launch_tsel(const Dims& p, const __bf16* hj_bf, const uint32_t* bits, __bf16* t_bf,
-                       hipStream_t stream) {
+                       hipStream_t stream, const uint32_t* flags) {
   const int tiles_m = (p.nb + kGemmM - 1) / kGemmM;
   const int tiles_n = p.d * p.d / kGemmN;
   const int total = tiles_m * tiles_n * p.B * p.H;
   if (p.d == 128)
     tsel_kernel<128><<<total, kGemmThreads, 0, stream>>>(hj_bf, bits, p.nb, mask_words(p.nb),
-                                                         tiles_m, tiles_n, t_bf);
+                                                         tiles_m, tiles_n, t_bf, flags);
   else
     tsel_kernel<64><<<total, kGemmThreads, 0, stream>>>(hj_bf, bits, p.nb, mask_words(p.nb),
-                                                        tiles_m, tiles_n, t_bf);
+                                                        tiles_m, tiles_n, t_bf, flags);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ template <class T, int D, int MODE>
 __global__ __launch_bounds__(kStateThreads) void state_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int N, int nb, int cb,
     float* __restrict__ zb, float* __restrict__ h_part, float* __restrict__ z_part,
-    void* __restrict__ hj) {
+    void* __restrict__ hj, const uint32_t* __restrict__ flags) {
   constexpr bool LITERAL = MODE != 0;
   // MODE 2 computes h_j = relu(K_j)^T V_j (rows: K channels) so that a lane's four consecutive
   // accumulator rows are four consecutive entries of a row of h_j^T; the others V^T relu(K)
@@ -46,6 +46,7 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
   const int lane = tid % kWave, wave = tid / kWave;
   const int bh = blockIdx.y, chunk = blockIdx.x;
   const int nchunk = gridDim.x;
+  if (flags && (flags[bh] & kDropLinear)) return;  // the head's linear branch is dropped
   const int j0 = chunk * cb;
   const int j1 = min(nb, j0 + cb);
   const T* Kb = K + (size_t)bh * N * D;
@@ -266,18 +267,18 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
 template <class T, int D>
 hipError_t launch_states_t(const Dims& p, const void* K, const void* V, float* zb,
                            float* h_part, float* z_part, float* hj, __bf16* hj_bf,
-                           hipStream_t stream) {
+                           hipStream_t stream, const uint32_t* flags) {
   const int cb = state_chunk_blocks(p);
   dim3 grid((p.nb + cb - 1) / cb, p.B * p.H);
   if (hj)
     state_kernel<T, D, 1><<<grid, kStateThreads, 0, stream>>>(
-        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj);
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj, flags);
   else if (hj_bf)
     state_kernel<T, D, 2><<<grid, kStateThreads, 0, stream>>>(
-        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj_bf);
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj_bf, flags);
   else
     state_kernel<T, D, 0><<<grid, kStateThreads, 0, stream>>>(
-        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, nullptr);
+        (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, nullptr, flags);
   return hipGetLastError();
 }
 
@@ -295,14 +296,14 @@ int state_chunk_blocks(const Dims& p) {
 
 hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
                          float* z_part, float* hj, __bf16* hj_bf,
-                         hipStream_t stream) {
+                         hipStream_t stream, const uint32_t* flags) {
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream);
+    return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags);
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream);
+    return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream);
-  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream);
+    return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags);
+  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags);
 }
 
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,

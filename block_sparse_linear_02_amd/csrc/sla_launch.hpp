@@ -13,6 +13,11 @@ struct Dims {
   int B, H, N, d, nb, topk, dtype;
 };
 
+// Per-(batch, head) branch flags of alpha-driven branch dropping ([BH] uint32).
+enum : uint32_t { kDropLinear = 1u, kDropSparse = 2u };
+hipError_t launch_branch_flags(const Dims& p, const float* alpha, float tau, uint32_t* flags,
+                               hipStream_t stream);
+
 // Router: pool + project (split bf16 outputs [BH][nb][d]) then scores + HardTop-k.
 hipError_t launch_route(const Dims& p, const void* Q, const void* K, const float* Wq,
                         const float* Wk, __bf16* q_hi, __bf16* q_lo, __bf16* k_hi,
@@ -26,8 +31,10 @@ int route_max_blocks();
 // mode), or transposed, h_j^T [d][d] (V-channel major), rounded to bf16 (hj_bf, mask-product
 // mode) in slices of 64 entries: [BH][d*d/64][nb][64].
 int state_chunk_blocks(const Dims& p);
+// flags (optional): heads flagged kDropLinear are skipped.
 hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
-                         float* z_part, float* hj, __bf16* hj_bf, hipStream_t stream);
+                         float* z_part, float* hj, __bf16* hj_bf, hipStream_t stream,
+                         const uint32_t* flags = nullptr);
 
 // Mask-product mode: the complements of the router's index lists as bit rows
 // [BH][nb][mask_words(nb)], then T_i^T = sum_{j not in sel(i)} h_j^T for every query block in
@@ -36,13 +43,16 @@ int mask_words(int nb);
 hipError_t launch_mask_bits(const Dims& p, const int32_t* idx, uint32_t* bits,
                             hipStream_t stream);
 hipError_t launch_tsel(const Dims& p, const __bf16* hj_bf, const uint32_t* bits, __bf16* t_bf,
-                       hipStream_t stream);
+                       hipStream_t stream, const uint32_t* flags = nullptr);
 
 // Sparse branch with the linear part from the precomputed T_i (bf16) and zeta from z_j, two
 // query blocks per workgroup over the union of their kept blocks (n_b <= 2048).
+// flags (optional): a kDropLinear head writes alpha O_s only, a kDropSparse head
+// (1 - alpha) O_l only.
 hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
-                              const float* Z, const float* zb, float* O, hipStream_t stream);
+                              const float* Z, const float* zb, float* O, hipStream_t stream,
+                              const uint32_t* flags = nullptr);
 // Reduce the chunk partials (fixed order): H^T as bf16 hi/lo [d][d], Z [d]; optionally H [d][d]
 // in fp32 (K-channel major, literal mode); Z alone when h_part is null (mask-product mode).
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,

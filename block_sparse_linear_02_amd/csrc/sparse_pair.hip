@@ -83,7 +83,8 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
-    float* __restrict__ O, int N, int nb, int topk, float c_log2) {
+    float* __restrict__ O, int N, int nb, int topk, float c_log2,
+    const uint32_t* __restrict__ flags) {
   constexpr int NS = D / 16;  // MFMA k-steps over the head dim
   constexpr int NC = D / 32;  // 32-channel output tiles
   constexpr int TILE = TileLayout<D>::ELEMS;
@@ -141,7 +142,11 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     }
   }
   __syncthreads();
-  const int nu = ucount;
+  // branch dropping (workgroup-uniform): a dropped sparse branch walks no tiles, a dropped
+  // linear branch loads no state
+  const uint32_t fl = flags ? flags[bh] : 0u;
+  const bool lin = !(fl & kDropLinear);
+  const int nu = (fl & kDropSparse) ? 0 : ucount;
 
   // Tile staging: every thread moves its share of each tile.  bf16 tiles with d = 128 and all
   // 64 rows valid go HBM -> LDS directly (no registers), issued at the start of the iteration
@@ -367,9 +372,14 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     }
   }
 
+  // a dropped sparse branch staged no tiles, so the kept blocks' z_j are summed here
+  if ((fl & kDropSparse) && lin && z_lane && (zb_blk == 0 || has1)) {
+    const int32_t* il = idx + ((size_t)bh * nb + qb0 + zb_blk) * topk;
+    for (int t = 0; t < topk; ++t) zacc += zb[((size_t)bh * nb + il[t]) * D + tid % D];
+  }
   // ---- epilogue: T_i^T [c][c'] of block b into tile buffer b (both free since the last
   // step's barrier), in the tile row layout; zeta of each block ----
-  {
+  if (lin) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const __bf16* th = t_g + ((size_t)bh * nb + min(qb0 + b, nb - 1)) * D * D;
@@ -386,10 +396,10 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
       }
     }
     if (z_lane) zeta[zb_blk][tid % D] = Z[(size_t)bh * D + tid % D] - zacc;
+    wait_vmem();
+    __syncthreads();
+    launder();
   }
-  wait_vmem();
-  __syncthreads();
-  launder();
   const float ltot = xor32_sum(lsum);
   const float inv_l = ltot > 0.f ? 1.f / ltot : 0.f;
   // num^T[c][m] = sum_c' T_i^T[c][c'] relu(Q)[m][c']: the A operand (rows c, k = c') is a
@@ -399,16 +409,18 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
 #pragma unroll
   for (int c = 0; c < NC; ++c) num[c] = f32x16{};
   float den = 0.f;
+  if (lin) {
 #pragma unroll
-  for (int k = 0; k < NS; ++k) {
-    const bf16x8 pq = relu8(q[k]);
+    for (int k = 0; k < NS; ++k) {
+      const bf16x8 pq = relu8(q[k]);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) num[c] = mfma32(rd_row(tt, 32 * c, k), pq, num[c]);
+      for (int c = 0; c < NC; ++c) num[c] = mfma32(rd_row(tt, 32 * c, k), pq, num[c]);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[blk][16 * k + 8 * g + jj];
+      for (int jj = 0; jj < 8; ++jj) den += bf2f(pq[jj]) * zeta[blk][16 * k + 8 * g + jj];
+    }
+    den = xor32_sum(den);
   }
-  den = xor32_sum(den);
-  const float inv_den = (topk < nb && den != 0.f) ? 1.f / den : 0.f;
+  const float inv_den = (lin && topk < nb && den != 0.f) ? 1.f / den : 0.f;
   if (!row_ok) return;
   const float a = alpha[(size_t)bh * N + row];
   const float ws = a * inv_l, wl = (1.f - a) * inv_den;
@@ -427,12 +439,13 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
 template <class T, int D>
 hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const float* alpha, const __bf16* t_bf,
-                         const float* Z, const float* zb, float* O, hipStream_t stream) {
+                         const float* Z, const float* zb, float* O, hipStream_t stream,
+                         const uint32_t* flags) {
   const int total = p.B * p.H * ((p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   pair_kernel<T, D><<<total, kPairThreads, 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-      c_log2);
+      c_log2, flags);
   return hipGetLastError();
 }
 
@@ -440,15 +453,16 @@ hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void
 
 hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
-                              const float* Z, const float* zb, float* O, hipStream_t stream) {
+                              const float* Z, const float* zb, float* O, hipStream_t stream,
+                              const uint32_t* flags) {
   if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
+    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags);
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
+    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
-  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream);
+    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags);
+  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags);
 }
 
 }  // namespace sla

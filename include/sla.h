@@ -91,6 +91,17 @@ typedef struct {
   hipEvent_t sparse_end;   /* if non-null: recorded on `stream` right after it */
   hipEvent_t states_begin; /* if non-null: recorded right before the linear-state kernels */
   hipEvent_t states_end;   /* if non-null: recorded right after them (state build + reduction) */
+  /* Branch dropping ("SALAD: Achieve High-Sparsity Attention via Efficient Linear Attention
+   * Tuning for Video Diffusion Transformer", section 2, Post-Tuning Branch Dropping): when
+   * branch_drop is non-zero, a (b, h) whose linear weight max_t (1 - alpha_t) is <= drop_tau
+   * skips its linear branch (states, mask GEMM, apply) and one whose sparse weight max_t alpha_t
+   * is <= drop_tau skips its sparse branch; the dropped term is omitted, the other keeps its
+   * weight.  The decision is taken on the GPU from alpha (no host synchronisation).
+   * drop_tau = 0 drops only branches whose weight is exactly 0 everywhere (the output is then
+   * unchanged).  0 <= drop_tau < 0.5, else SLA_ERR_INVALID; only the bf16 forward in the
+   * mask-product linear mode supports it (else SLA_ERR_UNSUPPORTED). */
+  int32_t branch_drop;
+  float drop_tau;
 } sla_forward_opts;
 
 /* Workspace sizes in bytes for a problem (0 when the problem is invalid or unsupported). */

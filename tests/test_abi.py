@@ -127,6 +127,24 @@ def test_fp8_and_mode_checks(L):
     assert L.sla_quantize_e4m3(ctypes.byref(p), None, FAKE, FAKE, None) == sla.SLA_ERR_INVALID
 
 
+def test_branch_drop_checks(L):
+    p = P()
+    ws = 1 << 40
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    mp, fused = sla.LINEAR_MODES["mask_product"], sla.LINEAR_MODES["fused"]
+    for tau in (-0.01, 0.5, float("nan")):
+        o = sla.ForwardOpts(mp, None, None, None, None, 1, tau)
+        assert L.sla_forward_ex(ctypes.byref(p), *args, ctypes.byref(o)) == sla.SLA_ERR_INVALID
+    o = sla.ForwardOpts(fused, None, None, None, None, 1, 0.0)
+    assert L.sla_forward_ex(ctypes.byref(p), *args, ctypes.byref(o)) == sla.SLA_ERR_UNSUPPORTED
+    o = sla.ForwardOpts(mp, None, None, None, None, 1, 0.0)
+    assert L.sla_forward_fp8_ex(ctypes.byref(p), *args, ctypes.byref(o)) == sla.SLA_ERR_UNSUPPORTED
+    # accepted settings stop at the workspace check here (one byte), before anything is enqueued
+    small = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None)
+    o = sla.ForwardOpts(mp, None, None, None, None, 1, 0.25)
+    assert L.sla_forward_ex(ctypes.byref(p), *small, ctypes.byref(o)) == sla.SLA_ERR_WORKSPACE
+
+
 def test_status_strings(L):
     for st in (0, -1, -2, -3, -4):
         assert L.sla_status_string(st).decode()

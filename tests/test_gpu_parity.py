@@ -311,6 +311,65 @@ def test_fp8_forward_branches_isolated():
                 what="linear branch beside fp8 (alpha=0)")
 
 
+# ---------------------------------------------------------------------------------- branch dropping
+
+
+def drop_alpha(alpha, seed=5):
+    """alpha [B, H, N] with per-head patterns: head 0 all 1 (linear weight 0), head 1 all 0,
+    head 2 in [0.97, 1] with one token exactly at 1 - 1/32, head 3 in [0, 0.02], the rest as
+    drawn."""
+    a = alpha.clone()
+    g = torch.Generator().manual_seed(seed)
+    a[:, 0] = 1.0
+    a[:, 1] = 0.0
+    a[:, 2] = 0.97 + 0.03 * torch.rand(a[:, 2].shape, generator=g)
+    a[:, 2, 7] = 1.0 - 0.03125
+    a[:, 3] = 0.02 * torch.rand(a[:, 3].shape, generator=g)
+    return a
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.03125])
+def test_branch_drop(tau):
+    """Mask-product forward with branch dropping against the oracle's forward_dropped; with
+    tau = 0 the output equals the undropped run bit for bit."""
+    wl = small_ragged(H=5)
+    c = case("ragged_h5", wl)
+    r = oracle_route(c, wl.topk)
+    alpha = drop_alpha(c["alpha"])
+    ref, dl, ds = oracle.forward_dropped(c["Q"], c["K"], c["V"], r["idx"], alpha, tau, 64)
+    say(f"branch drop tau={tau}: linear {dl.tolist()}, sparse {ds.tolist()}")
+    a_dev = alpha.to("cuda:0")
+    got = run_forward(c, r["idx"], alpha=a_dev, linear_mode="mask_product", drop_tau=tau)
+    check_close(got, ref, what=f"branch drop tau={tau}")
+    if tau == 0.0:
+        plain = run_forward(c, r["idx"], alpha=a_dev, linear_mode="mask_product")
+        assert np.array_equal(got, plain), "tau = 0 must not change the output"
+
+
+def test_branch_drop_full_size():
+    c = case("video_s", gen.workload("video_s"))
+    g = dev(c)
+    r = oracle_route(c, 51)
+    alpha = drop_alpha(c["alpha"])
+    tau = 0.03125
+    idx = torch.from_numpy(r["idx"]).to(g["Q"].device)
+    say("branch drop video_s")
+    O = sla.forward(g["Q"], g["K"], g["V"], idx, alpha.to(g["Q"].device), linear_mode="mask_product",
+                    drop_tau=tau)
+    torch.cuda.synchronize()
+    got = O.cpu().double().numpy()
+    dl, ds = oracle.branch_drops(alpha, tau)
+    gots, refs = [], []
+    for h in (0, 1, 2, 3, 9):
+        _, os_, ol = oracle.forward_head(c["Q"][0, h], c["K"][0, h], c["V"][0, h], r["idx"][0, h],
+                                         alpha[0, h], 64, q_blocks=[0, 300, 511])
+        for i, a_s, a_l in zip([0, 300, 511], os_, ol):
+            a = alpha[0, h, i * 64 : i * 64 + len(a_s)].double().numpy()[:, None]
+            refs.append((0.0 if ds[0, h] else a * a_s) + (0.0 if dl[0, h] else (1 - a) * a_l))
+            gots.append(got[0, h, i * 64 : i * 64 + len(a_s)])
+    check_close(np.concatenate(gots), np.concatenate(refs), what="branch drop video_s")
+
+
 # ---------------------------------------------------------------------------------- full size
 
 
