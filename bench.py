@@ -46,6 +46,12 @@ def parse():
                     help="video_s | video_l | video_l_fp8 | pisa_video_s | pisa_video_l")
     ap.add_argument("--linear-mode", default="mask_product", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--drop-tau", type=float, default=None,
+                    help="branch dropping threshold (mask-product mode): a head drops its linear "
+                         "branch when max(1 - alpha) <= tau, its sparse branch when max(alpha) <= tau")
+    ap.add_argument("--drop-heads", default=None,
+                    help="L,S: give the first L heads alpha = 1 and the next S heads alpha = 0 "
+                         "(heads whose branches the dropping can remove)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -411,6 +417,10 @@ def main():
     if wl.fp8 and a.linear_mode == "literal":
         a.linear_mode = "fused"  # the fp8 path has the fused and mask-product linear modes
     inputs = gen.draw(wl, 0)
+    if a.drop_heads:
+        nl, ns = (int(x) for x in a.drop_heads.split(","))
+        inputs["alpha"][:, :nl] = 1.0
+        inputs["alpha"][:, nl : nl + ns] = 0.0
     Q, K, V, alpha = (inputs[k].to(dev) for k in ("Q", "K", "V", "alpha"))
     Wq, Wk = inputs["Wq"].to(dev), inputs["Wk"].to(dev)
     B, H, N, d = Q.shape
@@ -437,7 +447,7 @@ def main():
             ev_r[i][1].record()
         sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O,
                     events=ev[i] if i is not None else None,
-                    state_events=ev_s[i] if i is not None else None)
+                    state_events=ev_s[i] if i is not None else None, drop_tau=a.drop_tau)
         if i is not None:
             ev_t[i][1].record()
 
@@ -461,7 +471,8 @@ def main():
         scratch.fill_(i & 0xff)
         ev_c[i][0].record()
         sla.route(Q, K, Wq, Wk, wl.topk, workspace=ws_r, idx_out=idx)
-        sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O)
+        sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O,
+                    drop_tau=a.drop_tau)
         ev_c[i][1].record()
     torch.cuda.synchronize()
     cold_q = quantiles(ev_c)
@@ -516,7 +527,9 @@ def main():
         "data": "synthetic (seeded clustered video-DiT-shaped tensors, random projections)",
         "config": {
             "workload": f"{a.workload}: B={B} H={H} N={N} d={d} block=64 topk={wl.topk} of {nb} "
-                        f"({100 * (1 - wl.topk / nb):.1f}% block sparsity), linear={a.linear_mode}",
+                        f"({100 * (1 - wl.topk / nb):.1f}% block sparsity), linear={a.linear_mode}"
+                        + (f", alpha=1/0 on heads {a.drop_heads}" if a.drop_heads else "")
+                        + (f", branch drop tau={a.drop_tau}" if a.drop_tau is not None else ""),
             "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": wl.topk,
         },
         "sparse_tflop_per_call": flops / 1e12,

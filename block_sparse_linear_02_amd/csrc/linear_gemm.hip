@@ -101,12 +101,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
     for (int e = 0; e < 4; ++e) v[e] = ((tid >> e) & 1) ? f2bf(1.f) : f2bf(0.f);
     nib[tid] = v;
   }
-  // workgroup -> (query-block tile, state rows, head) with the query-block tiles fastest, so
-  // that the workgroups reading the same rows of h run next to each other on one XCD
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  // workgroup -> (head, query-block tile, state rows) with the query-block tiles fastest, so
+  // that the workgroups reading the same rows of h run next to each other on one XCD; every XCD
+  // takes the same eighth of every head (a head whose linear branch is dropped does no work)
+  int bh, item;
+  if (!xcd_chunk_map(blockIdx.x, tiles_m * tiles_n, &bh, &item)) return;
   const int mt = item % tiles_m;
-  const int nt = (item / tiles_m) % tiles_n;
-  const int bh = item / (tiles_m * tiles_n);
+  const int nt = item / tiles_m;
   if (flags && (flags[bh] & kDropLinear)) return;  // the head's linear branch is dropped
   const int n0 = nt * kGemmN;
   const int i0 = mt * kGemmM + 32 * kGemmCT * w;  // this wavefront's query blocks
@@ -265,7 +266,7 @@ hipError_t launch_tsel(const Dims& p, const __bf16* hj_bf, const uint32_t* bits,
                        hipStream_t stream, const uint32_t* flags) {
   const int tiles_m = (p.nb + kGemmM - 1) / kGemmM;
   const int tiles_n = p.d * p.d / kGemmN;
-  const int total = tiles_m * tiles_n * p.B * p.H;
+  const int total = xcd_chunk_grid(p.B * p.H, tiles_m * tiles_n);
   if (p.d == 128)
     tsel_kernel<128><<<total, kGemmThreads, 0, stream>>>(hj_bf, bits, p.nb, mask_words(p.nb),
                                                          tiles_m, tiles_n, t_bf, flags);

@@ -193,10 +193,30 @@ __device__ __forceinline__ i16x4 lds_tr_at(const __bf16* base, int byte_off) {
 // Map a workgroup id to a logical work item so that each of the 8 XCDs (which receive
 // workgroups round-robin) processes one contiguous range of items: neighbouring query blocks
 // of a head share their XCD's L2.  A bijection on [0, total).
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
+__host__ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   const int q = total / 8, r = total % 8;
   const int xcd = wg % 8, k = wg / 8;
   return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+// Workgroup -> (head, item within the head) for work grouped by head, when heads may carry
+// unequal work (a dropped branch): each XCD takes the same eighth of every head, chunk x of a
+// head being its items x * per_head / 8 ..  (sizes differ by at most one), so no XCD idles while
+// others finish; consecutive workgroups of an XCD walk consecutive items of one head (they share
+// L2).  The grid has 8 * heads * ceil(per_head / 8) workgroups (xcd_chunk_grid): XCD x (the
+// workgroups wg % 8 == x) runs k = wg / 8 -> head k / ceil(per_head / 8), item chunk_start(x) +
+// k % ceil(per_head / 8); the few workgroups past a short chunk get false and exit at once.
+__host__ __device__ __forceinline__ int xcd_chunk_grid(int heads, int per_head) {
+  return 8 * heads * ((per_head + 7) / 8);
+}
+__host__ __device__ __forceinline__ bool xcd_chunk_map(int wg, int per_head, int* head, int* item) {
+  const int q = per_head / 8, r = per_head % 8;
+  const int smax = q + (r > 0 ? 1 : 0);
+  const int x = wg % 8, k = wg / 8;
+  const int off = k % smax;
+  *head = k / smax;
+  *item = x * q + (x < r ? x : r) + off;
+  return off < q + (x < r ? 1 : 0);
 }
 
 }  // namespace sla

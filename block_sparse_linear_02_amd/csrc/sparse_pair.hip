@@ -104,9 +104,11 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   const int tid = threadIdx.x;
   const int lane = tid % kWave, g = lane / 32;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wavefront-uniform (scalar branches)
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  // every XCD takes the same eighth of every head's pairs (heads may differ in work when a
+  // branch is dropped); the grid's padding workgroups exit here, before any barrier
   const int npair = (nb + 1) / 2;
-  const int bh = item / npair, pr = item % npair;
+  int bh, pr;
+  if (!xcd_chunk_map(blockIdx.x, npair, &bh, &pr)) return;
   const int qb0 = 2 * pr;
   const bool has1 = qb0 + 1 < nb;  // an odd n_b leaves the last workgroup one block
   const int blk = wave / 2;        // this wavefront's query block: qb0 + blk
@@ -441,7 +443,7 @@ hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void
                          const int32_t* idx, const float* alpha, const __bf16* t_bf,
                          const float* Z, const float* zb, float* O, hipStream_t stream,
                          const uint32_t* flags) {
-  const int total = p.B * p.H * ((p.nb + 1) / 2);
+  const int total = xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   pair_kernel<T, D><<<total, kPairThreads, 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
