@@ -50,3 +50,10 @@ from .pisa import (  # noqa: F401
     pisa_forward_head,
     pisa_forward,
 )
+from .int8 import (  # noqa: F401
+    INT8_MAX,
+    int8_encode,
+    quantize_blocks_int8,
+    forward_int8_head,
+    forward_int8,
+)

@@ -386,6 +386,76 @@ def pin_fp8_error_scale(orc):
 
 
 # ----------------------------------------------------------------------------------------------
+# int8 sparse branch
+
+
+def pin_int8_encode_matches_torch_round(orc):
+    """Codes of a grid with every half-way point: torch.round (ties to even) clamped to +-127."""
+    y = np.arange(-140.0, 140.0, 0.25)
+    ref = torch.clamp(torch.round(torch.from_numpy(y)), -127, 127).numpy().astype(np.int8)
+    assert np.array_equal(orc.int8_encode(y), ref)
+    assert orc.int8_encode(np.array([0.5, 1.5, 2.5, -0.5, -2.5])).tolist() == [0, 2, 2, 0, -2]
+
+
+def pin_int8_quantize_blocks(orc):
+    """Per-block absmax: the largest magnitude maps to +-127, every value is reconstructed within
+    half a step (s / 2), s = fp32(a / 127); an all-zero block keeps s = 1 and codes 0; the short
+    last block's scale comes from its valid rows only."""
+    X = _rand((150, 16), 101)
+    X[64:128] = 0.0
+    X[140, 3] = 9.0  # the last block (rows 128..149) has its own maximum
+    codes, scales, deq = orc.quantize_blocks_int8(X, 64)
+    assert scales[1] == 1.0 and np.all(codes[64:128] == 0)
+    for t, (a, b) in enumerate(((0, 64), (128, 150))):
+        blk = X[a:b]
+        amax = np.float32(np.abs(blk).max())
+        s = scales[0 if t == 0 else 2]
+        assert s == np.float32(amax / np.float32(127.0))
+        assert np.abs(codes[a:b]).max() == 127
+        assert np.all(np.abs(deq[a:b] - blk) <= 0.5 * float(s) * (1 + 1e-6))
+    assert codes[140, 3] == 127
+
+
+def pin_int8_forward_error_bound(orc):
+    """Q, K, V whose block values are exact multiples of 2^-4 within +-127 steps quantise without
+    error, so the only error left is P's rounding: |O_int8 - O| <= sum_j (sP_j / 2) sum_n |v_n|
+    / sum P^ per row (each P code is off by at most half a step), and the bound is met while
+    the error is not zero."""
+    N, d, blk, k = 128, 16, 64, 2
+    rng = np.random.default_rng(102)
+    Q, K, V = (rng.integers(-127, 128, (N, d)).astype(np.float64) / 16.0 for _ in range(3))
+    for X in (Q, K, V):
+        for t in range(0, N, blk):
+            X[t, 0] = 127.0 / 16.0  # each block's absmax is exactly 127 steps
+    idx = np.array([[0, 1], [0, 1]], dtype=np.int32)
+    alpha = np.ones(N)
+    O8, Os8, _ = orc.forward_int8_head(Q, K, V, idx, alpha, blk)
+    _, Os, _ = orc.forward_head(Q, K, V, idx, alpha, blk)
+    for i in range(2):
+        q = Q[i * blk : (i + 1) * blk]
+        S = [(q @ K[j * blk : (j + 1) * blk].T) / 4.0 for j in range(2)]
+        m = np.maximum(S[0].max(axis=1), S[1].max(axis=1))[:, None]
+        P = [np.exp(s - m) for s in S]
+        den = (P[0].sum(axis=1) + P[1].sum(axis=1))[:, None]
+        bound = sum((p.max() / 127.0 / 2.0) * np.abs(V[j * blk : (j + 1) * blk]).sum(axis=0)[None, :] for j, p in enumerate(P)) / den
+        err = np.abs(Os8[i] - Os[i])
+        assert np.all(err <= bound * (1 + 1e-9) + 1e-12), (err - bound).max()
+        assert err.max() > 0
+        np.testing.assert_allclose(O8[i], Os8[i], rtol=0, atol=1e-15)
+
+
+def pin_int8_error_scale(orc):
+    """On random data the int8 sparse branch stays within a few percent of the exact one, and the
+    linear branch is untouched."""
+    Q, K, V, alpha, idx, blk = _small_case(103, N=256, d=32, blk=64, k=2)
+    _, Os, Ol = orc.forward(Q, K, V, idx, alpha, blk)
+    _, Os8, Ol8 = orc.forward_int8(Q, K, V, idx, alpha, blk)
+    np.testing.assert_array_equal(Ol8, Ol)
+    rel = np.linalg.norm(Os8 - Os) / np.linalg.norm(Os)
+    assert 1e-3 < rel < 0.05, rel
+
+
+# ----------------------------------------------------------------------------------------------
 # branch dropping
 
 

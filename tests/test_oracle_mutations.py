@@ -32,6 +32,11 @@ MUTATIONS = {
     "fp8_scale_dropped": ("fp8.py", "deq[a:b] = e4m3_decode(codes[a:b]) * np.float64(scales[t])", "deq[a:b] = e4m3_decode(codes[a:b])"),
     "fp8_truncating_round": ("fp8.py", "m8 = np.rint((mant * 2.0 - 1.0) * 8.0)", "m8 = np.floor((mant * 2.0 - 1.0) * 8.0)"),
     "fp8_bias_off_by_one": ("fp8.py", "_E4M3_BIAS = 7", "_E4M3_BIAS = 8"),
+    "int8_truncating_round": ("int8.py", "return np.clip(np.rint(y), -INT8_MAX, INT8_MAX).astype(np.int8)", "return np.clip(np.trunc(y), -INT8_MAX, INT8_MAX).astype(np.int8)"),
+    "int8_clamp_128": ("int8.py", "return np.clip(np.rint(y), -INT8_MAX, INT8_MAX).astype(np.int8)", "return np.clip(np.rint(y), -128, 127).astype(np.int8)"),
+    "int8_scale_over_128": ("int8.py", "scales[t] = np.float32(amax / np.float32(INT8_MAX))", "scales[t] = np.float32(amax / np.float32(128.0))"),
+    "int8_p_scale_dropped": ("int8.py", "num += (p8 @ v8[starts[j]:ends[j]]).astype(np.float64) * (sP * float(sv[j]))", "num += (p8 @ v8[starts[j]:ends[j]]).astype(np.float64) * float(sv[j])"),
+    "int8_k_scale_of_query_block": ("int8.py", "(float(sq[i]) * float(sk[j]) * scale)", "(float(sq[i]) * float(sk[i]) * scale)"),
     "drop_strict_threshold": ("sla.py", "return (1.0 - a).max(axis=-1) <= t, a.max(axis=-1) <= t", "return (1.0 - a).max(axis=-1) < t, a.max(axis=-1) <= t"),
     "drop_by_mean_weight": ("sla.py", "return (1.0 - a).max(axis=-1) <= t, a.max(axis=-1) <= t", "return (1.0 - a).mean(axis=-1) <= t, a.max(axis=-1) <= t"),
     "drop_sparse_by_min": ("sla.py", "return (1.0 - a).max(axis=-1) <= t, a.max(axis=-1) <= t", "return (1.0 - a).max(axis=-1) <= t, a.min(axis=-1) <= t"),
