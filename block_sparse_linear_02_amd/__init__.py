@@ -8,6 +8,7 @@ a GPU every call raises.
     idx, mask, scores = route(Q, K, proj_q, proj_k, topk, want_mask=False, want_scores=False)
     O = forward(Q, K, V, idx, alpha)                     # bf16 (or fp32-input) sparse branch
     O = forward(Q, K, V, idx, alpha, fp8=True)           # e4m3 sparse branch
+    O = forward(Q, K, V, idx, alpha, int8=True, linear_mode="mask_product")  # int8 sparse branch
     O = forward(Q, K, V, idx, alpha, linear_mode="literal")
 
 PISA exact-or-approximate attention (C ABI in include/sla_pisa.h):
@@ -34,6 +35,7 @@ __all__ = [
     "route",
     "forward",
     "quantize_e4m3",
+    "quantize_int8",
     "route_workspace_bytes",
     "forward_workspace_bytes",
     "PisaStats",
@@ -104,11 +106,15 @@ def lib() -> ctypes.CDLL:
         for name in ("sla_forward", "sla_forward_fp8"):
             getattr(L, name).argtypes = fwd
             getattr(L, name).restype = i32
-        for name in ("sla_forward_ex", "sla_forward_fp8_ex"):
+        for name in ("sla_forward_int8",):
+            getattr(L, name).argtypes = fwd
+            getattr(L, name).restype = i32
+        for name in ("sla_forward_ex", "sla_forward_fp8_ex", "sla_forward_int8_ex"):
             getattr(L, name).argtypes = fwd + [ctypes.POINTER(ForwardOpts)]
             getattr(L, name).restype = i32
-        L.sla_quantize_e4m3.argtypes = [P, vp, vp, vp, vp]
-        L.sla_quantize_e4m3.restype = i32
+        for name in ("sla_quantize_e4m3", "sla_quantize_int8"):
+            getattr(L, name).argtypes = [P, vp, vp, vp, vp]
+            getattr(L, name).restype = i32
         L.sla_pisa_stats_bytes.argtypes = [P]
         L.sla_pisa_stats_bytes.restype = sz
         L.sla_pisa_workspace_bytes.argtypes = [P]
@@ -191,7 +197,7 @@ def route(Q, K, proj_q, proj_k, topk: int, want_mask: bool = False, want_scores:
 
 
 def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", workspace=None,
-            out=None, events=None, state_events=None, drop_tau=None):
+            out=None, events=None, state_events=None, drop_tau=None, int8: bool = False):
     """O = alpha * O_s + (1 - alpha) * O_l.  `events` = (begin, end) torch.cuda.Event pair
     recorded around the sparse kernel, `state_events` likewise around the linear-state kernels
     (the events must already exist, e.g. recorded once).  drop_tau (0 <= tau < 0.5, bf16
@@ -205,7 +211,9 @@ def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", 
     alpha = alpha.contiguous().to(torch.float32)
     p = _problem(Q, topk)
     mode = LINEAR_MODES[linear_mode]
-    variant = (4 if mode == 2 else 1) if fp8 else {0: 0, 1: 2, 2: 3}[mode]
+    if fp8 and int8:
+        raise ValueError("fp8 and int8 exclude each other")
+    variant = 5 if int8 else ((4 if mode == 2 else 1) if fp8 else {0: 0, 1: 2, 2: 3}[mode])
     need = lib().sla_forward_workspace_bytes(ctypes.byref(p), variant)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
     O = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device)
@@ -217,12 +225,27 @@ def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", 
     if state_events is not None:
         opts.states_begin = ctypes.c_void_p(state_events[0].cuda_event)
         opts.states_end = ctypes.c_void_p(state_events[1].cuda_event)
-    fn = lib().sla_forward_fp8_ex if fp8 else lib().sla_forward_ex
+    fn = lib().sla_forward_int8_ex if int8 else (lib().sla_forward_fp8_ex if fp8 else lib().sla_forward_ex)
     st = fn(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(alpha), _ptr(O), _ptr(ws),
             ws.numel(), _stream(), ctypes.byref(opts))
     if st != SLA_OK:
-        raise SLAError(st, "sla_forward_fp8" if fp8 else "sla_forward")
+        raise SLAError(st, "sla_forward_int8" if int8 else ("sla_forward_fp8" if fp8 else "sla_forward"))
     return O
+
+
+def quantize_int8(X):
+    """Per-(b, h, 64-token block) absmax int8 codes of X (bf16, d = 128) and their scales."""
+    _check_qkv(X)
+    X = X.contiguous()
+    B, H, N, d = X.shape
+    nb = -(-N // BLOCK)
+    codes = torch.empty((B, H, N, d), dtype=torch.int8, device=X.device)
+    scales = torch.empty((B, H, nb), dtype=torch.float32, device=X.device)
+    p = _problem(X, 0)
+    st = lib().sla_quantize_int8(ctypes.byref(p), _ptr(X), _ptr(codes), _ptr(scales), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_quantize_int8")
+    return codes, scales
 
 
 def quantize_e4m3(X):

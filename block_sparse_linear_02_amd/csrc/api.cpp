@@ -74,14 +74,16 @@ struct FwdWs {
   uint8_t *q8, *k8, *v8;
   float *sq, *sk, *sv;
 };
-// variant: 0 fused, 1 fp8 (fused), 2 literal, 3 mask product, 4 fp8 (mask product)
+// variant: 0 fused, 1 fp8 (fused), 2 literal, 3 mask product, 4 fp8 (mask product),
+// 5 int8 (mask product)
 size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
   Carve c(ws);
   const size_t BH = (size_t)d.B * d.H;
   const size_t dd = (size_t)d.d * d.d;
   const int cb = sla::state_chunk_blocks(d);
   const size_t nchunk = (d.nb + cb - 1) / cb;
-  const bool mp = variant == 3 || variant == 4, f8 = variant == 1 || variant == 4;
+  const bool mp = variant == 3 || variant == 4 || variant == 5;
+  const bool f8 = variant == 1 || variant == 4 || variant == 5;  // low-bit codes and scales
   FwdWs f = {};
   f.zb = c.take<float>(BH * d.nb * d.d);
   if (!mp) f.h_part = c.take<float>(BH * nchunk * dd);
@@ -158,23 +160,27 @@ inline int hip_fail(hipError_t e) {
   return SLA_ERR_HIP;
 }
 
+// lowbit: 0 none, 1 e4m3, 2 int8 (int8 exists in the mask-product mode only, its default)
 int forward_impl(const sla_problem* p, const void* Q, const void* K, const void* V,
                  const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
-                 hipStream_t stream, const sla_forward_opts* opts, bool fp8) {
+                 hipStream_t stream, const sla_forward_opts* opts, int lowbit) {
   sla::Dims d;
   int st = check_problem(p, &d);
   if (st != SLA_OK) return st;
-  const int mode = opts ? opts->linear_mode : SLA_LINEAR_FUSED;
+  const bool fp8 = lowbit != 0, int8 = lowbit == 2;
+  const int mode = opts ? opts->linear_mode : (int8 ? SLA_LINEAR_MASK_PRODUCT : SLA_LINEAR_FUSED);
   if (mode != SLA_LINEAR_FUSED && mode != SLA_LINEAR_LITERAL && mode != SLA_LINEAR_MASK_PRODUCT)
     return SLA_ERR_INVALID;
   if (fp8 && mode == SLA_LINEAR_LITERAL) return SLA_ERR_INVALID;
+  if (int8 && mode != SLA_LINEAR_MASK_PRODUCT) return SLA_ERR_UNSUPPORTED;
   const bool drop = opts && opts->branch_drop;
   if (drop && !(opts->drop_tau >= 0.f && opts->drop_tau < 0.5f)) return SLA_ERR_INVALID;
   if (drop && (fp8 || mode != SLA_LINEAR_MASK_PRODUCT)) return SLA_ERR_UNSUPPORTED;
   if (fp8 && (d.dtype != sla::kBF16 || d.d != 128)) return SLA_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !alpha || !O || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
-  const int variant = fp8 ? (mode == SLA_LINEAR_MASK_PRODUCT ? 4 : 1)
-                          : (mode == SLA_LINEAR_LITERAL ? 2 : (mode == SLA_LINEAR_MASK_PRODUCT ? 3 : 0));
+  const int variant = int8  ? 5
+                      : fp8 ? (mode == SLA_LINEAR_MASK_PRODUCT ? 4 : 1)
+                            : (mode == SLA_LINEAR_LITERAL ? 2 : (mode == SLA_LINEAR_MASK_PRODUCT ? 3 : 0));
   const size_t need = carve_forward(d, variant, nullptr, nullptr);
   if (!ws) return SLA_ERR_INVALID;
   if (ws_bytes < need) return SLA_ERR_WORKSPACE;
@@ -206,9 +212,9 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     if (e != hipSuccess) return hip_fail(e);
   }
   if (fp8) {
-    e = sla::launch_quantize(d, Q, w.q8, w.sq, stream);
-    if (e == hipSuccess) e = sla::launch_quantize(d, K, w.k8, w.sk, stream);
-    if (e == hipSuccess) e = sla::launch_quantize_v8t(d, V, w.v8, w.sv, stream);
+    e = sla::launch_quantize(d, Q, w.q8, w.sq, stream, int8);
+    if (e == hipSuccess) e = sla::launch_quantize(d, K, w.k8, w.sk, stream, int8);
+    if (e == hipSuccess) e = sla::launch_quantize_v8t(d, V, w.v8, w.sv, stream, int8);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (opts && opts->sparse_begin) {
@@ -217,7 +223,7 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   }
   if (fp8 && mode == SLA_LINEAR_MASK_PRODUCT)
     e = sla::launch_sparse_pair8(d, Q, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha, w.t_bf,
-                                 w.Z, w.zb, O, stream);
+                                 w.Z, w.zb, O, stream, int8);
   else if (fp8)
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
@@ -250,7 +256,7 @@ size_t sla_route_workspace_bytes(const sla_problem* p) {
 
 size_t sla_forward_workspace_bytes(const sla_problem* p, int variant) {
   sla::Dims d;
-  if (check_problem(p, &d) != SLA_OK || variant < 0 || variant > 4) return 0;
+  if (check_problem(p, &d) != SLA_OK || variant < 0 || variant > 5) return 0;
   return carve_forward(d, variant, nullptr, nullptr);
 }
 
@@ -273,37 +279,59 @@ int sla_route(const sla_problem* p, const void* Q, const void* K, const float* p
 int sla_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
                 const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                 hipStream_t stream) {
-  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, nullptr, false);
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, nullptr, 0);
 }
 
 int sla_forward_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
                    const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                    hipStream_t stream, const sla_forward_opts* opts) {
-  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, opts, false);
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, opts, 0);
 }
 
 int sla_forward_fp8(const sla_problem* p, const void* Q, const void* K, const void* V,
                     const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                     hipStream_t stream) {
-  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, nullptr, true);
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, nullptr, 1);
 }
 
 int sla_forward_fp8_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const float* alpha, float* O, void* ws,
                        size_t ws_bytes, hipStream_t stream, const sla_forward_opts* opts) {
-  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, opts, true);
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, opts, 1);
 }
 
-int sla_quantize_e4m3(const sla_problem* p, const void* X, uint8_t* codes, float* scales,
-                      hipStream_t stream) {
+int sla_forward_int8(const sla_problem* p, const void* Q, const void* K, const void* V,
+                     const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, nullptr, 2);
+}
+
+int sla_forward_int8_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
+                        const int32_t* idx, const float* alpha, float* O, void* ws,
+                        size_t ws_bytes, hipStream_t stream, const sla_forward_opts* opts) {
+  return forward_impl(p, Q, K, V, idx, alpha, O, ws, ws_bytes, stream, opts, 2);
+}
+
+int quantize_impl(const sla_problem* p, const void* X, uint8_t* codes, float* scales,
+                  hipStream_t stream, int int8) {
   sla::Dims d;
   int st = check_problem(p, &d);
   if (st != SLA_OK) return st;
   if (d.dtype != sla::kBF16 || d.d != 128) return SLA_ERR_UNSUPPORTED;
   if (!X || !codes || !scales) return SLA_ERR_INVALID;
-  hipError_t e = sla::launch_quantize(d, X, codes, scales, stream);
+  hipError_t e = sla::launch_quantize(d, X, codes, scales, stream, int8);
   if (e != hipSuccess) return hip_fail(e);
   return SLA_OK;
+}
+
+int sla_quantize_e4m3(const sla_problem* p, const void* X, uint8_t* codes, float* scales,
+                      hipStream_t stream) {
+  return quantize_impl(p, X, codes, scales, stream, 0);
+}
+
+int sla_quantize_int8(const sla_problem* p, const void* X, int8_t* codes, float* scales,
+                      hipStream_t stream) {
+  return quantize_impl(p, X, reinterpret_cast<uint8_t*>(codes), scales, stream, 1);
 }
 
 size_t sla_pisa_stats_bytes(const sla_problem* p) {

@@ -21,6 +21,14 @@
 //                     S, form P = exp(S - max), exchange the 64x64 tile maximum, quantise P and
 //                     accumulate (P8 V8) sP sV by fp8 MFMA.  Epilogue and combine as in the
 //                     bf16 kernel.
+//
+// INT8 (the other low-bit format the SLA2 summaries name for the sparse branch): the quantiser
+// and the two-query-block kernel are templated on the code format.  int8 codes are symmetric
+// (+-127, ties to even) with scale a / 127 per block, P's tile scale is max(tile) / 127, and the
+// products run on v_mfma_i32_32x32x32_i8 (each 32-byte fp8 operand chunk is two 16-byte int8
+// operands; int32 accumulation is exact: |S| <= 128 * 127^2, |PV| <= 64 * 127^2 < 2^24, so the
+// conversion to fp32 is exact too).  P's codes come from one fma with 1.5 * 2^23, which leaves
+// round-half-even(P / sP) in the low byte of the float.
 #include <type_traits>
 
 #include "sla_device.hpp"
@@ -32,10 +40,40 @@ namespace sla {
 namespace {
 
 constexpr float kE4M3Max = 448.f;
+constexpr float kInt8Max = 127.f;
+enum { kFmtE4M3 = 0, kFmtInt8 = 1 };
+template <int FMT>
+constexpr float fmt_max() { return FMT == kFmtInt8 ? kInt8Max : kE4M3Max; }
 
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   // formats 0/0 = e4m3 for both operands; scale exponents 127 = 2^0
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+// 64-deep int8 product of two 32-byte operand chunks: two v_mfma_i32_32x32x32_i8 over the
+// halves (A and B use the same byte order, so the k-slot assignment inside the halves is free)
+__device__ __forceinline__ i32x16 mfma_i8x64(i32x8 a, i32x8 b, i32x16 c) {
+  c = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[0], a[1], a[2], a[3]}, i32x4{b[0], b[1], b[2], b[3]}, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{a[4], a[5], a[6], a[7]}, i32x4{b[4], b[5], b[6], b[7]}, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 i2f16(i32x16 v) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = (float)v[i];
+  return r;
+}
+// int8 codes of p * qs for 4 non-negative p with p * qs below 127.5: fma(p, qs, 1.5 * 2^23)
+// rounds the exact product once to an integer (ties to even) held in the float's low byte
+__device__ __forceinline__ u32 cvt4_u7(float a, float b, float c, float d, float qs) {
+  constexpr float kMagic = 12582912.f;
+  const u32 x = __float_as_uint(fmaf(a, qs, kMagic)), y = __float_as_uint(fmaf(b, qs, kMagic));
+  const u32 z = __float_as_uint(fmaf(c, qs, kMagic)), w = __float_as_uint(fmaf(d, qs, kMagic));
+  return (x & 0xffu) | ((y & 0xffu) << 8) | ((z & 0xffu) << 16) | (w << 24);
+}
+// int8 codes of 4 floats (round to nearest even, saturating at +-127)
+__device__ __forceinline__ u32 cvt4_i8(float a, float b, float c, float d) {
+  auto q = [](float v) { return (u32)(uint8_t)(int8_t)(int)rintf(fminf(fmaxf(v, -kInt8Max), kInt8Max)); };
+  return q(a) | (q(b) << 8) | (q(c) << 16) | (q(d) << 24);
 }
 
 // e4m3 codes of 4 floats (round to nearest even; the caller keeps |x| <= 448)
@@ -53,7 +91,7 @@ __device__ __forceinline__ int v8_pos(int n) {
   return 32 * g + 16 * kt + 4 * q + e;
 }
 
-template <int D, bool TRANSPOSED>
+template <int D, bool TRANSPOSED, int FMT>
 __global__ __launch_bounds__(256) void quantize_kernel(const __bf16* __restrict__ X, int N,
                                                        int nb, uint8_t* __restrict__ codes,
                                                        float* __restrict__ scales) {
@@ -79,25 +117,32 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16* __restrict_
   if (lane == 0) wmax[w] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float inv = amax > 0.f ? kE4M3Max / amax : 0.f;
-  if (tid == 0) scales[(size_t)bh * nb + t] = amax > 0.f ? amax / kE4M3Max : 1.f;
+  constexpr float QMAX = fmt_max<FMT>();
+  const float inv = amax > 0.f ? QMAX / amax : 0.f;
+  if (tid == 0) scales[(size_t)bh * nb + t] = amax > 0.f ? amax / QMAX : 1.f;
+  auto cvt4 = [](float a, float b, float c, float d) -> u32 {
+    if constexpr (FMT == kFmtInt8)
+      return cvt4_i8(a, b, c, d);
+    else
+      return cvt4_e4m3(sat(a), sat(b), sat(c), sat(d));
+  };
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int q = tid + u * 256, r = q / CPR, ch = q % CPR;
     if (!TRANSPOSED && r >= cnt) continue;  // past N: no such row in the output
     float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = sat(bf2f(v[u][e]) * inv);
+    for (int e = 0; e < 8; ++e) y[e] = bf2f(v[u][e]) * inv;
     if constexpr (!TRANSPOSED) {
-      const u32 lo = cvt4_e4m3(y[0], y[1], y[2], y[3]);
-      const u32 hi = cvt4_e4m3(y[4], y[5], y[6], y[7]);
+      const u32 lo = cvt4(y[0], y[1], y[2], y[3]);
+      const u32 hi = cvt4(y[4], y[5], y[6], y[7]);
       uint8_t* dst = codes + ((size_t)bh * N + row0 + r) * D + ch * 8;
       *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
     } else {
       // [c][pos(r)] staged in LDS (keys past N get code 0: their P8 is 0 as well), written out
       // below with 16-byte stores
-      const u32 lo = cvt4_e4m3(y[0], y[1], y[2], y[3]);
-      const u32 hi = cvt4_e4m3(y[4], y[5], y[6], y[7]);
+      const u32 lo = cvt4(y[0], y[1], y[2], y[3]);
+      const u32 hi = cvt4(y[4], y[5], y[6], y[7]);
       const int pos = v8_pos(r);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -492,7 +537,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
 //   the partner wavefront's in LDS at the step's barrier, so tile t's P is quantised (scale
 //   max / 448) and (P8 V8) sP sV accumulated by fp8 MFMA in step t + 1: one barrier per tile.
 //   The denominator sums the unquantised P.
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     const __bf16* __restrict__ Q, const uint8_t* __restrict__ q8,
     const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
@@ -504,6 +549,28 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   constexpr int NS = D / 16, NC = D / 32, N8 = D / 64;
   constexpr int K8B = kBlock * D;  // bytes of a K8 (or V8^T) tile
   constexpr int kMaxWords = 64;    // union bitmap words: n_b <= 2048
+  constexpr float QMAX = fmt_max<FMT>();
+  // products over the head dim: N8 steps of 64-deep products of 32-byte operand chunks, in fp32
+  auto dot64 = [](const i32x8* a, const i32x8* b) -> f32x16 {
+    if constexpr (FMT == kFmtInt8) {
+      i32x16 acc = i32x16{};
+#pragma unroll
+      for (int st = 0; st < N8; ++st) acc = mfma_i8x64(a[st], b[st], acc);
+      return i2f16(acc);
+    } else {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int st = 0; st < N8; ++st) acc = mfma_f8(a[st], b[st], acc);
+      return acc;
+    }
+  };
+  // one 64-deep product (the PV step: 64 keys)
+  auto dot1 = [](i32x8 a, i32x8 b) -> f32x16 {
+    if constexpr (FMT == kFmtInt8)
+      return i2f16(mfma_i8x64(a, b, i32x16{}));
+    else
+      return mfma_f8(a, b, f32x16{});
+  };
   // K8 and V8^T tiles double-buffered, one LDS array each so that the compiler can tell the
   // buffers being filled by direct-to-LDS loads from the ones being read
   __shared__ __attribute__((aligned(16))) uint8_t kb0[K8B];
@@ -620,9 +687,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
       const int lim = nv - 4 * g;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x16 s = f32x16{};
-#pragma unroll
-        for (int st = 0; st < N8; ++st) s = mfma_f8(kr[BUF][kt][st], qf[st], s);
+        const f32x16 s = dot64(kr[BUF][kt], qf);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[i] * sc);
@@ -675,7 +740,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   auto pv_prev = [&](auto VBC, auto PBC) {
     constexpr int PB = decltype(PBC)::value;
     const float tmax = fmaxf(tmx[PB][blk][0], tmx[PB][blk][1]);
-    const float qs = tmax > 0.f ? kE4M3Max / tmax : 0.f;  // an all-underflow tile adds 0
+    const float qs = tmax > 0.f ? QMAX / tmax : 0.f;  // an all-underflow tile adds 0
     const uint8_t* vs = vbuf(VBC);
     i32x8 va[NC];
 #pragma unroll
@@ -689,13 +754,18 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        pf[4 * kt + qd] = (int)cvt4_e4m3(sat(pp[kt][4 * qd] * qs), sat(pp[kt][4 * qd + 1] * qs),
-                                         sat(pp[kt][4 * qd + 2] * qs), sat(pp[kt][4 * qd + 3] * qs));
-    const float pv_scale = (tmax / kE4M3Max) * sv[(size_t)bh * nb + j_prev];
+      for (int qd = 0; qd < 4; ++qd) {
+        const float* pq4 = &pp[kt][4 * qd];
+        if constexpr (FMT == kFmtInt8)  // P in [0, tmax]: codes 0 .. 127
+          pf[4 * kt + qd] = (int)cvt4_u7(pq4[0], pq4[1], pq4[2], pq4[3], qs);
+        else
+          pf[4 * kt + qd] = (int)cvt4_e4m3(sat(pq4[0] * qs), sat(pq4[1] * qs), sat(pq4[2] * qs),
+                                           sat(pq4[3] * qs));
+      }
+    const float pv_scale = (tmax / QMAX) * sv[(size_t)bh * nb + j_prev];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const f32x16 tmp = mfma_f8(va[c], pf, f32x16{});
+      const f32x16 tmp = dot1(va[c], pf);
       os[c] += tmp * pv_scale;
     }
   };
@@ -721,14 +791,15 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
       const uint8_t* ks = kbuf(BUFC);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x16 s = f32x16{};
+        i32x8 ka[N8];
 #pragma unroll
         for (int st = 0; st < N8; ++st) {
           const int r = 32 * kt + lane % 32;
           const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g));
           const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g + 16));
-          s = mfma_f8(join8(a0, a1), qf[st], s);
+          ka[st] = join8(a0, a1);
         }
+        const f32x16 s = dot64(ka, qf);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           pp[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
@@ -806,16 +877,22 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
 }  // namespace
 
 hipError_t launch_quantize(const Dims& p, const void* X, uint8_t* codes, float* scales,
-                           hipStream_t stream) {
+                           hipStream_t stream, int int8) {
   dim3 grid(p.nb, p.B * p.H);
-  quantize_kernel<128, false><<<grid, 256, 0, stream>>>((const __bf16*)X, p.N, p.nb, codes, scales);
+  if (int8)
+    quantize_kernel<128, false, kFmtInt8><<<grid, 256, 0, stream>>>((const __bf16*)X, p.N, p.nb, codes, scales);
+  else
+    quantize_kernel<128, false, kFmtE4M3><<<grid, 256, 0, stream>>>((const __bf16*)X, p.N, p.nb, codes, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_v8t(const Dims& p, const void* X, uint8_t* codes, float* scales,
-                               hipStream_t stream) {
+                               hipStream_t stream, int int8) {
   dim3 grid(p.nb, p.B * p.H);
-  quantize_kernel<128, true><<<grid, 256, 0, stream>>>((const __bf16*)X, p.N, p.nb, codes, scales);
+  if (int8)
+    quantize_kernel<128, true, kFmtInt8><<<grid, 256, 0, stream>>>((const __bf16*)X, p.N, p.nb, codes, scales);
+  else
+    quantize_kernel<128, true, kFmtE4M3><<<grid, 256, 0, stream>>>((const __bf16*)X, p.N, p.nb, codes, scales);
   return hipGetLastError();
 }
 
@@ -836,12 +913,18 @@ hipError_t launch_sparse_pair8(const Dims& p, const void* Q, const uint8_t* q8, 
                                const uint8_t* v8, const float* sq, const float* sk,
                                const float* sv, const int32_t* idx, const float* alpha,
                                const __bf16* t_bf, const float* Z, const float* zb, float* O,
-                               hipStream_t stream) {
+                               hipStream_t stream, int int8) {
   if (p.nb > 2048) return hipErrorInvalidValue;
   const float c_log2 = 1.4426950408889634f / sqrtf((float)p.d);
-  pair8_kernel<128><<<p.B * p.H * ((p.nb + 1) / 2), kF8Threads, 0, stream>>>(
-      (const __bf16*)Q, q8, k8, v8, sq, sk, sv, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-      c_log2);
+  const int grid = p.B * p.H * ((p.nb + 1) / 2);
+  if (int8)
+    pair8_kernel<128, kFmtInt8><<<grid, kF8Threads, 0, stream>>>(
+        (const __bf16*)Q, q8, k8, v8, sq, sk, sv, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
+        c_log2);
+  else
+    pair8_kernel<128, kFmtE4M3><<<grid, kF8Threads, 0, stream>>>(
+        (const __bf16*)Q, q8, k8, v8, sq, sk, sv, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
+        c_log2);
   return hipGetLastError();
 }
 

@@ -71,19 +71,19 @@ hipError_t launch_linear_literal(const Dims& p, const void* Q, const int32_t* id
                                  const float* alpha, const float* h_full, const float* Z,
                                  const float* hj, const float* zb, float* O, hipStream_t stream);
 
-// fp8 path.
+// Low-bit path (int8 = 0: e4m3 codes, 1: int8 codes).
 hipError_t launch_quantize(const Dims& p, const void* X, uint8_t* codes, float* scales,
-                           hipStream_t stream);
-// V codes in the per-block transposed layout [BH][nb][d][64] read by the fp8 PV MFMA.
+                           hipStream_t stream, int int8 = 0);
+// V codes in the per-block transposed layout [BH][nb][d][64] read by the low-bit PV MFMA.
 hipError_t launch_quantize_v8t(const Dims& p, const void* X, uint8_t* codes, float* scales,
-                               hipStream_t stream);
+                               hipStream_t stream, int int8 = 0);
 // fp8 sparse branch, mask-product linear mode: two query blocks per workgroup over the union of
 // their kept blocks, T_i (bf16) from memory.
 hipError_t launch_sparse_pair8(const Dims& p, const void* Q, const uint8_t* q8, const uint8_t* k8,
                                const uint8_t* v8, const float* sq, const float* sk,
                                const float* sv, const int32_t* idx, const float* alpha,
                                const __bf16* t_bf, const float* Z, const float* zb, float* O,
-                               hipStream_t stream);
+                               hipStream_t stream, int int8 = 0);
 hipError_t launch_sparse_fp8(const Dims& p, const void* Q, const void* K, const void* V,
                              const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                              const float* sq, const float* sk, const float* sv,

@@ -107,7 +107,8 @@ typedef struct {
 /* Workspace sizes in bytes for a problem (0 when the problem is invalid or unsupported). */
 size_t sla_route_workspace_bytes(const sla_problem* p);
 /* variant: 0 = sla_forward (fused linear), 1 = sla_forward_fp8 (fused linear), 2 = literal
- * linear mode, 3 = mask-product linear mode, 4 = sla_forward_fp8 in the mask-product mode. */
+ * linear mode, 3 = mask-product linear mode, 4 = sla_forward_fp8 in the mask-product mode,
+ * 5 = sla_forward_int8 (mask-product mode). */
 size_t sla_forward_workspace_bytes(const sla_problem* p, int variant);
 
 /* Router (SLA2 Italian summary section 2.B, Arabic summary section 2.ba and 2.dal): block
@@ -148,6 +149,28 @@ int sla_forward_fp8(const sla_problem* p, const void* Q, const void* K, const vo
 int sla_forward_fp8_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const float* alpha, float* O, void* ws,
                        size_t ws_bytes, hipStream_t stream, const sla_forward_opts* opts);
+
+/* Forward with the INT8 sparse branch (SLA2 Italian summary section 2.C and Arabic summary
+ * section 2.jim name INT8 beside FP8): as sla_forward_fp8 in the mask-product mode with int8
+ * codes instead of e4m3: per (b, h, 64-token block) symmetric absmax scales a / 127,
+ * code = round-half-even(x * fp32(127 / a)) in [-127, 127]; P per (query block x key block)
+ * tile with scale max(tile) / 127 over exp(S - rowmax) (exact row maximum), codes in
+ * [0, 127]; S and P V from exact int32 products (v_mfma_i32_32x32x32_i8) times the scales;
+ * the denominator sums the unquantised exp(S - rowmax).  Only dtype SLA_BF16 with d = 128 is
+ * compiled.  Needs sla_forward_workspace_bytes(p, 5) bytes.  The _ex form takes opts whose
+ * linear_mode must be SLA_LINEAR_MASK_PRODUCT (else SLA_ERR_UNSUPPORTED); branch dropping is
+ * not available with it. */
+int sla_forward_int8(const sla_problem* p, const void* Q, const void* K, const void* V,
+                     const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+int sla_forward_int8_ex(const sla_problem* p, const void* Q, const void* K, const void* V,
+                        const int32_t* idx, const float* alpha, float* O, void* ws,
+                        size_t ws_bytes, hipStream_t stream, const sla_forward_opts* opts);
+
+/* Quantisation step of sla_forward_int8 on its own (byte-exact checks): int8 codes of X
+ * [B][H][N][d] (bf16) to codes [B][H][N][d] and the per-block scales to scales [B][H][n_b]. */
+int sla_quantize_int8(const sla_problem* p, const void* X, int8_t* codes, float* scales,
+                      hipStream_t stream);
 
 /* Quantisation step of sla_forward_fp8 on its own (for byte-exact checks): writes e4m3 codes
  * of X [B][H][N][d] (bf16) to codes [B][H][N][d] (uint8) and the per-block scales to

@@ -62,7 +62,8 @@ def test_workspace_sizes(L):
     assert f(P(), 4) > f(P(), 3) and f(P(), 4) > f(P(), 1)
     # invalid or unsupported problems size to 0
     assert r(P(B=0)) == 0 and r(P(block=32)) == 0 and r(P(d=96)) == 0 and r(P(topk=65)) == 0
-    assert f(P(), 5) == 0 and f(P(), -1) == 0
+    assert f(P(), 5) == f(P(), 4)  # int8 codes take the space of the fp8 ones
+    assert f(P(), 6) == 0 and f(P(), -1) == 0
     assert L.sla_route_workspace_bytes(None) == 0
 
 
@@ -125,6 +126,24 @@ def test_fp8_and_mode_checks(L):
     assert L.sla_forward_ex(ctypes.byref(p), *args, ctypes.byref(opts_bad)) == sla.SLA_ERR_INVALID
     assert L.sla_quantize_e4m3(ctypes.byref(P(d=64)), FAKE, FAKE, FAKE, None) == sla.SLA_ERR_UNSUPPORTED
     assert L.sla_quantize_e4m3(ctypes.byref(p), None, FAKE, FAKE, None) == sla.SLA_ERR_INVALID
+
+
+def test_int8_checks(L):
+    p = P()
+    ws = 1 << 40
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert L.sla_forward_int8(ctypes.byref(P(d=64)), *args) == sla.SLA_ERR_UNSUPPORTED
+    assert L.sla_forward_int8(ctypes.byref(P(dtype=sla.SLA_F32)), *args) == sla.SLA_ERR_UNSUPPORTED
+    for mode in ("fused", "literal"):
+        o = sla.ForwardOpts(sla.LINEAR_MODES[mode], None, None)
+        assert L.sla_forward_int8_ex(ctypes.byref(p), *args, ctypes.byref(o)) in (
+            sla.SLA_ERR_UNSUPPORTED, sla.SLA_ERR_INVALID)
+    o = sla.ForwardOpts(sla.LINEAR_MODES["mask_product"], None, None, None, None, 1, 0.0)
+    assert L.sla_forward_int8_ex(ctypes.byref(p), *args, ctypes.byref(o)) == sla.SLA_ERR_UNSUPPORTED
+    small = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None)
+    assert L.sla_forward_int8(ctypes.byref(p), *small) == sla.SLA_ERR_WORKSPACE
+    assert L.sla_quantize_int8(ctypes.byref(P(d=64)), FAKE, FAKE, FAKE, None) == sla.SLA_ERR_UNSUPPORTED
+    assert L.sla_quantize_int8(ctypes.byref(p), FAKE, None, FAKE, None) == sla.SLA_ERR_INVALID
 
 
 def test_branch_drop_checks(L):

@@ -1,8 +1,8 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU float64 oracle.
 
 Bars: router indices and mask bit-exact; O within max-abs 1e-2 and relative L2 5e-3 (bf16 or
-fp32 inputs, fp32 accumulation), relative L2 3e-2 for the fp8 sparse branch; e4m3 codes and
-scales byte-exact.  Small cases are compared element by element over every output; the
+fp32 inputs, fp32 accumulation), relative L2 3e-2 for the fp8 and int8 sparse branches; e4m3 and
+int8 codes and scales byte-exact.  Small cases are compared element by element over every output; the
 full-size workloads (the ones the benchmark times) over every router row and over sampled query
 blocks of sampled heads (always including the first and the last, possibly short, block).
 """
@@ -296,6 +296,39 @@ def test_fp8_forward_mask_product(k):
     check_close(got, fused, rel_tol=1e-2, max_tol=None, what=f"fp8 mask_product vs fused k={k}")
 
 
+def test_quantize_int8_bytes_exact():
+    wl = small_ragged()
+    c = case("ragged_bf16", wl)
+    g = dev(c)
+    for name in ("Q", "K", "V"):
+        say(f"quantize int8 {name}")
+        codes, scales = sla.quantize_int8(g[name])
+        codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+        for b in range(wl.B):
+            for h in range(wl.H):
+                rc, rs, _ = oracle.quantize_blocks_int8(c[name][b, h], 64)
+                assert np.array_equal(scales[b, h], rs)
+                assert np.array_equal(codes[b, h], rc)
+
+
+@pytest.mark.parametrize("k", [6, 0, 1, 57])
+def test_int8_forward(k):
+    """The INT8 sparse branch (two query blocks per workgroup, mask-product linear mode) against
+    the int8 oracle on every element, for k = 6 and the degenerate counts; alpha = 1 isolates
+    the quantised branch."""
+    wl = small_ragged(k=k)
+    c = case("ragged_bf16" if k == 6 else f"ragged_k{k}", wl)
+    r = oracle_route(c, k)
+    say(f"forward int8 k={k}")
+    got = run_forward(c, r["idx"], int8=True, linear_mode="mask_product")
+    ref, Os, _ = oracle.forward_int8(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what=f"forward int8 k={k}")
+    if 0 < k:
+        one = torch.ones_like(c["alpha"]).to("cuda:0")
+        check_close(run_forward(c, r["idx"], alpha=one, int8=True, linear_mode="mask_product"), Os,
+                    rel_tol=TOL_REL_FP8, max_tol=None, what=f"int8 sparse branch alone k={k}")
+
+
 def test_fp8_forward_branches_isolated():
     """alpha = 1: the quantised sparse branch alone; alpha = 0: the linear branch, unquantised."""
     wl = small_ragged()
@@ -436,6 +469,28 @@ def test_video_l_fp8_full_size_mask_product():
               linear_mode="mask_product")
 
 
+def test_video_l_int8_full_size():
+    c = case("video_l", gen.workload("video_l"))
+    wl = c["workload"]
+    g = dev(c)
+    r = oracle_route(c, wl.topk)
+    idx = torch.from_numpy(r["idx"]).to(g["Q"].device)
+    say("forward video_l int8")
+    O = sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], int8=True, linear_mode="mask_product")
+    torch.cuda.synchronize()
+    got = O.cpu().double().numpy()
+    gots, refs = [], []
+    for bh in (5, 33):
+        b, h = divmod(bh, wl.H)
+        o, _, _ = oracle.forward_int8_head(c["Q"][b, h], c["K"][b, h], c["V"][b, h], r["idx"][b, h],
+                                           c["alpha"][b, h], 64, q_blocks=[0, 700, 1181])
+        for i, oi in zip([0, 700, 1181], o):
+            refs.append(oi)
+            gots.append(got[b, h, i * 64 : i * 64 + len(oi)])
+    check_close(np.concatenate(gots), np.concatenate(refs), rel_tol=TOL_REL_FP8, max_tol=None,
+                what="video_l int8")
+
+
 @pytest.mark.parametrize("k", [102, 51, 26, 15])
 @pytest.mark.parametrize("scale", [0.5, 1.0, 2.0])
 def test_sparsity_sweep(scale, k):
@@ -505,6 +560,10 @@ def test_edge_shapes(wl):
             say(f"edge forward {wl.name} fp8 {mode}")
             check_close(run_forward(c, r["idx"], fp8=True, linear_mode=mode), ref8, rel_tol=TOL_REL_FP8,
                         max_tol=None, what=f"{wl.name} fp8 {mode}")
+        ref_i8, _, _ = oracle.forward_int8(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+        say(f"edge forward {wl.name} int8")
+        check_close(run_forward(c, r["idx"], int8=True, linear_mode="mask_product"), ref_i8,
+                    rel_tol=TOL_REL_FP8, max_tol=None, what=f"{wl.name} int8")
     _CACHE.pop(wl.name, None)
 
 
