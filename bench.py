@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_INT8_TOPS = 5000.0    # MI355X dense int8 MFMA (TOP/s)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 
@@ -46,6 +47,8 @@ def parse():
                     help="video_s | video_l | video_l_fp8 | pisa_video_s | pisa_video_l")
     ap.add_argument("--linear-mode", default="mask_product", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--int8", action="store_true",
+                    help="the INT8 sparse branch (mask-product linear mode) on the workload's tensors")
     ap.add_argument("--drop-tau", type=float, default=None,
                     help="branch dropping threshold (mask-product mode): a head drops its linear "
                          "branch when max(1 - alpha) <= tau, its sparse branch when max(alpha) <= tau")
@@ -416,6 +419,9 @@ def main():
         return
     if wl.fp8 and a.linear_mode == "literal":
         a.linear_mode = "fused"  # the fp8 path has the fused and mask-product linear modes
+    int8 = a.int8
+    if int8:
+        a.linear_mode = "mask_product"  # the int8 path exists in the mask-product mode only
     inputs = gen.draw(wl, 0)
     if a.drop_heads:
         nl, ns = (int(x) for x in a.drop_heads.split(","))
@@ -428,7 +434,7 @@ def main():
     fp8 = wl.fp8
     idx = torch.empty((B, H, nb, wl.topk), dtype=torch.int32, device=dev)
     ws_r = torch.empty(sla.route_workspace_bytes(Q, wl.topk), dtype=torch.uint8, device=dev)
-    variant = ({"fused": 1, "mask_product": 4}[a.linear_mode] if fp8
+    variant = (5 if int8 else {"fused": 1, "mask_product": 4}[a.linear_mode] if fp8
                else {"fused": 0, "literal": 2, "mask_product": 3}[a.linear_mode])
     ws_f = torch.empty(sla.forward_workspace_bytes(Q, wl.topk, variant), dtype=torch.uint8, device=dev)
     O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
@@ -447,7 +453,7 @@ def main():
             ev_r[i][1].record()
         sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O,
                     events=ev[i] if i is not None else None,
-                    state_events=ev_s[i] if i is not None else None, drop_tau=a.drop_tau)
+                    state_events=ev_s[i] if i is not None else None, drop_tau=a.drop_tau, int8=int8)
         if i is not None:
             ev_t[i][1].record()
 
@@ -472,7 +478,7 @@ def main():
         ev_c[i][0].record()
         sla.route(Q, K, Wq, Wk, wl.topk, workspace=ws_r, idx_out=idx)
         sla.forward(Q, K, V, idx, alpha, fp8=fp8, linear_mode=a.linear_mode, workspace=ws_f, out=O,
-                    drop_tau=a.drop_tau)
+                    drop_tau=a.drop_tau, int8=int8)
         ev_c[i][1].record()
     torch.cuda.synchronize()
     cold_q = quantiles(ev_c)
@@ -485,11 +491,11 @@ def main():
     # linear state (one bf16 T_i in the mask-product mode, hi and lo halves in the fused one),
     # and the fused mode rebuilds relu(K_j)^T V_j of every kept pair on chip (the sparse count
     # again): reported as executed MFMA work, not counted in `achieved`.
-    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    peak = PEAK_INT8_TOPS if int8 else PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     achieved = flops / (sparse_ms * 1e-3) / 1e12
     apply_flops = 2.0 * B * H * N * d * d  # relu(q) T per query row, one bf16 operand
     executed = flops + {"fused": flops + 2 * apply_flops, "literal": 0.0, "mask_product": apply_flops}[a.linear_mode]
-    if fp8:
+    if fp8 or int8:
         sources = ["block_sparse_linear_02_amd/csrc/fp8.hip"]
         kname = "pair8_kernel" if a.linear_mode == "mask_product" else "sparse_fp8_kernel"
     elif a.linear_mode == "mask_product":
@@ -497,7 +503,7 @@ def main():
     else:
         sources, kname = SPARSE_SOURCES, "sparse_kernel"
     digest = source_digest(sources)
-    kernel_key = kname + f"@{a.workload}"
+    kernel_key = kname + ("<int8>" if int8 else "") + f"@{a.workload}"
     # HBM streams: the router reads Q and K once and writes the index lists; the state kernels
     # read K and V once and write per-block z_j plus the per-(b, h) totals; in the mask-product
     # mode they also write every h_j^T (bf16), which the mask GEMM reads back (once per 256 query
@@ -523,11 +529,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 sparse branch, bf16 linear" if fp8 else ("bf16" if es == 2 else "f32"),
+        "dtype": ("int8 sparse branch, bf16 linear" if int8 else
+                  "fp8-e4m3 sparse branch, bf16 linear" if fp8 else ("bf16" if es == 2 else "f32")),
         "data": "synthetic (seeded clustered video-DiT-shaped tensors, random projections)",
         "config": {
             "workload": f"{a.workload}: B={B} H={H} N={N} d={d} block=64 topk={wl.topk} of {nb} "
                         f"({100 * (1 - wl.topk / nb):.1f}% block sparsity), linear={a.linear_mode}"
+                        + (", int8 sparse branch" if int8 else "")
                         + (f", alpha=1/0 on heads {a.drop_heads}" if a.drop_heads else "")
                         + (f", branch drop tau={a.drop_tau}" if a.drop_tau is not None else ""),
             "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": wl.topk,
@@ -542,7 +550,7 @@ def main():
             "kernel": kernel_key.split("@")[0],
             "achieved": achieved,
             "peak": peak,
-            "unit": "TFLOP/s",
+            "unit": "TOP/s" if int8 else "TFLOP/s",
             "frac": achieved / peak,
             "traffic": traffic_for(kernel_key, digest),
             "flops_per_launch": flops,
