@@ -57,3 +57,4 @@ from .int8 import (  # noqa: F401
     forward_int8_head,
     forward_int8,
 )
+from .train import backward_head, backward  # noqa: F401

@@ -386,6 +386,81 @@ def pin_fp8_error_scale(orc):
 
 
 # ----------------------------------------------------------------------------------------------
+# backward (training path)
+
+
+def _torch_sla_forward(Q, K, V, idx, alpha, blk):
+    """A dense float64 torch re-statement of the SLA2 forward of one head (token-level masks),
+    written independently of the oracle, for autograd."""
+    N, d = Q.shape
+    bid = torch.arange(N) // blk
+    kept = torch.zeros((N, N), dtype=torch.bool)
+    for t in range(N):
+        kept[t] = torch.isin(bid, torch.as_tensor(np.asarray(idx[int(bid[t])], dtype=np.int64)))
+    x = (Q @ K.T) / math.sqrt(d)
+    any_kept = kept.any(dim=1, keepdim=True)
+    p = torch.softmax(torch.where(kept, x, torch.full_like(x, -1e300)), dim=1)
+    O_s = torch.where(any_kept, p @ V, torch.zeros_like(Q))
+    w = (torch.relu(Q) @ torch.relu(K).T) * (~kept)
+    num, den = w @ V, w.sum(dim=1, keepdim=True)
+    safe = torch.where(den != 0, den, torch.ones_like(den))
+    O_l = torch.where(den != 0, num / safe, torch.zeros_like(num))
+    a = alpha[:, None]
+    return a * O_s + (1 - a) * O_l
+
+
+def _bwd_case(seed, N=150, d=8, blk=32, k=2):
+    rng = np.random.default_rng(seed)
+    Q, K, V, dO = (rng.standard_normal((N, d)) for _ in range(4))
+    alpha = rng.uniform(0, 1, N)
+    n_b = -(-N // blk)
+    idx = _rand_idx(n_b, k, seed + 1)
+    return Q, K, V, dO, alpha, idx, blk
+
+
+def pin_backward_matches_autograd(orc):
+    """dQ, dK, dV, dalpha equal torch.autograd's gradients of an independent dense torch
+    forward (float64), for k in {0, 2, n_b} with a short last block, and rows whose linear
+    denominator is exactly 0 (queries with no positive channel)."""
+    for seed, k in ((111, 2), (113, 0), (115, 5)):
+        Q, K, V, dO, alpha, idx, blk = _bwd_case(seed, k=k)
+        Q[3] = -np.abs(Q[3])  # relu(q) = 0: zero linear denominator
+        got = orc.backward_head(Q, K, V, idx, alpha, dO, blk)
+        ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V, alpha)]
+        O = _torch_sla_forward(ts[0], ts[1], ts[2], idx, ts[3], blk)
+        (O * torch.from_numpy(dO)).sum().backward()
+        for name, gv, tv in zip(("dQ", "dK", "dV", "dalpha"), got, ts):
+            np.testing.assert_allclose(gv, tv.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=f"k={k} {name}")
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of sum(O * dO) through the oracle's own forward match the backward on a
+    tiny head (entries kept away from the ReLU kink)."""
+    Q, K, V, dO, alpha, idx, blk = _bwd_case(117, N=40, d=4, blk=8, k=2)
+    for X in (Q, K):
+        X[np.abs(X) < 0.05] += 0.1
+    dQ, dK, dV, da = orc.backward_head(Q, K, V, idx, alpha, dO, blk)
+    L = lambda Q_, K_, V_, a_: float((orc.forward(Q_[None, None], K_[None, None], V_[None, None], idx[None, None], a_[None, None], blk)[0][0, 0] * dO).sum())  # noqa: E731
+    eps = 1e-6
+    rng = np.random.default_rng(118)
+    for which, G in ((0, dQ), (1, dK), (2, dV)):
+        for _ in range(6):
+            r, c = rng.integers(0, 40), rng.integers(0, 4)
+            args_p = [Q.copy(), K.copy(), V.copy(), alpha.copy()]
+            args_m = [Q.copy(), K.copy(), V.copy(), alpha.copy()]
+            args_p[which][r, c] += eps
+            args_m[which][r, c] -= eps
+            fd = (L(*args_p) - L(*args_m)) / (2 * eps)
+            assert abs(fd - G[r, c]) < 1e-6 * (1 + abs(fd)), (which, r, c, fd, G[r, c])
+    for r in (0, 17, 39):
+        ap, am = alpha.copy(), alpha.copy()
+        ap[r] += eps
+        am[r] -= eps
+        fd = (L(Q, K, V, ap) - L(Q, K, V, am)) / (2 * eps)
+        assert abs(fd - da[r]) < 1e-6 * (1 + abs(fd)), (r, fd, da[r])
+
+
+# ----------------------------------------------------------------------------------------------
 # int8 sparse branch
 
 

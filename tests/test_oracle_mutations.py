@@ -32,6 +32,14 @@ MUTATIONS = {
     "fp8_scale_dropped": ("fp8.py", "deq[a:b] = e4m3_decode(codes[a:b]) * np.float64(scales[t])", "deq[a:b] = e4m3_decode(codes[a:b])"),
     "fp8_truncating_round": ("fp8.py", "m8 = np.rint((mant * 2.0 - 1.0) * 8.0)", "m8 = np.floor((mant * 2.0 - 1.0) * 8.0)"),
     "fp8_bias_off_by_one": ("fp8.py", "_E4M3_BIAS = 7", "_E4M3_BIAS = 8"),
+    "bwd_no_D_term": ("train.py", "ds = p * (dp - D)", "ds = p * dp"),
+    "bwd_dk_unscaled": ("train.py", "dK[tok] += (ds.T @ q) * scale", "dK[tok] += ds.T @ q"),
+    "bwd_no_relu_mask_q": ("train.py", "dQ[a:b] += dphi * (q > 0.0)", "dQ[a:b] += dphi"),
+    "bwd_den_grad_sign": ("train.py", "e = -(g * o_l).sum(axis=1)", "e = (g * o_l).sum(axis=1)"),
+    "bwd_dalpha_sign": ("train.py", "dalpha[a:b] = (g_o * (o_s - o_l)).sum(axis=1)", "dalpha[a:b] = (g_o * (o_l - o_s)).sum(axis=1)"),
+    "bwd_no_linear_dv": ("train.py", "dV[a:b] += pK[a:b] @ dh[j]", "dV[a:b] += 0.0"),
+    "bwd_dz_dropped": ("train.py", "dK[a:b] += (V[a:b] @ dh[j].T + dz[j][None, :]) * (K[a:b] > 0.0)", "dK[a:b] += (V[a:b] @ dh[j].T) * (K[a:b] > 0.0)"),
+    "bwd_linear_over_kept": ("train.py", "dh[uns] += dA[None]", "dh[:] += dA[None]"),
     "int8_truncating_round": ("int8.py", "return np.clip(np.rint(y), -INT8_MAX, INT8_MAX).astype(np.int8)", "return np.clip(np.trunc(y), -INT8_MAX, INT8_MAX).astype(np.int8)"),
     "int8_clamp_128": ("int8.py", "return np.clip(np.rint(y), -INT8_MAX, INT8_MAX).astype(np.int8)", "return np.clip(np.rint(y), -128, 127).astype(np.int8)"),
     "int8_scale_over_128": ("int8.py", "scales[t] = np.float32(amax / np.float32(INT8_MAX))", "scales[t] = np.float32(amax / np.float32(128.0))"),
