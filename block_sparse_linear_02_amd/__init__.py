@@ -36,6 +36,7 @@ __all__ = [
     "forward",
     "quantize_e4m3",
     "quantize_int8",
+    "backward",
     "route_workspace_bytes",
     "forward_workspace_bytes",
     "PisaStats",
@@ -115,6 +116,10 @@ def lib() -> ctypes.CDLL:
         for name in ("sla_quantize_e4m3", "sla_quantize_int8"):
             getattr(L, name).argtypes = [P, vp, vp, vp, vp]
             getattr(L, name).restype = i32
+        L.sla_backward_workspace_bytes.argtypes = [P]
+        L.sla_backward_workspace_bytes.restype = sz
+        L.sla_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sla_backward.restype = i32
         L.sla_pisa_stats_bytes.argtypes = [P]
         L.sla_pisa_stats_bytes.restype = sz
         L.sla_pisa_workspace_bytes.argtypes = [P]
@@ -231,6 +236,30 @@ def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", 
     if st != SLA_OK:
         raise SLAError(st, "sla_forward_int8" if int8 else ("sla_forward_fp8" if fp8 else "sla_forward"))
     return O
+
+
+def backward(Q, K, V, idx, alpha, dO, workspace=None, want_O=False, out=None):
+    """Gradients (dQ, dK, dV, dalpha) of O = alpha O_s + (1 - alpha) O_l for the kept sets idx
+    (bf16, d = 128); the forward is recomputed on the GPU.  Returns (dQ, dK, dV, dalpha[, O])."""
+    _check_qkv(Q, K, V, dO)
+    Q, K, V, dO = Q.contiguous(), K.contiguous(), V.contiguous(), dO.contiguous()
+    B, H, N, d = Q.shape
+    topk = idx.shape[-1]
+    idx = idx.contiguous().to(torch.int32)
+    alpha = alpha.contiguous().to(torch.float32)
+    p = _problem(Q, topk)
+    need = lib().sla_backward_workspace_bytes(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    if out is None:
+        out = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device) for _ in range(3)) + (
+            torch.empty((B, H, N), dtype=torch.float32, device=Q.device),)
+    dQ, dK, dV, da = out
+    O = torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device) if want_O else None
+    st = lib().sla_backward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(alpha), _ptr(dO),
+                            _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(da), _ptr(O), _ptr(ws), ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_backward")
+    return (dQ, dK, dV, da, O) if want_O else (dQ, dK, dV, da)
 
 
 def quantize_int8(X):

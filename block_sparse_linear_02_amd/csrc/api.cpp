@@ -155,6 +155,47 @@ size_t carve_pisa_ws(const sla::Dims& d, void* base, PisaWs* out) {
   return c.off;
 }
 
+// Backward scratch
+struct BwdWs {
+  float *zb, *z_part, *Z, *O, *Os, *Ol, *lse2, *rden, *Dr, *e, *dzeta, *dz, *zb2, *z_part2;
+  __bf16 *hj_bf, *t_bf, *dh_bf, *dOs, *G;
+  uint32_t *bits, *kept_t, *unsel_t;
+};
+size_t carve_backward(const sla::Dims& d, void* ws, BwdWs* out) {
+  Carve c(ws);
+  const size_t BH = (size_t)d.B * d.H;
+  const size_t dd = (size_t)d.d * d.d;
+  const size_t rows = BH * d.N, elems = rows * d.d, blocks = BH * d.nb;
+  const int cb = sla::state_chunk_blocks(d);
+  const size_t nchunk = (d.nb + cb - 1) / cb;
+  const size_t words = blocks * sla::mask_words(d.nb);
+  BwdWs w = {};
+  w.zb = c.take<float>(blocks * d.d);
+  w.z_part = c.take<float>(BH * nchunk * d.d);
+  w.Z = c.take<float>(BH * d.d);
+  w.hj_bf = c.take<__bf16>(blocks * dd);  // h_j^T of the forward, then dA_i^T
+  w.t_bf = c.take<__bf16>(blocks * dd);
+  w.dh_bf = c.take<__bf16>(blocks * dd);
+  w.bits = c.take<uint32_t>(words);
+  w.kept_t = c.take<uint32_t>(words);
+  w.unsel_t = c.take<uint32_t>(words);
+  w.O = c.take<float>(elems);
+  w.Os = c.take<float>(elems);
+  w.Ol = c.take<float>(elems);
+  w.lse2 = c.take<float>(rows);
+  w.rden = c.take<float>(rows);
+  w.dOs = c.take<__bf16>(elems);
+  w.G = c.take<__bf16>(elems);
+  w.Dr = c.take<float>(rows);
+  w.e = c.take<float>(rows);
+  w.dzeta = c.take<float>(blocks * d.d);
+  w.dz = c.take<float>(blocks * d.d);
+  w.zb2 = c.take<float>(blocks * d.d);
+  w.z_part2 = c.take<float>(BH * nchunk * d.d);
+  if (out) *out = w;
+  return c.off;
+}
+
 inline int hip_fail(hipError_t e) {
   g_last_hip_error = (int)e;
   return SLA_ERR_HIP;
@@ -407,6 +448,55 @@ int sla_pisa_forward(const sla_problem* p, const void* Q, const void* K, const v
   PisaStats s;
   carve_pisa_stats(d, const_cast<void*>(stats), &s, nullptr);
   hipError_t e = sla::launch_pisa(d, Q, K, V, idx, s.kbar_hi, s.kbar_lo, s.vsum, s.hbar_t, O, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+size_t sla_backward_workspace_bytes(const sla_problem* p) {
+  sla::Dims d;
+  if (check_problem(p, &d) != SLA_OK) return 0;
+  return carve_backward(d, nullptr, nullptr);
+}
+
+int sla_backward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                 const int32_t* idx, const float* alpha, const void* dO, float* dQ, float* dK,
+                 float* dV, float* dalpha, float* O, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (d.dtype != sla::kBF16 || d.d != 128) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !alpha || !dO || !dQ || !dK || !dV || !dalpha || (d.topk > 0 && !idx) || !ws)
+    return SLA_ERR_INVALID;
+  if (ws_bytes < carve_backward(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  BwdWs w;
+  carve_backward(d, ws, &w);
+  hipError_t e;
+  // the forward in the mask-product mode, keeping what the backward reads
+  e = sla::launch_states(d, K, V, w.zb, nullptr, w.z_part, nullptr, w.hj_bf, stream);
+  if (e == hipSuccess)
+    e = sla::launch_state_reduce(d, nullptr, w.z_part, nullptr, nullptr, w.Z, nullptr, stream);
+  if (e == hipSuccess) e = sla::launch_mask_bits(d, idx, w.bits, stream);
+  if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.bits, w.t_bf, stream);
+  const sla::TrainRows tr = {w.Os, w.Ol, w.lse2, w.rden};
+  if (e == hipSuccess)
+    e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O ? O : w.O, stream,
+                                nullptr, &tr);
+  // per-row terms, the transposed kept sets, the linear branch's dA_i, dh_j and dz_j
+  if (e == hipSuccess)
+    e = sla::launch_bwd_prep(d, Q, dO, alpha, tr, dalpha, w.dOs, w.Dr, w.G, w.e, w.dzeta, stream);
+  if (e == hipSuccess) e = sla::launch_bits_t(d, idx, w.kept_t, w.unsel_t, stream);
+  if (e == hipSuccess)
+    e = sla::launch_states(d, Q, w.G, w.zb2, nullptr, w.z_part2, nullptr, w.hj_bf, stream);
+  if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.unsel_t, w.dh_bf, stream);
+  if (e == hipSuccess) e = sla::launch_bwd_dz(d, w.dzeta, w.unsel_t, w.dz, stream);
+  // the gradients
+  if (e == hipSuccess)
+    e = sla::launch_bwd_dq(d, Q, K, V, idx, w.dOs, w.lse2, w.Dr, w.G, w.e, w.t_bf, w.Z, w.zb, dQ,
+                           stream);
+  if (e == hipSuccess)
+    e = sla::launch_bwd_dkv(d, Q, K, V, w.kept_t, w.dOs, w.lse2, w.Dr, w.dh_bf, w.dz, dK, dV,
+                            stream);
   if (e != hipSuccess) return hip_fail(e);
   return SLA_OK;
 }

@@ -47,12 +47,18 @@ hipError_t launch_tsel(const Dims& p, const __bf16* hj_bf, const uint32_t* bits,
 
 // Sparse branch with the linear part from the precomputed T_i (bf16) and zeta from z_j, two
 // query blocks per workgroup over the union of their kept blocks (n_b <= 2048).
+// Per-row outputs of the forward that the backward reads ([BH][N][d] fp32 for Os, Ol; [BH][N]
+// for lse2 = log2 sum_n 2^(s_n c) of the sparse branch, +inf without kept keys, and rden =
+// 1 / den, 0 where the linear branch is defined as 0).
+struct TrainRows {
+  float *Os, *Ol, *lse2, *rden;
+};
 // flags (optional): a kDropLinear head writes alpha O_s only, a kDropSparse head
-// (1 - alpha) O_l only.
+// (1 - alpha) O_l only.  tr (optional, bf16 with d = 128): also write the TrainRows.
 hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream,
-                              const uint32_t* flags = nullptr);
+                              const uint32_t* flags = nullptr, const TrainRows* tr = nullptr);
 // Reduce the chunk partials (fixed order): H^T as bf16 hi/lo [d][d], Z [d]; optionally H [d][d]
 // in fp32 (K-channel major, literal mode); Z alone when h_part is null (mask-product mode).
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,
@@ -108,5 +114,25 @@ int pisa_max_blocks();
 hipError_t launch_pisa(const Dims& p, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const __bf16* kbar_hi, const __bf16* kbar_lo,
                        const __bf16* vsum, const __bf16* hbar_t, float* O, hipStream_t stream);
+
+// Backward (bwd.hip; bf16, d = 128).  prep: dalpha, dO_s = alpha dO and G = (1 - alpha) dO / den
+// in bf16 [BH][N][d], D = dO_s . O_s and e = -G . O_l [BH][N], dzeta_i [BH][nb][d].
+hipError_t launch_bwd_prep(const Dims& p, const void* Q, const void* dO, const float* alpha,
+                           const TrainRows& tr, float* dalpha, __bf16* dOs, float* Dr, __bf16* G,
+                           float* e, float* dzeta, hipStream_t stream);
+// The kept sets transposed: bit rows [BH][nb][mask_words(nb)] of the query blocks keeping each
+// key block, and the complement within n_b.
+hipError_t launch_bits_t(const Dims& p, const int32_t* idx, uint32_t* kept_t, uint32_t* unsel_t,
+                         hipStream_t stream);
+hipError_t launch_bwd_dz(const Dims& p, const float* dzeta, const uint32_t* unsel_t, float* dz,
+                         hipStream_t stream);
+hipError_t launch_bwd_dq(const Dims& p, const void* Q, const void* K, const void* V,
+                         const int32_t* idx, const __bf16* dOs, const float* lse2, const float* Dr,
+                         const __bf16* G, const float* e, const __bf16* t_bf, const float* Z,
+                         const float* zb, float* dQ, hipStream_t stream);
+hipError_t launch_bwd_dkv(const Dims& p, const void* Q, const void* K, const void* V,
+                          const uint32_t* kept_t, const __bf16* dOs, const float* lse2,
+                          const float* Dr, const __bf16* dh, const float* dz, float* dK, float* dV,
+                          hipStream_t stream);
 
 }  // namespace sla

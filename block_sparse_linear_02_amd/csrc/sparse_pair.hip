@@ -78,13 +78,16 @@ __device__ __forceinline__ float pair_sum8(bf16x8 v, float acc) {
 
 constexpr float kPairRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before the maximum moves
 
-template <class T, int D>
+// TRAIN: also write what the backward needs per query row (TrainRows, sla_launch.hpp): the
+// normalised branches O_s and O_l, the sparse branch's log2-sum-exp2 and 1 / den (0 where the
+// linear branch is defined as 0)
+template <class T, int D, bool TRAIN>
 __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
     float* __restrict__ O, int N, int nb, int topk, float c_log2,
-    const uint32_t* __restrict__ flags) {
+    const uint32_t* __restrict__ flags, TrainRows tr) {
   constexpr int NS = D / 16;  // MFMA k-steps over the head dim
   constexpr int NC = D / 32;  // 32-channel output tiles
   constexpr int TILE = TileLayout<D>::ELEMS;
@@ -436,18 +439,45 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
       for (int e = 0; e < 4; ++e) v[e] = fmaf(num[c][4 * qd + e], wl, os[c][4 * qd + e] * ws);
       *reinterpret_cast<f32x4*>(orow + 32 * c + 8 * qd + 4 * g) = v;
     }
+  if constexpr (TRAIN) {
+    float* srow = tr.Os + hoff + (size_t)row * D;
+    float* lrow = tr.Ol + hoff + (size_t)row * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        f32x4 vs, vl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vs[e] = os[c][4 * qd + e] * inv_l;
+          vl[e] = num[c][4 * qd + e] * inv_den;
+        }
+        *reinterpret_cast<f32x4*>(srow + 32 * c + 8 * qd + 4 * g) = vs;
+        *reinterpret_cast<f32x4*>(lrow + 32 * c + 8 * qd + 4 * g) = vl;
+      }
+    if (g == 0) {
+      // a row with no kept key has no sparse probabilities: +inf makes every recomputed P 0
+      tr.lse2[(size_t)bh * N + row] = ltot > 0.f ? mrun + __log2f(ltot) : INFINITY;
+      tr.rden[(size_t)bh * N + row] = inv_den;
+    }
+  }
 }
 
 template <class T, int D>
 hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const float* alpha, const __bf16* t_bf,
                          const float* Z, const float* zb, float* O, hipStream_t stream,
-                         const uint32_t* flags) {
+                         const uint32_t* flags, const TrainRows* tr) {
   const int total = xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
-  pair_kernel<T, D><<<total, kPairThreads, 0, stream>>>(
-      (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-      c_log2, flags);
+  if (tr)
+    pair_kernel<T, D, true><<<total, kPairThreads, 0, stream>>>(
+        (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
+        c_log2, flags, *tr);
+  else
+    pair_kernel<T, D, false><<<total, kPairThreads, 0, stream>>>(
+        (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
+        c_log2, flags, TrainRows{});
   return hipGetLastError();
 }
 
@@ -456,15 +486,16 @@ hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void
 hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream,
-                              const uint32_t* flags) {
+                              const uint32_t* flags, const TrainRows* tr) {
   if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags);
+    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, tr);
+  if (tr) return hipErrorInvalidValue;  // the training outputs exist for bf16, d = 128 only
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags);
+    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags);
-  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags);
+    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr);
+  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr);
 }
 
 }  // namespace sla

@@ -178,6 +178,21 @@ int sla_quantize_int8(const sla_problem* p, const void* X, int8_t* codes, float*
 int sla_quantize_e4m3(const sla_problem* p, const void* X, uint8_t* codes, float* scales,
                       hipStream_t stream);
 
+/* Backward of the forward (the training path; SLA2 Italian summary section 2, Arabic summary
+ * sections 2 and 2.jim: fine-tuning with the attention in place, the backward taken on the
+ * unquantised values): gradients of O = alpha O_s + (1 - alpha) O_l with respect to Q, K, V and
+ * alpha for the given kept sets (the HardTop-k router has no gradient).  dO [B][H][N][d] in the
+ * dtype of Q; dQ, dK, dV [B][H][N][d] and dalpha [B][H][N] float32 outputs (overwritten).  The
+ * forward is recomputed in the mask-product mode; O (optional, NULL to skip) receives it.  The
+ * linear branch passes no gradient through rows where it is defined as 0 (empty unselected set
+ * or zero denominator), and ReLU's derivative at 0 is taken as 0.  Only dtype SLA_BF16 with
+ * d = 128 is compiled.  Needs sla_backward_workspace_bytes(p) bytes of workspace. */
+size_t sla_backward_workspace_bytes(const sla_problem* p);
+int sla_backward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                 const int32_t* idx, const float* alpha, const void* dO, float* dQ, float* dK,
+                 float* dV, float* dalpha, float* O, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+
 const char* sla_status_string(int status);
 /* hipError_t of the most recent SLA_ERR_HIP on the calling thread (0 if none). */
 int sla_last_hip_error(void);

@@ -164,6 +164,24 @@ def test_branch_drop_checks(L):
     assert L.sla_forward_ex(ctypes.byref(p), *small, ctypes.byref(o)) == sla.SLA_ERR_WORKSPACE
 
 
+def test_backward_checks(L):
+    p = P()
+    wb = L.sla_backward_workspace_bytes(ctypes.byref(p))
+    assert wb > 0 and L.sla_backward_workspace_bytes(ctypes.byref(P(H=4))) > wb
+    assert L.sla_backward_workspace_bytes(ctypes.byref(P(d=96))) == 0
+    f = L.sla_backward
+    args = [FAKE] * 10 + [None, FAKE, wb, None]  # Q K V idx alpha dO dQ dK dV dalpha O ws bytes stream
+    assert f(ctypes.byref(P(d=64)), *args) == sla.SLA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(P(dtype=sla.SLA_F32)), *args) == sla.SLA_ERR_UNSUPPORTED
+    for i in range(10):
+        bad = list(args)
+        bad[i] = None
+        assert f(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID, i
+    short = list(args)
+    short[12] = wb - 1
+    assert f(ctypes.byref(p), *short) == sla.SLA_ERR_WORKSPACE
+
+
 def test_status_strings(L):
     for st in (0, -1, -2, -3, -4):
         assert L.sla_status_string(st).decode()
