@@ -47,6 +47,9 @@ def parse():
                     help="video_s | video_l | video_l_fp8 | pisa_video_s | pisa_video_l")
     ap.add_argument("--linear-mode", default="mask_product", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="the training step: route + sla_backward (forward recomputed inside, then "
+                         "the gradients of Q, K, V and alpha)")
     ap.add_argument("--int8", action="store_true",
                     help="the INT8 sparse branch (mask-product linear mode) on the workload's tensors")
     ap.add_argument("--drop-tau", type=float, default=None,
@@ -355,6 +358,96 @@ def bench_pisa(a, wl):
     print(json.dumps(rec), flush=True)
 
 
+def bench_backward(a, wl):
+    """One step = sla.route + sla.backward: the forward recomputed in the mask-product mode, then
+    dQ, dK, dV and dalpha for a fixed dO."""
+    import numpy as np
+    import torch
+
+    import block_sparse_linear_02_amd as sla
+    import gen
+
+    dev = torch.device("cuda:0")
+    inputs = gen.draw(wl, 0)
+    Q, K, V, alpha = (inputs[k].to(dev) for k in ("Q", "K", "V", "alpha"))
+    Wq, Wk = inputs["Wq"].to(dev), inputs["Wk"].to(dev)
+    B, H, N, d = Q.shape
+    nb = wl.n_blocks
+    dO = torch.from_numpy(np.random.default_rng(77).standard_normal((B, H, N, d)).astype(np.float32)).to(
+        torch.bfloat16).to(dev)
+    idx = torch.empty((B, H, nb, wl.topk), dtype=torch.int32, device=dev)
+    ws_r = torch.empty(sla.route_workspace_bytes(Q, wl.topk), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(sla.lib().sla_backward_workspace_bytes(__import__("ctypes").byref(sla.make_problem(
+        B, H, N, d, wl.topk, Q.dtype))), dtype=torch.uint8, device=dev)
+    grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3)) + (
+        torch.empty((B, H, N), dtype=torch.float32, device=dev),)
+    ev_t, ev_b = events(a.steps), events(a.steps)
+    for e in ev_t + ev_b:
+        e[0].record()
+        e[1].record()
+    torch.cuda.synchronize()
+
+    def step(i=None):
+        if i is not None:
+            ev_t[i][0].record()
+        sla.route(Q, K, Wq, Wk, wl.topk, workspace=ws_r, idx_out=idx)
+        if i is not None:
+            ev_b[i][0].record()
+        sla.backward(Q, K, V, idx, alpha, dO, workspace=ws_b, out=grads)
+        if i is not None:
+            ev_b[i][1].record()
+            ev_t[i][1].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / a.steps
+    sp = sparse_flops(idx, N, d)  # the forward's sparse FLOPs (QK^T and PV over the kept pairs)
+    # attention training step by the usual count: forward 2 products + backward 5 (S again, dP,
+    # dV, dQ, dK) per kept tile, i.e. 3.5 x the forward's sparse FLOPs; the kernels execute 10
+    # products (S in the forward, in the dQ kernel and in both roles of the dK/dV kernel; PV; dP
+    # in both backward kernels; dQ, dV, dK), i.e. 5 x
+    algo, executed = 3.5 * sp, 5.0 * sp
+    bwd_ms = avg_ms(ev_b)
+    rec = {
+        "metric": "SLA2 attention training step (forward + backward) ms/call + effective TFLOPS",
+        "value": algo / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective: 3.5 x sparse forward FLOPs / step time)",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded clustered video-DiT-shaped tensors, random projections, dO ~ N(0, 1))",
+        "config": {
+            "workload": f"{wl.name}: B={B} H={H} N={N} d={d} block=64 topk={wl.topk} of {nb}, "
+                        f"route + backward (forward recomputed, mask-product linear mode)",
+            "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": wl.topk,
+        },
+        "step_ms_events": quantiles(ev_t),
+        "kernels_ms": {"backward_call": bwd_ms, "route_and_other": ms - bwd_ms},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "sla_backward (all kernels)",
+            "achieved": algo / (bwd_ms * 1e-3) / 1e12,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": algo / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "flops_per_launch": algo,
+            "mfma_flops_executed_per_launch": executed,
+        },
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def mass_covered(inputs, wl, idx_np, blocks):
     """Diagnostic (not pass/fail): the share of each query row's full softmax attention mass
     that falls on the tokens of its query block's kept blocks, for a few query blocks of head
@@ -416,6 +509,9 @@ def main():
     wl = gen.workload(a.workload)
     if wl.name.startswith("pisa"):
         bench_pisa(a, wl)
+        return
+    if a.backward:
+        bench_backward(a, wl)
         return
     if wl.fp8 and a.linear_mode == "literal":
         a.linear_mode = "fused"  # the fp8 path has the fused and mask-product linear modes

@@ -26,7 +26,8 @@
 //   bwd_dkv_kernel   key-major, one key block per workgroup over the query blocks that keep it
 //                    (Q and dO_s tiles, lse2 and D rows staged in LDS, double-buffered):
 //                    wavefronts 0-1 accumulate dV^T += dO_s^T P for 32 keys each, wavefronts 2-3
-//                    dK^T += Q^T dS; epilogue: the linear branch's dV and dK from dh_j^T, dz_j.
+//                    dK^T += Q^T dS (with dP = dO_s V^T), one 32-row query half of a tile at a
+//                    time; epilogue: the linear branch's dV and dK from dh_j^T and dz_j.
 // bf16 Q, K, V, dO with d = 128; gradients in fp32.
 #include <type_traits>
 
@@ -50,60 +51,67 @@ __global__ __launch_bounds__(kBwdThreads) void prep_kernel(
     int N, int nb, float* __restrict__ dalpha, __bf16* __restrict__ dOs, float* __restrict__ Dr,
     __bf16* __restrict__ G, float* __restrict__ e_out, float* __restrict__ dzeta) {
   constexpr int D = kBwdD;
-  constexpr int CPT = D / 4;  // channels per thread: four threads per row
-  __shared__ float red[kBlock][D + 1];
+  constexpr int TPR = D / 8;                 // threads per row: 8 channels (16 bytes of bf16) each
+  constexpr int RPP = kBwdThreads / TPR;     // rows per pass
+  __shared__ float red[RPP][D];
   const int tid = threadIdx.x;
-  const int r = tid / 4, part = tid % 4;
+  const int ch = (tid % TPR) * 8, rg = tid / TPR;
   const int i = blockIdx.x, bh = blockIdx.y;
-  const int row = i * kBlock + r;
-  const bool ok = row < N;
-  const size_t ro = ((size_t)bh * N + (ok ? row : 0)) * D + part * CPT;
-  float da = 0.f, dd = 0.f, ee = 0.f;
-  float q[CPT];
-  const float a = ok ? alpha[(size_t)bh * N + row] : 0.f;
-  const float rd = ok ? rden[(size_t)bh * N + row] : 0.f;
-  float gv[CPT];
+  float zacc[8];
 #pragma unroll
-  for (int u = 0; u < CPT / 8; ++u) {
-    const bf16x8 o8 = ok ? *reinterpret_cast<const bf16x8*>(dO + ro + 8 * u) : bf16x8{};
-    const bf16x8 q8 = ok ? *reinterpret_cast<const bf16x8*>(Q + ro + 8 * u) : bf16x8{};
+  for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
+  for (int pass = 0; pass < kBlock / RPP; ++pass) {
+    const int row = i * kBlock + pass * RPP + rg;
+    const bool ok = row < N;
+    const size_t ro = ((size_t)bh * N + (ok ? row : 0)) * D + ch;
+    const bf16x8 o8 = ok ? *reinterpret_cast<const bf16x8*>(dO + ro) : bf16x8{};
+    const bf16x8 q8 = ok ? *reinterpret_cast<const bf16x8*>(Q + ro) : bf16x8{};
+    const f32x4 os0 = ok ? *reinterpret_cast<const f32x4*>(Os + ro) : f32x4{};
+    const f32x4 os1 = ok ? *reinterpret_cast<const f32x4*>(Os + ro + 4) : f32x4{};
+    const f32x4 ol0 = ok ? *reinterpret_cast<const f32x4*>(Ol + ro) : f32x4{};
+    const f32x4 ol1 = ok ? *reinterpret_cast<const f32x4*>(Ol + ro + 4) : f32x4{};
+    const float a = ok ? alpha[(size_t)bh * N + row] : 0.f;
+    const float rd = ok ? rden[(size_t)bh * N + row] : 0.f;
+    float da = 0.f, dd = 0.f, ee = 0.f;
     bf16x8 s8, g8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int c = 8 * u + e;
       const float o = bf2f(o8[e]);
-      const float os = ok ? Os[ro + c] : 0.f, ol = ok ? Ol[ro + c] : 0.f;
+      const float os = e < 4 ? os0[e] : os1[e - 4], ol = e < 4 ? ol0[e] : ol1[e - 4];
       da = fmaf(o, os - ol, da);
       s8[e] = f2bf(a * o);
       dd = fmaf(bf2f(s8[e]), os, dd);
       g8[e] = f2bf((1.f - a) * o * rd);
-      gv[c] = bf2f(g8[e]);
-      ee = fmaf(gv[c], ol, ee);
-      q[c] = fmaxf(bf2f(q8[e]), 0.f);
+      ee = fmaf(bf2f(g8[e]), ol, ee);
     }
     if (ok) {
-      *reinterpret_cast<bf16x8*>(dOs + ro + 8 * u) = s8;
-      *reinterpret_cast<bf16x8*>(G + ro + 8 * u) = g8;
+      *reinterpret_cast<bf16x8*>(dOs + ro) = s8;
+      *reinterpret_cast<bf16x8*>(G + ro) = g8;
     }
-  }
+    // row sums over the TPR consecutive lanes of the row
 #pragma unroll
-  for (int o = 1; o < 4; o <<= 1) {
-    da += __shfl_xor(da, o);
-    dd += __shfl_xor(dd, o);
-    ee += __shfl_xor(ee, o);
-  }
-  const float e = -ee;  // rows past N: 0
-  if (ok && part == 0) {
-    dalpha[(size_t)bh * N + row] = da;
-    Dr[(size_t)bh * N + row] = dd;
-    e_out[(size_t)bh * N + row] = e;
-  }
+    for (int o = 1; o < TPR; o <<= 1) {
+      da += __shfl_xor(da, o);
+      dd += __shfl_xor(dd, o);
+      ee += __shfl_xor(ee, o);
+    }
+    const float e = -ee;  // rows past N: 0
+    if (ok && tid % TPR == 0) {
+      dalpha[(size_t)bh * N + row] = da;
+      Dr[(size_t)bh * N + row] = dd;
+      e_out[(size_t)bh * N + row] = e;
+    }
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) red[r][part * CPT + c] = e * q[c];
+    for (int k = 0; k < 8; ++k) zacc[k] = fmaf(e, fmaxf(bf2f(q8[k]), 0.f), zacc[k]);
+  }
+  // dzeta_i: the RPP row groups' partial sums through LDS, in a fixed order
+#pragma unroll
+  for (int k = 0; k < 8; ++k) red[rg][ch + k] = zacc[k];
   __syncthreads();
   if (tid < D) {
     float s = 0.f;
-    for (int rr = 0; rr < kBlock; ++rr) s += red[rr][tid];
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) s += red[r][tid];
     dzeta[((size_t)bh * nb + i) * D + tid] = s;
   }
 }
@@ -429,6 +437,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 
 // ---------------------------------------------------------------------------------- dK, dV
 
+// One key block per workgroup.  Wavefronts 0-1 accumulate dV for keys 32 (w % 2) .. + 31 (the B
+// operand, one key per lane), wavefronts 2-3 dK for the same keys; every tile is taken one
+// 32-row query half at a time, so only one half's S, dP and P or dS are live at once.
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const uint32_t* __restrict__ kept_t, const __bf16* __restrict__ dOs,
@@ -542,62 +553,42 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(
     if (t + 1 < nq) stage(t + 1, std::integral_constant<int, 1 - BUF>{});
     const __bf16* Qs = buf(BUFC);
     const __bf16* Os_t = Qs + TILE;
-    // lse2 and D of the 16 query rows a lane holds per half: rows 32 qt + 8 r + 4 g + 0..3
-    const float* lr = rl[BUF][0];
-    const float* dr = rl[BUF][1];
-    if (!dk_role) {
-      // S[query][key] (query halves qt): A = Q rows, B = this wavefront's keys
-      f32x16 s[2];
+    const __bf16* At = dk_role ? Qs : Os_t;  // transposed A operand of the accumulation
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) s[qt] = f32x16{};
-#pragma unroll
-      for (int k = 0; k < NS; ++k)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[qt] = mfma32(rd_row(Qs, 32 * qt, k), kr[k], s[qt]);
-      // dV^T += dO_s^T P: P of register i in half qt (query 32 qt + 8 (i / 4) + 4 g + i % 4)
-      bf16x8 pb[4];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lr + 32 * qt + 8 * r + 4 * g);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * r + e;
-            pb[2 * qt + i / 8][i % 8] = f2bf(fast_exp2(fmaf(s[qt][i], c_log2, -l4[e])));
-          }
-        }
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[c] = mfma32(rd_tr(Os_t, 16 * u, 32 * c), pb[u], acc[c]);
-    } else {
-      // per query half: S, dP[query][key] = dO_s . V, dS = P (dP - D); then dK^T += Q^T dS
-      bf16x8 db[4];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int qt = 0; qt < 2; ++qt) {
+      // S[query][key] of query rows 32 qt .. (A = Q rows, B = this wavefront's keys); the dK
+      // wavefronts also dP[query][key] = dO_s . V
+      f32x16 s = f32x16{}, dp = f32x16{};
+      if (dk_role) {
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
           s = mfma32(rd_row(Qs, 32 * qt, k), kr[k], s);
           dp = mfma32(rd_row(Os_t, 32 * qt, k), vr[k], dp);
         }
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lr + 32 * qt + 8 * r + 4 * g);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dr + 32 * qt + 8 * r + 4 * g);
+        for (int k = 0; k < NS; ++k) s = mfma32(rd_row(Qs, 32 * qt, k), kr[k], s);
+      }
+      // register i <-> query 32 qt + 8 (i / 4) + 4 g + i % 4; lse2 and D of those rows
+      const float* lr = rl[BUF][0] + 32 * qt;
+      const float* dr = rl[BUF][1] + 32 * qt;
+      bf16x8 pb[2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * r + e;
-            const float p = fast_exp2(fmaf(s[i], c_log2, -l4[e]));
-            db[2 * qt + i / 8][i % 8] = f2bf(p * (dp[i] - d4[e]));
-          }
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lr + 8 * r + 4 * g);
+        const f32x4 d4 = dk_role ? *reinterpret_cast<const f32x4*>(dr + 8 * r + 4 * g) : f32x4{};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * r + e;
+          const float p = fast_exp2(fmaf(s[i], c_log2, -l4[e]));
+          pb[i / 8][i % 8] = f2bf(dk_role ? p * (dp[i] - d4[e]) : p);
         }
       }
+      // dV^T += dO_s^T P or dK^T += Q^T dS: the A operand read transposed from rows 32 qt + 16 u
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[c] = mfma32(rd_tr(Qs, 16 * u, 32 * c), db[u], acc[c]);
+        for (int u = 0; u < 2; ++u) acc[c] = mfma32(rd_tr(At, 32 * qt + 16 * u, 32 * c), pb[u], acc[c]);
     }
     nv_cur = nv_next;
     wait_vmem();
@@ -614,7 +605,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(
     if (t < nq) step(t, B0{});
   }
 
-  // ---- linear branch: dh_j^T [c][c'] into buffer 0 (free since the last step's barrier) ----
+  // ---- linear branch: dh_j^T [c][c'] into buffer 0 (free since the last step's barrier).
+  // Every lane takes part in the MFMAs below (they read operands from all 64 lanes); keys past
+  // N hold zeros and store nothing ----
   {
     const __bf16* th = dh_g + ((size_t)bh * nb + j) * D * D;
 #pragma unroll
@@ -624,9 +617,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(
   wait_vmem();
   __syncthreads();
   launder();
-  // every lane takes part in the MFMAs below (they read operands from all 64 lanes); keys past
-  // N hold zeros and store nothing
-  const float* dzr = dz + ((size_t)bh * nb + j) * D;
   if (!dk_role) {
     // dV^T[c][key] += sum_c' dh^T[c][c'] relu(K)[key][c']: row reads of dh^T, relu(K) as B
 #pragma unroll
@@ -662,6 +652,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(
       for (int c = 0; c < NC; ++c) dl[c] = mfma32(rd_tr(lb0, 16 * u, 32 * c), vb, dl[c]);
     }
     if (!key_ok) return;
+    const float* dzr = dz + ((size_t)bh * nb + j) * D;
     const __bf16* krw = K + hoff + (size_t)key * D;
     float* o = dK + hoff + (size_t)key * D;
 #pragma unroll
