@@ -13,6 +13,10 @@ Sources (cited by page title and section; the summaries number their sections th
 * "PISA - Piecewise Sparse Attention per Efficient Diffusion Transformers" - Italian technical
   summary (gist.science/it/paper/2602.01077), section 2 (exact-or-approximate forward,
   covariance-aware routing): ``pisa.py``.
+* "Training-Free Sparse Attention for Fast Video Generation via Offline Layer-Wise Sparsity
+  Profiling and Online Bidirectional Co-Clustering" (SVOO) - Italian summary
+  (gist.science/it/paper/2603.18636), section 2.B (online bidirectional co-clustering):
+  ``svoo.py``.
 * "SALAD: Achieve High-Sparsity Attention via Efficient Linear Attention Tuning for Video
   Diffusion Transformer" (gist.science/it/paper/2601.16515), section 2 (ReLU kernel function,
   linear branch sharing Q, K, V with the sparse branch).
@@ -58,3 +62,11 @@ from .int8 import (  # noqa: F401
     forward_int8,
 )
 from .train import backward_head, backward  # noqa: F401
+from .svoo import (  # noqa: F401
+    svoo_assign,
+    svoo_centroids,
+    svoo_cocluster_head,
+    svoo_cocluster,
+    svoo_order,
+    svoo_forward,
+)

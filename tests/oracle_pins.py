@@ -728,4 +728,129 @@ def pin_pisa_route_minimises_error_bound(orc):
         assert tuple(rp["idx"][i]) == top, (i, rp["idx"][i], top)
 
 
+
+# ---------------------------------------------------------------------------------------- SVOO
+
+
+def _svoo_planted(seed, pi, n_b=8, blk=8, d=16, scale=4.0, noise=0.05, misplaced=2):
+    """Queries and keys in n_b blocks of blk tokens along orthonormal directions e_0..e_{n_b-1}:
+    query block c holds blk - misplaced tokens of direction pi[c], key block c of direction c,
+    and each block's remaining tokens take other directions so that every direction has blk
+    tokens in all.  Returns (Q, K, query directions, key directions)."""
+    rng = np.random.default_rng(seed)
+
+    def dirs(major):
+        lab = np.repeat(major, blk)
+        # swap `misplaced` tokens of each block with tokens of the next block (cyclically), so
+        # direction counts stay blk each and every block keeps its majority
+        for c in range(n_b):
+            nxt = (c + 1) % n_b
+            for m in range(misplaced):
+                a, b = c * blk + m, nxt * blk + blk - 1 - m
+                lab[a], lab[b] = lab[b], lab[a]
+        return lab
+
+    dq = dirs(np.asarray(pi))
+    dk = dirs(np.arange(n_b))
+    E = np.eye(d)[:n_b]
+    Q = scale * E[dq] + noise * rng.standard_normal((n_b * blk, d))
+    K = scale * E[dk] + noise * rng.standard_normal((n_b * blk, d))
+    return Q, K, dq, dk
+
+
+def pin_svoo_recovers_planted_coclusters(orc):
+    """Planted co-clusters: query block c mostly of direction pi(c), key block c mostly of
+    direction c, a quarter of each block misplaced.  A key of direction a has its largest
+    affinity with the query centroid whose block looks for a, cluster pi^-1(a); the queries then
+    follow the key centroids.  So every token lands in cluster pi^-1(its direction), from the
+    first iteration on, and the stable order lists each cluster's tokens in their original order
+    (a non-identity pi separates the query-driven key step from a key-only clustering)."""
+    pi = np.array([3, 0, 6, 1, 7, 2, 5, 4])
+    inv = np.argsort(pi)
+    Q, K, dq, dk = _svoo_planted(211, pi)
+    for iters in (1, 3):
+        qa, ka = orc.svoo_cocluster_head(Q, K, iters, block=8)
+        np.testing.assert_array_equal(qa, inv[dq], err_msg=f"queries, {iters} iterations")
+        np.testing.assert_array_equal(ka, inv[dk], err_msg=f"keys, {iters} iterations")
+    order = orc.svoo_order(qa)
+    want = np.concatenate([np.flatnonzero(inv[dq] == c) for c in range(8)])
+    np.testing.assert_array_equal(order, want)
+
+
+def pin_svoo_fixed_point_on_coclustered_input(orc):
+    """Input already co-clustered (block c of Q and K both of direction c): every token stays in
+    its block's cluster, both permutations are the identity, and the forward on the permuted
+    sequence is the plain forward."""
+    n_b, blk = 8, 8
+    E = np.eye(16)[:n_b]
+    rng = np.random.default_rng(212)
+    lab = np.repeat(np.arange(n_b), blk)
+    Q = 4.0 * E[lab] + 0.05 * rng.standard_normal((n_b * blk, 16))
+    K = 4.0 * E[lab] + 0.05 * rng.standard_normal((n_b * blk, 16))
+    qa, ka = orc.svoo_cocluster_head(Q, K, 2, block=blk)
+    np.testing.assert_array_equal(qa, lab)
+    np.testing.assert_array_equal(ka, lab)
+    np.testing.assert_array_equal(orc.svoo_order(qa), np.arange(n_b * blk))
+    V = rng.standard_normal((1, 1, n_b * blk, 16))
+    alpha = rng.uniform(0, 1, (1, 1, n_b * blk))
+    W = rng.standard_normal((16, 16)) / 4
+    ident = np.arange(n_b * blk)[None, None]
+    O, idx = orc.svoo_forward(Q[None, None], K[None, None], V, W, W.T, alpha, 3, ident, ident, blk)
+    ref_idx = orc.route(Q[None, None], K[None, None], W, W.T, 3, blk)["idx"]
+    np.testing.assert_array_equal(idx, ref_idx)
+    np.testing.assert_allclose(O, orc.forward(Q[None, None], K[None, None], V, ref_idx, alpha, blk)[0],
+                               rtol=0, atol=0)
+
+
+def pin_svoo_assign_and_centroid_worked_example(orc):
+    """Hand-computed: rows [1, 0], [1, 3], [2, 0] against centroids [1, 0], [1, 0], [0, 1] have
+    affinities [1, 1, 0], [1, 1, 3], [2, 2, 0]: clusters 0 (a tie of 0 and 1 goes to the lower
+    index), 2, 0 with leads 0, 2, 0.  Cluster 0's members average to [1.5, 0], cluster 1 is
+    empty and keeps its previous centroid, cluster 2's one member is its mean."""
+    X = np.array([[1.0, 0.0], [1.0, 3.0], [2.0, 0.0]])
+    cent = np.array([[1.0, 0.0], [1.0, 0.0], [0.0, 1.0]])
+    a, lead = orc.svoo_assign(X, cent)
+    np.testing.assert_array_equal(a, [0, 2, 0])
+    np.testing.assert_allclose(lead, [0.0, 2.0, 0.0], rtol=0, atol=0)
+    prev = np.array([[9.0, 9.0], [7.0, -7.0], [5.0, 5.0]])
+    c = orc.svoo_centroids(X, a, prev)
+    np.testing.assert_allclose(c, [[1.5, 0.0], [7.0, -7.0], [1.0, 3.0]], rtol=0, atol=0)
+
+
+def pin_svoo_order_is_counting_sort(orc):
+    """The permutation equals a counting sort written out: clusters in index order, each
+    cluster's tokens in their original order (many equal keys, long enough that an unstable
+    sort reorders them)."""
+    rng = np.random.default_rng(213)
+    a = rng.integers(0, 5, (2, 300))
+    got = orc.svoo_order(a)
+    for r in range(2):
+        want = [t for c in range(5) for t in range(300) if a[r, t] == c]
+        np.testing.assert_array_equal(got[r], want)
+
+
+def pin_svoo_forward_permutation_invariant_limits(orc):
+    """Random permutations of queries and keys: with every block kept the linear branch is empty
+    and the output is alpha times full softmax attention of the unpermuted inputs; with none
+    kept it is (1 - alpha) times global ReLU linear attention.  Both limits ignore the blocking,
+    so only a correct gather of Q, alpha, K, V and scatter of O reproduce them."""
+    rng = np.random.default_rng(214)
+    N, d, blk = 90, 8, 16
+    n_b = -(-N // blk)
+    Q, K, V = (rng.standard_normal((1, 2, N, d)) for _ in range(3))
+    alpha = rng.uniform(0.1, 0.9, (1, 2, N))
+    W = rng.standard_normal((d, d)) / math.sqrt(d)
+    pq = np.stack([rng.permutation(N) for _ in range(2)])[None]
+    pk = np.stack([rng.permutation(N) for _ in range(2)])[None]
+    x = Q @ np.swapaxes(K, -1, -2) / math.sqrt(d)
+    p = np.exp(x - x.max(axis=-1, keepdims=True))
+    full = (p / p.sum(axis=-1, keepdims=True)) @ V
+    O, _ = orc.svoo_forward(Q, K, V, W, W, alpha, n_b, pq, pk, blk)
+    np.testing.assert_allclose(O, alpha[..., None] * full, rtol=1e-10, atol=1e-12)
+    rq, rk = np.maximum(Q, 0), np.maximum(K, 0)
+    lin = (rq @ (np.swapaxes(rk, -1, -2) @ V)) / (rq @ rk.sum(axis=-2)[..., None])
+    O, _ = orc.svoo_forward(Q, K, V, W, W, alpha, 0, pq, pk, blk)
+    np.testing.assert_allclose(O, (1 - alpha[..., None]) * lin, rtol=1e-10, atol=1e-12)
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -60,6 +60,15 @@ MUTATIONS = {
     "pisa_kept_also_approximated": ("pisa.py", "uns = np.flatnonzero(~keep)", "uns = np.arange(n_b)"),
     "pisa_no_centroid_scale": ("pisa.py", "y = q @ kbar[uns].T", "y = Q[a:b] @ kbar[uns].T"),
     "pisa_route_unscaled": ("pisa.py", "s = (qbar @ st[\"centroid\"].T) / np.sqrt(Q.shape[1])", "s = qbar @ st[\"centroid\"].T"),
+    "svoo_argmin": ("svoo.py", "assign = np.argmax(aff, axis=1)", "assign = np.argmin(aff, axis=1)"),
+    "svoo_keys_by_key_centroids": ("svoo.py", "k_assign, k_margin = svoo_assign(K, q_cent)", "k_assign, k_margin = svoo_assign(K, k_cent)"),
+    "svoo_queries_by_stale_key_centroids": ("svoo.py", "q_assign, q_margin = svoo_assign(Q, k_cent)", "q_assign, q_margin = svoo_assign(Q, pool_blocks(K, block))"),
+    "svoo_empty_cluster_zeroed": ("svoo.py", "out = np.array(_f64(prev), copy=True)", "out = np.zeros_like(_f64(prev))"),
+    "svoo_centroid_sum_not_mean": ("svoo.py", "out[c] = members.sum(axis=0) / len(members)", "out[c] = members.sum(axis=0)"),
+    "svoo_unstable_order": ("svoo.py", 'axis=-1, kind="stable")', 'axis=-1, kind="quicksort")'),
+    "svoo_scatter_as_gather": ("svoo.py", "np.put_along_axis(O, pq[..., None], Op, axis=2)", "O = np.take_along_axis(Op, pq[..., None], axis=2)"),
+    "svoo_alpha_unpermuted": ("svoo.py", "ap = np.take_along_axis(alpha, pq, axis=2)", "ap = alpha"),
+    "svoo_v_by_query_perm": ("svoo.py", "Vp = np.take_along_axis(V, pk[..., None], axis=2)", "Vp = np.take_along_axis(V, pq[..., None], axis=2)"),
     "fp8_tile_scale_dropped": ("fp8.py", "num += (enc(p / sP) * sP) @ Vd[starts[j]:ends[j]]", "num += enc(p / sP) @ Vd[starts[j]:ends[j]]"),
 }
 
