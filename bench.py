@@ -44,12 +44,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video_s",
-                    help="video_s | video_l | video_l_fp8 | pisa_video_s | pisa_video_l")
+                    help="video_s | video_l | video_l_fp8 | pisa_video_s | pisa_video_l | svoo_video_s")
     ap.add_argument("--linear-mode", default="mask_product", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="the training step: route + sla_backward (forward recomputed inside, then "
                          "the gradients of Q, K, V and alpha)")
+    ap.add_argument("--svoo-iters", type=int, default=3, help="co-clustering iterations (svoo workloads)")
+    ap.add_argument("--svoo-reuse", type=int, default=20,
+                    help="steps that reuse one co-clustering (svoo workloads)")
     ap.add_argument("--int8", action="store_true",
                     help="the INT8 sparse branch (mask-product linear mode) on the workload's tensors")
     ap.add_argument("--drop-tau", type=float, default=None,
@@ -448,6 +451,173 @@ def bench_backward(a, wl):
     print(json.dumps(rec), flush=True)
 
 
+def svoo_cpu_baseline(inputs, wl, iters, reuse, budget_s=15.0):
+    """The SVOO oracle on a bounded sample: the co-clustering of head 0 (charged once per `reuse`
+    steps), its gathers, router and block states, then its forward on a random subset of query
+    blocks until about `budget_s` of CPU time; scaled to the whole workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+
+    nb = wl.n_blocks
+    Q, K, V, alpha = (inputs[n][0, 0] for n in ("Q", "K", "V", "alpha"))
+    t0 = time.perf_counter()
+    qa, ka = oracle.svoo_cocluster_head(Q, K, iters, 64)
+    t_cluster = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    pq, pk = oracle.svoo_order(qa), oracle.svoo_order(ka)
+    Qp, Kp, Vp = (x.double().numpy() for x in (Q, K, V))
+    Qp, Kp, Vp, ap = Qp[pq], Kp[pk], Vp[pk], alpha.double().numpy()[pq]
+    r = oracle.route(Qp[None, None], Kp[None, None], inputs["Wq"].double(), inputs["Wk"].double(), wl.topk, 64)
+    states = oracle.block_states(Kp, Vp, 64)
+    t_fixed = time.perf_counter() - t0
+    order = np.random.default_rng(0).permutation(nb)
+    done, t_fwd = 0, 0.0
+    while done < nb and t_cluster + t_fixed + t_fwd < budget_s:
+        t0 = time.perf_counter()
+        oracle.forward_head(Qp, Kp, Vp, r["idx"][0, 0], ap, 64, q_blocks=order[done : done + 8], states=states)
+        t_fwd += time.perf_counter() - t0
+        done += len(order[done : done + 8])
+    per_head = t_cluster / reuse + t_fixed + t_fwd * nb / max(done, 1)
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    return {
+        "seconds_per_call": wl.B * wl.H * per_head,
+        "cores": threads,
+        "sample": f"head 0 of {wl.B * wl.H}: co-clustering ({iters} iterations, {t_cluster:.1f} s, charged 1/{reuse} "
+                  f"per step), gathers, router, states and {done} of {nb} query blocks' forward; scaled to "
+                  f"{wl.B * wl.H} heads",
+    }
+
+
+def bench_svoo(a, wl):
+    """One step = the SLA2 path on co-clustered blocks (gather Q, K, V, alpha; route; forward in
+    the mask-product mode; scatter O), with the co-clustering itself run on every `reuse`-th step
+    (the clusters are reused over that many diffusion steps)."""
+    import torch
+
+    import block_sparse_linear_02_amd as sla
+    import gen
+
+    iters, reuse = a.svoo_iters, a.svoo_reuse
+    dev = torch.device("cuda:0")
+    inputs = gen.draw(wl, 0)
+    Q, K, V, alpha = (inputs[n].to(dev) for n in ("Q", "K", "V", "alpha"))
+    Wq, Wk = inputs["Wq"].to(dev), inputs["Wk"].to(dev)
+    B, H, N, d = Q.shape
+    nb, k = wl.n_blocks, wl.topk
+    pq, pk, qa, ka = sla.svoo_cluster(Q, K, iters)
+    ws_c = torch.empty(sla.svoo_workspace_bytes(Q), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(sla.route_workspace_bytes(Q, k), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(sla.forward_workspace_bytes(Q, k, 3), dtype=torch.uint8, device=dev)
+    Qp, Kp, Vp = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    ap = torch.empty_like(alpha)
+    idx = torch.empty((B, H, nb, k), dtype=torch.int32, device=dev)
+    Op = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    O = torch.empty_like(Op)
+    n_cl = (a.steps + reuse - 1) // reuse
+    ev_t, ev_c, ev_g, ev_r, ev_f, ev_s, ev_sp = (events(n) for n in (a.steps, n_cl, a.steps, a.steps, a.steps,
+                                                                       a.steps, a.steps))
+    for e in ev_t + ev_c + ev_g + ev_r + ev_f + ev_s + ev_sp:
+        e[0].record()
+        e[1].record()
+    torch.cuda.synchronize()
+
+    def step(i=None):
+        rec = (lambda evs, j, n=i: evs[n][j].record()) if i is not None else (lambda evs, j: None)
+        rec(ev_t, 0)
+        if i is None or i % reuse == 0:
+            if i is not None:
+                ev_c[i // reuse][0].record()
+            sla.svoo_cluster(Q, K, iters, workspace=ws_c, out=(pq, pk, qa, ka))
+            if i is not None:
+                ev_c[i // reuse][1].record()
+        rec(ev_g, 0)
+        sla.svoo_gather(Q, pq, out=Qp)
+        sla.svoo_gather(K, pk, out=Kp)
+        sla.svoo_gather(V, pk, out=Vp)
+        sla.svoo_gather(alpha, pq, out=ap)
+        rec(ev_g, 1)
+        rec(ev_r, 0)
+        sla.route(Qp, Kp, Wq, Wk, k, workspace=ws_r, idx_out=idx)
+        rec(ev_r, 1)
+        rec(ev_f, 0)
+        sla.forward(Qp, Kp, Vp, idx, ap, linear_mode="mask_product", workspace=ws_f, out=Op,
+                    events=ev_sp[i] if i is not None else None)
+        rec(ev_f, 1)
+        rec(ev_s, 0)
+        sla.svoo_scatter(Op, pq, out=O)
+        rec(ev_s, 1)
+        rec(ev_t, 1)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / a.steps
+    sp = sparse_flops(idx, N, d)
+    cl_ms, g_ms, r_ms, f_ms, s_ms, sp_ms = (avg_ms(e) for e in (ev_c, ev_g, ev_r, ev_f, ev_s, ev_sp))
+    # co-clustering MFMA work: per iteration two assignments (keys, queries), each N x C x d
+    # products against the centroid's hi and lo halves
+    assign_flops = iters * 2 * 2 * 2.0 * N * nb * d * B * H
+    es = Q.element_size()
+    move_bytes = 2 * (3 * B * H * N * d * es + B * H * N * 4)  # gathers: read + write
+    scat_bytes = 2 * B * H * N * d * 4
+    achieved = sp / (sp_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "sparse-linear attn fwd ms/call + effective TFLOPS on SVOO co-clustered blocks",
+        "value": sp / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective: sparse FLOPs / step time, co-clustering amortised)",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded clustered video-DiT-shaped tensors, random projections)",
+        "config": {
+            "workload": f"{wl.name}: B={B} H={H} N={N} d={d} block=64 topk={k} of {nb}, co-clustering "
+                        f"{iters} iterations into {nb} clusters, reused for {reuse} steps, mask-product mode",
+            "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": k, "iters": iters, "reuse": reuse,
+            "cluster_calls_timed": n_cl,
+        },
+        "step_ms_events": quantiles(ev_t),
+        "kernels_ms": {"cluster_call": cl_ms, "gathers": g_ms, "route": r_ms, "forward": f_ms,
+                       "sparse_kernel": sp_ms, "scatter": s_ms},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "pair_kernel<bf16, 128> (sparse branch, permuted sequence)",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "flops_per_launch": sp,
+        },
+        "cluster": {
+            "assign_mfma_flops_per_call": assign_flops,
+            "cluster_call_tflops": assign_flops / (cl_ms * 1e-3) / 1e12,
+        },
+        "hbm_kernels": {"gathers": hbm(move_bytes, g_ms), "scatter": hbm(scat_bytes, s_ms)},
+    }
+    if not a.no_cpu_baseline:
+        cb = svoo_cpu_baseline(inputs, wl, iters, reuse)
+        rec["cpu_baseline"] = {
+            "value": sp / cb["seconds_per_call"] / 1e12,
+            "unit": "TFLOP/s (effective, same FLOP count)",
+            "ms_per_call": 1e3 * cb["seconds_per_call"],
+            "cores": cb["cores"],
+            "kind": "oracle",
+            "sample": cb["sample"],
+        }
+    print(json.dumps(rec), flush=True)
+
+
 def mass_covered(inputs, wl, idx_np, blocks):
     """Diagnostic (not pass/fail): the share of each query row's full softmax attention mass
     that falls on the tokens of its query block's kept blocks, for a few query blocks of head
@@ -512,6 +682,9 @@ def main():
         return
     if a.backward:
         bench_backward(a, wl)
+        return
+    if wl.name.startswith("svoo"):
+        bench_svoo(a, wl)
         return
     if wl.fp8 and a.linear_mode == "literal":
         a.linear_mode = "fused"  # the fp8 path has the fused and mask-product linear modes

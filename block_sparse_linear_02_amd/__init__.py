@@ -17,6 +17,11 @@ PISA exact-or-approximate attention (C ABI in include/sla_pisa.h):
     idx, mask, scores = pisa_route(Q, st, topk, covariance=True)
     O = pisa_forward(Q, K, V, st, idx)
 
+SVOO co-clustered blocks (C ABI in include/sla_svoo.h):
+
+    perm_q, perm_k, q_assign, k_assign = svoo_cluster(Q, K, iters=3)
+    O = svoo_forward(Q, K, V, proj_q, proj_k, alpha, topk, perm_q, perm_k)
+
 Shapes: Q, K, V [B, H, N, d] (bf16 or fp32, d in {64, 128}), proj_q / proj_k [d, d] fp32,
 alpha [B, H, N] fp32, idx [B, H, ceil(N/64), topk] int32 ascending, O [B, H, N, d] fp32.
 """
@@ -132,6 +137,13 @@ def lib() -> ctypes.CDLL:
         L.sla_pisa_route.restype = i32
         L.sla_pisa_forward.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
         L.sla_pisa_forward.restype = i32
+        L.sla_svoo_workspace_bytes.argtypes = [P]
+        L.sla_svoo_workspace_bytes.restype = sz
+        L.sla_svoo_cluster.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.sla_svoo_cluster.restype = i32
+        for name in ("sla_svoo_gather", "sla_svoo_scatter"):
+            getattr(L, name).argtypes = [P, vp, i32, vp, vp, vp]
+            getattr(L, name).restype = i32
         L.sla_status_string.argtypes = [i32]
         L.sla_status_string.restype = ctypes.c_char_p
         L.sla_last_hip_error.argtypes = []
@@ -382,3 +394,67 @@ def pisa_forward(Q, K, V, stats: PisaStats, idx, out=None):
     if st != SLA_OK:
         raise SLAError(st, "sla_pisa_forward")
     return O
+
+
+def svoo_workspace_bytes(Q) -> int:
+    return lib().sla_svoo_workspace_bytes(ctypes.byref(_problem(Q, 0)))
+
+
+def svoo_cluster(Q, K, iters: int = 3, workspace=None, out=None):
+    """SVOO co-clustering of queries and keys (bf16, d = 128): returns (perm_q, perm_k, q_assign,
+    k_assign), all [B, H, N] int32; perm maps a position of the cluster-sorted sequence to the
+    original token."""
+    _check_qkv(Q, K)
+    Q, K = Q.contiguous(), K.contiguous()
+    B, H, N, d = Q.shape
+    p = _problem(Q, 0)
+    need = lib().sla_svoo_workspace_bytes(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    if out is None:
+        out = tuple(torch.empty((B, H, N), dtype=torch.int32, device=Q.device) for _ in range(4))
+    pq, pk, qa, ka = out
+    st = lib().sla_svoo_cluster(ctypes.byref(p), _ptr(Q), _ptr(K), int(iters), _ptr(qa), _ptr(ka), _ptr(pq),
+                                _ptr(pk), _ptr(ws), ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_svoo_cluster")
+    return pq, pk, qa, ka
+
+
+def _permute(X, perm, out, scatter):
+    if X.device.type != "cuda" or X.dim() < 3:
+        raise ValueError("X must be a GPU tensor [B, H, N, ...]")
+    X = X.contiguous()
+    B, H, N = X.shape[:3]
+    perm = perm.contiguous().to(torch.int32)
+    if tuple(perm.shape) != (B, H, N):
+        raise ValueError("perm must be [B, H, N]")
+    row_bytes = X.element_size() * (X.numel() // max(B * H * N, 1))
+    Y = out if out is not None else torch.empty_like(X)
+    p = make_problem(B, H, N, 128, 0, torch.bfloat16)
+    fn = lib().sla_svoo_scatter if scatter else lib().sla_svoo_gather
+    st = fn(ctypes.byref(p), _ptr(X), int(row_bytes), _ptr(perm), _ptr(Y), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_svoo_scatter" if scatter else "sla_svoo_gather")
+    return Y
+
+
+def svoo_gather(X, perm, out=None):
+    """Y[b, h, p] = X[b, h, perm[b, h, p]] for the rows of X [B, H, N, ...]."""
+    return _permute(X, perm, out, 0)
+
+
+def svoo_scatter(X, perm, out=None):
+    """Y[b, h, perm[b, h, p]] = X[b, h, p] for the rows of X [B, H, N, ...]."""
+    return _permute(X, perm, out, 1)
+
+
+def svoo_forward(Q, K, V, proj_q, proj_k, alpha, topk: int, perm_q, perm_k, linear_mode: str = "mask_product",
+                 out=None):
+    """The SLA2 path on co-clustered blocks: Q and alpha gathered by perm_q, K and V by perm_k,
+    route and forward on the permuted sequence, output rows scattered back.  Returns (O in the
+    original query order, idx of the permuted blocks)."""
+    Qp, Kp, Vp = svoo_gather(Q, perm_q), svoo_gather(K, perm_k), svoo_gather(V, perm_k)
+    ap = svoo_gather(alpha.contiguous().to(torch.float32), perm_q)
+    idx, _, _ = route(Qp, Kp, proj_q, proj_k, topk)
+    Op = forward(Qp, Kp, Vp, idx, ap, linear_mode=linear_mode)
+    return svoo_scatter(Op, perm_q, out=out), idx

@@ -2,6 +2,7 @@
 // carving and the launch sequence on the caller's stream.
 #include "sla.h"
 #include "sla_pisa.h"
+#include "sla_svoo.h"
 
 #include <climits>
 #include <cstdint>
@@ -285,6 +286,49 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   return SLA_OK;
 }
 
+// SVOO co-clustering workspace
+struct SvooWs {
+  __bf16 *q_hi, *q_lo, *k_hi, *k_lo;
+  int32_t *qa, *ka, *hist, *start;
+};
+size_t carve_svoo(const sla::Dims& d, void* ws, SvooWs* out) {
+  Carve c(ws);
+  const size_t BH = (size_t)d.B * d.H;
+  const size_t n = BH * d.nb * d.d;
+  SvooWs w;
+  w.q_hi = c.take<__bf16>(n);
+  w.q_lo = c.take<__bf16>(n);
+  w.k_hi = c.take<__bf16>(n);
+  w.k_lo = c.take<__bf16>(n);
+  w.qa = c.take<int32_t>(BH * d.N);
+  w.ka = c.take<int32_t>(BH * d.N);
+  w.hist = c.take<int32_t>(BH * sla::svoo_segments(d.N) * d.nb);
+  w.start = c.take<int32_t>(BH * (d.nb + 1));
+  if (out) *out = w;
+  return c.off;
+}
+
+int check_svoo(const sla_problem* p, sla::Dims* d) {
+  int st = check_problem(p, d);
+  if (st != SLA_OK) return st;
+  if (d->dtype != sla::kBF16 || d->d != 128) return SLA_ERR_UNSUPPORTED;
+  return SLA_OK;
+}
+
+int permute_impl(const sla_problem* p, const void* X, int32_t row_bytes, const int32_t* perm,
+                 void* Y, int scatter, hipStream_t stream) {
+  if (!p || p->B < 1 || p->H < 1 || p->N < 1) return SLA_ERR_INVALID;
+  if (!X || !Y || !perm || row_bytes < 4 || row_bytes > 4096 || row_bytes % 4) return SLA_ERR_INVALID;
+  if ((int64_t)p->B * p->H > 65535) return SLA_ERR_UNSUPPORTED;  // grid y
+  sla::Dims d = {};
+  d.B = p->B;
+  d.H = p->H;
+  d.N = p->N;
+  const hipError_t e = sla::launch_permute_rows(d, X, row_bytes, perm, Y, scatter, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -499,6 +543,51 @@ int sla_backward(const sla_problem* p, const void* Q, const void* K, const void*
                             stream);
   if (e != hipSuccess) return hip_fail(e);
   return SLA_OK;
+}
+
+size_t sla_svoo_workspace_bytes(const sla_problem* p) {
+  sla::Dims d;
+  if (check_svoo(p, &d) != SLA_OK) return 0;
+  return carve_svoo(d, nullptr, nullptr);
+}
+
+int sla_svoo_cluster(const sla_problem* p, const void* Q, const void* K, int32_t iters,
+                     int32_t* q_assign, int32_t* k_assign, int32_t* perm_q, int32_t* perm_k,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  sla::Dims d;
+  int st = check_svoo(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !K || !perm_q || !perm_k || !ws || iters < 1 || iters > 64) return SLA_ERR_INVALID;
+  if ((int64_t)d.B * d.H > 65535) return SLA_ERR_UNSUPPORTED;  // grid y
+  if (ws_bytes < carve_svoo(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  SvooWs w;
+  carve_svoo(d, ws, &w);
+  int32_t* qa = q_assign ? q_assign : w.qa;
+  int32_t* ka = k_assign ? k_assign : w.ka;
+  hipError_t e = sla::launch_pool_means(d, Q, K, w.q_hi, w.q_lo, w.k_hi, w.k_lo, stream);
+  for (int it = 0; it < iters && e == hipSuccess; ++it) {
+    // key step: keys by the query centroids, then the key centroids of the new clusters
+    e = sla::launch_svoo_assign(d, K, w.q_hi, w.q_lo, ka, stream);
+    if (e == hipSuccess) e = sla::launch_svoo_order(d, ka, w.hist, w.start, perm_k, stream);
+    if (e == hipSuccess) e = sla::launch_svoo_centroids(d, K, perm_k, w.start, w.k_hi, w.k_lo, stream);
+    // query step: queries by the updated key centroids (their centroids feed the next pass)
+    if (e == hipSuccess) e = sla::launch_svoo_assign(d, Q, w.k_hi, w.k_lo, qa, stream);
+    if (e == hipSuccess) e = sla::launch_svoo_order(d, qa, w.hist, w.start, perm_q, stream);
+    if (e == hipSuccess && it + 1 < iters)
+      e = sla::launch_svoo_centroids(d, Q, perm_q, w.start, w.q_hi, w.q_lo, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+int sla_svoo_gather(const sla_problem* p, const void* X, int32_t row_bytes, const int32_t* perm,
+                    void* Y, hipStream_t stream) {
+  return permute_impl(p, X, row_bytes, perm, Y, 0, stream);
+}
+
+int sla_svoo_scatter(const sla_problem* p, const void* X, int32_t row_bytes, const int32_t* perm,
+                     void* Y, hipStream_t stream) {
+  return permute_impl(p, X, row_bytes, perm, Y, 1, stream);
 }
 
 const char* sla_status_string(int status) {

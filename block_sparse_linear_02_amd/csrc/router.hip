@@ -318,6 +318,25 @@ hipError_t launch_route(const Dims& p, const void* Q, const void* K, const float
   return launch_topk<64>(p, q_hi, q_lo, k_hi, k_lo, nullptr, 0, idx, mask, probs, lds, stream);
 }
 
+hipError_t launch_pool_means(const Dims& p, const void* Q, const void* K, __bf16* q_hi,
+                             __bf16* q_lo, __bf16* k_hi, __bf16* k_lo, hipStream_t stream) {
+  // both tensors (grid z = 2), no projection
+  dim3 g1((p.nb + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg, p.B * p.H, 2);
+  if (p.dtype == kBF16 && p.d == 128)
+    pool_project_kernel<__bf16, 128><<<g1, kPoolThreads, 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)K, nullptr, nullptr, p.N, p.nb, q_hi, q_lo, k_hi, k_lo);
+  else if (p.dtype == kBF16 && p.d == 64)
+    pool_project_kernel<__bf16, 64><<<g1, kPoolThreads, 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)K, nullptr, nullptr, p.N, p.nb, q_hi, q_lo, k_hi, k_lo);
+  else if (p.dtype == kF32 && p.d == 128)
+    pool_project_kernel<float, 128><<<g1, kPoolThreads, 0, stream>>>(
+        (const float*)Q, (const float*)K, nullptr, nullptr, p.N, p.nb, q_hi, q_lo, k_hi, k_lo);
+  else
+    pool_project_kernel<float, 64><<<g1, kPoolThreads, 0, stream>>>(
+        (const float*)Q, (const float*)K, nullptr, nullptr, p.N, p.nb, q_hi, q_lo, k_hi, k_lo);
+  return hipGetLastError();
+}
+
 hipError_t launch_pisa_route(const Dims& p, const void* Q, __bf16* q_hi, __bf16* q_lo,
                              const __bf16* kbar_hi, const __bf16* kbar_lo, const float* bias,
                              int32_t* idx, uint8_t* mask, float* scores, hipStream_t stream) {

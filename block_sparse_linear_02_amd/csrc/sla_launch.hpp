@@ -24,6 +24,9 @@ hipError_t launch_route(const Dims& p, const void* Q, const void* K, const float
                         __bf16* k_lo, int32_t* idx, uint8_t* mask, float* probs,
                         hipStream_t stream);
 size_t route_lds_bytes(int nb);
+// Block means of Q and K without projection, split bf16 [BH][nb][d] (SVOO's initial centroids).
+hipError_t launch_pool_means(const Dims& p, const void* Q, const void* K, __bf16* q_hi,
+                             __bf16* q_lo, __bf16* k_hi, __bf16* k_lo, hipStream_t stream);
 int route_max_blocks();
 
 // Linear-branch states. Per chunk of `chunk_blocks` key blocks: partial H^T [d][d] and partial
@@ -134,5 +137,22 @@ hipError_t launch_bwd_dkv(const Dims& p, const void* Q, const void* K, const voi
                           const uint32_t* kept_t, const __bf16* dOs, const float* lse2,
                           const float* Dr, const __bf16* dh, const float* dz, float* dK, float* dV,
                           hipStream_t stream);
+
+// SVOO co-clustering (bf16, d = 128, C = nb clusters).  assign: nearest centroid (split bf16
+// [BH][C][d]) of every row of X by inner product -> [BH][N].  order: the stable sort of the
+// tokens by cluster -> perm [BH][N] (position -> token) and start [BH][C + 1], through the
+// per-segment counts hist [BH][svoo_segments(N)][C].  centroids: member means (empty clusters
+// untouched).  permute_rows: y[p] = x[perm[p]] (scatter = 0) or y[perm[p]] = x[p] (scatter = 1)
+// for rows of row_bytes (a multiple of 4) of every (batch, head).
+int svoo_segments(int N);
+hipError_t launch_svoo_assign(const Dims& p, const void* X, const __bf16* c_hi,
+                              const __bf16* c_lo, int32_t* assign, hipStream_t stream);
+hipError_t launch_svoo_order(const Dims& p, const int32_t* assign, int32_t* hist, int32_t* start,
+                             int32_t* perm, hipStream_t stream);
+hipError_t launch_svoo_centroids(const Dims& p, const void* X, const int32_t* perm,
+                                 const int32_t* start, __bf16* c_hi, __bf16* c_lo,
+                                 hipStream_t stream);
+hipError_t launch_permute_rows(const Dims& p, const void* X, int row_bytes, const int32_t* perm,
+                               void* Y, int scatter, hipStream_t stream);
 
 }  // namespace sla

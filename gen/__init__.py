@@ -18,6 +18,7 @@ tensors stand in for it with the same shapes and an attention-concentrating stru
 * ``pisa_video_s``, ``pisa_video_l`` the ``video_s`` / ``video_l`` tensors with 12.5 % of the
                  KV blocks kept (k = 64 of 512, 148 of 1182), the 87.5 % sparsity at which the
                  PISA summary reports its Wan2.1-14B result, for the PISA forward.
+* ``svoo_video_s`` the ``video_s`` tensors, for the path on SVOO co-clustered blocks.
 
 Clustered Q/K: the latent grid is cut into boxes of (2, 8, 8) tokens (smaller at the edges);
 per (batch, head, box) a centre mu ~ N(0, s^2 I_d) is shared by the box's queries and keys,
@@ -90,6 +91,7 @@ WORKLOADS = {
     ),
     "pisa_video_s": Workload("pisa_video_s", 1, 12, 32768, 128, 64, "bf16", "clustered", (8, 64, 64), wid=2),
     "pisa_video_l": Workload("pisa_video_l", 1, 40, 75600, 128, 148, "bf16", "clustered", (21, 45, 80), wid=3),
+    "svoo_video_s": Workload("svoo_video_s", 1, 12, 32768, 128, 51, "bf16", "clustered", (8, 64, 64), wid=2),
 }
 
 
