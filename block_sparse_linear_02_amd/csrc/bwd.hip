@@ -319,6 +319,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     __syncthreads();
     zero_tail(B0{}, nv_cur);
   }
+  // every path into the loop has waited for the operands loaded into registers above (else the
+  // compiler waits for all memory traffic, the next tile's prefetch included, in every step)
+  wait_vmem();
   auto step = [&](int t, auto BUFC) {
     constexpr int BUF = decltype(BUFC)::value;
     const int nv = nv_cur;
@@ -547,6 +550,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(
     __syncthreads();
     zero_tail(B0{}, nv_cur);
   }
+  // every path into the loop has waited for the operands loaded into registers above (else the
+  // compiler waits for all memory traffic, the next tile's prefetch included, in every step)
+  wait_vmem();
   auto step = [&](int t, auto BUFC) {
     constexpr int BUF = decltype(BUFC)::value;
     launder();

@@ -774,6 +774,9 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     wait_vmem();
     __syncthreads();
   }
+  // every path into the loop has waited for the operands loaded into registers above (else the
+  // compiler waits for all memory traffic, the next tile's prefetch included, in every step)
+  wait_vmem();
   // step t: K(t) in kbuf(B) (B = t & 1), V(t - 1) in vbuf(1 - B); stage K(t + 1) and V(t)
   auto step2 = [&](int t, auto BUFC) {
     constexpr int BUF = decltype(BUFC)::value;

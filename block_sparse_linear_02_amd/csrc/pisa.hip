@@ -334,6 +334,9 @@ __global__ __launch_bounds__(kPisaThreads, 2) void pisa_kernel(
     __syncthreads();
     zero_tail(B0{}, nv_cur);
   }
+  // every path into the loop has waited for the operands loaded into registers above (else the
+  // compiler waits for all memory traffic, the next tile's prefetch included, in every step)
+  wait_vmem();
   // the end of every step: tile t + 1 has landed in the other buffer
   auto finish = [&](int t, auto OTHERC) {
     nv_cur = nv_next;

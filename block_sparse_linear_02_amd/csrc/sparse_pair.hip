@@ -269,6 +269,10 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     __syncthreads();
     zero_tail(B0{}, nv_cur);
   }
+  // every path into the loop has waited for the Q operands (loaded above into registers):
+  // otherwise the compiler cannot tell and waits for all memory traffic, the prefetch of the
+  // next tile included, before the first MFMA of every step
+  wait_vmem();
   // one tile of the union; BUF (= t & 1, a compile-time constant through the unrolled pair
   // below) is the buffer holding tile t, and tile t + 1 is staged into the other one (last read
   // in iteration t - 1).  MASK: the tile may be short (only the last block of the sequence is,
