@@ -245,3 +245,47 @@ def test_pisa_binding_refuses_cpu_tensors(L):
     x = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sla.pisa_stats(x, x)
+
+
+def test_svoo_checks(L):
+    """SVOO co-clustering and row permutations: every call below is refused on the host, before
+    anything is enqueued."""
+    p = P()
+    wb = L.sla_svoo_workspace_bytes(ctypes.byref(p))
+    assert wb > 0 and L.sla_svoo_workspace_bytes(ctypes.byref(P(H=4))) > wb
+    for bad in (P(d=64), P(d=96), P(dtype=sla.SLA_F32)):
+        assert L.sla_svoo_workspace_bytes(ctypes.byref(bad)) == 0
+    c = L.sla_svoo_cluster
+    args = [FAKE, FAKE, 3, None, None, FAKE, FAKE, FAKE, wb, None]  # Q K iters qa ka pq pk ws bytes stream
+    assert c(ctypes.byref(P(d=64)), *args) == sla.SLA_ERR_UNSUPPORTED
+    assert c(ctypes.byref(P(dtype=sla.SLA_F32)), *args) == sla.SLA_ERR_UNSUPPORTED
+    for i in (0, 1, 5, 6, 7):  # Q, K, perm_q, perm_k, workspace
+        bad = list(args)
+        bad[i] = None
+        assert c(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID, i
+    for iters in (0, -1, 65):
+        bad = list(args)
+        bad[2] = iters
+        assert c(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID, iters
+    short = list(args)
+    short[8] = wb - 1
+    assert c(ctypes.byref(p), *short) == sla.SLA_ERR_WORKSPACE
+    for fn in (L.sla_svoo_gather, L.sla_svoo_scatter):
+        for rb in (0, 3, 6, 4100, -4):
+            assert fn(ctypes.byref(p), FAKE, rb, FAKE, FAKE, None) == sla.SLA_ERR_INVALID, rb
+        assert fn(ctypes.byref(p), None, 256, FAKE, FAKE, None) == sla.SLA_ERR_INVALID
+        assert fn(ctypes.byref(p), FAKE, 256, None, FAKE, None) == sla.SLA_ERR_INVALID
+        assert fn(ctypes.byref(p), FAKE, 256, FAKE, None, None) == sla.SLA_ERR_INVALID
+        assert fn(ctypes.byref(P(N=0)), FAKE, 256, FAKE, FAKE, None) == sla.SLA_ERR_INVALID
+        assert fn(ctypes.byref(P(B=2, H=40000)), FAKE, 256, FAKE, FAKE, None) == sla.SLA_ERR_UNSUPPORTED
+
+
+def test_svoo_binding_refuses_cpu_tensors(L):
+    x = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    perm = torch.zeros((1, 1, 64), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sla.svoo_cluster(x, x)
+    with pytest.raises(ValueError):
+        sla.svoo_gather(x, perm)
+    with pytest.raises(ValueError):
+        sla.svoo_scatter(x, perm)
