@@ -277,6 +277,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
     const int m = 32 * role + lane % 32;
     const int row = qb * kBlock + m;
     const bool row_ok = row < N;
+    const bool rows_all_ok = __ballot(!row_ok) == 0;  // every row of this wavefront exists
     i32x8 qf[N8];  // e4m3 Q as the B operand: k-slot 32g + b of step s <-> channel 64s + 32g + b
 #pragma unroll
     for (int s = 0; s < N8; ++s) {
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
         k8_regs(t + 1, kr[1 - BUF]);
       }
       const int j = sel[t];
-      const int nv = min(kBlock, N - j * kBlock);
+      const int nv = min(kBlock, N - __builtin_amdgcn_readfirstlane(j) * kBlock);
       const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
       const int lim = nv - 4 * g;
 #pragma unroll
@@ -324,9 +325,16 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
         f32x16 s = f32x16{};
 #pragma unroll
         for (int st = 0; st < N8; ++st) s = mfma_f8(kr[BUF][kt][st], qf[st], s);
+        if (nv == kBlock) {  // a full tile: no key mask; sc > 0 scales the maximum once
+          float mx = s[0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[i] * sc);
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+          mrow = fmaxf(mrow, mx * sc);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[i] * sc);
+        }
       }
       publish1(t + 1, NEXT{});
     });
@@ -363,11 +371,20 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
           const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g + 16));
           s = mfma_f8(join8(a0, a1), qf[st], s);
         }
+        if (rows_all_ok && nv == kBlock) {  // wavefront-uniform: no key or row mask
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
-          lsum += p[kt][i];
-          pmax = fmaxf(pmax, p[kt][i]);
+          for (int i = 0; i < 16; ++i) {
+            p[kt][i] = fast_exp2(fmaf(s[i], sc, -mrow));
+            lsum += p[kt][i];
+            pmax = fmaxf(pmax, p[kt][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            p[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
+            lsum += p[kt][i];
+            pmax = fmaxf(pmax, p[kt][i]);
+          }
         }
       }
       pmax = wave_max(pmax);
@@ -638,6 +655,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   const int m = 32 * half + lane % 32;
   const int row = (qb0 + blk) * kBlock + m;
   const bool row_ok = row < N;
+  const bool rows_all_ok = __ballot(!row_ok) == 0;  // every row of this wavefront exists
   i32x8 qf[N8];  // e4m3 Q as the B operand: k-slot 32g + b of step s <-> channel 64s + 32g + b
   {
     const uint8_t* qr = q8 + hoff + (size_t)min(row, N - 1) * D + 32 * g;
@@ -683,14 +701,25 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
       k8_regs(jn, kr[1 - BUF]);
       zr[1 - BUF] = zb[((size_t)bh * nb + jn) * D + tid % D];
       skr[1 - BUF] = sk[(size_t)bh * nb + jn];
-      const int nv = min(kBlock, N - j * kBlock);
-      const int lim = nv - 4 * g;
+      const int nv = min(kBlock, N - __builtin_amdgcn_readfirstlane(j) * kBlock);
+      if (nv == kBlock) {  // a full tile: no key mask; sc > 0 scales the maximum once
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const f32x16 s = dot64(kr[BUF][kt], qf);
+        for (int kt = 0; kt < 2; ++kt) {
+          const f32x16 s = dot64(kr[BUF][kt], qf);
+          float mx = s[0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[i] * sc);
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+          mrow = fmaxf(mrow, mx * sc);
+        }
+      } else {
+        const int lim = nv - 4 * g;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const f32x16 s = dot64(kr[BUF][kt], qf);
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + 8 * (i / 4) + i % 4 < lim) mrow = fmaxf(mrow, s[i] * sc);
+        }
       }
     };
     if (nsel > 0) {
@@ -790,7 +819,9 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     float pmax = 0.f;
     if (kept) {
       const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
-      const int lim = row_ok ? min(kBlock, N - j * kBlock) - 4 * g : 0;
+      const int nv = min(kBlock, N - j * kBlock);
+      const int lim = row_ok ? nv - 4 * g : 0;
+      const bool full = rows_all_ok && nv == kBlock;  // wavefront-uniform: no key or row mask
       const uint8_t* ks = kbuf(BUFC);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -803,11 +834,20 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
           ka[st] = join8(a0, a1);
         }
         const f32x16 s = dot64(ka, qf);
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pp[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
-          lsum += pp[kt][i];
-          pmax = fmaxf(pmax, pp[kt][i]);
+          for (int i = 0; i < 16; ++i) {
+            pp[kt][i] = fast_exp2(fmaf(s[i], sc, -mrow));
+            lsum += pp[kt][i];
+            pmax = fmaxf(pmax, pp[kt][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            pp[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
+            lsum += pp[kt][i];
+            pmax = fmaxf(pmax, pp[kt][i]);
+          }
         }
       }
       pmax = wave_max(pmax);
