@@ -75,6 +75,7 @@ class ForwardOpts(ctypes.Structure):
         ("states_end", ctypes.c_void_p),
         ("branch_drop", ctypes.c_int32),
         ("drop_tau", ctypes.c_float),
+        ("idx_ready", ctypes.c_void_p),
     ]
 
 
@@ -214,12 +215,15 @@ def route(Q, K, proj_q, proj_k, topk: int, want_mask: bool = False, want_scores:
 
 
 def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", workspace=None,
-            out=None, events=None, state_events=None, drop_tau=None, int8: bool = False):
+            out=None, events=None, state_events=None, drop_tau=None, int8: bool = False,
+            idx_ready=None):
     """O = alpha * O_s + (1 - alpha) * O_l.  `events` = (begin, end) torch.cuda.Event pair
     recorded around the sparse kernel, `state_events` likewise around the linear-state kernels
     (the events must already exist, e.g. recorded once).  drop_tau (0 <= tau < 0.5, bf16
     mask-product mode): per (b, h), drop the linear branch when max(1 - alpha) <= tau and the
-    sparse branch when max(alpha) <= tau, decided on the GPU."""
+    sparse branch when max(alpha) <= tau, decided on the GPU.  idx_ready (a recorded
+    torch.cuda.Event): the linear states are built at once and the stream waits for the event
+    only before idx is read, so a router on another stream overlaps them."""
     _check_qkv(Q, K, V)
     Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
     B, H, N, d = Q.shape
@@ -242,6 +246,8 @@ def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", 
     if state_events is not None:
         opts.states_begin = ctypes.c_void_p(state_events[0].cuda_event)
         opts.states_end = ctypes.c_void_p(state_events[1].cuda_event)
+    if idx_ready is not None:
+        opts.idx_ready = ctypes.c_void_p(idx_ready.cuda_event)
     fn = lib().sla_forward_int8_ex if int8 else (lib().sla_forward_fp8_ex if fp8 else lib().sla_forward_ex)
     st = fn(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(alpha), _ptr(O), _ptr(ws),
             ws.numel(), _stream(), ctypes.byref(opts))

@@ -244,6 +244,10 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   if (e != hipSuccess) return hip_fail(e);
   e = sla::launch_state_reduce(d, w.h_part, w.z_part, w.ht_hi, w.ht_lo, w.Z, w.h_full, stream);
   if (e != hipSuccess) return hip_fail(e);
+  if (opts && opts->idx_ready) {  // nothing above reads idx
+    e = hipStreamWaitEvent(stream, opts->idx_ready, 0);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if (mode == SLA_LINEAR_MASK_PRODUCT) {
     e = sla::launch_mask_bits(d, idx, w.bits, stream);  // every block unselected when topk == 0
     if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.bits, w.t_bf, stream, flags);

@@ -102,6 +102,11 @@ typedef struct {
    * mask-product linear mode supports it (else SLA_ERR_UNSUPPORTED). */
   int32_t branch_drop;
   float drop_tau;
+  /* if non-null: `stream` waits for this event after the linear-state kernels and before the
+   * first kernel that reads idx, so that the router (sla_route on another stream, the event
+   * recorded after it) overlaps the state build.  The caller keeps idx unchanged until this
+   * forward has finished. */
+  hipEvent_t idx_ready;
 } sla_forward_opts;
 
 /* Workspace sizes in bytes for a problem (0 when the problem is invalid or unsupported). */

@@ -227,6 +227,34 @@ def test_forward_literal_linear_mode():
     check_close(got, fused, rel_tol=1e-3, max_tol=1e-3, what="literal vs fused")
 
 
+@pytest.mark.parametrize("mode", ["mask_product", "fused"])
+def test_router_on_second_stream(mode):
+    """sla_route on a second stream with the forward waiting on its event (idx_ready) only
+    before idx is read: the same output, bit for bit, as route then forward on one stream; three
+    steps in a row, each router waiting for the previous step's forward."""
+    c = case("ragged_bf16", small_ragged())
+    g = dev(c)
+    k = c["workload"].topk
+    idx_ref, _, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], k)
+    O_ref = sla.forward(g["Q"], g["K"], g["V"], idx_ref, g["alpha"], linear_mode=mode)
+    idx = torch.empty_like(idx_ref)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    outs = []
+    for _ in range(3):
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], k, idx_out=idx)
+            ready.record()
+        outs.append(sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], linear_mode=mode, idx_ready=ready))
+    torch.cuda.synchronize()
+    say(f"router on a second stream ({mode}): 3 steps")
+    assert torch.equal(idx, idx_ref)
+    for O in outs:
+        assert torch.equal(O, O_ref)
+
+
 def test_forward_deterministic():
     wl = small_ragged()
     c = case("ragged_bf16", wl)
