@@ -116,7 +116,7 @@ def sweep_workloads():
 
 
 def workers() -> int:
-    """Host threads for per-head work (bounded: the GPU machines grant a 16-core share)."""
+    """Host threads for per-head work: the affinity mask, at most 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
