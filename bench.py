@@ -656,7 +656,7 @@ def mass_covered(inputs, wl, idx_np, blocks):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the forward shards over (batch, head) with no communication); run with --gpus 1",
               file=sys.stderr)
         sys.exit(1)
