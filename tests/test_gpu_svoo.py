@@ -262,3 +262,43 @@ def test_svoo_rejects_bad_arguments():
         sla.svoo_cluster(Q, Q, 0)
     with pytest.raises(sla.SLAError):
         sla.svoo_cluster(Q.float(), Q.float(), 1)
+
+
+def test_svoo_video_s_forward_sampled():
+    """video_s at full size on co-clustered blocks (the oracle's permutations of every head,
+    three iterations): the GPU router on the permuted sequence against the oracle's on head 5
+    (bit-exact or a valid top-k at near ties), and the GPU forward of that head, with the
+    oracle's kept sets, on sampled query blocks (the first, the last and six more)."""
+    c = gen.draw(gen.workload("video_s"), 0)
+    wl = c["workload"]
+    k, nb, bh = wl.topk, wl.n_blocks, 5
+    qa, ka = oracle.svoo_cocluster(c["Q"], c["K"], 3)
+    pq, pk = oracle.svoo_order(qa).astype(np.int32), oracle.svoo_order(ka).astype(np.int32)
+    d = torch.device("cuda:0")
+    g = {n: c[n].to(d) for n in ("Q", "K", "V", "alpha", "Wq", "Wk")}
+    tq, tk = torch.from_numpy(pq).to(d), torch.from_numpy(pk).to(d)
+    Qp, Kp, Vp = sla.svoo_gather(g["Q"], tq), sla.svoo_gather(g["K"], tk), sla.svoo_gather(g["V"], tk)
+    ap = sla.svoo_gather(g["alpha"], tq)
+    idx_gpu, _, _ = sla.route(Qp, Kp, g["Wq"], g["Wk"], k)
+    # the oracle on head 5 of the permuted sequence
+    Q5, K5, V5 = (f64(c[n][0, bh])[p] for n, p in (("Q", pq[0, bh]), ("K", pk[0, bh]), ("V", pk[0, bh])))
+    a5 = f64(c["alpha"][0, bh])[pq[0, bh]]
+    r5 = oracle.route(Q5[None, None], K5[None, None], c["Wq"].double(), c["Wk"].double(), k, 64)
+    ig = idx_gpu.cpu().numpy()[0, bh]
+    bad = np.flatnonzero(np.any(ig != r5["idx"][0, 0], axis=-1))
+    for i in bad:
+        s = r5["scores"][0, 0, i]
+        assert _valid_topk(ig[i], s, k, 1e-5 * (1 + np.abs(s).max())), f"route row {i}"
+    say(f"video_s co-clustered: router rows of head {bh} differing at near ties: {len(bad)}")
+    idx_use = idx_gpu.clone()
+    idx_use[0, bh] = torch.from_numpy(r5["idx"][0, 0]).to(d)
+    Op = sla.forward(Qp, Kp, Vp, idx_use, ap, linear_mode="mask_product").cpu().double().numpy()[0, bh]
+    rng = np.random.default_rng(11)
+    blocks = sorted({0, nb - 1, *rng.choice(nb, 6, replace=False).tolist()})
+    ref, _, _ = oracle.forward_head(Q5, K5, V5, r5["idx"][0, 0], a5, 64, q_blocks=blocks)
+    got = np.concatenate([Op[64 * i : 64 * (i + 1)] for i in blocks])
+    ref = np.concatenate(ref)
+    err = float(np.abs(got - ref).max())
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    say(f"video_s co-clustered forward, head {bh}, blocks {blocks}: max|d| {err:.3e} rel-L2 {rel:.3e}")
+    assert err <= TOL_MAX and rel <= TOL_REL
