@@ -344,15 +344,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
           dp[kt] = mfma32(rd_row(Vs, 32 * kt, k), dos[k], dp[kt]);
         }
       // dS = P (dP - D) in bf16; key of register i in half kt: 32 kt + 8 (i / 4) + 4 g + i % 4
-      const int lim = nv - 4 * g;
+      if (nv < kBlock) {  // the short last block (workgroup-uniform): keys past it get P = 0
+        const int lim = nv - 4 * g;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + 8 * (i / 4) + i % 4 >= lim) s[kt][i] = -INFINITY;
+      }
       bf16x8 pb[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const int kt = u / 2, i = 8 * (u % 2) + jj;
-          const float p = (32 * kt + 8 * (i / 4) + i % 4 < lim) ? fast_exp2(fmaf(s[kt][i], c_log2, -l2)) : 0.f;
-          pb[u][jj] = f2bf(p * (dp[kt][i] - dr));
+          pb[u][jj] = f2bf(fast_exp2(fmaf(s[kt][i], c_log2, -l2)) * (dp[kt][i] - dr));
         }
       // dQ^T += K^T dS^T: K read transposed (rows = keys in the k-order of pb)
 #pragma unroll
