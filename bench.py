@@ -496,8 +496,9 @@ def svoo_cpu_baseline(inputs, wl, iters, reuse, budget_s=15.0):
 
 def bench_svoo(a, wl):
     """One step = the SLA2 path on co-clustered blocks (gather Q, K, V, alpha; route; forward in
-    the mask-product mode; scatter O), with the co-clustering itself run on every `reuse`-th step
-    (the clusters are reused over that many diffusion steps)."""
+    the mask-product mode, whose epilogue writes O back in the original row order), with the
+    co-clustering itself run on every `reuse`-th step (the clusters are reused over that many
+    diffusion steps)."""
     import torch
 
     import block_sparse_linear_02_amd as sla
@@ -517,12 +518,11 @@ def bench_svoo(a, wl):
     Qp, Kp, Vp = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
     ap = torch.empty_like(alpha)
     idx = torch.empty((B, H, nb, k), dtype=torch.int32, device=dev)
-    Op = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
-    O = torch.empty_like(Op)
+    O = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     n_cl = (a.steps + reuse - 1) // reuse
-    ev_t, ev_c, ev_g, ev_r, ev_f, ev_s, ev_sp = (events(n) for n in (a.steps, n_cl, a.steps, a.steps, a.steps,
-                                                                       a.steps, a.steps))
-    for e in ev_t + ev_c + ev_g + ev_r + ev_f + ev_s + ev_sp:
+    ev_t, ev_c, ev_g, ev_r, ev_f, ev_sp = (events(n) for n in (a.steps, n_cl, a.steps, a.steps, a.steps,
+                                                               a.steps))
+    for e in ev_t + ev_c + ev_g + ev_r + ev_f + ev_sp:
         e[0].record()
         e[1].record()
     torch.cuda.synchronize()
@@ -546,12 +546,10 @@ def bench_svoo(a, wl):
         sla.route(Qp, Kp, Wq, Wk, k, workspace=ws_r, idx_out=idx)
         rec(ev_r, 1)
         rec(ev_f, 0)
-        sla.forward(Qp, Kp, Vp, idx, ap, linear_mode="mask_product", workspace=ws_f, out=Op,
-                    events=ev_sp[i] if i is not None else None)
+        # the pair kernel's epilogue writes each output row back to its original position
+        sla.forward(Qp, Kp, Vp, idx, ap, linear_mode="mask_product", workspace=ws_f, out=O,
+                    events=ev_sp[i] if i is not None else None, out_rows=pq)
         rec(ev_f, 1)
-        rec(ev_s, 0)
-        sla.svoo_scatter(Op, pq, out=O)
-        rec(ev_s, 1)
         rec(ev_t, 1)
 
     for _ in range(a.warmup):
@@ -563,13 +561,12 @@ def bench_svoo(a, wl):
     torch.cuda.synchronize()
     ms = 1e3 * (time.perf_counter() - t0) / a.steps
     sp = sparse_flops(idx, N, d)
-    cl_ms, g_ms, r_ms, f_ms, s_ms, sp_ms = (avg_ms(e) for e in (ev_c, ev_g, ev_r, ev_f, ev_s, ev_sp))
+    cl_ms, g_ms, r_ms, f_ms, sp_ms = (avg_ms(e) for e in (ev_c, ev_g, ev_r, ev_f, ev_sp))
     # co-clustering MFMA work: per iteration two assignments (keys, queries), each N x C x d
     # products against the centroid's hi and lo halves
     assign_flops = iters * 2 * 2 * 2.0 * N * nb * d * B * H
     es = Q.element_size()
     move_bytes = 2 * (3 * B * H * N * d * es + B * H * N * 4)  # gathers: read + write
-    scat_bytes = 2 * B * H * N * d * 4
     achieved = sp / (sp_ms * 1e-3) / 1e12
     rec = {
         "metric": "sparse-linear attn fwd ms/call + effective TFLOPS on SVOO co-clustered blocks",
@@ -586,13 +583,14 @@ def bench_svoo(a, wl):
         "data": "synthetic (seeded clustered video-DiT-shaped tensors, random projections)",
         "config": {
             "workload": f"{wl.name}: B={B} H={H} N={N} d={d} block=64 topk={k} of {nb}, co-clustering "
-                        f"{iters} iterations into {nb} clusters, reused for {reuse} steps, mask-product mode",
+                        f"{iters} iterations into {nb} clusters, reused for {reuse} steps, mask-product mode, "
+                        f"output rows written back in place",
             "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": k, "iters": iters, "reuse": reuse,
             "cluster_calls_timed": n_cl,
         },
         "step_ms_events": quantiles(ev_t),
-        "kernels_ms": {"cluster_call": cl_ms, "gathers": g_ms, "route": r_ms, "forward": f_ms,
-                       "sparse_kernel": sp_ms, "scatter": s_ms},
+        "kernels_ms": {"cluster_call": cl_ms, "gathers": g_ms, "route": r_ms,
+                       "forward_with_scatter": f_ms, "sparse_kernel": sp_ms},
         "roofline": {
             "bound": "mfma",
             "kernel": "pair_kernel<bf16, 128> (sparse branch, permuted sequence)",
@@ -607,7 +605,7 @@ def bench_svoo(a, wl):
             "assign_mfma_flops_per_call": assign_flops,
             "cluster_call_tflops": assign_flops / (cl_ms * 1e-3) / 1e12,
         },
-        "hbm_kernels": {"gathers": hbm(move_bytes, g_ms), "scatter": hbm(scat_bytes, s_ms)},
+        "hbm_kernels": {"gathers": hbm(move_bytes, g_ms)},
     }
     if not a.no_cpu_baseline:
         cb = svoo_cpu_baseline(inputs, wl, iters, reuse)

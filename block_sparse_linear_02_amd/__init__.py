@@ -76,6 +76,7 @@ class ForwardOpts(ctypes.Structure):
         ("branch_drop", ctypes.c_int32),
         ("drop_tau", ctypes.c_float),
         ("idx_ready", ctypes.c_void_p),
+        ("out_rows", ctypes.c_void_p),
     ]
 
 
@@ -216,14 +217,15 @@ def route(Q, K, proj_q, proj_k, topk: int, want_mask: bool = False, want_scores:
 
 def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", workspace=None,
             out=None, events=None, state_events=None, drop_tau=None, int8: bool = False,
-            idx_ready=None):
+            idx_ready=None, out_rows=None):
     """O = alpha * O_s + (1 - alpha) * O_l.  `events` = (begin, end) torch.cuda.Event pair
     recorded around the sparse kernel, `state_events` likewise around the linear-state kernels
     (the events must already exist, e.g. recorded once).  drop_tau (0 <= tau < 0.5, bf16
     mask-product mode): per (b, h), drop the linear branch when max(1 - alpha) <= tau and the
     sparse branch when max(alpha) <= tau, decided on the GPU.  idx_ready (a recorded
     torch.cuda.Event): the linear states are built at once and the stream waits for the event
-    only before idx is read, so a router on another stream overlaps them."""
+    only before idx is read, so a router on another stream overlaps them.  out_rows ([B, H, N]
+    int32 permutation, bf16 mask-product mode): output row r is written to row out_rows[r]."""
     _check_qkv(Q, K, V)
     Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
     B, H, N, d = Q.shape
@@ -248,6 +250,11 @@ def forward(Q, K, V, idx, alpha, fp8: bool = False, linear_mode: str = "fused", 
         opts.states_end = ctypes.c_void_p(state_events[1].cuda_event)
     if idx_ready is not None:
         opts.idx_ready = ctypes.c_void_p(idx_ready.cuda_event)
+    if out_rows is not None:
+        out_rows = out_rows.contiguous().to(torch.int32)
+        if tuple(out_rows.shape) != (B, H, N) or out_rows.device != Q.device:
+            raise ValueError("out_rows must be [B, H, N] on the inputs' device")
+        opts.out_rows = _ptr(out_rows)
     fn = lib().sla_forward_int8_ex if int8 else (lib().sla_forward_fp8_ex if fp8 else lib().sla_forward_ex)
     st = fn(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(alpha), _ptr(O), _ptr(ws),
             ws.numel(), _stream(), ctypes.byref(opts))
@@ -462,5 +469,8 @@ def svoo_forward(Q, K, V, proj_q, proj_k, alpha, topk: int, perm_q, perm_k, line
     Qp, Kp, Vp = svoo_gather(Q, perm_q), svoo_gather(K, perm_k), svoo_gather(V, perm_k)
     ap = svoo_gather(alpha.contiguous().to(torch.float32), perm_q)
     idx, _, _ = route(Qp, Kp, proj_q, proj_k, topk)
+    if linear_mode == "mask_product" and Q.dtype == torch.bfloat16:
+        # the forward's epilogue writes each row straight to its original position
+        return forward(Qp, Kp, Vp, idx, ap, linear_mode=linear_mode, out=out, out_rows=perm_q), idx
     Op = forward(Qp, Kp, Vp, idx, ap, linear_mode=linear_mode)
     return svoo_scatter(Op, perm_q, out=out), idx

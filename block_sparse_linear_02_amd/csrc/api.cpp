@@ -218,6 +218,8 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   const bool drop = opts && opts->branch_drop;
   if (drop && !(opts->drop_tau >= 0.f && opts->drop_tau < 0.5f)) return SLA_ERR_INVALID;
   if (drop && (fp8 || mode != SLA_LINEAR_MASK_PRODUCT)) return SLA_ERR_UNSUPPORTED;
+  const int32_t* out_rows = opts ? opts->out_rows : nullptr;
+  if (out_rows && (fp8 || mode != SLA_LINEAR_MASK_PRODUCT)) return SLA_ERR_UNSUPPORTED;
   if (fp8 && (d.dtype != sla::kBF16 || d.d != 128)) return SLA_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !alpha || !O || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
   const int variant = int8  ? 5
@@ -274,7 +276,8 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
   else if (mode == SLA_LINEAR_MASK_PRODUCT)
-    e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream, flags);
+    e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream, flags,
+                                nullptr, out_rows);
   else
     e = sla::launch_sparse(d, Q, K, V, idx, alpha, w.ht_hi, w.ht_lo, w.Z, w.zb, O,
                            mode == SLA_LINEAR_FUSED ? 1 : 0, stream);

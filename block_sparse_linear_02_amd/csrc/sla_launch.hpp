@@ -58,10 +58,12 @@ struct TrainRows {
 };
 // flags (optional): a kDropLinear head writes alpha O_s only, a kDropSparse head
 // (1 - alpha) O_l only.  tr (optional, bf16 with d = 128): also write the TrainRows.
+// out_rows (optional, [BH][N]): O row r goes to row out_rows[r] (TrainRows stay in place).
 hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream,
-                              const uint32_t* flags = nullptr, const TrainRows* tr = nullptr);
+                              const uint32_t* flags = nullptr, const TrainRows* tr = nullptr,
+                              const int32_t* out_rows = nullptr);
 // Reduce the chunk partials (fixed order): H^T as bf16 hi/lo [d][d], Z [d]; optionally H [d][d]
 // in fp32 (K-channel major, literal mode); Z alone when h_part is null (mask-product mode).
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
     float* __restrict__ O, int N, int nb, int topk, float c_log2,
-    const uint32_t* __restrict__ flags, TrainRows tr) {
+    const uint32_t* __restrict__ flags, TrainRows tr, const int32_t* __restrict__ out_rows) {
   constexpr int NS = D / 16;  // MFMA k-steps over the head dim
   constexpr int NC = D / 32;  // 32-channel output tiles
   constexpr int TILE = TileLayout<D>::ELEMS;
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   if (!row_ok) return;
   const float a = alpha[(size_t)bh * N + row];
   const float ws = a * inv_l, wl = (1.f - a) * inv_den;
-  float* orow = O + hoff + (size_t)row * D;
+  float* orow = O + hoff + (size_t)(out_rows ? out_rows[(size_t)bh * N + row] : row) * D;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -471,17 +471,17 @@ template <class T, int D>
 hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const float* alpha, const __bf16* t_bf,
                          const float* Z, const float* zb, float* O, hipStream_t stream,
-                         const uint32_t* flags, const TrainRows* tr) {
+                         const uint32_t* flags, const TrainRows* tr, const int32_t* out_rows) {
   const int total = xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (tr)
     pair_kernel<T, D, true><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, flags, *tr);
+        c_log2, flags, *tr, out_rows);
   else
     pair_kernel<T, D, false><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, flags, TrainRows{});
+        c_log2, flags, TrainRows{}, out_rows);
   return hipGetLastError();
 }
 
@@ -490,16 +490,17 @@ hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void
 hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream,
-                              const uint32_t* flags, const TrainRows* tr) {
+                              const uint32_t* flags, const TrainRows* tr,
+                              const int32_t* out_rows) {
   if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, tr);
+    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, tr, out_rows);
   if (tr) return hipErrorInvalidValue;  // the training outputs exist for bf16, d = 128 only
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr);
+    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr);
-  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr);
+    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows);
+  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows);
 }
 
 }  // namespace sla

@@ -107,6 +107,11 @@ typedef struct {
    * recorded after it) overlaps the state build.  The caller keeps idx unchanged until this
    * forward has finished. */
   hipEvent_t idx_ready;
+  /* if non-null ([B][H][N] int32, a permutation of 0 .. N-1 per (b, h)): output row r of (b, h)
+   * is written to row out_rows[b][h][r] of O, e.g. SVOO's query permutation to return rows of a
+   * co-clustered sequence to their original order without a separate scatter.  Only the bf16
+   * forward in the mask-product mode supports it (else SLA_ERR_UNSUPPORTED). */
+  const int32_t* out_rows;
 } sla_forward_opts;
 
 /* Workspace sizes in bytes for a problem (0 when the problem is invalid or unsupported). */

@@ -289,3 +289,16 @@ def test_svoo_binding_refuses_cpu_tensors(L):
         sla.svoo_gather(x, perm)
     with pytest.raises(ValueError):
         sla.svoo_scatter(x, perm)
+
+
+def test_out_rows_checks(L):
+    """out_rows is refused outside the bf16 mask-product forward, on the host."""
+    p = P()
+    o = sla.ForwardOpts(sla.LINEAR_MODES["fused"], None, None, None, None, 0, 0.0, None, FAKE)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert L.sla_forward_ex(ctypes.byref(p), *args, ctypes.byref(o)) == sla.SLA_ERR_UNSUPPORTED
+    o = sla.ForwardOpts(sla.LINEAR_MODES["mask_product"], None, None, None, None, 0, 0.0, None, FAKE)
+    assert L.sla_forward_fp8_ex(ctypes.byref(p), *args, ctypes.byref(o)) == sla.SLA_ERR_UNSUPPORTED
+    # accepted: stops at the workspace check (one byte), before anything is enqueued
+    small = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None)
+    assert L.sla_forward_ex(ctypes.byref(p), *small, ctypes.byref(o)) == sla.SLA_ERR_WORKSPACE

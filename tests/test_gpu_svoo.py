@@ -255,6 +255,24 @@ def test_svoo_video_s_heads():
     compare_cluster(c, 3, heads=[0, 5, 11])
 
 
+@pytest.mark.parametrize("k", [6, 0, 57])
+def test_svoo_forward_writes_rows_in_place(k):
+    """The forward's out_rows (the query permutation): the same bytes as a forward on the
+    co-clustered sequence followed by the scatter, in the bf16 mask-product mode."""
+    c = gen.draw(small(name=f"svoo_inplace_k{k}", k=k), 0)
+    d = torch.device("cuda:0")
+    g = {n: c[n].to(d) for n in ("Q", "K", "V", "alpha", "Wq", "Wk")}
+    pq, pk, _, _ = sla.svoo_cluster(g["Q"], g["K"], 2)
+    O1, idx1 = sla.svoo_forward(g["Q"], g["K"], g["V"], g["Wq"], g["Wk"], g["alpha"], k, pq, pk)
+    Qp, Kp, Vp = sla.svoo_gather(g["Q"], pq), sla.svoo_gather(g["K"], pk), sla.svoo_gather(g["V"], pk)
+    ap = sla.svoo_gather(g["alpha"], pq)
+    idx2, _, _ = sla.route(Qp, Kp, g["Wq"], g["Wk"], k)
+    O2 = sla.svoo_scatter(sla.forward(Qp, Kp, Vp, idx2, ap, linear_mode="mask_product"), pq)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(O1, O2)
+
+
 def test_svoo_rejects_bad_arguments():
     d = torch.device("cuda:0")
     Q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device=d)
@@ -262,6 +280,12 @@ def test_svoo_rejects_bad_arguments():
         sla.svoo_cluster(Q, Q, 0)
     with pytest.raises(sla.SLAError):
         sla.svoo_cluster(Q.float(), Q.float(), 1)
+    # out_rows exists in the bf16 mask-product forward only
+    idx = torch.zeros((1, 1, 1, 1), dtype=torch.int32, device=d)
+    rows = torch.arange(64, dtype=torch.int32, device=d).view(1, 1, 64)
+    alpha = torch.ones((1, 1, 64), device=d)
+    with pytest.raises(sla.SLAError):
+        sla.forward(Q, Q, Q, idx, alpha, linear_mode="fused", out_rows=rows)
 
 
 def test_svoo_video_s_forward_sampled():
