@@ -433,7 +433,10 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   if (!row_ok) return;
   const float a = alpha[(size_t)bh * N + row];
   const float ws = a * inv_l, wl = (1.f - a) * inv_den;
-  float* orow = O + hoff + (size_t)(out_rows ? out_rows[(size_t)bh * N + row] : row) * D;
+  // out_rows entries are clamped to the sequence: a malformed permutation misplaces rows but
+  // never writes outside O
+  const int orow_i = out_rows ? min(max(out_rows[(size_t)bh * N + row], 0), N - 1) : row;
+  float* orow = O + hoff + (size_t)orow_i * D;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll

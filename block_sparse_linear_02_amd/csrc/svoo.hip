@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint32_t* __restrict
   const size_t hoff = (size_t)bh * N * words;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
     const int row = (int)(i / per), u = (int)(i % per);
-    const int pr = perm[(size_t)bh * N + row];
+    const int pr = min(max(perm[(size_t)bh * N + row], 0), N - 1);  // clamped: never outside X, Y
     const int src = scatter ? row : pr, dst = scatter ? pr : row;
     if constexpr (VEC4) {
       const i32x4 v = *reinterpret_cast<const i32x4*>(X + hoff + (size_t)src * words + 4 * u);

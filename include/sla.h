@@ -109,8 +109,9 @@ typedef struct {
   hipEvent_t idx_ready;
   /* if non-null ([B][H][N] int32, a permutation of 0 .. N-1 per (b, h)): output row r of (b, h)
    * is written to row out_rows[b][h][r] of O, e.g. SVOO's query permutation to return rows of a
-   * co-clustered sequence to their original order without a separate scatter.  Only the bf16
-   * forward in the mask-product mode supports it (else SLA_ERR_UNSUPPORTED). */
+   * co-clustered sequence to their original order without a separate scatter.  Entries are
+   * clamped to 0 .. N-1 (a malformed permutation misplaces rows, it never writes outside O).
+   * Only the bf16 forward in the mask-product mode supports it (else SLA_ERR_UNSUPPORTED). */
   const int32_t* out_rows;
 } sla_forward_opts;
 

@@ -54,9 +54,10 @@ int sla_svoo_cluster(const sla_problem* p, const void* Q, const void* K, int32_t
 
 /* Row permutations of [B][H][N] rows of row_bytes bytes each (a multiple of 4, at most 4096):
  * gather Y[b][h][p] = X[b][h][perm[b][h][p]], scatter Y[b][h][perm[b][h][p]] = X[b][h][p].
- * perm must be a permutation of 0 .. N-1 for every (b, h); X and Y must not overlap.  Q, K, V
- * (d bf16 values a row), alpha (one float) and O (d floats) all fit.  Only p->B, p->H and p->N
- * are read. */
+ * perm must be a permutation of 0 .. N-1 for every (b, h) (entries are clamped to that range,
+ * so a malformed one gives wrong rows but no access outside X and Y); X and Y must not overlap.
+ * Q, K, V (d bf16 values a row), alpha (one float) and O (d floats) all fit.  Only p->B, p->H
+ * and p->N are read. */
 int sla_svoo_gather(const sla_problem* p, const void* X, int32_t row_bytes, const int32_t* perm,
                     void* Y, hipStream_t stream);
 int sla_svoo_scatter(const sla_problem* p, const void* X, int32_t row_bytes, const int32_t* perm,
