@@ -88,6 +88,7 @@ def _load_mutant(tmp_path, fname, old, new):
     return mod
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # a mutant may divide by zero on purpose
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS))
 def test_mutation_is_caught(tmp_path, mutation):
     mod = _load_mutant(tmp_path, *MUTATIONS[mutation])
