@@ -158,7 +158,7 @@ size_t carve_pisa_ws(const sla::Dims& d, void* base, PisaWs* out) {
 
 // Backward scratch
 struct BwdWs {
-  float *zb, *z_part, *Z, *O, *Os, *Ol, *lse2, *rden, *Dr, *e, *dzeta, *dz, *zb2, *z_part2;
+  float *zb, *z_part, *Z, *O, *Os, *Ol, *lse2, *rden, *Dr, *e, *dzeta, *dz, *zb2, *z_part2, *dzt;
   __bf16 *hj_bf, *t_bf, *dh_bf, *dOs, *G;
   uint32_t *bits, *kept_t, *unsel_t;
 };
@@ -193,6 +193,7 @@ size_t carve_backward(const sla::Dims& d, void* ws, BwdWs* out) {
   w.dz = c.take<float>(blocks * d.d);
   w.zb2 = c.take<float>(blocks * d.d);
   w.z_part2 = c.take<float>(BH * nchunk * d.d);
+  w.dzt = c.take<float>(BH * d.d);
   if (out) *out = w;
   return c.off;
 }
@@ -540,7 +541,7 @@ int sla_backward(const sla_problem* p, const void* Q, const void* K, const void*
   if (e == hipSuccess)
     e = sla::launch_states(d, Q, w.G, w.zb2, nullptr, w.z_part2, nullptr, w.hj_bf, stream);
   if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.unsel_t, w.dh_bf, stream);
-  if (e == hipSuccess) e = sla::launch_bwd_dz(d, w.dzeta, w.unsel_t, w.dz, stream);
+  if (e == hipSuccess) e = sla::launch_bwd_dz(d, w.dzeta, w.kept_t, w.dzt, w.dz, stream);
   // the gradients
   if (e == hipSuccess)
     e = sla::launch_bwd_dq(d, Q, K, V, idx, w.dOs, w.lse2, w.Dr, w.G, w.e, w.t_bf, w.Z, w.zb, dQ,

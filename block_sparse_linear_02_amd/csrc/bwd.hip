@@ -118,77 +118,125 @@ __global__ __launch_bounds__(kBwdThreads) void prep_kernel(
 
 // ---------------------------------------------------------------------------------- bits
 
-// one thread per (key block j, 32-bit word w of query blocks): bit b of the kept word is set when
-// query block 32 w + b keeps j (binary search in its ascending list)
+// one workgroup per (32-bit word w of query blocks, head): the kept lists of query blocks 32 w ..
+// 32 w + 31 are read once (coalesced) and each entry j sets bit b of key block j's word in LDS;
+// then word w of every key block's kept row and of its complement (within n_b) is written out
 __global__ __launch_bounds__(256) void bits_t_kernel(const int32_t* __restrict__ idx, int nb,
                                                      int topk, int nw, uint32_t* __restrict__ kept_t,
                                                      uint32_t* __restrict__ unsel_t) {
-  const int bh = blockIdx.y;
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= nb * nw) return;
-  const int j = q / nw, w = q % nw;
-  uint32_t kb = 0;
+  __shared__ uint32_t bm[kBwdMaxWords * 32];
+  const int bh = blockIdx.y, w = blockIdx.x, tid = threadIdx.x;
+  for (int j = tid; j < nb; j += 256) bm[j] = 0u;
+  __syncthreads();
   const int valid = min(32, nb - 32 * w);
-  for (int b = 0; b < valid; ++b) {
-    const int32_t* row = idx + ((size_t)bh * nb + 32 * w + b) * topk;
-    int lo = 0, hi = topk;  // first entry >= j
-    while (lo < hi) {
-      const int mid = (lo + hi) / 2;
-      if (row[mid] < j) lo = mid + 1; else hi = mid;
-    }
-    if (lo < topk && row[lo] == j) kb |= 1u << b;
+  const int32_t* ib = idx + ((size_t)bh * nb + 32 * w) * topk;
+  for (int q = tid; q < valid * topk; q += 256) {
+    const int j = ib[q];
+    if (j >= 0 && j < nb) atomicOr(&bm[j], 1u << (q / topk));
   }
+  __syncthreads();
   const uint32_t all = valid == 32 ? 0xffffffffu : (1u << valid) - 1u;
-  kept_t[((size_t)bh * nb + j) * nw + w] = kb;
-  unsel_t[((size_t)bh * nb + j) * nw + w] = all & ~kb;
+  for (int j = tid; j < nb; j += 256) {
+    const uint32_t kb = bm[j];
+    kept_t[((size_t)bh * nb + j) * nw + w] = kb;
+    unsel_t[((size_t)bh * nb + j) * nw + w] = all & ~kb;
+  }
 }
 
 // ---------------------------------------------------------------------------------- dz
 
-// dz_j = sum_i unsel_t[j][i] dzeta_i: a workgroup takes 16 key blocks and streams dzeta in chunks
-// of 64 query blocks through LDS; thread (j = tid / 16, channels 8 (tid % 16) ..) accumulates
-// its 8 sums in query-block order (deterministic)
+// the head's total of dzeta over its query blocks: a workgroup per (32 channels, head), 32 row
+// groups x 8 lanes of 4 channels, reduced in a fixed order through LDS (deterministic)
+__global__ __launch_bounds__(256) void dz_total_kernel(const float* __restrict__ dzeta, int nb,
+                                                       float* __restrict__ tot) {
+  constexpr int D = kBwdD;
+  __shared__ float part[32][33];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int rg = tid / 8, cl = (tid % 8) * 4, c = blockIdx.x * 32 + cl;
+  const float* zb = dzeta + (size_t)bh * nb * D;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = rg; i < nb; i += 32) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(zb + (size_t)i * D + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += a[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) part[rg][cl + e] = acc[e];
+  __syncthreads();
+  if (tid < 32) {
+    float t = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) t += part[r][tid];
+    tot[(size_t)bh * D + blockIdx.x * 32 + tid] = t;
+  }
+}
+
+// dz_j = sum over the query blocks leaving j unselected of dzeta_i, formed as the head's total
+// minus the query blocks that keep j (about k of them instead of n_b - k).  A workgroup takes 16
+// key blocks and stages their kept rows in LDS; thread (j = tid / 16, channels 8 (tid % 16) ..)
+// walks its row and subtracts the kept query blocks in ascending order (deterministic), issuing
+// the row loads four at a time
 __global__ __launch_bounds__(256) void dz_kernel(const float* __restrict__ dzeta,
-                                                 const uint32_t* __restrict__ unsel_t, int nb, int nw,
+                                                 const float* __restrict__ tot,
+                                                 const uint32_t* __restrict__ kept_t, int nb, int nw,
                                                  float* __restrict__ dz) {
   constexpr int D = kBwdD;
-  __shared__ f32x4 st[kBlock][D / 4];
+  __shared__ uint32_t kw[16][kBwdMaxWords];
   const int bh = blockIdx.y;
   const int tid = threadIdx.x;
-  const int jj = tid / 16, c8 = (tid % 16) * 8;
-  const int j = blockIdx.x * 16 + jj;
+  const int j0 = blockIdx.x * 16;
+  for (int q = tid; q < 16 * nw; q += 256)
+    kw[q / nw][q % nw] = j0 + q / nw < nb ? kept_t[((size_t)bh * nb + j0) * nw + q] : 0u;
+  __syncthreads();
+  const int jj = tid / 16, j = j0 + jj, c8 = (tid % 16) * 8;
+  if (j >= nb) return;
+  const float* zb = dzeta + (size_t)bh * nb * D + c8;
+  const f32x4 t0 = *reinterpret_cast<const f32x4*>(tot + (size_t)bh * D + c8);
+  const f32x4 t1 = *reinterpret_cast<const f32x4*>(tot + (size_t)bh * D + c8 + 4);
   float acc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int i0 = 0; i0 < nb; i0 += kBlock) {
-    __syncthreads();
-    for (int q = tid; q < kBlock * D / 4; q += 256) {
-      const int r = q / (D / 4), c = q % (D / 4);
-      st[r][c] = i0 + r < nb ? reinterpret_cast<const f32x4*>(dzeta + ((size_t)bh * nb + i0 + r) * D)[c]
-                             : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 4; ++e) {
+    acc[e] = t0[e];
+    acc[4 + e] = t1[e];
+  }
+  int w = 0;
+  uint32_t m = kw[jj][0];
+  auto next = [&]() -> int {  // the next kept query block in ascending order, -1 past the end
+    while (m == 0u) {
+      if (++w >= nw) return -1;
+      m = kw[jj][w];
     }
-    __syncthreads();
-    if (j < nb) {
-      const uint32_t* br = unsel_t + ((size_t)bh * nb + j) * nw + i0 / 32;
-      const uint32_t w0 = br[0], w1 = (i0 / 32 + 1 < nw) ? br[1] : 0u;
-      for (int r = 0; r < kBlock; ++r) {
-        const uint32_t bit = ((r < 32 ? w0 >> r : w1 >> (r - 32)) & 1u);
-        if (bit) {
-          const f32x4 a = st[r][c8 / 4], b = st[r][c8 / 4 + 1];
+    const int i = 32 * w + __ffs(m) - 1;
+    m &= m - 1u;
+    return i;
+  };
+  for (;;) {
+    int i[4];
+    i[0] = next();
+    if (i[0] < 0) break;
+    i[1] = next();
+    i[2] = next();
+    i[3] = next();
+    f32x4 a[4], b[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[e] += a[e];
-            acc[4 + e] += b[e];
-          }
+    for (int u = 0; u < 4; ++u) {
+      const float* r = zb + (size_t)(i[u] < 0 ? i[0] : i[u]) * D;
+      a[u] = *reinterpret_cast<const f32x4*>(r);
+      b[u] = *reinterpret_cast<const f32x4*>(r + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i[u] >= 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] -= a[u][e];
+          acc[4 + e] -= b[u][e];
         }
       }
-    }
   }
-  if (j < nb) {
-    float* o = dz + ((size_t)bh * nb + j) * D + c8;
-    *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-  }
+  float* o = dz + ((size_t)bh * nb + j) * D + c8;
+  *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
 // ---------------------------------------------------------------------------------- dQ
@@ -699,15 +747,20 @@ hipError_t launch_bwd_prep(const Dims& p, const void* Q, const void* dO, const f
 hipError_t launch_bits_t(const Dims& p, const int32_t* idx, uint32_t* kept_t, uint32_t* unsel_t,
                          hipStream_t stream) {
   const int nw = mask_words(p.nb);
-  dim3 grid((p.nb * nw + 255) / 256, p.B * p.H);
+  if (nw > kBwdMaxWords) return hipErrorInvalidValue;
+  dim3 grid(nw, p.B * p.H);
   bits_t_kernel<<<grid, 256, 0, stream>>>(idx, p.nb, p.topk, nw, kept_t, unsel_t);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dz(const Dims& p, const float* dzeta, const uint32_t* unsel_t, float* dz,
-                         hipStream_t stream) {
+hipError_t launch_bwd_dz(const Dims& p, const float* dzeta, const uint32_t* kept_t, float* tot,
+                         float* dz, hipStream_t stream) {
+  if (p.d != kBwdD) return hipErrorInvalidValue;
+  dz_total_kernel<<<dim3(kBwdD / 32, p.B * p.H), 256, 0, stream>>>(dzeta, p.nb, tot);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid((p.nb + 15) / 16, p.B * p.H);
-  dz_kernel<<<grid, 256, 0, stream>>>(dzeta, unsel_t, p.nb, mask_words(p.nb), dz);
+  dz_kernel<<<grid, 256, 0, stream>>>(dzeta, tot, kept_t, p.nb, mask_words(p.nb), dz);
   return hipGetLastError();
 }
 

@@ -129,8 +129,8 @@ hipError_t launch_bwd_prep(const Dims& p, const void* Q, const void* dO, const f
 // key block, and the complement within n_b.
 hipError_t launch_bits_t(const Dims& p, const int32_t* idx, uint32_t* kept_t, uint32_t* unsel_t,
                          hipStream_t stream);
-hipError_t launch_bwd_dz(const Dims& p, const float* dzeta, const uint32_t* unsel_t, float* dz,
-                         hipStream_t stream);
+hipError_t launch_bwd_dz(const Dims& p, const float* dzeta, const uint32_t* kept_t, float* tot,
+                         float* dz, hipStream_t stream);
 hipError_t launch_bwd_dq(const Dims& p, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const __bf16* dOs, const float* lse2, const float* Dr,
                          const __bf16* G, const float* e, const __bf16* t_bf, const float* Z,
