@@ -81,9 +81,9 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
   Carve c(ws);
   const size_t BH = (size_t)d.B * d.H;
   const size_t dd = (size_t)d.d * d.d;
-  const int cb = sla::state_chunk_blocks(d);
-  const size_t nchunk = (d.nb + cb - 1) / cb;
   const bool mp = variant == 3 || variant == 4 || variant == 5;
+  const int cb = sla::state_chunk_blocks(d, !mp);  // the mask-product mode has no h partials
+  const size_t nchunk = (d.nb + cb - 1) / cb;
   const bool f8 = variant == 1 || variant == 4 || variant == 5;  // low-bit codes and scales
   FwdWs f = {};
   f.zb = c.take<float>(BH * d.nb * d.d);
@@ -167,7 +167,7 @@ size_t carve_backward(const sla::Dims& d, void* ws, BwdWs* out) {
   const size_t BH = (size_t)d.B * d.H;
   const size_t dd = (size_t)d.d * d.d;
   const size_t rows = BH * d.N, elems = rows * d.d, blocks = BH * d.nb;
-  const int cb = sla::state_chunk_blocks(d);
+  const int cb = sla::state_chunk_blocks(d, false);  // mask-product states: z partials only
   const size_t nchunk = (d.nb + cb - 1) / cb;
   const size_t words = blocks * sla::mask_words(d.nb);
   BwdWs w = {};

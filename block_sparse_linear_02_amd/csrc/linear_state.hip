@@ -268,7 +268,7 @@ template <class T, int D>
 hipError_t launch_states_t(const Dims& p, const void* K, const void* V, float* zb,
                            float* h_part, float* z_part, float* hj, __bf16* hj_bf,
                            hipStream_t stream, const uint32_t* flags) {
-  const int cb = state_chunk_blocks(p);
+  const int cb = state_chunk_blocks(p, hj != nullptr || hj_bf == nullptr);
   dim3 grid((p.nb + cb - 1) / cb, p.B * p.H);
   if (hj)
     state_kernel<T, D, 1><<<grid, kStateThreads, 0, stream>>>(
@@ -284,11 +284,13 @@ hipError_t launch_states_t(const Dims& p, const void* K, const void* V, float* z
 
 }  // namespace
 
-int state_chunk_blocks(const Dims& p) {
-  // about >= 512 workgroups (two per CU) while keeping the partials (64 KB per chunk at d = 128)
-  // small next to the K/V stream (32 KB per block)
+int state_chunk_blocks(const Dims& p, bool h_partials) {
+  // about >= 512 workgroups (two per CU) while keeping the partials of h (64 KB per chunk at
+  // d = 128) small next to the K/V stream (32 KB per block); a launch without them (the
+  // mask-product mode, whose chunk partials are z alone) takes about >= 1024, which keeps more
+  // tile loads in flight
   const long work = (long)p.nb * p.B * p.H;
-  long cb = work / 512;
+  long cb = work / (h_partials ? 512 : 1024);
   if (cb < 1) cb = 1;
   if (cb > 64) cb = 64;
   return (int)cb;
@@ -309,7 +311,7 @@ hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb,
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,
                                __bf16* ht_hi, __bf16* ht_lo, float* Z, float* h_full,
                                hipStream_t stream) {
-  const int cb = state_chunk_blocks(p);
+  const int cb = state_chunk_blocks(p, h_part != nullptr);
   const int nchunk = (p.nb + cb - 1) / cb;
   // 256 elements (64 float4 columns) of H^T per workgroup; Z alone without chunk partials of H
   dim3 grid(h_part ? p.d * p.d / 256 : 1, p.B * p.H);

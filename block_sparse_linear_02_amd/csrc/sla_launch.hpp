@@ -33,7 +33,7 @@ int route_max_blocks();
 // Z [d]; per block z_j [d]; optionally every h_j [d][d] (K-channel major) in fp32 (hj, literal
 // mode), or transposed, h_j^T [d][d] (V-channel major), rounded to bf16 (hj_bf, mask-product
 // mode) in slices of 64 entries: [BH][d*d/64][nb][64].
-int state_chunk_blocks(const Dims& p);
+int state_chunk_blocks(const Dims& p, bool h_partials = true);
 // flags (optional): heads flagged kDropLinear are skipped.
 hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
                          float* z_part, float* hj, __bf16* hj_bf, hipStream_t stream,
