@@ -248,16 +248,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
     }
   }
   if (z_part && blockIdx.x == 0 && threadIdx.x < D) {
-    // in chunk order (deterministic), four loads in flight
+    // in chunk order (deterministic), sixteen loads in flight
     const float* zp = z_part + (size_t)bh * nchunk * D + threadIdx.x;
     float z = 0.f;
     int c = 0;
-    for (; c + 4 <= nchunk; c += 4) {
-      float v[4];
+    for (; c + 16 <= nchunk; c += 16) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = zp[(size_t)(c + u) * D];
+      for (int u = 0; u < 16; ++u) v[u] = zp[(size_t)(c + u) * D];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) z += v[u];
+      for (int u = 0; u < 16; ++u) z += v[u];
     }
     for (; c < nchunk; ++c) z += zp[(size_t)c * D];
     Z[(size_t)bh * D + threadIdx.x] = z;
