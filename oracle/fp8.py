@@ -116,13 +116,15 @@ def quantize_blocks(X, block: int = 64, codec=None):
     return codes, scales, deq
 
 
-def forward_fp8_head(Q, K, V, idx, alpha, block: int = 64, q_blocks=None, codec=None, states=None):
+def forward_fp8_head(Q, K, V, idx, alpha, block: int = 64, q_blocks=None, codec=None, states=None, trace=None):
     """SLA2 output rows of one head with the sparse branch on quantised Q, K, P, V.
 
     SLA2 (Italian summary) section 2.C, (Arabic summary) section 2.jim: low-bit attention in the
     sparse branch only; the forward pass quantises Q, K, P and V.  The linear branch and the
     combine are those of forward_head (unquantised inputs).  ``codec`` replaces the e4m3
     encode/decode pair (identity: the structural pin).  Returns (O, O_s, O_l) lists of [r_i, d].
+    ``trace``, a list, receives (query block, key block, P^ tile, sP) for every kept tile: the
+    values the P codes are rounded from, exposed for tests that bound the effect of rounding.
     """
     Q64 = _f64(Q)
     K64 = _f64(K)
@@ -157,6 +159,8 @@ def forward_fp8_head(Q, K, V, idx, alpha, block: int = 64, q_blocks=None, codec=
             num = np.zeros((b - a, V64.shape[1]))
             for p, j in zip(P, sel):
                 sP = p.max() / E4M3_MAX
+                if trace is not None:
+                    trace.append((i, int(j), p, sP))
                 if sP == 0:
                     continue
                 num += (enc(p / sP) * sP) @ Vd[starts[j]:ends[j]]

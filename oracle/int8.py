@@ -58,12 +58,13 @@ def quantize_blocks_int8(X, block: int = 64):
     return codes, scales, deq
 
 
-def forward_int8_head(Q, K, V, idx, alpha, block: int = 64, q_blocks=None, states=None):
+def forward_int8_head(Q, K, V, idx, alpha, block: int = 64, q_blocks=None, states=None, trace=None):
     """SLA2 output rows of one head with the sparse branch on int8 Q, K, P, V.
 
     SLA2 (Italian summary) section 2.C, (Arabic summary) section 2.jim.  The linear branch and
     the combine are those of forward_head (unquantised inputs).  Returns (O, O_s, O_l) lists of
-    [r_i, d] float64 arrays in the order of q_blocks.
+    [r_i, d] float64 arrays in the order of q_blocks.  ``trace``, a list, receives (query block,
+    key block, P^ tile, sP) for every kept tile (as in forward_fp8_head).
     """
     Q64 = _f64(Q)
     K64 = _f64(K)
@@ -99,6 +100,8 @@ def forward_int8_head(Q, K, V, idx, alpha, block: int = 64, q_blocks=None, state
             num = np.zeros((b - a, V64.shape[1]))
             for p, j in zip(P, sel):
                 sP = p.max() / INT8_MAX
+                if trace is not None:
+                    trace.append((i, int(j), p, sP))
                 if sP == 0:
                     continue
                 p8 = int8_encode(p / sP).astype(np.int64)

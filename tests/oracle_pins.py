@@ -385,6 +385,51 @@ def pin_fp8_error_scale(orc):
     assert 5e-3 < rel < 0.1, rel
 
 
+def _lowbit_golden(kind):
+    """Inputs of tests/golden/lowbit_p_worked_example.json for 'fp8' or 'int8' (the carrier
+    value c makes every block's Q, K, V quantisation exact)."""
+    with open(os.path.join(GOLDEN, "lowbit_p_worked_example.json")) as f:
+        g = json.load(f)
+    c = g["carrier"][kind]
+    arr = lambda rows: np.array([[c if x == "c" else float(x) for x in r] for r in rows])  # noqa: E731
+    return g, arr(g["Q"]), arr(g["K"]), arr(g["V"]), np.array(g["idx"], dtype=np.int32), c
+
+
+def _lowbit_expected_from_codes(g, kind, V):
+    """O_s of the worked example's query block from its hand-listed codes: the sum over keys of
+    code * (tile maximum / largest code) * v, over the sum of the unquantised exp(S - m)."""
+    qmax = 448.0 if kind == "fp8" else 127.0
+    blk = g["block"]
+    ex = np.array(g["exponents_S_minus_m"], dtype=np.float64)
+    tile = np.exp(np.array(g["tile_max_exponent"], dtype=np.float64))
+    deq = np.array(g["codes"][kind], dtype=np.float64) * (tile[np.arange(ex.shape[1]) // blk] / qmax)[None, :]
+    return (deq @ V) / np.exp(ex).sum(axis=1, keepdims=True)
+
+
+def pin_fp8_p_quantisation_worked_example(orc):
+    """The hand-derived e4m3 case in tests/golden/lowbit_p_worked_example.json: one P scale per
+    (query block x key block) tile, the exact row maximum, the denominator over the unquantised
+    P^.  Rows with different maxima inside one tile and a tile holding no row maximum make a
+    per-row or per-query-block scale, or a dequantised denominator, give other values."""
+    g, Q, K, V, idx, _ = _lowbit_golden("fp8")
+    want = np.array(g["expected_O_s"]["fp8"])
+    np.testing.assert_allclose(_lowbit_expected_from_codes(g, "fp8", V), want, rtol=0, atol=1e-13)
+    qb = g["query_block"]
+    _, Os, _ = orc.forward_fp8_head(Q, K, V, idx, np.ones(g["N"]), g["block"], q_blocks=[qb])
+    np.testing.assert_allclose(Os[0], want, rtol=0, atol=1e-12)
+
+
+def pin_int8_p_quantisation_worked_example(orc):
+    """The int8 half of tests/golden/lowbit_p_worked_example.json (same readings as the e4m3
+    case, largest code 127, round to nearest integer)."""
+    g, Q, K, V, idx, _ = _lowbit_golden("int8")
+    want = np.array(g["expected_O_s"]["int8"])
+    np.testing.assert_allclose(_lowbit_expected_from_codes(g, "int8", V), want, rtol=0, atol=1e-13)
+    qb = g["query_block"]
+    _, Os, _ = orc.forward_int8_head(Q, K, V, idx, np.ones(g["N"]), g["block"], q_blocks=[qb])
+    np.testing.assert_allclose(Os[0], want, rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------------------------
 # backward (training path)
 

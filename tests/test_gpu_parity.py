@@ -17,6 +17,7 @@ import block_sparse_linear_02_amd as sla
 import gen
 import oracle
 from tests import cases
+from tests import lowbit_slack
 
 pytestmark = pytest.mark.gpu
 
@@ -357,6 +358,41 @@ def test_int8_forward(k):
                     rel_tol=TOL_REL_FP8, max_tol=None, what=f"int8 sparse branch alone k={k}")
 
 
+@pytest.mark.parametrize("k", [6, 30])
+def test_lowbit_p_reading_conformance(k):
+    """alpha = 1: the fp8 (fused and mask-product kernels) and int8 sparse branches alone against
+    the oracle's O_s, element by element within the flip-aware bound of tests/lowbit_slack.py:
+    one code step for P entries whose code the kernels' fp32 rounding (and, for e4m3, the fp8
+    product's accumulation) may decide either way, plus a small relative tolerance of each row's
+    magnitude.  Another reading of the P step (a per-row or per-query-block
+    scale, a dequantised denominator) breaks it on thousands of elements, which the 3e-2
+    acceptance bar cannot see."""
+    wl = small_ragged(k=k)
+    c = case(f"ragged_k{k}", wl)
+    r = oracle_route(c, k)
+    one = torch.ones_like(c["alpha"]).to(torch.device("cuda:0"))
+    starts, ends, _ = oracle.block_ranges(wl.N, 64)
+    qb = list(range(wl.n_blocks))
+    runs = [("fp8", "fused"), ("fp8", "mask_product"), ("int8", "mask_product")]
+    gots = {run: run_forward(c, r["idx"], alpha=one, linear_mode=run[1], **{run[0]: True}) for run in runs}
+    for fmt in ("fp8", "int8"):
+        head = oracle.forward_fp8_head if fmt == "fp8" else oracle.forward_int8_head
+        quant = oracle.quantize_blocks if fmt == "fp8" else oracle.quantize_blocks_int8
+        for h in range(wl.H):
+            trace = []
+            _, Os, _ = head(c["Q"][0, h], c["K"][0, h], c["V"][0, h], r["idx"][0, h], np.ones(wl.N), 64, trace=trace)
+            Qd, Kd, Vd = (quant(c[n][0, h], 64)[2] for n in ("Q", "K", "V"))
+            sl = lowbit_slack.slack_rows(trace, Vd, starts, ends, qb, fmt, Qd, Kd)
+            slack = np.concatenate([s_ for s_, _ in sl])
+            tol = np.concatenate([t_ for _, t_ in sl])
+            ref = np.concatenate(Os)
+            for run in [x for x in runs if x[0] == fmt]:
+                got = gots[run][0, h]
+                res = lowbit_slack.check_within_slack(got, ref, slack, tol)
+                say(f"{fmt} P reading k={k} {run[1]} head {h}: rel-L2 {rel_l2(got, ref):.3e} {res}")
+                assert res["violations"] == 0, (fmt, run, h, res)
+
+
 def test_fp8_forward_branches_isolated():
     """alpha = 1: the quantised sparse branch alone; alpha = 0: the linear branch, unquantised."""
     wl = small_ragged()
@@ -434,21 +470,37 @@ def test_branch_drop_full_size():
 # ---------------------------------------------------------------------------------- full size
 
 
-def sampled_compare(c, idx_np, got_O, heads, blocks, fp8=False, what=""):
+def oracle_blocks(c, idx_np, heads, blocks, fp8=False, alpha=None):
+    """Oracle output rows of the given query blocks of the given (flattened b*H + h) heads,
+    concatenated in that order; blocks=None means every query block."""
     wl = c["workload"]
-    gots, refs = [], []
+    alpha = c["alpha"] if alpha is None else alpha
+    refs = []
     for bh in heads:
         b, h = divmod(bh, wl.H)
-        args = (c["Q"][b, h], c["K"][b, h], c["V"][b, h], idx_np[b, h], c["alpha"][b, h], 64)
-        if fp8:
-            o, _, _ = oracle.forward_fp8_head(*args, q_blocks=blocks)
+        args = (c["Q"][b, h], c["K"][b, h], c["V"][b, h], idx_np[b, h], alpha[b, h], 64)
+        qb = list(range(wl.n_blocks)) if blocks is None else blocks
+        o, _, _ = (oracle.forward_fp8_head if fp8 else oracle.forward_head)(*args, q_blocks=qb)
+        refs.extend(o)
+    return np.concatenate(refs)
+
+
+def gpu_blocks(c, got_O, heads, blocks):
+    """The GPU rows matching oracle_blocks(c, ..., heads, blocks)."""
+    wl = c["workload"]
+    gots = []
+    for bh in heads:
+        b, h = divmod(bh, wl.H)
+        if blocks is None:
+            gots.append(got_O[b, h])
         else:
-            o, _, _ = oracle.forward_head(*args, q_blocks=blocks)
-        for i, oi in zip(blocks, o):
-            refs.append(oi)
-            gots.append(got_O[b, h, i * 64 : i * 64 + len(oi)])
-    got = np.concatenate(gots)
-    ref = np.concatenate(refs)
+            gots.extend(got_O[b, h, i * 64 : min((i + 1) * 64, wl.N)] for i in blocks)
+    return np.concatenate(gots)
+
+
+def sampled_compare(c, idx_np, got_O, heads, blocks, fp8=False, what=""):
+    ref = oracle_blocks(c, idx_np, heads, blocks, fp8=fp8)
+    got = gpu_blocks(c, got_O, heads, blocks)
     if fp8:
         check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what=what)
     else:
@@ -481,9 +533,47 @@ def test_video_s_full_size_mask_product():
     full_size(c, heads=[0, 7], blocks=[0, 300, 511], what="video_s mask_product", linear_mode="mask_product")
 
 
-def test_video_l_full_size():
+@pytest.mark.parametrize("mode", ["fused", "mask_product"])
+def test_video_l_full_size(mode):
     c = case("video_l", gen.workload("video_l"))
-    full_size(c, heads=[0, 39], blocks=[0, 600, 1181], what="video_l N=75600 H=40 k=60")
+    full_size(c, heads=[0, 39], blocks=[0, 600, 1181], what=f"video_l N=75600 H=40 k=60 {mode}",
+              linear_mode=mode)
+
+
+def test_video_s_whole_output_mask_product():
+    """The benchmarked launch (router, then the mask-product forward) at N=32768 H=12 k=51 against
+    the oracle on every output element: every query block of every head."""
+    c = case("video_s", gen.workload("video_s"))
+    wl = c["workload"]
+    g = dev(c)
+    say("video_s whole output: route + mask_product forward")
+    idx, _, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], wl.topk)
+    r = oracle_route(c, wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"]), "video_s: router indices differ"
+    O = sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], linear_mode="mask_product")
+    torch.cuda.synchronize()
+    got = O.cpu().double().numpy()
+    say("video_s whole output: oracle (12 heads)")
+    ref, _, _ = oracle.forward(c["Q"], c["K"], c["V"], r["idx"], c["alpha"], 64)
+    check_close(got, ref, what="video_s whole output mask_product")
+
+
+def test_video_l_whole_head_mask_product():
+    """N=75600 (1182 key blocks, a 16-token last block) in the benchmarked mask-product mode:
+    every query block of two heads against the oracle."""
+    c = case("video_l", gen.workload("video_l"))
+    wl = c["workload"]
+    g = dev(c)
+    say("video_l whole heads: route + mask_product forward")
+    idx, _, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], wl.topk)
+    r = oracle_route(c, wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"]), "video_l: router indices differ"
+    O = sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], linear_mode="mask_product")
+    torch.cuda.synchronize()
+    got = O.cpu().double().numpy()
+    say("video_l whole heads: oracle (heads 7, 38)")
+    ref = oracle_blocks(c, r["idx"], [7, 38], None)
+    check_close(gpu_blocks(c, got, [7, 38], None), ref, what="video_l whole heads mask_product")
 
 
 def test_video_l_fp8_full_size():
@@ -523,7 +613,8 @@ def test_video_l_int8_full_size():
 @pytest.mark.parametrize("scale", [0.5, 1.0, 2.0])
 def test_sparsity_sweep(scale, k):
     """keep {20,10,5,3}% of 512 key blocks at cluster scale {0.5,1,2}, B=2, H=12, N=32768;
-    alpha fixed at 0.5 and random sigmoid(N(0,1)) (the same Q, K, V for both)."""
+    alpha fixed at 0.5 and random sigmoid(N(0,1)) (the same Q, K, V for both); the fused and the
+    mask-product linear modes."""
     wl = gen.workload("video_s").with_(B=2, topk=k, cluster_scale=scale, name=f"sweep_s{scale:g}_k{k}", wid=4)
     c = case(wl.name, wl)
     g = dev(c)
@@ -533,12 +624,13 @@ def test_sparsity_sweep(scale, k):
     assert np.array_equal(idx.cpu().numpy(), r["idx"]), f"sweep s={scale} k={k}: indices differ"
     for a in ("half", "random"):
         alpha = torch.full_like(g["alpha"], 0.5) if a == "half" else g["alpha"]
-        cc = dict(c, alpha=alpha.cpu())
-        say(f"sweep s={scale} k={k} alpha={a} forward")
-        O = sla.forward(g["Q"], g["K"], g["V"], idx, alpha)
-        torch.cuda.synchronize()
-        sampled_compare(cc, r["idx"], O.cpu().double().numpy(), heads=[0, 23], blocks=[0, 511],
-                        what=f"sweep s={scale} k={k} alpha={a}")
+        ref = oracle_blocks(c, r["idx"], [0, 23], [0, 511], alpha=alpha.cpu())
+        for mode in ("fused", "mask_product"):
+            say(f"sweep s={scale} k={k} alpha={a} forward {mode}")
+            O = sla.forward(g["Q"], g["K"], g["V"], idx, alpha, linear_mode=mode)
+            torch.cuda.synchronize()
+            check_close(gpu_blocks(c, O.cpu().double().numpy(), [0, 23], [0, 511]), ref,
+                        what=f"sweep s={scale} k={k} alpha={a} {mode}")
     _CACHE.pop(wl.name, None)  # keep host memory bounded
 
 

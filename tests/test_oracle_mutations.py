@@ -1,7 +1,8 @@
 """Planted mistakes in a copy of the oracle must each fail at least one pin (CPU only).
 
-Each mutation edits one line of the oracle's source in a temporary copy of the package (the
-real oracle is never touched), imports the copy, and runs every pin against it.
+Each mutation edits the oracle's source in a temporary copy of the package (one line, or a few
+lines that only make sense together; the real oracle is never touched), imports the copy, and runs
+every pin against it.
 """
 
 import importlib.util
@@ -12,6 +13,11 @@ import uuid
 
 import pytest
 
+import numpy as np
+
+import gen
+import oracle
+from tests import lowbit_slack
 from tests.oracle_pins import ALL_PINS
 
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
@@ -70,17 +76,36 @@ MUTATIONS = {
     "svoo_alpha_unpermuted": ("svoo.py", "ap = np.take_along_axis(alpha, pq, axis=2)", "ap = alpha"),
     "svoo_v_by_query_perm": ("svoo.py", "Vp = np.take_along_axis(V, pk[..., None], axis=2)", "Vp = np.take_along_axis(V, pq[..., None], axis=2)"),
     "fp8_tile_scale_dropped": ("fp8.py", "num += (enc(p / sP) * sP) @ Vd[starts[j]:ends[j]]", "num += enc(p / sP) @ Vd[starts[j]:ends[j]]"),
+    # low-bit P quantisation: other granularities of the P scale and a denominator over the
+    # dequantised P (SLA2, Arabic summary section 2.jim fixes neither; the readings are one scale
+    # per query-block x key-block tile and the unquantised P^ in the denominator)
+    "fp8_p_scale_per_row": ("fp8.py", [
+        ("sP = p.max() / E4M3_MAX", "sP = p.max(axis=1, keepdims=True) / E4M3_MAX"),
+        ("if sP == 0:\n                    continue\n                ", "")]),
+    "fp8_p_scale_per_query_block": ("fp8.py", "sP = p.max() / E4M3_MAX", "sP = max(x.max() for x in P) / E4M3_MAX"),
+    "fp8_dequantised_denominator": ("fp8.py", "den = np.sum([p.sum(axis=1) for p in P], axis=0)[:, None]",
+                                    "den = np.sum([(enc(p / (p.max() / E4M3_MAX)) * (p.max() / E4M3_MAX)).sum(axis=1) for p in P], axis=0)[:, None]"),
+    "int8_p_scale_per_row": ("int8.py", [
+        ("sP = p.max() / INT8_MAX", "sP = p.max(axis=1, keepdims=True) / INT8_MAX"),
+        ("if sP == 0:\n                    continue\n                ", "")]),
+    "int8_p_scale_per_query_block": ("int8.py", "sP = p.max() / INT8_MAX", "sP = max(x.max() for x in P) / INT8_MAX"),
+    "int8_dequantised_denominator": ("int8.py", "den = np.sum([p.sum(axis=1) for p in P], axis=0)[:, None]",
+                                     "den = np.sum([(int8_encode(p / (p.max() / INT8_MAX)) * (p.max() / INT8_MAX)).sum(axis=1) for p in P], axis=0)[:, None]"),
 }
 
 
-def _load_mutant(tmp_path, fname, old, new):
+def _load_mutant(tmp_path, fname, *edit):
+    """Copy the oracle, apply the edit (one (old, new) pair, or a list of them) and import it."""
+    pairs = edit[0] if len(edit) == 1 else [edit]
     name = f"oracle_mutant_{uuid.uuid4().hex[:8]}"
     dst = tmp_path / name
     shutil.copytree(ORACLE_DIR, dst, ignore=shutil.ignore_patterns("__pycache__"))
     path = dst / fname
     src = path.read_text()
-    assert src.count(old) == 1, f"mutation anchor not unique in {fname}: {old!r}"
-    path.write_text(src.replace(old, new))
+    for old, new in pairs:
+        assert src.count(old) == 1, f"mutation anchor not unique in {fname}: {old!r}"
+        src = src.replace(old, new)
+    path.write_text(src)
     spec = importlib.util.spec_from_file_location(name, dst / "__init__.py", submodule_search_locations=[str(dst)])
     mod = importlib.util.module_from_spec(spec)
     sys.modules[name] = mod
@@ -99,3 +124,49 @@ def test_mutation_is_caught(tmp_path, mutation):
         except Exception:  # an AssertionError, or the mutant crashing on a pin's input
             caught.append(name)
     assert caught, f"no pin catches the planted mistake '{mutation}'"
+
+
+READING_MUTATIONS = ["fp8_p_scale_per_row", "fp8_p_scale_per_query_block", "fp8_dequantised_denominator",
+                     "int8_p_scale_per_row", "int8_p_scale_per_query_block", "int8_dequantised_denominator"]
+# an implementation with the oracle's readings whose P^ carries a relative error of 3e-6 (about
+# the fp32 rounding of the kernels' exponent argument at logits near 30)
+P_NOISE = ("P = [np.exp(s - m) for s in S]",
+           "P = [np.exp(s - m) * (1 + 3e-6 * np.random.default_rng(1).standard_normal(s.shape)) for s in S]")
+
+
+@pytest.fixture(scope="module")
+def _reading_case():
+    wl = gen.workload("video_l", H=1, N=3600, grid=(1, 45, 80), topk=6)  # 57 blocks, last 16 tokens
+    c = gen.draw(wl, 0)
+    idx = oracle.route(c["Q"], c["K"], c["Wq"].double(), c["Wk"].double(), wl.topk, 64)["idx"][0, 0]
+    starts, ends, _ = oracle.block_ranges(wl.N, 64)
+    args = (c["Q"][0, 0], c["K"][0, 0], c["V"][0, 0], idx, np.ones(wl.N), 64)
+    ref = {}
+    for fmt, head, quant in (("fp8", oracle.forward_fp8_head, oracle.quantize_blocks),
+                             ("int8", oracle.forward_int8_head, oracle.quantize_blocks_int8)):
+        trace = []
+        Os = np.concatenate(head(*args, trace=trace)[1])
+        Qd, Kd, Vd = (quant(c[n][0, 0], 64)[2] for n in ("Q", "K", "V"))
+        sl = lowbit_slack.slack_rows(trace, Vd, starts, ends, range(wl.n_blocks), fmt, Qd, Kd)
+        ref[fmt] = (Os, np.concatenate([s_ for s_, _ in sl]), np.concatenate([m_ for _, m_ in sl]))
+    return args, ref
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("mutation", READING_MUTATIONS + ["fp8_noise", "int8_noise"])
+def test_lowbit_slack_separates_readings(tmp_path, _reading_case, mutation):
+    """On the small ragged clustered workload of the GPU reading test, the flip-aware bound of
+    tests/lowbit_slack.py accepts an implementation of the oracle's readings whose P^ carries
+    fp32-sized errors (rel-L2 about 4e-4 from code flips alone) and rejects every other reading
+    of the P step on many elements."""
+    args, ref = _reading_case
+    kind = mutation.split("_")[0]
+    fname = "fp8.py" if kind == "fp8" else "int8.py"
+    mod = _load_mutant(tmp_path, fname, *P_NOISE) if mutation.endswith("noise") else _load_mutant(tmp_path, *MUTATIONS[mutation])
+    head = mod.forward_fp8_head if kind == "fp8" else mod.forward_int8_head
+    got = np.concatenate(head(*args)[1])
+    res = lowbit_slack.check_within_slack(got, *ref[kind])
+    if mutation.endswith("noise"):
+        assert res["violations"] == 0, res
+    else:
+        assert res["violations"] > 1000, (mutation, res)
