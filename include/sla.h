@@ -79,9 +79,11 @@ typedef struct {
  * SLA_LINEAR_LITERAL: every h_j = relu(K_j)^T V_j is materialised in the workspace and a
  *   separate kernel sums the kept ones per query block before applying relu(Q).
  * SLA_LINEAR_MASK_PRODUCT: every h_j is materialised in bf16 and
- *   T_i = H - sum_{j in sel(i)} h_j is formed for all query blocks at once as the product of the
- *   0/1 mask with the stacked states (one MFMA GEMM per head, fp32 accumulation), stored in bf16;
- *   the sparse kernel applies relu(Q) to its T_i.  The two bf16 roundings put a relative error
+ *   T_i = sum_{j not in sel(i)} h_j is formed for all query blocks at once as the product of the
+ *   complement (unselected) 0/1 mask, built from idx as a bit mask, with the stacked states (one
+ *   MFMA GEMM per head, fp32 accumulation), stored in bf16; the sparse kernel applies relu(Q)
+ *   to its T_i.  The unselected blocks are summed directly, never as H minus the kept ones, so
+ *   no cancellation appears when almost every block is kept.  The two bf16 roundings put a relative error
  *   of about 2^-9 on the linear branch's numerator (the other modes keep it near fp32). */
 enum { SLA_LINEAR_FUSED = 0, SLA_LINEAR_LITERAL = 1, SLA_LINEAR_MASK_PRODUCT = 2 };
 
