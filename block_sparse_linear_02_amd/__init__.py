@@ -38,6 +38,7 @@ __all__ = [
     "lib",
     "lib_path",
     "route",
+    "route_noalloc",
     "forward",
     "quantize_e4m3",
     "quantize_int8",
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
         L.sla_forward_workspace_bytes.restype = sz
         L.sla_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sla_route.restype = i32
+        L.sla_route_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.sla_route_noalloc.restype = i32
         fwd = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("sla_forward", "sla_forward_fp8"):
             getattr(L, name).argtypes = fwd
@@ -212,6 +215,25 @@ def route(Q, K, proj_q, proj_k, topk: int, want_mask: bool = False, want_scores:
                          _ptr(mask), _ptr(scores), _ptr(ws), ws.numel(), _stream())
     if st != SLA_OK:
         raise SLAError(st, "sla_route")
+    return idx, mask, scores
+
+
+def route_noalloc(Q, K, proj_q, proj_k, idx, mask=None, scores=None):
+    """The router on the library's static per-GPU scratch (sla_route_noalloc): no workspace, and
+    the caller passes every output (idx [B, H, n_b, topk] int32; mask, scores optional), so the
+    call allocates nothing.  Q, K, proj_q and proj_k must already be contiguous, with proj_q and
+    proj_k in float32.  Calls that overlap on one GPU share the scratch and race."""
+    _check_qkv(Q, K)
+    for t in (Q, K, proj_q, proj_k, idx):
+        if not t.is_contiguous():
+            raise ValueError("route_noalloc takes contiguous tensors")
+    if proj_q.dtype != torch.float32 or proj_k.dtype != torch.float32 or idx.dtype != torch.int32:
+        raise ValueError("route_noalloc takes float32 projections and an int32 idx")
+    p = _problem(Q, idx.shape[-1])
+    st = lib().sla_route_noalloc(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(proj_q), _ptr(proj_k),
+                                 _ptr(idx), _ptr(mask), _ptr(scores), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_route_noalloc")
     return idx, mask, scores
 
 

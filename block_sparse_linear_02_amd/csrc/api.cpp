@@ -4,8 +4,10 @@
 #include "sla_pisa.h"
 #include "sla_svoo.h"
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "sla_launch.hpp"
 
@@ -337,6 +339,36 @@ int permute_impl(const sla_problem* p, const void* X, int32_t row_bytes, const i
   return SLA_OK;
 }
 
+// Static workspace of sla_route_noalloc: one copy per GPU, alive until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: only the address that
+// hipGetSymbolAddress returns (kept per device below) is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[SLA_ROUTE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's `scratch`, looked up on the first call with the device current.
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return SLA_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e);
+      if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return SLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -361,6 +393,25 @@ int sla_route(const sla_problem* p, const void* Q, const void* K, const float* p
   if (st != SLA_OK) return st;
   if (!Q || !K || !proj_q || !proj_k || (d.topk > 0 && !idx) || !ws) return SLA_ERR_INVALID;
   if (ws_bytes < carve_route(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  RouteWs w;
+  carve_route(d, ws, &w);
+  hipError_t e = sla::launch_route(d, Q, K, proj_q, proj_k, w.q_hi, w.q_lo, w.k_hi, w.k_lo, idx,
+                                   mask, scores, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+int sla_route_noalloc(const sla_problem* p, const void* Q, const void* K, const float* proj_q,
+                      const float* proj_k, int32_t* idx, uint8_t* mask, float* scores,
+                      hipStream_t stream) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !K || !proj_q || !proj_k || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
+  if (carve_route(d, nullptr, nullptr) > SLA_ROUTE_NOALLOC_SCRATCH_BYTES) return SLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != SLA_OK) return st;
   RouteWs w;
   carve_route(d, ws, &w);
   hipError_t e = sla::launch_route(d, Q, K, proj_q, proj_k, w.q_hi, w.q_lo, w.k_hi, w.k_lo, idx,

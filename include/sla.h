@@ -206,6 +206,23 @@ int sla_backward(const sla_problem* p, const void* Q, const void* K, const void*
                  float* dV, float* dalpha, float* O, void* ws, size_t ws_bytes,
                  hipStream_t stream);
 
+/* Allocation-free router, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): sla_route with the
+ * workspace taken from a static device array of SLA_ROUTE_NOALLOC_SCRATCH_BYTES bytes inside
+ * the library instead of an argument.  Each GPU the library runs on holds its own copy of the
+ * array from the first call on it until the process ends; the call allocates nothing and calls
+ * no allocating routine.  The array's address is looked up once per device, with that device
+ * current, on its first call; call with the stream's device current (as torch does).  Every call
+ * on a GPU shares that GPU's array (nothing in it needs to start at zero; the router overwrites
+ * what it reads), so calls that overlap on one GPU (two streams, two threads) race: serialise
+ * them.  A problem whose sla_route_workspace_bytes() exceeds the array gives
+ * SLA_ERR_WORKSPACE (4 * B * H * n_b * d bf16 values plus alignment, e.g. B*H = 40 heads at
+ * N = 75600, d = 128 need 48.4 MB).  Other arguments and errors as sla_route. */
+#define SLA_ROUTE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sla_route_noalloc(const sla_problem* p, const void* Q, const void* K, const float* proj_q,
+                      const float* proj_k, int32_t* idx, uint8_t* mask, float* scores,
+                      hipStream_t stream);
+
 const char* sla_status_string(int status);
 /* hipError_t of the most recent SLA_ERR_HIP on the calling thread (0 if none). */
 int sla_last_hip_error(void);
