@@ -80,6 +80,21 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base)
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
 
+// Buffer resource over `bytes` bytes at `base` (raw buffer: stride 0, the offset is a byte
+// offset; reads at or past `bytes` return zero).  Word 3 = 0x00020000 (32-bit data format, no
+// swizzle) for gfx9-class buffer instructions.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Asynchronous 16-byte buffer -> LDS copy (gfx950 buffer_load_dwordx4 ... lds): lane i's 16
+// bytes from rsrc + voff + soff land at lds_wave_base + 16 i.  voff is per lane (a VGPR), soff
+// wavefront-uniform (an SGPR), so a tile walk adds no per-lane address arithmetic.
+__device__ __forceinline__ void load_lds16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                               void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           voff, soff, 0, 0);
+}
+
 // Wave-wide reductions over all 64 lanes.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -113,6 +113,29 @@ __device__ __forceinline__ void load_tile_direct(const __bf16* src, __bf16* tile
   }
 }
 
+// load_tile_direct through a buffer resource: the tile starts `soff` bytes into the resource
+// (wavefront-uniform), each lane's offset inside it is lane_voff(tid).  Rows past the
+// resource's end read as zero.
+template <int THREADS>
+__device__ __forceinline__ uint32_t tile_lane_voff(int tid) {
+  constexpr int NW = THREADS / 64;
+  static_assert(NW == 4, "the per-lane offset is load-invariant for four wavefronts");
+  const int w = tid / 64, lane = tid % 64;
+  const int f = 4 * (lane / 16) + (w & 3);
+  return (uint32_t)(((lane / 16) * 128 + ((lane % 16) ^ f) * 8) * 2);
+}
+template <int THREADS>
+__device__ __forceinline__ void load_tile_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                              __bf16* tile, int tid) {
+  constexpr int NW = THREADS / 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+#pragma unroll
+  for (int u = 0; u < 16 / NW; ++u) {
+    const int r0 = 4 * (NW * u + w);
+    load_lds16_buf(rsrc, voff, soff + (uint32_t)r0 * 256u, tile + r0 * 128);
+  }
+}
+
 // load_tile_direct for a tile of `valid` < 64 rows: rows at or past `valid` re-read the last
 // valid row (every address stays inside the source tensor); the caller zeroes them with
 // zero_tile_rows once the loads have landed.
