@@ -17,6 +17,8 @@ Sources (cited by page title and section; the summaries number their sections th
   Profiling and Online Bidirectional Co-Clustering" (SVOO) - Italian summary
   (gist.science/it/paper/2603.18636), section 2.B (online bidirectional co-clustering):
   ``svoo.py``.
+* SLA2's training path (SoftTop-k router, soft-mask forward and its gradients, the stage-1 MSE
+  fit of proj_q, proj_k and alpha): ``soft.py``.
 * "SALAD: Achieve High-Sparsity Attention via Efficient Linear Attention Tuning for Video
   Diffusion Transformer" (gist.science/it/paper/2601.16515), section 2 (ReLU kernel function,
   linear branch sharing Q, K, V with the sparse branch).
@@ -69,4 +71,17 @@ from .svoo import (  # noqa: F401
     svoo_cocluster,
     svoo_order,
     svoo_forward,
+)
+from .soft import (  # noqa: F401
+    soft_topk,
+    soft_topk_backward,
+    soft_route,
+    forward_soft_head,
+    forward_soft,
+    backward_soft_head,
+    backward_soft,
+    router_backward,
+    full_attention,
+    stage1_loss,
+    stage1_grads,
 )

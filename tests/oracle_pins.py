@@ -898,4 +898,135 @@ def pin_svoo_forward_permutation_invariant_limits(orc):
     np.testing.assert_allclose(O, (1 - alpha[..., None]) * lin, rtol=1e-10, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------------------------
+# SoftTop-k training path
+
+
+def pin_soft_topk_budget_and_hard_limit(orc):
+    """Every row of the soft mask sums to k with entries in (0, 1), ranks like the scores, and as
+    the temperature goes to 0 it becomes the HardTop-k mask (scores with distinct values)."""
+    rng = np.random.default_rng(301)
+    s = rng.standard_normal((3, 4, 40))
+    for k in (1, 7, 39):
+        M = orc.soft_topk(s, k, 0.5)
+        np.testing.assert_allclose(M.sum(axis=-1), k, rtol=0, atol=1e-10)
+        assert np.all((M > 0) & (M < 1))
+        order = np.argsort(s, axis=-1)
+        assert np.all(np.diff(np.take_along_axis(M, order, axis=-1), axis=-1) >= 0)
+        hard = orc.hard_topk(s, k)[1]
+        np.testing.assert_allclose(orc.soft_topk(s, k, 1e-5), hard, rtol=0, atol=1e-6)
+    np.testing.assert_array_equal(orc.soft_topk(s, 0, 0.5), 0.0)
+    np.testing.assert_array_equal(orc.soft_topk(s, 40, 0.5), 1.0)
+
+
+def pin_soft_topk_backward_finite_differences(orc):
+    """The implicit gradient of the budget-constrained mask matches central differences of the
+    forward along random directions (tau re-solved at every point)."""
+    rng = np.random.default_rng(302)
+    s = rng.standard_normal((2, 25))
+    T, k, eps = 0.7, 6, 1e-6
+    M = orc.soft_topk(s, k, T)
+    for _ in range(3):
+        dM = rng.standard_normal(s.shape)
+        u = rng.standard_normal(s.shape)
+        num = ((orc.soft_topk(s + eps * u, k, T) - orc.soft_topk(s - eps * u, k, T)) * dM).sum() / (2 * eps)
+        ana = (orc.soft_topk_backward(M, dM, T, k) * u).sum()
+        np.testing.assert_allclose(ana, num, rtol=1e-6, atol=1e-9)
+
+
+def _soft_case(seed, N=150, d=8, blk=32):
+    rng = np.random.default_rng(seed)
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    Q[:, 0] = np.abs(Q[:, 0]) + 0.1  # no zero linear denominators
+    K[:, 0] = np.abs(K[:, 0]) + 0.1
+    nb = -(-N // blk)
+    M = rng.uniform(0.05, 0.95, (nb, nb))
+    alpha = rng.uniform(0.1, 0.9, N)
+    return Q, K, V, M, alpha, blk
+
+
+def pin_soft_forward_binary_mask_is_hard_forward(orc):
+    """A 0/1 soft mask gives exactly the HardTop-k forward of the kept sets it encodes."""
+    Q, K, V, _, alpha, blk = _soft_case(303)
+    nb = -(-Q.shape[0] // blk)
+    idx = _rand_idx(nb, 2, 304)
+    M = np.zeros((nb, nb))
+    for i in range(nb):
+        M[i, idx[i]] = 1.0
+    O, Os, Ol, _, _ = orc.forward_soft_head(Q, K, V, M, alpha, blk)
+    Oh, Osh, Olh = orc.forward(Q[None, None], K[None, None], V[None, None], idx[None, None], alpha[None, None], blk)
+    np.testing.assert_allclose(Os, Osh[0, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Ol, Olh[0, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O, Oh[0, 0], rtol=1e-12, atol=1e-12)
+
+
+def pin_soft_forward_limits(orc):
+    """M = 1 with alpha = 1 is full softmax attention (torch SDPA); M = 0 with alpha = 0 is plain
+    ReLU linear attention over every key."""
+    Q, K, V, _, _, blk = _soft_case(305)
+    N = Q.shape[0]
+    nb = -(-N // blk)
+    O1 = orc.forward_soft_head(Q, K, V, np.ones((nb, nb)), np.ones(N), blk)[0]
+    np.testing.assert_allclose(O1, _sdpa(Q, K, V), rtol=1e-10, atol=1e-12)
+    O0 = orc.forward_soft_head(Q, K, V, np.zeros((nb, nb)), np.zeros(N), blk)[0]
+    rq, rk = np.maximum(Q, 0), np.maximum(K, 0)
+    np.testing.assert_allclose(O0, (rq @ (rk.T @ V)) / (rq @ rk.sum(axis=0))[:, None], rtol=1e-10, atol=1e-12)
+
+
+def _torch_soft_forward(Q, K, V, M, alpha, blk):
+    """A dense float64 torch re-statement of the soft-mask forward (token-level weights), written
+    independently of the oracle, for autograd."""
+    N, d = Q.shape
+    bid = torch.arange(N) // blk
+    W = M[bid][:, bid]  # weight of key n for query t: M[block(t), block(n)]
+    x = (Q @ K.T) / math.sqrt(d)
+    e = W * torch.exp(x - x.max(dim=1, keepdim=True).values)
+    Os = (e @ V) / e.sum(dim=1, keepdim=True)
+    lin = (1.0 - W) * (torch.relu(Q) @ torch.relu(K).T)
+    Ol = (lin @ V) / lin.sum(dim=1, keepdim=True)
+    return alpha[:, None] * Os + (1.0 - alpha[:, None]) * Ol
+
+
+def pin_soft_backward_matches_autograd(orc):
+    """dM and dalpha of the oracle's soft backward equal torch.autograd's gradients of the dense
+    re-statement, for a random upstream gradient."""
+    Q, K, V, M, alpha, blk = _soft_case(306)
+    dO = np.random.default_rng(307).standard_normal(Q.shape)
+    Mt = torch.tensor(M, requires_grad=True)
+    at = torch.tensor(alpha, requires_grad=True)
+    O = _torch_soft_forward(torch.tensor(Q), torch.tensor(K), torch.tensor(V), Mt, at, blk)
+    np.testing.assert_allclose(O.detach().numpy(), orc.forward_soft_head(Q, K, V, M, alpha, blk)[0], rtol=1e-10, atol=1e-12)
+    (O * torch.tensor(dO)).sum().backward()
+    dM, dal = orc.backward_soft_head(Q, K, V, M, alpha, dO, blk)
+    np.testing.assert_allclose(dM, Mt.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dal, at.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+def pin_stage1_finite_differences(orc):
+    """The stage-1 gradients (proj_q, proj_k, alpha: soft router, soft forward, SoftTop-k's
+    implicit gradient, the projection chain) match central differences of the stage-1 loss."""
+    rng = np.random.default_rng(308)
+    B, H, N, d, blk, k, T = 1, 2, 96, 8, 16, 2, 0.3
+    Q, K, V = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    Q[..., 0] = np.abs(Q[..., 0]) + 0.1
+    K[..., 0] = np.abs(K[..., 0]) + 0.1
+    Wq, Wk = (rng.standard_normal((d, d)) / math.sqrt(d) for _ in range(2))
+    alpha = rng.uniform(0.2, 0.8, (B, H, N))
+    Of = orc.full_attention(Q, K, V)
+    g = orc.stage1_grads(Q, K, V, Wq, Wk, alpha, k, T, Of, blk)
+    L = lambda wq, wk, al: orc.stage1_loss(Q, K, V, wq, wk, al, k, T, Of, blk)  # noqa: E731
+    eps = 1e-5
+    for name, X in (("dWq", Wq), ("dWk", Wk), ("dalpha", alpha)):
+        u = rng.standard_normal(X.shape)
+        args_p = [Wq, Wk, alpha]
+        args_m = [Wq, Wk, alpha]
+        pos = {"dWq": 0, "dWk": 1, "dalpha": 2}[name]
+        args_p[pos] = X + eps * u
+        args_m[pos] = X - eps * u
+        num = (L(*args_p) - L(*args_m)) / (2 * eps)
+        ana = (g[name] * u).sum()
+        np.testing.assert_allclose(ana, num, rtol=2e-5, atol=1e-10)
+    assert abs(g["loss"] - L(Wq, Wk, alpha)) < 1e-15
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -91,6 +91,17 @@ MUTATIONS = {
     "int8_p_scale_per_query_block": ("int8.py", "sP = p.max() / INT8_MAX", "sP = max(x.max() for x in P) / INT8_MAX"),
     "int8_dequantised_denominator": ("int8.py", "den = np.sum([p.sum(axis=1) for p in P], axis=0)[:, None]",
                                      "den = np.sum([(int8_encode(p / (p.max() / INT8_MAX)) * (p.max() / INT8_MAX)).sum(axis=1) for p in P], axis=0)[:, None]"),
+    # SoftTop-k training path
+    "soft_tau_direction": ("soft.py", "above = tot > k  # the threshold is too low: raise it", "above = tot < k"),
+    "soft_backward_no_tau_term": ("soft.py", "return (sp / T) * (dM - corr)", "return (sp / T) * dM"),
+    "soft_backward_no_temperature": ("soft.py", "return (sp / T) * (dM - corr)", "return sp * (dM - corr)"),
+    "soft_sparse_weight_dropped": ("soft.py", "e = w[None, :] * np.exp(x - m)", "e = np.exp(x - m)"),
+    "soft_linear_weight_not_complement": ("soft.py", "A = np.tensordot(1.0 - M[i], h, axes=(0, 0))", "A = np.tensordot(M[i], h, axes=(0, 0))"),
+    "soft_linear_dm_sign": ("soft.py", "dM[i] -= np.tensordot(h, dT, axes=([1, 2], [0, 1])) + z @ dzeta",
+                            "dM[i] += np.tensordot(h, dT, axes=([1, 2], [0, 1])) + z @ dzeta"),
+    "soft_dalpha_sign": ("soft.py", "dalpha = (dO * (Os - Ol)).sum(axis=1)", "dalpha = (dO * (Ol - Os)).sum(axis=1)"),
+    "router_backward_dk_untransposed": ("soft.py", "dkt = (np.swapaxes(ds, -1, -2) @ qt) / np.sqrt(d)", "dkt = (ds @ qt) / np.sqrt(d)"),
+    "stage1_dO_halved": ("soft.py", "dO = 2.0 * diff / diff.size", "dO = diff / diff.size"),
 }
 
 
