@@ -17,6 +17,13 @@ PISA exact-or-approximate attention (C ABI in include/sla_pisa.h):
     idx, mask, scores = pisa_route(Q, st, topk, covariance=True)
     O = pisa_forward(Q, K, V, st, idx)
 
+SoftTop-k training path (C ABI in include/sla_soft.h; bf16, d = 128):
+
+    M = soft_route(Q, K, proj_q, proj_k, topk, temperature)    # soft mask [B, H, n_b, n_b]
+    O = soft_forward(Q, K, V, M, alpha)
+    dWq, dWk, dalpha, dM = soft_backward(Q, K, V, proj_q, proj_k, temperature, M, alpha, dO)
+    loss = stage1_step(Q, K, V, O_full, proj_q, proj_k, alpha, topk, temperature, lr, lr_alpha)
+
 SVOO co-clustered blocks (C ABI in include/sla_svoo.h):
 
     perm_q, perm_k, q_assign, k_assign = svoo_cluster(Q, K, iters=3)
@@ -50,6 +57,11 @@ __all__ = [
     "pisa_route",
     "pisa_forward",
     "pisa_workspace_bytes",
+    "soft_workspace_bytes",
+    "soft_route",
+    "soft_forward",
+    "soft_backward",
+    "stage1_step",
     "BLOCK",
 ]
 
@@ -149,6 +161,17 @@ def lib() -> ctypes.CDLL:
         for name in ("sla_svoo_gather", "sla_svoo_scatter"):
             getattr(L, name).argtypes = [P, vp, i32, vp, vp, vp]
             getattr(L, name).restype = i32
+        f32 = ctypes.c_float
+        L.sla_soft_workspace_bytes.argtypes = [P]
+        L.sla_soft_workspace_bytes.restype = sz
+        L.sla_soft_route.argtypes = [P, vp, vp, vp, vp, f32, vp, vp, sz, vp]
+        L.sla_soft_route.restype = i32
+        L.sla_soft_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sla_soft_forward.restype = i32
+        L.sla_soft_backward.argtypes = [P, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sla_soft_backward.restype = i32
+        L.sla_stage1_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, sz, vp]
+        L.sla_stage1_step.restype = i32
         L.sla_status_string.argtypes = [i32]
         L.sla_status_string.restype = ctypes.c_char_p
         L.sla_last_hip_error.argtypes = []
@@ -307,6 +330,100 @@ def backward(Q, K, V, idx, alpha, dO, workspace=None, want_O=False, out=None):
     if st != SLA_OK:
         raise SLAError(st, "sla_backward")
     return (dQ, dK, dV, da, O) if want_O else (dQ, dK, dV, da)
+
+
+def soft_workspace_bytes(Q, topk: int) -> int:
+    return lib().sla_soft_workspace_bytes(ctypes.byref(_problem(Q, topk)))
+
+
+def _soft_ws(p, dev, workspace):
+    need = lib().sla_soft_workspace_bytes(ctypes.byref(p))
+    if need == 0:
+        raise SLAError(SLA_ERR_UNSUPPORTED, "sla_soft_workspace_bytes")
+    return workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+
+
+def soft_route(Q, K, proj_q, proj_k, topk: int, temperature: float, workspace=None, out=None):
+    """SoftTop-k router (training): the soft mask M [B, H, n_b, n_b] fp32 with row sums topk."""
+    _check_qkv(Q, K)
+    Q, K = Q.contiguous(), K.contiguous()
+    proj_q = proj_q.contiguous().to(torch.float32)
+    proj_k = proj_k.contiguous().to(torch.float32)
+    B, H, N, d = Q.shape
+    nb = -(-N // BLOCK)
+    p = _problem(Q, topk)
+    ws = _soft_ws(p, Q.device, workspace)
+    M = out if out is not None else torch.empty((B, H, nb, nb), dtype=torch.float32, device=Q.device)
+    st = lib().sla_soft_route(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(proj_q), _ptr(proj_k), float(temperature),
+                              _ptr(M), _ptr(ws), ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_soft_route")
+    return M
+
+
+def soft_forward(Q, K, V, M, alpha, workspace=None, out=None):
+    """Soft-mask forward: O = alpha O_s + (1 - alpha) O_l, key block j of query block i weighted
+    by M[i][j] in the sparse branch and 1 - M[i][j] in the linear one."""
+    _check_qkv(Q, K, V)
+    Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
+    M = M.contiguous().to(torch.float32)
+    alpha = alpha.contiguous().to(torch.float32)
+    B, H, N, d = Q.shape
+    p = _problem(Q, 0)
+    ws = _soft_ws(p, Q.device, workspace)
+    O = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device)
+    st = lib().sla_soft_forward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(M), _ptr(alpha), _ptr(O),
+                                _ptr(ws), ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_soft_forward")
+    return O
+
+
+def soft_backward(Q, K, V, proj_q, proj_k, temperature: float, M, alpha, dO, topk: int,
+                  want_dM: bool = True, workspace=None):
+    """Gradients of <dO, O> for the soft forward with M = soft_route(..., topk, temperature):
+    returns (dproj_q, dproj_k, dalpha, dM or None)."""
+    _check_qkv(Q, K, V, dO)
+    Q, K, V, dO = Q.contiguous(), K.contiguous(), V.contiguous(), dO.contiguous()
+    proj_q = proj_q.contiguous().to(torch.float32)
+    proj_k = proj_k.contiguous().to(torch.float32)
+    M = M.contiguous().to(torch.float32)
+    alpha = alpha.contiguous().to(torch.float32)
+    B, H, N, d = Q.shape
+    nb = -(-N // BLOCK)
+    p = _problem(Q, topk)
+    ws = _soft_ws(p, Q.device, workspace)
+    dev = Q.device
+    dWq = torch.empty((d, d), dtype=torch.float32, device=dev)
+    dWk = torch.empty((d, d), dtype=torch.float32, device=dev)
+    da = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dM = torch.empty((B, H, nb, nb), dtype=torch.float32, device=dev) if want_dM else None
+    st = lib().sla_soft_backward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(proj_q), _ptr(proj_k),
+                                 float(temperature), _ptr(M), _ptr(alpha), _ptr(dO), _ptr(dWq), _ptr(dWk),
+                                 _ptr(da), _ptr(dM), None, _ptr(ws), ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_soft_backward")
+    return dWq, dWk, da, dM
+
+
+def stage1_step(Q, K, V, O_full, proj_q, proj_k, alpha, topk: int, temperature: float,
+                lr_proj: float, lr_alpha: float, workspace=None, loss=None):
+    """One stage-1 step in place on proj_q, proj_k, alpha (fp32 contiguous GPU tensors); returns
+    the step's loss (before the update) as a one-element GPU tensor."""
+    _check_qkv(Q, K, V)
+    for t in (proj_q, proj_k, alpha, O_full):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != Q.device:
+            raise ValueError("proj_q, proj_k, alpha, O_full must be contiguous fp32 tensors on the inputs' device")
+    Q, K, V = Q.contiguous(), K.contiguous(), V.contiguous()
+    p = _problem(Q, topk)
+    ws = _soft_ws(p, Q.device, workspace)
+    loss = loss if loss is not None else torch.empty(1, dtype=torch.float32, device=Q.device)
+    st = lib().sla_stage1_step(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(O_full), _ptr(proj_q),
+                               _ptr(proj_k), _ptr(alpha), float(temperature), float(lr_proj), float(lr_alpha),
+                               _ptr(loss), _ptr(ws), ws.numel(), _stream())
+    if st != SLA_OK:
+        raise SLAError(st, "sla_stage1_step")
+    return loss
 
 
 def quantize_int8(X):

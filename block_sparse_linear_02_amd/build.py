@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["router.hip", "linear_state.hip", "linear_gemm.hip", "sparse.hip", "sparse_pair.hip",
            "linear_apply.hip", "fp8.hip", "pisa_stats.hip", "pisa.hip", "branch_drop.hip",
-           "bwd.hip", "svoo.hip", "api.cpp"]
+           "bwd.hip", "svoo.hip", "soft.hip", "api.cpp"]
 
 FLAGS = [
     "-O3",

@@ -3,6 +3,7 @@
 #include "sla.h"
 #include "sla_pisa.h"
 #include "sla_svoo.h"
+#include "sla_soft.h"
 
 #include <atomic>
 #include <climits>
@@ -339,6 +340,98 @@ int permute_impl(const sla_problem* p, const void* X, int32_t row_bytes, const i
   return SLA_OK;
 }
 
+// SoftTop-k training path workspace
+struct SoftWs {
+  float *qbar, *kbar, *qt, *kt, *dqt, *dkt;
+  __bf16* wt;
+  float *zb, *z_part, *Z;
+  __bf16 *hj_bf, *t_bf, *dA_bf;
+  float *O, *Os, *Ol, *lse2, *rden;
+  __bf16 *dOs, *G, *dO;
+  float *Dr, *e, *dzeta, *zb2, *z_part2;
+  float *dmsp, *dmlin, *ds, *Mw, *dWq, *dWk, *dalpha, *parts;
+};
+size_t carve_soft(const sla::Dims& d, void* ws, SoftWs* out) {
+  Carve c(ws);
+  const size_t BH = (size_t)d.B * d.H;
+  const size_t dd = (size_t)d.d * d.d;
+  const size_t rows = BH * d.N, elems = rows * d.d, blocks = BH * d.nb, pairs = blocks * d.nb;
+  const int cb = sla::state_chunk_blocks(d, false);
+  const size_t nchunk = (d.nb + cb - 1) / cb;
+  SoftWs w = {};
+  w.qbar = c.take<float>(blocks * d.d);
+  w.kbar = c.take<float>(blocks * d.d);
+  w.qt = c.take<float>(blocks * d.d);
+  w.kt = c.take<float>(blocks * d.d);
+  w.dqt = c.take<float>(blocks * d.d);
+  w.dkt = c.take<float>(blocks * d.d);
+  w.wt = c.take<__bf16>(blocks * sla::tsel_weight_pitch(d.nb));
+  w.zb = c.take<float>(blocks * d.d);
+  w.z_part = c.take<float>(BH * nchunk * d.d);
+  w.Z = c.take<float>(BH * d.d);
+  w.hj_bf = c.take<__bf16>(blocks * dd);
+  w.t_bf = c.take<__bf16>(blocks * dd);
+  w.dA_bf = c.take<__bf16>(blocks * dd);
+  w.O = c.take<float>(elems);
+  w.Os = c.take<float>(elems);
+  w.Ol = c.take<float>(elems);
+  w.lse2 = c.take<float>(rows);
+  w.rden = c.take<float>(rows);
+  w.dOs = c.take<__bf16>(elems);
+  w.G = c.take<__bf16>(elems);
+  w.dO = c.take<__bf16>(elems);
+  w.Dr = c.take<float>(rows);
+  w.e = c.take<float>(rows);
+  w.dzeta = c.take<float>(blocks * d.d);
+  w.zb2 = c.take<float>(blocks * d.d);
+  w.z_part2 = c.take<float>(BH * nchunk * d.d);
+  w.dmsp = c.take<float>(pairs * 4);
+  w.dmlin = c.take<float>(pairs);
+  w.ds = c.take<float>(pairs);
+  w.Mw = c.take<float>(pairs);
+  w.dWq = c.take<float>(dd);
+  w.dWk = c.take<float>(dd);
+  w.dalpha = c.take<float>(rows);
+  w.parts = c.take<float>(sla::soft_loss_parts(d));
+  if (out) *out = w;
+  return c.off;
+}
+int check_soft(const sla_problem* p, sla::Dims* d) {
+  const int st = check_problem(p, d);
+  if (st != SLA_OK) return st;
+  if (d->dtype != sla::kBF16 || d->d != 128) return SLA_ERR_UNSUPPORTED;
+  return SLA_OK;
+}
+// the soft forward: states, the weighted mask GEMM, the weighted sparse branch (+ its rows)
+hipError_t soft_forward_impl(const sla::Dims& d, const void* Q, const void* K, const void* V,
+                             const float* M, const float* alpha, float* O, const SoftWs& w,
+                             hipStream_t stream) {
+  hipError_t e = sla::launch_states(d, K, V, w.zb, nullptr, w.z_part, nullptr, w.hj_bf, stream);
+  if (e == hipSuccess)
+    e = sla::launch_state_reduce(d, nullptr, w.z_part, nullptr, nullptr, w.Z, nullptr, stream);
+  if (e == hipSuccess) e = sla::launch_soft_weights(d, M, w.wt, stream);
+  if (e == hipSuccess) e = sla::launch_tsel_weighted(d, w.hj_bf, w.wt, w.t_bf, stream);
+  const sla::TrainRows tr = {w.Os, w.Ol, w.lse2, w.rden};
+  if (e == hipSuccess) e = sla::launch_sparse_soft(d, Q, K, V, M, alpha, w.t_bf, w.Z, w.zb, O, stream, &tr);
+  return e;
+}
+// the soft backward after soft_forward_impl: dalpha, dM (parts), ds, the router gradients
+hipError_t soft_backward_impl(const sla::Dims& d, const void* Q, const void* K, const void* V,
+                              const float* Wq, const float* Wk, float temp, const float* M,
+                              const float* alpha, const void* dO, float* dWq, float* dWk,
+                              float* dalpha, float* dM, const SoftWs& w, hipStream_t stream) {
+  const sla::TrainRows tr = {w.Os, w.Ol, w.lse2, w.rden};
+  hipError_t e = sla::launch_bwd_prep(d, Q, dO, alpha, tr, dalpha, w.dOs, w.Dr, w.G, w.e, w.dzeta, stream);
+  if (e == hipSuccess) e = sla::launch_states(d, Q, w.G, w.zb2, nullptr, w.z_part2, nullptr, w.dA_bf, stream);
+  if (e == hipSuccess) e = sla::launch_soft_dm_sparse(d, Q, K, V, w.dOs, w.lse2, w.Dr, w.dmsp, stream);
+  if (e == hipSuccess) e = sla::launch_soft_dm_linear(d, w.dA_bf, w.hj_bf, w.dzeta, w.zb, w.dmlin, stream);
+  if (e == hipSuccess) e = sla::launch_soft_topk_bwd(d, M, w.dmsp, w.dmlin, temp, w.ds, dM, stream);
+  if (e == hipSuccess) e = sla::launch_soft_pool(d, Q, K, Wq, Wk, w.qbar, w.kbar, w.qt, w.kt, stream);
+  if (e == hipSuccess)
+    e = sla::launch_router_bwd(d, w.ds, w.qbar, w.kbar, w.qt, w.kt, w.dqt, w.dkt, dWq, dWk, stream);
+  return e;
+}
+
 // Static workspace of sla_route_noalloc: one copy per GPU, alive until the process ends.  In
 // host code `scratch` names a host-side stand-in, not device memory: only the address that
 // hipGetSymbolAddress returns (kept per device below) is handed to kernels.
@@ -397,6 +490,91 @@ int sla_route(const sla_problem* p, const void* Q, const void* K, const float* p
   carve_route(d, ws, &w);
   hipError_t e = sla::launch_route(d, Q, K, proj_q, proj_k, w.q_hi, w.q_lo, w.k_hi, w.k_lo, idx,
                                    mask, scores, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+size_t sla_soft_workspace_bytes(const sla_problem* p) {
+  sla::Dims d;
+  if (check_soft(p, &d) != SLA_OK) return 0;
+  return carve_soft(d, nullptr, nullptr);
+}
+
+int sla_soft_route(const sla_problem* p, const void* Q, const void* K, const float* proj_q,
+                   const float* proj_k, float temperature, float* M, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  sla::Dims d;
+  int st = check_soft(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !K || !proj_q || !proj_k || !M || !ws) return SLA_ERR_INVALID;
+  if (!(temperature > 0.f) || !(temperature < 1e30f)) return SLA_ERR_INVALID;
+  if (ws_bytes < carve_soft(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  SoftWs w;
+  carve_soft(d, ws, &w);
+  hipError_t e = sla::launch_soft_pool(d, Q, K, proj_q, proj_k, w.qbar, w.kbar, w.qt, w.kt, stream);
+  if (e == hipSuccess) e = sla::launch_soft_topk(d, w.qt, w.kt, temperature, M, w.wt, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+int sla_soft_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                     const float* M, const float* alpha, float* O, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  sla::Dims d;
+  int st = check_soft(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !K || !V || !M || !alpha || !O || !ws) return SLA_ERR_INVALID;
+  if (ws_bytes < carve_soft(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  SoftWs w;
+  carve_soft(d, ws, &w);
+  const hipError_t e = soft_forward_impl(d, Q, K, V, M, alpha, O, w, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+int sla_soft_backward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                      const float* proj_q, const float* proj_k, float temperature, const float* M,
+                      const float* alpha, const void* dO, float* dproj_q, float* dproj_k,
+                      float* dalpha, float* dM, float* O, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  sla::Dims d;
+  int st = check_soft(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !K || !V || !proj_q || !proj_k || !M || !alpha || !dO || !dproj_q || !dproj_k || !dalpha || !ws)
+    return SLA_ERR_INVALID;
+  if (!(temperature > 0.f) || !(temperature < 1e30f)) return SLA_ERR_INVALID;
+  if (ws_bytes < carve_soft(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  SoftWs w;
+  carve_soft(d, ws, &w);
+  hipError_t e = soft_forward_impl(d, Q, K, V, M, alpha, O ? O : w.O, w, stream);
+  if (e == hipSuccess)
+    e = soft_backward_impl(d, Q, K, V, proj_q, proj_k, temperature, M, alpha, dO, dproj_q, dproj_k,
+                           dalpha, dM, w, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return SLA_OK;
+}
+
+int sla_stage1_step(const sla_problem* p, const void* Q, const void* K, const void* V,
+                    const float* O_full, float* proj_q, float* proj_k, float* alpha,
+                    float temperature, float lr_proj, float lr_alpha, float* loss, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  sla::Dims d;
+  int st = check_soft(p, &d);
+  if (st != SLA_OK) return st;
+  if (!Q || !K || !V || !O_full || !proj_q || !proj_k || !alpha || !loss || !ws) return SLA_ERR_INVALID;
+  if (!(temperature > 0.f) || !(temperature < 1e30f)) return SLA_ERR_INVALID;
+  if (ws_bytes < carve_soft(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  SoftWs w;
+  carve_soft(d, ws, &w);
+  hipError_t e = sla::launch_soft_pool(d, Q, K, proj_q, proj_k, w.qbar, w.kbar, w.qt, w.kt, stream);
+  if (e == hipSuccess) e = sla::launch_soft_topk(d, w.qt, w.kt, temperature, w.Mw, w.wt, stream);
+  if (e == hipSuccess) e = soft_forward_impl(d, Q, K, V, w.Mw, alpha, w.O, w, stream);
+  if (e == hipSuccess) e = sla::launch_soft_loss(d, w.O, O_full, w.dO, w.parts, loss, stream);
+  if (e == hipSuccess)
+    e = soft_backward_impl(d, Q, K, V, proj_q, proj_k, temperature, w.Mw, alpha, w.dO, w.dWq, w.dWk,
+                           w.dalpha, nullptr, w, stream);
+  if (e == hipSuccess)
+    e = sla::launch_soft_update(d, proj_q, proj_k, alpha, w.dWq, w.dWk, w.dalpha, lr_proj, lr_alpha, stream);
   if (e != hipSuccess) return hip_fail(e);
   return SLA_OK;
 }

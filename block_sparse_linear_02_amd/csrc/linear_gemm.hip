@@ -78,10 +78,14 @@ __device__ __forceinline__ int hs_off(int j, int c) {
   return j * (2 * kGemmN) + (((c >> 3) ^ (4 * (j & 3))) << 4) + (c & 7) * 2;
 }
 
-template <int D>
+// WT (the SoftTop-k training path): the B operand comes from a bf16 weight matrix wt
+// [BH][nb][wpitch] (row i: the weights of the key blocks j for query block i, zero past n_b)
+// instead of the complement bits: T_i = sum_j wt[i][j] h_j.
+template <int D, bool WT = false>
 __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
     const __bf16* __restrict__ hj, const uint32_t* __restrict__ bits, int nb, int nw,
-    int tiles_m, int tiles_n, __bf16* __restrict__ t_out, const uint32_t* __restrict__ flags) {
+    int tiles_m, int tiles_n, __bf16* __restrict__ t_out, const uint32_t* __restrict__ flags,
+    const __bf16* __restrict__ wt = nullptr, int wpitch = 0) {
   constexpr int DD = D * D;
   constexpr int STAGE = kGemmK * kGemmN;  // bf16 elements of one h stage
   __shared__ __attribute__((aligned(16))) __bf16 sb0[STAGE];
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
   };
 
   stage(0, B0{});
-  mask_words(0);
+  if constexpr (!WT) mask_words(0);
   wait_vmem();
   __syncthreads();
   auto step = [&](int s, auto BUFC) {
@@ -183,22 +187,28 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
 #pragma unroll
     for (int ct = 0; ct < kGemmCT; ++ct)
 #pragma unroll
-      for (int h = 0; h < kGemmKW; ++h) cur[ct][h] = kGemmKW * s + h < nw ? mw[ct][h] : 0u;
+      for (int h = 0; h < kGemmKW; ++h) cur[ct][h] = (!WT && kGemmKW * s + h < nw) ? mw[ct][h] : 0u;
     if (s + 1 < nstage) {
       stage(s + 1, std::integral_constant<int, 1 - BUF>{});
-      mask_words(s + 1);
+      if constexpr (!WT) mask_words(s + 1);
     }
     const __bf16* tile = buf(BUFC);
 #pragma unroll
     for (int ks = 0; ks < kGemmK / 16; ++ks) {
-      // mask operand: bits 16 ks + 8 g .. + 7 of the stage, i.e. of word ks / 2
+      // mask operand: bits 16 ks + 8 g .. + 7 of the stage, i.e. of word ks / 2 (or, WT, the
+      // weights of key blocks kGemmK s + 16 ks + 8 g .. + 7)
       bf16x8 bm[kGemmCT];
 #pragma unroll
       for (int ct = 0; ct < kGemmCT; ++ct)
       {
-        const u32 byte = (cur[ct][ks / 2] >> (16 * (ks % 2) + 8 * g)) & 0xffu;
-        const bf16x4 lo = nib[byte & 15u], hi = nib[byte >> 4];
-        bm[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (WT) {
+          const int i = min(i0 + 32 * ct + lane % 32, nb - 1);
+          bm[ct] = *reinterpret_cast<const bf16x8*>(wt + ((size_t)bh * nb + i) * wpitch + kGemmK * s + 16 * ks + 8 * g);
+        } else {
+          const u32 byte = (cur[ct][ks / 2] >> (16 * (ks % 2) + 8 * g)) & 0xffu;
+          const bf16x4 lo = nib[byte & 15u], hi = nib[byte >> 4];
+          bm[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
       }
       bf16x8 ah[kGemmRT];
 #pragma unroll
@@ -253,6 +263,23 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
 }  // namespace
 
 int mask_words(int nb) { return (nb + 31) / 32; }
+
+int tsel_weight_pitch(int nb) { return (nb + kGemmK - 1) / kGemmK * kGemmK; }
+
+hipError_t launch_tsel_weighted(const Dims& p, const __bf16* hj_bf, const __bf16* wt, __bf16* t_bf,
+                                hipStream_t stream) {
+  const int tiles_m = (p.nb + kGemmM - 1) / kGemmM;
+  const int tiles_n = p.d * p.d / kGemmN;
+  const int total = xcd_chunk_grid(p.B * p.H, tiles_m * tiles_n);
+  const int wpitch = tsel_weight_pitch(p.nb);
+  if (p.d == 128)
+    tsel_kernel<128, true><<<total, kGemmThreads, 0, stream>>>(hj_bf, nullptr, p.nb, 0, tiles_m, tiles_n,
+                                                               t_bf, nullptr, wt, wpitch);
+  else
+    tsel_kernel<64, true><<<total, kGemmThreads, 0, stream>>>(hj_bf, nullptr, p.nb, 0, tiles_m, tiles_n,
+                                                              t_bf, nullptr, wt, wpitch);
+  return hipGetLastError();
+}
 
 hipError_t launch_mask_bits(const Dims& p, const int32_t* idx, uint32_t* bits,
                             hipStream_t stream) {

@@ -64,6 +64,54 @@ hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const
                               const float* Z, const float* zb, float* O, hipStream_t stream,
                               const uint32_t* flags = nullptr, const TrainRows* tr = nullptr,
                               const int32_t* out_rows = nullptr);
+// SoftTop-k training path (soft.hip, and the SOFT forms of the mask GEMM and the pair kernel;
+// bf16, d = 128).  Weighted mask GEMM: T_i = sum_j wt[i][j] h_j with wt [BH][nb][pitch] bf16
+// (pitch = tsel_weight_pitch(nb), zero past n_b).  Soft sparse branch: every key block j of
+// query block i weighted by msoft [BH][nb][nb] (fp32), zeta_i = Z - sum_j M_ij z_j.
+int tsel_weight_pitch(int nb);
+hipError_t launch_tsel_weighted(const Dims& p, const __bf16* hj_bf, const __bf16* wt, __bf16* t_bf,
+                                hipStream_t stream);
+hipError_t launch_sparse_soft(const Dims& p, const void* Q, const void* K, const void* V,
+                              const float* msoft, const float* alpha, const __bf16* t_bf,
+                              const float* Z, const float* zb, float* O, hipStream_t stream,
+                              const TrainRows* tr);
+// Pooled means (fp32 [BH][nb][d]) and their projections by Wq, Wk (fp32 [BH][nb][d]).
+hipError_t launch_soft_pool(const Dims& p, const void* Q, const void* K, const float* Wq,
+                            const float* Wk, float* qbar, float* kbar, float* qt, float* kt,
+                            hipStream_t stream);
+// SoftTop-k per row: scores s = qt kt^T / sqrt(d), M = sigmoid((s - tau) / T) with sum_j M = topk
+// (fp32 [BH][nb][nb]) and wt = bf16(1 - M) [BH][nb][tsel_weight_pitch(nb)].
+hipError_t launch_soft_topk(const Dims& p, const float* qt, const float* kt, float temp, float* M,
+                            __bf16* wt, hipStream_t stream);
+// wt = bf16(1 - M), zero-padded to tsel_weight_pitch(nb).
+hipError_t launch_soft_weights(const Dims& p, const float* M, __bf16* wt, hipStream_t stream);
+// dM of the sparse branch, per (query block, key block) tile in four parts (32 rows x 32 keys
+// each): dmsp [BH][nb][nb][4], the sum over each part of 2^(S c - lse2) (dO_s . v - D).
+hipError_t launch_soft_dm_sparse(const Dims& p, const void* Q, const void* K, const void* V,
+                                 const __bf16* dOs, const float* lse2, const float* Dr, float* dmsp,
+                                 hipStream_t stream);
+// dM of the linear branch: dmlin [BH][nb][nb] = -(<dA_i, h_j> + dzeta_i . z_j) from the sliced
+// bf16 dA_i^T and h_j^T and the fp32 dzeta [BH][nb][d], z [BH][nb][d].
+hipError_t launch_soft_dm_linear(const Dims& p, const __bf16* dA_bf, const __bf16* hj_bf,
+                                 const float* dzeta, const float* zb, float* dmlin,
+                                 hipStream_t stream);
+// ds = SoftTop-k backward of dM = dmsp[..][0] + dmsp[..][1] + dmlin ([BH][nb][nb]; zero for
+// topk 0 or n_b), optionally writing dM itself.
+hipError_t launch_soft_topk_bwd(const Dims& p, const float* M, const float* dmsp, const float* dmlin,
+                                float temp, float* ds, float* dM_out, hipStream_t stream);
+// Router backward: dqt = ds kt / sqrt(d), dkt = ds^T qt / sqrt(d) per head, then
+// dWq = sum qbar^T dqt, dWk = sum kbar^T dkt over every (b, h) and block (fp32 [d][d]).
+hipError_t launch_router_bwd(const Dims& p, const float* ds, const float* qbar, const float* kbar,
+                             const float* qt, const float* kt, float* dqt, float* dkt, float* dWq,
+                             float* dWk, hipStream_t stream);
+// Stage 1: dO = bf16(2 (O - O_full) / count) and the loss partials (one per workgroup of
+// kLossThreads rows x channels), then the loss (fixed-order sum); the parameter update.
+int soft_loss_parts(const Dims& p);
+hipError_t launch_soft_loss(const Dims& p, const float* O, const float* O_full, __bf16* dO,
+                            float* parts, float* loss, hipStream_t stream);
+hipError_t launch_soft_update(const Dims& p, float* Wq, float* Wk, float* alpha, const float* dWq,
+                              const float* dWk, const float* dalpha, float lr_w, float lr_a,
+                              hipStream_t stream);
 // Reduce the chunk partials (fixed order): H^T as bf16 hi/lo [d][d], Z [d]; optionally H [d][d]
 // in fp32 (K-channel major, literal mode); Z alone when h_part is null (mask-product mode).
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,

@@ -84,13 +84,17 @@ constexpr float kPairRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before 
 // TRAIN: also write what the backward needs per query row (TrainRows, sla_launch.hpp): the
 // normalised branches O_s and O_l, the sparse branch's log2-sum-exp2 and 1 / den (0 where the
 // linear branch is defined as 0)
-template <class T, int D, bool TRAIN>
+// SOFT (the SoftTop-k training path): every key block is walked, the tile of key block j
+// weighted by msoft[query block][j] in the sparse branch (P = M_ij 2^(S c - m)), and the
+// linear branch's zeta_i = Z - sum_j M_ij z_j (T_i from the weighted mask GEMM); idx is unused.
+template <class T, int D, bool TRAIN, bool SOFT = false>
 __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
     float* __restrict__ O, int N, int nb, int topk, float c_log2,
-    const uint32_t* __restrict__ flags, TrainRows tr, const int32_t* __restrict__ out_rows) {
+    const uint32_t* __restrict__ flags, TrainRows tr, const int32_t* __restrict__ out_rows,
+    const float* __restrict__ msoft = nullptr) {
   constexpr int NS = D / 16;  // MFMA k-steps over the head dim
   constexpr int NC = D / 32;  // 32-channel output tiles
   constexpr int TILE = TileLayout<D>::ELEMS;
@@ -122,9 +126,13 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   const int nw = (nb + 31) / 32;
 
   // ---- the union of the two ascending index lists, with the kept-by bits ----
+  if constexpr (SOFT) {  // every key block, weighted for both query blocks
+    for (int t = tid; t < nb; t += kPairThreads) ul[t] = (t << 2) | 3;
+    if (tid == 0) ucount = nb;
+  }
   if (tid < 2 * kPairMaxWords) bm[tid / kPairMaxWords][tid % kPairMaxWords] = 0u;
   __syncthreads();
-  for (int t = tid; t < 2 * topk; t += kPairThreads) {
+  for (int t = tid; !SOFT && t < 2 * topk; t += kPairThreads) {
     const int b = t / topk;
     if (b == 0 || has1) {
       const int j = idx[((size_t)bh * nb + qb0 + b) * topk + t % topk];
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     }
   }
   __syncthreads();
-  if (wave == 0) {
+  if (!SOFT && wave == 0) {
     const uint32_t w0 = lane < nw ? bm[0][lane] : 0u, w1 = lane < nw ? bm[1][lane] : 0u;
     const uint32_t u = w0 | w1;
     const int cnt = __popc(u);
@@ -181,6 +189,9 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const T* ksrc = K + hoff + (size_t)j * kBlock * D;
     const T* vsrc = V + hoff + (size_t)j * kBlock * D;
     if (z_lane) z_in = zb[((size_t)bh * nb + j) * D + tid % D];
+    if constexpr (SOFT) {
+      if (z_lane) z_in *= msoft[((size_t)bh * nb + min(qb0 + zb_blk, nb - 1)) * nb + j];
+    }
     f_next = e & 3;
     nv_next = nv;
     if constexpr (DIRECT) {
@@ -289,6 +300,8 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     launder();
     if (t + 1 < nu) stage(t + 1, std::integral_constant<int, 1 - BUF>{});
     if ((f_cur >> blk) & 1) {  // this wavefront's block kept the tile (wavefront-uniform)
+      // SOFT: this wavefront's block's weight of key block t (the union is every block in order)
+      const float wgt = SOFT ? msoft[((size_t)bh * nb + min(qb0 + blk, nb - 1)) * nb + t] : 1.f;
       const __bf16* Ks = buf(BUFC);
       const __bf16* Vs = Ks + TILE;
       // K operands of both 32-key halves, issued together ahead of their MFMAs
@@ -347,7 +360,10 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pb[u][jj] = f2bf(fast_exp2(fmaf(s[u / 2][8 * (u % 2) + jj], c_log2, -mrun)));
+        for (int jj = 0; jj < 8; ++jj) {
+          const float pe = fast_exp2(fmaf(s[u / 2][8 * (u % 2) + jj], c_log2, -mrun));
+          pb[u][jj] = f2bf(SOFT ? wgt * pe : pe);
+        }
         lsum = pair_sum8(pb[u], lsum);
       }
       if constexpr (MASK) read_v();
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     }
     den = xor32_sum(den);
   }
-  const float inv_den = (lin && topk < nb && den != 0.f) ? 1.f / den : 0.f;
+  const float inv_den = (lin && (SOFT || topk < nb) && den != 0.f) ? 1.f / den : 0.f;
   if (!row_ok) return;
   const float a = alpha[(size_t)bh * N + row];
   const float ws = a * inv_l, wl = (1.f - a) * inv_den;
@@ -493,6 +509,24 @@ hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void
 }
 
 }  // namespace
+
+hipError_t launch_sparse_soft(const Dims& p, const void* Q, const void* K, const void* V,
+                              const float* msoft, const float* alpha, const __bf16* t_bf,
+                              const float* Z, const float* zb, float* O, hipStream_t stream,
+                              const TrainRows* tr) {
+  if (p.nb > kPairMaxWords * 32 || p.dtype != kBF16 || p.d != 128 || !msoft) return hipErrorInvalidValue;
+  const int total = xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2);
+  const float c_log2 = 1.4426950408889634f / sqrtf(128.f);
+  if (tr)
+    pair_kernel<__bf16, 128, true, true><<<total, kPairThreads, 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, nullptr, alpha, t_bf, Z, zb, O, p.N, p.nb,
+        p.nb, c_log2, nullptr, *tr, nullptr, msoft);
+  else
+    pair_kernel<__bf16, 128, false, true><<<total, kPairThreads, 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, nullptr, alpha, t_bf, Z, zb, O, p.N, p.nb,
+        p.nb, c_log2, nullptr, TrainRows{}, nullptr, msoft);
+  return hipGetLastError();
+}
 
 hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,

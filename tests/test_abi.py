@@ -182,6 +182,63 @@ def test_backward_checks(L):
     assert f(ctypes.byref(p), *short) == sla.SLA_ERR_WORKSPACE
 
 
+def test_soft_checks(L):
+    """SoftTop-k entry points: bf16 with d = 128 only, null pointers and a temperature that is not
+    a positive finite number rejected, a short workspace rejected, all before anything is
+    enqueued."""
+    p = P()
+    ws = L.sla_soft_workspace_bytes(ctypes.byref(p))
+    assert ws > 0 and L.sla_soft_workspace_bytes(ctypes.byref(P(H=4))) > ws
+    assert L.sla_soft_workspace_bytes(ctypes.byref(P(d=64))) == 0
+    assert L.sla_soft_workspace_bytes(ctypes.byref(P(dtype=sla.SLA_F32))) == 0
+    route = L.sla_soft_route
+    r_args = [FAKE, FAKE, FAKE, FAKE, 0.5, FAKE, FAKE, ws, None]  # Q K Wq Wk T M ws bytes stream
+    assert route(ctypes.byref(P(d=64)), *r_args) == sla.SLA_ERR_UNSUPPORTED
+    for i in (0, 1, 2, 3, 5, 6):
+        bad = list(r_args)
+        bad[i] = None
+        assert route(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID, i
+    for t in (0.0, -1.0, float("inf"), float("nan")):
+        bad = list(r_args)
+        bad[4] = t
+        assert route(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID, t
+    short = list(r_args)
+    short[7] = ws - 1
+    assert route(ctypes.byref(p), *short) == sla.SLA_ERR_WORKSPACE
+    fwd = L.sla_soft_forward
+    f_args = [FAKE] * 7 + [ws, None]  # Q K V M alpha O ws bytes stream
+    for i in range(7):
+        bad = list(f_args)
+        bad[i] = None
+        assert fwd(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID, i
+    short = list(f_args)
+    short[7] = ws - 1
+    assert fwd(ctypes.byref(p), *short) == sla.SLA_ERR_WORKSPACE
+    bwd = L.sla_soft_backward
+    # Q K V Wq Wk T M alpha dO dWq dWk dalpha dM O ws bytes stream
+    b_args = [FAKE] * 5 + [0.5] + [FAKE] * 6 + [None, None, FAKE, ws, None]
+    for i in (0, 1, 2, 3, 4, 6, 7, 8, 9, 10, 11, 14):
+        bad = list(b_args)
+        bad[i] = None
+        assert bwd(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID, i
+    bad = list(b_args)
+    bad[5] = 0.0
+    assert bwd(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID
+    short = list(b_args)
+    short[15] = ws - 1
+    assert bwd(ctypes.byref(p), *short) == sla.SLA_ERR_WORKSPACE
+    step = L.sla_stage1_step
+    # Q K V O_full Wq Wk alpha T lr lra loss ws bytes stream
+    s_args = [FAKE] * 7 + [0.5, 1.0, 1.0, FAKE, FAKE, ws, None]
+    for i in (0, 1, 2, 3, 4, 5, 6, 10, 11):
+        bad = list(s_args)
+        bad[i] = None
+        assert step(ctypes.byref(p), *bad) == sla.SLA_ERR_INVALID, i
+    short = list(s_args)
+    short[12] = ws - 1
+    assert step(ctypes.byref(p), *short) == sla.SLA_ERR_WORKSPACE
+
+
 def test_status_strings(L):
     for st in (0, -1, -2, -3, -4):
         assert L.sla_status_string(st).decode()
