@@ -550,10 +550,12 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
 //   z_j of the kept blocks summed on the way.
 //   Pass 2: the workgroup walks the ascending union of the two lists and stages each K8 and V8^T
 //   tile into LDS once for both blocks (K one step ahead of V); per tile t a wavefront whose
-//   block kept it forms P = exp(S - max) and its part of the 64 x 64 tile maximum, which meets
-//   the partner wavefront's in LDS at the step's barrier, so tile t's P is quantised (scale
-//   max / 448) and (P8 V8) sP sV accumulated by fp8 MFMA in step t + 1: one barrier per tile.
-//   The denominator sums the unquantised P.
+//   block kept it forms S and, per row, log2 of its largest P^ = 2^(S sc - m) in the tile (no
+//   exponential: max(S) sc - m), whose max over its 32 rows meets the partner wavefront's in LDS
+//   at the step's barrier.  In step t + 1, with e = log2 max(tile), each P code comes from one
+//   exponential, code(2^(S sc - m + log2 448 - e)) = code(P^ 448 / max), and (P8 V8) sP sV is
+//   accumulated by fp8 MFMA with sP = 2^e / 448: one barrier per tile.  The denominator sums the
+//   unquantised P^ = y sP.
 template <int D, int FMT>
 __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     const __bf16* __restrict__ Q, const uint8_t* __restrict__ q8,
@@ -762,14 +764,23 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
 #pragma unroll
   for (int c = 0; c < NC; ++c) os[c] = f32x16{};
   float lsum = 0.f;
-  float pp[2][16];        // P of the previous tile (quantised once its tile maximum is known)
+  // S of the previous tile (keys past a short block and absent rows at -inf) and its score scale:
+  // P is formed one step late, once the 64 x 64 tile's largest P^ is known
+  f32x16 ss[2];
+  float sc_prev = 0.f;
   bool prev_kept = false;
   int j_prev = 0;
-  // PV of the previous tile from vbuf(VB) with the tile maximum from tmx[PB]
+  // log2 of the largest code (448 for e4m3, 127 for int8)
+  constexpr float LOG2_QMAX = FMT == kFmtInt8 ? 6.98868468677216585f : 8.80735492205760410f;
+  // P and PV of the previous tile from vbuf(VB), with its largest P^ from tmx[PB]: tmx holds
+  // each half's max over rows of (row's tile maximum of S sc - the row's exact maximum), i.e. the
+  // log2 of the tile's largest P^ = 2^(S sc - m).  The code's argument P^ QMAX / max(tile) is
+  // then one exponential, 2^(S sc - m + log2 QMAX - e), and the tile's scale sP = 2^e / QMAX.
   auto pv_prev = [&](auto VBC, auto PBC) {
     constexpr int PB = decltype(PBC)::value;
-    const float tmax = fmaxf(tmx[PB][blk][0], tmx[PB][blk][1]);
-    const float qs = tmax > 0.f ? QMAX / tmax : 0.f;  // an all-underflow tile adds 0
+    const float e = fmaxf(tmx[PB][blk][0], tmx[PB][blk][1]);
+    if (e == -INFINITY) return;  // every P^ underflows: the tile adds 0 (workgroup-uniform per block)
+    const float bias = LOG2_QMAX - e - mrow;
     const uint8_t* vs = vbuf(VBC);
     i32x8 va[NC];
 #pragma unroll
@@ -780,18 +791,26 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     }
     // P8 as the B operand: slot 16kt + i <-> key 32kt + 8(i/4) + 4g + i%4
     i32x8 pf;
+    float ysum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const float* pq4 = &pp[kt][4 * qd];
-        if constexpr (FMT == kFmtInt8)  // P in [0, tmax]: codes 0 .. 127
-          pf[4 * kt + qd] = (int)cvt4_u7(pq4[0], pq4[1], pq4[2], pq4[3], qs);
-        else
-          pf[4 * kt + qd] = (int)cvt4_e4m3(sat(pq4[0] * qs), sat(pq4[1] * qs), sat(pq4[2] * qs),
-                                           sat(pq4[3] * qs));
+        float y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          y[u] = fast_exp2(fmaf(ss[kt][4 * qd + u], sc_prev, bias));
+          ysum += y[u];
+        }
+        if constexpr (FMT == kFmtInt8)  // y in [0, 127]: codes 0 .. 127
+          pf[4 * kt + qd] = (int)cvt4_u7(y[0], y[1], y[2], y[3], 1.f);
+        else  // y >= 0; one rounding above 448 is clamped back to it
+          pf[4 * kt + qd] = (int)cvt4_e4m3(fminf(y[0], kE4M3Max), fminf(y[1], kE4M3Max),
+                                           fminf(y[2], kE4M3Max), fminf(y[3], kE4M3Max));
       }
-    const float pv_scale = (tmax / QMAX) * sv[(size_t)bh * nb + j_prev];
+    const float sp = fast_exp2(e - LOG2_QMAX);  // the tile's scale max / QMAX
+    lsum = fmaf(ysum, sp, lsum);                // the unquantised P^ = y sP
+    const float pv_scale = sp * sv[(size_t)bh * nb + j_prev];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const f32x16 tmp = dot1(va[c], pf);
@@ -816,13 +835,14 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     const int e = ul[t];
     const int j = e >> 2;
     const bool kept = (e >> blk) & 1;  // wavefront-uniform
-    float pmax = 0.f;
+    float emax = -INFINITY;
     if (kept) {
       const float sc = sqi * sk[(size_t)bh * nb + j] * c_log2;
       const int nv = min(kBlock, N - j * kBlock);
       const int lim = row_ok ? nv - 4 * g : 0;
       const bool full = rows_all_ok && nv == kBlock;  // wavefront-uniform: no key or row mask
       const uint8_t* ks = kbuf(BUFC);
+      float amax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         i32x8 ka[N8];
@@ -833,26 +853,21 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
           const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + k8_off(r, 64 * st + 32 * g + 16));
           ka[st] = join8(a0, a1);
         }
-        const f32x16 s = dot64(ka, qf);
-        if (full) {
+        f32x16 s = dot64(ka, qf);
+        if (!full) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            pp[kt][i] = fast_exp2(fmaf(s[i], sc, -mrow));
-            lsum += pp[kt][i];
-            pmax = fmaxf(pmax, pp[kt][i]);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            pp[kt][i] = 32 * kt + 8 * (i / 4) + i % 4 < lim ? fast_exp2(fmaf(s[i], sc, -mrow)) : 0.f;
-            lsum += pp[kt][i];
-            pmax = fmaxf(pmax, pp[kt][i]);
-          }
+          for (int i = 0; i < 16; ++i)
+            if (32 * kt + 8 * (i / 4) + i % 4 >= lim) s[i] = -INFINITY;
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, s[i]);
+        ss[kt] = s;
       }
-      pmax = wave_max(pmax);
+      // log2 of this row's largest P^ in the tile (sc > 0), then the max over the 32 rows
+      emax = wave_max(amax * sc - mrow);
+      sc_prev = sc;
     }
-    if (lane == 0) tmx[BUF][blk][half] = pmax;
+    if (lane == 0) tmx[BUF][blk][half] = emax;
     prev_kept = kept;
     j_prev = j;
     wait_vmem();
