@@ -115,44 +115,20 @@ def traffic_for(kernel_key, digest):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(inputs, wl, idx_gpu, budget_s=15.0):
-    """The oracle as it stands on a bounded sample: whole heads (router, block states, every
-    query block's forward) in order until about `budget_s` of CPU time, the last head possibly
-    on a random subset of its query blocks; scaled to the whole workload."""
+def cpu_baseline(inputs, wl):
+    """The oracle as it stands, timed on one whole call of the workload: the router over every
+    head, then the forward (block states and every query block) of every head."""
     import numpy as np
     import threadpoolctl
 
     import oracle
 
-    nb = wl.n_blocks
-    heads = wl.B * wl.H
-    per_head, used, blocks_done = [], 0.0, 0
-    for bh in range(heads):
-        b, h = divmod(bh, wl.H)
-        Q, K, V = inputs["Q"][b, h], inputs["K"][b, h], inputs["V"][b, h]
-        t0 = time.perf_counter()
-        r = oracle.route(Q[None, None], K[None, None], inputs["Wq"].double(), inputs["Wk"].double(), wl.topk, 64)
-        states = oracle.block_states(K, V, 64)
-        t_fixed = time.perf_counter() - t0
-        idx = r["idx"][0, 0]
-        order = np.random.default_rng(bh).permutation(nb)
-        done, t_fwd = 0, 0.0
-        while done < nb and used + t_fixed + t_fwd < budget_s:
-            blocks = order[done : done + 8]
-            t0 = time.perf_counter()
-            if wl.fp8:
-                oracle.forward_fp8_head(Q, K, V, idx, inputs["alpha"][b, h], 64, q_blocks=blocks, states=states)
-            else:
-                oracle.forward_head(Q, K, V, idx, inputs["alpha"][b, h], 64, q_blocks=blocks, states=states)
-            t_fwd += time.perf_counter() - t0
-            done += len(blocks)
-        used += t_fixed + t_fwd
-        blocks_done += done
-        per_head.append(t_fixed + t_fwd * nb / max(done, 1))
-        if used >= budget_s:
-            break
-    per_call = heads * sum(per_head) / len(per_head)
-    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    t0 = time.perf_counter()
+    r = oracle.route(inputs["Q"], inputs["K"], inputs["Wq"].double(), inputs["Wk"].double(), wl.topk, 64)
+    fwd = oracle.forward_fp8 if wl.fp8 else oracle.forward
+    fwd(inputs["Q"], inputs["K"], inputs["V"], r["idx"], inputs["alpha"], 64)
+    per_call = time.perf_counter() - t0
+    blas_threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
     try:
         blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
         blas = f"{blas.get('name')} {blas.get('version')}"
@@ -161,10 +137,10 @@ def cpu_baseline(inputs, wl, idx_gpu, budget_s=15.0):
     return {
         "seconds_per_call": per_call,
         "blas": blas,
-        "sample": f"{len(per_head)} of {heads} heads (router, block states and {blocks_done} query "
-                  f"blocks of {len(per_head) * nb}; {used:.1f} s of CPU time), scaled to all heads "
-                  f"and query blocks",
-        "cores": int(threads),
+        "blas_threads": int(blas_threads),
+        "sample": f"one whole call, measured: router over all {wl.B * wl.H} heads, then block states "
+                  f"and every query block of every head",
+        "cores": len(os.sched_getaffinity(0)),
     }
 
 
@@ -231,10 +207,11 @@ def pisa_cpu_baseline(inputs, wl, budget_s=15.0):
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
     return {
         "seconds_per_call": heads * sum(per_head) / len(per_head),
-        "sample": f"{len(per_head)} of {heads} heads (statistics, routing and {blocks_done} query "
-                  f"blocks of {len(per_head) * nb}; {used:.1f} s of CPU time), scaled to all heads "
-                  f"and query blocks",
-        "cores": int(threads),
+        "sample": f"extrapolated: {len(per_head)} of {heads} heads (statistics, routing and "
+                  f"{blocks_done} query blocks of {len(per_head) * nb}; {used:.1f} s of CPU time), "
+                  f"scaled to all heads and query blocks",
+        "cores": len(os.sched_getaffinity(0)),
+        "blas_threads": int(threads),
     }
 
 
@@ -359,6 +336,7 @@ def bench_pisa(a, wl):
             "unit": "TFLOP/s (effective, same FLOP count)",
             "ms_per_call": 1e3 * cb["seconds_per_call"],
             "cores": cb["cores"],
+            "blas_threads": cb["blas_threads"],
             "kind": "oracle",
             "sample": cb["sample"],
         }
@@ -487,8 +465,9 @@ def svoo_cpu_baseline(inputs, wl, iters, reuse, budget_s=15.0):
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
     return {
         "seconds_per_call": wl.B * wl.H * per_head,
-        "cores": threads,
-        "sample": f"head 0 of {wl.B * wl.H}: co-clustering ({iters} iterations, {t_cluster:.1f} s, charged 1/{reuse} "
+        "cores": len(os.sched_getaffinity(0)),
+        "blas_threads": int(threads),
+        "sample": f"extrapolated: head 0 of {wl.B * wl.H}: co-clustering ({iters} iterations, {t_cluster:.1f} s, charged 1/{reuse} "
                   f"per step), gathers, router, states and {done} of {nb} query blocks' forward; scaled to "
                   f"{wl.B * wl.H} heads",
     }
@@ -614,6 +593,7 @@ def bench_svoo(a, wl):
             "unit": "TFLOP/s (effective, same FLOP count)",
             "ms_per_call": 1e3 * cb["seconds_per_call"],
             "cores": cb["cores"],
+            "blas_threads": cb["blas_threads"],
             "kind": "oracle",
             "sample": cb["sample"],
         }
@@ -622,8 +602,8 @@ def bench_svoo(a, wl):
 
 def mass_covered(inputs, wl, idx_np, blocks):
     """Diagnostic (not pass/fail): the share of each query row's full softmax attention mass
-    that falls on the tokens of its query block's kept blocks, for a few query blocks of head
-    (0, 0), float64 on the host; mean and minimum over their rows.  `best_k_mean` is the same
+    that falls on the tokens of its query block's kept blocks, for the given query blocks of
+    head (0, 0), float64 on the host; mean and minimum over their rows.  `best_k_mean` is the same
     share for the k blocks holding the most mass (the most any k-block selection could cover):
     it shows how concentrated the data are, independently of the router's projections."""
     import numpy as np
@@ -647,7 +627,8 @@ def mass_covered(inputs, wl, idx_np, blocks):
         top = np.argsort(-pb.mean(axis=0))[:k]
         best.append(pb[:, top].sum(axis=1))
     sh, bt = np.concatenate(shares), np.concatenate(best)
-    return {"query_blocks": [int(b) for b in blocks], "head": [0, 0], "mean": float(sh.mean()),
+    blocks = list(blocks)
+    return {"query_blocks": len(blocks), "head": [0, 0], "mean": float(sh.mean()),
             "min": float(sh.min()), "best_k_mean": float(bt.mean())}
 
 
@@ -861,15 +842,15 @@ def main():
                             "note": "inside the states time: the complement-mask x stacked-states "
                                     "GEMM (2 n_b^2 d^2 per head)"}
     nbk = wl.n_blocks
-    rec["diagnostic_mass_covered"] = mass_covered(
-        inputs, wl, idx[0, 0].cpu().numpy(), sorted({0, nbk // 3, (2 * nbk) // 3, nbk - 1}))
+    rec["diagnostic_mass_covered"] = mass_covered(inputs, wl, idx[0, 0].cpu().numpy(), range(nbk))
     if not a.no_cpu_baseline:
-        cb = cpu_baseline(inputs, wl, idx)
+        cb = cpu_baseline(inputs, wl)
         rec["cpu_baseline"] = {
             "value": flops / cb["seconds_per_call"] / 1e12,
             "unit": "TFLOP/s (effective, same FLOP count)",
             "ms_per_call": 1e3 * cb["seconds_per_call"],
             "cores": cb["cores"],
+            "blas_threads": cb["blas_threads"],
             "blas": cb["blas"],
             "kind": "oracle",
             "sample": cb["sample"],
