@@ -106,6 +106,74 @@ def lib_path() -> str:
     return _LIB_PATH
 
 
+def configure(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Argument and result types of every libsla entry point on a loaded copy of the library."""
+    P = ctypes.POINTER(Problem)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.sla_route_workspace_bytes.argtypes = [P]
+    L.sla_route_workspace_bytes.restype = sz
+    L.sla_forward_workspace_bytes.argtypes = [P, i32]
+    L.sla_forward_workspace_bytes.restype = sz
+    L.sla_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sla_route.restype = i32
+    L.sla_route_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.sla_route_noalloc.restype = i32
+    L.sla_validate_idx.argtypes = [P, vp, vp]
+    L.sla_validate_idx.restype = i32
+    fwd = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for name in ("sla_forward", "sla_forward_fp8"):
+        getattr(L, name).argtypes = fwd
+        getattr(L, name).restype = i32
+    for name in ("sla_forward_int8",):
+        getattr(L, name).argtypes = fwd
+        getattr(L, name).restype = i32
+    for name in ("sla_forward_ex", "sla_forward_fp8_ex", "sla_forward_int8_ex"):
+        getattr(L, name).argtypes = fwd + [ctypes.POINTER(ForwardOpts)]
+        getattr(L, name).restype = i32
+    for name in ("sla_quantize_e4m3", "sla_quantize_int8"):
+        getattr(L, name).argtypes = [P, vp, vp, vp, vp]
+        getattr(L, name).restype = i32
+    L.sla_backward_workspace_bytes.argtypes = [P]
+    L.sla_backward_workspace_bytes.restype = sz
+    L.sla_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sla_backward.restype = i32
+    L.sla_pisa_stats_bytes.argtypes = [P]
+    L.sla_pisa_stats_bytes.restype = sz
+    L.sla_pisa_workspace_bytes.argtypes = [P]
+    L.sla_pisa_workspace_bytes.restype = sz
+    L.sla_pisa_stats_offsets.argtypes = [P, ctypes.POINTER(sz)]
+    L.sla_pisa_stats_offsets.restype = i32
+    L.sla_pisa_stats.argtypes = [P, vp, vp, vp, sz, vp, sz, vp]
+    L.sla_pisa_stats.restype = i32
+    L.sla_pisa_route.argtypes = [P, vp, vp, sz, i32, vp, vp, vp, vp, sz, vp]
+    L.sla_pisa_route.restype = i32
+    L.sla_pisa_forward.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
+    L.sla_pisa_forward.restype = i32
+    L.sla_svoo_workspace_bytes.argtypes = [P]
+    L.sla_svoo_workspace_bytes.restype = sz
+    L.sla_svoo_cluster.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.sla_svoo_cluster.restype = i32
+    for name in ("sla_svoo_gather", "sla_svoo_scatter"):
+        getattr(L, name).argtypes = [P, vp, i32, vp, vp, vp]
+        getattr(L, name).restype = i32
+    f32 = ctypes.c_float
+    L.sla_soft_workspace_bytes.argtypes = [P]
+    L.sla_soft_workspace_bytes.restype = sz
+    L.sla_soft_route.argtypes = [P, vp, vp, vp, vp, f32, vp, vp, sz, vp]
+    L.sla_soft_route.restype = i32
+    L.sla_soft_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sla_soft_forward.restype = i32
+    L.sla_soft_backward.argtypes = [P, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sla_soft_backward.restype = i32
+    L.sla_stage1_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, sz, vp]
+    L.sla_stage1_step.restype = i32
+    L.sla_status_string.argtypes = [i32]
+    L.sla_status_string.restype = ctypes.c_char_p
+    L.sla_last_hip_error.argtypes = []
+    L.sla_last_hip_error.restype = i32
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """The loaded libsla.so (raises if it has not been built)."""
     global _LIB
@@ -114,69 +182,7 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{_LIB_PATH} is missing: build it with `python -m block_sparse_linear_02_amd.build`"
             )
-        L = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.POINTER(Problem)
-        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
-        L.sla_route_workspace_bytes.argtypes = [P]
-        L.sla_route_workspace_bytes.restype = sz
-        L.sla_forward_workspace_bytes.argtypes = [P, i32]
-        L.sla_forward_workspace_bytes.restype = sz
-        L.sla_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.sla_route.restype = i32
-        L.sla_route_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.sla_route_noalloc.restype = i32
-        fwd = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for name in ("sla_forward", "sla_forward_fp8"):
-            getattr(L, name).argtypes = fwd
-            getattr(L, name).restype = i32
-        for name in ("sla_forward_int8",):
-            getattr(L, name).argtypes = fwd
-            getattr(L, name).restype = i32
-        for name in ("sla_forward_ex", "sla_forward_fp8_ex", "sla_forward_int8_ex"):
-            getattr(L, name).argtypes = fwd + [ctypes.POINTER(ForwardOpts)]
-            getattr(L, name).restype = i32
-        for name in ("sla_quantize_e4m3", "sla_quantize_int8"):
-            getattr(L, name).argtypes = [P, vp, vp, vp, vp]
-            getattr(L, name).restype = i32
-        L.sla_backward_workspace_bytes.argtypes = [P]
-        L.sla_backward_workspace_bytes.restype = sz
-        L.sla_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.sla_backward.restype = i32
-        L.sla_pisa_stats_bytes.argtypes = [P]
-        L.sla_pisa_stats_bytes.restype = sz
-        L.sla_pisa_workspace_bytes.argtypes = [P]
-        L.sla_pisa_workspace_bytes.restype = sz
-        L.sla_pisa_stats_offsets.argtypes = [P, ctypes.POINTER(sz)]
-        L.sla_pisa_stats_offsets.restype = i32
-        L.sla_pisa_stats.argtypes = [P, vp, vp, vp, sz, vp, sz, vp]
-        L.sla_pisa_stats.restype = i32
-        L.sla_pisa_route.argtypes = [P, vp, vp, sz, i32, vp, vp, vp, vp, sz, vp]
-        L.sla_pisa_route.restype = i32
-        L.sla_pisa_forward.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
-        L.sla_pisa_forward.restype = i32
-        L.sla_svoo_workspace_bytes.argtypes = [P]
-        L.sla_svoo_workspace_bytes.restype = sz
-        L.sla_svoo_cluster.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
-        L.sla_svoo_cluster.restype = i32
-        for name in ("sla_svoo_gather", "sla_svoo_scatter"):
-            getattr(L, name).argtypes = [P, vp, i32, vp, vp, vp]
-            getattr(L, name).restype = i32
-        f32 = ctypes.c_float
-        L.sla_soft_workspace_bytes.argtypes = [P]
-        L.sla_soft_workspace_bytes.restype = sz
-        L.sla_soft_route.argtypes = [P, vp, vp, vp, vp, f32, vp, vp, sz, vp]
-        L.sla_soft_route.restype = i32
-        L.sla_soft_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.sla_soft_forward.restype = i32
-        L.sla_soft_backward.argtypes = [P, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.sla_soft_backward.restype = i32
-        L.sla_stage1_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, sz, vp]
-        L.sla_stage1_step.restype = i32
-        L.sla_status_string.argtypes = [i32]
-        L.sla_status_string.restype = ctypes.c_char_p
-        L.sla_last_hip_error.argtypes = []
-        L.sla_last_hip_error.restype = i32
-        _LIB = L
+        _LIB = configure(ctypes.CDLL(_LIB_PATH))
     return _LIB
 
 
@@ -215,6 +221,23 @@ def route_workspace_bytes(Q, topk: int) -> int:
 
 def forward_workspace_bytes(Q, topk: int, variant: int = 0) -> int:
     return lib().sla_forward_workspace_bytes(ctypes.byref(_problem(Q, topk)), variant)
+
+
+def validate_idx(Q, idx) -> bool:
+    """Debug check of idx [B, H, n_b, topk] int32 for inputs shaped like Q (sla_validate_idx):
+    True when every entry lies in [0, n_b) and each row is strictly ascending.  Synchronises
+    the current stream."""
+    B, H, N, d = Q.shape
+    nb = -(-N // BLOCK)
+    if idx.dtype != torch.int32 or idx.dim() != 4 or tuple(idx.shape[:3]) != (B, H, nb):
+        raise ValueError("idx must be int32 [B, H, n_b, topk]")
+    idx = idx.contiguous()
+    st = lib().sla_validate_idx(ctypes.byref(_problem(Q, idx.shape[3])), _ptr(idx), _stream())
+    if st == SLA_ERR_INVALID:
+        return False
+    if st != SLA_OK:
+        raise SLAError(st, "sla_validate_idx")
+    return True
 
 
 def route(Q, K, proj_q, proj_k, topk: int, want_mask: bool = False, want_scores: bool = False,

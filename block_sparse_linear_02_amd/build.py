@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["router.hip", "linear_state.hip", "linear_gemm.hip", "sparse.hip", "sparse_pair.hip",
            "linear_apply.hip", "fp8.hip", "pisa_stats.hip", "pisa.hip", "branch_drop.hip",
-           "bwd.hip", "svoo.hip", "soft.hip", "api.cpp"]
+           "bwd.hip", "svoo.hip", "soft.hip", "validate.hip", "api.cpp"]
 
 FLAGS = [
     "-O3",
@@ -69,6 +69,50 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(f"built {OUT}")
     return OUT
+
+
+ASAN_DIR = os.path.join(PKG, "_build_asan")
+ASAN_OUT = os.path.join(ASAN_DIR, "libsla_asan.so")
+
+
+def asan_runtime() -> str:
+    """The compiler's AddressSanitizer runtime (to preload into a host process using ASAN_OUT)."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime of the HIP compiler was not found")
+    return path
+
+
+def build_asan(verbose: bool = False) -> str:
+    """A copy of the library with AddressSanitizer on its host code only (argument checks,
+    workspace carving, status strings; the device code is built as usual), for CPU tests of
+    those paths.  Returns its path."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    flags = [f for f in FLAGS if f != "-O3"] + [
+        "-O1", "-g", *"-Xarch_host -fsanitize=address".split(), "-fno-omit-frame-pointer"]
+
+    def comp(src: str) -> str:
+        obj = os.path.join(ASAN_DIR, os.path.basename(src) + ".o")
+        lang = ["-x", "hip"] if src.endswith(".cpp") else []
+        cmd = [_hipcc(), *flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    tmp = ASAN_OUT + ".tmp"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *"-Xarch_host -fsanitize=address".split(),
+           "-shared-libasan", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ASAN_OUT)
+    if verbose:
+        print(f"built {ASAN_OUT}")
+    return ASAN_OUT
 
 
 if __name__ == "__main__":

@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cstdlib>
 #include <cstdint>
 #include <mutex>
 
@@ -206,6 +207,9 @@ inline int hip_fail(hipError_t e) {
   return SLA_ERR_HIP;
 }
 
+bool validate_requested();
+int validate_idx_impl(const sla::Dims& d, const int32_t* idx, hipStream_t stream);
+
 // lowbit: 0 none, 1 e4m3, 2 int8 (int8 exists in the mask-product mode only, its default)
 int forward_impl(const sla_problem* p, const void* Q, const void* K, const void* V,
                  const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
@@ -236,6 +240,14 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   carve_forward(d, variant, ws, &w);
 
   hipError_t e = hipSuccess;
+  if (validate_requested()) {
+    if (opts && opts->idx_ready) {
+      e = hipStreamWaitEvent(stream, opts->idx_ready, 0);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    st = validate_idx_impl(d, idx, stream);
+    if (st != SLA_OK) return st;
+  }
   const uint32_t* flags = nullptr;
   if (drop) {
     e = sla::launch_branch_flags(d, alpha, opts->drop_tau, w.flags, stream);
@@ -441,25 +453,57 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::mutex g_scratch_mu;
 
-// Device address of this device's `scratch`, looked up on the first call with the device current.
-int scratch_of_current_device(void** out) {
+// Device address of a file-scope __device__ symbol on the current device, looked up on the
+// first call with that device current and kept in cache[device].
+int symbol_of_current_device(const void* symbol, std::atomic<void*>* cache, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
   if (dev < 0 || dev >= kMaxDevices) return SLA_ERR_UNSUPPORTED;
-  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  void* ptr = cache[dev].load(std::memory_order_acquire);
   if (!ptr) {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
-    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    ptr = cache[dev].load(std::memory_order_relaxed);
     if (!ptr) {
-      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      e = hipGetSymbolAddress(&ptr, symbol);
       if (e != hipSuccess) return hip_fail(e);
       if (!ptr) return hip_fail(hipErrorInvalidSymbol);
-      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+      cache[dev].store(ptr, std::memory_order_release);
     }
   }
   *out = ptr;
   return SLA_OK;
+}
+
+// Device address of this device's `scratch`.
+int scratch_of_current_device(void** out) {
+  return symbol_of_current_device(HIP_SYMBOL(scratch), g_scratch_ptr, out);
+}
+
+// Result word of the debug idx check: one per GPU, alive until the process ends; checks that
+// overlap on one GPU race on it (a debug path).
+static __device__ int validate_bad[1];
+std::atomic<void*> g_validate_ptr[kMaxDevices];
+
+// SLA_VALIDATE=1 in the environment: the entry points that read idx check it first.
+bool validate_requested() {
+  const char* e = getenv("SLA_VALIDATE");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+// Check idx on the device (entries in [0, n_b), rows strictly ascending), synchronise the
+// stream and read the verdict: SLA_OK or SLA_ERR_INVALID.
+int validate_idx_impl(const sla::Dims& d, const int32_t* idx, hipStream_t stream) {
+  if (d.topk == 0) return SLA_OK;
+  void* flag = nullptr;
+  int st = symbol_of_current_device(HIP_SYMBOL(validate_bad), g_validate_ptr, &flag);
+  if (st != SLA_OK) return st;
+  int bad = 0;
+  hipError_t e = sla::launch_validate_idx(d, idx, static_cast<int*>(flag), stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(&bad, flag, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return bad == 0 ? SLA_OK : SLA_ERR_INVALID;
 }
 
 }  // namespace
@@ -726,6 +770,10 @@ int sla_pisa_forward(const sla_problem* p, const void* Q, const void* K, const v
   if (!Q || !K || !V || !stats || !O || (d.topk > 0 && !idx)) return SLA_ERR_INVALID;
   if (d.nb > sla::pisa_max_blocks()) return SLA_ERR_UNSUPPORTED;
   if (stats_bytes < carve_pisa_stats(d, nullptr, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  if (validate_requested()) {
+    st = validate_idx_impl(d, idx, stream);
+    if (st != SLA_OK) return st;
+  }
   PisaStats s;
   carve_pisa_stats(d, const_cast<void*>(stats), &s, nullptr);
   hipError_t e = sla::launch_pisa(d, Q, K, V, idx, s.kbar_hi, s.kbar_lo, s.vsum, s.hbar_t, O, stream);
@@ -750,6 +798,10 @@ int sla_backward(const sla_problem* p, const void* Q, const void* K, const void*
   if (!Q || !K || !V || !alpha || !dO || !dQ || !dK || !dV || !dalpha || (d.topk > 0 && !idx) || !ws)
     return SLA_ERR_INVALID;
   if (ws_bytes < carve_backward(d, nullptr, nullptr)) return SLA_ERR_WORKSPACE;
+  if (validate_requested()) {
+    st = validate_idx_impl(d, idx, stream);
+    if (st != SLA_OK) return st;
+  }
   BwdWs w;
   carve_backward(d, ws, &w);
   hipError_t e;
@@ -836,6 +888,14 @@ const char* sla_status_string(int status) {
     case SLA_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
   }
+}
+
+int sla_validate_idx(const sla_problem* p, const int32_t* idx, hipStream_t stream) {
+  sla::Dims d;
+  int st = check_problem(p, &d);
+  if (st != SLA_OK) return st;
+  if (d.topk > 0 && !idx) return SLA_ERR_INVALID;
+  return validate_idx_impl(d, idx, stream);
 }
 
 int sla_last_hip_error(void) { return g_last_hip_error; }

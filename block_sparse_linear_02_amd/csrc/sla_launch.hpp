@@ -64,6 +64,9 @@ hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const
                               const float* Z, const float* zb, float* O, hipStream_t stream,
                               const uint32_t* flags = nullptr, const TrainRows* tr = nullptr,
                               const int32_t* out_rows = nullptr);
+// Debug check of idx (validate.hip): *bad = the number of rows with an entry outside [0, n_b)
+// or not strictly ascending.
+hipError_t launch_validate_idx(const Dims& p, const int32_t* idx, int* bad, hipStream_t stream);
 // SoftTop-k training path (soft.hip, and the SOFT forms of the mask GEMM and the pair kernel;
 // bf16, d = 128).  Weighted mask GEMM: T_i = sum_j wt[i][j] h_j with wt [BH][nb][pitch] bf16
 // (pitch = tsel_weight_pitch(nb), zero past n_b).  Soft sparse branch: every key block j of

@@ -39,8 +39,8 @@
  * SLA_ERR_INVALID; a shape outside the compiled set (block != 64, d not in {64, 128}, dtype
  * not in sla_dtype) gives SLA_ERR_UNSUPPORTED; a workspace smaller than the matching
  * *_workspace_bytes() gives SLA_ERR_WORKSPACE; a failed launch gives SLA_ERR_HIP (the hipError_t
- * is available from sla_last_hip_error()).  idx contents are trusted (ascending, in range);
- * non-finite inputs give undefined output.
+ * is available from sla_last_hip_error()).  idx contents are trusted (ascending, in range)
+ * unless SLA_VALIDATE=1 (sla_validate_idx); non-finite inputs give undefined output.
  */
 #ifndef SLA_H
 #define SLA_H
@@ -222,6 +222,18 @@ int sla_backward(const sla_problem* p, const void* Q, const void* K, const void*
 int sla_route_noalloc(const sla_problem* p, const void* Q, const void* K, const float* proj_q,
                       const float* proj_k, int32_t* idx, uint8_t* mask, float* scores,
                       hipStream_t stream);
+
+/* Debug check of an index list (HardTop-k's output: SLA2 Italian summary section 2.B, Arabic
+ * summary section 2.ba): every entry of idx [B][H][n_b][topk] int32 lies in [0, n_b) and each
+ * row is strictly ascending.  Runs one kernel on `stream`, then synchronises the stream (so
+ * the host waits for everything enqueued before it) and returns SLA_OK, or SLA_ERR_INVALID for a
+ * malformed list; topk = 0 checks nothing.  The result word is a file-scope device variable (one
+ * per GPU): checks that overlap on one GPU race.
+ * With SLA_VALIDATE=1 in the environment, sla_forward*, sla_backward and sla_pisa_forward run
+ * this check first (after the host-side checks, after waiting for opts->idx_ready if given) and
+ * return its SLA_ERR_INVALID with nothing else enqueued; this debug mode synchronises the host,
+ * against the no-synchronisation rule above.  Without it, idx contents are trusted. */
+int sla_validate_idx(const sla_problem* p, const int32_t* idx, hipStream_t stream);
 
 const char* sla_status_string(int status);
 /* hipError_t of the most recent SLA_ERR_HIP on the calling thread (0 if none). */

@@ -20,6 +20,11 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its
 
 @pytest.fixture(scope="module")
 def L():
+    # SLA_TEST_LIB: another build of the library to run these checks against (the host-only
+    # AddressSanitizer build, tests/test_asan_host.py)
+    other = os.environ.get("SLA_TEST_LIB")
+    if other:
+        return sla.configure(ctypes.CDLL(other))
     if not os.path.exists(sla.lib_path()):
         from block_sparse_linear_02_amd import build
 
@@ -180,6 +185,16 @@ def test_backward_checks(L):
     short = list(args)
     short[12] = wb - 1
     assert f(ctypes.byref(p), *short) == sla.SLA_ERR_WORKSPACE
+
+
+def test_validate_checks(L):
+    """sla_validate_idx: the host-side checks run before the device check; topk = 0 checks
+    nothing (no device call)."""
+    f = L.sla_validate_idx
+    assert f(ctypes.byref(P()), None, None) == sla.SLA_ERR_INVALID
+    assert f(ctypes.byref(P(topk=65)), FAKE, None) == sla.SLA_ERR_INVALID  # topk > n_b
+    assert f(ctypes.byref(P(d=96)), FAKE, None) == sla.SLA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(P(topk=0)), None, None) == sla.SLA_OK
 
 
 def test_soft_checks(L):
