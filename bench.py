@@ -47,6 +47,8 @@ def parse():
                     help="video_s | video_l | video_l_fp8 | pisa_video_s | pisa_video_l | svoo_video_s")
     ap.add_argument("--linear-mode", default="mask_product", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage1", action="store_true",
+                    help="the SoftTop-k stage-1 fit step (sla_stage1_step) instead of the forward")
     ap.add_argument("--backward", action="store_true",
                     help="the training step: route + sla_backward (forward recomputed inside, then "
                          "the gradients of Q, K, V and alpha)")
@@ -340,6 +342,82 @@ def bench_pisa(a, wl):
             "kind": "oracle",
             "sample": cb["sample"],
         }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_stage1(a, wl):
+    """One step = sla.stage1_step: the SoftTop-k router, the soft-mask forward (every key block
+    weighted by M, so the sparse branch walks all n_b^2 tile pairs), the MSE loss against a
+    full-attention output computed once beforehand, the gradients into proj_q, proj_k and alpha,
+    and the in-place update."""
+    import torch
+
+    import block_sparse_linear_02_amd as sla
+    import gen
+
+    dev = torch.device("cuda:0")
+    inputs = gen.draw(wl, 0)
+    Q, K, V = (inputs[k].to(dev) for k in ("Q", "K", "V"))
+    alpha = inputs["alpha"].to(dev).float().contiguous()
+    Wq, Wk = inputs["Wq"].to(dev).float().contiguous(), inputs["Wk"].to(dev).float().contiguous()
+    B, H, N, d = Q.shape
+    nb = wl.n_blocks
+    temperature, lr_proj, lr_alpha = 0.3, 10.0, 1000.0
+    # full attention: every block kept, alpha = 1 (outside the timed region)
+    idx_all = torch.arange(nb, dtype=torch.int32, device=dev).expand(B, H, nb, nb).contiguous()
+    O_full = sla.forward(Q, K, V, idx_all, torch.ones_like(alpha), linear_mode="mask_product")
+    del idx_all
+    ws = torch.empty(sla.soft_workspace_bytes(Q, wl.topk), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    ev_t = events(a.steps)
+    for e in ev_t:
+        e[0].record()
+        e[1].record()
+    torch.cuda.synchronize()
+
+    def step(i=None):
+        if i is not None:
+            ev_t[i][0].record()
+        sla.stage1_step(Q, K, V, O_full, Wq, Wk, alpha, wl.topk, temperature, lr_proj, lr_alpha,
+                        workspace=ws, loss=loss)
+        if i is not None:
+            ev_t[i][1].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    first = float(loss.item())
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / a.steps
+    # the soft forward's attention products over every (query, key) pair: 4 N^2 d per head
+    dense = 4.0 * N * N * d * B * H
+    rec = {
+        "metric": "SLA2 stage-1 router fit (SoftTop-k forward + gradients + update) ms/step",
+        "value": ms,
+        "unit": "ms/step",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded clustered video-DiT-shaped tensors, random projections)",
+        "config": {
+            "workload": f"{wl.name}: B={B} H={H} N={N} d={d} block=64 topk={wl.topk} of {nb}, "
+                        f"stage-1 step at temperature {temperature}, lr {lr_proj} (projections), "
+                        f"{lr_alpha} (alpha)",
+            "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": wl.topk,
+        },
+        "step_ms_events": quantiles(ev_t),
+        "soft_forward_dense_tflops": dense / (ms * 1e-3) / 1e12,
+        "loss_after_warmup": first,
+        "loss_last": float(loss.item()),
+    }
     print(json.dumps(rec), flush=True)
 
 
@@ -662,6 +740,9 @@ def main():
     wl = gen.workload(a.workload)
     if wl.name.startswith("pisa"):
         bench_pisa(a, wl)
+        return
+    if a.stage1:
+        bench_stage1(a, wl)
         return
     if a.backward:
         bench_backward(a, wl)
