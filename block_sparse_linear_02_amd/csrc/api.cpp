@@ -361,7 +361,7 @@ struct SoftWs {
   float *O, *Os, *Ol, *lse2, *rden;
   __bf16 *dOs, *G, *dO;
   float *Dr, *e, *dzeta, *zb2, *z_part2;
-  float *dmsp, *dmlin, *ds, *Mw, *dWq, *dWk, *dalpha, *parts;
+  float *dmsp, *dmlin, *ds, *Mw, *dWq, *dWk, *dalpha, *parts, *pg;
 };
 size_t carve_soft(const sla::Dims& d, void* ws, SoftWs* out) {
   Carve c(ws);
@@ -405,6 +405,7 @@ size_t carve_soft(const sla::Dims& d, void* ws, SoftWs* out) {
   w.dWk = c.take<float>(dd);
   w.dalpha = c.take<float>(rows);
   w.parts = c.take<float>(sla::soft_loss_parts(d));
+  w.pg = c.take<float>(sla::router_bwd_part_floats());
   if (out) *out = w;
   return c.off;
 }
@@ -440,7 +441,7 @@ hipError_t soft_backward_impl(const sla::Dims& d, const void* Q, const void* K, 
   if (e == hipSuccess) e = sla::launch_soft_topk_bwd(d, M, w.dmsp, w.dmlin, temp, w.ds, dM, stream);
   if (e == hipSuccess) e = sla::launch_soft_pool(d, Q, K, Wq, Wk, w.qbar, w.kbar, w.qt, w.kt, stream);
   if (e == hipSuccess)
-    e = sla::launch_router_bwd(d, w.ds, w.qbar, w.kbar, w.qt, w.kt, w.dqt, w.dkt, dWq, dWk, stream);
+    e = sla::launch_router_bwd(d, w.ds, w.qbar, w.kbar, w.qt, w.kt, w.dqt, w.dkt, dWq, dWk, w.pg, stream);
   return e;
 }
 

@@ -104,9 +104,11 @@ hipError_t launch_soft_topk_bwd(const Dims& p, const float* M, const float* dmsp
                                 float temp, float* ds, float* dM_out, hipStream_t stream);
 // Router backward: dqt = ds kt / sqrt(d), dkt = ds^T qt / sqrt(d) per head, then
 // dWq = sum qbar^T dqt, dWk = sum kbar^T dkt over every (b, h) and block (fp32 [d][d]).
+// (part: router_bwd_part_floats() fp32 of workspace for the chunk partials of dW)
+size_t router_bwd_part_floats();
 hipError_t launch_router_bwd(const Dims& p, const float* ds, const float* qbar, const float* kbar,
                              const float* qt, const float* kt, float* dqt, float* dkt, float* dWq,
-                             float* dWk, hipStream_t stream);
+                             float* dWk, float* part, hipStream_t stream);
 // Stage 1: dO = bf16(2 (O - O_full) / count) and the loss partials (one per workgroup of
 // kLossThreads rows x channels), then the loss (fixed-order sum); the parameter update.
 int soft_loss_parts(const Dims& p);

@@ -25,7 +25,8 @@
 //   soft_topk_bwd_kernel per row: dM = the parts summed, ds = (M(1-M)/T)(dM - sum dM M(1-M) /
 //                        sum M(1-M)).
 //   router_rows_kernel   dqt_i = sum_j ds_ij kt_j / sqrt(d), dkt_j = sum_i ds_ij qt_i / sqrt(d).
-//   proj_grad_kernel     dW[r][c] = sum over every (b, h, block) of xbar[r] dy[c] (fixed order).
+//   proj_grad_kernel     dW[r][c] = sum over every (b, h, block) of xbar[r] dy[c]: partial sums
+//                        over 64 chunks of the rows, added in order by proj_grad_sum_kernel.
 //   soft_loss_kernel / soft_loss_sum_kernel / soft_update_kernel  the stage-1 loss, dO and the
 //                        step W -= lr dW, alpha = clamp(alpha - lr dalpha, 0, 1).
 // bf16 Q, K, V with d = 128; everything else fp32.  No float atomics: every sum has a fixed
@@ -297,32 +298,61 @@ __global__ __launch_bounds__(kSoftD) void router_rows_kernel(const float* __rest
                                                              float* __restrict__ dqt,
                                                              float* __restrict__ dkt) {
   constexpr int D = kSoftD;
+  constexpr int U = 8;  // independent partial sums (loads in flight), added in a fixed order
   const int c = threadIdx.x, r = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
   const float* dsh = ds + (size_t)bh * nb * nb;
-  float acc = 0.f;
-  if (which == 0) {  // dqt_r = sum_j ds[r][j] kt_j
-    const float* kth = kt + (size_t)bh * nb * D;
-    for (int j = 0; j < nb; ++j) acc = fmaf(dsh[(size_t)r * nb + j], kth[(size_t)j * D + c], acc);
-    dqt[((size_t)bh * nb + r) * D + c] = acc * inv_sqrt_d;
-  } else {  // dkt_r = sum_i ds[i][r] qt_i
-    const float* qth = qt + (size_t)bh * nb * D;
-    for (int i = 0; i < nb; ++i) acc = fmaf(dsh[(size_t)i * nb + r], qth[(size_t)i * D + c], acc);
-    dkt[((size_t)bh * nb + r) * D + c] = acc * inv_sqrt_d;
-  }
+  // which 0: dqt_r = sum_j ds[r][j] kt_j; which 1: dkt_r = sum_i ds[i][r] qt_i
+  const float* other = (which == 0 ? kt : qt) + (size_t)bh * nb * D;
+  const size_t sstride = which == 0 ? 1 : (size_t)nb;
+  const float* srow = dsh + (which == 0 ? (size_t)r * nb : (size_t)r);
+  float acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = 0.f;
+  int j = 0;
+  for (; j + U <= nb; j += U)
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = fmaf(srow[(size_t)(j + u) * sstride], other[(size_t)(j + u) * D + c], acc[u]);
+  for (; j < nb; ++j) acc[0] = fmaf(srow[(size_t)j * sstride], other[(size_t)j * D + c], acc[0]);
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) sum += acc[u];
+  (which == 0 ? dqt : dkt)[((size_t)bh * nb + r) * D + c] = sum * inv_sqrt_d;
 }
+
+// dW = x^T dy over `rows` rows in chunks: part[which][chunk][r][c] = sum over the chunk's rows
+// of x[t][r] dy[t][c] (four partial sums in flight), then proj_grad_sum_kernel adds the chunks in
+// order
+constexpr int kProjChunks = 64;
 
 __global__ __launch_bounds__(kSoftD) void proj_grad_kernel(const float* __restrict__ qbar,
                                                            const float* __restrict__ kbar,
                                                            const float* __restrict__ dqt,
                                                            const float* __restrict__ dkt, int rows,
-                                                           float* __restrict__ dWq,
-                                                           float* __restrict__ dWk) {
+                                                           int per_chunk, float* __restrict__ part) {
   constexpr int D = kSoftD;
-  const int c = threadIdx.x, r = blockIdx.x, which = blockIdx.y;
+  const int c = threadIdx.x, r = blockIdx.x, which = blockIdx.y, ch = blockIdx.z;
   const float* x = which ? kbar : qbar;
   const float* dy = which ? dkt : dqt;
+  const int t0 = ch * per_chunk, t1 = min(rows, t0 + per_chunk);
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int t = t0;
+  for (; t + 4 <= t1; t += 4) {
+    a0 = fmaf(x[(size_t)t * D + r], dy[(size_t)t * D + c], a0);
+    a1 = fmaf(x[(size_t)(t + 1) * D + r], dy[(size_t)(t + 1) * D + c], a1);
+    a2 = fmaf(x[(size_t)(t + 2) * D + r], dy[(size_t)(t + 2) * D + c], a2);
+    a3 = fmaf(x[(size_t)(t + 3) * D + r], dy[(size_t)(t + 3) * D + c], a3);
+  }
+  for (; t < t1; ++t) a0 = fmaf(x[(size_t)t * D + r], dy[(size_t)t * D + c], a0);
+  part[(((size_t)which * kProjChunks + ch) * D + r) * D + c] = (a0 + a1) + (a2 + a3);
+}
+
+__global__ __launch_bounds__(kSoftD) void proj_grad_sum_kernel(const float* __restrict__ part,
+                                                               float* __restrict__ dWq,
+                                                               float* __restrict__ dWk) {
+  constexpr int D = kSoftD;
+  const int c = threadIdx.x, r = blockIdx.x, which = blockIdx.y;
   float acc = 0.f;
-  for (int t = 0; t < rows; ++t) acc = fmaf(x[(size_t)t * D + r], dy[(size_t)t * D + c], acc);
+  for (int ch = 0; ch < kProjChunks; ++ch) acc += part[(((size_t)which * kProjChunks + ch) * D + r) * D + c];
   (which ? dWk : dWq)[r * D + c] = acc;
 }
 
@@ -420,15 +450,23 @@ hipError_t launch_soft_topk_bwd(const Dims& p, const float* M, const float* dmsp
   return hipGetLastError();
 }
 
+size_t router_bwd_part_floats() { return (size_t)2 * kProjChunks * kSoftD * kSoftD; }
+
 hipError_t launch_router_bwd(const Dims& p, const float* ds, const float* qbar, const float* kbar,
                              const float* qt, const float* kt, float* dqt, float* dkt, float* dWq,
-                             float* dWk, hipStream_t stream) {
+                             float* dWk, float* part, hipStream_t stream) {
   if (p.d != kSoftD) return hipErrorInvalidValue;
   router_rows_kernel<<<dim3(p.nb, p.B * p.H, 2), kSoftD, 0, stream>>>(ds, qt, kt, p.nb,
                                                                        1.f / sqrtf((float)kSoftD), dqt, dkt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  proj_grad_kernel<<<dim3(kSoftD, 2), kSoftD, 0, stream>>>(qbar, kbar, dqt, dkt, p.B * p.H * p.nb, dWq, dWk);
+  const int rows = p.B * p.H * p.nb;
+  const int per_chunk = (rows + kProjChunks - 1) / kProjChunks;
+  proj_grad_kernel<<<dim3(kSoftD, 2, kProjChunks), kSoftD, 0, stream>>>(qbar, kbar, dqt, dkt, rows, per_chunk,
+                                                                       part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  proj_grad_sum_kernel<<<dim3(kSoftD, 2), kSoftD, 0, stream>>>(part, dWq, dWk);
   return hipGetLastError();
 }
 
