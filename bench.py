@@ -47,6 +47,8 @@ def parse():
                     help="video_s | video_l | video_l_fp8 | pisa_video_s | pisa_video_l | svoo_video_s")
     ap.add_argument("--linear-mode", default="mask_product", choices=["fused", "literal", "mask_product"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", default="on", choices=["on", "off"],
+                    help="time the forward step as replays of one captured HIP graph (on) or as eager calls")
     ap.add_argument("--stage1", action="store_true",
                     help="the SoftTop-k stage-1 fit step (sla_stage1_step) instead of the forward")
     ap.add_argument("--backward", action="store_true",
@@ -823,9 +825,41 @@ def main():
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = 1e3 * elapsed / a.steps
-
+    ms = eager_ms = 1e3 * elapsed / a.steps
     step_q = quantiles(ev_t)
+
+    # the same step captured once in a HIP graph and replayed (the library enqueues kernels only,
+    # so route + forward is capturable): the seven launches then go out as one submission; the
+    # per-kernel times above come from the eager steps
+    launch, graph_q = "eager", None
+    if a.graph == "on" and side is None:
+        try:
+            gs = torch.cuda.Stream()
+            gs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(gs):
+                route_then_forward()
+            torch.cuda.current_stream().wait_stream(gs)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                route_then_forward()
+            for _ in range(a.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            ev_g = events(a.steps)
+            t0 = time.perf_counter()
+            for i in range(a.steps):
+                ev_g[i][0].record()
+                graph.replay()
+                ev_g[i][1].record()
+            torch.cuda.synchronize()
+            ms = 1e3 * (time.perf_counter() - t0) / a.steps
+            graph_q = quantiles(ev_g)
+            launch = "hip graph replay of route + forward"
+        except RuntimeError as e:  # reported, and the eager timing stands
+            launch = f"eager (graph capture failed: {e})"
+            ms = eager_ms
+
     # cold cache: the same call after writing a 512 MB scratch buffer (larger than the 256 MB
     # MALL), so that Q, K, V and the states come from HBM
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -894,15 +928,20 @@ def main():
                         + (", int8 sparse branch" if int8 else "")
                         + (f", alpha=1/0 on heads {a.drop_heads}" if a.drop_heads else "")
                         + (f", branch drop tau={a.drop_tau}" if a.drop_tau is not None else "")
-                        + (", router on a second stream beside the state kernels" if a.route_stream else ""),
+                        + (", router on a second stream beside the state kernels" if a.route_stream else "")
+                        + (", each step replayed as one HIP graph" if graph_q else ""),
             "B": B, "H": H, "N": N, "d": d, "block": 64, "topk": wl.topk,
         },
         "sparse_tflop_per_call": flops / 1e12,
-        "step_ms_events": step_q,
+        "launch": launch,
+        "eager_ms_per_step": eager_ms,
+        "step_ms_events": graph_q if graph_q else step_q,
+        "eager_step_ms_events": step_q,
         "cold_cache_step_ms": cold_q,
-        # with the router on the second stream its time overlaps the states' ("other" can be < 0)
+        # per-kernel event times of the eager steps ("other": the rest of an eager step; with the
+        # router on the second stream its time overlaps the states' and "other" can be < 0)
         "kernels_ms": {"route": route_ms, "states": states_ms, "sparse": sparse_ms,
-                       "other": ms - route_ms - states_ms - sparse_ms,
+                       "other": eager_ms - route_ms - states_ms - sparse_ms,
                        "route_overlaps_states": bool(a.route_stream)},
         "roofline": {
             "bound": "mfma",
