@@ -76,6 +76,7 @@ struct FwdWs {
   __bf16 *ht_hi, *ht_lo;
   __bf16 *hj_bf, *t_bf;
   uint32_t *bits, *flags;
+  int32_t *psize, *porder;  // the pair kernel's dispatch order (bf16 / fp32 mask product)
   uint8_t *q8, *k8, *v8;
   float *sq, *sk, *sv;
 };
@@ -105,6 +106,10 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
     f.t_bf = c.take<__bf16>(BH * d.nb * dd);
     f.bits = c.take<uint32_t>(BH * d.nb * sla::mask_words(d.nb));
     f.flags = c.take<uint32_t>(BH);
+  }
+  if (variant == 3) {
+    f.psize = c.take<int32_t>(sla::pair_order_ints(d));
+    f.porder = c.take<int32_t>(sla::pair_order_ints(d));
   }
   if (f8) {
     const size_t n = BH * d.N * d.d;
@@ -291,9 +296,12 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   else if (fp8)
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
-  else if (mode == SLA_LINEAR_MASK_PRODUCT)
-    e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream, flags,
-                                nullptr, out_rows);
+  else if (mode == SLA_LINEAR_MASK_PRODUCT) {
+    e = sla::launch_pair_order(d, w.bits, w.psize, w.porder, stream);
+    if (e == hipSuccess)
+      e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream, flags,
+                                  nullptr, out_rows, w.porder);
+  }
   else
     e = sla::launch_sparse(d, Q, K, V, idx, alpha, w.ht_hi, w.ht_lo, w.Z, w.zb, O,
                            mode == SLA_LINEAR_FUSED ? 1 : 0, stream);

@@ -63,7 +63,13 @@ hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream,
                               const uint32_t* flags = nullptr, const TrainRows* tr = nullptr,
-                              const int32_t* out_rows = nullptr);
+                              const int32_t* out_rows = nullptr, const int32_t* order = nullptr);
+// Dispatch order of the pair kernel (each XCD's workgroups by the size of their union of kept
+// blocks, largest first) from the complement bit rows: pair_order_ints(p) int32 each of
+// scratch (size) and output (order).
+int pair_order_ints(const Dims& p);
+hipError_t launch_pair_order(const Dims& p, const uint32_t* bits, int32_t* size, int32_t* order,
+                             hipStream_t stream);
 // Debug check of idx (validate.hip): *bad = the number of rows with an entry outside [0, n_b)
 // or not strictly ascending.
 hipError_t launch_validate_idx(const Dims& p, const int32_t* idx, int* bad, hipStream_t stream);

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
     float* __restrict__ O, int N, int nb, int topk, float c_log2,
     const uint32_t* __restrict__ flags, TrainRows tr, const int32_t* __restrict__ out_rows,
-    const float* __restrict__ msoft = nullptr) {
+    const float* __restrict__ msoft = nullptr, const int32_t* __restrict__ order = nullptr) {
   constexpr int NS = D / 16;  // MFMA k-steps over the head dim
   constexpr int NC = D / 32;  // 32-channel output tiles
   constexpr int TILE = TileLayout<D>::ELEMS;
@@ -118,7 +118,10 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   // branch is dropped); the grid's padding workgroups exit here, before any barrier
   const int npair = (nb + 1) / 2;
   int bh, pr;
-  if (!xcd_chunk_map(blockIdx.x, npair, &bh, &pr)) return;
+  // order (optional): the workgroup ids in dispatch order, each XCD's own items largest union
+  // first (pair_order_kernel), so that the shortest workgroups fill the end of the launch
+  const int wg = order ? order[blockIdx.x] : (int)blockIdx.x;
+  if (!xcd_chunk_map(wg, npair, &bh, &pr)) return;
   const int qb0 = 2 * pr;
   const bool has1 = qb0 + 1 < nb;  // an odd n_b leaves the last workgroup one block
   const int blk = wave / 2;        // this wavefront's query block: qb0 + blk
@@ -494,17 +497,18 @@ template <class T, int D>
 hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const float* alpha, const __bf16* t_bf,
                          const float* Z, const float* zb, float* O, hipStream_t stream,
-                         const uint32_t* flags, const TrainRows* tr, const int32_t* out_rows) {
+                         const uint32_t* flags, const TrainRows* tr, const int32_t* out_rows,
+                         const int32_t* order) {
   const int total = xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (tr)
     pair_kernel<T, D, true><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, flags, *tr, out_rows);
+        c_log2, flags, *tr, out_rows, nullptr, order);
   else
     pair_kernel<T, D, false><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, flags, TrainRows{}, out_rows);
+        c_log2, flags, TrainRows{}, out_rows, nullptr, order);
   return hipGetLastError();
 }
 
@@ -532,16 +536,76 @@ hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream,
                               const uint32_t* flags, const TrainRows* tr,
-                              const int32_t* out_rows) {
+                              const int32_t* out_rows, const int32_t* order) {
   if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, tr, out_rows);
+    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, tr, out_rows, order);
   if (tr) return hipErrorInvalidValue;  // the training outputs exist for bf16, d = 128 only
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows);
+    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows);
-  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows);
+    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order);
+  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order);
+}
+
+// The pair kernel's dispatch order: each XCD's items (the workgroup ids wg with wg % 8 == x),
+// within each head by the size of their union of kept blocks, largest first.
+//   pair_sizes_kernel  one thread per workgroup id: the union size of its two query blocks from
+//                      their complement bit rows (n_b - |unselected by both|), -1 for an id past
+//                      a short chunk (it exits at once, so it goes last).
+//   pair_order_kernel  one workgroup per XCD: its ids keep their head-by-head order (each
+//                      XCD's co-resident workgroups share a head's kept K/V in L2) and inside
+//                      each head's group go by size, largest first (a stable rank); the order
+//                      changes which workgroup runs when, never what one computes.
+__global__ __launch_bounds__(256) void pair_sizes_kernel(const uint32_t* __restrict__ bits, int nb, int nw,
+                                                         int topk, int npair, int total,
+                                                         int32_t* __restrict__ size) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  int bh, pr, sz = -1;
+  if (xcd_chunk_map(t, npair, &bh, &pr)) {
+    const int q0 = 2 * pr;
+    if (q0 + 1 < nb) {
+      const uint32_t* u0 = bits + ((size_t)bh * nb + q0) * nw;
+      int both = 0;
+      for (int w = 0; w < nw; ++w) both += __popc(u0[w] & u0[nw + w]);
+      sz = nb - both;
+    } else {
+      sz = topk;
+    }
+  }
+  size[t] = sz;
+}
+
+__global__ __launch_bounds__(256) void pair_order_kernel(const int32_t* __restrict__ size, int per_xcd,
+                                                         int smax, int32_t* __restrict__ order) {
+  // XCD x walks its ids head by head (the consecutive groups of smax ids, one head each, which
+  // share L2); inside each group the ids go by union size, largest first (stable rank)
+  const int x = blockIdx.x;
+  for (int k = threadIdx.x; k < per_xcd; k += 256) {
+    const int g0 = k - k % smax;
+    const int my = size[8 * k + x];
+    int rank = 0;
+    for (int j = g0; j < g0 + smax; ++j) {
+      const int o = size[8 * j + x];
+      rank += (o > my || (o == my && j < k)) ? 1 : 0;
+    }
+    order[8 * (g0 + rank) + x] = 8 * k + x;
+  }
+}
+
+int pair_order_ints(const Dims& p) { return xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2); }
+
+hipError_t launch_pair_order(const Dims& p, const uint32_t* bits, int32_t* size, int32_t* order,
+                             hipStream_t stream) {
+  if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
+  const int total = pair_order_ints(p);
+  pair_sizes_kernel<<<(total + 255) / 256, 256, 0, stream>>>(bits, p.nb, mask_words(p.nb), p.topk,
+                                                              (p.nb + 1) / 2, total, size);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  pair_order_kernel<<<8, 256, 0, stream>>>(size, total / 8, ((p.nb + 1) / 2 + 7) / 8, order);
+  return hipGetLastError();
 }
 
 }  // namespace sla
