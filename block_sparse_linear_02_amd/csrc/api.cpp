@@ -76,7 +76,7 @@ struct FwdWs {
   __bf16 *ht_hi, *ht_lo;
   __bf16 *hj_bf, *t_bf;
   uint32_t *bits, *flags;
-  int32_t *psize, *porder;  // the pair kernel's dispatch order (bf16 / fp32 mask product)
+  int32_t *psize, *porder, *pairs;  // the pair kernel's block pairs and dispatch order
   uint8_t *q8, *k8, *v8;
   float *sq, *sk, *sv;
 };
@@ -110,6 +110,7 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
   if (variant == 3) {
     f.psize = c.take<int32_t>(sla::pair_order_ints(d));
     f.porder = c.take<int32_t>(sla::pair_order_ints(d));
+    f.pairs = c.take<int32_t>(sla::pair_match_ints(d));
   }
   if (f8) {
     const size_t n = BH * d.N * d.d;
@@ -272,7 +273,9 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     if (e != hipSuccess) return hip_fail(e);
   }
   if (mode == SLA_LINEAR_MASK_PRODUCT) {
-    e = sla::launch_mask_bits(d, idx, w.bits, stream);  // every block unselected when topk == 0
+    // every block unselected when topk == 0; the bf16 / fp32 path also pairs its query blocks
+    e = fp8 ? sla::launch_mask_bits(d, idx, w.bits, stream)
+            : sla::launch_pair_match(d, idx, w.bits, w.pairs, w.psize, stream);
     if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.bits, w.t_bf, stream, flags);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -297,10 +300,10 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
   else if (mode == SLA_LINEAR_MASK_PRODUCT) {
-    e = sla::launch_pair_order(d, w.bits, w.psize, w.porder, stream);
+    e = sla::launch_pair_order(d, w.psize, w.porder, stream);
     if (e == hipSuccess)
       e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream, flags,
-                                  nullptr, out_rows, w.porder);
+                                  nullptr, out_rows, w.porder, w.pairs);
   }
   else
     e = sla::launch_sparse(d, Q, K, V, idx, alpha, w.ht_hi, w.ht_lo, w.Z, w.zb, O,

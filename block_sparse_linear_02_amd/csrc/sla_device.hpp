@@ -107,6 +107,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Maximum of an int over all 64 lanes, in every lane (all lanes active): DPP inside each row of
+// 16 lanes (swap within pairs, then within quads, then the half-row and row mirrors), then the
+// four rows' maxima read into scalars.
+__device__ __forceinline__ int wave_max_int(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
 // Order-preserving map of a float to uint32 (larger float -> larger key); -0 and +0 map to
 // the same key.
 __device__ __forceinline__ u32 float_key(float f) {

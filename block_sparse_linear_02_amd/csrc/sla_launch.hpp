@@ -59,17 +59,25 @@ struct TrainRows {
 // flags (optional): a kDropLinear head writes alpha O_s only, a kDropSparse head
 // (1 - alpha) O_l only.  tr (optional, bf16 with d = 128): also write the TrainRows.
 // out_rows (optional, [BH][N]): O row r goes to row out_rows[r] (TrainRows stay in place).
+// order (optional, launch_pair_order): workgroup ids in dispatch order.  pairs (optional,
+// launch_pair_match): the two query blocks of pair slot p, else 2p and 2p + 1.
 hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream,
                               const uint32_t* flags = nullptr, const TrainRows* tr = nullptr,
-                              const int32_t* out_rows = nullptr, const int32_t* order = nullptr);
+                              const int32_t* out_rows = nullptr, const int32_t* order = nullptr,
+                              const int32_t* pairs = nullptr);
 // Dispatch order of the pair kernel (each XCD's workgroups by the size of their union of kept
-// blocks, largest first) from the complement bit rows: pair_order_ints(p) int32 each of
-// scratch (size) and output (order).
+// blocks, largest first) from those sizes (launch_pair_match): pair_order_ints(p) int32 each
+// of size and order.
 int pair_order_ints(const Dims& p);
-hipError_t launch_pair_order(const Dims& p, const uint32_t* bits, int32_t* size, int32_t* order,
-                             hipStream_t stream);
+hipError_t launch_pair_order(const Dims& p, const int32_t* size, int32_t* order, hipStream_t stream);
+// Query blocks paired by the overlap of their kept sets, in windows of 32 (pairs [BH][npair][2]
+// int32, second id -1 for a block alone: pair_match_ints(p) int32), the pairs' union sizes per
+// workgroup id (what launch_pair_order ranks), and the complement bit rows (as launch_mask_bits).
+int pair_match_ints(const Dims& p);
+hipError_t launch_pair_match(const Dims& p, const int32_t* idx, uint32_t* bits, int32_t* pairs,
+                             int32_t* size, hipStream_t stream);
 // Debug check of idx (validate.hip): *bad = the number of rows with an entry outside [0, n_b)
 // or not strictly ascending.
 hipError_t launch_validate_idx(const Dims& p, const int32_t* idx, int* bad, hipStream_t stream);

@@ -241,5 +241,14 @@ __host__ __device__ __forceinline__ bool xcd_chunk_map(int wg, int per_head, int
   *item = x * q + (x < r ? x : r) + off;
   return off < q + (x < r ? 1 : 0);
 }
+// The inverse of xcd_chunk_map: the workgroup id that runs item `item` of head `head`.
+__host__ __device__ __forceinline__ int xcd_chunk_id(int head, int item, int per_head) {
+  const int q = per_head / 8, r = per_head % 8;
+  const int smax = q + (r > 0 ? 1 : 0);
+  const int big = r * (q + 1);  // the items of the r XCDs that take q + 1
+  const int x = item < big ? item / (q + 1) : r + (item - big) / q;
+  const int off = item - (x * q + (x < r ? x : r));
+  return 8 * (head * smax + off) + x;
+}
 
 }  // namespace sla

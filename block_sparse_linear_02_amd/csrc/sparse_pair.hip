@@ -7,11 +7,13 @@
 // (sparse branch renormalised over the kept blocks; O = alpha O_s + (1 - alpha) O_l); SALAD
 // section 2 (ReLU feature map of the linear branch, over the blocks the sparse branch leaves).
 //
-// One workgroup = query blocks 2p and 2p + 1 of one (batch, head).  Neighbouring query blocks
-// keep mostly the same key blocks, so the workgroup walks the ascending union of their two
-// index lists and stages each K_j, V_j tile into LDS once for both: every tile byte read from L2
-// serves up to 128 query rows instead of 64.  Wavefront w takes rows 32 (w % 2) .. + 31 of query
-// block 2p + w / 2 against all 64 keys of a tile, and skips the tiles its block did not keep
+// One workgroup = two query blocks of one (batch, head): 2p and 2p + 1, or (the mask-product
+// forward) the pair that pair_match_kernel below chose among nearby blocks for the most kept
+// key blocks in common.  Nearby query blocks keep mostly the same key blocks, so the workgroup
+// walks the ascending union of their two index lists and stages each K_j, V_j tile into LDS
+// once for both: every tile byte read from L2 serves up to 128 query rows instead of 64.
+// Wavefront w takes rows 32 (w % 2) .. + 31 of the pair's block w / 2 against all 64 keys of a
+// tile, and skips the tiles its block did not keep
 // (the result is exactly each block's own sparse branch).  Per tile: S^T = K_j Q^T
 // (v_mfma_f32_32x32x16_bf16, Q in registers as the B operand, so each lane owns one query row
 // and the row statistics stay in-lane), online softmax in the log2 domain (the running maximum
@@ -94,7 +96,8 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
     float* __restrict__ O, int N, int nb, int topk, float c_log2,
     const uint32_t* __restrict__ flags, TrainRows tr, const int32_t* __restrict__ out_rows,
-    const float* __restrict__ msoft = nullptr, const int32_t* __restrict__ order = nullptr) {
+    const float* __restrict__ msoft = nullptr, const int32_t* __restrict__ order = nullptr,
+    const int32_t* __restrict__ pairs = nullptr) {
   constexpr int NS = D / 16;  // MFMA k-steps over the head dim
   constexpr int NC = D / 32;  // 32-channel output tiles
   constexpr int TILE = TileLayout<D>::ELEMS;
@@ -122,9 +125,18 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   // first (pair_order_kernel), so that the shortest workgroups fill the end of the launch
   const int wg = order ? order[blockIdx.x] : (int)blockIdx.x;
   if (!xcd_chunk_map(wg, npair, &bh, &pr)) return;
-  const int qb0 = 2 * pr;
-  const bool has1 = qb0 + 1 < nb;  // an odd n_b leaves the last workgroup one block
-  const int blk = wave / 2;        // this wavefront's query block: qb0 + blk
+  // the two query blocks: 2p and 2p + 1, or (pairs) the ones matched by overlap of their kept
+  // sets; an odd n_b (or an odd matching window) leaves one workgroup one block, whose absent
+  // second block is given the id n_b (all its rows lie past N)
+  int qa = 2 * pr, qbv = 2 * pr + 1;
+  if (pairs) {
+    qa = pairs[2 * ((size_t)bh * npair + pr)];
+    qbv = pairs[2 * ((size_t)bh * npair + pr) + 1];
+  }
+  const bool has1 = pairs ? qbv >= 0 : qbv < nb;
+  const int qb1 = has1 ? qbv : nb;
+  auto qsel = [&](int b) { return b ? qb1 : qa; };
+  const int blk = wave / 2;  // this wavefront's query block: qsel(blk)
   const size_t hoff = (size_t)bh * N * D;
   const int nw = (nb + 31) / 32;
 
@@ -138,7 +150,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   for (int t = tid; !SOFT && t < 2 * topk; t += kPairThreads) {
     const int b = t / topk;
     if (b == 0 || has1) {
-      const int j = idx[((size_t)bh * nb + qb0 + b) * topk + t % topk];
+      const int j = idx[((size_t)bh * nb + qsel(b)) * topk + t % topk];
       atomicOr(&bm[b][j / 32], 1u << (j % 32));
     }
   }
@@ -193,7 +205,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const T* vsrc = V + hoff + (size_t)j * kBlock * D;
     if (z_lane) z_in = zb[((size_t)bh * nb + j) * D + tid % D];
     if constexpr (SOFT) {
-      if (z_lane) z_in *= msoft[((size_t)bh * nb + min(qb0 + zb_blk, nb - 1)) * nb + j];
+      if (z_lane) z_in *= msoft[((size_t)bh * nb + min(qsel(zb_blk), nb - 1)) * nb + j];
     }
     f_next = e & 3;
     nv_next = nv;
@@ -259,7 +271,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   // channel 16s + 8g + jj (rows past N, and the absent second block of an odd n_b, read a
   // clamped row and are zeroed)
   const int m = 32 * (wave % 2) + lane % 32;
-  const int row = (qb0 + blk) * kBlock + m;
+  const int row = qsel(blk) * kBlock + m;
   const bool row_ok = row < N;
   bf16x8 q[NS], ql[SPLIT ? NS : 1];
   {
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     if (t + 1 < nu) stage(t + 1, std::integral_constant<int, 1 - BUF>{});
     if ((f_cur >> blk) & 1) {  // this wavefront's block kept the tile (wavefront-uniform)
       // SOFT: this wavefront's block's weight of key block t (the union is every block in order)
-      const float wgt = SOFT ? msoft[((size_t)bh * nb + min(qb0 + blk, nb - 1)) * nb + t] : 1.f;
+      const float wgt = SOFT ? msoft[((size_t)bh * nb + min(qsel(blk), nb - 1)) * nb + t] : 1.f;
       const __bf16* Ks = buf(BUFC);
       const __bf16* Vs = Ks + TILE;
       // K operands of both 32-key halves, issued together ahead of their MFMAs
@@ -406,7 +418,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
 
   // a dropped sparse branch staged no tiles, so the kept blocks' z_j are summed here
   if ((fl & kDropSparse) && lin && z_lane && (zb_blk == 0 || has1)) {
-    const int32_t* il = idx + ((size_t)bh * nb + qb0 + zb_blk) * topk;
+    const int32_t* il = idx + ((size_t)bh * nb + qsel(zb_blk)) * topk;
     for (int t = 0; t < topk; ++t) zacc += zb[((size_t)bh * nb + il[t]) * D + tid % D];
   }
   // ---- epilogue: T_i^T [c][c'] of block b into tile buffer b (both free since the last
@@ -414,7 +426,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   if (lin) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const __bf16* th = t_g + ((size_t)bh * nb + min(qb0 + b, nb - 1)) * D * D;
+      const __bf16* th = t_g + ((size_t)bh * nb + min(qsel(b), nb - 1)) * D * D;
       __bf16* dst = b ? lb1 : lb0;
 #pragma unroll
       for (int half = 0; half < D / kBlock; ++half) {
@@ -498,17 +510,17 @@ hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void
                          const int32_t* idx, const float* alpha, const __bf16* t_bf,
                          const float* Z, const float* zb, float* O, hipStream_t stream,
                          const uint32_t* flags, const TrainRows* tr, const int32_t* out_rows,
-                         const int32_t* order) {
+                         const int32_t* order, const int32_t* pairs) {
   const int total = xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (tr)
     pair_kernel<T, D, true><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, flags, *tr, out_rows, nullptr, order);
+        c_log2, flags, *tr, out_rows, nullptr, order, pairs);
   else
     pair_kernel<T, D, false><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, flags, TrainRows{}, out_rows, nullptr, order);
+        c_log2, flags, TrainRows{}, out_rows, nullptr, order, pairs);
   return hipGetLastError();
 }
 
@@ -536,75 +548,180 @@ hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const
                               const int32_t* idx, const float* alpha, const __bf16* t_bf,
                               const float* Z, const float* zb, float* O, hipStream_t stream,
                               const uint32_t* flags, const TrainRows* tr,
-                              const int32_t* out_rows, const int32_t* order) {
+                              const int32_t* out_rows, const int32_t* order,
+                              const int32_t* pairs) {
   if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, tr, out_rows, order);
+    return launch_pair_t<__bf16, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, tr, out_rows, order, pairs);
   if (tr) return hipErrorInvalidValue;  // the training outputs exist for bf16, d = 128 only
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order);
+    return launch_pair_t<__bf16, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order, pairs);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order);
-  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order);
+    return launch_pair_t<float, 128>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order, pairs);
+  return launch_pair_t<float, 64>(p, Q, K, V, idx, alpha, t_bf, Z, zb, O, stream, flags, nullptr, out_rows, order, pairs);
 }
 
 // The pair kernel's dispatch order: each XCD's items (the workgroup ids wg with wg % 8 == x),
-// within each head by the size of their union of kept blocks, largest first.
-//   pair_sizes_kernel  one thread per workgroup id: the union size of its two query blocks from
-//                      their complement bit rows (n_b - |unselected by both|), -1 for an id past
-//                      a short chunk (it exits at once, so it goes last).
-//   pair_order_kernel  one workgroup per XCD: its ids keep their head-by-head order (each
-//                      XCD's co-resident workgroups share a head's kept K/V in L2) and inside
-//                      each head's group go by size, largest first (a stable rank); the order
-//                      changes which workgroup runs when, never what one computes.
-__global__ __launch_bounds__(256) void pair_sizes_kernel(const uint32_t* __restrict__ bits, int nb, int nw,
-                                                         int topk, int npair, int total,
-                                                         int32_t* __restrict__ size) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;
-  int bh, pr, sz = -1;
-  if (xcd_chunk_map(t, npair, &bh, &pr)) {
-    const int q0 = 2 * pr;
-    if (q0 + 1 < nb) {
-      const uint32_t* u0 = bits + ((size_t)bh * nb + q0) * nw;
-      int both = 0;
-      for (int w = 0; w < nw; ++w) both += __popc(u0[w] & u0[nw + w]);
-      sz = nb - both;
-    } else {
-      sz = topk;
-    }
-  }
-  size[t] = sz;
-}
+// within each head by the size of their union of kept blocks (from pair_match_kernel; -1 for
+// an id past a short chunk, which exits at once and so goes last), largest first.
+//   pair_order_kernel  one workgroup per (XCD, head): that XCD's ids of the head, staged in LDS
+//                      and ranked by size, largest first (a stable rank); the order changes
+//                      which workgroup runs when, never what one computes.
+constexpr int kOrderMax = 128;  // ids per (XCD, head) group: ceil(ceil(n_b / 2) / 8) <= 128
 
-__global__ __launch_bounds__(256) void pair_order_kernel(const int32_t* __restrict__ size, int per_xcd,
-                                                         int smax, int32_t* __restrict__ order) {
-  // XCD x walks its ids head by head (the consecutive groups of smax ids, one head each, which
-  // share L2); inside each group the ids go by union size, largest first (stable rank)
-  const int x = blockIdx.x;
-  for (int k = threadIdx.x; k < per_xcd; k += 256) {
-    const int g0 = k - k % smax;
-    const int my = size[8 * k + x];
-    int rank = 0;
-    for (int j = g0; j < g0 + smax; ++j) {
-      const int o = size[8 * j + x];
-      rank += (o > my || (o == my && j < k)) ? 1 : 0;
-    }
-    order[8 * (g0 + rank) + x] = 8 * k + x;
+__global__ __launch_bounds__(kOrderMax) void pair_order_kernel(const int32_t* __restrict__ size, int smax,
+                                                              int32_t* __restrict__ order) {
+  // group (x, head): XCD x's ids of one head, 8 (g0 + t) + x for t < smax, which keep their
+  // head-by-head place (co-resident workgroups of an XCD share a head's kept K/V in L2) and
+  // inside the group go by size, largest first (a stable rank)
+  __shared__ int sz[kOrderMax];
+  const int x = blockIdx.x, g0 = blockIdx.y * smax, t = threadIdx.x;
+  if (t < smax) sz[t] = size[8 * (g0 + t) + x];
+  __syncthreads();
+  if (t >= smax) return;
+  const int my = sz[t];
+  int rank = 0;
+  for (int j = 0; j < smax; ++j) {
+    const int o = sz[j];
+    rank += (o > my || (o == my && j < t)) ? 1 : 0;
   }
+  order[8 * (g0 + rank) + x] = 8 * (g0 + t) + x;
 }
 
 int pair_order_ints(const Dims& p) { return xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2); }
 
-hipError_t launch_pair_order(const Dims& p, const uint32_t* bits, int32_t* size, int32_t* order,
-                             hipStream_t stream) {
+// Query blocks paired by the overlap of their kept sets.  Windows of kMatchWin consecutive query
+// blocks (neighbouring blocks are the ones that share kept blocks, and a window's pairs stay
+// next to each other in the launch, sharing L2); inside a window, greedily, the two unpaired
+// blocks with the most kept blocks in common (ties: the lowest pair of indices), until at most
+// one is left (an odd last window: that block goes alone, second id -1).  Window w fills pair
+// slots 16 w ..; the union a pair walks is |K_a| + |K_b| - |K_a & K_b|, so the most shared
+// blocks make the shortest walks.
+//   pair_match_kernel  one workgroup per (window, head): the window's kept bit rows, set from
+//                      the index lists (row pitch odd, so that lanes reading one word of
+//                      different rows hit different banks), written out as their complement
+//                      for the linear branch (as mask_bits_kernel), and their pairwise
+//                      overlaps in LDS; then wavefront 0 picks the pairs, one max-reduction
+//                      over its lanes per pair, and writes each pair's union size where pair_order_kernel
+//                      reads it (the workgroup id xcd_chunk_id gives the pair's slot; window
+//                      0 also marks the head's padding ids -1).
+constexpr int kMatchWin = 32;
+constexpr int kMatchThreads = 256;
+constexpr int kMatchPitch = kPairMaxWords + 1;
+
+__global__ __launch_bounds__(kMatchThreads) void pair_match_kernel(const int32_t* __restrict__ idx, int nb,
+                                                                  int nw, int topk, int npair,
+                                                                  uint32_t* __restrict__ bits,
+                                                                  int32_t* __restrict__ pairs,
+                                                                  int32_t* __restrict__ size) {
+  __shared__ uint32_t kb[kMatchWin * kMatchPitch];
+  __shared__ int ov[kMatchWin][kMatchWin + 1];  // ov[a][b], a <= b: |K_a & K_b| (a = b: |K_a|)
+  const int win = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int b0 = win * kMatchWin, nblk = min(kMatchWin, nb - b0);
+  for (int e = tid; e < nblk * kMatchPitch; e += kMatchThreads) kb[e] = 0u;
+  __syncthreads();
+  // the window's index lists, eight loads in flight per thread before their LDS bit sets
+  const int32_t* rows = idx + ((size_t)bh * nb + b0) * topk;
+  const int nent = nblk * topk;
+  for (int e0 = tid; e0 < nent; e0 += 8 * kMatchThreads) {
+    int jv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) jv[u] = e0 + u * kMatchThreads < nent ? rows[e0 + u * kMatchThreads] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * kMatchThreads, j = jv[u];
+      if (j >= 0 && j < nb) atomicOr(&kb[(e / topk) * kMatchPitch + j / 32], 1u << (j % 32));
+    }
+  }
+  __syncthreads();
+  // the complement rows (every block j < n_b not kept) for the linear branch's mask product
+  for (int e = tid; e < nblk * nw; e += kMatchThreads) {
+    const int i = e / nw, w = e % nw;
+    const int valid = min(32, nb - 32 * w);
+    const uint32_t all = valid == 32 ? 0xffffffffu : (1u << valid) - 1u;
+    bits[((size_t)bh * nb + b0 + i) * nw + w] = all & ~kb[i * kMatchPitch + w];
+  }
+  for (int e = tid; e < kMatchWin * kMatchWin; e += kMatchThreads) {
+    const int a = e / kMatchWin, b = e % kMatchWin;
+    if (a <= b && b < nblk) {
+      int o = 0;
+#pragma unroll 4
+      for (int w = 0; w < nw; ++w) o += __popc(kb[a * kMatchPitch + w] & kb[b * kMatchPitch + w]);
+      ov[a][b] = o;
+    }
+  }
+  __syncthreads();
+  if (tid >= kWave) return;
+  // lane (a, h) = (tid % 32, tid / 32) holds the half h of row a of the (symmetric) overlap
+  // matrix in registers, partners b = 16 h + u; each round every lane of an unpaired a offers its
+  // best unpaired partner as one key (overlap, then the lower index pair a' * 32 + b', a' < b',
+  // first), and the wavefront's maximum key is the pair taken.  Lane r keeps pair r and all
+  // pairs are written after the last round.
+  constexpr int kHalf = kMatchWin / 2;
+  const int a = tid % kMatchWin, h = tid / kMatchWin;
+  int row[kHalf];
+#pragma unroll
+  for (int u = 0; u < kHalf; ++u) {
+    const int b = kHalf * h + u;
+    const int v = ov[min(a, b)][max(a, b)];
+    row[u] = (a < nblk && b < nblk) ? v : 0;
+  }
+  uint32_t used = 0;  // wavefront-uniform
+  int my_pa = 0, my_pb = 0, my_ov = 0;
+  const int npw = nblk / 2;
+  for (int r = 0; r < npw; ++r) {
+    int key = -1;
+    if (a < nblk && !((used >> a) & 1u)) {
+#pragma unroll
+      for (int u = 0; u < kHalf; ++u) {
+        const int b = kHalf * h + u;
+        if (b != a && b < nblk && !((used >> b) & 1u)) {
+          const int pid = a < b ? a * kMatchWin + b : b * kMatchWin + a;
+          key = max(key, (row[u] << 10) | (1023 - pid));
+        }
+      }
+    }
+    key = wave_max_int(key);
+    const int pid = 1023 - (key & 1023), pa = pid / kMatchWin, pb = pid % kMatchWin;
+    used |= (1u << pa) | (1u << pb);
+    if (tid == r) {
+      my_pa = pa;
+      my_pb = pb;
+      my_ov = key >> 10;
+    }
+  }
+  int32_t* out = pairs + 2 * ((size_t)bh * npair + (size_t)win * kHalf);
+  const int slot0 = win * kHalf;
+  if (tid < npw) {
+    out[2 * tid] = b0 + my_pa;
+    out[2 * tid + 1] = b0 + my_pb;
+    size[xcd_chunk_id(bh, slot0 + tid, npair)] = ov[my_pa][my_pa] + ov[my_pb][my_pb] - my_ov;
+  } else if ((nblk & 1) && tid == npw) {  // the one block left (an odd window has nblk <= 31)
+    const int left = __builtin_ctz(~used);
+    out[2 * tid] = b0 + left;
+    out[2 * tid + 1] = -1;
+    size[xcd_chunk_id(bh, slot0 + tid, npair)] = ov[left][left];
+  }
+  // the head's padding ids (XCDs x >= npair % 8 hold one item fewer than the slots per head)
+  const int q = npair / 8, rem = npair % 8;
+  if (win == 0 && rem > 0 && tid >= rem && tid < 8) size[8 * (bh * (q + 1) + q) + tid] = -1;
+}
+
+int pair_match_ints(const Dims& p) { return 2 * p.B * p.H * ((p.nb + 1) / 2); }
+
+hipError_t launch_pair_match(const Dims& p, const int32_t* idx, uint32_t* bits, int32_t* pairs,
+                             int32_t* size, hipStream_t stream) {
   if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
-  const int total = pair_order_ints(p);
-  pair_sizes_kernel<<<(total + 255) / 256, 256, 0, stream>>>(bits, p.nb, mask_words(p.nb), p.topk,
-                                                              (p.nb + 1) / 2, total, size);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  pair_order_kernel<<<8, 256, 0, stream>>>(size, total / 8, ((p.nb + 1) / 2 + 7) / 8, order);
+  const dim3 grid((p.nb + kMatchWin - 1) / kMatchWin, p.B * p.H);
+  pair_match_kernel<<<grid, kMatchThreads, 0, stream>>>(idx, p.nb, mask_words(p.nb), p.topk, (p.nb + 1) / 2,
+                                                        bits, pairs, size);
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_order(const Dims& p, const int32_t* size, int32_t* order, hipStream_t stream) {
+  const int smax = ((p.nb + 1) / 2 + 7) / 8;
+  if (smax > kOrderMax) return hipErrorInvalidValue;
+  pair_order_kernel<<<dim3(8, p.B * p.H), kOrderMax, 0, stream>>>(size, smax, order);
   return hipGetLastError();
 }
 
