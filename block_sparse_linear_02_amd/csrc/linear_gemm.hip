@@ -121,34 +121,48 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
   const uint32_t* brow = bits + (size_t)bh * nb * nw;
   const int nstage = (nb + kGemmK - 1) / kGemmK;
 
-  // stage s: rows j = kGemmK s + 0 .. kGemmK - 1 (clamped to n_b - 1: their mask bits are 0),
-  // 256 bytes each (chunks 0..7 from the first slice, 8..15 from the second); each 1 KB direct
-  // load covers 4 rows, wavefront w loads rows 32 w .. 32 w + 31
+  // stage s: rows j = kGemmK s + 0 .. kGemmK - 1, 256 bytes each (chunks 0..7 from the first
+  // slice, 8..15 from the second); each 1 KB direct load covers 4 rows, wavefront w loads rows
+  // 32 w .. 32 w + 31.  The loads go through a buffer resource over the two slices: the lane's
+  // offset is fixed (row 32 w + lane / 16 of its chunk's slice; the swizzle depends on the row
+  // mod 4 only), the stage and the 4-row step are scalar offsets.  Rows past n_b read the
+  // second slice's first rows or, past its end, zero: finite values whose mask bits are 0.
+  const __amdgpu_buffer_rsrc_t hrs = make_rsrc(hh, (uint32_t)(2 * nb * kSlice * sizeof(__bf16)));
+  uint32_t hvoff;
+  {
+    const int r = (kGemmK / 4) * w + lane / 16;
+    const int chunk = (lane % 16) ^ (4 * (r & 3));
+    hvoff = (uint32_t)((((chunk / 8) * nb + r) * kSlice + (chunk % 8) * 8) * sizeof(__bf16));
+  }
   auto stage = [&](int s, auto BUFC) {
     __bf16* dst = buf(BUFC);
 #pragma unroll
-    for (int u = 0; u < kGemmK / 16; ++u) {
-      const int r0 = (kGemmK / 4) * w + 4 * u;
-      const int r = r0 + lane / 16;
-      const int j = min(kGemmK * s + r, nb - 1);
-      const int chunk = (lane % 16) ^ (4 * (r & 3));
-      load_lds16(hh + ((size_t)(chunk / 8) * nb + j) * kSlice + (chunk % 8) * 8, dst + r0 * kGemmN);
-    }
+    for (int u = 0; u < kGemmK / 16; ++u)
+      load_lds16_buf(hrs, hvoff, (uint32_t)((kGemmK * s + 4 * u) * kSlice * sizeof(__bf16)),
+                     dst + ((kGemmK / 4) * w + 4 * u) * kGemmN);
   };
-  // mask words of this lane's query-block columns (i0 + 32 ct + lane % 32) for stage s; words
-  // past the row are read clamped and zeroed when used (no branch around the loads and no use
-  // right after them: either makes the compiler wait for every outstanding load, the stage
-  // prefetch included, on the spot)
+  // mask words of this lane's query-block columns (i0 + 32 ct + lane % 32, clamped to n_b - 1)
+  // for stage s, through a buffer resource over the head's bit rows: words past a row read the
+  // next row's (or, past the last, zero) and are zeroed when used (no branch around the loads
+  // and no use right after them: either makes the compiler wait for every outstanding load, the
+  // stage prefetch included, on the spot)
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(brow, (uint32_t)((size_t)nb * nw * sizeof(uint32_t)));
+  uint32_t mvoff[kGemmCT];
+#pragma unroll
+  for (int ct = 0; ct < kGemmCT; ++ct)
+    mvoff[ct] = (uint32_t)(min(i0 + 32 * ct + lane % 32, nb - 1) * nw * sizeof(uint32_t));
   uint32_t mw[kGemmCT][kGemmKW];
   auto mask_words = [&](int s) {
 #pragma unroll
-    for (int ct = 0; ct < kGemmCT; ++ct) {
-      const int i = min(i0 + 32 * ct + lane % 32, nb - 1);
+    for (int ct = 0; ct < kGemmCT; ++ct)
 #pragma unroll
       for (int h = 0; h < kGemmKW; ++h)
-        mw[ct][h] = brow[(size_t)i * nw + min(kGemmKW * s + h, nw - 1)];
-    }
+        mw[ct][h] = __builtin_amdgcn_raw_buffer_load_b32(brs, (int)(mvoff[ct] + 4 * h),
+                                                         (int)(kGemmKW * s * sizeof(uint32_t)), 0);
   };
+  // this wavefront's column tiles with a query block < n_b (wavefront-uniform): the others
+  // issue no MFMA
+  const int ncv = min(kGemmCT, max(0, (nb - i0 + 31) / 32));
 
   f32x16 acc[kGemmRT][kGemmCT];  // [state row tile][query-block column tile]
 #pragma unroll
@@ -193,31 +207,46 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
       if constexpr (!WT) mask_words(s + 1);
     }
     const __bf16* tile = buf(BUFC);
+    // KEDGE: the stage holds fewer than kGemmK key blocks (steps of 16 past n_b are skipped);
+    // NCT: the wavefront's column tiles with a query block < n_b (the others issue no MFMA)
+    auto compute = [&](auto KEDGEC, auto NCTC) {
+      constexpr bool KEDGE = decltype(KEDGEC)::value;
+      constexpr int NCT = decltype(NCTC)::value;
+      const int rem = nb - kGemmK * s;
 #pragma unroll
-    for (int ks = 0; ks < kGemmK / 16; ++ks) {
-      // mask operand: bits 16 ks + 8 g .. + 7 of the stage, i.e. of word ks / 2 (or, WT, the
-      // weights of key blocks kGemmK s + 16 ks + 8 g .. + 7)
-      bf16x8 bm[kGemmCT];
+      for (int ks = 0; ks < kGemmK / 16; ++ks) {
+        if (KEDGE && 16 * ks >= rem) break;
+        // mask operand: bits 16 ks + 8 g .. + 7 of the stage, i.e. of word ks / 2 (or, WT, the
+        // weights of key blocks kGemmK s + 16 ks + 8 g .. + 7)
+        bf16x8 bm[NCT];
 #pragma unroll
-      for (int ct = 0; ct < kGemmCT; ++ct)
-      {
-        if constexpr (WT) {
-          const int i = min(i0 + 32 * ct + lane % 32, nb - 1);
-          bm[ct] = *reinterpret_cast<const bf16x8*>(wt + ((size_t)bh * nb + i) * wpitch + kGemmK * s + 16 * ks + 8 * g);
-        } else {
-          const u32 byte = (cur[ct][ks / 2] >> (16 * (ks % 2) + 8 * g)) & 0xffu;
-          const bf16x4 lo = nib[byte & 15u], hi = nib[byte >> 4];
-          bm[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int ct = 0; ct < NCT; ++ct) {
+          if constexpr (WT) {
+            const int i = min(i0 + 32 * ct + lane % 32, nb - 1);
+            bm[ct] = *reinterpret_cast<const bf16x8*>(wt + ((size_t)bh * nb + i) * wpitch + kGemmK * s + 16 * ks + 8 * g);
+          } else {
+            const u32 byte = (cur[ct][ks / 2] >> (16 * (ks % 2) + 8 * g)) & 0xffu;
+            const bf16x4 lo = nib[byte & 15u], hi = nib[byte >> 4];
+            bm[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
         }
+        bf16x8 ah[kGemmRT];
+#pragma unroll
+        for (int a = 0; a < kGemmRT; ++a) ah[a] = tr_a(tile, ks, a);
+#pragma unroll
+        for (int a = 0; a < kGemmRT; ++a)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) acc[a][ct] = mfma32(ah[a], bm[ct], acc[a][ct]);
       }
-      bf16x8 ah[kGemmRT];
-#pragma unroll
-      for (int a = 0; a < kGemmRT; ++a) ah[a] = tr_a(tile, ks, a);
-#pragma unroll
-      for (int a = 0; a < kGemmRT; ++a)
-#pragma unroll
-        for (int ct = 0; ct < kGemmCT; ++ct) acc[a][ct] = mfma32(ah[a], bm[ct], acc[a][ct]);
-    }
+    };
+    static_assert(kGemmCT == 2, "column-tile dispatch below");
+    const bool kfull = kGemmK * (s + 1) <= nb;
+    if (ncv == kGemmCT && kfull)
+      compute(std::false_type{}, std::integral_constant<int, 2>{});
+    else if (ncv == kGemmCT)
+      compute(std::true_type{}, std::integral_constant<int, 2>{});
+    else if (ncv == 1)
+      compute(std::true_type{}, std::integral_constant<int, 1>{});
     wait_vmem();
     __syncthreads();
   };
