@@ -124,9 +124,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
   // stage s: rows j = kGemmK s + 0 .. kGemmK - 1, 256 bytes each (chunks 0..7 from the first
   // slice, 8..15 from the second); each 1 KB direct load covers 4 rows, wavefront w loads rows
   // 32 w .. 32 w + 31.  The loads go through a buffer resource over the two slices: the lane's
-  // offset is fixed (row 32 w + lane / 16 of its chunk's slice; the swizzle depends on the row
-  // mod 4 only), the stage and the 4-row step are scalar offsets.  Rows past n_b read the
-  // second slice's first rows or, past its end, zero: finite values whose mask bits are 0.
+  // offset is row 32 w + lane / 16 of its chunk's slice (the swizzle depends on the row mod 4
+  // only) plus the stage's rows, the 4-row step an immediate offset; the whole offset is in the
+  // vector and immediate parts, which the range check covers (the scalar offset is not
+  // checked).  Rows past n_b read the second slice's first rows or, past its end, zero: finite
+  // values whose mask bits are 0.
   const __amdgpu_buffer_rsrc_t hrs = make_rsrc(hh, (uint32_t)(2 * nb * kSlice * sizeof(__bf16)));
   uint32_t hvoff;
   {
@@ -136,14 +138,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
   }
   auto stage = [&](int s, auto BUFC) {
     __bf16* dst = buf(BUFC);
+    const uint32_t vs = hvoff + (uint32_t)(kGemmK * s * kSlice * sizeof(__bf16));
 #pragma unroll
     for (int u = 0; u < kGemmK / 16; ++u)
-      load_lds16_buf(hrs, hvoff, (uint32_t)((kGemmK * s + 4 * u) * kSlice * sizeof(__bf16)),
+      load_lds16_buf(hrs, vs + (uint32_t)(4 * u * kSlice * sizeof(__bf16)), 0u,
                      dst + ((kGemmK / 4) * w + 4 * u) * kGemmN);
   };
   // mask words of this lane's query-block columns (i0 + 32 ct + lane % 32, clamped to n_b - 1)
-  // for stage s, through a buffer resource over the head's bit rows: words past a row read the
-  // next row's (or, past the last, zero) and are zeroed when used (no branch around the loads
+  // for stage s, through a buffer resource over the head's bit rows (the stage's word offset in
+  // the range-checked vector offset): words past a row read the next row's (or, past the last,
+  // zero) and are zeroed when used (no branch around the loads
   // and no use right after them: either makes the compiler wait for every outstanding load, the
   // stage prefetch included, on the spot)
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(brow, (uint32_t)((size_t)nb * nw * sizeof(uint32_t)));
@@ -157,8 +161,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void tsel_kernel(
     for (int ct = 0; ct < kGemmCT; ++ct)
 #pragma unroll
       for (int h = 0; h < kGemmKW; ++h)
-        mw[ct][h] = __builtin_amdgcn_raw_buffer_load_b32(brs, (int)(mvoff[ct] + 4 * h),
-                                                         (int)(kGemmKW * s * sizeof(uint32_t)), 0);
+        mw[ct][h] = __builtin_amdgcn_raw_buffer_load_b32(
+            brs, (int)(mvoff[ct] + (kGemmKW * s + h) * sizeof(uint32_t)), 0, 0);
   };
   // this wavefront's column tiles with a query block < n_b (wavefront-uniform): the others
   // issue no MFMA

@@ -113,9 +113,13 @@ __device__ __forceinline__ void load_tile_direct(const __bf16* src, __bf16* tile
   }
 }
 
-// load_tile_direct through a buffer resource: the tile starts `soff` bytes into the resource
-// (wavefront-uniform), each lane's offset inside it is lane_voff(tid).  Rows past the
-// resource's end read as zero.
+// load_tile_direct through a buffer resource: the tile starts `toff` bytes into the resource
+// (wavefront-uniform), each lane's offset inside it is lane_voff(tid).  The buffer range check
+// covers the vector and immediate offsets only, not the scalar one: a full tile (every row
+// inside the resource) takes the tile and row-group offsets as scalars, no per-lane
+// arithmetic; a tile that crosses the resource's end (`crosses`, wavefront-uniform: the short
+// last block of a sequence) puts them in the vector offset, so its rows past the end read as
+// zero and no read leaves the resource.
 template <int THREADS>
 __device__ __forceinline__ uint32_t tile_lane_voff(int tid) {
   constexpr int NW = THREADS / 64;
@@ -125,14 +129,22 @@ __device__ __forceinline__ uint32_t tile_lane_voff(int tid) {
   return (uint32_t)(((lane / 16) * 128 + ((lane % 16) ^ f) * 8) * 2);
 }
 template <int THREADS>
-__device__ __forceinline__ void load_tile_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
-                                              __bf16* tile, int tid) {
+__device__ __forceinline__ void load_tile_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t toff,
+                                              __bf16* tile, int tid, bool crosses) {
   constexpr int NW = THREADS / 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  if (crosses) {
 #pragma unroll
-  for (int u = 0; u < 16 / NW; ++u) {
-    const int r0 = 4 * (NW * u + w);
-    load_lds16_buf(rsrc, voff, soff + (uint32_t)r0 * 256u, tile + r0 * 128);
+    for (int u = 0; u < 16 / NW; ++u) {
+      const int r0 = 4 * (NW * u + w);
+      load_lds16_buf(rsrc, voff + toff + (uint32_t)r0 * 256u, 0u, tile + r0 * 128);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16 / NW; ++u) {
+      const int r0 = 4 * (NW * u + w);
+      load_lds16_buf(rsrc, voff, toff + (uint32_t)r0 * 256u, tile + r0 * 128);
+    }
   }
 }
 

@@ -164,9 +164,9 @@ __global__ __launch_bounds__(256, 2) void soft_dm_sparse_kernel(
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, (uint32_t)((size_t)N * D * 2));
   const uint32_t lane_voff = tile_lane_voff<256>(tid);
   auto stage = [&](int j, int buf) {
-    const uint32_t soff = (uint32_t)j * (uint32_t)(TILE * 2);
-    load_tile_buf<256>(rk, lane_voff, soff, buf ? kb1 : kb0, tid);
-    load_tile_buf<256>(rv, lane_voff, soff, buf ? vb1 : vb0, tid);
+    const uint32_t toff = (uint32_t)j * (uint32_t)(TILE * 2);
+    load_tile_buf<256>(rk, lane_voff, toff, buf ? kb1 : kb0, tid, (j + 1) * kBlock > N);
+    load_tile_buf<256>(rv, lane_voff, toff, buf ? vb1 : vb0, tid, (j + 1) * kBlock > N);
   };
   // this wavefront's 32 query rows (B operands) and keys 32 (w / 2) .. + 31 of every tile
   const int row = i * kBlock + 32 * (w % 2) + lane % 32;

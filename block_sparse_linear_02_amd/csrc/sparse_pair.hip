@@ -23,7 +23,9 @@
 // the buffer being filled by direct-to-LDS loads from the one being read.  bf16 tiles with
 // d = 128 come through per-head buffer resources (buffer_load_dwordx4 ... lds): the tile offset
 // is a scalar register and each lane's offset a fixed VGPR, so staging a tile costs no per-lane
-// address arithmetic (a head spans at most 2048 x 64 x 128 x 2 bytes, inside the 32-bit range).
+// address arithmetic (a head spans at most 2048 x 64 x 128 x 2 bytes, inside the 32-bit range);
+// the short last tile of a sequence takes its offsets in the range-checked vector part, so it
+// reads zeros past N, never past the tensor.
 // Epilogue: T_i^T (bf16, [c][c']) of each block is loaded into a tile buffer, zeta_i = Z -
 // sum_kept z_j; each wavefront computes num = relu(Q) T_i by MFMA, den = relu(q) . zeta_i, and
 // O = alpha O_s / l + (1 - alpha) num / den (the linear part is 0 when nothing is unselected or
@@ -186,7 +188,8 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   // tid < D keep the sum over the first block's kept tiles, threads D .. 2D - 1 the second's.
   constexpr bool DIRECT = sizeof(T) == 2 && D == 128;
   // DIRECT tiles come through per-head buffer resources: the tile offset is a scalar, each
-  // lane's offset inside a tile a fixed register, and rows past N read as zero
+  // lane's offset inside a tile a fixed register, and the short last tile's rows past N read as
+  // zero
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + hoff, (uint32_t)((size_t)N * D * sizeof(T)));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + hoff, (uint32_t)((size_t)N * D * sizeof(T)));
   const uint32_t lane_voff = DIRECT ? tile_lane_voff<kPairThreads>(tid) : 0u;
@@ -212,9 +215,9 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     if constexpr (DIRECT) {
       // a short tile (the last block of the sequence) reads zeros past N, and its tail rows are
       // zeroed again after the loads land (zero_tail), so no register path sits in the loop
-      const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(j) * (uint32_t)(kBlock * D * sizeof(T));
-      load_tile_buf<kPairThreads>(rk, lane_voff, soff, dst, tid);
-      load_tile_buf<kPairThreads>(rv, lane_voff, soff, dst + TILE, tid);
+      const uint32_t toff = (uint32_t)__builtin_amdgcn_readfirstlane(j) * (uint32_t)(kBlock * D * sizeof(T));
+      load_tile_buf<kPairThreads>(rk, lane_voff, toff, dst, tid, nv < kBlock);
+      load_tile_buf<kPairThreads>(rv, lane_voff, toff, dst + TILE, tid, nv < kBlock);
     } else {
       TileLoader<T, D, kPairThreads> lk, lv;
       lk.load(ksrc, nv, tid);
