@@ -64,38 +64,41 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
   const int col = (tid % TPR) * VEC;
   const int roff = tid / TPR;
 
-  for (int b = 0; b < nblk; ++b) {
-    const int t = t0 + b;
-    const int row0 = t * kBlock;
-    const int cnt = min(kBlock, N - row0);
-    float acc[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-    float tmp[kBlock / RPP][VEC];
-#pragma unroll
-    for (int p = 0; p < kBlock / RPP; ++p) {
-      const int r = roff + p * RPP;
-      if (r < cnt) {
-        load_vec<T>(X + (size_t)(row0 + r) * D + col, tmp[p]);
-      } else {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) tmp[p][v] = 0.f;
-      }
-    }
+  // block b's rows: every load issued unconditionally (rows past N re-read the block's last
+  // row and are dropped in the sum; a block past n_b re-reads the last block), and block b + 1's
+  // loads go out before block b's sum, so each thread keeps two blocks' loads in flight
+  float tmp[2][kBlock / RPP][VEC];
+  auto load_block = [&](int b, float (&dst)[kBlock / RPP][VEC]) {
+    const int row0 = min(t0 + b, nb - 1) * kBlock;
+    const int last = min(kBlock, N - row0) - 1;
 #pragma unroll
     for (int p = 0; p < kBlock / RPP; ++p)
+      load_vec<T>(X + (size_t)(row0 + min(roff + p * RPP, last)) * D + col, dst[p]);
+  };
+  load_block(0, tmp[0]);
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[v] += tmp[p][v];
+  for (int b = 0; b < kPoolBlocksPerWg; ++b) {
+    if (b + 1 < kPoolBlocksPerWg) load_block(b + 1, tmp[(b + 1) & 1]);
+    if (b < nblk) {
+      const int cnt = min(kBlock, N - (t0 + b) * kBlock);
+      float acc[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) red[roff][col + v] = acc[v];
-    __syncthreads();
-    if (tid < D) {
-      float s = 0.f;
+      for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 #pragma unroll
-      for (int r = 0; r < RPP; ++r) s += red[r][tid];
-      xbar[b][tid] = s / (float)cnt;
+      for (int p = 0; p < kBlock / RPP; ++p)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] += roff + p * RPP < cnt ? tmp[b & 1][p][v] : 0.f;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) red[roff][col + v] = acc[v];
+      __syncthreads();
+      if (tid < D) {
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPP; ++r) sum += red[r][tid];
+        xbar[b][tid] = sum / (float)cnt;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // projection: y[b][c] = sum_r xbar[b][r] * W[r][c]; no W: the pooled means themselves
@@ -106,6 +109,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
   if (W) {
 #pragma unroll
     for (int u = 0; u < kPoolBlocksPerWg / G; ++u) y[u] = 0.f;
+#pragma unroll 32
     for (int r = 0; r < D; ++r) {
       const float w = W[r * D + c];
 #pragma unroll
