@@ -110,8 +110,8 @@ size_t carve_forward(const sla::Dims& d, int variant, void* ws, FwdWs* out) {
   if (variant == 3) {
     f.psize = c.take<int32_t>(sla::pair_order_ints(d));
     f.porder = c.take<int32_t>(sla::pair_order_ints(d));
-    f.pairs = c.take<int32_t>(sla::pair_match_ints(d));
   }
+  if (mp) f.pairs = c.take<int32_t>(sla::pair_match_ints(d));
   if (f8) {
     const size_t n = BH * d.N * d.d;
     f.q8 = c.take<uint8_t>(n);
@@ -273,9 +273,9 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     if (e != hipSuccess) return hip_fail(e);
   }
   if (mode == SLA_LINEAR_MASK_PRODUCT) {
-    // every block unselected when topk == 0; the bf16 / fp32 path also pairs its query blocks
-    e = fp8 ? sla::launch_mask_bits(d, idx, w.bits, stream)
-            : sla::launch_pair_match(d, idx, w.bits, w.pairs, w.psize, stream);
+    // every block unselected when topk == 0; the query blocks are paired on the way (the fp8
+    // kernel takes no dispatch order, so no sizes)
+    e = sla::launch_pair_match(d, idx, w.bits, w.pairs, fp8 ? nullptr : w.psize, stream);
     if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.bits, w.t_bf, stream, flags);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -295,7 +295,7 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   }
   if (fp8 && mode == SLA_LINEAR_MASK_PRODUCT)
     e = sla::launch_sparse_pair8(d, Q, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha, w.t_bf,
-                                 w.Z, w.zb, O, stream, int8);
+                                 w.Z, w.zb, O, stream, int8, w.pairs);
   else if (fp8)
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);

@@ -563,7 +563,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
-    float* __restrict__ O, int N, int nb, int topk, float c_log2) {
+    float* __restrict__ O, int N, int nb, int topk, float c_log2,
+    const int32_t* __restrict__ pairs = nullptr) {
   static_assert(D == 128, "the fp8 kernel is compiled for d = 128");
   constexpr int NS = D / 16, NC = D / 32, N8 = D / 64;
   constexpr int K8B = kBlock * D;  // bytes of a K8 (or V8^T) tile
@@ -613,11 +614,20 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int npair = (nb + 1) / 2;
   const int bh = item / npair, pr = item % npair;
-  const int qb0 = 2 * pr;
-  const bool has1 = qb0 + 1 < nb;
+  // the two query blocks: 2p and 2p + 1, or (pairs) the ones matched by the overlap of their
+  // kept sets; an odd n_b (or matching window) leaves one block alone, the absent second block
+  // taking the id n_b (all its rows lie past N)
+  int qa = 2 * pr, qbv = 2 * pr + 1;
+  if (pairs) {
+    qa = pairs[2 * ((size_t)bh * npair + pr)];
+    qbv = pairs[2 * ((size_t)bh * npair + pr) + 1];
+  }
+  const bool has1 = pairs ? qbv >= 0 : qbv < nb;
+  const int qb1 = has1 ? qbv : nb;
+  auto qsel = [&](int b) { return b ? qb1 : qa; };
   const int blk = w / 2, half = w % 2;
-  const bool present = blk == 0 || has1;  // the second block of an odd n_b's last pair is absent
-  const int qb = min(qb0 + blk, nb - 1);
+  const bool present = blk == 0 || has1;  // the second block of a lone block's pair is absent
+  const int qb = min(qsel(blk), nb - 1);
   const size_t hoff = (size_t)bh * N * D;
   const int nw = (nb + 31) / 32;
 
@@ -627,7 +637,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   for (int t = tid; t < 2 * topk; t += kF8Threads) {
     const int b = t / topk;
     if (b == 0 || has1) {
-      const int j = idx[((size_t)bh * nb + qb0 + b) * topk + t % topk];
+      const int j = idx[((size_t)bh * nb + qsel(b)) * topk + t % topk];
       atomicOr(&bm[b][j / 32], 1u << (j % 32));
       sl[b][t % topk] = j;
     }
@@ -655,7 +665,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
 
   // this wavefront's 32 rows (absent rows read a clamped one and are zeroed)
   const int m = 32 * half + lane % 32;
-  const int row = (qb0 + blk) * kBlock + m;
+  const int row = qsel(blk) * kBlock + m;
   const bool row_ok = row < N;
   const bool rows_all_ok = __ballot(!row_ok) == 0;  // every row of this wavefront exists
   i32x8 qf[N8];  // e4m3 Q as the B operand: k-slot 32g + b of step s <-> channel 64s + 32g + b
@@ -971,18 +981,18 @@ hipError_t launch_sparse_pair8(const Dims& p, const void* Q, const uint8_t* q8, 
                                const uint8_t* v8, const float* sq, const float* sk,
                                const float* sv, const int32_t* idx, const float* alpha,
                                const __bf16* t_bf, const float* Z, const float* zb, float* O,
-                               hipStream_t stream, int int8) {
+                               hipStream_t stream, int int8, const int32_t* pairs) {
   if (p.nb > 2048) return hipErrorInvalidValue;
   const float c_log2 = 1.4426950408889634f / sqrtf((float)p.d);
   const int grid = p.B * p.H * ((p.nb + 1) / 2);
   if (int8)
     pair8_kernel<128, kFmtInt8><<<grid, kF8Threads, 0, stream>>>(
         (const __bf16*)Q, q8, k8, v8, sq, sk, sv, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2);
+        c_log2, pairs);
   else
     pair8_kernel<128, kFmtE4M3><<<grid, kF8Threads, 0, stream>>>(
         (const __bf16*)Q, q8, k8, v8, sq, sk, sv, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2);
+        c_log2, pairs);
   return hipGetLastError();
 }
 

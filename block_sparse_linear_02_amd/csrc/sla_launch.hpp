@@ -74,7 +74,8 @@ int pair_order_ints(const Dims& p);
 hipError_t launch_pair_order(const Dims& p, const int32_t* size, int32_t* order, hipStream_t stream);
 // Query blocks paired by the overlap of their kept sets, in windows of 32 (pairs [BH][npair][2]
 // int32, second id -1 for a block alone: pair_match_ints(p) int32), the pairs' union sizes per
-// workgroup id (what launch_pair_order ranks), and the complement bit rows (as launch_mask_bits).
+// workgroup id (what launch_pair_order ranks; size may be null), and the complement bit rows (as
+// launch_mask_bits).
 int pair_match_ints(const Dims& p);
 hipError_t launch_pair_match(const Dims& p, const int32_t* idx, uint32_t* bits, int32_t* pairs,
                              int32_t* size, hipStream_t stream);
@@ -156,12 +157,13 @@ hipError_t launch_quantize(const Dims& p, const void* X, uint8_t* codes, float* 
 hipError_t launch_quantize_v8t(const Dims& p, const void* X, uint8_t* codes, float* scales,
                                hipStream_t stream, int int8 = 0);
 // fp8 sparse branch, mask-product linear mode: two query blocks per workgroup over the union of
-// their kept blocks, T_i (bf16) from memory.
+// their kept blocks, T_i (bf16) from memory.  pairs (optional, launch_pair_match): the two query
+// blocks of pair slot p, else 2p and 2p + 1.
 hipError_t launch_sparse_pair8(const Dims& p, const void* Q, const uint8_t* q8, const uint8_t* k8,
                                const uint8_t* v8, const float* sq, const float* sk,
                                const float* sv, const int32_t* idx, const float* alpha,
                                const __bf16* t_bf, const float* Z, const float* zb, float* O,
-                               hipStream_t stream, int int8 = 0);
+                               hipStream_t stream, int int8 = 0, const int32_t* pairs = nullptr);
 hipError_t launch_sparse_fp8(const Dims& p, const void* Q, const void* K, const void* V,
                              const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                              const float* sq, const float* sk, const float* sv,

@@ -698,16 +698,16 @@ __global__ __launch_bounds__(kMatchThreads) void pair_match_kernel(const int32_t
   if (tid < npw) {
     out[2 * tid] = b0 + my_pa;
     out[2 * tid + 1] = b0 + my_pb;
-    size[xcd_chunk_id(bh, slot0 + tid, npair)] = ov[my_pa][my_pa] + ov[my_pb][my_pb] - my_ov;
+    if (size) size[xcd_chunk_id(bh, slot0 + tid, npair)] = ov[my_pa][my_pa] + ov[my_pb][my_pb] - my_ov;
   } else if ((nblk & 1) && tid == npw) {  // the one block left (an odd window has nblk <= 31)
     const int left = __builtin_ctz(~used);
     out[2 * tid] = b0 + left;
     out[2 * tid + 1] = -1;
-    size[xcd_chunk_id(bh, slot0 + tid, npair)] = ov[left][left];
+    if (size) size[xcd_chunk_id(bh, slot0 + tid, npair)] = ov[left][left];
   }
   // the head's padding ids (XCDs x >= npair % 8 hold one item fewer than the slots per head)
   const int q = npair / 8, rem = npair % 8;
-  if (win == 0 && rem > 0 && tid >= rem && tid < 8) size[8 * (bh * (q + 1) + q) + tid] = -1;
+  if (size && win == 0 && rem > 0 && tid >= rem && tid < 8) size[8 * (bh * (q + 1) + q) + tid] = -1;
 }
 
 int pair_match_ints(const Dims& p) { return 2 * p.B * p.H * ((p.nb + 1) / 2); }
