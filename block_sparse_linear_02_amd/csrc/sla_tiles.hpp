@@ -263,4 +263,37 @@ __host__ __device__ __forceinline__ int xcd_chunk_id(int head, int item, int per
   return 8 * (head * smax + off) + x;
 }
 
+// The same with the heads split among 8 / XG groups of XG XCDs (XG = 8, 4, 2 or 1): head h runs
+// on the XCDs of group h % (8 / XG), each of them taking 1 / XG of the head's items, so each XCD
+// works through a larger, contiguous share of fewer heads at a time (XG = 8 is the map above).
+// XCD x = wg % 8 is position x % XG of group x / XG; its k-th workgroup (k = wg / 8) runs item
+// chunk_start(x % XG) + k % smax of head (k / smax) (8 / XG) + x / XG, smax = ceil(per_head / XG).
+template <int XG>
+__host__ __device__ __forceinline__ int xcd_group_grid(int heads, int per_head) {
+  constexpr int G = 8 / XG;
+  return 8 * ((heads + G - 1) / G) * ((per_head + XG - 1) / XG);
+}
+template <int XG>
+__host__ __device__ __forceinline__ bool xcd_group_map(int wg, int heads, int per_head, int* head, int* item) {
+  static_assert(XG == 1 || XG == 2 || XG == 4 || XG == 8, "XCDs per head group");
+  constexpr int G = 8 / XG;
+  const int q = per_head / XG, r = per_head % XG;
+  const int smax = q + (r > 0 ? 1 : 0);
+  const int x = wg % 8, k = wg / 8, px = x % XG;
+  const int off = k % smax;
+  *head = (k / smax) * G + x / XG;
+  *item = px * q + (px < r ? px : r) + off;
+  return *head < heads && off < q + (px < r ? 1 : 0);
+}
+template <int XG>
+__host__ __device__ __forceinline__ int xcd_group_id(int head, int item, int per_head) {
+  constexpr int G = 8 / XG;
+  const int q = per_head / XG, r = per_head % XG;
+  const int smax = q + (r > 0 ? 1 : 0);
+  const int big = r * (q + 1);
+  const int px = item < big ? item / (q + 1) : r + (item - big) / q;
+  const int off = item - (px * q + (px < r ? px : r));
+  return 8 * ((head / G) * smax + off) + (head % G) * XG + px;
+}
+
 }  // namespace sla

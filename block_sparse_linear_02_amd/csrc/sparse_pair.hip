@@ -42,6 +42,9 @@ namespace {
 
 constexpr int kPairThreads = 256;
 constexpr int kPairMaxWords = 64;  // bitmap words of the union: n_b <= 2048
+// XCDs per head group of the pair kernel's grid (xcd_group_map): each head's pairs are shared by
+// this many XCDs, the heads alternating between the 8 / kPairXg groups
+constexpr int kPairXg = 4;
 
 template <class T>
 __device__ __forceinline__ bf16x8 pair_row8(const T* p);
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
-    float* __restrict__ O, int N, int nb, int topk, float c_log2,
+    float* __restrict__ O, int N, int nb, int topk, float c_log2, int heads,
     const uint32_t* __restrict__ flags, TrainRows tr, const int32_t* __restrict__ out_rows,
     const float* __restrict__ msoft = nullptr, const int32_t* __restrict__ order = nullptr,
     const int32_t* __restrict__ pairs = nullptr) {
@@ -119,14 +122,14 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   const int tid = threadIdx.x;
   const int lane = tid % kWave, g = lane / 32;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wavefront-uniform (scalar branches)
-  // every XCD takes the same eighth of every head's pairs (heads may differ in work when a
-  // branch is dropped); the grid's padding workgroups exit here, before any barrier
+  // each head's pairs are split evenly among the XCDs of its group (heads may differ in work
+  // when a branch is dropped); the grid's padding workgroups exit here, before any barrier
   const int npair = (nb + 1) / 2;
   int bh, pr;
   // order (optional): the workgroup ids in dispatch order, each XCD's own items largest union
   // first (pair_order_kernel), so that the shortest workgroups fill the end of the launch
   const int wg = order ? order[blockIdx.x] : (int)blockIdx.x;
-  if (!xcd_chunk_map(wg, npair, &bh, &pr)) return;
+  if (!xcd_group_map<kPairXg>(wg, heads, npair, &bh, &pr)) return;
   // the two query blocks: 2p and 2p + 1, or (pairs) the ones matched by overlap of their kept
   // sets; an odd n_b (or an odd matching window) leaves one workgroup one block, whose absent
   // second block is given the id n_b (all its rows lie past N)
@@ -514,16 +517,16 @@ hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void
                          const float* Z, const float* zb, float* O, hipStream_t stream,
                          const uint32_t* flags, const TrainRows* tr, const int32_t* out_rows,
                          const int32_t* order, const int32_t* pairs) {
-  const int total = xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2);
+  const int total = xcd_group_grid<kPairXg>(p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (tr)
     pair_kernel<T, D, true><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, flags, *tr, out_rows, nullptr, order, pairs);
+        c_log2, p.B * p.H, flags, *tr, out_rows, nullptr, order, pairs);
   else
     pair_kernel<T, D, false><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, flags, TrainRows{}, out_rows, nullptr, order, pairs);
+        c_log2, p.B * p.H, flags, TrainRows{}, out_rows, nullptr, order, pairs);
   return hipGetLastError();
 }
 
@@ -534,16 +537,16 @@ hipError_t launch_sparse_soft(const Dims& p, const void* Q, const void* K, const
                               const float* Z, const float* zb, float* O, hipStream_t stream,
                               const TrainRows* tr) {
   if (p.nb > kPairMaxWords * 32 || p.dtype != kBF16 || p.d != 128 || !msoft) return hipErrorInvalidValue;
-  const int total = xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2);
+  const int total = xcd_group_grid<kPairXg>(p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf(128.f);
   if (tr)
     pair_kernel<__bf16, 128, true, true><<<total, kPairThreads, 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, nullptr, alpha, t_bf, Z, zb, O, p.N, p.nb,
-        p.nb, c_log2, nullptr, *tr, nullptr, msoft);
+        p.nb, c_log2, p.B * p.H, nullptr, *tr, nullptr, msoft);
   else
     pair_kernel<__bf16, 128, false, true><<<total, kPairThreads, 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, nullptr, alpha, t_bf, Z, zb, O, p.N, p.nb,
-        p.nb, c_log2, nullptr, TrainRows{}, nullptr, msoft);
+        p.nb, c_log2, p.B * p.H, nullptr, TrainRows{}, nullptr, msoft);
   return hipGetLastError();
 }
 
@@ -565,21 +568,23 @@ hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const
 }
 
 // The pair kernel's dispatch order: each XCD's items (the workgroup ids wg with wg % 8 == x),
-// within each head by the size of their union of kept blocks (from pair_match_kernel; -1 for
-// an id past a short chunk, which exits at once and so goes last), largest first.
-//   pair_order_kernel  one workgroup per (XCD, head): that XCD's ids of the head, staged in LDS
-//                      and ranked by size, largest first (a stable rank); the order changes
-//                      which workgroup runs when, never what one computes.
-constexpr int kOrderMax = 128;  // ids per (XCD, head) group: ceil(ceil(n_b / 2) / 8) <= 128
+// within each head by the size of their union of kept blocks (from pair_match_kernel), largest
+// first; ids that run nothing (past a short chunk, or a padding head) go last.
+//   pair_order_kernel  one workgroup per (XCD, head of its group): that XCD's ids of the head,
+//                      their sizes staged in LDS and ranked, largest first (a stable rank);
+//                      the order changes which workgroup runs when, never what one computes.
+constexpr int kOrderMax = 256;  // ids per (XCD, head): ceil(ceil(n_b / 2) / kPairXg) <= 256
 
-__global__ __launch_bounds__(kOrderMax) void pair_order_kernel(const int32_t* __restrict__ size, int smax,
+__global__ __launch_bounds__(kOrderMax) void pair_order_kernel(const int32_t* __restrict__ size, int heads,
+                                                              int npair, int smax,
                                                               int32_t* __restrict__ order) {
-  // group (x, head): XCD x's ids of one head, 8 (g0 + t) + x for t < smax, which keep their
-  // head-by-head place (co-resident workgroups of an XCD share a head's kept K/V in L2) and
-  // inside the group go by size, largest first (a stable rank)
   __shared__ int sz[kOrderMax];
   const int x = blockIdx.x, g0 = blockIdx.y * smax, t = threadIdx.x;
-  if (t < smax) sz[t] = size[8 * (g0 + t) + x];
+  const int id = 8 * (g0 + t) + x;
+  if (t < smax) {
+    int bh, pr;
+    sz[t] = xcd_group_map<kPairXg>(id, heads, npair, &bh, &pr) ? size[id] : -1;
+  }
   __syncthreads();
   if (t >= smax) return;
   const int my = sz[t];
@@ -588,10 +593,10 @@ __global__ __launch_bounds__(kOrderMax) void pair_order_kernel(const int32_t* __
     const int o = sz[j];
     rank += (o > my || (o == my && j < t)) ? 1 : 0;
   }
-  order[8 * (g0 + rank) + x] = 8 * (g0 + t) + x;
+  order[8 * (g0 + rank) + x] = id;
 }
 
-int pair_order_ints(const Dims& p) { return xcd_chunk_grid(p.B * p.H, (p.nb + 1) / 2); }
+int pair_order_ints(const Dims& p) { return xcd_group_grid<kPairXg>(p.B * p.H, (p.nb + 1) / 2); }
 
 // Query blocks paired by the overlap of their kept sets.  Windows of kMatchWin consecutive query
 // blocks (neighbouring blocks are the ones that share kept blocks, and a window's pairs stay
@@ -605,9 +610,9 @@ int pair_order_ints(const Dims& p) { return xcd_chunk_grid(p.B * p.H, (p.nb + 1)
 //                      different rows hit different banks), written out as their complement
 //                      for the linear branch (as mask_bits_kernel), and their pairwise
 //                      overlaps in LDS; then wavefront 0 picks the pairs, one max-reduction
-//                      over its lanes per pair, and writes each pair's union size where pair_order_kernel
-//                      reads it (the workgroup id xcd_chunk_id gives the pair's slot; window
-//                      0 also marks the head's padding ids -1).
+//                      over its lanes per pair, and writes each pair's union size where
+//                      pair_order_kernel reads it (at the workgroup id that xcd_group_id gives
+//                      the pair's slot).
 constexpr int kMatchWin = 32;
 constexpr int kMatchThreads = 256;
 constexpr int kMatchPitch = kPairMaxWords + 1;
@@ -698,16 +703,13 @@ __global__ __launch_bounds__(kMatchThreads) void pair_match_kernel(const int32_t
   if (tid < npw) {
     out[2 * tid] = b0 + my_pa;
     out[2 * tid + 1] = b0 + my_pb;
-    if (size) size[xcd_chunk_id(bh, slot0 + tid, npair)] = ov[my_pa][my_pa] + ov[my_pb][my_pb] - my_ov;
+    if (size) size[xcd_group_id<kPairXg>(bh, slot0 + tid, npair)] = ov[my_pa][my_pa] + ov[my_pb][my_pb] - my_ov;
   } else if ((nblk & 1) && tid == npw) {  // the one block left (an odd window has nblk <= 31)
     const int left = __builtin_ctz(~used);
     out[2 * tid] = b0 + left;
     out[2 * tid + 1] = -1;
-    if (size) size[xcd_chunk_id(bh, slot0 + tid, npair)] = ov[left][left];
+    if (size) size[xcd_group_id<kPairXg>(bh, slot0 + tid, npair)] = ov[left][left];
   }
-  // the head's padding ids (XCDs x >= npair % 8 hold one item fewer than the slots per head)
-  const int q = npair / 8, rem = npair % 8;
-  if (size && win == 0 && rem > 0 && tid >= rem && tid < 8) size[8 * (bh * (q + 1) + q) + tid] = -1;
 }
 
 int pair_match_ints(const Dims& p) { return 2 * p.B * p.H * ((p.nb + 1) / 2); }
@@ -722,9 +724,11 @@ hipError_t launch_pair_match(const Dims& p, const int32_t* idx, uint32_t* bits, 
 }
 
 hipError_t launch_pair_order(const Dims& p, const int32_t* size, int32_t* order, hipStream_t stream) {
-  const int smax = ((p.nb + 1) / 2 + 7) / 8;
+  const int npair = (p.nb + 1) / 2, heads = p.B * p.H;
+  const int smax = (npair + kPairXg - 1) / kPairXg;
   if (smax > kOrderMax) return hipErrorInvalidValue;
-  pair_order_kernel<<<dim3(8, p.B * p.H), kOrderMax, 0, stream>>>(size, smax, order);
+  const int groups = (heads + 8 / kPairXg - 1) / (8 / kPairXg);
+  pair_order_kernel<<<dim3(8, groups), kOrderMax, 0, stream>>>(size, heads, npair, smax, order);
   return hipGetLastError();
 }
 
