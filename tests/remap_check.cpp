@@ -1,11 +1,58 @@
 // Host-side check of the workgroup -> work-item maps of sla_tiles.hpp: xcd_remap is a
 // bijection, and xcd_chunk_map sends the valid workgroups of an xcd_chunk_grid grid one to one
-// onto every (head, item) with every XCD holding the same share (within one item) of every head.
-// Built and run on the CPU by tests/test_remap.py.
+// onto every (head, item) with every XCD holding the same share (within one item) of every head;
+// xcd_chunk_id inverts it.  xcd_group_map<XG> does the same over xcd_group_grid<XG> with each
+// head on the XG XCDs of its group only (group h % (8 / XG)), balanced within one item over
+// them, and xcd_group_id<XG> inverts it.  Built and run on the CPU by tests/test_remap.py.
 #include <cstdio>
 #include <vector>
 
 #include "sla_tiles.hpp"
+
+template <int XG>
+int check_group(int heads, int per) {
+  constexpr int G = 8 / XG;
+  const int grid = sla::xcd_group_grid<XG>(heads, per);
+  std::vector<int> seen(heads * per, 0), share(8 * heads, 0);
+  int valid = 0;
+  for (int wg = 0; wg < grid; ++wg) {
+    int h, it;
+    if (!sla::xcd_group_map<XG>(wg, heads, per, &h, &it)) continue;
+    ++valid;
+    if (h < 0 || h >= heads || it < 0 || it >= per || seen[h * per + it]++) {
+      std::printf("xcd_group_map<%d>: heads %d per %d wg %d -> (%d, %d) out of range or repeated\n", XG, heads,
+                  per, wg, h, it);
+      return 1;
+    }
+    if ((wg % 8) / XG != h % G) {
+      std::printf("xcd_group_map<%d>: head %d on XCD %d outside its group\n", XG, h, wg % 8);
+      return 1;
+    }
+    if (sla::xcd_group_id<XG>(h, it, per) != wg) {
+      std::printf("xcd_group_id<%d>: (%d, %d) -> %d, expected %d\n", XG, h, it,
+                  sla::xcd_group_id<XG>(h, it, per), wg);
+      return 1;
+    }
+    share[(wg % 8) * heads + h]++;
+  }
+  if (valid != heads * per) {
+    std::printf("xcd_group_map<%d>: heads %d per %d covers %d of %d items\n", XG, heads, per, valid, heads * per);
+    return 1;
+  }
+  for (int h = 0; h < heads; ++h) {
+    int mn = 1 << 30, mx = 0;
+    for (int x = (h % G) * XG; x < (h % G + 1) * XG; ++x) {
+      const int v = share[x * heads + h];
+      mn = v < mn ? v : mn;
+      mx = v > mx ? v : mx;
+    }
+    if (mx - mn > 1) {
+      std::printf("xcd_group_map<%d> unbalanced: heads %d per %d head %d: %d..%d\n", XG, heads, per, h, mn, mx);
+      return 1;
+    }
+  }
+  return 0;
+}
 
 int main() {
   int bad = 0;
@@ -35,6 +82,11 @@ int main() {
           bad = 1;
           break;
         }
+        if (sla::xcd_chunk_id(h, it, per) != wg) {
+          std::printf("xcd_chunk_id: (%d, %d) -> %d, expected %d\n", h, it, sla::xcd_chunk_id(h, it, per), wg);
+          bad = 1;
+          break;
+        }
         share[(wg % 8) * heads + h]++;
       }
       if (!bad && valid != heads * per) {
@@ -55,6 +107,10 @@ int main() {
       }
     }
   }
+  for (int heads = 1; heads <= 41 && !bad; heads += 2)
+    for (int per = 1; per <= 1024 && !bad; per += (per < 40 ? 1 : 53))
+      bad = check_group<8>(heads, per) || check_group<4>(heads, per) || check_group<2>(heads, per) ||
+            check_group<1>(heads, per);
   std::printf(bad ? "FAIL\n" : "OK\n");
   return bad;
 }
