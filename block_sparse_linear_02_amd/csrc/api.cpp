@@ -275,7 +275,7 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   if (mode == SLA_LINEAR_MASK_PRODUCT) {
     // every block unselected when topk == 0; the query blocks are paired on the way (the fp8
     // kernel takes no dispatch order, so no sizes)
-    e = sla::launch_pair_match(d, idx, w.bits, w.pairs, fp8 ? nullptr : w.psize, stream);
+    e = sla::launch_pair_match(d, idx, w.bits, w.pairs, fp8 ? nullptr : w.psize, flags != nullptr, stream);
     if (e == hipSuccess) e = sla::launch_tsel(d, w.hj_bf, w.bits, w.t_bf, stream, flags);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -300,7 +300,7 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);
   else if (mode == SLA_LINEAR_MASK_PRODUCT) {
-    e = sla::launch_pair_order(d, w.psize, w.porder, stream);
+    e = sla::launch_pair_order(d, w.psize, w.porder, flags != nullptr, stream);
     if (e == hipSuccess)
       e = sla::launch_sparse_pair(d, Q, K, V, idx, alpha, w.t_bf, w.Z, w.zb, O, stream, flags,
                                   nullptr, out_rows, w.porder, w.pairs);

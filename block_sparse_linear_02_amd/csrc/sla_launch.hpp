@@ -71,14 +71,17 @@ hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const
 // blocks, largest first) from those sizes (launch_pair_match): pair_order_ints(p) int32 each
 // of size and order.
 int pair_order_ints(const Dims& p);
-hipError_t launch_pair_order(const Dims& p, const int32_t* size, int32_t* order, hipStream_t stream);
+// unequal_heads (branch dropping on): the grid shares every head among all 8 XCDs instead of 4;
+// launch_pair_match, launch_pair_order and launch_sparse_pair (flags != null) must agree.
+hipError_t launch_pair_order(const Dims& p, const int32_t* size, int32_t* order, bool unequal_heads,
+                             hipStream_t stream);
 // Query blocks paired by the overlap of their kept sets, in windows of 32 (pairs [BH][npair][2]
 // int32, second id -1 for a block alone: pair_match_ints(p) int32), the pairs' union sizes per
 // workgroup id (what launch_pair_order ranks; size may be null), and the complement bit rows (as
 // launch_mask_bits).
 int pair_match_ints(const Dims& p);
 hipError_t launch_pair_match(const Dims& p, const int32_t* idx, uint32_t* bits, int32_t* pairs,
-                             int32_t* size, hipStream_t stream);
+                             int32_t* size, bool unequal_heads, hipStream_t stream);
 // Debug check of idx (validate.hip): *bad = the number of rows with an entry outside [0, n_b)
 // or not strictly ascending.
 hipError_t launch_validate_idx(const Dims& p, const int32_t* idx, int* bad, hipStream_t stream);

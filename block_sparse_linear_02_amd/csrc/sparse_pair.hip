@@ -42,9 +42,21 @@ namespace {
 
 constexpr int kPairThreads = 256;
 constexpr int kPairMaxWords = 64;  // bitmap words of the union: n_b <= 2048
-// XCDs per head group of the pair kernel's grid (xcd_group_map): each head's pairs are shared by
-// this many XCDs, the heads alternating between the 8 / kPairXg groups
-constexpr int kPairXg = 4;
+// XCDs per head of the pair kernel's grid (xcd_group_map): 4 by default, each head's pairs
+// shared by the XCDs of one half of the chip, the heads alternating between the halves (an XCD
+// works through a larger share of fewer heads, which its L2 holds better); 8 (every XCD takes an
+// eighth of every head) when branch dropping may leave heads with unequal work, so that no half
+// of the chip idles while the other finishes its heads
+__host__ __device__ __forceinline__ bool pair_map(int xg, int wg, int heads, int npair, int* bh, int* pr) {
+  return xg == 8 ? xcd_group_map<8>(wg, heads, npair, bh, pr) : xcd_group_map<4>(wg, heads, npair, bh, pr);
+}
+__host__ __device__ __forceinline__ int pair_id(int xg, int bh, int pr, int npair) {
+  return xg == 8 ? xcd_group_id<8>(bh, pr, npair) : xcd_group_id<4>(bh, pr, npair);
+}
+__host__ __device__ __forceinline__ int pair_grid(int xg, int heads, int npair) {
+  return xg == 8 ? xcd_group_grid<8>(heads, npair) : xcd_group_grid<4>(heads, npair);
+}
+inline int pair_xg(bool unequal_heads) { return unequal_heads ? 8 : 4; }
 
 template <class T>
 __device__ __forceinline__ bf16x8 pair_row8(const T* p);
@@ -99,7 +111,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const __bf16* __restrict__ t_g, const float* __restrict__ Z, const float* __restrict__ zb,
-    float* __restrict__ O, int N, int nb, int topk, float c_log2, int heads,
+    float* __restrict__ O, int N, int nb, int topk, float c_log2, int heads, int xg,
     const uint32_t* __restrict__ flags, TrainRows tr, const int32_t* __restrict__ out_rows,
     const float* __restrict__ msoft = nullptr, const int32_t* __restrict__ order = nullptr,
     const int32_t* __restrict__ pairs = nullptr) {
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void pair_kernel(
   // order (optional): the workgroup ids in dispatch order, each XCD's own items largest union
   // first (pair_order_kernel), so that the shortest workgroups fill the end of the launch
   const int wg = order ? order[blockIdx.x] : (int)blockIdx.x;
-  if (!xcd_group_map<kPairXg>(wg, heads, npair, &bh, &pr)) return;
+  if (!pair_map(xg, wg, heads, npair, &bh, &pr)) return;
   // the two query blocks: 2p and 2p + 1, or (pairs) the ones matched by overlap of their kept
   // sets; an odd n_b (or an odd matching window) leaves one workgroup one block, whose absent
   // second block is given the id n_b (all its rows lie past N)
@@ -517,16 +529,17 @@ hipError_t launch_pair_t(const Dims& p, const void* Q, const void* K, const void
                          const float* Z, const float* zb, float* O, hipStream_t stream,
                          const uint32_t* flags, const TrainRows* tr, const int32_t* out_rows,
                          const int32_t* order, const int32_t* pairs) {
-  const int total = xcd_group_grid<kPairXg>(p.B * p.H, (p.nb + 1) / 2);
+  const int xg = pair_xg(flags != nullptr);
+  const int total = pair_grid(xg, p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (tr)
     pair_kernel<T, D, true><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, p.B * p.H, flags, *tr, out_rows, nullptr, order, pairs);
+        c_log2, p.B * p.H, xg, flags, *tr, out_rows, nullptr, order, pairs);
   else
     pair_kernel<T, D, false><<<total, kPairThreads, 0, stream>>>(
         (const T*)Q, (const T*)K, (const T*)V, idx, alpha, t_bf, Z, zb, O, p.N, p.nb, p.topk,
-        c_log2, p.B * p.H, flags, TrainRows{}, out_rows, nullptr, order, pairs);
+        c_log2, p.B * p.H, xg, flags, TrainRows{}, out_rows, nullptr, order, pairs);
   return hipGetLastError();
 }
 
@@ -537,16 +550,16 @@ hipError_t launch_sparse_soft(const Dims& p, const void* Q, const void* K, const
                               const float* Z, const float* zb, float* O, hipStream_t stream,
                               const TrainRows* tr) {
   if (p.nb > kPairMaxWords * 32 || p.dtype != kBF16 || p.d != 128 || !msoft) return hipErrorInvalidValue;
-  const int total = xcd_group_grid<kPairXg>(p.B * p.H, (p.nb + 1) / 2);
+  const int total = pair_grid(4, p.B * p.H, (p.nb + 1) / 2);
   const float c_log2 = 1.4426950408889634f / sqrtf(128.f);
   if (tr)
     pair_kernel<__bf16, 128, true, true><<<total, kPairThreads, 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, nullptr, alpha, t_bf, Z, zb, O, p.N, p.nb,
-        p.nb, c_log2, p.B * p.H, nullptr, *tr, nullptr, msoft);
+        p.nb, c_log2, p.B * p.H, 4, nullptr, *tr, nullptr, msoft);
   else
     pair_kernel<__bf16, 128, false, true><<<total, kPairThreads, 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)K, (const __bf16*)V, nullptr, alpha, t_bf, Z, zb, O, p.N, p.nb,
-        p.nb, c_log2, p.B * p.H, nullptr, TrainRows{}, nullptr, msoft);
+        p.nb, c_log2, p.B * p.H, 4, nullptr, TrainRows{}, nullptr, msoft);
   return hipGetLastError();
 }
 
@@ -573,17 +586,17 @@ hipError_t launch_sparse_pair(const Dims& p, const void* Q, const void* K, const
 //   pair_order_kernel  one workgroup per (XCD, head of its group): that XCD's ids of the head,
 //                      their sizes staged in LDS and ranked, largest first (a stable rank);
 //                      the order changes which workgroup runs when, never what one computes.
-constexpr int kOrderMax = 256;  // ids per (XCD, head): ceil(ceil(n_b / 2) / kPairXg) <= 256
+constexpr int kOrderMax = 256;  // ids per (XCD, head): ceil(ceil(n_b / 2) / xg) <= 256
 
 __global__ __launch_bounds__(kOrderMax) void pair_order_kernel(const int32_t* __restrict__ size, int heads,
-                                                              int npair, int smax,
+                                                              int npair, int smax, int xg,
                                                               int32_t* __restrict__ order) {
   __shared__ int sz[kOrderMax];
   const int x = blockIdx.x, g0 = blockIdx.y * smax, t = threadIdx.x;
   const int id = 8 * (g0 + t) + x;
   if (t < smax) {
     int bh, pr;
-    sz[t] = xcd_group_map<kPairXg>(id, heads, npair, &bh, &pr) ? size[id] : -1;
+    sz[t] = pair_map(xg, id, heads, npair, &bh, &pr) ? size[id] : -1;
   }
   __syncthreads();
   if (t >= smax) return;
@@ -596,7 +609,10 @@ __global__ __launch_bounds__(kOrderMax) void pair_order_kernel(const int32_t* __
   order[8 * (g0 + rank) + x] = id;
 }
 
-int pair_order_ints(const Dims& p) { return xcd_group_grid<kPairXg>(p.B * p.H, (p.nb + 1) / 2); }
+int pair_order_ints(const Dims& p) {
+  const int a = pair_grid(4, p.B * p.H, (p.nb + 1) / 2), b = pair_grid(8, p.B * p.H, (p.nb + 1) / 2);
+  return a > b ? a : b;
+}
 
 // Query blocks paired by the overlap of their kept sets.  Windows of kMatchWin consecutive query
 // blocks (neighbouring blocks are the ones that share kept blocks, and a window's pairs stay
@@ -618,7 +634,7 @@ constexpr int kMatchThreads = 256;
 constexpr int kMatchPitch = kPairMaxWords + 1;
 
 __global__ __launch_bounds__(kMatchThreads) void pair_match_kernel(const int32_t* __restrict__ idx, int nb,
-                                                                  int nw, int topk, int npair,
+                                                                  int nw, int topk, int npair, int xg,
                                                                   uint32_t* __restrict__ bits,
                                                                   int32_t* __restrict__ pairs,
                                                                   int32_t* __restrict__ size) {
@@ -703,32 +719,34 @@ __global__ __launch_bounds__(kMatchThreads) void pair_match_kernel(const int32_t
   if (tid < npw) {
     out[2 * tid] = b0 + my_pa;
     out[2 * tid + 1] = b0 + my_pb;
-    if (size) size[xcd_group_id<kPairXg>(bh, slot0 + tid, npair)] = ov[my_pa][my_pa] + ov[my_pb][my_pb] - my_ov;
+    if (size) size[pair_id(xg, bh, slot0 + tid, npair)] = ov[my_pa][my_pa] + ov[my_pb][my_pb] - my_ov;
   } else if ((nblk & 1) && tid == npw) {  // the one block left (an odd window has nblk <= 31)
     const int left = __builtin_ctz(~used);
     out[2 * tid] = b0 + left;
     out[2 * tid + 1] = -1;
-    if (size) size[xcd_group_id<kPairXg>(bh, slot0 + tid, npair)] = ov[left][left];
+    if (size) size[pair_id(xg, bh, slot0 + tid, npair)] = ov[left][left];
   }
 }
 
 int pair_match_ints(const Dims& p) { return 2 * p.B * p.H * ((p.nb + 1) / 2); }
 
 hipError_t launch_pair_match(const Dims& p, const int32_t* idx, uint32_t* bits, int32_t* pairs,
-                             int32_t* size, hipStream_t stream) {
+                             int32_t* size, bool unequal_heads, hipStream_t stream) {
   if (p.nb > kPairMaxWords * 32) return hipErrorInvalidValue;
   const dim3 grid((p.nb + kMatchWin - 1) / kMatchWin, p.B * p.H);
   pair_match_kernel<<<grid, kMatchThreads, 0, stream>>>(idx, p.nb, mask_words(p.nb), p.topk, (p.nb + 1) / 2,
-                                                        bits, pairs, size);
+                                                        pair_xg(unequal_heads), bits, pairs, size);
   return hipGetLastError();
 }
 
-hipError_t launch_pair_order(const Dims& p, const int32_t* size, int32_t* order, hipStream_t stream) {
+hipError_t launch_pair_order(const Dims& p, const int32_t* size, int32_t* order, bool unequal_heads,
+                             hipStream_t stream) {
   const int npair = (p.nb + 1) / 2, heads = p.B * p.H;
-  const int smax = (npair + kPairXg - 1) / kPairXg;
+  const int xg = pair_xg(unequal_heads);
+  const int smax = (npair + xg - 1) / xg;
   if (smax > kOrderMax) return hipErrorInvalidValue;
-  const int groups = (heads + 8 / kPairXg - 1) / (8 / kPairXg);
-  pair_order_kernel<<<dim3(8, groups), kOrderMax, 0, stream>>>(size, heads, npair, smax, order);
+  const int groups = (heads + 8 / xg - 1) / (8 / xg);
+  pair_order_kernel<<<dim3(8, groups), kOrderMax, 0, stream>>>(size, heads, npair, smax, xg, order);
   return hipGetLastError();
 }
 
