@@ -576,6 +576,25 @@ def test_video_l_whole_head_mask_product():
     check_close(gpu_blocks(c, got, [7, 38], None), ref, what="video_l whole heads mask_product")
 
 
+def test_mask_product_odd_blocks_lone_last_window():
+    """n_b = 1025 (N = 65590, a 54-token last block): the last matching window of query blocks
+    holds one block alone, which runs in a workgroup by itself; every query block of the one
+    head against the oracle."""
+    wl = gen.workload("video_l", H=1, N=65590, grid=(1, 70, 937), topk=24)
+    c = case("odd_1025", wl)
+    g = dev(c)
+    say("odd n_b 1025: route + mask_product forward")
+    idx, _, _ = sla.route(g["Q"], g["K"], g["Wq"], g["Wk"], wl.topk)
+    r = oracle_route(c, wl.topk)
+    assert np.array_equal(idx.cpu().numpy(), r["idx"]), "odd n_b 1025: router indices differ"
+    O = sla.forward(g["Q"], g["K"], g["V"], idx, g["alpha"], linear_mode="mask_product")
+    torch.cuda.synchronize()
+    got = O.cpu().double().numpy()
+    say("odd n_b 1025: oracle (1 head)")
+    ref = oracle_blocks(c, r["idx"], [0], None)
+    check_close(gpu_blocks(c, got, [0], None), ref, what="odd n_b 1025 mask_product")
+
+
 def test_video_l_fp8_full_size():
     c = case("video_l", gen.workload("video_l"))
     full_size(c, heads=[0, 21], blocks=[0, 1181], fp8=True, what="video_l fp8")
