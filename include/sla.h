@@ -82,7 +82,10 @@ typedef struct {
  *   T_i = sum_{j not in sel(i)} h_j is formed for all query blocks at once as the product of the
  *   complement (unselected) 0/1 mask, built from idx as a bit mask, with the stacked states (one
  *   MFMA GEMM per head, fp32 accumulation), stored in bf16; the sparse kernel applies relu(Q)
- *   to its T_i.  The unselected blocks are summed directly, never as H minus the kept ones, so
+ *   to its T_i.  The sparse kernel runs two query blocks per workgroup, paired among nearby
+ *   blocks by the overlap of their kept sets; the pairing decides only which blocks share a
+ *   workgroup (and its staged K/V tiles): each block still walks its own kept tiles in
+ *   ascending order, so its result does not depend on its partner.  The unselected blocks are summed directly, never as H minus the kept ones, so
  *   no cancellation appears when almost every block is kept.  The two bf16 roundings put a relative error
  *   of about 2^-9 on the linear branch's numerator (the other modes keep it near fp32). */
 enum { SLA_LINEAR_FUSED = 0, SLA_LINEAR_LITERAL = 1, SLA_LINEAR_MASK_PRODUCT = 2 };
