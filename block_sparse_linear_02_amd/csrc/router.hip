@@ -2,20 +2,26 @@
 // sections 2.ba and 2.dal): block mean-pool of Q and K, learnable projections, block-score map
 // and the inference-time HardTop-k.
 //
-//   pool_project_kernel  one workgroup per (8 blocks, head, Q|K): streams the block's rows
-//                        (16-byte coalesced loads, fp32 sums), divides by the number of valid
+//   pool_project_kernel  one workgroup per (8 blocks, head, Q|K): streams the blocks' rows
+//                        (16-byte coalesced loads, two blocks in flight, fp32 sums reduced
+//                        inside each wavefront by shuffles, per-wavefront partials in LDS and
+//                        one barrier after the last block), divides by the number of valid
 //                        tokens, multiplies by W (fp32) and stores the result split into a
 //                        bf16 high part and a bf16 low part (x = hi + lo + O(2^-17 |x|)).
-//   score_topk_kernel    one workgroup per (16 query blocks, head): the 16 x n_b score tile
+//   score_topk_kernel    one workgroup per (16 query blocks, head), each XCD taking a
+//                        contiguous range of heads: the 16 x n_b score tile
 //                        s = (q~ . k~) / sqrt(d) by bf16 MFMA on the split operands
 //                        (hi*hi + hi*lo + lo*hi, fp32 accumulation: about fp32 accuracy) into
-//                        LDS (8 wavefronts, operand loads of two key tiles issued ahead of
-//                        their MFMAs), then per row (one wavefront) the k-th largest score by
-//                        a 32-step bitwise search on order-preserving keys (counts by ballot),
-//                        and an ascending compaction that keeps the lowest indices among equal
-//                        scores.
+//                        LDS (8 wavefronts, each key tile's operands loaded through a range-
+//                        checked buffer resource while the previous tile's MFMAs run), then per
+//                        row (one wavefront) the k-th largest score by a bitwise search on
+//                        order-preserving keys (counts by ballot): the top 12 bits over every
+//                        key, the low 20 over the band of keys sharing those bits, compacted in
+//                        LDS; then an ascending compaction that keeps the lowest indices among
+//                        equal scores.
 #include "sla_device.hpp"
 #include "sla_launch.hpp"
+#include "sla_tiles.hpp"
 
 namespace sla {
 
@@ -24,20 +30,16 @@ namespace {
 constexpr int kPoolBlocksPerWg = 8;
 constexpr int kPoolThreads = 256;
 
+// element v of a 16-byte load of T values, as float
 template <class T>
-__device__ __forceinline__ void load_vec(const T* p, float* out);
+__device__ __forceinline__ float raw_elem(i32x4 x, int v);
 template <>
-__device__ __forceinline__ void load_vec<__bf16>(const __bf16* p, float* out) {
-  bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+__device__ __forceinline__ float raw_elem<__bf16>(i32x4 x, int v) {
+  const u32 w = (u32)x[v / 2];
+  return __uint_as_float(v % 2 ? (w & 0xffff0000u) : (w << 16));
 }
 template <>
-__device__ __forceinline__ void load_vec<float>(const float* p, float* out) {
-  f32x4 v = *reinterpret_cast<const f32x4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = v[i];
-}
+__device__ __forceinline__ float raw_elem<float>(i32x4 x, int v) { return __int_as_float(x[v]); }
 
 template <class T, int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
@@ -47,11 +49,15 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
   constexpr int VEC = 16 / sizeof(T);      // elements per 16-byte load
   constexpr int TPR = D / VEC;             // threads per row
   constexpr int RPP = kPoolThreads / TPR;  // rows per pass
+  constexpr int NW = kPoolThreads / kWave;
   static_assert(kBlock % RPP == 0, "rows per pass must divide the block");
-  __shared__ float red[RPP][D];
+  static_assert(TPR <= kWave && kWave % TPR == 0, "a row is read by lanes of one wavefront");
+  __shared__ float part[kPoolBlocksPerWg][NW][D];  // per-wavefront column sums of each block
   __shared__ float xbar[kPoolBlocksPerWg][D];
 
   const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
   const int bh = blockIdx.y;
   const bool is_k = blockIdx.z != 0;
   const T* X = (is_k ? K : Q) + (size_t)bh * N * D;
@@ -64,16 +70,18 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
   const int col = (tid % TPR) * VEC;
   const int roff = tid / TPR;
 
-  // block b's rows: every load issued unconditionally (rows past N re-read the block's last
-  // row and are dropped in the sum; a block past n_b re-reads the last block), and block b + 1's
-  // loads go out before block b's sum, so each thread keeps two blocks' loads in flight
-  float tmp[2][kBlock / RPP][VEC];
-  auto load_block = [&](int b, float (&dst)[kBlock / RPP][VEC]) {
+  // block b's rows as raw 16-byte loads: every load issued unconditionally (rows past N re-read
+  // the block's last row and are dropped in the sum; a block past n_b re-reads the last block),
+  // and block b + 1's loads go out before block b's sum, so each thread keeps two blocks' loads
+  // in flight.  A block's column sums are reduced inside each wavefront (the lanes reading the
+  // same columns, by shuffles) and left per wavefront in LDS: no barrier until every block is
+  // summed.
+  i32x4 tmp[2][kBlock / RPP];
+  auto load_block = [&](int b, i32x4 (&dst)[kBlock / RPP]) {
     const int row0 = min(t0 + b, nb - 1) * kBlock;
     const int last = min(kBlock, N - row0) - 1;
 #pragma unroll
-    for (int p = 0; p < kBlock / RPP; ++p)
-      load_vec<T>(X + (size_t)(row0 + min(roff + p * RPP, last)) * D + col, dst[p]);
+    for (int p = 0; p < kBlock / RPP; ++p) dst[p] = ld16(X + (size_t)(row0 + min(roff + p * RPP, last)) * D + col);
   };
   load_block(0, tmp[0]);
 #pragma unroll
@@ -87,19 +95,26 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
 #pragma unroll
       for (int p = 0; p < kBlock / RPP; ++p)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] += roff + p * RPP < cnt ? tmp[b & 1][p][v] : 0.f;
+        for (int v = 0; v < VEC; ++v) acc[v] += roff + p * RPP < cnt ? raw_elem<T>(tmp[b & 1][p], v) : 0.f;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) red[roff][col + v] = acc[v];
-      __syncthreads();
-      if (tid < D) {
-        float sum = 0.f;
+      for (int o = TPR; o < kWave; o <<= 1)
 #pragma unroll
-        for (int r = 0; r < RPP; ++r) sum += red[r][tid];
-        xbar[b][tid] = sum / (float)cnt;
+        for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], o);
+      if (lane < TPR) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) part[b][wave][col + v] = acc[v];
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
+  for (int e = tid; e < nblk * D; e += kPoolThreads) {
+    const int b = e / D, c = e % D;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += part[b][w][c];
+    xbar[b][c] = sum / (float)min(kBlock, N - (t0 + b) * kBlock);
+  }
+  __syncthreads();
 
   // projection: y[b][c] = sum_r xbar[b][r] * W[r][c]; no W: the pooled means themselves
   constexpr int G = kPoolThreads / D;  // thread groups, each covering all D output columns
@@ -135,12 +150,19 @@ constexpr int kRowsPerWg = 16;   // query blocks per score/top-k workgroup (one 
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kMaxChunks = 32;   // n_b <= 2048
+// the float whose order-preserving key (float_key) is 0, below the key of every score: the
+// all-ones bit pattern (a NaN, never produced by the score arithmetic on finite inputs)
+#define kKeyZero __uint_as_float(0xffffffffu)
+
+// score row pitch in floats: a multiple of 16 plus 4, so that the four rows one MFMA result
+// register spans (4 apart) start 16 banks apart and a score store is free of bank conflicts
+__host__ __device__ constexpr int score_pitch(int nb) { return (nb + 15) / 16 * 16 + 4; }
 
 // Scores of 16 query blocks against all key blocks into LDS, then per row the k-th largest
 // score and the ascending compaction.  NCH = key slots per lane (at least ceil(n_b / 64)):
-// invalid slots hold key 0, below every valid key, so no slot needs a guard.  bias (optional,
-// [bh][n_b]) is added to every score of key block j before the selection; probs receives the
-// row softmax of the scores, or (raw) the scores themselves.
+// slots past n_b hold key 0, below every valid key.  bias (optional, [bh][n_b]) is added to
+// every score of key block j before the selection; probs receives the row softmax of the
+// scores, or (raw) the scores themselves.
 template <int D, int NCH>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     const __bf16* __restrict__ q_hi, const __bf16* __restrict__ q_lo,
@@ -150,113 +172,181 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
   extern __shared__ float S[];  // [kRowsPerWg][nbp]
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wavefront-uniform
-  const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * kRowsPerWg;
+  // workgroup -> (head, 16-row tile): each XCD takes a contiguous range of the head-major
+  // items, so the workgroups sharing a head's key projections share that XCD's L2
+  const int ntile_rows = (nb + kRowsPerWg - 1) / kRowsPerWg;
+  const int item = xcd_remap(blockIdx.x, (int)gridDim.x);  // gridDim.x = row tiles x heads
+  const int bh = item / ntile_rows;
+  const int i0 = (item % ntile_rows) * kRowsPerWg;
   const size_t base = (size_t)bh * nb * D;
 
   // ---- scores: 16 x n_b tile, 16x16x32 MFMA on split operands (hi*hi + hi*lo + lo*hi) ----
+  // Operands come through buffer resources over the head's projections: rows past n_b read
+  // zero (range check), so no load sits behind a branch.  Wavefront w takes the key tiles
+  // w, w + 8, ..., each tile's loads issued while the previous tile's MFMAs run.
   {
     constexpr int KS = D / 32;
+    const uint32_t bytes = (uint32_t)((size_t)nb * D * sizeof(__bf16));
+    const __amdgpu_buffer_rsrc_t rqh = make_rsrc(q_hi + base, bytes), rql = make_rsrc(q_lo + base, bytes);
+    const __amdgpu_buffer_rsrc_t rkh = make_rsrc(k_hi + base, bytes), rkl = make_rsrc(k_lo + base, bytes);
+    // lane's row of a 16-row tile and its 8 columns of k step s: (lane % 16, 32 s + 8 (lane / 16))
+    const uint32_t loff = (uint32_t)(((lane % 16) * D + 8 * (lane / 16)) * sizeof(__bf16));
+    auto ld = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    };
     bf16x8 ahi[KS], alo[KS];
-    const int arow = i0 + lane % 16;
+    const uint32_t aoff = loff + (uint32_t)(i0 * D * sizeof(__bf16));
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int col = 32 * s + 8 * (lane / 16);
-      ahi[s] = arow < nb ? *reinterpret_cast<const bf16x8*>(q_hi + base + (size_t)arow * D + col) : bf16x8{};
-      alo[s] = arow < nb ? *reinterpret_cast<const bf16x8*>(q_lo + base + (size_t)arow * D + col) : bf16x8{};
+      ahi[s] = ld(rqh, aoff + 64 * s);
+      alo[s] = ld(rql, aoff + 64 * s);
     }
     const int ntiles = (nb + 15) / 16;
-    // two key tiles per step: all their operand loads are issued before the MFMAs
-    for (int jt = wave; jt < ntiles; jt += 2 * kTopkWaves) {
-      bf16x8 bhi[2][KS], blo[2][KS];
+    bf16x8 bhi[2][KS], blo[2][KS];
+    auto load_tile = [&](int t, bf16x8 (&h)[KS], bf16x8 (&l)[KS]) {
+      const uint32_t off = loff + (uint32_t)(t * 16 * D * sizeof(__bf16));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int j = (jt + u * kTopkWaves) * 16 + lane % 16;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int col = 32 * s + 8 * (lane / 16);
-          bhi[u][s] = j < nb ? *reinterpret_cast<const bf16x8*>(k_hi + base + (size_t)j * D + col) : bf16x8{};
-          blo[u][s] = j < nb ? *reinterpret_cast<const bf16x8*>(k_lo + base + (size_t)j * D + col) : bf16x8{};
-        }
+      for (int s = 0; s < KS; ++s) {
+        h[s] = ld(rkh, off + 64 * s);
+        l[s] = ld(rkl, off + 64 * s);
       }
+    };
+    auto score_tile = [&](int t, const bf16x8 (&h)[KS], const bf16x8 (&l)[KS]) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = jt + u * kTopkWaves;
-        if (t >= ntiles) break;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          acc = mfma16(alo[s], bhi[u][s], acc);
-          acc = mfma16(ahi[s], blo[u][s], acc);
-          acc = mfma16(ahi[s], bhi[u][s], acc);
-        }
-        const int j = t * 16 + lane % 16;
-        const float bj = (bias && j < nb) ? bias[(size_t)bh * nb + j] : 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[(4 * (lane / 16) + r) * nbp + j] = fmaf(acc[r], scale, bj);
+      for (int s = 0; s < KS; ++s) {
+        acc = mfma16(alo[s], h[s], acc);
+        acc = mfma16(ahi[s], l[s], acc);
+        acc = mfma16(ahi[s], h[s], acc);
       }
+      const int j = t * 16 + lane % 16;  // columns past n_b land in the row padding
+      const bool jok = j < nb;
+      const float bj = (bias && jok) ? bias[(size_t)bh * nb + j] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[(4 * (lane / 16) + r) * nbp + j] = jok ? fmaf(acc[r], scale, bj) : kKeyZero;
+    };
+    // the row padding past the last 16-column tile
+    for (int e = threadIdx.x; e < kRowsPerWg * (nbp - 16 * ntiles); e += kTopkThreads)
+      S[(e / (nbp - 16 * ntiles)) * nbp + 16 * ntiles + e % (nbp - 16 * ntiles)] = kKeyZero;
+    // tiles past the last one read zero (range check) and are never scored
+    load_tile(wave, bhi[0], blo[0]);
+    for (int t = wave; t < ntiles; t += 2 * kTopkWaves) {
+      load_tile(t + kTopkWaves, bhi[1], blo[1]);
+      score_tile(t, bhi[0], blo[0]);
+      if (t + kTopkWaves >= ntiles) break;
+      load_tile(t + 2 * kTopkWaves, bhi[0], blo[0]);
+      score_tile(t + kTopkWaves, bhi[1], blo[1]);
     }
   }
   __syncthreads();
 
-  // ---- per row: k-th largest key, then ascending compaction ----
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // ---- per row: the k-th largest key T, then ascending compaction ----
+  // T is found bit by bit from the top: T is the largest value with at least topk keys >= T, so
+  // bit b of T is set iff count(key >= T | 2^b) >= topk, a count taken by ballots.  After the
+  // top 12 bits the k-th largest key lies in the band of keys sharing T's top 12 bits (a band
+  // an eighth of a binade wide, which typically holds a few percent of the scores); the keys
+  // above the band are counted, the band's keys are compacted into the row's LDS storage (the
+  // scores are in registers by then), and the low 20 bits are searched over the band alone
+  // (two keys per lane).  A band of more than 128 keys (many equal scores) keeps the search over
+  // every key.  The padding columns of a score row hold the float whose key is 0 (below every
+  // score), so the slots past n_b need no test.
+  // The lane index is laundered through an empty asm in every row so that the compiler keeps
+  // no per-lane comparison across rows (it would hold them as scalar masks and spill them).
+  constexpr int kBandShift = 20;
   for (int r = wave; r < kRowsPerWg; r += kTopkWaves) {
     const int i = i0 + r;
     if (i >= nb) break;
-    const float* srow = S + r * nbp;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint64_t lt_mask = (ln == 0) ? 0ull : (~0ull >> (64 - ln));
+    float* srow = S + r * nbp;
+    if (probs && raw) {
+      float* prow = probs + ((size_t)bh * nb + i) * nb;
+      for (int j = ln; j < nb; j += kWave) prow[j] = srow[j];
+    } else if (probs) {
+      float mx = -INFINITY;
+      for (int j = ln; j < nb; j += kWave) mx = fmaxf(mx, srow[j]);
+      mx = wave_max(mx);
+      float sum = 0.f;
+      for (int j = ln; j < nb; j += kWave) sum += __expf(srow[j] - mx);
+      sum = wave_sum(sum);
+      const float inv = 1.f / sum;
+      float* prow = probs + ((size_t)bh * nb + i) * nb;
+      for (int j = ln; j < nb; j += kWave) prow[j] = __expf(srow[j] - mx) * inv;
+    }
     u32 key[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int j = c * kWave + lane;
-      key[c] = j < nb ? float_key(srow[j]) : 0u;
-    }
-    // largest threshold T with count(key >= T) >= topk (all valid keys are >= 1)
+    for (int c = 0; c < NCH; ++c) key[c] = float_key(srow[min(c * kWave + ln, nbp - 1)]);
     u32 T = 0xffffffffu;  // topk == 0: nothing is kept
     if (topk > 0) {
       T = 0;
-      for (int bit = 31; bit >= 0; --bit) {
+      for (int bit = 31; bit >= kBandShift; --bit) {
         const u32 cand = T | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) cnt += __popcll(__ballot(key[c] >= cand));
         if (cnt >= topk) T = cand;
       }
-    }
-    int gt = 0;
+      const u32 tb = T >> kBandShift;
+      int above = 0, m = 0;
+      u32* band = reinterpret_cast<u32*>(srow);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the score reads come first
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) gt += __popcll(__ballot(key[c] > T));
-    const int need = topk - gt;  // equal keys to keep, lowest index first
-    int pos = 0, ties = 0;
+      for (int c = 0; c < NCH; ++c) {
+        above += __popcll(__ballot((key[c] >> kBandShift) > tb));
+        const bool inb = (key[c] >> kBandShift) == tb && key[c] != 0u;
+        const uint64_t bmask = __ballot(inb);
+        const int at = m + __popcll(bmask & lt_mask);
+        if (inb && at < nbp) band[at] = key[c];
+        m += __popcll(bmask);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (m <= 2 * kWave) {
+        const int need = topk - above;  // 1 <= need <= m
+        const u32 b0 = ln < m ? band[ln] : 0u;
+        const u32 b1 = ln + kWave < m ? band[ln + kWave] : 0u;
+        for (int bit = kBandShift - 1; bit >= 0; --bit) {
+          const u32 cand = T | (1u << bit);
+          const int cnt = __popcll(__ballot(b0 >= cand)) + __popcll(__ballot(b1 >= cand));
+          if (cnt >= need) T = cand;
+        }
+      } else {
+        for (int bit = kBandShift - 1; bit >= 0; --bit) {
+          const u32 cand = T | (1u << bit);
+          int cnt = 0;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) cnt += __popcll(__ballot(key[c] >= cand));
+          if (cnt >= topk) T = cand;
+        }
+      }
+    }
     int32_t* irow = idx + ((size_t)bh * nb + i) * topk;
     uint8_t* mrow = mask ? mask + ((size_t)bh * nb + i) * nb : nullptr;
+    if (topk > 0) {
+      int gt = 0;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int j = c * kWave + lane;
-      const bool valid = j < nb;
-      const bool eq = valid && topk > 0 && key[c] == T;
-      const uint64_t eqm = __ballot(eq);
-      const int rank = ties + __popcll(eqm & lt_mask);
-      const bool sel = valid && topk > 0 && (key[c] > T || (eq && rank < need));
-      const uint64_t selm = __ballot(sel);
-      if (sel) irow[pos + __popcll(selm & lt_mask)] = j;
-      if (mrow && valid) mrow[j] = sel ? 1 : 0;
-      pos += __popcll(selm);
-      ties += __popcll(eqm);
-    }
-    if (probs && raw) {
-      float* prow = probs + ((size_t)bh * nb + i) * nb;
-      for (int j = lane; j < nb; j += kWave) prow[j] = srow[j];
-    } else if (probs) {
-      float mx = -INFINITY;
-      for (int j = lane; j < nb; j += kWave) mx = fmaxf(mx, srow[j]);
-      mx = wave_max(mx);
-      float sum = 0.f;
-      for (int j = lane; j < nb; j += kWave) sum += __expf(srow[j] - mx);
-      sum = wave_sum(sum);
-      const float inv = 1.f / sum;
-      float* prow = probs + ((size_t)bh * nb + i) * nb;
-      for (int j = lane; j < nb; j += kWave) prow[j] = __expf(srow[j] - mx) * inv;
+      for (int c = 0; c < NCH; ++c) gt += __popcll(__ballot(key[c] > T));
+      const int need = topk - gt;  // equal keys to keep, lowest index first
+      int pos = 0, ties = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int j = c * kWave + ln;
+        const bool eq = key[c] == T;  // T >= 1, so no slot past n_b is equal or above
+        const uint64_t eqm = __ballot(eq);
+        const int rank = ties + __popcll(eqm & lt_mask);
+        const bool sel = key[c] > T || (eq && rank < need);
+        const uint64_t selm = __ballot(sel);
+        const int at = pos + __popcll(selm & lt_mask);
+        if (sel && at < topk) irow[at] = j;  // at < topk always; the test keeps idx in bounds
+        if (mrow && j < nb) mrow[j] = sel ? 1 : 0;
+        pos += __popcll(selm);
+        ties += __popcll(eqm);
+      }
+    } else if (mrow) {
+      for (int j = ln; j < nb; j += kWave) mrow[j] = 0;
     }
   }
 }
@@ -266,8 +356,9 @@ hipError_t launch_topk(const Dims& p, const __bf16* q_hi, const __bf16* q_lo,
                        const __bf16* k_hi, const __bf16* k_lo, const float* bias, int raw,
                        int32_t* idx, uint8_t* mask, float* probs, size_t lds,
                        hipStream_t stream) {
-  const int nbp = (p.nb + 15) / 16 * 16;
-  dim3 grid((p.nb + kRowsPerWg - 1) / kRowsPerWg, p.B * p.H);
+  const int nbp = score_pitch(p.nb);
+  // a 1-D grid: one workgroup per (16-row tile, head)
+  dim3 grid((p.nb + kRowsPerWg - 1) / kRowsPerWg * p.B * p.H, 1);
   const float scale = 1.0f / sqrtf((float)D);
   const int nch = (p.nb + kWave - 1) / kWave;
   auto go = [&](auto kern) -> hipError_t {
@@ -289,8 +380,7 @@ hipError_t launch_topk(const Dims& p, const __bf16* q_hi, const __bf16* q_lo,
 }  // namespace
 
 size_t route_lds_bytes(int nb) {
-  const int nbp = (nb + 15) / 16 * 16;
-  return (size_t)kRowsPerWg * nbp * sizeof(float);
+  return (size_t)kRowsPerWg * score_pitch(nb) * sizeof(float);
 }
 
 int route_max_blocks() { return kMaxChunks * kWave; }
