@@ -121,6 +121,30 @@ def test_route_exact_ties_keep_lowest_index():
     assert idx.cpu().numpy().tolist() == [[[[0, 1, 2, 3, 4]] * 16]]
 
 
+@pytest.mark.parametrize("k", [150, 250])
+def test_route_wide_ties_fall_back_to_the_full_search(k):
+    """600 key blocks whose scores take two values (every third block high): more than 128 keys
+    share the k-th largest score's top bits, so the select keeps its bitwise search over every
+    key rather than over the compacted band; the lowest indices win every tie."""
+    d = torch.device("cuda:0")
+    nb = 600
+    Q = torch.ones((1, 1, nb * 64, 128), dtype=torch.bfloat16, device=d)
+    scale = torch.where(torch.arange(nb) % 3 == 0, 1.0, 0.5).repeat_interleave(64)
+    K = (torch.ones((1, 1, nb * 64, 128)) * scale[None, None, :, None]).to(torch.bfloat16).to(d)
+    W = torch.eye(128, dtype=torch.float32, device=d)
+    say(f"route wide ties k={k}")
+    idx, mask, _ = sla.route(Q, K, W, W, k, want_mask=True)
+    high = [j for j in range(nb) if j % 3 == 0]
+    low = [j for j in range(nb) if j % 3 != 0]
+    want = sorted(high[:k] + low[:max(0, k - len(high))])
+    got = idx.cpu().numpy()
+    assert got.shape == (1, 1, nb, k)
+    assert (got == np.array(want)[None, None, None, :]).all()
+    r = oracle.route(Q.cpu(), K.cpu(), W.cpu().double(), W.cpu().double(), k, 64)
+    assert np.array_equal(got, r["idx"])
+    assert np.array_equal(mask.cpu().numpy(), r["mask"])
+
+
 # ---------------------------------------------------------------------------------- forward
 
 
