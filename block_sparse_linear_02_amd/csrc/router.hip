@@ -28,6 +28,7 @@ namespace sla {
 namespace {
 
 constexpr int kPoolBlocksPerWg = 8;
+constexpr int kPoolDepth = 2;  // blocks whose loads a thread keeps in flight
 constexpr int kPoolThreads = 256;
 
 // element v of a 16-byte load of T values, as float
@@ -72,21 +73,23 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
 
   // block b's rows as raw 16-byte loads: every load issued unconditionally (rows past N re-read
   // the block's last row and are dropped in the sum; a block past n_b re-reads the last block),
-  // and block b + 1's loads go out before block b's sum, so each thread keeps two blocks' loads
-  // in flight.  A block's column sums are reduced inside each wavefront (the lanes reading the
+  // and block b + kPoolDepth - 1's loads go out before block b's sum, so each thread keeps
+  // kPoolDepth blocks' loads in flight.  A block's column sums are reduced inside each wavefront (the lanes reading the
   // same columns, by shuffles) and left per wavefront in LDS: no barrier until every block is
   // summed.
-  i32x4 tmp[2][kBlock / RPP];
+  i32x4 tmp[kPoolDepth][kBlock / RPP];
   auto load_block = [&](int b, i32x4 (&dst)[kBlock / RPP]) {
     const int row0 = min(t0 + b, nb - 1) * kBlock;
     const int last = min(kBlock, N - row0) - 1;
 #pragma unroll
     for (int p = 0; p < kBlock / RPP; ++p) dst[p] = ld16(X + (size_t)(row0 + min(roff + p * RPP, last)) * D + col);
   };
-  load_block(0, tmp[0]);
+#pragma unroll
+  for (int b = 0; b + 1 < kPoolDepth; ++b) load_block(b, tmp[b]);
 #pragma unroll
   for (int b = 0; b < kPoolBlocksPerWg; ++b) {
-    if (b + 1 < kPoolBlocksPerWg) load_block(b + 1, tmp[(b + 1) & 1]);
+    if (b + kPoolDepth - 1 < kPoolBlocksPerWg)
+      load_block(b + kPoolDepth - 1, tmp[(b + kPoolDepth - 1) % kPoolDepth]);
     if (b < nblk) {
       const int cnt = min(kBlock, N - (t0 + b) * kBlock);
       float acc[VEC];
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(
 #pragma unroll
       for (int p = 0; p < kBlock / RPP; ++p)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] += roff + p * RPP < cnt ? raw_elem<T>(tmp[b & 1][p], v) : 0.f;
+        for (int v = 0; v < VEC; ++v) acc[v] += roff + p * RPP < cnt ? raw_elem<T>(tmp[b % kPoolDepth][p], v) : 0.f;
 #pragma unroll
       for (int o = TPR; o < kWave; o <<= 1)
 #pragma unroll
