@@ -897,7 +897,8 @@ def main():
     # HBM streams: the router reads Q and K once and writes the index lists; the state kernels
     # read K and V once and write per-block z_j plus the per-(b, h) totals; in the mask-product
     # mode they also write every h_j^T (bf16), which the mask GEMM reads back (once per 256 query
-    # blocks) before writing every T_i (bf16)
+    # blocks) before writing every T_i (bf16); with a low-bit sparse branch they also write the
+    # K and V codes
     es = Q.element_size()
     route_bytes = 2 * B * H * N * d * es + B * H * nb * wl.topk * 4
     states_bytes = 2 * B * H * N * d * es + B * H * nb * d * 4 + B * H * (d * d * 4 + d * 4)
@@ -907,6 +908,8 @@ def main():
         states_bytes = (2 * B * H * N * d * es + B * H * nb * d * 4 + hj_bytes
                         + hj_bytes * -(-nb // 256) + hj_bytes)
         gemm_flops = 2.0 * B * H * nb * nb * d * d
+    if fp8 or int8:  # the state kernel also writes the K and V codes (1 byte each) and scales
+        states_bytes += 2 * B * H * N * d + 2 * B * H * nb * 4
 
     rec = {
         "metric": "sparse-linear attn fwd ms/call + effective TFLOPS, N=32768 H=12 d=128 90% sparse",

@@ -264,7 +264,13 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = hipEventRecord(opts->states_begin, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
-  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, w.hj_bf, stream, flags);
+  // the low-bit branch's K and V codes come out of the state kernel, which reads K and V anyway
+  // (heads with a dropped linear branch skip that kernel, so then they are quantised apart)
+  const sla::StateQuant sq{w.k8, w.v8, w.sk, w.sv, int8};
+  const char* sep = getenv("SLA_SEPARATE_QUANT");
+  const bool kv_codes = fp8 && !flags && !w.hj && !(sep && sep[0] == '1' && sep[1] == '\0');
+  e = sla::launch_states(d, K, V, w.zb, w.h_part, w.z_part, w.hj, w.hj_bf, stream, flags,
+                         kv_codes ? &sq : nullptr);
   if (e != hipSuccess) return hip_fail(e);
   e = sla::launch_state_reduce(d, w.h_part, w.z_part, w.ht_hi, w.ht_lo, w.Z, w.h_full, stream);
   if (e != hipSuccess) return hip_fail(e);
@@ -285,8 +291,8 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
   }
   if (fp8) {
     e = sla::launch_quantize(d, Q, w.q8, w.sq, stream, int8);
-    if (e == hipSuccess) e = sla::launch_quantize(d, K, w.k8, w.sk, stream, int8);
-    if (e == hipSuccess) e = sla::launch_quantize_v8t(d, V, w.v8, w.sv, stream, int8);
+    if (e == hipSuccess && !kv_codes) e = sla::launch_quantize(d, K, w.k8, w.sk, stream, int8);
+    if (e == hipSuccess && !kv_codes) e = sla::launch_quantize_v8t(d, V, w.v8, w.sv, stream, int8);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (opts && opts->sparse_begin) {

@@ -34,16 +34,12 @@
 #include "sla_device.hpp"
 #include "sla_launch.hpp"
 #include "sla_tiles.hpp"
+#include "sla_quant.hpp"
 
 namespace sla {
 
 namespace {
 
-constexpr float kE4M3Max = 448.f;
-constexpr float kInt8Max = 127.f;
-enum { kFmtE4M3 = 0, kFmtInt8 = 1 };
-template <int FMT>
-constexpr float fmt_max() { return FMT == kFmtInt8 ? kInt8Max : kE4M3Max; }
 
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   // formats 0/0 = e4m3 for both operands; scale exponents 127 = 2^0
@@ -70,26 +66,6 @@ __device__ __forceinline__ u32 cvt4_u7(float a, float b, float c, float d, float
   const u32 z = __float_as_uint(fmaf(c, qs, kMagic)), w = __float_as_uint(fmaf(d, qs, kMagic));
   return (x & 0xffu) | ((y & 0xffu) << 8) | ((z & 0xffu) << 16) | (w << 24);
 }
-// int8 codes of 4 floats (round to nearest even, saturating at +-127)
-__device__ __forceinline__ u32 cvt4_i8(float a, float b, float c, float d) {
-  auto q = [](float v) { return (u32)(uint8_t)(int8_t)(int)rintf(fminf(fmaxf(v, -kInt8Max), kInt8Max)); };
-  return q(a) | (q(b) << 8) | (q(c) << 16) | (q(d) << 24);
-}
-
-// e4m3 codes of 4 floats (round to nearest even; the caller keeps |x| <= 448)
-__device__ __forceinline__ u32 cvt4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (u32)w;
-}
-__device__ __forceinline__ float sat(float x) { return fminf(fmaxf(x, -kE4M3Max), kE4M3Max); }
-
-// key position inside a transposed V8 row: lane group g of the PV MFMA reads bytes
-// 32g .. 32g + 31, k-slot 16kt + 4q + e <-> key 32kt + 8q + 4g + e
-__device__ __forceinline__ int v8_pos(int n) {
-  const int kt = n / 32, q = (n % 32) / 8, g = (n % 8) / 4, e = n % 4;
-  return 32 * g + 16 * kt + 4 * q + e;
-}
 
 template <int D, bool TRANSPOSED, int FMT>
 __global__ __launch_bounds__(256) void quantize_kernel(const __bf16* __restrict__ X, int N,
@@ -104,59 +80,32 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16* __restrict_
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int PER = kBlock * CPR / 256;     // chunks per thread
   const __bf16* Xb = X + ((size_t)bh * N + row0) * D;
-  bf16x8 v[PER];
-  float amax = 0.f;
+  i32x4 v[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int q = tid + u * 256, r = q / CPR, ch = q % CPR;
-    v[u] = r < cnt ? *reinterpret_cast<const bf16x8*>(Xb + (size_t)r * D + ch * 8) : bf16x8{};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf2f(v[u][e])));
+    v[u] = r < cnt ? ld16(Xb + (size_t)r * D + ch * 8) : i32x4{0, 0, 0, 0};
   }
-  amax = wave_max(amax);
+  float amax = wave_max(qz_local_amax(v));
   if (lane == 0) wmax[w] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  constexpr float QMAX = fmt_max<FMT>();
-  const float inv = amax > 0.f ? QMAX / amax : 0.f;
-  if (tid == 0) scales[(size_t)bh * nb + t] = amax > 0.f ? amax / QMAX : 1.f;
-  auto cvt4 = [](float a, float b, float c, float d) -> u32 {
-    if constexpr (FMT == kFmtInt8)
-      return cvt4_i8(a, b, c, d);
-    else
-      return cvt4_e4m3(sat(a), sat(b), sat(c), sat(d));
-  };
+  const float inv = qz_inv<FMT>(amax);
+  if (tid == 0) scales[(size_t)bh * nb + t] = qz_scale<FMT>(amax);
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int q = tid + u * 256, r = q / CPR, ch = q % CPR;
-    if (!TRANSPOSED && r >= cnt) continue;  // past N: no such row in the output
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = bf2f(v[u][e]) * inv;
     if constexpr (!TRANSPOSED) {
-      const u32 lo = cvt4(y[0], y[1], y[2], y[3]);
-      const u32 hi = cvt4(y[4], y[5], y[6], y[7]);
-      uint8_t* dst = codes + ((size_t)bh * N + row0 + r) * D + ch * 8;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+      if (r >= cnt) continue;  // past N: no such row in the output
+      *reinterpret_cast<uint2*>(codes + ((size_t)bh * N + row0 + r) * D + ch * 8) = qz_row_codes<FMT>(v[u], inv);
     } else {
-      // [c][pos(r)] staged in LDS (keys past N get code 0: their P8 is 0 as well), written out
-      // below with 16-byte stores
-      const u32 lo = cvt4(y[0], y[1], y[2], y[3]);
-      const u32 hi = cvt4(y[4], y[5], y[6], y[7]);
-      const int pos = v8_pos(r);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tl[(ch * 8 + e) * kBlock + pos] = (uint8_t)(lo >> (8 * e));
-        tl[(ch * 8 + 4 + e) * kBlock + pos] = (uint8_t)(hi >> (8 * e));
-      }
+      // [c][pos(r)] staged in LDS (keys past N get code 0: their P8 is 0 as well)
+      qz_tr_codes<FMT>(v[u], inv, tl, r, ch);
     }
   }
   if constexpr (TRANSPOSED) {
     __syncthreads();
-    // [bh][t][c][pos]: D rows of 64 bytes, one 16-byte piece per thread and step
-    uint8_t* dst = codes + ((size_t)bh * nb + t) * D * kBlock;
-    for (int q = tid; q < D * kBlock / 16; q += 256)
-      *reinterpret_cast<i32x4*>(dst + q * 16) = *reinterpret_cast<const i32x4*>(tl + q * 16);
+    qz_tr_flush<D, 256>(tl, codes + ((size_t)bh * nb + t) * D * kBlock, tid);  // [bh][t][c][pos]
   }
 }
 

@@ -18,6 +18,7 @@
 #include "sla_device.hpp"
 #include "sla_launch.hpp"
 #include "sla_tiles.hpp"
+#include "sla_quant.hpp"
 
 namespace sla {
 
@@ -27,12 +28,20 @@ constexpr int kStateThreads = 256;
 
 // MODE: 0 totals only, 1 also every h_j in fp32 in the natural layout h_j[c'][c] (K channel
 // major), 2 also every h_j^T[c][c'] (V channel major) rounded to bf16, stored in slices of 64
-// entries, slice-major, so that one slice of all blocks is contiguous
-template <class T, int D, int MODE>
+// entries, slice-major, so that one slice of all blocks is contiguous.
+// QF (bf16 inputs, d = 128): -1 nothing more; kFmtE4M3 or kFmtInt8: also the low-bit sparse
+// branch's per-block codes and scales of K (row-major) and V (transposed per block), from the
+// tiles' registers on their way to LDS, the same bytes as the stand-alone quantiser (the
+// quantisation helpers are shared), so K and V are read once for both
+template <class T, int D, int MODE, int QF = -1>
 __global__ __launch_bounds__(kStateThreads) void state_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int N, int nb, int cb,
     float* __restrict__ zb, float* __restrict__ h_part, float* __restrict__ z_part,
-    void* __restrict__ hj, const uint32_t* __restrict__ flags) {
+    void* __restrict__ hj, const uint32_t* __restrict__ flags,
+    uint8_t* __restrict__ k8 = nullptr, uint8_t* __restrict__ v8t = nullptr,
+    float* __restrict__ sk = nullptr, float* __restrict__ sv = nullptr) {
+  constexpr bool QUANT = QF >= 0;
+  static_assert(!QUANT || (sizeof(T) == 2 && D == 128), "the quantised branch takes bf16, d = 128");
   constexpr bool LITERAL = MODE != 0;
   // MODE 2 computes h_j = relu(K_j)^T V_j (rows: K channels) so that a lane's four consecutive
   // accumulator rows are four consecutive entries of a row of h_j^T; the others V^T relu(K)
@@ -41,6 +50,8 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
   __shared__ __attribute__((aligned(16))) __bf16 Ks[TileLayout<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[TileLayout<D>::ELEMS];
   __shared__ float zred[kStateThreads / D][D];
+  __shared__ float qmax[2][kStateThreads / kWave];  // per-wavefront absmax of the K and V tiles
+  __shared__ __attribute__((aligned(16))) uint8_t tl[QUANT ? D * kBlock : 16];  // V codes, transposed
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
@@ -78,9 +89,42 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
 
   for (int j = j0; j < j1; ++j) {
     __syncthreads();  // previous tile fully consumed
+    if constexpr (QUANT) {
+      // the previous block's V codes, staged below in its iteration
+      if (j > j0) qz_tr_flush<D, kStateThreads>(tl, v8t + ((size_t)bh * nb + j - 1) * D * kBlock, tid);
+      const float ak = wave_max(qz_local_amax(lk.r)), av = wave_max(qz_local_amax(lv.r));
+      if (lane == 0) {
+        qmax[0][wave] = ak;
+        qmax[1][wave] = av;
+      }
+    }
     lk.store(Ks, tid);
     lv.store(Vs, tid);
     __syncthreads();
+    if constexpr (QUANT) {
+      // block j's scales and codes from the registers, before they take the next tile's loads
+      float ak = qmax[0][0], av = qmax[1][0];
+#pragma unroll
+      for (int w = 1; w < kStateThreads / kWave; ++w) {
+        ak = fmaxf(ak, qmax[0][w]);
+        av = fmaxf(av, qmax[1][w]);
+      }
+      const float ik = qz_inv<QF>(ak), iv = qz_inv<QF>(av);
+      if (tid == 0) {
+        sk[(size_t)bh * nb + j] = qz_scale<QF>(ak);
+        sv[(size_t)bh * nb + j] = qz_scale<QF>(av);
+      }
+      const int cnt = min(kBlock, N - j * kBlock);
+      constexpr int CPR = D / 8;
+#pragma unroll
+      for (int u = 0; u < kBlock * CPR / kStateThreads; ++u) {
+        const int q = tid + u * kStateThreads, r = q / CPR, ch = q % CPR;
+        if (r < cnt)
+          *reinterpret_cast<uint2*>(k8 + ((size_t)bh * N + (size_t)j * kBlock + r) * D + ch * 8) =
+              qz_row_codes<QF>(lk.r[u], ik);
+        qz_tr_codes<QF>(lv.r[u], iv, tl, r, ch);
+      }
+    }
     if (j + 1 < j1) {
       const int nv = min(kBlock, N - (j + 1) * kBlock);
       lk.load(Kb + (size_t)(j + 1) * kBlock * D, nv, tid);
@@ -178,6 +222,11 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(
     }
   }
 
+  // the last block's V codes (staged before the loop's last barrier)
+  if constexpr (QUANT) {
+    if (j1 > j0) qz_tr_flush<D, kStateThreads>(tl, v8t + ((size_t)bh * nb + j1 - 1) * D * kBlock, tid);
+  }
+
   // chunk partial of H^T [c][c'] (not in MODE 2) and Z
   if constexpr (MODE != 2) {
     float* hp = h_part + ((size_t)bh * nchunk + chunk) * D * D;
@@ -267,9 +316,21 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ h
 template <class T, int D>
 hipError_t launch_states_t(const Dims& p, const void* K, const void* V, float* zb,
                            float* h_part, float* z_part, float* hj, __bf16* hj_bf,
-                           hipStream_t stream, const uint32_t* flags) {
+                           hipStream_t stream, const uint32_t* flags, const StateQuant* q) {
   const int cb = state_chunk_blocks(p, hj != nullptr || hj_bf == nullptr);
   dim3 grid((p.nb + cb - 1) / cb, p.B * p.H);
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    if (q) {  // the low-bit branch's K and V codes on the way (no literal mode, no dropped heads)
+      auto go = [&](auto kern, void* out) {
+        kern<<<grid, kStateThreads, 0, stream>>>((const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part,
+                                                 z_part, out, nullptr, q->k8, q->v8t, q->sk, q->sv);
+        return hipGetLastError();
+      };
+      if (hj_bf)
+        return q->int8 ? go(state_kernel<T, D, 2, kFmtInt8>, hj_bf) : go(state_kernel<T, D, 2, kFmtE4M3>, hj_bf);
+      return q->int8 ? go(state_kernel<T, D, 0, kFmtInt8>, nullptr) : go(state_kernel<T, D, 0, kFmtE4M3>, nullptr);
+    }
+  }
   if (hj)
     state_kernel<T, D, 1><<<grid, kStateThreads, 0, stream>>>(
         (const T*)K, (const T*)V, p.N, p.nb, cb, zb, h_part, z_part, hj, flags);
@@ -298,14 +359,15 @@ int state_chunk_blocks(const Dims& p, bool h_partials) {
 
 hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
                          float* z_part, float* hj, __bf16* hj_bf,
-                         hipStream_t stream, const uint32_t* flags) {
+                         hipStream_t stream, const uint32_t* flags, const StateQuant* q) {
+  if (q && (hj || flags || p.dtype != kBF16 || p.d != 128)) return hipErrorInvalidValue;
   if (p.dtype == kBF16 && p.d == 128)
-    return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags);
+    return launch_states_t<__bf16, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags, q);
   if (p.dtype == kBF16 && p.d == 64)
-    return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags);
+    return launch_states_t<__bf16, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags, q);
   if (p.dtype == kF32 && p.d == 128)
-    return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags);
-  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags);
+    return launch_states_t<float, 128>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags, q);
+  return launch_states_t<float, 64>(p, K, V, zb, h_part, z_part, hj, hj_bf, stream, flags, q);
 }
 
 hipError_t launch_state_reduce(const Dims& p, const float* h_part, const float* z_part,

@@ -35,9 +35,19 @@ int route_max_blocks();
 // mode) in slices of 64 entries: [BH][d*d/64][nb][64].
 int state_chunk_blocks(const Dims& p, bool h_partials = true);
 // flags (optional): heads flagged kDropLinear are skipped.
+// q (optional; bf16, d = 128, not with hj or flags): the low-bit sparse branch's per-block K
+// codes (row-major [BH][N][d]), V codes (transposed per block, [BH][nb][d][64]) and their scales
+// [BH][nb], the same bytes as launch_quantize / launch_quantize_v8t, written on the way.
+struct StateQuant {
+  uint8_t* k8;
+  uint8_t* v8t;
+  float* sk;
+  float* sv;
+  int int8;  // 0: OCP e4m3, 1: symmetric int8
+};
 hipError_t launch_states(const Dims& p, const void* K, const void* V, float* zb, float* h_part,
                          float* z_part, float* hj, __bf16* hj_bf, hipStream_t stream,
-                         const uint32_t* flags = nullptr);
+                         const uint32_t* flags = nullptr, const StateQuant* q = nullptr);
 
 // Mask-product mode: the complements of the router's index lists as bit rows
 // [BH][nb][mask_words(nb)], then T_i^T = sum_{j not in sel(i)} h_j^T for every query block in

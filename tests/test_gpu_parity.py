@@ -334,6 +334,23 @@ def test_fp8_forward_degenerate_k(k):
     check_close(got, ref, rel_tol=TOL_REL_FP8, max_tol=None, what=f"forward fp8 k={k}")
 
 
+@pytest.mark.parametrize("lowbit,mode", [("fp8", "mask_product"), ("fp8", "fused"), ("int8", "mask_product")])
+def test_lowbit_kv_codes_from_the_state_kernel(lowbit, mode, monkeypatch):
+    """The K and V codes the state kernel writes on its way through K and V give the same output,
+    bit for bit, as codes from the stand-alone quantiser (SLA_SEPARATE_QUANT=1), on a ragged
+    sequence (last block 16 tokens) with two heads."""
+    wl = small_ragged(k=6)
+    c = case("ragged_bf16", wl)
+    r = oracle_route(c, 6)
+    kw = {"fp8": lowbit == "fp8", "int8": lowbit == "int8", "linear_mode": mode}
+    say(f"forward {lowbit} {mode}: codes from the state kernel, then from their own launches")
+    monkeypatch.delenv("SLA_SEPARATE_QUANT", raising=False)
+    fused = run_forward(c, r["idx"], **kw)
+    monkeypatch.setenv("SLA_SEPARATE_QUANT", "1")
+    apart = run_forward(c, r["idx"], **kw)
+    assert np.array_equal(fused, apart), f"{lowbit} {mode}: max |diff| {np.abs(fused - apart).max()}"
+
+
 @pytest.mark.parametrize("k", [6, 0, 1, 57])
 def test_fp8_forward_mask_product(k):
     """The quantised sparse branch on two query blocks per workgroup (mask-product linear mode)
