@@ -34,7 +34,7 @@ constexpr int kStateThreads = 256;
 // tiles' registers on their way to LDS, the same bytes as the stand-alone quantiser (the
 // quantisation helpers are shared), so K and V are read once for both
 template <class T, int D, int MODE, int QF = -1>
-__global__ __launch_bounds__(kStateThreads) void state_kernel(
+__global__ __launch_bounds__(kStateThreads, QF >= 0 ? 2 : 1) void state_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int N, int nb, int cb,
     float* __restrict__ zb, float* __restrict__ h_part, float* __restrict__ z_part,
     void* __restrict__ hj, const uint32_t* __restrict__ flags,
