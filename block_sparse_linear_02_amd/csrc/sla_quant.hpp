@@ -78,23 +78,36 @@ __device__ __forceinline__ uint2 qz_row_codes(i32x4 chunk, float inv) {
   return make_uint2(qz_cvt4<FMT>(y[0], y[1], y[2], y[3]), qz_cvt4<FMT>(y[4], y[5], y[6], y[7]));
 }
 
-// the 8 codes of the chunk (row r, channels 8 ch .. + 7) into a transposed [D][64] byte tile
+// The transposed [D][64] byte tile in LDS: byte pos of channel row c sits at word
+// (pos / 4) ^ (c / 8) of the row (the words of a row permuted by the row's 8-channel group), so
+// that the 16 lanes writing one byte position of 16 channel groups at once hit 16 different
+// words (unpermuted, every row's byte pos falls in the same bank).
+__device__ __forceinline__ int qz_tr_at(int c, int pos) { return c * kBlock + ((((pos >> 2) ^ (c >> 3)) & 15) << 2) + (pos & 3); }
+
+// the 8 codes of the chunk (row r, channels 8 ch .. + 7) into the transposed tile
 template <int FMT>
 __device__ __forceinline__ void qz_tr_codes(i32x4 chunk, float inv, uint8_t* tl, int r, int ch) {
   const uint2 c = qz_row_codes<FMT>(chunk, inv);
   const int pos = v8_pos(r);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    tl[(ch * 8 + e) * kBlock + pos] = (uint8_t)(c.x >> (8 * e));
-    tl[(ch * 8 + 4 + e) * kBlock + pos] = (uint8_t)(c.y >> (8 * e));
+    tl[qz_tr_at(ch * 8 + e, pos)] = (uint8_t)(c.x >> (8 * e));
+    tl[qz_tr_at(ch * 8 + 4 + e, pos)] = (uint8_t)(c.y >> (8 * e));
   }
 }
 
-// a transposed [D][64] byte tile from LDS to its block's place in memory, 16 bytes per store
+// the transposed tile from LDS to its block's place in memory ([D][64] bytes, keys in v8_pos
+// order), 16 bytes per store
 template <int D, int THREADS>
 __device__ __forceinline__ void qz_tr_flush(const uint8_t* tl, uint8_t* dst, int tid) {
-  for (int q = tid; q < D * kBlock / 16; q += THREADS)
-    *reinterpret_cast<i32x4*>(dst + q * 16) = *reinterpret_cast<const i32x4*>(tl + q * 16);
+  for (int q = tid; q < D * kBlock / 16; q += THREADS) {
+    const int c = q / 4, k = q % 4;
+    const u32* row = reinterpret_cast<const u32*>(tl + c * kBlock);
+    i32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (int)row[((4 * k + i) ^ (c >> 3)) & 15];
+    *reinterpret_cast<i32x4*>(dst + q * 16) = v;
+  }
 }
 
 }  // namespace sla
