@@ -289,8 +289,11 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     e = hipEventRecord(opts->states_end, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
+  // the mask-product low-bit kernel quantises its own query blocks (each is read by one
+  // workgroup) unless the codes are made apart
+  const bool q_in_kernel = kv_codes && mode == SLA_LINEAR_MASK_PRODUCT;
   if (fp8) {
-    e = sla::launch_quantize(d, Q, w.q8, w.sq, stream, int8);
+    if (!q_in_kernel) e = sla::launch_quantize(d, Q, w.q8, w.sq, stream, int8);
     if (e == hipSuccess && !kv_codes) e = sla::launch_quantize(d, K, w.k8, w.sk, stream, int8);
     if (e == hipSuccess && !kv_codes) e = sla::launch_quantize_v8t(d, V, w.v8, w.sv, stream, int8);
     if (e != hipSuccess) return hip_fail(e);
@@ -300,8 +303,8 @@ int forward_impl(const sla_problem* p, const void* Q, const void* K, const void*
     if (e != hipSuccess) return hip_fail(e);
   }
   if (fp8 && mode == SLA_LINEAR_MASK_PRODUCT)
-    e = sla::launch_sparse_pair8(d, Q, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha, w.t_bf,
-                                 w.Z, w.zb, O, stream, int8, w.pairs);
+    e = sla::launch_sparse_pair8(d, Q, q_in_kernel ? nullptr : w.q8, w.k8, w.v8, w.sq, w.sk, w.sv,
+                                 idx, alpha, w.t_bf, w.Z, w.zb, O, stream, int8, w.pairs);
   else if (fp8)
     e = sla::launch_sparse_fp8(d, Q, K, V, w.q8, w.k8, w.v8, w.sq, w.sk, w.sv, idx, alpha,
                                w.ht_hi, w.ht_lo, w.Z, w.zb, O, stream);

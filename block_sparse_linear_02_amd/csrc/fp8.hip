@@ -493,7 +493,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void sparse_fp8_kernel(
 
 // The quantised sparse branch for two query blocks per workgroup, with the linear branch's
 // T_i = sum of the unselected blocks' states taken from memory (mask-product mode).  Wavefront w
-// takes rows 32 (w % 2) .. + 31 of query block 2p + w / 2.
+// takes rows 32 (w % 2) .. + 31 of query block 2p + w / 2.  Q's codes come from the stand-alone
+// quantiser (q8) or, q8 null, from this workgroup, which quantises its two query blocks itself.
 //   Pass 1 (no LDS, no barrier): each wavefront walks its own block's kept list with its K8
 //   operands read straight from memory one tile ahead, S = Q8 K8^T, each row's exact maximum;
 //   z_j of the kept blocks summed on the way.
@@ -552,6 +553,7 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   __shared__ int32_t sl[2][kMaxWords * 32];  // the two kept lists (pass 1 reads them from here)
   __shared__ float zeta[2][D];
   __shared__ float tmx[2][2][2];  // [step parity][block][wavefront half]: partial P tile maxima
+  __shared__ float qam[2][2];     // [block][wavefront half]: Q absmax (in-kernel quantisation)
   auto kbuf = [&](auto BUFC) -> uint8_t* { return decltype(BUFC)::value ? kb1 : kb0; };
   auto vbuf = [&](auto BUFC) -> uint8_t* { return decltype(BUFC)::value ? vb1 : vb0; };
   using B0 = std::integral_constant<int, 0>;
@@ -618,15 +620,43 @@ __global__ __launch_bounds__(kF8Threads, 2) void pair8_kernel(
   const bool row_ok = row < N;
   const bool rows_all_ok = __ballot(!row_ok) == 0;  // every row of this wavefront exists
   i32x8 qf[N8];  // e4m3 Q as the B operand: k-slot 32g + b of step s <-> channel 64s + 32g + b
-  {
+  float sqi;
+  if (q8) {  // codes and scales from the stand-alone quantiser
     const uint8_t* qr = q8 + hoff + (size_t)min(row, N - 1) * D + 32 * g;
 #pragma unroll
     for (int st = 0; st < N8; ++st) {
       const i32x4* pq = reinterpret_cast<const i32x4*>(qr + 64 * st);
       qf[st] = row_ok ? join8(pq[0], pq[1]) : i32x8{};
     }
+    sqi = sq[(size_t)bh * nb + qb];
+  } else {
+    // q8 null (grid-uniform): this workgroup quantises its own two query blocks, the only
+    // workgroup that reads them, with the shared quantiser helpers (the same codes and scale):
+    // each wavefront's absmax over its 32 rows meets its partner's in LDS
+    i32x4 qv[N8][4];  // channels 64 st + 32 g + 8 i .. + 7 of this lane's row, bf16
+    const __bf16* qr = Q + hoff + (size_t)min(row, N - 1) * D + 32 * g;
+    float am = 0.f;
+#pragma unroll
+    for (int st = 0; st < N8; ++st) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[st][i] = row_ok ? ld16(qr + 64 * st + 8 * i) : i32x4{0, 0, 0, 0};
+      am = fmaxf(am, qz_local_amax(qv[st]));
+    }
+    am = wave_max(am);
+    if (lane == 0) qam[blk][half] = am;
+    __syncthreads();
+    const float amax = fmaxf(qam[blk][0], qam[blk][1]);
+    const float inv = qz_inv<FMT>(amax);
+    sqi = qz_scale<FMT>(amax);
+#pragma unroll
+    for (int st = 0; st < N8; ++st) {
+      uint2 c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = qz_row_codes<FMT>(qv[st][i], inv);
+      qf[st] = i32x8{(int)c[0].x, (int)c[0].y, (int)c[1].x, (int)c[1].y,
+                     (int)c[2].x, (int)c[2].y, (int)c[3].x, (int)c[3].y};
+    }
   }
-  const float sqi = sq[(size_t)bh * nb + qb];
 
   // ---- pass 1: each row's exact maximum of S (log2 units) over its block's kept tiles (list
   // from LDS); K8 operands, the K scale and z_j from memory one tile ahead (rows past a short

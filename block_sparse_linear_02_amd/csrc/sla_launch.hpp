@@ -171,7 +171,8 @@ hipError_t launch_quantize_v8t(const Dims& p, const void* X, uint8_t* codes, flo
                                hipStream_t stream, int int8 = 0);
 // fp8 sparse branch, mask-product linear mode: two query blocks per workgroup over the union of
 // their kept blocks, T_i (bf16) from memory.  pairs (optional, launch_pair_match): the two query
-// blocks of pair slot p, else 2p and 2p + 1.
+// blocks of pair slot p, else 2p and 2p + 1.  q8 null: each workgroup quantises its own query
+// blocks from Q (sq unused), the same codes and scales as launch_quantize.
 hipError_t launch_sparse_pair8(const Dims& p, const void* Q, const uint8_t* q8, const uint8_t* k8,
                                const uint8_t* v8, const float* sq, const float* sk,
                                const float* sv, const int32_t* idx, const float* alpha,

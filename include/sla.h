@@ -155,10 +155,12 @@ int sla_forward_ex(const sla_problem* p, const void* Q, const void* K, const voi
  * (query block x key block) tile with scale max(tile) / 448 over exp(S - rowmax) using the
  * exact row maximum, and O_s = sum (P8 sP)(V8 sV) / sum exp(S - rowmax).  Only dtype
  * SLA_BF16 with d = 128 is compiled.  Needs sla_forward_workspace_bytes(p, 1) bytes.
- * The codes of K and V come out of the linear branch's state kernel, which reads K and V anyway;
- * with SLA_SEPARATE_QUANT=1 in the environment (read on every call; a debug switch for
- * comparing the two) they are made by launches of their own, as Q's are.  The bytes, and so the
- * output, are the same either way.  The same holds for sla_forward_int8. */
+ * The codes of K and V come out of the linear branch's state kernel, which reads K and V anyway,
+ * and in the mask-product mode each workgroup of the sparse kernel quantises its own two query
+ * blocks (in the fused mode Q has a launch of its own); with SLA_SEPARATE_QUANT=1 in the
+ * environment (read on every call; a debug switch for comparing the two) all three are made by
+ * launches of their own.  The bytes, and so the output, are the same either way.  The same
+ * holds for sla_forward_int8. */
 int sla_forward_fp8(const sla_problem* p, const void* Q, const void* K, const void* V,
                     const int32_t* idx, const float* alpha, float* O, void* ws, size_t ws_bytes,
                     hipStream_t stream);
