@@ -38,7 +38,7 @@ __device__ __forceinline__ float sat(float x) { return fminf(fmaxf(x, -kE4M3Max)
 
 // key position inside a transposed V8 row: lane group g of the PV MFMA reads bytes
 // 32g .. 32g + 31, k-slot 16kt + 4q + e <-> key 32kt + 8q + 4g + e
-__device__ __forceinline__ int v8_pos(int n) {
+__host__ __device__ __forceinline__ int v8_pos(int n) {
   const int kt = n / 32, q = (n % 32) / 8, g = (n % 8) / 4, e = n % 4;
   return 32 * g + 16 * kt + 4 * q + e;
 }
@@ -82,7 +82,8 @@ __device__ __forceinline__ uint2 qz_row_codes(i32x4 chunk, float inv) {
 // (pos / 4) ^ (c / 8) of the row (the words of a row permuted by the row's 8-channel group), so
 // that the 16 lanes writing one byte position of 16 channel groups at once hit 16 different
 // words (unpermuted, every row's byte pos falls in the same bank).
-__device__ __forceinline__ int qz_tr_at(int c, int pos) { return c * kBlock + ((((pos >> 2) ^ (c >> 3)) & 15) << 2) + (pos & 3); }
+__host__ __device__ __forceinline__ int qz_tr_word(int c, int w) { return ((w ^ (c >> 3)) & 15); }
+__host__ __device__ __forceinline__ int qz_tr_at(int c, int pos) { return c * kBlock + (qz_tr_word(c, pos >> 2) << 2) + (pos & 3); }
 
 // the 8 codes of the chunk (row r, channels 8 ch .. + 7) into the transposed tile
 template <int FMT>
@@ -105,7 +106,7 @@ __device__ __forceinline__ void qz_tr_flush(const uint8_t* tl, uint8_t* dst, int
     const u32* row = reinterpret_cast<const u32*>(tl + c * kBlock);
     i32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (int)row[((4 * k + i) ^ (c >> 3)) & 15];
+    for (int i = 0; i < 4; ++i) v[i] = (int)row[qz_tr_word(c, 4 * k + i)];
     *reinterpret_cast<i32x4*>(dst + q * 16) = v;
   }
 }

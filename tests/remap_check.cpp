@@ -3,10 +3,14 @@
 // onto every (head, item) with every XCD holding the same share (within one item) of every head;
 // xcd_chunk_id inverts it.  xcd_group_map<XG> does the same over xcd_group_grid<XG> with each
 // head on the XG XCDs of its group only (group h % (8 / XG)), balanced within one item over
-// them, and xcd_group_id<XG> inverts it.  Built and run on the CPU by tests/test_remap.py.
+// them, and xcd_group_id<XG> inverts it.  The quantiser's transposed staging of sla_quant.hpp:
+// v8_pos permutes the 64 keys, qz_tr_at places every byte of a channel row once inside that
+// row, the flush's qz_tr_word finds each 4-byte word again, and the 16 channel groups writing
+// one key position hit 16 different banks.  Built and run on the CPU by tests/test_remap.py.
 #include <cstdio>
 #include <vector>
 
+#include "sla_quant.hpp"
 #include "sla_tiles.hpp"
 
 template <int XG>
@@ -51,6 +55,42 @@ int check_group(int heads, int per) {
       return 1;
     }
   }
+  return 0;
+}
+
+int check_quant_staging() {
+  constexpr int D = 128;
+  std::vector<int> hit(64, 0);
+  for (int n = 0; n < 64; ++n) {
+    const int p = sla::v8_pos(n);
+    if (p < 0 || p >= 64 || hit[p]++) {
+      std::printf("v8_pos: key %d -> %d out of range or repeated\n", n, p);
+      return 1;
+    }
+  }
+  for (int c = 0; c < D; ++c) {
+    std::vector<int> row(64, 0);
+    for (int pos = 0; pos < 64; ++pos) {
+      const int a = sla::qz_tr_at(c, pos) - c * 64;
+      if (a < 0 || a >= 64 || row[a]++) {
+        std::printf("qz_tr_at: channel %d byte %d -> %d outside its row or repeated\n", c, pos, a);
+        return 1;
+      }
+      if (sla::qz_tr_word(c, pos >> 2) * 4 + (pos & 3) != a) {
+        std::printf("qz_tr_word: channel %d byte %d not found again by the flush\n", c, pos);
+        return 1;
+      }
+    }
+  }
+  for (int e = 0; e < 8; ++e)
+    for (int pos = 0; pos < 64; ++pos) {
+      std::vector<int> bank(64, 0);
+      for (int ch = 0; ch < 16; ++ch)
+        if (bank[(sla::qz_tr_at(8 * ch + e, pos) / 4) % 64]++) {
+          std::printf("qz_tr_at: channel groups share a bank at e %d byte %d\n", e, pos);
+          return 1;
+        }
+    }
   return 0;
 }
 
@@ -111,6 +151,7 @@ int main() {
     for (int per = 1; per <= 1024 && !bad; per += (per < 40 ? 1 : 53))
       bad = check_group<8>(heads, per) || check_group<4>(heads, per) || check_group<2>(heads, per) ||
             check_group<1>(heads, per);
+  if (!bad) bad = check_quant_staging();
   std::printf(bad ? "FAIL\n" : "OK\n");
   return bad;
 }
