@@ -10,7 +10,10 @@
 //   quantize_kernel   per (block, head): absmax -> inv = 448 / a, s = a / 448 (fp32, IEEE
 //                     division), code = e4m3_rne(min(max(x * inv, -448), 448)).  Row-major
 //                     codes, or (for V) a per-block transposed layout [d][64] whose key order
-//                     matches the P operand of the PV MFMA.
+//                     matches the P operand of the PV MFMA.  The forwards use it for Q in the
+//                     fused mode only (the state kernel writes the K and V codes, the
+//                     mask-product kernel quantises its own query blocks, all with the helpers
+//                     of sla_quant.hpp), and for everything under SLA_SEPARATE_QUANT=1.
 //   sparse_fp8_kernel one workgroup per query block, four wavefronts in the two roles of the
 //                     bf16 kernel.  Pass 1 over the kept blocks: the sparse wavefronts
 //                     compute S = Q8 K8^T (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales; K8

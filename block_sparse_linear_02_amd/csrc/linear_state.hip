@@ -12,7 +12,10 @@
 //                  4 wavefronts read them back transposed (ds_read_b64_tr_b16) as MFMA operands
 //                  and accumulate H^T = V^T relu(K) (bf16 MFMA, fp32 accumulation) for the
 //                  chunk, z_j by fp32 sums.  Literal mode also stores every h_j (fp32); the
-//                  mask-product mode stores every h_j^T rounded to bf16.
+//                  mask-product mode stores every h_j^T rounded to bf16.  With a low-bit
+//                  sparse branch it also writes each block's K and V codes and scales from the
+//                  tiles' registers (SLA2 Italian summary section 2.C: the forward quantises K
+//                  and V), so the quantiser does not read K and V again.
 //   reduce_kernel  sums the chunk partials in a fixed order (deterministic), splits H^T into
 //                  bf16 hi + lo parts (the sparse kernel's MFMA operand) and writes Z.
 #include "sla_device.hpp"
